@@ -1,0 +1,196 @@
+/*
+ * vsa.h -- C ABI of the MI355X (gfx950) library for the batched verify step of lossless
+ * speculative decoding.
+ *
+ * The step (as the mlx-dspark pages describe it): a target model verifies, for each of B
+ * sequences, a block of R_b = K_b + 1 rows -- the last committed token (the "anchor") and
+ * K_b drafted tokens -- in one forward pass, then accepts a prefix of the drafts.
+ *   - verify_attention: the multi-row causal attention of those rows against the
+ *     sequence's KV cache (mlx-dspark Changelog [0.20.0] "Added": multi-row decode
+ *     attention over the whole KV cache, every GQA head x query row of a KV head consuming
+ *     each KV tile; [0.3.1] "Fixed": native GQA, n_kv-head K/V with no tiling).
+ *   - verify_sample_accept: penalties, temperature, top-k / top-p truncation and
+ *     acceptance over the full vocabulary (Changelog [0.2.0] "Added": presence/frequency
+ *     penalties per verify position, logprobs / top_logprobs; [0.20.2] "Changed": top-k
+ *     threshold and nucleus cutoff without full-vocabulary sorts; release v0.1.0
+ *     "Highlights": truncation of both draft and target; release v0.0.2 "Highlights":
+ *     accept with probability min(1, p/q), resample the residual on rejection, greedy by
+ *     default; Changelog [0.2.0] "Decode-path performance": greedy acceptance as the
+ *     cumulative product of positionwise matches, one device sync per round).
+ *
+ * Conventions for every entry point:
+ *   - All array arguments are DEVICE pointers into caller-owned memory (e.g. torch
+ *     tensors' data_ptr()), row-major and densely packed, unless stated otherwise.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Calls only enqueue work: they
+ *     never synchronize and never allocate. Results are valid once the stream reaches the
+ *     point after the call.
+ *   - Host-checkable argument errors return a status before anything is enqueued. A launch
+ *     failure returns VSA_ERR_LAUNCH.
+ *   - Values only the device can see (lengths, token ids, per-sequence parameters) get
+ *     defined behaviour (clamped, or the row is treated as stated below) and set a bit in
+ *     the workspace's device error word: the uint32 at byte 0 of `workspace`. Bits are ORed
+ *     in and never cleared by the library; the caller reads (and may zero) it after the
+ *     stream completes.
+ *   - Workspace: caller-owned device memory of at least *_workspace_size() bytes, 256-byte
+ *     aligned, ZERO-FILLED BEFORE ITS FIRST USE. Calls leave their internal counters at
+ *     zero, so one workspace serves any number of calls in stream order. Two calls that
+ *     share a workspace must not run concurrently (different streams), and a workspace
+ *     sized for one problem serves any problem whose size query is not larger.
+ *   - No call keeps state between calls; the library is reentrant across workspaces.
+ */
+#ifndef VSA_H
+#define VSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum vsa_status {
+    VSA_OK = 0,
+    VSA_ERR_INVALID_ARG = 1,  /* a host-side argument is null, negative or inconsistent */
+    VSA_ERR_UNSUPPORTED = 2,  /* valid but outside the supported shapes (see limits) */
+    VSA_ERR_WORKSPACE = 3,    /* workspace missing, misaligned or too small */
+    VSA_ERR_LAUNCH = 4        /* the HIP runtime refused a launch */
+} vsa_status;
+
+typedef enum vsa_dtype {
+    VSA_F32 = 0,              /* IEEE binary32 */
+    VSA_BF16 = 1              /* bfloat16 bit patterns (uint16) */
+} vsa_dtype;
+
+/* Device error word bits (uint32 at workspace byte 0). */
+#define VSA_DEVERR_SEQ_SHAPE      0x01u /* R_b outside [1, max_rows_per_seq], ctx_b < 0, or
+                                           ctx_b + R_b > S_max or > max_kv_len: the
+                                           sequence is clamped into range */
+#define VSA_DEVERR_DRAFT_ID       0x02u /* a draft token id outside [0, V): that draft is
+                                           rejected and adds nothing to penalty counts */
+#define VSA_DEVERR_PARAMS         0x04u /* a sequence's parameters are out of range
+                                           (T < 0 or not finite, top_p outside (0, 1],
+                                           top_k < 0 or > max_top_k, top_logprobs outside
+                                           [0, max_top_logprobs]): the sequence is
+                                           verified greedily with no logprobs */
+#define VSA_DEVERR_NO_DRAFT_LOGITS 0x08u /* T > 0 but draft_logits is NULL: greedy */
+#define VSA_DEVERR_TIE_OVERFLOW   0x10u /* more ids tie at a top-k threshold than the
+                                           candidate capacity holds: the kept set is
+                                           truncated to the capacity */
+
+/* Per-sequence sampling parameters: the request parameters the pages list (temperature,
+ * top_p, top_k, presence/frequency penalty, logprobs, top_logprobs; release v0.1.0 and
+ * Changelog [0.2.0]). 28 bytes, 4-byte aligned, field order fixed. */
+typedef struct vsa_row_params {
+    float temperature;        /* 0 => greedy; > 0 => sampled at this temperature */
+    int32_t top_k;            /* 0 => off; else keep every id whose penalized logit is >= the
+                                 k-th largest (ties at the threshold are kept) */
+    float top_p;              /* 1 => off; in (0, 1): nucleus over the top-k set */
+    float presence_penalty;   /* subtracted once from every id with count > 0 */
+    float frequency_penalty;  /* subtracted count times from every id */
+    int32_t logprobs;         /* nonzero => write the chosen token's raw logprob */
+    int32_t top_logprobs;     /* number of raw top logprobs to write per row */
+} vsa_row_params;
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int vsa_version(void);
+
+/* Human-readable name of a status code (static string). */
+const char* vsa_status_string(vsa_status status);
+
+/* ------------------------------------------------------------------------------------
+ * verify_attention
+ *
+ * For sequence b (rows cu_rows[b] .. cu_rows[b+1]-1, R_b rows, ctx_b = ctx_lens[b] cached
+ * tokens before the block, whose K/V the caller has already written at cache positions
+ * ctx_b .. ctx_b + R_b - 1), verify row i and query head h, with G = Hq / Hkv:
+ *     g = h / G;  n = ctx_b + i + 1   (row i sees the cache and block rows 0..i)
+ *     out[row][h][:] = sum_{t<n} softmax_t(scale * <q[row][h], k[b][g][t]>) v[b][g][t][:]
+ * computed with fp32 accumulation (bf16 products are exact in fp32).
+ *
+ *   q          [total_rows, Hq, D]     dtype
+ *   k_cache    [B, Hkv, S_max, D]      dtype (positions >= ctx_b + R_b are never read)
+ *   v_cache    [B, Hkv, S_max, D]      dtype
+ *   dtype      VSA_BF16 (MFMA path) or VSA_F32
+ *   cu_rows    [B + 1] int32           0 = cu_rows[0] < cu_rows[1] < ... = total_rows
+ *   ctx_lens   [B] int32
+ *   B, total_rows, Hq, Hkv, D, S_max   host sizes; Hq % Hkv == 0; D in {64, 128}
+ *   max_rows_per_seq  host bound >= every R_b (at most 32)
+ *   max_kv_len host bound >= every ctx_b + R_b (sizes the key split; <= S_max)
+ *   scale      softmax scale; 0 => 1/sqrt(D)
+ *   out        [total_rows, Hq, D] float32, written for every row
+ * Limits: (Hq / Hkv) * max_rows_per_seq <= 128.
+ * ------------------------------------------------------------------------------------ */
+size_t verify_attention_workspace_size(int B, int Hq, int Hkv, int D, int max_rows_per_seq,
+                                       int max_kv_len);
+
+vsa_status verify_attention(const void* q, const void* k_cache, const void* v_cache,
+                            vsa_dtype dtype, const int32_t* cu_rows, const int32_t* ctx_lens,
+                            int B, int total_rows, int Hq, int Hkv, int D, int S_max,
+                            int max_rows_per_seq, int max_kv_len, float scale, float* out,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * verify_sample_accept
+ *
+ * Row i of sequence b (i = 0..K_b, K_b = R_b - 1) holds the target logits that decide the
+ * token at absolute position positions[b] + i; draft t (1..K_b) of sequence b is entry
+ * cu_rows[b] - b + t - 1 of draft_tokens / draft_logits and proposes that same token for
+ * row t - 1. For each sequence, with its parameters:
+ *   z_i = (x_i - frequency * c_i) - presence * [c_i > 0]   (fp32, this operation order)
+ *         c_i = token_counts[b] + the counts of drafts d_1..d_i
+ *   greedy (T == 0): a = length of the longest prefix with d_{t} = argmax z_{t-1} (lowest
+ *         id on ties); emit d_1..d_a and argmax z_a.
+ *   sampled (T > 0): p_i = softmax(z_i / T) truncated to {z >= k-th largest z} (top-k)
+ *         then to the smallest prefix by probability reaching top_p (ties kept), and
+ *         renormalized; q_t likewise from draft row t (no penalties). For t = 1..K_b draw
+ *         u (Philox4x32-10 keyed by seed, stream (b, position, tag 0)); accept d_t iff
+ *         u * q_t(d_t) < p_{t-1}(d_t); at the first rejection emit a draw from
+ *         max(0, p_{t-1} - q_t) and stop; if all are accepted emit a draw from p_{K_b}.
+ *         Draws are exponential races argmax_j w_j / E_j with E_j = -ln U'_j from the
+ *         (b, position, tag 1) stream.
+ *   logprobs: raw log-softmax of x (no penalties, temperature or truncation).
+ *
+ *   target_logits  [total_rows, V] float32
+ *   draft_logits   [total_rows - B, V] float32, or NULL when no sequence is sampled
+ *   draft_tokens   [total_rows - B] int32 (may be NULL when total_rows == B)
+ *   cu_rows        [B + 1] int32 (as above)
+ *   token_counts   [B, V] int32 base completion counts, or NULL (all zero)
+ *   params         [B] vsa_row_params (device memory)
+ *   positions      [B] int32 absolute position decided by row 0
+ *   seed           64-bit Philox key
+ *   max_rows_per_seq host bound >= every R_b (at most 32)
+ *   max_top_k      host bound >= every top_k in use (0 if no sequence uses top-k); <= 1024
+ *   max_top_logprobs host bound >= every top_logprobs (<= 32); the width of top_lp_*
+ * Outputs (each may be NULL when not wanted, except accepted_len and out_tokens):
+ *   accepted_len   [B] int32   accepted drafts a_b
+ *   out_tokens     [total_rows] int32   row i < a_b + 1 holds the emitted token, else -1
+ *   chosen_logprob [total_rows] float32 raw logprob of the emitted token at that row
+ *                  (sequences with logprobs != 0), NaN elsewhere
+ *   top_lp_vals    [total_rows, max_top_logprobs] float32 raw top logprobs, best first
+ *   top_lp_ids     [total_rows, max_top_logprobs] int32 their ids (ties: lower id first);
+ *                  entries past a sequence's top_logprobs are -1 / 0
+ *   diag_threshold [total_rows] float32 top-k threshold of each target row of a sampled
+ *                  sequence (-inf when top-k is off), NaN for greedy sequences
+ *   diag_kept      [total_rows, 2] int32 kept-set sizes after top-k and after top-p of
+ *                  each target row of a sampled sequence (0 for greedy sequences)
+ * Limits: V >= 1; K_b <= 31; top_p < 1 requires top_k > 0 (a nucleus over the whole
+ * vocabulary without top-k is not supported: VSA_DEVERR_PARAMS).
+ * ------------------------------------------------------------------------------------ */
+size_t verify_sample_accept_workspace_size(int B, int total_rows, int V, int max_rows_per_seq,
+                                           int max_top_k, int max_top_logprobs);
+
+vsa_status verify_sample_accept(const float* target_logits, const float* draft_logits,
+                                const int32_t* draft_tokens, const int32_t* cu_rows,
+                                const int32_t* token_counts, const vsa_row_params* params,
+                                const int32_t* positions, uint64_t seed, int B, int total_rows,
+                                int V, int max_rows_per_seq, int max_top_k,
+                                int max_top_logprobs, int32_t* accepted_len,
+                                int32_t* out_tokens, float* chosen_logprob, float* top_lp_vals,
+                                int32_t* top_lp_ids, float* diag_threshold, int32_t* diag_kept,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VSA_H */

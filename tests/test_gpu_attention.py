@@ -1,0 +1,102 @@
+"""GPU parity of verify_attention against the CPU oracle (elementwise,
+|gpu - oracle| <= 1e-3 + 2e-3 |oracle|), through the C ABI."""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from verify_step_attention_amd import workloads as wl  # noqa: E402
+from gpu_helpers import attention_gpu, attention_oracle, assert_attention_close  # noqa: E402
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+@pytest.mark.parametrize("name", ["tiny", "qwen3_4b", "batched", "verify_b4k4_ctx8192",
+                                  "long", "swarm"])
+def test_workload_parity(name):
+    _log(f"attention parity: workload {name}")
+    w = wl.make_workload(name)
+    got, err = attention_gpu(w)
+    assert err == 0
+    assert_attention_close(got, attention_oracle(w))
+
+
+@pytest.mark.parametrize("case", [
+    # (Hq, Hkv, D, dtype, ctx list, drafts list, max_kv_len override)
+    (32, 8, 128, wl.BF16, [0, 1, 127, 128], [0, 3, 4, 31], None),      # ctx 0, K=0, K=31
+    (8, 8, 64, wl.BF16, [300, 5], [2, 6], 4096),                        # D=64, MHA, empty splits
+    (64, 8, 128, wl.BF16, [700], [15], None),                           # 128 columns (4 blocks)
+    (48, 8, 128, wl.BF16, [1000, 2000], [8, 2], None),                  # 2 column blocks
+    (16, 2, 64, wl.F32, [333, 40], [3, 9], None),                       # fp32, ragged
+    (32, 8, 128, wl.BF16, [5], [4], 8192),                              # mostly empty splits
+])
+def test_edge_shapes(case):
+    hq, hkv, d, dtype, ctxs, drafts, mkv = case
+    _log(f"attention edge case {case}")
+    w = _custom(hq, hkv, d, dtype, ctxs, drafts)
+    if mkv is not None:
+        mkv = min(mkv, w.s_max)
+    got, err = attention_gpu(w, max_kv_len=mkv)
+    assert err == 0
+    assert_attention_close(got, attention_oracle(w))
+
+
+def _custom(hq, hkv, d, dtype, ctxs, drafts, seed=5):
+    rng = np.random.default_rng(seed)
+    batch = len(ctxs)
+    rows = np.array(drafts) + 1
+    cu = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
+    kv_len = np.array(ctxs) + rows
+    s_max = int(-(-int(kv_len.max() + 8) // 64) * 64)
+    s_max = max(s_max, 4096 + 64) if max(ctxs) < 400 else s_max
+    qf = rng.standard_normal((cu[-1], hq, d), dtype=np.float32)
+    kf = rng.standard_normal((batch, hkv, s_max, d), dtype=np.float32)
+    vf = rng.standard_normal((batch, hkv, s_max, d), dtype=np.float32)
+    for b in range(batch):
+        kf[b, :, kv_len[b]:] = np.nan
+        vf[b, :, kv_len[b]:] = np.nan
+    if dtype == wl.BF16:
+        q, k, v = wl.bf16_bits(qf), wl.bf16_bits(kf), wl.bf16_bits(vf)
+    else:
+        q, k, v = qf, kf, vf
+    z = np.zeros((cu[-1], 4), np.float32)
+    return wl.Workload(name="custom", batch=batch, num_q_heads=hq, num_kv_heads=hkv,
+                       head_dim=d, dtype=dtype, vocab=4, ctx_lens=np.array(ctxs, np.int32),
+                       cu_rows=cu, s_max=s_max, q=q, k_cache=k, v_cache=v, target_logits=z,
+                       draft_logits=z[:cu[-1] - batch], draft_tokens=np.zeros(cu[-1] - batch,
+                                                                             np.int32),
+                       token_counts=None, params=[wl.Params()] * batch,
+                       positions=np.array(ctxs, np.int32) + 1)
+
+
+def test_batch_invariance_and_workspace_reuse():
+    """Identical sequences give identical rows (row isolation), and a workspace reused by a
+    second call gives the same bits (counters were returned to zero)."""
+    w1 = _custom(32, 8, 128, wl.BF16, [3000], [4])
+    rep = _custom(32, 8, 128, wl.BF16, [3000], [4])
+    for f in ("q", "k_cache", "v_cache"):
+        setattr(rep, f, np.concatenate([getattr(w1, f)] * 3))
+    rep.batch = 3
+    rep.ctx_lens = np.array([3000] * 3, np.int32)
+    rep.cu_rows = np.array([0, 5, 10, 15], np.int32)
+    a, _ = attention_gpu(rep)
+    for b in range(1, 3):
+        assert np.array_equal(a[5 * b:5 * b + 5], a[0:5])
+    ws = torch.zeros(1 << 24, dtype=torch.uint8, device="cuda")
+    x, _ = attention_gpu(w1, workspace=ws)
+    y, _ = attention_gpu(w1, workspace=ws)
+    assert np.array_equal(x, y)
+    assert int(ws[256:512].view(torch.int32).abs().sum().item()) == 0
+
+
+def test_device_error_word_on_bad_context():
+    w = _custom(8, 2, 64, wl.BF16, [100], [2])
+    w.ctx_lens = np.array([w.s_max], np.int32)          # ctx + R beyond S_max: clamped
+    _, err = attention_gpu(w, max_kv_len=w.s_max)
+    assert err & 0x01

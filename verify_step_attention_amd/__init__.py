@@ -1,0 +1,171 @@
+"""MI355X (gfx950) library for the batched verify step of lossless speculative decoding.
+
+Python binding of the C ABI in include/vsa.h: argument marshalling only. Every step of the
+verify path runs in the HIP kernels of libvsa.so; torch is used for device memory and
+streams. Importing this package never loads the library; the first call does, and fails
+loudly if libvsa.so has not been built (`python -m verify_step_attention_amd.build`).
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libvsa.so")
+
+VSA_OK, VSA_ERR_INVALID_ARG, VSA_ERR_UNSUPPORTED, VSA_ERR_WORKSPACE, VSA_ERR_LAUNCH = range(5)
+VSA_F32, VSA_BF16 = 0, 1
+DEVERR_SEQ_SHAPE = 0x01
+DEVERR_DRAFT_ID = 0x02
+DEVERR_PARAMS = 0x04
+DEVERR_NO_DRAFT_LOGITS = 0x08
+DEVERR_TIE_OVERFLOW = 0x10
+
+# vsa_row_params, field for field
+ROW_PARAMS_DTYPE = np.dtype([("temperature", "<f4"), ("top_k", "<i4"), ("top_p", "<f4"),
+                             ("presence_penalty", "<f4"), ("frequency_penalty", "<f4"),
+                             ("logprobs", "<i4"), ("top_logprobs", "<i4")])
+
+EXPORTED_SYMBOLS = ("vsa_version", "vsa_status_string", "verify_attention_workspace_size",
+                    "verify_attention", "verify_sample_accept_workspace_size",
+                    "verify_sample_accept")
+
+
+class VsaError(RuntimeError):
+    def __init__(self, status, where):
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+        self.status = status
+
+
+_lib_handle = None
+
+
+def _lib():
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run "
+                               "`python -m verify_step_attention_amd.build` first")
+        lib = ctypes.CDLL(LIB_PATH)
+        c_int, c_size, c_void, c_float = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, \
+            ctypes.c_float
+        lib.vsa_version.restype = c_int
+        lib.vsa_status_string.restype = ctypes.c_char_p
+        lib.vsa_status_string.argtypes = [c_int]
+        lib.verify_attention_workspace_size.restype = c_size
+        lib.verify_attention_workspace_size.argtypes = [c_int] * 6
+        lib.verify_attention.restype = c_int
+        lib.verify_attention.argtypes = [c_void, c_void, c_void, c_int, c_void, c_void,
+                                         c_int, c_int, c_int, c_int, c_int, c_int, c_int,
+                                         c_int, c_float, c_void, c_void, c_size, c_void]
+        lib.verify_sample_accept_workspace_size.restype = c_size
+        lib.verify_sample_accept_workspace_size.argtypes = [c_int] * 6
+        lib.verify_sample_accept.restype = c_int
+        lib.verify_sample_accept.argtypes = [c_void, c_void, c_void, c_void, c_void, c_void,
+                                             c_void, ctypes.c_uint64, c_int, c_int, c_int,
+                                             c_int, c_int, c_int, c_void, c_void, c_void,
+                                             c_void, c_void, c_void, c_void, c_void, c_size,
+                                             c_void]
+        _lib_handle = lib
+    return _lib_handle
+
+
+def library():
+    """The loaded ctypes handle of libvsa.so."""
+    return _lib()
+
+
+def vsa_version():
+    return _lib().vsa_version()
+
+
+def status_string(status):
+    return _lib().vsa_status_string(int(status)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _check(status, where):
+    if status != VSA_OK:
+        raise VsaError(status, where)
+
+
+# ----------------------------------------------------------------------------- attention
+def verify_attention_workspace_size(B, Hq, Hkv, D, max_rows_per_seq, max_kv_len):
+    return int(_lib().verify_attention_workspace_size(B, Hq, Hkv, D, max_rows_per_seq,
+                                                      max_kv_len))
+
+
+def verify_attention(q, k_cache, v_cache, cu_rows, ctx_lens, out, workspace, *,
+                     max_rows_per_seq, max_kv_len, scale=0.0, stream=None):
+    """q [T, Hq, D], k_cache / v_cache [B, Hkv, S_max, D] (bf16 or float32 tensors on the
+    GPU), cu_rows [B+1] / ctx_lens [B] int32, out [T, Hq, D] float32, workspace uint8."""
+    import torch
+    total, hq, d = q.shape
+    batch, hkv, s_max, d2 = k_cache.shape
+    if d2 != d or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("q / k_cache / v_cache shapes disagree")
+    if q.dtype == torch.bfloat16:
+        dtype = VSA_BF16
+    elif q.dtype == torch.float32:
+        dtype = VSA_F32
+    else:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype or out.dtype != torch.float32:
+        raise ValueError("dtype mismatch")
+    for t in (q, k_cache, v_cache, cu_rows, ctx_lens, out, workspace):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    st = _lib().verify_attention(_ptr(q), _ptr(k_cache), _ptr(v_cache), dtype, _ptr(cu_rows),
+                                 _ptr(ctx_lens), batch, total, hq, hkv, d, s_max,
+                                 int(max_rows_per_seq), int(max_kv_len), float(scale),
+                                 _ptr(out), _ptr(workspace), workspace.numel(),
+                                 _stream(stream))
+    _check(st, "verify_attention")
+
+
+# ----------------------------------------------------------------------------- sampling
+def verify_sample_accept_workspace_size(B, total_rows, V, max_rows_per_seq, max_top_k,
+                                        max_top_logprobs):
+    return int(_lib().verify_sample_accept_workspace_size(B, total_rows, V, max_rows_per_seq,
+                                                          max_top_k, max_top_logprobs))
+
+
+def pack_row_params(params):
+    """List of objects with the vsa_row_params fields -> numpy structured array."""
+    arr = np.zeros(len(params), dtype=ROW_PARAMS_DTYPE)
+    for i, p in enumerate(params):
+        for name in ROW_PARAMS_DTYPE.names:
+            arr[i][name] = getattr(p, name)
+    return arr
+
+
+def verify_sample_accept(target_logits, draft_logits, draft_tokens, cu_rows, token_counts,
+                         params, positions, seed, accepted_len, out_tokens, workspace, *,
+                         max_rows_per_seq, max_top_k, max_top_logprobs, chosen_logprob=None,
+                         top_lp_vals=None, top_lp_ids=None, diag_threshold=None,
+                         diag_kept=None, stream=None):
+    """target_logits [T, V] float32, draft_logits [T-B, V] float32 or None, draft_tokens
+    [T-B] int32, cu_rows [B+1] int32, token_counts [B, V] int32 or None, params: a device
+    uint8 tensor holding B packed vsa_row_params (see pack_row_params), positions [B] int32;
+    outputs as in include/vsa.h."""
+    total, vocab = target_logits.shape
+    batch = cu_rows.numel() - 1
+    st = _lib().verify_sample_accept(
+        _ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(cu_rows),
+        _ptr(token_counts), _ptr(params), _ptr(positions),
+        ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF), batch, total, vocab,
+        int(max_rows_per_seq), int(max_top_k), int(max_top_logprobs), _ptr(accepted_len),
+        _ptr(out_tokens), _ptr(chosen_logprob), _ptr(top_lp_vals), _ptr(top_lp_ids),
+        _ptr(diag_threshold), _ptr(diag_kept), _ptr(workspace), workspace.numel(),
+        _stream(stream))
+    _check(st, "verify_sample_accept")

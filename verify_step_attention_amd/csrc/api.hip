@@ -1,0 +1,166 @@
+// C-ABI entry points: host-side validation, workspace layout and launches.
+#include <math.h>
+
+#include "vsa_internal.h"
+
+using namespace vsa;
+
+namespace {
+
+constexpr int kMaxRowsPerSeq = kMaxSeqRows;
+constexpr int kMaxTopK = kKeep;
+constexpr int kMaxTopLogprobs = 32;
+constexpr int kMaxVocab = 256 * kChunk;   // per-wave chunk tables hold 256 entries
+
+bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int vsa_version(void) { return 100; }
+
+const char* vsa_status_string(vsa_status status) {
+    switch (status) {
+        case VSA_OK: return "VSA_OK";
+        case VSA_ERR_INVALID_ARG: return "VSA_ERR_INVALID_ARG";
+        case VSA_ERR_UNSUPPORTED: return "VSA_ERR_UNSUPPORTED";
+        case VSA_ERR_WORKSPACE: return "VSA_ERR_WORKSPACE";
+        case VSA_ERR_LAUNCH: return "VSA_ERR_LAUNCH";
+    }
+    return "VSA_ERR_UNKNOWN";
+}
+
+size_t verify_attention_workspace_size(int B, int Hq, int Hkv, int D, int max_rows_per_seq,
+                                       int max_kv_len) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || (D != 64 && D != 128) ||
+        max_rows_per_seq < 1 || max_rows_per_seq > kMaxRowsPerSeq || max_kv_len < 1 ||
+        (Hq / Hkv) * max_rows_per_seq > 128)
+        return 0;
+    return plan_attention(B, Hq, Hkv, D, max_rows_per_seq, max_kv_len).bytes;
+}
+
+vsa_status verify_attention(const void* q, const void* k_cache, const void* v_cache,
+                            vsa_dtype dtype, const int32_t* cu_rows, const int32_t* ctx_lens,
+                            int B, int total_rows, int Hq, int Hkv, int D, int S_max,
+                            int max_rows_per_seq, int max_kv_len, float scale, float* out,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+    if (!q || !k_cache || !v_cache || !cu_rows || !ctx_lens || !out) return VSA_ERR_INVALID_ARG;
+    if (dtype != VSA_F32 && dtype != VSA_BF16) return VSA_ERR_INVALID_ARG;
+    if (B < 1 || total_rows < B || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || S_max < 1 ||
+        max_rows_per_seq < 1 || max_kv_len < 1 || max_kv_len > S_max ||
+        total_rows > B * max_rows_per_seq || !(scale >= 0.f) || !isfinite(scale))
+        return VSA_ERR_INVALID_ARG;
+    if ((D != 64 && D != 128) || max_rows_per_seq > kMaxRowsPerSeq ||
+        (Hq / Hkv) * max_rows_per_seq > 128)
+        return VSA_ERR_UNSUPPORTED;
+    const AttnPlan plan = plan_attention(B, Hq, Hkv, D, max_rows_per_seq, max_kv_len);
+    if (!workspace || !aligned256(workspace) || workspace_bytes < plan.bytes)
+        return VSA_ERR_WORKSPACE;
+
+    char* ws = static_cast<char*>(workspace);
+    AttnArgs a{};
+    a.q = q;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.cu_rows = cu_rows;
+    a.ctx_lens = ctx_lens;
+    a.out = out;
+    a.part_o = reinterpret_cast<float*>(ws + plan.off_o);
+    a.part_ml = reinterpret_cast<float2*>(ws + plan.off_ml);
+    a.counters = reinterpret_cast<uint32_t*>(ws + plan.off_counters);
+    a.err = reinterpret_cast<uint32_t*>(ws);
+    a.batch = B;
+    a.total_rows = total_rows;
+    a.hq = Hq;
+    a.hkv = Hkv;
+    a.group = Hq / Hkv;
+    a.d = D;
+    a.s_max = S_max;
+    a.max_rows = max_rows_per_seq;
+    a.max_kv_len = max_kv_len;
+    a.nsplit = plan.nsplit;
+    a.units = plan.units;
+    a.mcap = plan.mcap;
+    const float sc = scale == 0.f ? 1.f / sqrtf((float)D) : scale;
+    a.scale_log2 = sc * 1.4426950408889634f;
+    if (launch_attention(a, plan, dtype, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return VSA_ERR_LAUNCH;
+    return VSA_OK;
+}
+
+}  // extern "C"
+
+extern "C" {
+
+size_t verify_sample_accept_workspace_size(int B, int total_rows, int V, int max_rows_per_seq,
+                                           int max_top_k, int max_top_logprobs) {
+    if (B < 1 || total_rows < B || V < 1 || V > kMaxVocab || max_rows_per_seq < 1 ||
+        max_rows_per_seq > kMaxRowsPerSeq || total_rows > B * max_rows_per_seq ||
+        max_top_k < 0 || max_top_k > kMaxTopK || max_top_logprobs < 0 ||
+        max_top_logprobs > kMaxTopLogprobs)
+        return 0;
+    return plan_sample(B, total_rows, V, max_top_k, max_top_logprobs).bytes;
+}
+
+vsa_status verify_sample_accept(const float* target_logits, const float* draft_logits,
+                                const int32_t* draft_tokens, const int32_t* cu_rows,
+                                const int32_t* token_counts, const vsa_row_params* params,
+                                const int32_t* positions, uint64_t seed, int B, int total_rows,
+                                int V, int max_rows_per_seq, int max_top_k,
+                                int max_top_logprobs, int32_t* accepted_len,
+                                int32_t* out_tokens, float* chosen_logprob, float* top_lp_vals,
+                                int32_t* top_lp_ids, float* diag_threshold, int32_t* diag_kept,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    if (!target_logits || !cu_rows || !params || !positions || !accepted_len || !out_tokens)
+        return VSA_ERR_INVALID_ARG;
+    if (B < 1 || total_rows < B || V < 1 || max_rows_per_seq < 1 || max_top_k < 0 ||
+        max_top_logprobs < 0 || total_rows > B * max_rows_per_seq)
+        return VSA_ERR_INVALID_ARG;
+    if (total_rows > B && !draft_tokens) return VSA_ERR_INVALID_ARG;
+    if (V > kMaxVocab || max_rows_per_seq > kMaxRowsPerSeq || max_top_k > kMaxTopK ||
+        max_top_logprobs > kMaxTopLogprobs)
+        return VSA_ERR_UNSUPPORTED;
+    const SampPlan plan = plan_sample(B, total_rows, V, max_top_k, max_top_logprobs);
+    if (!workspace || !aligned256(workspace) || workspace_bytes < plan.bytes)
+        return VSA_ERR_WORKSPACE;
+    char* ws = static_cast<char*>(workspace);
+    SampArgs a{};
+    a.tl = target_logits;
+    a.dl = draft_logits;
+    a.drafts = draft_tokens;
+    a.cu_rows = cu_rows;
+    a.counts = token_counts;
+    a.params = params;
+    a.positions = positions;
+    a.seed = seed;
+    a.batch = B;
+    a.total_rows = total_rows;
+    a.vocab = V;
+    a.max_rows = max_rows_per_seq;
+    a.max_top_k = max_top_k;
+    a.max_top_lp = max_top_logprobs;
+    a.nchunk = plan.nchunk;
+    a.capc = plan.capc;
+    a.accepted = accepted_len;
+    a.out_tokens = out_tokens;
+    a.chosen_lp = chosen_logprob;
+    a.top_vals = top_lp_vals;
+    a.top_ids = top_lp_ids;
+    a.diag_thr = diag_threshold;
+    a.diag_kept = diag_kept;
+    a.err = reinterpret_cast<uint32_t*>(ws);
+    a.cnt_sweep = reinterpret_cast<uint32_t*>(ws + plan.off_cnt_sweep);
+    a.cnt_race = reinterpret_cast<uint32_t*>(ws + plan.off_cnt_race);
+    a.stats = reinterpret_cast<float4*>(ws + plan.off_stats);
+    a.cand = reinterpret_cast<uint2*>(ws + plan.off_cand);
+    a.cand_meta = reinterpret_cast<uint2*>(ws + plan.off_meta);
+    a.rows = reinterpret_cast<RowInfo*>(ws + plan.off_rows);
+    a.keep = reinterpret_cast<KeepEntry*>(ws + plan.off_keep);
+    a.race = reinterpret_cast<RaceReq*>(ws + plan.off_race);
+    a.race_part = reinterpret_cast<float4*>(ws + plan.off_race_part);
+    if (launch_sample(a, static_cast<hipStream_t>(stream)) != hipSuccess) return VSA_ERR_LAUNCH;
+    return VSA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,1101 @@
+// Vocabulary stage of the verify step (gfx950): presence/frequency penalties, temperature,
+// top-k threshold and nucleus cutoff, greedy or sampled acceptance, logprobs.
+//
+// Pages (mlx-dspark): penalties per verify position from base counts plus the position's
+// own draft prefix, and raw logprobs (Changelog [0.2.0] "Added"); top-k threshold and
+// nucleus cutoff from small grouped selections instead of full-vocabulary sorts, with the
+// same truncated distribution (Changelog [0.20.2] "Changed"); truncation of draft and
+// target (release v0.1.0); accept with probability min(1, p/q) and resample the residual
+// (release v0.0.2); greedy acceptance as the product of positionwise matches with one sync
+// per round (Changelog [0.2.0] "Decode-path performance").
+//
+// Kernels:
+//   sweep_kernel  grid (B x chunks of 2048 ids). One workgroup reads one chunk of every row
+//                 of one sequence with coalesced loads: the count histogram once, then each
+//                 target row (penalized z, and y = z / T when sampled), draft row and raw
+//                 row. Per (row, chunk) it writes max / sum-of-exp / argmax, and for
+//                 truncated rows the chunk's candidate set for the k-th-largest threshold
+//                 (radix select on order-preserving uint32 keys). The last workgroup of a
+//                 sequence to finish (arrival counter) merges the chunks, derives each
+//                 truncated row's threshold, kept set and nucleus (wave-level selection,
+//                 a small bitonic sort, an fp64 scan), and runs the acceptance loop.
+//   race_kernel   grid (B x chunks). For sampled rows without top-k, the final draw is an
+//                 exponential race over the whole vocabulary; the workgroups of the chunks
+//                 compute it in one more coalesced pass and the last one picks the winner.
+//                 Every other sequence returns at once.
+// Random numbers: Philox4x32-10 (Salmon et al., SC'11), keyed (seed), counter
+// (id >> 2, position, sequence, tag).
+#include <math.h>
+
+#include "vsa_internal.h"
+
+namespace vsa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kEpt = kChunk / kThreads;        // ids per thread per chunk (8)
+constexpr float kNegInf = -__builtin_inff();
+constexpr int kBigIdx = 0x7FFFFFFF;
+
+// ------------------------------------------------------------------ small device helpers
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const uint32_t lo0 = 0xD2511F53u * c.x, hi0 = __umulhi(0xD2511F53u, c.x);
+        const uint32_t lo1 = 0xCD9E8D57u * c.z, hi1 = __umulhi(0xCD9E8D57u, c.z);
+        c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+    }
+    return c;
+}
+
+__device__ __forceinline__ uint4 philox_block(uint64_t seed, uint32_t block, uint32_t pos,
+                                              uint32_t seq, uint32_t tag) {
+    return philox4x32_10(make_uint4(block, pos, seq, tag), (uint32_t)seed,
+                         (uint32_t)(seed >> 32));
+}
+
+__device__ __forceinline__ uint32_t pick(uint4 w, int i) {
+    return i == 0 ? w.x : i == 1 ? w.y : i == 2 ? w.z : w.w;
+}
+
+// U' = ((word >> 8) + 1) 2^-24 in (0, 1]
+__device__ __forceinline__ float race_u(uint32_t w) {
+    return (float)((w >> 8) + 1u) * 5.9604644775390625e-08f;
+}
+
+// order-preserving map float -> uint32 (larger float, larger key); -0 is folded into +0
+__device__ __forceinline__ uint32_t ord_key(float f) {
+    const uint32_t u = __float_as_uint(f + 0.0f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_float(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// z = (x - fp * c) - pp * [c > 0], each operation rounded once (no contraction)
+__device__ __forceinline__ float penalize(float x, int c, float pp, float fp) {
+    const float z = __fsub_rn(x, __fmul_rn(fp, (float)c));
+    return __fsub_rn(z, c > 0 ? pp : 0.f);
+}
+
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+    return v > bv || (v == bv && i < bi);
+}
+
+// (max, sum of exp(v - max)) pairs
+__device__ __forceinline__ void ms_merge(float& m, float& s, float m2, float s2) {
+    const float mn = fmaxf(m, m2);
+    if (mn == kNegInf) {
+        m = mn;
+        s = 0.f;
+        return;
+    }
+    s = s * expf(m - mn) + s2 * expf(m2 - mn);
+    m = mn;
+}
+
+// ------------------------------------------------------------------ per-sequence mode
+struct SeqMode {
+    int r0, rows, k, d0;
+    bool valid, sampled, topk, raw;
+    int ntop, topk_k, logprobs;
+    float temp, top_p, pp, fp;
+};
+
+__device__ SeqMode seq_mode(const SampArgs& a, int b, uint32_t* errbits) {
+    SeqMode m{};
+    m.r0 = a.cu_rows[b];
+    m.rows = a.cu_rows[b + 1] - m.r0;
+    m.k = m.rows - 1;
+    m.d0 = m.r0 - b;
+    m.valid = m.rows >= 1 && m.rows <= a.max_rows && m.r0 >= 0 &&
+              m.r0 + m.rows <= a.total_rows && m.d0 >= 0 &&
+              m.d0 + m.k <= a.total_rows - a.batch;
+    if (!m.valid) {
+        *errbits |= VSA_DEVERR_SEQ_SHAPE;
+        return m;
+    }
+    const vsa_row_params p = a.params[b];
+    const bool bad = !(p.temperature >= 0.f) || !isfinite(p.temperature) || p.top_k < 0 ||
+                     p.top_k > a.max_top_k || !(p.top_p > 0.f && p.top_p <= 1.f) ||
+                     p.top_logprobs < 0 || p.top_logprobs > a.max_top_lp ||
+                     (p.top_p < 1.f && p.top_k == 0 && p.temperature > 0.f);
+    if (bad) *errbits |= VSA_DEVERR_PARAMS;
+    m.temp = p.temperature;
+    m.sampled = !bad && p.temperature > 0.f;
+    if (m.sampled && m.k > 0 && a.dl == nullptr) {
+        *errbits |= VSA_DEVERR_NO_DRAFT_LOGITS;
+        m.sampled = false;
+    }
+    m.topk = m.sampled && p.top_k > 0 && p.top_k < a.vocab;
+    m.topk_k = p.top_k;
+    m.top_p = p.top_p;
+    m.pp = p.presence_penalty;
+    m.fp = p.frequency_penalty;
+    m.logprobs = bad ? 0 : p.logprobs;
+    m.ntop = bad ? 0 : p.top_logprobs;
+    m.raw = (m.logprobs != 0) || m.ntop > 0;
+    return m;
+}
+
+// Row q of a sequence's row list: target rows, then draft rows (sampled), then raw rows.
+struct RowRef {
+    int kind;   // 0 target, 1 draft, 2 raw
+    int i;      // target / raw: row 0..R-1; draft: t = 1..K
+    int slot;   // workspace slot
+};
+
+__device__ __forceinline__ int seq_nrows(const SeqMode& m) {
+    return m.rows + (m.sampled ? m.k : 0) + (m.raw ? m.rows : 0);
+}
+
+__device__ __forceinline__ RowRef row_ref(const SampArgs& a, const SeqMode& m, int q) {
+    RowRef r;
+    const int nd = m.sampled ? m.k : 0;
+    if (q < m.rows) {
+        r.kind = 0;
+        r.i = q;
+        r.slot = m.r0 + q;
+    } else if (q < m.rows + nd) {
+        r.kind = 1;
+        r.i = q - m.rows + 1;
+        r.slot = a.total_rows + m.d0 + r.i - 1;
+    } else {
+        r.kind = 2;
+        r.i = q - m.rows - nd;
+        r.slot = 2 * a.total_rows - a.batch + m.r0 + r.i;
+    }
+    return r;
+}
+
+__device__ __forceinline__ const float* row_ptr(const SampArgs& a, const SeqMode& m,
+                                                const RowRef& r) {
+    if (r.kind == 1) return a.dl + (size_t)(m.d0 + r.i - 1) * a.vocab;
+    return a.tl + (size_t)(m.r0 + r.i) * a.vocab;
+}
+
+// ------------------------------------------------------------------ workgroup radix select
+// The k-th largest key (1-based) among the valid keys of the workgroup, 8 bits at a time.
+// hist: LDS[256]; sh: LDS[>= 2].
+__device__ uint32_t wg_select_kth(const uint32_t (&key)[kEpt], uint32_t valid, int k,
+                                  uint32_t* hist, int* sh) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    uint32_t prefix = 0, mask = 0;
+    int need = k;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        hist[tid] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < kEpt; ++e)
+            if (((valid >> e) & 1u) && (key[e] & mask) == prefix)
+                atomicAdd(&hist[(key[e] >> shift) & 255u], 1u);
+        __syncthreads();
+        if (tid < 64) {
+            const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1];
+            const uint32_t h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+            const uint32_t sl = h0 + h1 + h2 + h3;
+            uint32_t incl = sl;
+            for (int off = 1; off < 64; off <<= 1) {
+                const uint32_t v = __shfl_down(incl, off);
+                if (lane + off < 64) incl += v;
+            }
+            const uint32_t above = incl - sl;
+            if (above < (uint32_t)need && (uint32_t)need <= incl) {
+                uint32_t cum = above;
+                int digit;
+                if (cum + h3 >= (uint32_t)need) digit = 4 * lane + 3;
+                else if ((cum += h3) + h2 >= (uint32_t)need) digit = 4 * lane + 2;
+                else if ((cum += h2) + h1 >= (uint32_t)need) digit = 4 * lane + 1;
+                else { cum += h1; digit = 4 * lane; }
+                sh[0] = digit;
+                sh[1] = need - (int)cum;
+            }
+        }
+        __syncthreads();
+        prefix |= (uint32_t)sh[0] << shift;
+        mask |= 0xFFu << shift;
+        need = sh[1];
+        __syncthreads();
+    }
+    return prefix;
+}
+
+// ------------------------------------------------------------------ wave-level pieces
+// The k-th largest candidate key of one row (candidates of every chunk, `ccount` valid
+// entries each, counts in LDS). hist: per-wave LDS[256].
+__device__ uint32_t wave_select_kth(const uint2* cand, const int* ccount, int nchunk, int capc,
+                                    int k, uint32_t* hist) {
+    const int lane = threadIdx.x & 63;
+    uint32_t prefix = 0, mask = 0;
+    int need = k;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        for (int i = lane; i < 256; i += 64) hist[i] = 0;
+        wave_sync();
+        for (int c = 0; c < nchunk; ++c) {
+            const uint2* cc = cand + (size_t)c * capc;
+            const int n = ccount[c];
+            for (int i = lane; i < n; i += 64) {
+                const uint32_t key = cc[i].x;
+                if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+            }
+        }
+        wave_sync();
+        const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1];
+        const uint32_t h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+        const uint32_t sl = h0 + h1 + h2 + h3;
+        uint32_t incl = sl;
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t v = __shfl_down(incl, off);
+            if (lane + off < 64) incl += v;
+        }
+        const uint32_t above = incl - sl;
+        int digit = -1, nneed = 0;
+        if (above < (uint32_t)need && (uint32_t)need <= incl) {
+            uint32_t cum = above;
+            if (cum + h3 >= (uint32_t)need) digit = 4 * lane + 3;
+            else if ((cum += h3) + h2 >= (uint32_t)need) digit = 4 * lane + 2;
+            else if ((cum += h2) + h1 >= (uint32_t)need) digit = 4 * lane + 1;
+            else { cum += h1; digit = 4 * lane; }
+            nneed = need - (int)cum;
+        }
+        const uint64_t found = __ballot(digit >= 0);
+        const int src = __ffsll((unsigned long long)found) - 1;
+        digit = __shfl(digit, src);
+        nneed = __shfl(nneed, src);
+        prefix |= (uint32_t)digit << shift;
+        mask |= 0xFFu << shift;
+        need = nneed;
+        wave_sync();
+    }
+    return prefix;
+}
+
+// Collects the candidates with key >= theta into a per-wave list (at most kKeep kept);
+// returns how many there are in total.
+__device__ int wave_collect(const uint2* cand, const int* ccount, int nchunk, int capc,
+                            uint32_t theta, uint32_t* lkey, int* lidx) {
+    const int lane = threadIdx.x & 63;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int n_s = 0;
+    for (int c = 0; c < nchunk; ++c) {
+        const uint2* cc = cand + (size_t)c * capc;
+        const int n = ccount[c];
+        for (int i0 = 0; i0 < n; i0 += 64) {
+            const int i = i0 + lane;
+            uint2 e = make_uint2(0, 0);
+            bool take = false;
+            if (i < n) {
+                e = cc[i];
+                take = e.x >= theta;
+            }
+            const uint64_t m = __ballot(take);
+            const int pos = n_s + __popcll(m & below);
+            if (take && pos < kKeep) {
+                lkey[pos] = e.x;
+                lidx[pos] = (int)e.y;
+            }
+            n_s += __popcll(m);
+        }
+    }
+    wave_sync();
+    return n_s;
+}
+
+// Bitonic sort of n <= kKeep (key, id) pairs: key descending, id ascending.
+__device__ void wave_sort(uint32_t* lkey, int* lidx, int n) {
+    const int lane = threadIdx.x & 63;
+    int np = 1;
+    while (np < n) np <<= 1;
+    for (int i = n + lane; i < np; i += 64) {
+        lkey[i] = 0u;
+        lidx[i] = kBigIdx;
+    }
+    wave_sync();
+    for (int size = 2; size <= np; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = lane; i < np / 2; i += 64) {
+                const int lo = 2 * i - (i & (stride - 1));
+                const int hi = lo + stride;
+                const bool desc = (lo & size) == 0;
+                const uint32_t ka = lkey[lo], kb = lkey[hi];
+                const int ia = lidx[lo], ib = lidx[hi];
+                const bool b_first = kb > ka || (kb == ka && ib < ia);
+                const bool a_first = ka > kb || (ka == kb && ia < ib);
+                if (desc ? b_first : a_first) {
+                    lkey[lo] = kb;
+                    lkey[hi] = ka;
+                    lidx[lo] = ib;
+                    lidx[hi] = ia;
+                }
+            }
+            wave_sync();
+        }
+    }
+}
+
+__device__ __forceinline__ double wave_sum_d(double v) {
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+__device__ __forceinline__ int wave_min_i(int v) {
+    for (int off = 32; off >= 1; off >>= 1) v = min(v, __shfl_xor(v, off));
+    return v;
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
+// ------------------------------------------------------------------ chunk loads
+template <bool VEC>
+__device__ __forceinline__ void load_chunk(const float* row, int base, int vocab,
+                                           float (&x)[kEpt]) {
+    const int tid = threadIdx.x;
+    if (VEC) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int j = base + 1024 * q + 4 * tid;
+            float4 v = make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
+            if (j < vocab) v = *reinterpret_cast<const float4*>(row + j);
+            x[4 * q] = v.x;
+            x[4 * q + 1] = v.y;
+            x[4 * q + 2] = v.z;
+            x[4 * q + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < kEpt; ++e) {
+            const int j = base + 1024 * (e >> 2) + 4 * tid + (e & 3);
+            x[e] = j < vocab ? row[j] : kNegInf;
+        }
+    }
+}
+
+template <bool VEC>
+__device__ __forceinline__ void load_counts(const int32_t* row, int base, int vocab,
+                                            int (&c)[kEpt]) {
+    const int tid = threadIdx.x;
+    if (row == nullptr) {
+#pragma unroll
+        for (int e = 0; e < kEpt; ++e) c[e] = 0;
+        return;
+    }
+    if (VEC) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int j = base + 1024 * q + 4 * tid;
+            int4 v = make_int4(0, 0, 0, 0);
+            if (j < vocab) v = *reinterpret_cast<const int4*>(row + j);
+            c[4 * q] = v.x;
+            c[4 * q + 1] = v.y;
+            c[4 * q + 2] = v.z;
+            c[4 * q + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < kEpt; ++e) {
+            const int j = base + 1024 * (e >> 2) + 4 * tid + (e & 3);
+            c[e] = j < vocab ? row[j] : 0;
+        }
+    }
+}
+
+__device__ __forceinline__ int elem_id(int base, int e) {
+    return base + 1024 * (e >> 2) + 4 * (int)threadIdx.x + (e & 3);
+}
+
+// Bits of this thread's ids that equal one of the first `k` drafts.
+__device__ __forceinline__ uint32_t special_mask(const int* s_draft, int k, int base) {
+    uint32_t mask = 0;
+    for (int t = 0; t < k; ++t) {
+        const int off = s_draft[t] - base;
+        if (off >= 0 && off < kChunk && ((off & 1023) >> 2) == (int)threadIdx.x)
+            mask |= 1u << ((off >> 10) * 4 + (off & 3));
+    }
+    return mask;
+}
+
+// Penalty count of id j at target row i: base count plus drafts d_1..d_i equal to j.
+__device__ __forceinline__ int row_count(int base_count, bool special, const int* s_draft, int i,
+                                         int j) {
+    int c = base_count;
+    if (special)
+        for (int t = 0; t < i; ++t) c += (s_draft[t] == j) ? 1 : 0;
+    return c;
+}
+
+// ------------------------------------------------------------------ finalize helpers
+// Probability of id d under row `slot`'s truncated distribution (its kept list).
+__device__ double keep_lookup(const SampArgs& a, int kslot, int n, int d) {
+    const int lane = threadIdx.x & 63;
+    const KeepEntry* k = a.keep + (size_t)kslot * kKeep;
+    double p = 0.0;
+    for (int i = lane; i < n; i += 64)
+        if (k[i].idx == d) p = k[i].p;
+    return wave_sum_d(p);
+}
+
+// Exponential race over a kept list: weights max(0, p - q) (q from another kept list, or
+// none) with a fallback to p if every weight is 0. fp64, ties to the lowest id.
+__device__ int keep_race(const SampArgs& a, int pslot, int np, int qslot, int nq, int b,
+                         int pos) {
+    const int lane = threadIdx.x & 63;
+    const KeepEntry* kp = a.keep + (size_t)pslot * kKeep;
+    const KeepEntry* kq = qslot >= 0 ? a.keep + (size_t)qslot * kKeep : nullptr;
+    double best = -1.0, fbest = -1.0;
+    int bi = kBigIdx, fbi = kBigIdx;
+    for (int i = lane; i < np; i += 64) {
+        const int j = kp[i].idx;
+        const double p = kp[i].p;
+        double q = 0.0;
+        if (kq)
+            for (int t = 0; t < nq; ++t)
+                if (kq[t].idx == j) q = kq[t].p;
+        const double r = kq ? fmax(0.0, p - q) : p;
+        const uint4 w = philox_block(a.seed, (uint32_t)j >> 2, (uint32_t)pos, (uint32_t)b, 1u);
+        const double e = -log((double)race_u(pick(w, j & 3)));
+        if (r > 0.0) {
+            const double key = r / e;
+            if (key > best || (key == best && j < bi)) { best = key; bi = j; }
+        }
+        if (p > 0.0) {
+            const double key = p / e;
+            if (key > fbest || (key == fbest && j < fbi)) { fbest = key; fbi = j; }
+        }
+    }
+    for (int off = 32; off >= 1; off >>= 1) {
+        const double ob = __shfl_xor(best, off);
+        const int oi = __shfl_xor(bi, off);
+        if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
+        const double fb = __shfl_xor(fbest, off);
+        const int fi = __shfl_xor(fbi, off);
+        if (fb > fbest || (fb == fbest && fi < fbi)) { fbest = fb; fbi = fi; }
+    }
+    return best > 0.0 ? bi : fbi;
+}
+
+// ------------------------------------------------------------------ finalize
+struct FinalShared {
+    uint32_t hist[4][256];
+    uint32_t lkey[4][kKeep];
+    int lidx[4][kKeep];
+    double lp[4][kKeep];
+    int ccount[4][256];
+    int drafts[kMaxSeqRows];
+};
+
+__device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, FinalShared& fs,
+                                  RowInfo* rinfo /* LDS, one per row of the list */) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nrows = seq_nrows(m);
+    uint32_t ebits = 0;
+
+    // ---- A: merge the chunk statistics of every row (one wave per row)
+    for (int q = wave; q < nrows; q += 4) {
+        const RowRef r = row_ref(a, m, q);
+        const bool greedy_row = r.kind == 0 && !m.sampled;
+        float bm = kNegInf, bs = 0.f;
+        float bv = kNegInf;
+        int bi = kBigIdx;
+        for (int c = lane; c < a.nchunk; c += 64) {
+            const float4 st = a.stats[(size_t)r.slot * a.nchunk + c];
+            if (greedy_row) {
+                const int ci = __float_as_int(st.w);
+                if (better(st.z, ci, bv, bi)) { bv = st.z; bi = ci; }
+            } else {
+                bm = fmaxf(bm, st.x);
+            }
+        }
+        for (int off = 32; off >= 1; off >>= 1) {
+            bm = fmaxf(bm, __shfl_xor(bm, off));
+            const float ov = __shfl_xor(bv, off);
+            const int oi = __shfl_xor(bi, off);
+            if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+        }
+        double z = 0.0;
+        if (!greedy_row && bm != kNegInf) {
+            for (int c = lane; c < a.nchunk; c += 64) {
+                const float4 st = a.stats[(size_t)r.slot * a.nchunk + c];
+                if (st.x != kNegInf) z += (double)st.y * exp((double)st.x - (double)bm);
+            }
+            z = wave_sum_d(z);
+        }
+        if (lane == 0) {
+            RowInfo ri{};
+            ri.m = bm;
+            ri.z = z;
+            ri.argmax = bi;
+            ri.theta = kNegInf;
+            ri.kept_k = a.vocab;
+            ri.kept_p = a.vocab;
+            rinfo[q] = ri;
+        }
+        (void)bs;
+    }
+    __syncthreads();
+
+    // ---- B: truncated rows (top-k threshold, kept set, nucleus) and raw top-n rows
+    for (int q = wave; q < nrows; q += 4) {
+        const RowRef r = row_ref(a, m, q);
+        const bool trunc = m.topk && r.kind != 2;
+        const bool topn = r.kind == 2 && m.ntop > 0;
+        if (!trunc && !topn) continue;
+        const int kk = trunc ? m.topk_k : m.ntop;
+        int* ccount = fs.ccount[wave];
+        bool overflow_risk = false;
+        for (int c = lane; c < a.nchunk; c += 64) {
+            const uint2 meta = a.cand_meta[(size_t)r.slot * a.nchunk + c];
+            ccount[c] = min((int)meta.x, a.capc);
+        }
+        wave_sync();
+        const uint2* cand = a.cand + (size_t)r.slot * a.nchunk * a.capc;
+        int total = 0;
+        for (int c = lane; c < a.nchunk; c += 64) total += ccount[c];
+        total = wave_sum_i(total);
+        const int ksel = min(kk, total);
+        if (ksel < 1) continue;
+        const uint32_t theta = wave_select_kth(cand, ccount, a.nchunk, a.capc, ksel, fs.hist[wave]);
+        for (int c = lane; c < a.nchunk; c += 64) {
+            const uint2 meta = a.cand_meta[(size_t)r.slot * a.nchunk + c];
+            if ((int)meta.x > a.capc && meta.y == theta) overflow_risk = true;
+        }
+        const int n_all = wave_collect(cand, ccount, a.nchunk, a.capc, theta, fs.lkey[wave],
+                                       fs.lidx[wave]);
+        if ((__ballot(overflow_risk) || n_all > kKeep) && lane == 0)
+            atomicOr(a.err, VSA_DEVERR_TIE_OVERFLOW);
+        const int n = min(n_all, kKeep);
+        wave_sort(fs.lkey[wave], fs.lidx[wave], n);
+        if (topn) {
+            // raw top-n ids with their log-softmax values
+            const RowInfo ri = rinfo[q];
+            const int grow = m.r0 + r.i;
+            const double lz = log(ri.z);
+            for (int i = lane; i < a.max_top_lp; i += 64) {
+                const bool has = i < m.ntop && i < n;
+                if (a.top_ids) a.top_ids[(size_t)grow * a.max_top_lp + i] = has ? fs.lidx[wave][i] : -1;
+                if (a.top_vals)
+                    a.top_vals[(size_t)grow * a.max_top_lp + i] =
+                        has ? (float)((double)key_float(fs.lkey[wave][i]) - (double)ri.m - lz)
+                            : 0.f;
+            }
+            continue;
+        }
+        // probabilities over the kept set, fp64, in sorted order
+        const double ymax = (double)__fdiv_rn(key_float(fs.lkey[wave][0]), m.temp);
+        double part = 0.0;
+        for (int i = lane; i < n; i += 64) {
+            const double y = (double)__fdiv_rn(key_float(fs.lkey[wave][i]), m.temp);
+            const double w = exp(y - ymax);
+            fs.lp[wave][i] = w;
+            part += w;
+        }
+        const double zs = wave_sum_d(part);
+        wave_sync();
+        for (int i = lane; i < n; i += 64) fs.lp[wave][i] /= zs;
+        wave_sync();
+        int n_keep = n;
+        if (m.top_p < 1.f) {
+            // inclusive scan in sorted order: lane owns a contiguous run
+            const int per = (n + 63) / 64;
+            const int i0 = min(lane * per, n), i1 = min(i0 + per, n);
+            double run = 0.0;
+            for (int i = i0; i < i1; ++i) run += fs.lp[wave][i];
+            double excl = run;
+            for (int off = 1; off < 64; off <<= 1) {
+                const double v = __shfl_up(excl, off);
+                if (lane >= off) excl += v;
+            }
+            excl -= run;
+            int first = kBigIdx;
+            double cum = excl;
+            for (int i = i0; i < i1; ++i) {
+                cum += fs.lp[wave][i];
+                if (cum >= (double)m.top_p && first == kBigIdx) first = i;
+            }
+            int mstar = wave_min_i(first);
+            if (mstar == kBigIdx) mstar = n - 1;
+            const double cutoff = fs.lp[wave][mstar];
+            int cnt = 0;
+            for (int i = lane; i < n; i += 64) cnt += fs.lp[wave][i] >= cutoff ? 1 : 0;
+            n_keep = wave_sum_i(cnt);
+            double ks = 0.0;
+            for (int i = lane; i < n_keep; i += 64) ks += fs.lp[wave][i];
+            ks = wave_sum_d(ks);
+            wave_sync();
+            for (int i = lane; i < n_keep; i += 64) fs.lp[wave][i] /= ks;
+            wave_sync();
+        }
+        KeepEntry* keep = a.keep + (size_t)r.slot * kKeep;
+        for (int i = lane; i < n_keep; i += 64) {
+            KeepEntry e;
+            e.idx = fs.lidx[wave][i];
+            e.pad = 0;
+            e.p = fs.lp[wave][i];
+            keep[i] = e;
+        }
+        if (lane == 0) {
+            rinfo[q].theta = key_float(theta);
+            rinfo[q].kept_k = n_all;
+            rinfo[q].kept_p = n_keep;
+        }
+        wave_sync();
+    }
+    if (tid < m.k) fs.drafts[tid] = a.drafts[m.d0 + tid];
+    __threadfence();
+    __syncthreads();
+
+    // ---- C: acceptance (wave 0)
+    if (wave == 0) {
+        int acc = 0;
+        int tok = -1;
+        bool pending = false;
+        RaceReq rq{};
+        if (!m.sampled) {
+            while (acc < m.k) {
+                const int d = fs.drafts[acc];
+                if (d < 0 || d >= a.vocab) ebits |= VSA_DEVERR_DRAFT_ID;
+                if (d != rinfo[acc].argmax) break;
+                ++acc;
+            }
+            tok = rinfo[acc].argmax;
+        } else {
+            const int nd = m.k;
+            const int base_pos = a.positions[b];
+            bool all = true;
+            for (int t = 1; t <= m.k; ++t) {
+                const int pos = base_pos + t - 1;
+                const int d = fs.drafts[t - 1];
+                const bool valid = d >= 0 && d < a.vocab;
+                if (!valid) ebits |= VSA_DEVERR_DRAFT_ID;
+                double pd = 0.0, qd = 0.0;
+                const int pq = t - 1;            // target row t-1 in the row list
+                const int qq = m.rows + t - 1;   // draft row t
+                const RowRef rp = row_ref(a, m, pq), rqr = row_ref(a, m, qq);
+                if (valid) {
+                    if (m.topk) {
+                        pd = keep_lookup(a, rp.slot, rinfo[pq].kept_p, d);
+                        qd = keep_lookup(a, rqr.slot, rinfo[qq].kept_p, d);
+                    } else {
+                        int c = a.counts ? a.counts[(size_t)b * a.vocab + d] : 0;
+                        for (int s = 0; s < t - 1; ++s) c += fs.drafts[s] == d ? 1 : 0;
+                        const float z = penalize(a.tl[(size_t)(m.r0 + t - 1) * a.vocab + d], c,
+                                                 m.pp, m.fp);
+                        const double y = (double)__fdiv_rn(z, m.temp);
+                        pd = exp(y - (double)rinfo[pq].m) / rinfo[pq].z;
+                        const double w =
+                            (double)__fdiv_rn(a.dl[(size_t)(m.d0 + t - 1) * a.vocab + d], m.temp);
+                        qd = exp(w - (double)rinfo[qq].m) / rinfo[qq].z;
+                    }
+                }
+                const uint4 wu = philox_block(a.seed, 0u, (uint32_t)pos, (uint32_t)b, 0u);
+                const double u = (double)(wu.x >> 8) * 5.9604644775390625e-08;
+                if (u * qd < pd) { ++acc; continue; }
+                all = false;
+                if (m.topk) {
+                    tok = keep_race(a, rp.slot, rinfo[pq].kept_p, rqr.slot, rinfo[qq].kept_p, b, pos);
+                } else {
+                    pending = true;
+                    rq.kind = 1;
+                    rq.a = acc;
+                    rq.pos = pos;
+                    rq.m_p = rinfo[pq].m;
+                    rq.z_p = rinfo[pq].z;
+                    rq.m_q = rinfo[qq].m;
+                    rq.z_q = rinfo[qq].z;
+                }
+                break;
+            }
+            (void)nd;
+            if (all) {
+                const int pos = base_pos + m.k;
+                const RowRef rp = row_ref(a, m, m.k);
+                if (m.topk) {
+                    tok = keep_race(a, rp.slot, rinfo[m.k].kept_p, -1, 0, b, pos);
+                } else {
+                    pending = true;
+                    rq.kind = 2;
+                    rq.a = acc;
+                    rq.pos = pos;
+                    rq.m_p = rinfo[m.k].m;
+                    rq.z_p = rinfo[m.k].z;
+                }
+            }
+        }
+        // raw statistics of the row whose token the race kernel will pick
+        if (pending) {
+            rq.logprobs = m.logprobs;
+            if (m.raw) {
+                const int xq = m.rows + (m.sampled ? m.k : 0) + acc;
+                rq.m_x = rinfo[xq].m;
+                rq.z_x = rinfo[xq].z;
+            }
+        }
+        if (lane == 0) {
+            a.race[b] = rq;
+            a.accepted[b] = acc;
+        }
+        // emitted tokens, logprobs, diagnostics
+        for (int s = lane; s < m.rows; s += 64) {
+            const int grow = m.r0 + s;
+            int out = -1;
+            if (s < acc) out = fs.drafts[s];
+            else if (s == acc) out = pending ? -1 : tok;
+            a.out_tokens[grow] = out;
+            if (a.chosen_lp) {
+                float lpv = __builtin_nanf("");
+                if (m.logprobs && out >= 0) {
+                    const int xq = m.rows + (m.sampled ? m.k : 0) + s;
+                    lpv = (float)((double)a.tl[(size_t)grow * a.vocab + out] -
+                                  (double)rinfo[xq].m - log(rinfo[xq].z));
+                }
+                a.chosen_lp[grow] = lpv;
+            }
+            if (a.diag_thr) a.diag_thr[grow] = m.sampled ? rinfo[s].theta : __builtin_nanf("");
+            if (a.diag_kept) {
+                a.diag_kept[2 * grow] = m.sampled ? rinfo[s].kept_k : 0;
+                a.diag_kept[2 * grow + 1] = m.sampled ? rinfo[s].kept_p : 0;
+            }
+            if (m.ntop == 0 && a.max_top_lp > 0) {
+                for (int i = 0; i < a.max_top_lp; ++i) {
+                    if (a.top_ids) a.top_ids[(size_t)grow * a.max_top_lp + i] = -1;
+                    if (a.top_vals) a.top_vals[(size_t)grow * a.max_top_lp + i] = 0.f;
+                }
+            }
+        }
+        if (ebits && lane == 0) atomicOr(a.err, ebits);
+    }
+    if (tid == 0) atomicExch(a.cnt_sweep + b, 0u);
+}
+
+// ------------------------------------------------------------------ sweep kernel
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
+    __shared__ float4 s_part[3 * kMaxSeqRows][4];
+    __shared__ int s_draft[kMaxSeqRows];
+    __shared__ uint32_t s_hist[256];
+    __shared__ int s_sh[4];
+    __shared__ int s_last;
+    __shared__ FinalShared s_final;
+    __shared__ RowInfo s_rinfo[3 * kMaxSeqRows];
+
+    const int b = blockIdx.x / a.nchunk, c = blockIdx.x % a.nchunk;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint32_t ebits = 0;
+    const SeqMode m = seq_mode(a, b, &ebits);
+    if (c == 0 && tid == 0 && ebits) atomicOr(a.err, ebits);
+    if (!m.valid) return;
+    if (tid < m.k) s_draft[tid] = a.drafts[m.d0 + tid];
+    __syncthreads();
+
+    const int base = c * kChunk;
+    const uint32_t special = special_mask(s_draft, m.k, base);
+    int cnt[kEpt];
+    load_counts<VEC>(a.counts ? a.counts + (size_t)b * a.vocab : nullptr, base, a.vocab, cnt);
+    uint32_t valid = 0;
+#pragma unroll
+    for (int e = 0; e < kEpt; ++e) valid |= (elem_id(base, e) < a.vocab ? 1u : 0u) << e;
+
+    const int nrows = seq_nrows(m);
+    // ---- per-row statistics of this chunk
+    for (int q = 0; q < nrows; ++q) {
+        const RowRef r = row_ref(a, m, q);
+        float x[kEpt];
+        load_chunk<VEC>(row_ptr(a, m, r), base, a.vocab, x);
+        const bool greedy_row = r.kind == 0 && !m.sampled;
+        float v[kEpt];
+#pragma unroll
+        for (int e = 0; e < kEpt; ++e) {
+            float val = x[e];
+            if (r.kind == 0) {
+                const int cc = row_count(cnt[e], (special >> e) & 1u, s_draft, r.i, elem_id(base, e));
+                val = penalize(val, cc, m.pp, m.fp);
+                if (m.sampled) val = __fdiv_rn(val, m.temp);
+            } else if (r.kind == 1) {
+                val = __fdiv_rn(val, m.temp);
+            }
+            v[e] = ((valid >> e) & 1u) ? val : kNegInf;
+        }
+        float4 res;
+        if (greedy_row) {
+            float bv = kNegInf;
+            int bi = kBigIdx;
+#pragma unroll
+            for (int e = 0; e < kEpt; ++e)
+                if (((valid >> e) & 1u) && better(v[e], elem_id(base, e), bv, bi)) {
+                    bv = v[e];
+                    bi = elem_id(base, e);
+                }
+            for (int off = 32; off >= 1; off >>= 1) {
+                const float ov = __shfl_xor(bv, off);
+                const int oi = __shfl_xor(bi, off);
+                if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+            }
+            res = make_float4(0.f, 0.f, bv, __int_as_float(bi));
+        } else {
+            float mx = kNegInf;
+#pragma unroll
+            for (int e = 0; e < kEpt; ++e) mx = fmaxf(mx, v[e]);
+            float s = 0.f;
+            if (mx != kNegInf) {
+#pragma unroll
+                for (int e = 0; e < kEpt; ++e) s += (v[e] == kNegInf) ? 0.f : expf(v[e] - mx);
+            }
+            for (int off = 32; off >= 1; off >>= 1) {
+                const float om = __shfl_xor(mx, off), os = __shfl_xor(s, off);
+                ms_merge(mx, s, om, os);
+            }
+            res = make_float4(mx, s, 0.f, 0.f);
+        }
+        if (lane == 0) s_part[q][wave] = res;
+    }
+    __syncthreads();
+    for (int q = tid; q < nrows; q += kThreads) {
+        const RowRef r = row_ref(a, m, q);
+        const bool greedy_row = r.kind == 0 && !m.sampled;
+        float4 acc = s_part[q][0];
+        for (int w = 1; w < 4; ++w) {
+            const float4 o = s_part[q][w];
+            if (greedy_row) {
+                if (better(o.z, __float_as_int(o.w), acc.z, __float_as_int(acc.w))) {
+                    acc.z = o.z;
+                    acc.w = o.w;
+                }
+            } else {
+                ms_merge(acc.x, acc.y, o.x, o.y);
+            }
+        }
+        a.stats[(size_t)r.slot * a.nchunk + c] = acc;
+    }
+
+    // ---- candidates for the k-th-largest threshold of truncated / top-n rows
+    if (m.topk || m.ntop > 0) {
+        for (int q = 0; q < nrows; ++q) {
+            const RowRef r = row_ref(a, m, q);
+            const bool trunc = m.topk && r.kind != 2;
+            const bool topn = r.kind == 2 && m.ntop > 0;
+            if (!trunc && !topn) continue;
+            const int kk = trunc ? m.topk_k : m.ntop;
+            float x[kEpt];
+            load_chunk<VEC>(row_ptr(a, m, r), base, a.vocab, x);
+            uint32_t key[kEpt];
+#pragma unroll
+            for (int e = 0; e < kEpt; ++e) {
+                float val = x[e];
+                if (r.kind == 0)
+                    val = penalize(val, row_count(cnt[e], (special >> e) & 1u, s_draft, r.i,
+                                                  elem_id(base, e)), m.pp, m.fp);
+                key[e] = ord_key(val);
+            }
+            const int n_valid = min(kChunk, a.vocab - base);
+            uint32_t vk = 0u;
+            if (n_valid > kk) vk = wg_select_kth(key, valid, kk, s_hist, s_sh);
+            if (tid == 0) s_sh[2] = 0;
+            __syncthreads();
+            uint2* out = a.cand + ((size_t)r.slot * a.nchunk + c) * a.capc;
+#pragma unroll
+            for (int e = 0; e < kEpt; ++e)
+                if (((valid >> e) & 1u) && key[e] > vk) {
+                    const int pos = atomicAdd(&s_sh[2], 1);
+                    out[pos] = make_uint2(key[e], (uint32_t)elem_id(base, e));
+                }
+            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < kEpt; ++e)
+                if (((valid >> e) & 1u) && key[e] == vk) {
+                    const int pos = atomicAdd(&s_sh[2], 1);
+                    if (pos < a.capc) out[pos] = make_uint2(key[e], (uint32_t)elem_id(base, e));
+                }
+            __syncthreads();
+            if (tid == 0)
+                a.cand_meta[(size_t)r.slot * a.nchunk + c] = make_uint2((uint32_t)s_sh[2], vk);
+            __syncthreads();
+        }
+    }
+
+    // ---- the last chunk of the sequence to finish merges and accepts
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) s_last = atomicAdd(a.cnt_sweep + b, 1u) == (uint32_t)(a.nchunk - 1);
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    finalize_sequence(a, m, b, s_final, s_rinfo);
+}
+
+// ------------------------------------------------------------------ race kernel
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void race_kernel(const SampArgs a) {
+    __shared__ int s_draft[kMaxSeqRows];
+    __shared__ float4 s_part[4];
+    __shared__ int s_last;
+    const int b = blockIdx.x / a.nchunk, c = blockIdx.x % a.nchunk;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint32_t ebits = 0;
+    const SeqMode m = seq_mode(a, b, &ebits);
+    if (!m.valid || !m.sampled || m.topk) return;
+    const RaceReq rq = a.race[b];
+    if (rq.kind == 0) return;
+    if (tid < rq.a) s_draft[tid] = a.drafts[m.d0 + tid];
+    __syncthreads();
+
+    const int base = c * kChunk;
+    const uint32_t special = special_mask(s_draft, rq.a, base);
+    int cnt[kEpt];
+    load_counts<VEC>(a.counts ? a.counts + (size_t)b * a.vocab : nullptr, base, a.vocab, cnt);
+    float xp[kEpt], xq[kEpt];
+    load_chunk<VEC>(a.tl + (size_t)(m.r0 + rq.a) * a.vocab, base, a.vocab, xp);
+    if (rq.kind == 1) load_chunk<VEC>(a.dl + (size_t)(m.d0 + rq.a) * a.vocab, base, a.vocab, xq);
+    const float inv_zp = (float)(1.0 / rq.z_p);
+    const float inv_zq = rq.kind == 1 ? (float)(1.0 / rq.z_q) : 0.f;
+
+    float best = -1.f, fbest = -1.f;
+    int bi = kBigIdx, fbi = kBigIdx;
+#pragma unroll
+    for (int qd = 0; qd < 2; ++qd) {
+        const int j0 = base + 1024 * qd + 4 * tid;
+        if (j0 >= a.vocab) continue;
+        const uint4 w = philox_block(a.seed, (uint32_t)j0 >> 2, (uint32_t)rq.pos, (uint32_t)b, 1u);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int e = 4 * qd + r;
+            const int j = j0 + r;
+            if (j >= a.vocab) continue;
+            const int cc = row_count(cnt[e], (special >> e) & 1u, s_draft, rq.a, j);
+            const float y = __fdiv_rn(penalize(xp[e], cc, m.pp, m.fp), m.temp);
+            const float p = expf(y - rq.m_p) * inv_zp;
+            float rr = p;
+            if (rq.kind == 1) {
+                const float q = expf(__fdiv_rn(xq[e], m.temp) - rq.m_q) * inv_zq;
+                rr = fmaxf(0.f, p - q);
+            }
+            const float ex = -logf(race_u(pick(w, r)));
+            if (rr > 0.f) {
+                const float key = rr / ex;
+                if (key > best || (key == best && j < bi)) { best = key; bi = j; }
+            }
+            if (p > 0.f) {
+                const float key = p / ex;
+                if (key > fbest || (key == fbest && j < fbi)) { fbest = key; fbi = j; }
+            }
+        }
+    }
+    for (int off = 32; off >= 1; off >>= 1) {
+        const float ob = __shfl_xor(best, off);
+        const int oi = __shfl_xor(bi, off);
+        if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
+        const float fb = __shfl_xor(fbest, off);
+        const int fi = __shfl_xor(fbi, off);
+        if (fb > fbest || (fb == fbest && fi < fbi)) { fbest = fb; fbi = fi; }
+    }
+    if (lane == 0) s_part[wave] = make_float4(best, __int_as_float(bi), fbest, __int_as_float(fbi));
+    __syncthreads();
+    if (tid == 0) {
+        float4 acc = s_part[0];
+        for (int w = 1; w < 4; ++w) {
+            const float4 o = s_part[w];
+            if (o.x > acc.x || (o.x == acc.x && __float_as_int(o.y) < __float_as_int(acc.y))) {
+                acc.x = o.x;
+                acc.y = o.y;
+            }
+            if (o.z > acc.z || (o.z == acc.z && __float_as_int(o.w) < __float_as_int(acc.w))) {
+                acc.z = o.z;
+                acc.w = o.w;
+            }
+        }
+        a.race_part[(size_t)b * a.nchunk + c] = acc;
+    }
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) s_last = atomicAdd(a.cnt_race + b, 1u) == (uint32_t)(a.nchunk - 1);
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    if (wave == 0) {
+        float bb = -1.f, fb = -1.f;
+        int bbi = kBigIdx, fbi2 = kBigIdx;
+        for (int cc = lane; cc < a.nchunk; cc += 64) {
+            const float4 o = a.race_part[(size_t)b * a.nchunk + cc];
+            const int oi = __float_as_int(o.y), ofi = __float_as_int(o.w);
+            if (o.x > bb || (o.x == bb && oi < bbi)) { bb = o.x; bbi = oi; }
+            if (o.z > fb || (o.z == fb && ofi < fbi2)) { fb = o.z; fbi2 = ofi; }
+        }
+        for (int off = 32; off >= 1; off >>= 1) {
+            const float ob = __shfl_xor(bb, off);
+            const int oi = __shfl_xor(bbi, off);
+            if (ob > bb || (ob == bb && oi < bbi)) { bb = ob; bbi = oi; }
+            const float of = __shfl_xor(fb, off);
+            const int ofi = __shfl_xor(fbi2, off);
+            if (of > fb || (of == fb && ofi < fbi2)) { fb = of; fbi2 = ofi; }
+        }
+        if (lane == 0) {
+            const int tok = bb > 0.f ? bbi : fbi2;
+            const int grow = m.r0 + rq.a;
+            a.out_tokens[grow] = tok;
+            if (a.chosen_lp && rq.logprobs)
+                a.chosen_lp[grow] = (float)((double)a.tl[(size_t)grow * a.vocab + tok] -
+                                            (double)rq.m_x - log(rq.z_x));
+            atomicExch(a.cnt_race + b, 0u);
+        }
+    }
+}
+
+}  // namespace
+
+SampPlan plan_sample(int B, int total_rows, int V, int max_top_k, int max_top_lp) {
+    SampPlan p{};
+    p.nchunk = (V + kChunk - 1) / kChunk;
+    const int kmax = max_top_k > max_top_lp ? max_top_k : max_top_lp;
+    int capc = kmax > 0 ? kmax + 32 : 0;
+    if (capc > kChunk) capc = kChunk;
+    if (capc > V) capc = V;
+    p.capc = capc;
+    p.slots = 3 * total_rows - B;
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    size_t off = 256;
+    p.off_cnt_sweep = off;
+    off += up((size_t)B * 4);
+    p.off_cnt_race = off;
+    off += up((size_t)B * 4);
+    p.off_stats = off;
+    off += up((size_t)p.slots * p.nchunk * 16);
+    p.off_cand = off;
+    off += up((size_t)p.slots * p.nchunk * capc * 8);
+    p.off_meta = off;
+    off += up((size_t)p.slots * p.nchunk * 8);
+    p.off_rows = off;
+    off += up((size_t)p.slots * sizeof(RowInfo));
+    p.off_keep = off;
+    off += up(max_top_k > 0 ? (size_t)(2 * total_rows - B) * kKeep * sizeof(KeepEntry) : 0);
+    p.off_race = off;
+    off += up((size_t)B * sizeof(RaceReq));
+    p.off_race_part = off;
+    off += up((size_t)B * p.nchunk * 16);
+    p.bytes = off;
+    return p;
+}
+
+hipError_t launch_sample(const SampArgs& a, hipStream_t stream) {
+    const dim3 grid((unsigned)a.batch * a.nchunk), block(kThreads);
+    const bool vec = (a.vocab % 4) == 0;
+    if (vec) hipLaunchKernelGGL(sweep_kernel<true>, grid, block, 0, stream, a);
+    else hipLaunchKernelGGL(sweep_kernel<false>, grid, block, 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // Always launched: only the device knows which sequences end in a full-vocabulary
+    // draw; every other workgroup returns at once.
+    if (vec) hipLaunchKernelGGL(race_kernel<true>, grid, block, 0, stream, a);
+    else hipLaunchKernelGGL(race_kernel<false>, grid, block, 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace vsa

@@ -1,0 +1,138 @@
+// Internal declarations shared by the library's HIP sources (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/vsa.h"
+
+namespace vsa {
+
+// ---------------------------------------------------------------- vector types
+typedef short bf16x8 __attribute__((ext_vector_type(8)));
+typedef short bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- small helpers
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// float -> bf16 bit pattern, round to nearest even (inputs here are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ void set_device_error(uint32_t* err, uint32_t bit) {
+    if (err) atomicOr(err, bit);
+}
+
+// ---------------------------------------------------------------- attention launch args
+struct AttnArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const int32_t* cu_rows;
+    const int32_t* ctx_lens;
+    float* out;
+    float* part_o;          // [units][nsplit][mcap][D]
+    float2* part_ml;        // [units][nsplit][mcap]   (running max (log2 units), sum)
+    uint32_t* counters;     // [units]
+    uint32_t* err;
+    int batch, total_rows, hq, hkv, group, d, s_max, max_rows, max_kv_len;
+    int nsplit, units, mcap;
+    float scale_log2;       // softmax scale * log2(e)
+};
+
+// Host-side plan shared by the size query and the launcher.
+struct AttnPlan {
+    int nb;          // 32-column blocks of the (row x head) query matrix per KV head
+    int mcap;        // 32 * nb
+    int nsplit;      // key splits per (sequence, KV head)
+    int units;       // B * Hkv
+    int tile;        // keys per workgroup tile
+    size_t off_counters, off_ml, off_o, bytes;
+};
+
+AttnPlan plan_attention(int B, int Hq, int Hkv, int D, int max_rows, int max_kv_len);
+hipError_t launch_attention(const AttnArgs& a, const AttnPlan& p, vsa_dtype dtype,
+                            hipStream_t stream);
+
+// ---------------------------------------------------------------- vocabulary stage
+constexpr int kChunk = 2048;         // vocabulary ids per workgroup chunk (8 per thread)
+constexpr int kKeep = 256;           // kept-set capacity of one truncated row
+constexpr int kMaxSeqRows = 32;      // verify rows per sequence (K <= 31)
+
+// Merged statistics of one row (finalize results, also handed to the race kernel).
+struct RowInfo {
+    double z;          // sum of exp(v - m) over the row (softmax normalizer)
+    float m;           // max of v over the row
+    int argmax;        // greedy argmax (lowest id on ties)
+    float theta;       // top-k threshold (value of the k-th largest)
+    int kept_k, kept_p;
+    int pad;
+};
+
+struct KeepEntry {     // one id of a truncated, renormalized distribution
+    int idx;
+    int pad;
+    double p;
+};
+
+struct RaceReq {       // a categorical draw over the whole vocabulary, done by race_kernel
+    int kind;          // 0 none, 1 residual max(0, p - q), 2 bonus (p)
+    int a;             // accepted drafts (the draw decides row a)
+    int pos;           // absolute position of the draw
+    int logprobs;
+    float m_p, m_q, m_x;
+    int pad;
+    double z_p, z_q, z_x;
+};
+
+struct SampArgs {
+    const float* tl;               // target logits [T, V]
+    const float* dl;               // draft logits [T - B, V] or null
+    const int32_t* drafts;         // [T - B]
+    const int32_t* cu_rows;        // [B + 1]
+    const int32_t* counts;         // [B, V] or null
+    const vsa_row_params* params;  // [B]
+    const int32_t* positions;      // [B]
+    uint64_t seed;
+    int batch, total_rows, vocab, max_rows, max_top_k, max_top_lp, nchunk, capc;
+    int32_t* accepted;
+    int32_t* out_tokens;
+    float* chosen_lp;
+    float* top_vals;
+    int32_t* top_ids;
+    float* diag_thr;
+    int32_t* diag_kept;
+    uint32_t* err;
+    uint32_t* cnt_sweep;           // [B]
+    uint32_t* cnt_race;            // [B]
+    float4* stats;                 // [slots][nchunk] (m, s, best value, best id bits)
+    uint2* cand;                   // [slots][nchunk][capc] (ordered key, id)
+    uint2* cand_meta;              // [slots][nchunk] (count, k-th key)
+    RowInfo* rows;                 // [slots]
+    KeepEntry* keep;               // [2T - B][kKeep]
+    RaceReq* race;                 // [B]
+    float4* race_part;             // [B][nchunk]
+};
+
+struct SampPlan {
+    int nchunk, capc, slots;
+    size_t off_cnt_sweep, off_cnt_race, off_stats, off_cand, off_meta, off_rows, off_keep,
+        off_race, off_race_part, bytes;
+};
+
+SampPlan plan_sample(int B, int total_rows, int V, int max_top_k, int max_top_lp);
+hipError_t launch_sample(const SampArgs& a, hipStream_t stream);
+
+}  // namespace vsa

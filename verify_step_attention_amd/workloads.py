@@ -221,3 +221,32 @@ def make_workload(name, *, batch=None, drafts=None, ctx=None, vocab=None, with_k
                     s_max=s_max, q=q, k_cache=k_cache, v_cache=v_cache,
                     target_logits=target, draft_logits=draft, draft_tokens=draft_tokens,
                     token_counts=counts, params=params, positions=positions, seed=0)
+
+
+def device_tensors(w, device="cuda", with_kv=True):
+    """Copy a workload to the GPU as torch tensors (bf16 inputs keep their bit patterns)."""
+    import torch
+
+    def t(x, dtype=None):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(device) if dtype is None else \
+            torch.from_numpy(np.ascontiguousarray(x)).to(device).view(dtype)
+
+    out = {}
+    if w.dtype == BF16:
+        out["q"] = t(w.q.view(np.int16), torch.bfloat16)
+        if with_kv:
+            out["k_cache"] = t(w.k_cache.view(np.int16), torch.bfloat16)
+            out["v_cache"] = t(w.v_cache.view(np.int16), torch.bfloat16)
+    else:
+        out["q"] = t(w.q)
+        if with_kv:
+            out["k_cache"] = t(w.k_cache)
+            out["v_cache"] = t(w.v_cache)
+    out["cu_rows"] = t(w.cu_rows.astype(np.int32))
+    out["ctx_lens"] = t(w.ctx_lens.astype(np.int32))
+    out["target_logits"] = t(w.target_logits)
+    out["draft_logits"] = t(w.draft_logits) if w.draft_logits.size else None
+    out["draft_tokens"] = t(w.draft_tokens.astype(np.int32)) if w.draft_tokens.size else None
+    out["token_counts"] = None if w.token_counts is None else t(w.token_counts.astype(np.int32))
+    out["positions"] = t(w.positions.astype(np.int32))
+    return out
