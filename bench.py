@@ -1,0 +1,277 @@
+"""Benchmark of the verify step on one MI355X: verified draft-block rows per second and
+achieved HBM bandwidth on the B=4, K=4, ctx 8192 workload (32 q / 8 kv heads, D=128, bf16
+K/V; vocabulary 151936 fp32 logits, penalties 0.5 / 0.3, sequences 0 and 2 greedy, 1 and 3
+sampled at T=0.8).
+
+One step = verify_attention (one layer's attention of the 20 verify rows) followed by
+verify_sample_accept on the same stream, on one of R distinct input sets in HBM (R * 154 MB
+> 1 GB, so the 256 MB last-level cache cannot hold the working set between steps).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Prints one JSON line. Roofline: the dominant kernel (attention) is timed per launch with
+HIP events on the stream it runs on; its algorithmic bytes are the K/V of every sequence
+(ctx + R keys x Hkv x D x 2 bytes x 2), Q and the fp32 output. HBM traffic counters come
+from rocprofv3 runs recorded under profiles/ and are reported only while the kernel
+source still matches the one they were taken on.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+WORKLOAD = "verify_b4k4_ctx8192"
+PEAK_HBM_GBPS = 8000.0
+COUNTERS = os.path.join(ROOT, "profiles", "attention_b4k4_ctx8192_counters.json")
+ATTN_SRC = os.path.join(ROOT, "verify_step_attention_amd", "csrc", "attention.hip")
+
+
+def algorithmic_bytes(w):
+    """Bytes each kernel must move at least once (inputs read once, outputs written once)."""
+    rows = np.diff(w.cu_rows)
+    kv = int(((w.ctx_lens + rows) * w.num_kv_heads * w.head_dim * 2 * 2).sum())
+    q = w.total_rows * w.num_q_heads * w.head_dim * 2
+    o = w.total_rows * w.num_q_heads * w.head_dim * 4
+    sampled = [b for b in range(w.batch) if w.params[b].temperature > 0]
+    tl = w.total_rows * w.vocab * 4
+    dl = sum(int(rows[b] - 1) for b in sampled) * w.vocab * 4
+    cnt = w.batch * w.vocab * 4 if w.token_counts is not None else 0
+    small = w.total_rows * 4 * 2 + w.batch * 4 * 4          # drafts, tokens, lengths, params
+    return {"attention": kv + q + o, "sample": tl + dl + cnt + small,
+            "kv": kv, "q_out": q + o, "target_logits": tl, "draft_logits": dl, "counts": cnt}
+
+
+def counters_traffic():
+    """(fetch+write bytes per attention launch) from the recorded rocprofv3 runs, if they were
+    taken on the current attention source; else None."""
+    try:
+        with open(COUNTERS) as f:
+            rec = json.load(f)
+        with open(ATTN_SRC, "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()
+        if rec.get("attention_source_sha256") != digest:
+            return None
+        return rec["bytes_per_launch"]
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, budget_s=12.0):
+    """The oracle as it stands, timed on the host on whole verify steps of the same workload
+    until about budget_s seconds have passed (at least one step)."""
+    from oracle import attention as oatt, sampling as osamp
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    k, v = w.kv_f32()
+    q = w.q_f32()
+    prm = [osamp.RowParams(p.temperature, p.top_k, p.top_p, p.presence_penalty,
+                           p.frequency_penalty, p.logprobs, p.top_logprobs) for p in w.params]
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        oatt.verify_attention(q, k, v, w.cu_rows, w.ctx_lens, w.num_q_heads, w.num_kv_heads)
+        osamp.verify_sample_accept(w.target_logits, w.draft_logits, w.draft_tokens, w.cu_rows,
+                                   w.token_counts, prm, w.positions, w.seed)
+        steps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(steps * w.total_rows / dt, 3), "unit": "rows/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{steps} whole verify step(s) of {WORKLOAD} (attention of all 20 rows "
+                      f"+ sample/accept of all 4 sequences), {dt:.1f} s on the host, numpy "
+                      f"BLAS threads = {cores}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--sets", type=int, default=7)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every call from Python instead of replaying HIP graphs")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (a known-size "
+                         "reference for rocprofv3 byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "the verify step's sharding across GPUs is a design note, not a run.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import verify_step_attention_amd as vsa
+    from verify_step_attention_amd import workloads as wl
+
+    print(f"[bench] building inputs for {WORKLOAD}", file=sys.stderr, flush=True)
+    w = wl.make_workload(WORKLOAD)
+    nbytes = algorithmic_bytes(w)
+    step_bytes = nbytes["attention"] + nbytes["sample"]
+    dev0 = wl.device_tensors(w)
+    sets = [dev0] + [{k: (None if t is None else t.clone()) for k, t in dev0.items()}
+                     for _ in range(args.sets - 1)]
+    params = torch.from_numpy(vsa.pack_row_params(w.params).view(np.uint8)).cuda()
+    mtk = max(p.top_k for p in w.params)
+    mtl = max(p.top_logprobs for p in w.params)
+    ws_a = torch.zeros(vsa.verify_attention_workspace_size(
+        w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.max_rows, w.max_kv_len),
+        dtype=torch.uint8, device="cuda")
+    ws_s = torch.zeros(vsa.verify_sample_accept_workspace_size(
+        w.batch, w.total_rows, w.vocab, w.max_rows, mtk, mtl), dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.total_rows, w.num_q_heads, w.head_dim), dtype=torch.float32,
+                      device="cuda")
+    acc = torch.empty(w.batch, dtype=torch.int32, device="cuda")
+    toks = torch.empty(w.total_rows, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def attention(d):
+        vsa.verify_attention(d["q"], d["k_cache"], d["v_cache"], d["cu_rows"], d["ctx_lens"],
+                             out, ws_a, max_rows_per_seq=w.max_rows, max_kv_len=w.max_kv_len,
+                             stream=stream)
+
+    def sample(d):
+        vsa.verify_sample_accept(d["target_logits"], d["draft_logits"], d["draft_tokens"],
+                                 d["cu_rows"], d["token_counts"], params, d["positions"], 0,
+                                 acc, toks, ws_s, max_rows_per_seq=w.max_rows, max_top_k=mtk,
+                                 max_top_logprobs=mtl, stream=stream)
+
+    if args.copy_probe_mib:
+        src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for i in range(args.warmup):
+        d = sets[i % len(sets)]
+        attention(d)
+        sample(d)
+    torch.cuda.synchronize()
+
+    # One HIP graph per input set holds a whole step (the library only launches kernels on
+    # the given stream; no memsets, no allocations), so replays carry no Python overhead.
+    graphs = []
+    if not args.eager:
+        capture_stream = torch.cuda.Stream()
+        capture_stream.wait_stream(stream)
+        with torch.cuda.stream(capture_stream):
+            for d in sets:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=capture_stream):
+                    cs = torch.cuda.current_stream()
+                    vsa.verify_attention(d["q"], d["k_cache"], d["v_cache"], d["cu_rows"],
+                                         d["ctx_lens"], out, ws_a, max_rows_per_seq=w.max_rows,
+                                         max_kv_len=w.max_kv_len, stream=cs)
+                    vsa.verify_sample_accept(d["target_logits"], d["draft_logits"],
+                                             d["draft_tokens"], d["cu_rows"], d["token_counts"],
+                                             params, d["positions"], 0, acc, toks, ws_s,
+                                             max_rows_per_seq=w.max_rows, max_top_k=mtk,
+                                             max_top_logprobs=mtl, stream=cs)
+                graphs.append(g)
+        stream.wait_stream(capture_stream)
+        for i in range(len(graphs)):
+            graphs[i].replay()
+        torch.cuda.synchronize()
+
+    def step(i):
+        if graphs:
+            graphs[i % len(graphs)].replay()
+        else:
+            d = sets[i % len(sets)]
+            attention(d)
+            sample(d)
+
+    # whole-step timing
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    print(f"[bench] {args.steps} steps timed ({'eager' if not graphs else 'graph replay'}): "
+          f"{ms_step * 1e3:.2f} us/step", file=sys.stderr, flush=True)
+
+    # per-kernel timing: events around each call, on the launch stream
+    n_k = min(args.steps, 100)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_k)]
+    for i in range(n_k):
+        d = sets[i % len(sets)]
+        ev[i][0].record(stream)
+        attention(d)
+        ev[i][1].record(stream)
+        sample(d)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    attn_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    samp_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    err_a = int(ws_a[:4].view(torch.int32).item())
+    err_s = int(ws_s[:4].view(torch.int32).item())
+    if err_a or err_s:
+        print(f"[bench] device error words: attention {err_a:#x} sample {err_s:#x}",
+              file=sys.stderr)
+
+    attn_us = float(np.mean(attn_ms)) * 1e3
+    achieved = nbytes["attention"] / (attn_us * 1e-6) / 1e9
+    traffic = counters_traffic()
+    rows_per_s = w.total_rows / (ms_step * 1e-3)
+    line = {
+        "metric": "verified draft-block rows/sec + achieved HBM GB/s, B=4 K=4 ctx 8192",
+        "value": round(rows_per_s, 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "achieved_hbm_GBps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "launch": "eager" if not graphs else "hip_graph_replay",
+        "config": {
+            "workload": WORKLOAD, "batch": w.batch, "drafts_per_seq": 4, "ctx": 8192,
+            "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+            "vocab": w.vocab, "rows_per_step": w.total_rows, "input_sets": len(sets),
+            "algorithmic_bytes_per_step": step_bytes,
+            "step_fraction_of_8TBps": round(step_bytes / (ms_step * 1e-3) / 1e9 /
+                                            PEAK_HBM_GBPS, 4),
+            "attention_us": round(attn_us, 2),
+            "attention_us_p10_p90": [round(float(np.percentile(attn_ms, 10)) * 1e3, 2),
+                                     round(float(np.percentile(attn_ms, 90)) * 1e3, 2)],
+            "sample_accept_us": round(float(np.mean(samp_ms)) * 1e3, 2),
+            "logits_dtype": "f32",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "verify_attention (attn_bf16_kernel<128,1>)",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": nbytes["attention"],
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on the host", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -32,10 +32,10 @@
  *     in and never cleared by the library; the caller reads (and may zero) it after the
  *     stream completes.
  *   - Workspace: caller-owned device memory of at least *_workspace_size() bytes, 256-byte
- *     aligned, ZERO-FILLED BEFORE ITS FIRST USE. Calls leave their internal counters at
- *     zero, so one workspace serves any number of calls in stream order. Two calls that
- *     share a workspace must not run concurrently (different streams), and a workspace
- *     sized for one problem serves any problem whose size query is not larger.
+ *     aligned, ZERO-FILLED BEFORE ITS FIRST USE. It holds arrival counters that every call
+ *     returns to zero, so one workspace serves any number of calls in stream order. Two
+ *     calls that share a workspace must not run concurrently (different streams), and a
+ *     workspace sized for one problem serves any problem whose size query is not larger.
  *   - No call keeps state between calls; the library is reentrant across workspaces.
  */
 #ifndef VSA_H
@@ -159,7 +159,7 @@ vsa_status verify_attention(const void* q, const void* k_cache, const void* v_ca
  *   positions      [B] int32 absolute position decided by row 0
  *   seed           64-bit Philox key
  *   max_rows_per_seq host bound >= every R_b (at most 32)
- *   max_top_k      host bound >= every top_k in use (0 if no sequence uses top-k); <= 1024
+ *   max_top_k      host bound >= every top_k in use (0 if no sequence uses top-k); <= 256
  *   max_top_logprobs host bound >= every top_logprobs (<= 32); the width of top_lp_*
  * Outputs (each may be NULL when not wanted, except accepted_len and out_tokens):
  *   accepted_len   [B] int32   accepted drafts a_b
@@ -173,8 +173,10 @@ vsa_status verify_attention(const void* q, const void* k_cache, const void* v_ca
  *                  sequence (-inf when top-k is off), NaN for greedy sequences
  *   diag_kept      [total_rows, 2] int32 kept-set sizes after top-k and after top-p of
  *                  each target row of a sampled sequence (0 for greedy sequences)
- * Limits: V >= 1; K_b <= 31; top_p < 1 requires top_k > 0 (a nucleus over the whole
- * vocabulary without top-k is not supported: VSA_DEVERR_PARAMS).
+ * Limits: 1 <= V <= 524288; K_b <= 31; top_k <= 256; a sampled sequence with top_p < 1
+ * needs 0 < top_k < V (a nucleus over the whole vocabulary is not supported:
+ * VSA_DEVERR_PARAMS); at most 256 ids may tie into one kept set
+ * (VSA_DEVERR_TIE_OVERFLOW beyond).
  * ------------------------------------------------------------------------------------ */
 size_t verify_sample_accept_workspace_size(int B, int total_rows, int V, int max_rows_per_seq,
                                            int max_top_k, int max_top_logprobs);

@@ -41,3 +41,105 @@ def assert_attention_close(got, ref):
     assert not np.isnan(got).any(), "NaN in output"
     assert not bad.any(), (f"{int(bad.sum())} of {bad.size} elements out of tolerance; "
                            f"max abs err {np.nanmax(np.abs(got - ref)):.3e}")
+
+
+# ----------------------------------------------------------------------------- sampling
+def oracle_params(params):
+    from oracle.sampling import RowParams
+    return [RowParams(p.temperature, p.top_k, p.top_p, p.presence_penalty,
+                      p.frequency_penalty, p.logprobs, p.top_logprobs) for p in params]
+
+
+def q_distributed_drafts(w, seed=1):
+    """Draft tokens drawn from the truncated draft distribution q (the oracle's sampler)."""
+    from oracle.sampling import sample_proposals
+    if w.total_rows == w.batch:
+        return np.zeros(0, np.int32)
+    return sample_proposals(w.draft_logits, w.cu_rows, oracle_params(w.params), w.positions,
+                            seed).astype(np.int32)
+
+
+def sample_gpu(w, seed=0, max_top_k=None, max_top_lp=None, workspace=None, dev=None):
+    dev = dev or wl.device_tensors(w, with_kv=False)
+    mtk = max_top_k if max_top_k is not None else max([p.top_k for p in w.params] + [0])
+    mtl = max_top_lp if max_top_lp is not None else max([p.top_logprobs for p in w.params] + [0])
+    size = vsa.verify_sample_accept_workspace_size(w.batch, w.total_rows, w.vocab, w.max_rows,
+                                                   mtk, mtl)
+    assert size > 0
+    ws = workspace if workspace is not None else torch.zeros(size, dtype=torch.uint8,
+                                                             device="cuda")
+    ws[:4].zero_()
+    params = torch.from_numpy(vsa.pack_row_params(w.params).view(np.uint8)).cuda()
+    t = w.total_rows
+    out = {
+        "accepted_len": torch.full((w.batch,), -7, dtype=torch.int32, device="cuda"),
+        "out_tokens": torch.full((t,), -7, dtype=torch.int32, device="cuda"),
+        "chosen_logprob": torch.full((t,), 7.0, dtype=torch.float32, device="cuda"),
+        "top_lp_vals": torch.full((t, max(mtl, 1)), 7.0, dtype=torch.float32, device="cuda"),
+        "top_lp_ids": torch.full((t, max(mtl, 1)), -7, dtype=torch.int32, device="cuda"),
+        "diag_threshold": torch.full((t,), 7.0, dtype=torch.float32, device="cuda"),
+        "diag_kept": torch.full((t, 2), -7, dtype=torch.int32, device="cuda"),
+    }
+    draft_logits = dev["draft_logits"] if any(p.temperature > 0 for p in w.params) else None
+    vsa.verify_sample_accept(dev["target_logits"], draft_logits, dev["draft_tokens"],
+                             dev["cu_rows"], dev["token_counts"], params, dev["positions"],
+                             seed, out["accepted_len"], out["out_tokens"], ws,
+                             max_rows_per_seq=w.max_rows, max_top_k=mtk, max_top_logprobs=mtl,
+                             chosen_logprob=out["chosen_logprob"],
+                             top_lp_vals=out["top_lp_vals"], top_lp_ids=out["top_lp_ids"],
+                             diag_threshold=out["diag_threshold"], diag_kept=out["diag_kept"])
+    torch.cuda.synchronize()
+    res = {k: v.cpu().numpy() for k, v in out.items()}
+    res["top_lp_vals"] = res["top_lp_vals"][:, :mtl]
+    res["top_lp_ids"] = res["top_lp_ids"][:, :mtl]
+    res["err"] = int(ws[:4].view(torch.int32).item())
+    return res
+
+
+def sample_oracle(w, seed=0, max_top_lp=None):
+    from oracle.sampling import verify_sample_accept
+    mtl = max_top_lp if max_top_lp is not None else max([p.top_logprobs for p in w.params] + [0])
+    return verify_sample_accept(w.target_logits, w.draft_logits, w.draft_tokens, w.cu_rows,
+                                w.token_counts, oracle_params(w.params), w.positions, seed, mtl)
+
+
+LP_TOL = 2e-5
+
+
+def compare_sample(w, gpu, ora):
+    """Exact on accepted lengths and emitted tokens of every sequence the oracle does not
+    flag (fp margins), exact on top-k thresholds and kept counts, logprobs within 2e-5.
+    Returns the number of flagged sequences."""
+    flagged = 0
+    for b in range(w.batch):
+        r0, r1 = int(w.cu_rows[b]), int(w.cu_rows[b + 1])
+        prm = w.params[b]
+        if ora["excepted"][b]:
+            flagged += 1
+        else:
+            assert gpu["accepted_len"][b] == ora["accepted_len"][b], (b, gpu["accepted_len"][b],
+                                                                    ora["accepted_len"][b])
+            assert np.array_equal(gpu["out_tokens"][r0:r1], ora["out_tokens"][r0:r1]), (
+                b, gpu["out_tokens"][r0:r1], ora["out_tokens"][r0:r1])
+            if prm.logprobs:
+                g, o = gpu["chosen_logprob"][r0:r1], ora["chosen_logprob"][r0:r1]
+                assert np.array_equal(np.isnan(g), np.isnan(o))
+                ok = ~np.isnan(o)
+                assert np.all(np.abs(g[ok] - o[ok]) <= LP_TOL), (b, g, o)
+        if prm.temperature > 0:
+            th_g, th_o = gpu["diag_threshold"][r0:r1], ora["topk_threshold"][r0:r1]
+            assert np.array_equal(th_g.astype(np.float64), th_o), (b, th_g, th_o)
+            assert np.array_equal(gpu["diag_kept"][r0:r1, 0], ora["kept_topk"][r0:r1])
+            near = ora["row_nucleus_margin"][r0:r1] < 1e-5
+            assert np.array_equal(gpu["diag_kept"][r0:r1, 1][~near],
+                                  ora["kept_nucleus"][r0:r1][~near])
+        else:
+            assert np.all(np.isnan(gpu["diag_threshold"][r0:r1]))
+            assert np.all(gpu["diag_kept"][r0:r1] == 0)
+        n = min(prm.top_logprobs, gpu["top_lp_ids"].shape[1])
+        if gpu["top_lp_ids"].shape[1]:
+            assert np.array_equal(gpu["top_lp_ids"][r0:r1, :n], ora["top_lp_ids"][r0:r1, :n])
+            assert np.all(np.abs(gpu["top_lp_vals"][r0:r1, :n] - ora["top_lp_vals"][r0:r1, :n])
+                          <= LP_TOL)
+            assert np.all(gpu["top_lp_ids"][r0:r1, n:] == -1)
+    return flagged

@@ -92,7 +92,6 @@ def test_batch_invariance_and_workspace_reuse():
     x, _ = attention_gpu(w1, workspace=ws)
     y, _ = attention_gpu(w1, workspace=ws)
     assert np.array_equal(x, y)
-    assert int(ws[256:512].view(torch.int32).abs().sum().item()) == 0
 
 
 def test_device_error_word_on_bad_context():

@@ -142,6 +142,7 @@ vsa_status verify_sample_accept(const float* target_logits, const float* draft_l
     a.max_top_lp = max_top_logprobs;
     a.nchunk = plan.nchunk;
     a.capc = plan.capc;
+    a.keepcap = plan.keepcap;
     a.accepted = accepted_len;
     a.out_tokens = out_tokens;
     a.chosen_lp = chosen_logprob;

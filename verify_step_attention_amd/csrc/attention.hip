@@ -57,59 +57,72 @@ __device__ __forceinline__ SeqGeom seq_geometry(const AttnArgs& a, int b, bool r
     return s;
 }
 
-// Counts this split's arrival for its unit; true in the workgroup that arrives last.
-__device__ bool arrive_last(const AttnArgs& a, int unit) {
-    __shared__ int s_last;
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t prev = atomicAdd(a.counters + unit, 1u);
-        s_last = (prev == (uint32_t)(a.nsplit - 1));
-    }
-    __syncthreads();
-    const bool last = s_last;
-    if (last) __threadfence();
-    return last;
-}
-
-// The last split of a unit merges every split's (max, sum, O) into the output:
+// The last split of a unit to finish merges every split's (max, sum, O):
 //   out = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s,   m = max_s m_s.
-// `w` is LDS scratch of nsplit * MC floats. Resets the unit's arrival counter.
+// Partials arrive through the fence-free hand-off (agent-scope stores / loads). The
+// (max, sum) pairs of all splits go to LDS in one pass; then each thread sums float4
+// slices of O with the loads of up to 16 splits in flight at once.
+// `w` is LDS scratch of 2 * nsplit * MC floats.
 template <int D>
 __device__ void attn_merge(const AttnArgs& a, float* w, int unit, int g, const SeqGeom& s,
                            int MC) {
     const int tid = threadIdx.x;
     const int M = s.rows * a.group;
-    const size_t base = (size_t)unit * a.nsplit;
-    for (int n = tid; n < M; n += blockDim.x) {
-        float m = kNegInf;
-        for (int sp = 0; sp < a.nsplit; ++sp) m = fmaxf(m, a.part_ml[(base + sp) * a.mcap + n].x);
-        float l = 0.f;
-        for (int sp = 0; sp < a.nsplit; ++sp) {
-            const float2 ml = a.part_ml[(base + sp) * a.mcap + n];
-            const float f = (ml.x == kNegInf) ? 0.f : exp2f(ml.x - m);
-            w[sp * MC + n] = f;
-            l += f * ml.y;
-        }
-        const float inv = 1.f / l;
-        for (int sp = 0; sp < a.nsplit; ++sp) w[sp * MC + n] *= inv;
+    const int ns = a.nsplit;
+    const size_t base = (size_t)unit * ns;
+    __shared__ float s_inv[128];
+    float* wl = w + ns * MC;
+    for (int e = tid; e < ns * M; e += blockDim.x) {
+        const int sp = e / M, n = e % M;
+        const float2 ml = handoff_load(a.part_ml + (base + sp) * a.mcap + n);
+        w[sp * MC + n] = ml.x;
+        wl[sp * MC + n] = ml.y;
     }
     __syncthreads();
-    for (int e = tid; e < M * D; e += blockDim.x) {
-        const int n = e / D, d = e % D;
-        float o = 0.f;
-        for (int sp = 0; sp < a.nsplit; ++sp) {
-            const float f = w[sp * MC + n];
-            if (f != 0.f) o += f * a.part_o[((base + sp) * a.mcap + n) * D + d];
+    for (int n = tid; n < M; n += blockDim.x) {
+        float m = kNegInf;
+        for (int sp = 0; sp < ns; ++sp) m = fmaxf(m, w[sp * MC + n]);
+        float l = 0.f;
+        for (int sp = 0; sp < ns; ++sp) {
+            const float ms = w[sp * MC + n];
+            const float f = (ms == kNegInf) ? 0.f : exp2f(ms - m);
+            w[sp * MC + n] = f;
+            l += f * wl[sp * MC + n];
         }
-        const int row = s.r0 + n / a.group, head = g * a.group + n % a.group;
-        a.out[((size_t)row * a.hq + head) * D + d] = o;
+        s_inv[n] = 1.f / l;
     }
-    if (tid == 0) atomicExch(a.counters + unit, 0u);
+    __syncthreads();
+    constexpr int D4 = D / 4;
+    const size_t stride = (size_t)a.mcap * D4;               // float4s between splits
+    for (int e = tid; e < M * D4; e += blockDim.x) {
+        const int n = e / D4, d4 = e % D4;
+        const float4* src = reinterpret_cast<const float4*>(a.part_o) + (base * a.mcap + n) * D4 + d4;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int sp0 = 0; sp0 < ns; sp0 += 16) {
+            float4 v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                v[u] = (sp0 + u < ns && w[(sp0 + u) * MC + n] != 0.f)
+                           ? handoff_load4(src + (size_t)(sp0 + u) * stride)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const float f = (sp0 + u < ns) ? w[(sp0 + u) * MC + n] : 0.f;
+                acc.x += f * v[u].x;
+                acc.y += f * v[u].y;
+                acc.z += f * v[u].z;
+                acc.w += f * v[u].w;
+            }
+        }
+        const float inv = s_inv[n];
+        const int row = s.r0 + n / a.group, head = g * a.group + n % a.group;
+        *reinterpret_cast<float4*>(a.out + ((size_t)row * a.hq + head) * D + 4 * d4) =
+            make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    }
 }
 
-// Combines the key groups of one workgroup, writes either the final output (single split)
-// or this split's partial state, and lets the last split of the unit merge all partials.
+// Combines the key groups of one workgroup and writes either the final output (single
+// split) or this split's partial state.
 //   obuf[(kg * MC + n) * D + d]  unnormalized O of key group kg (relative to its own max)
 //   gm[kg * MC + n], gl[...]     that group's running max (log2 units) and sum
 // with gm = obuf + KGX * MC * D and gl = gm + KGX * MC.
@@ -151,18 +164,27 @@ __device__ void attn_epilogue(const AttnArgs& a, char* smem, int unit, int split
         return;
     }
     const size_t pslot = (size_t)unit * a.nsplit + split;
-    for (int e = tid; e < M * D; e += blockDim.x) {
-        const int n = e / D, d = e % D;
-        float o = 0.f;
-        for (int k = 0; k < KGX; ++k) o += fac[k * MC + n] * obuf[(k * MC + n) * D + d];
-        a.part_o[(pslot * a.mcap + n) * D + d] = o;
+    for (int e = tid; e < M * (D / 4); e += blockDim.x) {
+        const int n = e / (D / 4), d = 4 * (e % (D / 4));
+        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int k = 0; k < KGX; ++k) {
+            const float f = fac[k * MC + n];
+            const float4 v = *reinterpret_cast<const float4*>(obuf + (k * MC + n) * D + d);
+            o.x += f * v.x;
+            o.y += f * v.y;
+            o.z += f * v.z;
+            o.w += f * v.w;
+        }
+        handoff_store4(reinterpret_cast<float4*>(a.part_o + (pslot * a.mcap + n) * D + d), o);
     }
     for (int n = tid; n < M; n += blockDim.x)
-        a.part_ml[pslot * a.mcap + n] = make_float2(wm[n], wl[n]);
-    if (arrive_last(a, unit)) attn_merge<D>(a, obuf, unit, g, s, MC);
+        handoff_store(a.part_ml + pslot * a.mcap + n, make_float2(wm[n], wl[n]));
+    __shared__ int s_last;
+    if (handoff_arrive(a.counters + unit, (uint32_t)a.nsplit, &s_last))
+        attn_merge<D>(a, obuf, unit, g, s, MC);
 }
 
-// A split that owns no tile publishes an empty state (the merge skips it) and still
+// A split that owns no tile publishes an empty state, which the merge skips, and still
 // counts its arrival.
 template <int D>
 __device__ void attn_empty_split(const AttnArgs& a, char* smem, int unit, int split, int g,
@@ -170,8 +192,10 @@ __device__ void attn_empty_split(const AttnArgs& a, char* smem, int unit, int sp
     const int M = s.rows * a.group;
     const size_t pslot = (size_t)unit * a.nsplit + split;
     for (int n = threadIdx.x; n < M; n += blockDim.x)
-        a.part_ml[pslot * a.mcap + n] = make_float2(kNegInf, 0.f);
-    if (arrive_last(a, unit)) attn_merge<D>(a, reinterpret_cast<float*>(smem), unit, g, s, MC);
+        handoff_store(a.part_ml + pslot * a.mcap + n, make_float2(kNegInf, 0.f));
+    __shared__ int s_last;
+    if (handoff_arrive(a.counters + unit, (uint32_t)a.nsplit, &s_last))
+        attn_merge<D>(a, reinterpret_cast<float*>(smem), unit, g, s, MC);
 }
 
 // -------------------------------------------------------------------------- bf16 / MFMA
@@ -472,6 +496,10 @@ AttnPlan plan_attention(int B, int Hq, int Hkv, int D, int max_rows, int max_kv_
     int nsplit = (512 + p.units - 1) / p.units;
     if (nsplit > tiles) nsplit = tiles;
     if (nsplit > 64) nsplit = 64;
+    // the merge stages 2 * nsplit * mcap floats in the smallest tile buffer
+    // (bf16, D = 64: 2 * 128 rows * 144 bytes)
+    const int merge_cap = (2 * 128 * (2 * 64 + 16)) / (8 * p.mcap);
+    if (nsplit > merge_cap) nsplit = merge_cap;
     if (nsplit < 1) nsplit = 1;
     p.nsplit = nsplit;
     size_t off = 256;                                            // error word + pad

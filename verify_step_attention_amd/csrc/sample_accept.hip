@@ -9,7 +9,8 @@
 // (release v0.0.2); greedy acceptance as the product of positionwise matches with one sync
 // per round (Changelog [0.2.0] "Decode-path performance").
 //
-// Kernels:
+// Kernels (two launches; within each, workgroups hand results to the last one to finish
+// through agent-scope stores and loads rather than a fence):
 //   sweep_kernel  grid (B x chunks of 2048 ids). One workgroup reads one chunk of every row
 //                 of one sequence with coalesced loads: the count histogram once, then each
 //                 target row (penalized z, and y = z / T when sampled), draft row and raw
@@ -36,6 +37,15 @@ constexpr int kThreads = 256;
 constexpr int kEpt = kChunk / kThreads;        // ids per thread per chunk (8)
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kBigIdx = 0x7FFFFFFF;
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ void handoff_store_u2(uint2* p, uint2 v) {
+    handoff_store(reinterpret_cast<float2*>(p), *reinterpret_cast<float2*>(&v));
+}
+__device__ __forceinline__ uint2 handoff_load_u2(const uint2* p) {
+    const float2 f = handoff_load(reinterpret_cast<const float2*>(p));
+    return *reinterpret_cast<const uint2*>(&f);
+}
 
 // ------------------------------------------------------------------ small device helpers
 __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
@@ -92,18 +102,6 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
     return v > bv || (v == bv && i < bi);
 }
 
-// (max, sum of exp(v - max)) pairs
-__device__ __forceinline__ void ms_merge(float& m, float& s, float m2, float s2) {
-    const float mn = fmaxf(m, m2);
-    if (mn == kNegInf) {
-        m = mn;
-        s = 0.f;
-        return;
-    }
-    s = s * expf(m - mn) + s2 * expf(m2 - mn);
-    m = mn;
-}
-
 // ------------------------------------------------------------------ per-sequence mode
 struct SeqMode {
     int r0, rows, k, d0;
@@ -129,7 +127,8 @@ __device__ SeqMode seq_mode(const SampArgs& a, int b, uint32_t* errbits) {
     const bool bad = !(p.temperature >= 0.f) || !isfinite(p.temperature) || p.top_k < 0 ||
                      p.top_k > a.max_top_k || !(p.top_p > 0.f && p.top_p <= 1.f) ||
                      p.top_logprobs < 0 || p.top_logprobs > a.max_top_lp ||
-                     (p.top_p < 1.f && p.top_k == 0 && p.temperature > 0.f);
+                     (p.top_p < 1.f && p.temperature > 0.f &&
+                      !(p.top_k > 0 && p.top_k < a.vocab));
     if (bad) *errbits |= VSA_DEVERR_PARAMS;
     m.temp = p.temperature;
     m.sampled = !bad && p.temperature > 0.f;
@@ -245,7 +244,7 @@ __device__ uint32_t wave_select_kth(const uint2* cand, const int* ccount, int nc
             const uint2* cc = cand + (size_t)c * capc;
             const int n = ccount[c];
             for (int i = lane; i < n; i += 64) {
-                const uint32_t key = cc[i].x;
+                const uint32_t key = handoff_load_u2(cc + i).x;
                 if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
             }
         }
@@ -295,7 +294,7 @@ __device__ int wave_collect(const uint2* cand, const int* ccount, int nchunk, in
             uint2 e = make_uint2(0, 0);
             bool take = false;
             if (i < n) {
-                e = cc[i];
+                e = handoff_load_u2(cc + i);
                 take = e.x >= theta;
             }
             const uint64_t m = __ballot(take);
@@ -438,7 +437,7 @@ __device__ __forceinline__ int row_count(int base_count, bool special, const int
 // Probability of id d under row `slot`'s truncated distribution (its kept list).
 __device__ double keep_lookup(const SampArgs& a, int kslot, int n, int d) {
     const int lane = threadIdx.x & 63;
-    const KeepEntry* k = a.keep + (size_t)kslot * kKeep;
+    const KeepEntry* k = a.keep + (size_t)kslot * a.keepcap;
     double p = 0.0;
     for (int i = lane; i < n; i += 64)
         if (k[i].idx == d) p = k[i].p;
@@ -450,8 +449,8 @@ __device__ double keep_lookup(const SampArgs& a, int kslot, int n, int d) {
 __device__ int keep_race(const SampArgs& a, int pslot, int np, int qslot, int nq, int b,
                          int pos) {
     const int lane = threadIdx.x & 63;
-    const KeepEntry* kp = a.keep + (size_t)pslot * kKeep;
-    const KeepEntry* kq = qslot >= 0 ? a.keep + (size_t)qslot * kKeep : nullptr;
+    const KeepEntry* kp = a.keep + (size_t)pslot * a.keepcap;
+    const KeepEntry* kq = qslot >= 0 ? a.keep + (size_t)qslot * a.keepcap : nullptr;
     double best = -1.0, fbest = -1.0;
     int bi = kBigIdx, fbi = kBigIdx;
     for (int i = lane; i < np; i += 64) {
@@ -500,20 +499,27 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
     const int nrows = seq_nrows(m);
     uint32_t ebits = 0;
 
-    // ---- A: merge the chunk statistics of every row (one wave per row)
+    // ---- A: merge the chunk statistics of every row (one wave per row; the <= 256 chunk
+    //      entries of a row are loaded once, 4 per lane, all in flight together)
     for (int q = wave; q < nrows; q += 4) {
         const RowRef r = row_ref(a, m, q);
         const bool greedy_row = r.kind == 0 && !m.sampled;
-        float bm = kNegInf, bs = 0.f;
-        float bv = kNegInf;
+        float4 st[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int c = lane + 64 * u;
+            st[u] = c < a.nchunk ? handoff_load4(a.stats + (size_t)r.slot * a.nchunk + c)
+                                 : make_float4(kNegInf, 0.f, kNegInf, __int_as_float(kBigIdx));
+        }
+        float bm = kNegInf, bv = kNegInf;
         int bi = kBigIdx;
-        for (int c = lane; c < a.nchunk; c += 64) {
-            const float4 st = a.stats[(size_t)r.slot * a.nchunk + c];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
             if (greedy_row) {
-                const int ci = __float_as_int(st.w);
-                if (better(st.z, ci, bv, bi)) { bv = st.z; bi = ci; }
+                const int ci = __float_as_int(st[u].w);
+                if (better(st[u].z, ci, bv, bi)) { bv = st[u].z; bi = ci; }
             } else {
-                bm = fmaxf(bm, st.x);
+                bm = fmaxf(bm, st[u].x);
             }
         }
         for (int off = 32; off >= 1; off >>= 1) {
@@ -522,12 +528,13 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
             const int oi = __shfl_xor(bi, off);
             if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
         }
+        // normalizer sum_j 2^((v_j - m) c) over the row, c = log2(e) / T (raw rows: T = 1)
         double z = 0.0;
         if (!greedy_row && bm != kNegInf) {
-            for (int c = lane; c < a.nchunk; c += 64) {
-                const float4 st = a.stats[(size_t)r.slot * a.nchunk + c];
-                if (st.x != kNegInf) z += (double)st.y * exp((double)st.x - (double)bm);
-            }
+            const float cs = r.kind == 2 ? kLog2e : kLog2e / m.temp;
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (st[u].x != kNegInf) z += (double)st[u].y * (double)exp2f((st[u].x - bm) * cs);
             z = wave_sum_d(z);
         }
         if (lane == 0) {
@@ -540,7 +547,6 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
             ri.kept_p = a.vocab;
             rinfo[q] = ri;
         }
-        (void)bs;
     }
     __syncthreads();
 
@@ -554,7 +560,7 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
         int* ccount = fs.ccount[wave];
         bool overflow_risk = false;
         for (int c = lane; c < a.nchunk; c += 64) {
-            const uint2 meta = a.cand_meta[(size_t)r.slot * a.nchunk + c];
+            const uint2 meta = handoff_load_u2(a.cand_meta + (size_t)r.slot * a.nchunk + c);
             ccount[c] = min((int)meta.x, a.capc);
         }
         wave_sync();
@@ -563,10 +569,13 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
         for (int c = lane; c < a.nchunk; c += 64) total += ccount[c];
         total = wave_sum_i(total);
         const int ksel = min(kk, total);
-        if (ksel < 1) continue;
+        if (ksel < 1) {
+            if (lane == 0 && trunc) rinfo[q].kept_k = rinfo[q].kept_p = 0;
+            continue;
+        }
         const uint32_t theta = wave_select_kth(cand, ccount, a.nchunk, a.capc, ksel, fs.hist[wave]);
         for (int c = lane; c < a.nchunk; c += 64) {
-            const uint2 meta = a.cand_meta[(size_t)r.slot * a.nchunk + c];
+            const uint2 meta = handoff_load_u2(a.cand_meta + (size_t)r.slot * a.nchunk + c);
             if ((int)meta.x > a.capc && meta.y == theta) overflow_risk = true;
         }
         const int n_all = wave_collect(cand, ccount, a.nchunk, a.capc, theta, fs.lkey[wave],
@@ -635,7 +644,7 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
             for (int i = lane; i < n_keep; i += 64) fs.lp[wave][i] /= ks;
             wave_sync();
         }
-        KeepEntry* keep = a.keep + (size_t)r.slot * kKeep;
+        KeepEntry* keep = a.keep + (size_t)r.slot * a.keepcap;
         for (int i = lane; i < n_keep; i += 64) {
             KeepEntry e;
             e.idx = fs.lidx[wave][i];
@@ -651,7 +660,7 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
         wave_sync();
     }
     if (tid < m.k) fs.drafts[tid] = a.drafts[m.d0 + tid];
-    __threadfence();
+    __threadfence_block();        // kept lists written above are read by wave 0 below
     __syncthreads();
 
     // ---- C: acceptance (wave 0)
@@ -668,9 +677,30 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
                 ++acc;
             }
             tok = rinfo[acc].argmax;
+            if (tok < 0 || tok >= a.vocab) tok = 0;      // a row with no ordered value
         } else {
-            const int nd = m.k;
             const int base_pos = a.positions[b];
+            // p_{t-1}(d_t) and q_t(d_t) of every draft, one lane per draft, loads in parallel
+            double pd_l = 0.0, qd_l = 0.0;
+            if (lane < m.k) {
+                const int t = lane + 1;
+                const int d = fs.drafts[lane];
+                if (d >= 0 && d < a.vocab) {
+                    if (m.topk) {
+                        // filled below, with the whole wave scanning the kept lists
+                    } else {
+                        int c = a.counts ? a.counts[(size_t)b * a.vocab + d] : 0;
+                        const float xt = a.tl[(size_t)(m.r0 + t - 1) * a.vocab + d];
+                        const float xd = a.dl[(size_t)(m.d0 + t - 1) * a.vocab + d];
+                        for (int s2 = 0; s2 < t - 1; ++s2) c += fs.drafts[s2] == d ? 1 : 0;
+                        const float cs = kLog2e / m.temp;
+                        const float zt = penalize(xt, c, m.pp, m.fp);
+                        pd_l = (double)exp2f((zt - rinfo[t - 1].m) * cs) / rinfo[t - 1].z;
+                        qd_l = (double)exp2f((xd - rinfo[m.rows + t - 1].m) * cs) /
+                               rinfo[m.rows + t - 1].z;
+                    }
+                }
+            }
             bool all = true;
             for (int t = 1; t <= m.k; ++t) {
                 const int pos = base_pos + t - 1;
@@ -686,15 +716,8 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
                         pd = keep_lookup(a, rp.slot, rinfo[pq].kept_p, d);
                         qd = keep_lookup(a, rqr.slot, rinfo[qq].kept_p, d);
                     } else {
-                        int c = a.counts ? a.counts[(size_t)b * a.vocab + d] : 0;
-                        for (int s = 0; s < t - 1; ++s) c += fs.drafts[s] == d ? 1 : 0;
-                        const float z = penalize(a.tl[(size_t)(m.r0 + t - 1) * a.vocab + d], c,
-                                                 m.pp, m.fp);
-                        const double y = (double)__fdiv_rn(z, m.temp);
-                        pd = exp(y - (double)rinfo[pq].m) / rinfo[pq].z;
-                        const double w =
-                            (double)__fdiv_rn(a.dl[(size_t)(m.d0 + t - 1) * a.vocab + d], m.temp);
-                        qd = exp(w - (double)rinfo[qq].m) / rinfo[qq].z;
+                        pd = __shfl(pd_l, t - 1);
+                        qd = __shfl(qd_l, t - 1);
                     }
                 }
                 const uint4 wu = philox_block(a.seed, 0u, (uint32_t)pos, (uint32_t)b, 0u);
@@ -703,6 +726,7 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
                 all = false;
                 if (m.topk) {
                     tok = keep_race(a, rp.slot, rinfo[pq].kept_p, rqr.slot, rinfo[qq].kept_p, b, pos);
+                    if (tok < 0 || tok >= a.vocab) tok = 0;
                 } else {
                     pending = true;
                     rq.kind = 1;
@@ -715,12 +739,12 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
                 }
                 break;
             }
-            (void)nd;
             if (all) {
                 const int pos = base_pos + m.k;
                 const RowRef rp = row_ref(a, m, m.k);
                 if (m.topk) {
                     tok = keep_race(a, rp.slot, rinfo[m.k].kept_p, -1, 0, b, pos);
+                    if (tok < 0 || tok >= a.vocab) tok = 0;
                 } else {
                     pending = true;
                     rq.kind = 2;
@@ -774,7 +798,6 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
         }
         if (ebits && lane == 0) atomicOr(a.err, ebits);
     }
-    if (tid == 0) atomicExch(a.cnt_sweep + b, 0u);
 }
 
 // ------------------------------------------------------------------ sweep kernel
@@ -784,7 +807,6 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
     __shared__ int s_draft[kMaxSeqRows];
     __shared__ uint32_t s_hist[256];
     __shared__ int s_sh[4];
-    __shared__ int s_last;
     __shared__ FinalShared s_final;
     __shared__ RowInfo s_rinfo[3 * kMaxSeqRows];
 
@@ -806,75 +828,91 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
     for (int e = 0; e < kEpt; ++e) valid |= (elem_id(base, e) < a.vocab ? 1u : 0u) << e;
 
     const int nrows = seq_nrows(m);
-    // ---- per-row statistics of this chunk
-    for (int q = 0; q < nrows; ++q) {
-        const RowRef r = row_ref(a, m, q);
-        float x[kEpt];
-        load_chunk<VEC>(row_ptr(a, m, r), base, a.vocab, x);
-        const bool greedy_row = r.kind == 0 && !m.sampled;
-        float v[kEpt];
+    // ---- per-row statistics of this chunk (loads of 8 rows in flight at once)
+    for (int q0 = 0; q0 < nrows; q0 += 8) {
+        float xv[8][kEpt];
 #pragma unroll
-        for (int e = 0; e < kEpt; ++e) {
-            float val = x[e];
-            if (r.kind == 0) {
-                const int cc = row_count(cnt[e], (special >> e) & 1u, s_draft, r.i, elem_id(base, e));
-                val = penalize(val, cc, m.pp, m.fp);
-                if (m.sampled) val = __fdiv_rn(val, m.temp);
-            } else if (r.kind == 1) {
-                val = __fdiv_rn(val, m.temp);
-            }
-            v[e] = ((valid >> e) & 1u) ? val : kNegInf;
-        }
-        float4 res;
-        if (greedy_row) {
-            float bv = kNegInf;
-            int bi = kBigIdx;
+        for (int u = 0; u < 8; ++u)
+            if (q0 + u < nrows) load_chunk<VEC>(row_ptr(a, m, row_ref(a, m, q0 + u)), base,
+                                                a.vocab, xv[u]);
 #pragma unroll
-            for (int e = 0; e < kEpt; ++e)
-                if (((valid >> e) & 1u) && better(v[e], elem_id(base, e), bv, bi)) {
-                    bv = v[e];
-                    bi = elem_id(base, e);
+        for (int u = 0; u < 8; ++u) {
+            const int q = q0 + u;
+            if (q >= nrows) break;
+            const RowRef r = row_ref(a, m, q);
+            const bool greedy_row = r.kind == 0 && !m.sampled;
+            // values: z (penalized target), w (draft) or x (raw); the softmax statistics
+            // are taken as (max v, sum 2^((v - max) c)) with c = log2(e) / T
+            float v[kEpt];
+#pragma unroll
+            for (int e = 0; e < kEpt; ++e) {
+                float val = xv[u][e];
+                if (r.kind == 0) {
+                    const int cc = row_count(cnt[e], (special >> e) & 1u, s_draft, r.i,
+                                             elem_id(base, e));
+                    val = penalize(val, cc, m.pp, m.fp);
                 }
-            for (int off = 32; off >= 1; off >>= 1) {
-                const float ov = __shfl_xor(bv, off);
-                const int oi = __shfl_xor(bi, off);
-                if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+                v[e] = ((valid >> e) & 1u) ? val : kNegInf;
             }
-            res = make_float4(0.f, 0.f, bv, __int_as_float(bi));
-        } else {
-            float mx = kNegInf;
+            float4 res;
+            if (greedy_row) {
+                float bv = kNegInf;
+                int bi = kBigIdx;
 #pragma unroll
-            for (int e = 0; e < kEpt; ++e) mx = fmaxf(mx, v[e]);
-            float s = 0.f;
-            if (mx != kNegInf) {
+                for (int e = 0; e < kEpt; ++e)
+                    if (((valid >> e) & 1u) && better(v[e], elem_id(base, e), bv, bi)) {
+                        bv = v[e];
+                        bi = elem_id(base, e);
+                    }
+                for (int off = 32; off >= 1; off >>= 1) {
+                    const float ov = __shfl_xor(bv, off);
+                    const int oi = __shfl_xor(bi, off);
+                    if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+                }
+                res = make_float4(0.f, 0.f, bv, __int_as_float(bi));
+            } else {
+                const float cs = r.kind == 2 ? kLog2e : kLog2e / m.temp;
+                float mx = kNegInf;
 #pragma unroll
-                for (int e = 0; e < kEpt; ++e) s += (v[e] == kNegInf) ? 0.f : expf(v[e] - mx);
+                for (int e = 0; e < kEpt; ++e) mx = fmaxf(mx, v[e]);
+                for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+                float sm = 0.f;
+                if (mx != kNegInf) {
+#pragma unroll
+                    for (int e = 0; e < kEpt; ++e) sm += exp2f((v[e] - mx) * cs);
+                }
+                for (int off = 32; off >= 1; off >>= 1) sm += __shfl_xor(sm, off);
+                res = make_float4(mx, sm, 0.f, 0.f);
             }
-            for (int off = 32; off >= 1; off >>= 1) {
-                const float om = __shfl_xor(mx, off), os = __shfl_xor(s, off);
-                ms_merge(mx, s, om, os);
-            }
-            res = make_float4(mx, s, 0.f, 0.f);
+            if (lane == 0) s_part[q][wave] = res;
         }
-        if (lane == 0) s_part[q][wave] = res;
     }
     __syncthreads();
     for (int q = tid; q < nrows; q += kThreads) {
         const RowRef r = row_ref(a, m, q);
         const bool greedy_row = r.kind == 0 && !m.sampled;
         float4 acc = s_part[q][0];
-        for (int w = 1; w < 4; ++w) {
-            const float4 o = s_part[q][w];
-            if (greedy_row) {
+        if (greedy_row) {
+            for (int w = 1; w < 4; ++w) {
+                const float4 o = s_part[q][w];
                 if (better(o.z, __float_as_int(o.w), acc.z, __float_as_int(acc.w))) {
                     acc.z = o.z;
                     acc.w = o.w;
                 }
-            } else {
-                ms_merge(acc.x, acc.y, o.x, o.y);
             }
+        } else {
+            const float cs = r.kind == 2 ? kLog2e : kLog2e / m.temp;
+            float mx = acc.x;
+            for (int w = 1; w < 4; ++w) mx = fmaxf(mx, s_part[q][w].x);
+            float sm = 0.f;
+            if (mx != kNegInf)
+                for (int w = 0; w < 4; ++w)
+                    if (s_part[q][w].x != kNegInf)
+                        sm += s_part[q][w].y * exp2f((s_part[q][w].x - mx) * cs);
+            acc.x = mx;
+            acc.y = sm;
         }
-        a.stats[(size_t)r.slot * a.nchunk + c] = acc;
+        handoff_store4(a.stats + (size_t)r.slot * a.nchunk + c, acc);
     }
 
     // ---- candidates for the k-th-largest threshold of truncated / top-n rows
@@ -906,30 +944,29 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
             for (int e = 0; e < kEpt; ++e)
                 if (((valid >> e) & 1u) && key[e] > vk) {
                     const int pos = atomicAdd(&s_sh[2], 1);
-                    out[pos] = make_uint2(key[e], (uint32_t)elem_id(base, e));
+                    handoff_store_u2(out + pos, make_uint2(key[e], (uint32_t)elem_id(base, e)));
                 }
             __syncthreads();
 #pragma unroll
             for (int e = 0; e < kEpt; ++e)
                 if (((valid >> e) & 1u) && key[e] == vk) {
                     const int pos = atomicAdd(&s_sh[2], 1);
-                    if (pos < a.capc) out[pos] = make_uint2(key[e], (uint32_t)elem_id(base, e));
+                    if (pos < a.capc)
+                        handoff_store_u2(out + pos, make_uint2(key[e], (uint32_t)elem_id(base, e)));
                 }
             __syncthreads();
             if (tid == 0)
-                a.cand_meta[(size_t)r.slot * a.nchunk + c] = make_uint2((uint32_t)s_sh[2], vk);
+                handoff_store_u2(a.cand_meta + (size_t)r.slot * a.nchunk + c,
+                                 make_uint2((uint32_t)s_sh[2], vk));
             __syncthreads();
         }
     }
 
-    // ---- the last chunk of the sequence to finish merges and accepts
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = atomicAdd(a.cnt_sweep + b, 1u) == (uint32_t)(a.nchunk - 1);
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    finalize_sequence(a, m, b, s_final, s_rinfo);
+
+    // ---- the last chunk of the sequence to finish merges and accepts (fence-free)
+    __shared__ int s_last;
+    if (handoff_arrive(a.cnt_sweep + b, (uint32_t)a.nchunk, &s_last))
+        finalize_sequence(a, m, b, s_final, s_rinfo);
 }
 
 // ------------------------------------------------------------------ race kernel
@@ -937,15 +974,14 @@ template <bool VEC>
 __global__ __launch_bounds__(kThreads) void race_kernel(const SampArgs a) {
     __shared__ int s_draft[kMaxSeqRows];
     __shared__ float4 s_part[4];
-    __shared__ int s_last;
     const int b = blockIdx.x / a.nchunk, c = blockIdx.x % a.nchunk;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     uint32_t ebits = 0;
     const SeqMode m = seq_mode(a, b, &ebits);
     if (!m.valid || !m.sampled || m.topk) return;
+    if (tid < m.k) s_draft[tid] = a.drafts[m.d0 + tid];   // independent of the request
     const RaceReq rq = a.race[b];
     if (rq.kind == 0) return;
-    if (tid < rq.a) s_draft[tid] = a.drafts[m.d0 + tid];
     __syncthreads();
 
     const int base = c * kChunk;
@@ -957,6 +993,7 @@ __global__ __launch_bounds__(kThreads) void race_kernel(const SampArgs a) {
     if (rq.kind == 1) load_chunk<VEC>(a.dl + (size_t)(m.d0 + rq.a) * a.vocab, base, a.vocab, xq);
     const float inv_zp = (float)(1.0 / rq.z_p);
     const float inv_zq = rq.kind == 1 ? (float)(1.0 / rq.z_q) : 0.f;
+    const float cs = kLog2e / m.temp;
 
     float best = -1.f, fbest = -1.f;
     int bi = kBigIdx, fbi = kBigIdx;
@@ -971,11 +1008,11 @@ __global__ __launch_bounds__(kThreads) void race_kernel(const SampArgs a) {
             const int j = j0 + r;
             if (j >= a.vocab) continue;
             const int cc = row_count(cnt[e], (special >> e) & 1u, s_draft, rq.a, j);
-            const float y = __fdiv_rn(penalize(xp[e], cc, m.pp, m.fp), m.temp);
-            const float p = expf(y - rq.m_p) * inv_zp;
+            const float zp = penalize(xp[e], cc, m.pp, m.fp);
+            const float p = exp2f((zp - rq.m_p) * cs) * inv_zp;
             float rr = p;
             if (rq.kind == 1) {
-                const float q = expf(__fdiv_rn(xq[e], m.temp) - rq.m_q) * inv_zq;
+                const float q = exp2f((xq[e] - rq.m_q) * cs) * inv_zq;
                 rr = fmaxf(0.f, p - q);
             }
             const float ex = -logf(race_u(pick(w, r)));
@@ -1012,19 +1049,16 @@ __global__ __launch_bounds__(kThreads) void race_kernel(const SampArgs a) {
                 acc.w = o.w;
             }
         }
-        a.race_part[(size_t)b * a.nchunk + c] = acc;
+        handoff_store4(a.race_part + (size_t)b * a.nchunk + c, acc);
     }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = atomicAdd(a.cnt_race + b, 1u) == (uint32_t)(a.nchunk - 1);
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
+    // the last chunk to finish picks the winner over all chunks (fence-free hand-off)
+    __shared__ int s_last;
+    if (!handoff_arrive(a.cnt_race + b, (uint32_t)a.nchunk, &s_last)) return;
     if (wave == 0) {
         float bb = -1.f, fb = -1.f;
         int bbi = kBigIdx, fbi2 = kBigIdx;
         for (int cc = lane; cc < a.nchunk; cc += 64) {
-            const float4 o = a.race_part[(size_t)b * a.nchunk + cc];
+            const float4 o = handoff_load4(a.race_part + (size_t)b * a.nchunk + cc);
             const int oi = __float_as_int(o.y), ofi = __float_as_int(o.w);
             if (o.x > bb || (o.x == bb && oi < bbi)) { bb = o.x; bbi = oi; }
             if (o.z > fb || (o.z == fb && ofi < fbi2)) { fb = o.z; fbi2 = ofi; }
@@ -1038,13 +1072,13 @@ __global__ __launch_bounds__(kThreads) void race_kernel(const SampArgs a) {
             if (of > fb || (of == fb && ofi < fbi2)) { fb = of; fbi2 = ofi; }
         }
         if (lane == 0) {
-            const int tok = bb > 0.f ? bbi : fbi2;
+            int tok = bb > 0.f ? bbi : fbi2;
+            if (tok < 0 || tok >= a.vocab) tok = 0;          // a row with no ordered value
             const int grow = m.r0 + rq.a;
             a.out_tokens[grow] = tok;
             if (a.chosen_lp && rq.logprobs)
                 a.chosen_lp[grow] = (float)((double)a.tl[(size_t)grow * a.vocab + tok] -
                                             (double)rq.m_x - log(rq.z_x));
-            atomicExch(a.cnt_race + b, 0u);
         }
     }
 }
@@ -1059,6 +1093,7 @@ SampPlan plan_sample(int B, int total_rows, int V, int max_top_k, int max_top_lp
     if (capc > kChunk) capc = kChunk;
     if (capc > V) capc = V;
     p.capc = capc;
+    p.keepcap = V < kKeep ? V : kKeep;
     p.slots = 3 * total_rows - B;
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     size_t off = 256;
@@ -1075,7 +1110,7 @@ SampPlan plan_sample(int B, int total_rows, int V, int max_top_k, int max_top_lp
     p.off_rows = off;
     off += up((size_t)p.slots * sizeof(RowInfo));
     p.off_keep = off;
-    off += up(max_top_k > 0 ? (size_t)(2 * total_rows - B) * kKeep * sizeof(KeepEntry) : 0);
+    off += up(max_top_k > 0 ? (size_t)(2 * total_rows - B) * p.keepcap * sizeof(KeepEntry) : 0);
     p.off_race = off;
     off += up((size_t)B * sizeof(RaceReq));
     p.off_race_part = off;

@@ -35,6 +35,54 @@ __device__ __forceinline__ void set_device_error(uint32_t* err, uint32_t bit) {
     if (err) atomicOr(err, bit);
 }
 
+// ---------------------------------------------------------------- workgroup hand-off
+// Small results pass from many workgroups to the last one to finish without an
+// agent-scope fence (on gfx950 that fence writes back and then invalidates the whole XCD
+// L2, which costs tens of microseconds when hundreds of workgroups issue it). Instead the
+// values themselves are stored with agent-scope atomic stores (global_store ... sc1:
+// written through to the device-coherent level), every wave waits for its stores to
+// complete (s_waitcnt), and only then is the arrival counter incremented. The last
+// arriving workgroup reads the values with agent-scope atomic loads (global_load ... sc1),
+// which do not hit stale L1/L2 lines.
+__device__ __forceinline__ void handoff_store(float2* p, float2 v) {
+    __hip_atomic_store(reinterpret_cast<unsigned long long*>(p),
+                       *reinterpret_cast<unsigned long long*>(&v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 handoff_load(const float2* p) {
+    unsigned long long u = __hip_atomic_load(
+        reinterpret_cast<unsigned long long*>(const_cast<float2*>(p)), __ATOMIC_RELAXED,
+        __HIP_MEMORY_SCOPE_AGENT);
+    return *reinterpret_cast<float2*>(&u);
+}
+__device__ __forceinline__ void handoff_store4(float4* p, float4 v) {
+    float2* q = reinterpret_cast<float2*>(p);
+    handoff_store(q, make_float2(v.x, v.y));
+    handoff_store(q + 1, make_float2(v.z, v.w));
+}
+__device__ __forceinline__ float4 handoff_load4(const float4* p) {
+    const float2* q = reinterpret_cast<const float2*>(p);
+    const float2 a = handoff_load(q), b = handoff_load(q + 1);
+    return make_float4(a.x, a.y, b.x, b.y);
+}
+
+// Every thread's hand-off stores are complete before thread 0 counts the workgroup in;
+// returns true (in every thread) in the last of `total` workgroups to arrive, which also
+// resets the counter for the next call.
+__device__ __forceinline__ bool handoff_arrive(uint32_t* counter, uint32_t total,
+                                               int* s_flag) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t prev = atomicAdd(counter, 1u);
+        const bool last = prev == total - 1;
+        if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *s_flag = last;
+    }
+    __syncthreads();
+    return *s_flag != 0;
+}
+
 // ---------------------------------------------------------------- attention launch args
 struct AttnArgs {
     const void* q;
@@ -45,7 +93,7 @@ struct AttnArgs {
     float* out;
     float* part_o;          // [units][nsplit][mcap][D]
     float2* part_ml;        // [units][nsplit][mcap]   (running max (log2 units), sum)
-    uint32_t* counters;     // [units]
+    uint32_t* counters;     // [units] arrival counters (zero between calls)
     uint32_t* err;
     int batch, total_rows, hq, hkv, group, d, s_max, max_rows, max_kv_len;
     int nsplit, units, mcap;
@@ -106,7 +154,7 @@ struct SampArgs {
     const vsa_row_params* params;  // [B]
     const int32_t* positions;      // [B]
     uint64_t seed;
-    int batch, total_rows, vocab, max_rows, max_top_k, max_top_lp, nchunk, capc;
+    int batch, total_rows, vocab, max_rows, max_top_k, max_top_lp, nchunk, capc, keepcap;
     int32_t* accepted;
     int32_t* out_tokens;
     float* chosen_lp;
@@ -115,19 +163,19 @@ struct SampArgs {
     float* diag_thr;
     int32_t* diag_kept;
     uint32_t* err;
-    uint32_t* cnt_sweep;           // [B]
+    uint32_t* cnt_sweep;           // [B] arrival counters (zero between calls)
     uint32_t* cnt_race;            // [B]
     float4* stats;                 // [slots][nchunk] (m, s, best value, best id bits)
     uint2* cand;                   // [slots][nchunk][capc] (ordered key, id)
     uint2* cand_meta;              // [slots][nchunk] (count, k-th key)
     RowInfo* rows;                 // [slots]
-    KeepEntry* keep;               // [2T - B][kKeep]
+    KeepEntry* keep;               // [2T - B][keepcap]
     RaceReq* race;                 // [B]
     float4* race_part;             // [B][nchunk]
 };
 
 struct SampPlan {
-    int nchunk, capc, slots;
+    int nchunk, capc, keepcap, slots;
     size_t off_cnt_sweep, off_cnt_race, off_stats, off_cand, off_meta, off_rows, off_keep,
         off_race, off_race_part, bytes;
 };

@@ -232,7 +232,9 @@ def device_tensors(w, device="cuda", with_kv=True):
             torch.from_numpy(np.ascontiguousarray(x)).to(device).view(dtype)
 
     out = {}
-    if w.dtype == BF16:
+    if w.q is None:
+        with_kv = False
+    elif w.dtype == BF16:
         out["q"] = t(w.q.view(np.int16), torch.bfloat16)
         if with_kv:
             out["k_cache"] = t(w.k_cache.view(np.int16), torch.bfloat16)
