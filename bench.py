@@ -160,17 +160,16 @@ def main():
         sample(d)
     torch.cuda.synchronize()
 
-    # One HIP graph per input set holds a whole step (the library only launches kernels on
-    # the given stream; no memsets, no allocations), so replays carry no Python overhead.
-    graphs = []
+    # HIP graphs hold whole steps (the library only launches kernels on the given stream; no
+    # memsets, no allocations): one graph per input set, and one "ring" graph that runs a
+    # step on every set in turn, so step-to-step transitions happen inside a graph.
+    graphs, ring = [], None
     if not args.eager:
-        capture_stream = torch.cuda.Stream()
-        capture_stream.wait_stream(stream)
-        with torch.cuda.stream(capture_stream):
-            for d in sets:
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=capture_stream):
-                    cs = torch.cuda.current_stream()
+        def capture(step_sets):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=capture_stream):
+                cs = torch.cuda.current_stream()
+                for d in step_sets:
                     vsa.verify_attention(d["q"], d["k_cache"], d["v_cache"], d["cu_rows"],
                                          d["ctx_lens"], out, ws_a, max_rows_per_seq=w.max_rows,
                                          max_kv_len=w.max_kv_len, stream=cs)
@@ -179,26 +178,39 @@ def main():
                                              params, d["positions"], 0, acc, toks, ws_s,
                                              max_rows_per_seq=w.max_rows, max_top_k=mtk,
                                              max_top_logprobs=mtl, stream=cs)
-                graphs.append(g)
+            return g
+        capture_stream = torch.cuda.Stream()
+        capture_stream.wait_stream(stream)
+        with torch.cuda.stream(capture_stream):
+            graphs = [capture([d]) for d in sets]
+            ring = capture(sets)
         stream.wait_stream(capture_stream)
-        for i in range(len(graphs)):
-            graphs[i].replay()
+        ring.replay()
+        for g in graphs:
+            g.replay()
         torch.cuda.synchronize()
 
-    def step(i):
+    def run_steps(k):
+        """Exactly k steps, rotating through the input sets."""
+        i = 0
         if graphs:
-            graphs[i % len(graphs)].replay()
+            while k - i >= len(sets):
+                ring.replay()
+                i += len(sets)
+            while i < k:
+                graphs[i % len(graphs)].replay()
+                i += 1
         else:
-            d = sets[i % len(sets)]
-            attention(d)
-            sample(d)
+            for i in range(k):
+                d = sets[i % len(sets)]
+                attention(d)
+                sample(d)
 
     # whole-step timing
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
-    for i in range(args.steps):
-        step(i)
+    run_steps(args.steps)
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / args.steps

@@ -23,6 +23,12 @@ namespace {
 
 constexpr float kNegInf = -__builtin_inff();
 
+#ifndef VSA_ATTN_TARGET_WGS
+#define VSA_ATTN_TARGET_WGS 256      // workgroups the key split aims for (one per CU)
+#endif
+constexpr int kMaxSplits = 32;       // key splits per (sequence, KV head)
+constexpr int kMergeGroup = 8;       // splits whose partials the merge loads in one round
+
 // Block index -> (unit, split). Consecutive block ids go to different XCDs (round-robin
 // dispatch), so units are dealt out across XCDs and all splits of one unit land on one XCD,
 // where the partial states merged at the end stay in that XCD's L2.
@@ -59,65 +65,83 @@ __device__ __forceinline__ SeqGeom seq_geometry(const AttnArgs& a, int b, bool r
 
 // The last split of a unit to finish merges every split's (max, sum, O):
 //   out = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s,   m = max_s m_s.
-// Partials arrive through the fence-free hand-off (agent-scope stores / loads). The
-// (max, sum) pairs of all splits go to LDS in one pass; then each thread sums float4
-// slices of O with the loads of up to 16 splits in flight at once.
-// `w` is LDS scratch of 2 * nsplit * MC floats.
+// Partials arrive through the fence-free hand-off (agent-scope loads, which go to the
+// device-coherent level), so each round trip is expensive: a thread issues the (max, sum)
+// and O loads of every split for all of its output slices in one round, then computes.
+// Empty splits publish m = -inf, l = 0 and O = 0, so no load depends on another.
 template <int D>
-__device__ void attn_merge(const AttnArgs& a, float* w, int unit, int g, const SeqGeom& s,
-                           int MC) {
-    const int tid = threadIdx.x;
+__device__ void attn_merge(const AttnArgs& a, int unit, int g, const SeqGeom& s) {
+    constexpr int D4 = D / 4;
+    constexpr int EPT = 2;                                   // output float4s per thread
+    constexpr int SG = kMergeGroup;                          // splits per round of loads
     const int M = s.rows * a.group;
     const int ns = a.nsplit;
     const size_t base = (size_t)unit * ns;
-    __shared__ float s_inv[128];
-    float* wl = w + ns * MC;
-    for (int e = tid; e < ns * M; e += blockDim.x) {
-        const int sp = e / M, n = e % M;
-        const float2 ml = handoff_load(a.part_ml + (base + sp) * a.mcap + n);
-        w[sp * MC + n] = ml.x;
-        wl[sp * MC + n] = ml.y;
-    }
-    __syncthreads();
-    for (int n = tid; n < M; n += blockDim.x) {
-        float m = kNegInf;
-        for (int sp = 0; sp < ns; ++sp) m = fmaxf(m, w[sp * MC + n]);
-        float l = 0.f;
-        for (int sp = 0; sp < ns; ++sp) {
-            const float ms = w[sp * MC + n];
-            const float f = (ms == kNegInf) ? 0.f : exp2f(ms - m);
-            w[sp * MC + n] = f;
-            l += f * wl[sp * MC + n];
-        }
-        s_inv[n] = 1.f / l;
-    }
-    __syncthreads();
-    constexpr int D4 = D / 4;
     const size_t stride = (size_t)a.mcap * D4;               // float4s between splits
-    for (int e = tid; e < M * D4; e += blockDim.x) {
-        const int n = e / D4, d4 = e % D4;
-        const float4* src = reinterpret_cast<const float4*>(a.part_o) + (base * a.mcap + n) * D4 + d4;
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int sp0 = 0; sp0 < ns; sp0 += 16) {
-            float4 v[16];
+    for (int e0 = threadIdx.x; e0 < M * D4; e0 += EPT * blockDim.x) {
+        float rm[EPT], rl[EPT];
+        float4 racc[EPT];
 #pragma unroll
-            for (int u = 0; u < 16; ++u)
-                v[u] = (sp0 + u < ns && w[(sp0 + u) * MC + n] != 0.f)
-                           ? handoff_load4(src + (size_t)(sp0 + u) * stride)
-                           : make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int x = 0; x < EPT; ++x) {
+            rm[x] = kNegInf;
+            rl[x] = 0.f;
+            racc[x] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        for (int s0 = 0; s0 < ns; s0 += SG) {
+            float2 ml[EPT][SG];
+            float4 v[EPT][SG];
 #pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                const float f = (sp0 + u < ns) ? w[(sp0 + u) * MC + n] : 0.f;
-                acc.x += f * v[u].x;
-                acc.y += f * v[u].y;
-                acc.z += f * v[u].z;
-                acc.w += f * v[u].w;
+            for (int x = 0; x < EPT; ++x) {
+                const int e = e0 + x * blockDim.x;
+                const int n = e / D4, d4 = e % D4;
+                const bool live = e < M * D4;
+                const float4* src =
+                    reinterpret_cast<const float4*>(a.part_o) + (base * a.mcap + n) * D4 + d4;
+#pragma unroll
+                for (int u = 0; u < SG; ++u) {
+                    const int sp = s0 + u;
+                    const bool use = live && sp < ns;
+                    ml[x][u] = use ? handoff_load(a.part_ml + (base + sp) * a.mcap + n)
+                                   : make_float2(kNegInf, 0.f);
+                    v[x][u] = use ? handoff_load4(src + (size_t)sp * stride)
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+            }
+#pragma unroll
+            for (int x = 0; x < EPT; ++x) {
+                float m = rm[x];
+#pragma unroll
+                for (int u = 0; u < SG; ++u) m = fmaxf(m, ml[x][u].x);
+                if (m == kNegInf) continue;
+                const float c = exp2f(rm[x] - m);            // rescale the running state
+                float l = rl[x] * c;
+                float4 acc = make_float4(racc[x].x * c, racc[x].y * c, racc[x].z * c,
+                                         racc[x].w * c);
+#pragma unroll
+                for (int u = 0; u < SG; ++u) {
+                    const float f = (ml[x][u].x == kNegInf) ? 0.f : exp2f(ml[x][u].x - m);
+                    l += f * ml[x][u].y;
+                    acc.x += f * v[x][u].x;
+                    acc.y += f * v[x][u].y;
+                    acc.z += f * v[x][u].z;
+                    acc.w += f * v[x][u].w;
+                }
+                rm[x] = m;
+                rl[x] = l;
+                racc[x] = acc;
             }
         }
-        const float inv = s_inv[n];
-        const int row = s.r0 + n / a.group, head = g * a.group + n % a.group;
-        *reinterpret_cast<float4*>(a.out + ((size_t)row * a.hq + head) * D + 4 * d4) =
-            make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+#pragma unroll
+        for (int x = 0; x < EPT; ++x) {
+            const int e = e0 + x * blockDim.x;
+            if (e >= M * D4) break;
+            const int n = e / D4, d4 = e % D4;
+            const float inv = 1.f / rl[x];
+            const int row = s.r0 + n / a.group, head = g * a.group + n % a.group;
+            *reinterpret_cast<float4*>(a.out + ((size_t)row * a.hq + head) * D + 4 * d4) =
+                make_float4(racc[x].x * inv, racc[x].y * inv, racc[x].z * inv,
+                            racc[x].w * inv);
+        }
     }
 }
 
@@ -181,21 +205,24 @@ __device__ void attn_epilogue(const AttnArgs& a, char* smem, int unit, int split
         handoff_store(a.part_ml + pslot * a.mcap + n, make_float2(wm[n], wl[n]));
     __shared__ int s_last;
     if (handoff_arrive(a.counters + unit, (uint32_t)a.nsplit, &s_last))
-        attn_merge<D>(a, obuf, unit, g, s, MC);
+        attn_merge<D>(a, unit, g, s);
 }
 
-// A split that owns no tile publishes an empty state, which the merge skips, and still
-// counts its arrival.
+// A split that owns no tile publishes an empty state (m = -inf, l = 0, O = 0), which
+// adds nothing in the merge, and still counts its arrival.
 template <int D>
-__device__ void attn_empty_split(const AttnArgs& a, char* smem, int unit, int split, int g,
-                                 const SeqGeom& s, int MC) {
+__device__ void attn_empty_split(const AttnArgs& a, int unit, int split, int g,
+                                 const SeqGeom& s) {
     const int M = s.rows * a.group;
     const size_t pslot = (size_t)unit * a.nsplit + split;
+    for (int e = threadIdx.x; e < M * (D / 4); e += blockDim.x)
+        handoff_store4(reinterpret_cast<float4*>(a.part_o + (pslot * a.mcap) * D) + e,
+                       make_float4(0.f, 0.f, 0.f, 0.f));
     for (int n = threadIdx.x; n < M; n += blockDim.x)
         handoff_store(a.part_ml + pslot * a.mcap + n, make_float2(kNegInf, 0.f));
     __shared__ int s_last;
     if (handoff_arrive(a.counters + unit, (uint32_t)a.nsplit, &s_last))
-        attn_merge<D>(a, reinterpret_cast<float*>(smem), unit, g, s, MC);
+        attn_merge<D>(a, unit, g, s);
 }
 
 // -------------------------------------------------------------------------- bf16 / MFMA
@@ -225,7 +252,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const AttnArgs a) {
     const int t_begin = (int)((long)split * ntiles / a.nsplit);
     const int t_end = (int)((long)(split + 1) * ntiles / a.nsplit);
     if (t_begin >= t_end) {
-        attn_empty_split<D>(a, smem, unit, split, g, s, MC);
+        attn_empty_split<D>(a, unit, split, g, s);
         return;
     }
 
@@ -412,7 +439,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const AttnArgs a) {
     const int t_begin = (int)((long)split * ntiles / a.nsplit);
     const int t_end = (int)((long)(split + 1) * ntiles / a.nsplit);
     if (t_begin >= t_end) {
-        attn_empty_split<D>(a, smem, unit, split, g, s, MC);
+        attn_empty_split<D>(a, unit, split, g, s);
         return;
     }
 
@@ -491,15 +518,11 @@ AttnPlan plan_attention(int B, int Hq, int Hkv, int D, int max_rows, int max_kv_
     p.mcap = 32 * p.nb;
     p.units = B * Hkv;
     p.tile = 128;
-    // Aim for about two resident workgroups per CU (256 CUs), with at least one tile each.
+    // Aim for about VSA_ATTN_TARGET_WGS workgroups over the 256 CUs, at least one tile each.
     const int tiles = (max_kv_len + p.tile - 1) / p.tile;
-    int nsplit = (512 + p.units - 1) / p.units;
+    int nsplit = (VSA_ATTN_TARGET_WGS + p.units - 1) / p.units;
     if (nsplit > tiles) nsplit = tiles;
-    if (nsplit > 64) nsplit = 64;
-    // the merge stages 2 * nsplit * mcap floats in the smallest tile buffer
-    // (bf16, D = 64: 2 * 128 rows * 144 bytes)
-    const int merge_cap = (2 * 128 * (2 * 64 + 16)) / (8 * p.mcap);
-    if (nsplit > merge_cap) nsplit = merge_cap;
+    if (nsplit > kMaxSplits) nsplit = kMaxSplits;
     if (nsplit < 1) nsplit = 1;
     p.nsplit = nsplit;
     size_t off = 256;                                            // error word + pad

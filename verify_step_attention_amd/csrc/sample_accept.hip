@@ -38,6 +38,7 @@ constexpr int kEpt = kChunk / kThreads;        // ids per thread per chunk (8)
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kBigIdx = 0x7FFFFFFF;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kRowBatch = 12;                  // rows whose chunk loads are in flight together
 
 __device__ __forceinline__ void handoff_store_u2(uint2* p, uint2 v) {
     handoff_store(reinterpret_cast<float2*>(p), *reinterpret_cast<float2*>(&v));
@@ -342,10 +343,7 @@ __device__ void wave_sort(uint32_t* lkey, int* lidx, int n) {
     }
 }
 
-__device__ __forceinline__ double wave_sum_d(double v) {
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-    return v;
-}
+__device__ __forceinline__ double wave_sum_d(double v) { return wave_sum_f64(v); }
 __device__ __forceinline__ int wave_min_i(int v) {
     for (int off = 32; off >= 1; off >>= 1) v = min(v, __shfl_xor(v, off));
     return v;
@@ -499,53 +497,62 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
     const int nrows = seq_nrows(m);
     uint32_t ebits = 0;
 
-    // ---- A: merge the chunk statistics of every row (one wave per row; the <= 256 chunk
-    //      entries of a row are loaded once, 4 per lane, all in flight together)
-    for (int q = wave; q < nrows; q += 4) {
-        const RowRef r = row_ref(a, m, q);
-        const bool greedy_row = r.kind == 0 && !m.sampled;
-        float4 st[4];
+    // ---- A: merge the chunk statistics of every row. One wave per row, rows q = wave,
+    //      wave + 4, ...; the (<= 256) chunk entries of up to 3 rows per wave are loaded in
+    //      one round (4 per lane per row).
+    for (int q0 = wave; q0 < nrows; q0 += 12) {
+        float4 st[3][4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int c = lane + 64 * u;
-            st[u] = c < a.nchunk ? handoff_load4(a.stats + (size_t)r.slot * a.nchunk + c)
-                                 : make_float4(kNegInf, 0.f, kNegInf, __int_as_float(kBigIdx));
-        }
-        float bm = kNegInf, bv = kNegInf;
-        int bi = kBigIdx;
+        for (int x = 0; x < 3; ++x) {
+            const int q = q0 + 4 * x;
+            const int slot = q < nrows ? row_ref(a, m, q).slot : 0;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (greedy_row) {
-                const int ci = __float_as_int(st[u].w);
-                if (better(st[u].z, ci, bv, bi)) { bv = st[u].z; bi = ci; }
-            } else {
-                bm = fmaxf(bm, st[u].x);
+            for (int u = 0; u < 4; ++u) {
+                const int c = lane + 64 * u;
+                st[x][u] = (q < nrows && c < a.nchunk)
+                               ? handoff_load4(a.stats + (size_t)slot * a.nchunk + c)
+                               : make_float4(kNegInf, 0.f, kNegInf, __int_as_float(kBigIdx));
             }
         }
-        for (int off = 32; off >= 1; off >>= 1) {
-            bm = fmaxf(bm, __shfl_xor(bm, off));
-            const float ov = __shfl_xor(bv, off);
-            const int oi = __shfl_xor(bi, off);
-            if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-        }
-        // normalizer sum_j 2^((v_j - m) c) over the row, c = log2(e) / T (raw rows: T = 1)
-        double z = 0.0;
-        if (!greedy_row && bm != kNegInf) {
-            const float cs = r.kind == 2 ? kLog2e : kLog2e / m.temp;
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-                if (st[u].x != kNegInf) z += (double)st[u].y * (double)exp2f((st[u].x - bm) * cs);
-            z = wave_sum_d(z);
-        }
-        if (lane == 0) {
-            RowInfo ri{};
-            ri.m = bm;
-            ri.z = z;
-            ri.argmax = bi;
-            ri.theta = kNegInf;
-            ri.kept_k = a.vocab;
-            ri.kept_p = a.vocab;
-            rinfo[q] = ri;
+        for (int x = 0; x < 3; ++x) {
+            const int q = q0 + 4 * x;
+            if (q >= nrows) break;
+            const RowRef r = row_ref(a, m, q);
+            const bool greedy_row = r.kind == 0 && !m.sampled;
+            float bm = kNegInf, bv = kNegInf;
+            int bi = kBigIdx;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (greedy_row) {
+                    const int ci = __float_as_int(st[x][u].w);
+                    if (better(st[x][u].z, ci, bv, bi)) { bv = st[x][u].z; bi = ci; }
+                } else {
+                    bm = fmaxf(bm, st[x][u].x);
+                }
+            }
+            if (greedy_row) wave_argmax(bv, bi);
+            else bm = wave_max(bm);
+            // normalizer sum_j 2^((v_j - m) c) over the row, c = log2(e) / T (raw: T = 1)
+            double z = 0.0;
+            if (!greedy_row && bm != kNegInf) {
+                const float cs = r.kind == 2 ? kLog2e : kLog2e / m.temp;
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (st[x][u].x != kNegInf)
+                        z += (double)st[x][u].y * (double)exp2f((st[x][u].x - bm) * cs);
+                z = wave_sum_d(z);
+            }
+            if (lane == 0) {
+                RowInfo ri{};
+                ri.m = bm;
+                ri.z = z;
+                ri.argmax = bi;
+                ri.theta = kNegInf;
+                ri.kept_k = a.vocab;
+                ri.kept_p = a.vocab;
+                rinfo[q] = ri;
+            }
         }
     }
     __syncthreads();
@@ -816,27 +823,32 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
     const SeqMode m = seq_mode(a, b, &ebits);
     if (c == 0 && tid == 0 && ebits) atomicOr(a.err, ebits);
     if (!m.valid) return;
-    if (tid < m.k) s_draft[tid] = a.drafts[m.d0 + tid];
-    __syncthreads();
-
+    // the draft ids, the counts and the first batch of rows are all requested before any of
+    // them is waited for
+    const int dreg = tid < m.k ? a.drafts[m.d0 + tid] : 0;
     const int base = c * kChunk;
-    const uint32_t special = special_mask(s_draft, m.k, base);
     int cnt[kEpt];
     load_counts<VEC>(a.counts ? a.counts + (size_t)b * a.vocab : nullptr, base, a.vocab, cnt);
+    uint32_t special = 0;
     uint32_t valid = 0;
 #pragma unroll
     for (int e = 0; e < kEpt; ++e) valid |= (elem_id(base, e) < a.vocab ? 1u : 0u) << e;
 
     const int nrows = seq_nrows(m);
-    // ---- per-row statistics of this chunk (loads of 8 rows in flight at once)
-    for (int q0 = 0; q0 < nrows; q0 += 8) {
-        float xv[8][kEpt];
+    // ---- per-row statistics of this chunk (loads of kRowBatch rows in flight at once)
+    for (int q0 = 0; q0 < nrows; q0 += kRowBatch) {
+        float xv[kRowBatch][kEpt];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
+        for (int u = 0; u < kRowBatch; ++u)
             if (q0 + u < nrows) load_chunk<VEC>(row_ptr(a, m, row_ref(a, m, q0 + u)), base,
                                                 a.vocab, xv[u]);
+        if (q0 == 0) {
+            if (tid < m.k) s_draft[tid] = dreg;
+            __syncthreads();
+            special = special_mask(s_draft, m.k, base);
+        }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < kRowBatch; ++u) {
             const int q = q0 + u;
             if (q >= nrows) break;
             const RowRef r = row_ref(a, m, q);
@@ -864,24 +876,22 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
                         bv = v[e];
                         bi = elem_id(base, e);
                     }
-                for (int off = 32; off >= 1; off >>= 1) {
-                    const float ov = __shfl_xor(bv, off);
-                    const int oi = __shfl_xor(bi, off);
-                    if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-                }
+                wave_argmax(bv, bi);
                 res = make_float4(0.f, 0.f, bv, __int_as_float(bi));
             } else {
                 const float cs = r.kind == 2 ? kLog2e : kLog2e / m.temp;
                 float mx = kNegInf;
 #pragma unroll
                 for (int e = 0; e < kEpt; ++e) mx = fmaxf(mx, v[e]);
-                for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+                mx = wave_max(mx);
                 float sm = 0.f;
                 if (mx != kNegInf) {
+                    // arguments are <= 0: the hardware exp2 (v_exp_f32) is exact enough and
+                    // terms below 2^-126 add nothing
 #pragma unroll
-                    for (int e = 0; e < kEpt; ++e) sm += exp2f((v[e] - mx) * cs);
+                    for (int e = 0; e < kEpt; ++e) sm += __builtin_amdgcn_exp2f((v[e] - mx) * cs);
                 }
-                for (int off = 32; off >= 1; off >>= 1) sm += __shfl_xor(sm, off);
+                sm = wave_sum(sm);
                 res = make_float4(mx, sm, 0.f, 0.f);
             }
             if (lane == 0) s_part[q][wave] = res;
@@ -974,28 +984,29 @@ template <bool VEC>
 __global__ __launch_bounds__(kThreads) void race_kernel(const SampArgs a) {
     __shared__ int s_draft[kMaxSeqRows];
     __shared__ float4 s_part[4];
+    __shared__ int s_last;
     const int b = blockIdx.x / a.nchunk, c = blockIdx.x % a.nchunk;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const RaceReq rq = a.race[b];                  // requested with the sequence's shape
     uint32_t ebits = 0;
     const SeqMode m = seq_mode(a, b, &ebits);
-    if (!m.valid || !m.sampled || m.topk) return;
-    if (tid < m.k) s_draft[tid] = a.drafts[m.d0 + tid];   // independent of the request
-    const RaceReq rq = a.race[b];
-    if (rq.kind == 0) return;
-    __syncthreads();
-
+    if (!m.valid || !m.sampled || m.topk || rq.kind == 0) return;
+    const int dreg = tid < m.k ? a.drafts[m.d0 + tid] : 0;
     const int base = c * kChunk;
-    const uint32_t special = special_mask(s_draft, rq.a, base);
     int cnt[kEpt];
     load_counts<VEC>(a.counts ? a.counts + (size_t)b * a.vocab : nullptr, base, a.vocab, cnt);
     float xp[kEpt], xq[kEpt];
     load_chunk<VEC>(a.tl + (size_t)(m.r0 + rq.a) * a.vocab, base, a.vocab, xp);
     if (rq.kind == 1) load_chunk<VEC>(a.dl + (size_t)(m.d0 + rq.a) * a.vocab, base, a.vocab, xq);
+    if (tid < m.k) s_draft[tid] = dreg;
+    __syncthreads();
+    const uint32_t special = special_mask(s_draft, rq.a, base);
     const float inv_zp = (float)(1.0 / rq.z_p);
     const float inv_zq = rq.kind == 1 ? (float)(1.0 / rq.z_q) : 0.f;
     const float cs = kLog2e / m.temp;
 
-    float best = -1.f, fbest = -1.f;
+    // residual race and, in case every residual weight is 0, the race on p itself
+    float best = 0.f, fbest = 0.f;
     int bi = kBigIdx, fbi = kBigIdx;
 #pragma unroll
     for (int qd = 0; qd < 2; ++qd) {
@@ -1026,14 +1037,10 @@ __global__ __launch_bounds__(kThreads) void race_kernel(const SampArgs a) {
             }
         }
     }
-    for (int off = 32; off >= 1; off >>= 1) {
-        const float ob = __shfl_xor(best, off);
-        const int oi = __shfl_xor(bi, off);
-        if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
-        const float fb = __shfl_xor(fbest, off);
-        const int fi = __shfl_xor(fbi, off);
-        if (fb > fbest || (fb == fbest && fi < fbi)) { fbest = fb; fbi = fi; }
-    }
+    wave_argmax(best, bi);
+    wave_argmax(fbest, fbi);
+    // one (key, id, fallback key, fallback id) per chunk, merged by the last chunk to finish
+    // (one slot per workgroup: atomics on a shared winner serialize badly)
     if (lane == 0) s_part[wave] = make_float4(best, __int_as_float(bi), fbest, __int_as_float(fbi));
     __syncthreads();
     if (tid == 0) {
@@ -1051,35 +1058,35 @@ __global__ __launch_bounds__(kThreads) void race_kernel(const SampArgs a) {
         }
         handoff_store4(a.race_part + (size_t)b * a.nchunk + c, acc);
     }
-    // the last chunk to finish picks the winner over all chunks (fence-free hand-off)
-    __shared__ int s_last;
     if (!handoff_arrive(a.cnt_race + b, (uint32_t)a.nchunk, &s_last)) return;
-    if (wave == 0) {
-        float bb = -1.f, fb = -1.f;
+    if (tid < 64) {
+        float bb = 0.f, fb = 0.f;
         int bbi = kBigIdx, fbi2 = kBigIdx;
-        for (int cc = lane; cc < a.nchunk; cc += 64) {
-            const float4 o = handoff_load4(a.race_part + (size_t)b * a.nchunk + cc);
+        float4 part[4];                                   // <= 256 chunks, one round
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int cc = lane + 64 * u;
+            part[u] = cc < a.nchunk ? handoff_load4(a.race_part + (size_t)b * a.nchunk + cc)
+                                    : make_float4(0.f, __int_as_float(kBigIdx), 0.f,
+                                                  __int_as_float(kBigIdx));
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float4 o = part[u];
             const int oi = __float_as_int(o.y), ofi = __float_as_int(o.w);
             if (o.x > bb || (o.x == bb && oi < bbi)) { bb = o.x; bbi = oi; }
             if (o.z > fb || (o.z == fb && ofi < fbi2)) { fb = o.z; fbi2 = ofi; }
         }
-        for (int off = 32; off >= 1; off >>= 1) {
-            const float ob = __shfl_xor(bb, off);
-            const int oi = __shfl_xor(bbi, off);
-            if (ob > bb || (ob == bb && oi < bbi)) { bb = ob; bbi = oi; }
-            const float of = __shfl_xor(fb, off);
-            const int ofi = __shfl_xor(fbi2, off);
-            if (of > fb || (of == fb && ofi < fbi2)) { fb = of; fbi2 = ofi; }
-        }
-        if (lane == 0) {
-            int tok = bb > 0.f ? bbi : fbi2;
-            if (tok < 0 || tok >= a.vocab) tok = 0;          // a row with no ordered value
-            const int grow = m.r0 + rq.a;
-            a.out_tokens[grow] = tok;
-            if (a.chosen_lp && rq.logprobs)
-                a.chosen_lp[grow] = (float)((double)a.tl[(size_t)grow * a.vocab + tok] -
-                                            (double)rq.m_x - log(rq.z_x));
-        }
+        wave_argmax(bb, bbi);
+        wave_argmax(fb, fbi2);
+        if (lane != 0) return;
+        int tok = bb > 0.f ? bbi : fbi2;
+        if (tok < 0 || tok >= a.vocab) tok = 0;          // a row with no ordered value
+        const int grow = m.r0 + rq.a;
+        a.out_tokens[grow] = tok;
+        if (a.chosen_lp && rq.logprobs)
+            a.chosen_lp[grow] = (float)((double)a.tl[(size_t)grow * a.vocab + tok] -
+                                        (double)rq.m_x - log(rq.z_x));
     }
 }
 

@@ -35,6 +35,96 @@ __device__ __forceinline__ void set_device_error(uint32_t* err, uint32_t bit) {
     if (err) atomicOr(err, bit);
 }
 
+// ---------------------------------------------------------------- wave reductions
+// Wave-wide reductions on DPP cross-lane moves (plain VALU ops, no LDS round trip as with
+// ds_bpermute): swap neighbours, swap pairs, mirror within 8, mirror within 16 (now every
+// lane of each 16-lane row holds the row's result), then row_bcast:15 / row_bcast:31 fold
+// the rows into lane 63, which is read back as a wave-uniform value.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ float dpp_f(float old, float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v),
+                                                      CTRL, ROWS, 0xF, false));
+}
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ int dpp_i(int old, int v) {
+    return __builtin_amdgcn_update_dpp(old, v, CTRL, ROWS, 0xF, false);
+}
+constexpr int kDppSwap1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppSwap2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+constexpr int kDppBcast15 = 0x142;
+constexpr int kDppBcast31 = 0x143;
+
+__device__ __forceinline__ float readlane63(float x) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+    x = fmaxf(x, dpp_f<kDppSwap1>(x, x));
+    x = fmaxf(x, dpp_f<kDppSwap2>(x, x));
+    x = fmaxf(x, dpp_f<kDppHalfMirror>(x, x));
+    x = fmaxf(x, dpp_f<kDppMirror>(x, x));
+    x = fmaxf(x, dpp_f<kDppBcast15, 0xA>(x, x));
+    x = fmaxf(x, dpp_f<kDppBcast31, 0xC>(x, x));
+    return readlane63(x);
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+    x += dpp_f<kDppSwap1>(0.f, x);
+    x += dpp_f<kDppSwap2>(0.f, x);
+    x += dpp_f<kDppHalfMirror>(0.f, x);
+    x += dpp_f<kDppMirror>(0.f, x);
+    x += dpp_f<kDppBcast15, 0xA>(0.f, x);
+    x += dpp_f<kDppBcast31, 0xC>(0.f, x);
+    return readlane63(x);
+}
+
+// (value, id) with the larger value, ties to the lower id; result in every lane
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ void argmax_step(float& v, int& i) {
+    const float ov = dpp_f<CTRL, ROWS>(v, v);
+    const int oi = dpp_i<CTRL, ROWS>(i, i);
+    if (ov > v || (ov == v && oi < i)) {
+        v = ov;
+        i = oi;
+    }
+}
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+    argmax_step<kDppSwap1>(v, i);
+    argmax_step<kDppSwap2>(v, i);
+    argmax_step<kDppHalfMirror>(v, i);
+    argmax_step<kDppMirror>(v, i);
+    argmax_step<kDppBcast15, 0xA>(v, i);
+    argmax_step<kDppBcast31, 0xC>(v, i);
+    v = readlane63(v);
+    i = __builtin_amdgcn_readlane(i, 63);
+}
+
+__device__ __forceinline__ double wave_sum_f64(double x) {
+    // 64-bit values move as two 32-bit halves
+#define VSA_DPP_F64(CTRL, ROWS)                                                             \
+    {                                                                                       \
+        const unsigned long long u = __double_as_longlong(x);                              \
+        const int lo = __builtin_amdgcn_update_dpp(0, (int)(u & 0xFFFFFFFFull), CTRL, ROWS, \
+                                                   0xF, false);                            \
+        const int hi = __builtin_amdgcn_update_dpp(0, (int)(u >> 32), CTRL, ROWS, 0xF,       \
+                                                   false);                                 \
+        x += __longlong_as_double(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo); \
+    }
+    VSA_DPP_F64(kDppSwap1, 0xF)
+    VSA_DPP_F64(kDppSwap2, 0xF)
+    VSA_DPP_F64(kDppHalfMirror, 0xF)
+    VSA_DPP_F64(kDppMirror, 0xF)
+    VSA_DPP_F64(kDppBcast15, 0xA)
+    VSA_DPP_F64(kDppBcast31, 0xC)
+#undef VSA_DPP_F64
+    const unsigned long long u = __double_as_longlong(x);
+    const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(u & 0xFFFFFFFFull), 63);
+    const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(u >> 32), 63);
+    return __longlong_as_double(((unsigned long long)hi << 32) | lo);
+}
+
 // ---------------------------------------------------------------- workgroup hand-off
 // Small results pass from many workgroups to the last one to finish without an
 // agent-scope fence (on gfx950 that fence writes back and then invalidates the whole XCD
@@ -171,7 +261,7 @@ struct SampArgs {
     RowInfo* rows;                 // [slots]
     KeepEntry* keep;               // [2T - B][keepcap]
     RaceReq* race;                 // [B]
-    float4* race_part;             // [B][nchunk]
+    float4* race_part;             // [B][nchunk] per-chunk race winners
 };
 
 struct SampPlan {
