@@ -92,7 +92,77 @@ def cpu_baseline(w, budget_s=12.0):
                       f"BLAS threads = {cores}"}
 
 
+def _counter_rows(d, counter):
+    """Per-kernel values of one rocprofv3 --pmc counter (KiB per dispatch) under folder d."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    out = {}
+    with open(files[0]) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def record_traffic(fetch_dir, write_dir, copy_mib, command):
+    """Turn two rocprofv3 --pmc runs of `bench.py --eager --copy-probe-mib M` (FETCH_SIZE, then
+    WRITE_SIZE) into bytes per attention launch. Each counter is scaled by what it reads for
+    the plain copy of M MiB that the run starts with (read M MiB, write M MiB)."""
+    fetch = _counter_rows(fetch_dir, "FETCH_SIZE")
+    write = _counter_rows(write_dir, "WRITE_SIZE")
+    copy_bytes = copy_mib << 20
+    copy_k = max((k for k in fetch if "copy" in k.lower()), key=lambda k: max(fetch[k]))
+    f_scale = max(fetch[copy_k]) * 1024 / copy_bytes
+    w_scale = max(write[copy_k]) * 1024 / copy_bytes
+    kernels = {}
+    for k in fetch:
+        if "vsa::" not in k:
+            continue
+        fb = float(np.median(fetch[k])) * 1024 / f_scale
+        wb = float(np.median(write.get(k, [0.0]))) * 1024 / w_scale
+        kernels[k] = {"fetch_bytes": round(fb), "write_bytes": round(wb),
+                      "dispatches": len(fetch[k])}
+    attn = [k for k in kernels if "attn_bf16_kernel" in k]
+    if len(attn) != 1:
+        raise SystemExit(f"expected one attention kernel in the counters, found {attn}")
+    a = kernels[attn[0]]
+    with open(ATTN_SRC, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    rec = {"command": command, "copy_probe_mib": copy_mib,
+           "copy_fetch_scale": round(f_scale, 4), "copy_write_scale": round(w_scale, 4),
+           "attention_source_sha256": digest,
+           "bytes_per_launch": a["fetch_bytes"] + a["write_bytes"], "kernels": kernels}
+    with open(COUNTERS, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
+def summarize_stats(path, command):
+    """Markdown table of a rocprofv3 --kernel-trace --stats kernel_stats.csv."""
+    import csv
+    print(f"command: `{command}`\n")
+    print("| kernel | calls | avg us | min us | max us | share % |")
+    print("|---|---|---|---|---|---|")
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            name = r["Name"] if len(r["Name"]) <= 90 else r["Name"][:87] + "..."
+            print(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                  f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                  f"{float(r['Percentage']):.1f} |")
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--record-traffic":
+        # bench.py --record-traffic FETCH_DIR WRITE_DIR COPY_MIB "<command>"
+        record_traffic(sys.argv[2], sys.argv[3], int(sys.argv[4]), sys.argv[5])
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-stats":
+        # bench.py --summarize-stats KERNEL_STATS_CSV "<command>"
+        summarize_stats(sys.argv[2], sys.argv[3])
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
@@ -136,16 +206,16 @@ def main():
     toks = torch.empty(w.total_rows, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def attention(d):
+    def attention(d, s=None):
         vsa.verify_attention(d["q"], d["k_cache"], d["v_cache"], d["cu_rows"], d["ctx_lens"],
                              out, ws_a, max_rows_per_seq=w.max_rows, max_kv_len=w.max_kv_len,
-                             stream=stream)
+                             stream=stream if s is None else s)
 
-    def sample(d):
+    def sample(d, s=None):
         vsa.verify_sample_accept(d["target_logits"], d["draft_logits"], d["draft_tokens"],
                                  d["cu_rows"], d["token_counts"], params, d["positions"], 0,
                                  acc, toks, ws_s, max_rows_per_seq=w.max_rows, max_top_k=mtk,
-                                 max_top_logprobs=mtl, stream=stream)
+                                 max_top_logprobs=mtl, stream=stream if s is None else s)
 
     if args.copy_probe_mib:
         src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device="cuda")
@@ -170,14 +240,8 @@ def main():
             with torch.cuda.graph(g, stream=capture_stream):
                 cs = torch.cuda.current_stream()
                 for d in step_sets:
-                    vsa.verify_attention(d["q"], d["k_cache"], d["v_cache"], d["cu_rows"],
-                                         d["ctx_lens"], out, ws_a, max_rows_per_seq=w.max_rows,
-                                         max_kv_len=w.max_kv_len, stream=cs)
-                    vsa.verify_sample_accept(d["target_logits"], d["draft_logits"],
-                                             d["draft_tokens"], d["cu_rows"], d["token_counts"],
-                                             params, d["positions"], 0, acc, toks, ws_s,
-                                             max_rows_per_seq=w.max_rows, max_top_k=mtk,
-                                             max_top_logprobs=mtl, stream=cs)
+                    attention(d, cs)
+                    sample(d, cs)
             return g
         capture_stream = torch.cuda.Stream()
         capture_stream.wait_stream(stream)
@@ -217,19 +281,49 @@ def main():
     print(f"[bench] {args.steps} steps timed ({'eager' if not graphs else 'graph replay'}): "
           f"{ms_step * 1e3:.2f} us/step", file=sys.stderr, flush=True)
 
-    # per-kernel timing: events around each call, on the launch stream
-    n_k = min(args.steps, 100)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_k)]
-    for i in range(n_k):
-        d = sets[i % len(sets)]
-        ev[i][0].record(stream)
-        attention(d)
-        ev[i][1].record(stream)
-        sample(d)
-        ev[i][2].record(stream)
+    # per-kernel timing on the launch stream. Graph mode: one graph per stage that runs that
+    # stage on every input set in turn, replayed back to back between two HIP events (the
+    # same launch sequence as the steps, minus the other stage). Eager mode: events around
+    # each call.
+    if graphs:
+        def stage_graph(fn):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(capture_stream):
+                with torch.cuda.graph(g, stream=capture_stream):
+                    for d in sets:
+                        fn(d, torch.cuda.current_stream())
+            stream.wait_stream(capture_stream)
+            return g
+        g_att = stage_graph(lambda d, s: attention(d, s))
+        g_smp = stage_graph(lambda d, s: sample(d, s))
+        reps = max(1, args.steps // len(sets))
+
+        def time_graph(g):
+            g.replay()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            per = []
+            for _ in range(reps):
+                e0.record(stream)
+                g.replay()
+                e1.record(stream)
+                e1.synchronize()
+                per.append(e0.elapsed_time(e1) / len(sets))
+            return np.array(per)
+        attn_ms, samp_ms = time_graph(g_att), time_graph(g_smp)
+    else:
+        n_k = min(args.steps, 100)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_k)]
+        for i in range(n_k):
+            d = sets[i % len(sets)]
+            ev[i][0].record(stream)
+            attention(d)
+            ev[i][1].record(stream)
+            sample(d)
+            ev[i][2].record(stream)
+        torch.cuda.synchronize()
+        attn_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+        samp_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
     torch.cuda.synchronize()
-    attn_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
-    samp_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
     err_a = int(ws_a[:4].view(torch.int32).item())
     err_s = int(ws_s[:4].view(torch.int32).item())
     if err_a or err_s:
