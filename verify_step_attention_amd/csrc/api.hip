@@ -68,7 +68,6 @@ vsa_status verify_attention(const void* q, const void* k_cache, const void* v_ca
     a.out = out;
     a.part_o = reinterpret_cast<float*>(ws + plan.off_o);
     a.part_ml = reinterpret_cast<float2*>(ws + plan.off_ml);
-    a.counters = reinterpret_cast<uint32_t*>(ws + plan.off_counters);
     a.err = reinterpret_cast<uint32_t*>(ws);
     a.batch = B;
     a.total_rows = total_rows;

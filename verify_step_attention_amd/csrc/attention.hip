@@ -26,8 +26,10 @@ constexpr float kNegInf = -__builtin_inff();
 #ifndef VSA_ATTN_TARGET_WGS
 #define VSA_ATTN_TARGET_WGS 256      // workgroups the key split aims for (one per CU)
 #endif
+constexpr int kThreads = 256;        // threads per workgroup (every kernel here; a constant,
+                                     // so loops do not load the size from the dispatch packet)
 constexpr int kMaxSplits = 32;       // key splits per (sequence, KV head)
-constexpr int kMergeGroup = 8;       // splits whose partials the merge loads in one round
+constexpr int kMergeGroup = 8;       // splits whose partials a merge thread loads together
 
 // Block index -> (unit, split). Consecutive block ids go to different XCDs (round-robin
 // dispatch), so units are dealt out across XCDs and all splits of one unit land on one XCD,
@@ -63,106 +65,42 @@ __device__ __forceinline__ SeqGeom seq_geometry(const AttnArgs& a, int b, bool r
     return s;
 }
 
-// The last split of a unit to finish merges every split's (max, sum, O):
-//   out = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s,   m = max_s m_s.
-// Partials arrive through the fence-free hand-off (agent-scope loads, which go to the
-// device-coherent level), so each round trip is expensive: a thread issues the (max, sum)
-// and O loads of every split for all of its output slices in one round, then computes.
-// Empty splits publish m = -inf, l = 0 and O = 0, so no load depends on another.
-template <int D>
-__device__ void attn_merge(const AttnArgs& a, int unit, int g, const SeqGeom& s) {
-    constexpr int D4 = D / 4;
-    constexpr int EPT = 2;                                   // output float4s per thread
-    constexpr int SG = kMergeGroup;                          // splits per round of loads
-    const int M = s.rows * a.group;
-    const int ns = a.nsplit;
-    const size_t base = (size_t)unit * ns;
-    const size_t stride = (size_t)a.mcap * D4;               // float4s between splits
-    for (int e0 = threadIdx.x; e0 < M * D4; e0 += EPT * blockDim.x) {
-        float rm[EPT], rl[EPT];
-        float4 racc[EPT];
-#pragma unroll
-        for (int x = 0; x < EPT; ++x) {
-            rm[x] = kNegInf;
-            rl[x] = 0.f;
-            racc[x] = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-        for (int s0 = 0; s0 < ns; s0 += SG) {
-            float2 ml[EPT][SG];
-            float4 v[EPT][SG];
-#pragma unroll
-            for (int x = 0; x < EPT; ++x) {
-                const int e = e0 + x * blockDim.x;
-                const int n = e / D4, d4 = e % D4;
-                const bool live = e < M * D4;
-                const float4* src =
-                    reinterpret_cast<const float4*>(a.part_o) + (base * a.mcap + n) * D4 + d4;
-#pragma unroll
-                for (int u = 0; u < SG; ++u) {
-                    const int sp = s0 + u;
-                    const bool use = live && sp < ns;
-                    ml[x][u] = use ? handoff_load(a.part_ml + (base + sp) * a.mcap + n)
-                                   : make_float2(kNegInf, 0.f);
-                    v[x][u] = use ? handoff_load4(src + (size_t)sp * stride)
-                                  : make_float4(0.f, 0.f, 0.f, 0.f);
-                }
-            }
-#pragma unroll
-            for (int x = 0; x < EPT; ++x) {
-                float m = rm[x];
-#pragma unroll
-                for (int u = 0; u < SG; ++u) m = fmaxf(m, ml[x][u].x);
-                if (m == kNegInf) continue;
-                const float c = exp2f(rm[x] - m);            // rescale the running state
-                float l = rl[x] * c;
-                float4 acc = make_float4(racc[x].x * c, racc[x].y * c, racc[x].z * c,
-                                         racc[x].w * c);
-#pragma unroll
-                for (int u = 0; u < SG; ++u) {
-                    const float f = (ml[x][u].x == kNegInf) ? 0.f : exp2f(ml[x][u].x - m);
-                    l += f * ml[x][u].y;
-                    acc.x += f * v[x][u].x;
-                    acc.y += f * v[x][u].y;
-                    acc.z += f * v[x][u].z;
-                    acc.w += f * v[x][u].w;
-                }
-                rm[x] = m;
-                rl[x] = l;
-                racc[x] = acc;
-            }
-        }
-#pragma unroll
-        for (int x = 0; x < EPT; ++x) {
-            const int e = e0 + x * blockDim.x;
-            if (e >= M * D4) break;
-            const int n = e / D4, d4 = e % D4;
-            const float inv = 1.f / rl[x];
-            const int row = s.r0 + n / a.group, head = g * a.group + n % a.group;
-            *reinterpret_cast<float4*>(a.out + ((size_t)row * a.hq + head) * D + 4 * d4) =
-                make_float4(racc[x].x * inv, racc[x].y * inv, racc[x].z * inv,
-                            racc[x].w * inv);
-        }
+// Workgroup statistics of the epilogue, in LDS: kStatCap floats each of
+//   gm[KGX][MC] key-group running max (log2 units) | gl[KGX][MC] key-group sum
+//   | fac[KGX][MC] factor 2^(m_kg - m_wg) | wm[MC] workgroup max | wl[MC] workgroup sum
+constexpr int kStatCap = 128;
+constexpr int kStatFloats = 5 * kStatCap;
+
+// Four LDS regions, picked by a runtime index (an array of LDS pointers would become a
+// static initializer, which the target does not support).
+struct LdsQuad {
+    float* p0;
+    float* p1;
+    float* p2;
+    float* p3;
+    __device__ __forceinline__ float* operator[](int i) const {
+        return i == 0 ? p0 : i == 1 ? p1 : i == 2 ? p2 : p3;
     }
-}
+};
 
 // Combines the key groups of one workgroup and writes either the final output (single
-// split) or this split's partial state.
-//   obuf[(kg * MC + n) * D + d]  unnormalized O of key group kg (relative to its own max)
-//   gm[kg * MC + n], gl[...]     that group's running max (log2 units) and sum
-// with gm = obuf + KGX * MC * D and gl = gm + KGX * MC.
-template <int D, int KGX>
-__device__ void attn_epilogue(const AttnArgs& a, char* smem, int unit, int split, int g,
-                              const SeqGeom& s, int MC) {
+// split) or this split's partial state (O relative to the split's max, unnormalized; max in
+// log2 units; sum), which the merge kernel combines after this kernel. The O of key group k
+// (relative to its own max) for columns 32 j .. 32 j + 31 is at ob[k * NBX + j], rows OS
+// floats apart.
+template <int D, int KGX, int NBX>
+__device__ void attn_epilogue(const AttnArgs& a, LdsQuad ob, float* st, int unit, int split,
+                              int g, const SeqGeom& s, int OS) {
     const int tid = threadIdx.x;
     const int M = s.rows * a.group;
-    float* obuf = reinterpret_cast<float*>(smem);
-    float* gm = obuf + KGX * MC * D;
-    float* gl = gm + KGX * MC;
-    float* fac = gl + KGX * MC;          // [KGX][MC] factor 2^(m_kg - m_wg)
-    float* wm = fac + KGX * MC;          // [MC] workgroup max
-    float* wl = wm + MC;                 // [MC] workgroup sum
+    const int MC = a.mcap;
+    float* gm = st;
+    float* gl = st + kStatCap;
+    float* fac = st + 2 * kStatCap;
+    float* wm = st + 3 * kStatCap;
+    float* wl = st + 4 * kStatCap;
 
-    for (int n = tid; n < M; n += blockDim.x) {
+    for (int n = tid; n < M; n += kThreads) {
         float m = kNegInf;
         for (int k = 0; k < KGX; ++k) m = fmaxf(m, gm[k * MC + n]);
         float l = 0.f;
@@ -177,86 +115,150 @@ __device__ void attn_epilogue(const AttnArgs& a, char* smem, int unit, int split
     }
     __syncthreads();
 
-    if (a.nsplit == 1) {
-        for (int e = tid; e < M * D; e += blockDim.x) {
-            const int n = e / D, d = e % D;
-            float o = 0.f;
-            for (int k = 0; k < KGX; ++k) o += fac[k * MC + n] * obuf[(k * MC + n) * D + d];
-            const int row = s.r0 + n / a.group, head = g * a.group + n % a.group;
-            a.out[((size_t)row * a.hq + head) * D + d] = o / wl[n];
-        }
-        return;
-    }
     const size_t pslot = (size_t)unit * a.nsplit + split;
-    for (int e = tid; e < M * (D / 4); e += blockDim.x) {
+    for (int e = tid; e < M * (D / 4); e += kThreads) {
         const int n = e / (D / 4), d = 4 * (e % (D / 4));
         float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
         for (int k = 0; k < KGX; ++k) {
             const float f = fac[k * MC + n];
-            const float4 v = *reinterpret_cast<const float4*>(obuf + (k * MC + n) * D + d);
+            const float4 v = *reinterpret_cast<const float4*>(ob[k * NBX + (n >> 5)] +
+                                                              (n & 31) * OS + d);
             o.x += f * v.x;
             o.y += f * v.y;
             o.z += f * v.z;
             o.w += f * v.w;
         }
-        handoff_store4(reinterpret_cast<float4*>(a.part_o + (pslot * a.mcap + n) * D + d), o);
+        if (a.nsplit == 1) {
+            const float il = 1.f / wl[n];
+            const int row = s.r0 + n / a.group, head = g * a.group + n % a.group;
+            *reinterpret_cast<float4*>(a.out + ((size_t)row * a.hq + head) * D + d) =
+                make_float4(o.x * il, o.y * il, o.z * il, o.w * il);
+        } else {
+            *reinterpret_cast<float4*>(a.part_o + (pslot * a.mcap + n) * D + d) = o;
+        }
     }
-    for (int n = tid; n < M; n += blockDim.x)
-        handoff_store(a.part_ml + pslot * a.mcap + n, make_float2(wm[n], wl[n]));
-    __shared__ int s_last;
-    if (handoff_arrive(a.counters + unit, (uint32_t)a.nsplit, &s_last))
-        attn_merge<D>(a, unit, g, s);
+    if (a.nsplit == 1) return;
+    for (int n = tid; n < M; n += kThreads)
+        a.part_ml[pslot * a.mcap + n] = make_float2(wm[n], wl[n]);
 }
 
 // A split that owns no tile publishes an empty state (m = -inf, l = 0, O = 0), which
-// adds nothing in the merge, and still counts its arrival.
+// adds nothing in the merge.
 template <int D>
-__device__ void attn_empty_split(const AttnArgs& a, int unit, int split, int g,
-                                 const SeqGeom& s) {
+__device__ void attn_empty_split(const AttnArgs& a, int unit, int split, const SeqGeom& s) {
     const int M = s.rows * a.group;
     const size_t pslot = (size_t)unit * a.nsplit + split;
-    for (int e = threadIdx.x; e < M * (D / 4); e += blockDim.x)
-        handoff_store4(reinterpret_cast<float4*>(a.part_o + (pslot * a.mcap) * D) + e,
-                       make_float4(0.f, 0.f, 0.f, 0.f));
-    for (int n = threadIdx.x; n < M; n += blockDim.x)
-        handoff_store(a.part_ml + pslot * a.mcap + n, make_float2(kNegInf, 0.f));
-    __shared__ int s_last;
-    if (handoff_arrive(a.counters + unit, (uint32_t)a.nsplit, &s_last))
-        attn_merge<D>(a, unit, g, s);
+    for (int e = threadIdx.x; e < M * (D / 4); e += kThreads)
+        reinterpret_cast<float4*>(a.part_o + (pslot * a.mcap) * D)[e] =
+            make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int n = threadIdx.x; n < M; n += kThreads)
+        a.part_ml[pslot * a.mcap + n] = make_float2(kNegInf, 0.f);
 }
 
 // -------------------------------------------------------------------------- bf16 / MFMA
+// K/V tiles of TK keys go straight from HBM into LDS (global_load_lds_dwordx4: lane l of a
+// wave writes bytes [16 l, 16 l + 16) of the wave's 1 KB destination block), two buffers
+// deep: while the waves compute on one tile, the next one is in flight. Rows are stored
+// unpadded, so the 16-byte chunks of row r are permuted (chunk c at position c ^ swz(r))
+// to keep both LDS read patterns free of bank conflicts:
+//   QK^T A operand: 16 lanes read one chunk of 16 consecutive rows  -> swz bijective on
+//                   16 consecutive rows;
+//   V^T (ds_read_b64_tr_b16): 32 lanes read 4 chunks of 4 consecutive rows -> the 4 rows
+//                   map the 4 chunks to different 64-byte blocks of the bank space.
+// A row of D = 128 bf16 is 256 bytes (all 64 banks); D = 64 packs two rows per bank span.
+template <int D>
+__device__ __forceinline__ int kv_swz(int r) {
+    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
 template <int D, int NB>
-__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const AttnArgs a) {
-    constexpr int TK = 128;                  // keys per workgroup tile
-    constexpr int ROWB = D * 2 + 16;         // LDS row stride in bytes (bank-spread padding)
+__global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const AttnArgs a) {
+    constexpr int TK = 128;                  // keys per tile
+    constexpr int ROWB = D * 2;              // LDS bytes per key row
+    constexpr int CH = ROWB / 16;            // 16-byte chunks per row
+    constexpr int RPI = 1024 / ROWB;         // rows per 1 KB wave DMA block
+    constexpr int BLOCKS = TK * ROWB / 1024; // DMA blocks per matrix tile
+    constexpr int BPW = BLOCKS / 4;          // ... per wave
+    constexpr int TILEB = TK * ROWB;         // bytes of one matrix tile
     constexpr int KSTEPS = D / 16;           // k-steps of QK^T
     constexpr int DB = D / 32;               // 32-wide d blocks of PV
     constexpr int KG = 4 / NB;               // key groups (waves sharing a column block)
-    constexpr int CHUNKS = D * 2 / 16;       // 16-byte chunks per K/V row
-    constexpr int RPP = 256 / CHUNKS;        // rows staged per pass
-    constexpr int PASSES = TK / RPP;
-    constexpr int MC = 32 * NB;
-    __shared__ __attribute__((aligned(16))) char smem[2 * TK * ROWB];
+    constexpr int OS = D + 4;                // epilogue row stride (floats)
+    static_assert(32 * OS * 4 <= TILEB, "a wave's O fits in one tile buffer");
+    static_assert(BLOCKS % 4 == 0, "whole DMA blocks per wave");
+    // Two tile buffers (K, V each) as four distinct LDS objects: the compiler then knows
+    // that the DMA into one buffer does not alias the reads of the other and does not wait
+    // for it before computing.
+    __shared__ __attribute__((aligned(1024))) char k0s[TILEB];
+    __shared__ __attribute__((aligned(1024))) char v0s[TILEB];
+    __shared__ __attribute__((aligned(1024))) char k1s[TILEB];
+    __shared__ __attribute__((aligned(1024))) char v1s[TILEB];
+    __shared__ float stats[kStatFloats];
 
     int unit, split;
     map_block(blockIdx.x, a.units, a.nsplit, &unit, &split);
     if (unit >= a.units) return;
     const int b = unit / a.hkv, g = unit % a.hkv;
     const int tid = threadIdx.x;
-    const SeqGeom s = seq_geometry(a, b, tid == 0 && split == 0 && g == 0);
-    if (!s.ok) return;
+    const int wave = tid >> 6, lane = tid & 63;
+    const size_t kv_off = ((size_t)b * a.hkv + g) * (size_t)a.s_max * D;
+    const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k) + kv_off;
+    const uint16_t* vbase = reinterpret_cast<const uint16_t*>(a.v) + kv_off;
 
+    // DMA of tile t: wave w fills blocks w, w + 4, ... of K and of V (so a wave only ever
+    // waits for its own blocks). Keys at or past key_lim read key key_lim - 1.
+    const int dma_ri = lane / CH, dma_pos = lane % CH;
+    int key_lim;
+    auto issue_tile = [&](int t, char* kt, char* vt) {
+#pragma unroll
+        for (int i = 0; i < BPW; ++i) {
+            const int blk = i * 4 + wave;
+            const int r = blk * RPI + dma_ri;
+            int key = t * TK + r;
+            key = key < key_lim ? key : key_lim - 1;
+            const size_t src = (size_t)key * D + (size_t)((dma_pos ^ kv_swz<D>(r)) * 8);
+            __builtin_amdgcn_global_load_lds(kbase + src, (lds_void*)(kt + blk * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vbase + src, (lds_void*)(vt + blk * 1024), 16, 0, 0);
+        }
+    };
+    // The first tile is requested before the sequence geometry arrives, as if the sequence
+    // held all kv_cap keys (the split's first tile is then the same whenever the sequence
+    // spans as many tiles as kv_cap). Rows past the true end are fixed up below.
+    const int kv_cap = a.max_kv_len < a.s_max ? a.max_kv_len : a.s_max;
+    const int t_spec = (int)((long)split * ((kv_cap + TK - 1) / TK) / a.nsplit);
+    key_lim = kv_cap;
+    issue_tile(t_spec, k0s, v0s);
+
+    const SeqGeom s = seq_geometry(a, b, tid == 0 && split == 0 && g == 0);
+    if (!s.ok) {
+        __builtin_amdgcn_s_waitcnt(0);                 // no DMA outlives the workgroup
+        return;
+    }
     const int L = s.ctx + s.rows;                      // keys of this sequence
     const int ntiles = (L + TK - 1) / TK;
     const int t_begin = (int)((long)split * ntiles / a.nsplit);
     const int t_end = (int)((long)(split + 1) * ntiles / a.nsplit);
+    key_lim = L;
     if (t_begin >= t_end) {
-        attn_empty_split<D>(a, unit, split, g, s);
+        __builtin_amdgcn_s_waitcnt(0);                 // no DMA outlives the workgroup
+        attn_empty_split<D>(a, unit, split, s);
         return;
     }
+    if (t_begin != t_spec) {
+        __builtin_amdgcn_s_waitcnt(0);                 // this wave's blocks are free again
+        issue_tile(t_begin, k0s, v0s);
+    } else if ((t_begin + 1) * TK > L) {
+        // the speculative tile runs past the sequence end: rows from L on may hold
+        // anything, and a V row is multiplied by P = 0, so those rows become zeros
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        const int r0 = L - t_begin * TK;
+        for (int e = r0 * CH + tid; e < TK * CH; e += kThreads)
+            *reinterpret_cast<uint4*>(v0s + (size_t)e * 16) = make_uint4(0, 0, 0, 0);
+    }
 
-    const int wave = tid >> 6, lane = tid & 63;
     const int nb = wave % NB, kg = wave / NB;
     const int h = lane >> 5, col = lane & 31;
     const int n = nb * 32 + col;
@@ -280,59 +282,33 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const AttnArgs a) {
         }
     }
 
-    const size_t kv_off = ((size_t)b * a.hkv + g) * (size_t)a.s_max * D;
-    const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k) + kv_off;
-    const uint16_t* vbase = reinterpret_cast<const uint16_t*>(a.v) + kv_off;
-    const int ld_row = tid / CHUNKS, ld_chunk = tid % CHUNKS;
-
-    uint4 pk[PASSES], pv[PASSES];
-    auto load_tile = [&](int t) {
-#pragma unroll
-        for (int p = 0; p < PASSES; ++p) {
-            const int key = t * TK + p * RPP + ld_row;
-            if (key < L) {
-                pk[p] = *reinterpret_cast<const uint4*>(kbase + (size_t)key * D + ld_chunk * 8);
-                pv[p] = *reinterpret_cast<const uint4*>(vbase + (size_t)key * D + ld_chunk * 8);
-            } else {
-                pk[p] = make_uint4(0, 0, 0, 0);
-                pv[p] = make_uint4(0, 0, 0, 0);
-            }
-        }
-    };
-
     f32x16 o[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
     float m_run = kNegInf, l_run = 0.f;
-    char* const ktile = smem;
-    char* const vtile = smem + TK * ROWB;
+    const int i16 = lane & 15;
+    const int half = (lane >> 4) & 1;
 
-    load_tile(t_begin);
-    for (int t = t_begin; t < t_end; ++t) {
-        __syncthreads();
-#pragma unroll
-        for (int p = 0; p < PASSES; ++p) {
-            const int row = p * RPP + ld_row;
-            *reinterpret_cast<uint4*>(ktile + row * ROWB + ld_chunk * 16) = pk[p];
-            *reinterpret_cast<uint4*>(vtile + row * ROWB + ld_chunk * 16) = pv[p];
-        }
-        __syncthreads();
-        if (t + 1 < t_end) load_tile(t + 1);
-
+    auto compute_tile = [&](int t, const char* ktile, const char* vtile) {
 #pragma unroll
         for (int st = 0; st < NB; ++st) {
             const int kl0 = kg * (TK / KG) + st * 32;       // first key of this sub-tile
-            // ---- S^T = K Q^T
+            // ---- S^T = K Q^T  (A operand: row kl0 + col, chunk 2 kk + h)
             f32x16 sacc;
 #pragma unroll
             for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+            {
+                const int krow = kl0 + col;
+                const int ksw = kv_swz<D>(krow);
+                const char* kr = ktile + krow * ROWB;
 #pragma unroll
-            for (int kk = 0; kk < KSTEPS; ++kk) {
-                const bf16x8 ka = *reinterpret_cast<const bf16x8*>(
-                    ktile + (kl0 + col) * ROWB + (16 * kk + 8 * h) * 2);
-                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], sacc, 0, 0, 0);
+                for (int kk = 0; kk < KSTEPS; ++kk) {
+                    const bf16x8 ka =
+                        *reinterpret_cast<const bf16x8*>(kr + (((2 * kk + h) ^ ksw) << 4));
+                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], sacc, 0, 0, 0);
+                }
             }
             // ---- mask + online softmax (lane owns column n; keys 8(r/4)+4h+r%4)
             float sv[16];
@@ -368,47 +344,65 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const AttnArgs a) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
             }
-            // ---- O^T += V^T P^T  (two 16-key k-steps)
-            const int i16 = lane & 15;
-            const int half = (lane >> 4) & 1;
+            // ---- O^T += V^T P^T  (two 16-key k-steps; rows vrow and vrow + 8)
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
                 const int vrow = kl0 + 16 * s2 + 4 * h + (i16 >> 2);
+                const int sw0 = kv_swz<D>(vrow), sw1 = kv_swz<D>(vrow + 8);
+                const char* r0p = vtile + vrow * ROWB + 8 * (i16 & 1);
+                const char* r1p = r0p + 8 * ROWB;
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
-                    const int vcol = 32 * db + 16 * half + 4 * (i16 & 3);
-                    const lds_char* base = (const lds_char*)(vtile + vrow * ROWB + vcol * 2);
+                    const int chunk = 4 * db + 2 * half + ((i16 & 3) >> 1);
                     const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_bf16x4*)(base));
+                        (lds_bf16x4*)(const lds_char*)(r0p + ((chunk ^ sw0) << 4)));
                     const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_bf16x4*)(base + 8 * ROWB));
+                        (lds_bf16x4*)(const lds_char*)(r1p + ((chunk ^ sw1) << 4)));
                     const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                     o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb_hi[s2], o[db], 0, 0, 0);
                     o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb_lo[s2], o[db], 0, 0, 0);
                 }
             }
         }
+    };
+
+    // Tile t + 1 is in flight while tile t is computed. Before each tile: this wave's DMA
+    // landed (s_waitcnt), then every wave's, and every wave is done with the other buffer.
+    for (int t = t_begin; t < t_end; t += 2) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (t + 1 < t_end) issue_tile(t + 1, k1s, v1s);
+        compute_tile(t, k0s, v0s);
+        if (t + 1 >= t_end) break;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (t + 2 < t_end) issue_tile(t + 2, k0s, v0s);
+        compute_tile(t + 1, k1s, v1s);
     }
 
-    // ---- combine the key groups through LDS
+    // ---- combine the key groups: wave w stores its 32 columns of O in tile buffer w,
+    // rows padded to OS floats so the 32 columns of one store hit different banks.
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     __syncthreads();                                    // tiles no longer needed
-    float* obuf = reinterpret_cast<float*>(smem);
-    float* gm = obuf + KG * MC * D;
-    float* gl = gm + KG * MC;
+    LdsQuad ob;
+    ob.p0 = reinterpret_cast<float*>(k0s);
+    ob.p1 = reinterpret_cast<float*>(v0s);
+    ob.p2 = reinterpret_cast<float*>(k1s);
+    ob.p3 = reinterpret_cast<float*>(v1s);
+    float* mine = ob[wave];
     if (h == 0) {
-        gm[kg * MC + n] = m_run;
-        gl[kg * MC + n] = l_tot;
+        stats[kg * a.mcap + n] = m_run;
+        stats[kStatCap + kg * a.mcap + n] = l_tot;
     }
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int d = 32 * db + 8 * (r >> 2) + 4 * h + (r & 3);
-            obuf[(kg * MC + n) * D + d] = o[db][r];
+            mine[col * OS + d] = o[db][r];
         }
     __syncthreads();
-    attn_epilogue<D, KG>(a, smem, unit, split, g, s, MC);
+    attn_epilogue<D, KG, NB>(a, ob, stats, unit, split, g, s, OS);
 }
 
 // -------------------------------------------------------------------------- fp32 / FMA
@@ -432,27 +426,27 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const AttnArgs a) {
     const int tid = threadIdx.x;
     const SeqGeom s = seq_geometry(a, b, tid == 0 && split == 0 && g == 0);
     if (!s.ok) return;
-    const int MC = a.mcap;
     const int M = s.rows * a.group;
     const int L = s.ctx + s.rows;
     const int ntiles = (L + TK - 1) / TK;
     const int t_begin = (int)((long)split * ntiles / a.nsplit);
     const int t_end = (int)((long)(split + 1) * ntiles / a.nsplit);
+    float* os = reinterpret_cast<float*>(smem);          // [MC][D]   (epilogue O)
+    float* st = os + MCOLS * D;                          // epilogue statistics
+    float* ms = st;                                      // [MC]      (epilogue gm)
+    float* ls = st + kStatCap;                           // [MC]      (epilogue gl)
+    float* ss = os + MCOLS * D + 5 * MCOLS;              // [MCOLS][TK]
     if (t_begin >= t_end) {
-        attn_empty_split<D>(a, unit, split, g, s);
+        attn_empty_split<D>(a, unit, split, s);
         return;
     }
 
-    float* os = reinterpret_cast<float*>(smem);          // [MC][D]   (epilogue obuf)
-    float* ms = os + MC * D;                             // [MC]      (epilogue gm)
-    float* ls = ms + MC;                                 // [MC]      (epilogue gl)
-    float* ss = os + MCOLS * D + 5 * MCOLS;              // [MCOLS][TK]
     float* al = ss + MCOLS * TK;                         // [MCOLS]
     float* ks = al + MCOLS;                              // [TK][KROW]
     float* vs = ks + TK * KROW;                          // [TK][D]
 
-    for (int e = tid; e < M * D; e += blockDim.x) os[e] = 0.f;
-    for (int n = tid; n < M; n += blockDim.x) { ms[n] = kNegInf; ls[n] = 0.f; }
+    for (int e = tid; e < M * D; e += kThreads) os[e] = 0.f;
+    for (int n = tid; n < M; n += kThreads) { ms[n] = kNegInf; ls[n] = 0.f; }
 
     const float* qg = reinterpret_cast<const float*>(a.q);
     const size_t kv_off = ((size_t)b * a.hkv + g) * (size_t)a.s_max * D;
@@ -461,7 +455,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const AttnArgs a) {
 
     for (int t = t_begin; t < t_end; ++t) {
         __syncthreads();
-        for (int e = tid; e < TK * D; e += blockDim.x) {
+        for (int e = tid; e < TK * D; e += kThreads) {
             const int kr = e / D, d = e % D;
             const int key = t * TK + kr;
             const bool in = key < L;
@@ -469,7 +463,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const AttnArgs a) {
             vs[e] = in ? vb[(size_t)key * D + d] : 0.f;
         }
         __syncthreads();
-        for (int e = tid; e < M * TK; e += blockDim.x) {
+        for (int e = tid; e < M * TK; e += kThreads) {
             const int n = e / TK, kr = e % TK;
             const int key = t * TK + kr;
             const float* qrow = qg + ((size_t)(s.r0 + n / a.group) * a.hq + g * a.group +
@@ -480,7 +474,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const AttnArgs a) {
             ss[n * TK + kr] = vis ? dot * a.scale_log2 : kNegInf;
         }
         __syncthreads();
-        for (int n = tid; n < M; n += blockDim.x) {
+        for (int n = tid; n < M; n += kThreads) {
             float mt = kNegInf;
             for (int kr = 0; kr < TK; ++kr) mt = fmaxf(mt, ss[n * TK + kr]);
             const float m_new = fmaxf(ms[n], mt);
@@ -497,7 +491,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const AttnArgs a) {
             al[n] = alpha;
         }
         __syncthreads();
-        for (int e = tid; e < M * D; e += blockDim.x) {
+        for (int e = tid; e < M * D; e += kThreads) {
             const int n = e / D, d = e % D;
             float o = os[e] * al[n];
             for (int kr = 0; kr < TK; ++kr) o = fmaf(ss[n * TK + kr], vs[kr * D + d], o);
@@ -505,7 +499,76 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const AttnArgs a) {
         }
     }
     __syncthreads();
-    attn_epilogue<D, 1>(a, smem, unit, split, g, s, MC);
+    LdsQuad ob;
+    ob.p0 = os;
+    ob.p1 = os + 32 * D;
+    ob.p2 = os + 64 * D;
+    ob.p3 = os + 96 * D;
+    attn_epilogue<D, 1, 4>(a, ob, st, unit, split, g, s, D);
+}
+
+
+// -------------------------------------------------------------------------- split merge
+// Runs after the attention kernel (stream order makes every partial visible):
+//   out = sum_s w_s O_s,   w_s = 2^(m_s - m) / sum_s' 2^(m_s' - m) l_s',   m = max_s m_s
+// over the key splits s of one (sequence, KV head) unit. Thread e of the unit's slice owns
+// column n = e / (D/4) and 4 consecutive d; the geometry, (max, sum) and O loads of up to
+// kMergeGroup splits are issued together, so one memory round trip covers <= 8 splits.
+// Columns past the sequence's M read workspace slots nobody wrote this call; their
+// results are computed and dropped.
+template <int D>
+__global__ __launch_bounds__(256) void attn_merge_kernel(const AttnArgs a) {
+    constexpr int D4 = D / 4;
+    constexpr int SG = kMergeGroup;
+    const int chunks = (a.mcap * D4 + kThreads - 1) / kThreads;
+    const int unit = blockIdx.x / chunks;
+    const int e = (blockIdx.x % chunks) * kThreads + threadIdx.x;
+    if (unit >= a.units || e >= a.mcap * D4) return;
+    const int b = unit / a.hkv, g = unit % a.hkv;
+    const int n = e / D4, d4 = e % D4;
+    const int ns = a.nsplit;
+    const size_t base = (size_t)unit * ns;
+    const float2* pml = a.part_ml + base * a.mcap + n;
+    const float4* po = reinterpret_cast<const float4*>(a.part_o) + (base * a.mcap + n) * D4 + d4;
+    const size_t sstride = (size_t)a.mcap * D4;              // float4s between splits
+
+    float m_run = kNegInf, l_run = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    SeqGeom s{};
+    for (int s0 = 0; s0 < ns; s0 += SG) {
+        float2 ml[SG];
+        float4 v[SG];
+#pragma unroll
+        for (int u = 0; u < SG; ++u) {
+            const int sp = s0 + u < ns ? s0 + u : ns - 1;    // in bounds; dropped below
+            ml[u] = pml[(size_t)sp * a.mcap];
+            v[u] = po[sp * sstride];
+        }
+        if (s0 == 0) s = seq_geometry(a, b, false);
+        float m = m_run;
+#pragma unroll
+        for (int u = 0; u < SG; ++u)
+            if (s0 + u < ns) m = fmaxf(m, ml[u].x);
+        if (m == kNegInf) continue;
+        const float c = exp2f(m_run - m);                    // m_run = -inf gives 0
+        l_run *= c;
+        acc = make_float4(acc.x * c, acc.y * c, acc.z * c, acc.w * c);
+#pragma unroll
+        for (int u = 0; u < SG; ++u) {
+            const float f = (s0 + u < ns && ml[u].x != kNegInf) ? exp2f(ml[u].x - m) : 0.f;
+            l_run += f * ml[u].y;
+            acc.x += f * v[u].x;
+            acc.y += f * v[u].y;
+            acc.z += f * v[u].z;
+            acc.w += f * v[u].w;
+        }
+        m_run = m;
+    }
+    if (!s.ok || n >= s.rows * a.group) return;
+    const float il = 1.f / l_run;
+    const int row = s.r0 + n / a.group, head = g * a.group + n % a.group;
+    *reinterpret_cast<float4*>(a.out + ((size_t)row * a.hq + head) * D + 4 * d4) =
+        make_float4(acc.x * il, acc.y * il, acc.z * il, acc.w * il);
 }
 
 }  // namespace
@@ -526,8 +589,6 @@ AttnPlan plan_attention(int B, int Hq, int Hkv, int D, int max_rows, int max_kv_
     if (nsplit < 1) nsplit = 1;
     p.nsplit = nsplit;
     size_t off = 256;                                            // error word + pad
-    p.off_counters = off;
-    off += ((size_t)p.units * 4 + 255) / 256 * 256;
     p.off_ml = off;
     off += ((size_t)p.units * nsplit * p.mcap * 8 + 255) / 256 * 256;
     p.off_o = off;
@@ -539,7 +600,7 @@ AttnPlan plan_attention(int B, int Hq, int Hkv, int D, int max_rows, int max_kv_
 hipError_t launch_attention(const AttnArgs& a, const AttnPlan& p, vsa_dtype dtype,
                             hipStream_t stream) {
     const int groups = (p.units + 7) / 8;
-    const dim3 grid(groups * 8 * p.nsplit), block(256);
+    const dim3 grid(groups * 8 * p.nsplit), block(kThreads);
     if (dtype == VSA_BF16) {
         if (a.d == 128) {
             if (p.nb == 1) hipLaunchKernelGGL((attn_bf16_kernel<128, 1>), grid, block, 0, stream, a);
@@ -553,6 +614,11 @@ hipError_t launch_attention(const AttnArgs& a, const AttnPlan& p, vsa_dtype dtyp
     } else {
         if (a.d == 128) hipLaunchKernelGGL((attn_f32_kernel<128>), grid, block, 0, stream, a);
         else hipLaunchKernelGGL((attn_f32_kernel<64>), grid, block, 0, stream, a);
+    }
+    if (p.nsplit > 1) {
+        const dim3 mgrid(p.units * ((p.mcap * (a.d / 4) + kThreads - 1) / kThreads));
+        if (a.d == 128) hipLaunchKernelGGL((attn_merge_kernel<128>), mgrid, block, 0, stream, a);
+        else hipLaunchKernelGGL((attn_merge_kernel<64>), mgrid, block, 0, stream, a);
     }
     return hipGetLastError();
 }

@@ -16,6 +16,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kWave = 64;
 
@@ -183,7 +184,6 @@ struct AttnArgs {
     float* out;
     float* part_o;          // [units][nsplit][mcap][D]
     float2* part_ml;        // [units][nsplit][mcap]   (running max (log2 units), sum)
-    uint32_t* counters;     // [units] arrival counters (zero between calls)
     uint32_t* err;
     int batch, total_rows, hq, hkv, group, d, s_max, max_rows, max_kv_len;
     int nsplit, units, mcap;
@@ -197,7 +197,7 @@ struct AttnPlan {
     int nsplit;      // key splits per (sequence, KV head)
     int units;       // B * Hkv
     int tile;        // keys per workgroup tile
-    size_t off_counters, off_ml, off_o, bytes;
+    size_t off_ml, off_o, bytes;
 };
 
 AttnPlan plan_attention(int B, int Hq, int Hkv, int D, int max_rows, int max_kv_len);
