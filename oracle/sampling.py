@@ -145,15 +145,23 @@ def truncated_distribution(z, temperature, top_k, top_p):
 
 
 # ----------------------------------------------------------------------------- race
+def race_keys(weights, u):
+    """Keys w_j / E_j of the exponential race (R14), E_j = -ln U'_j >= 0 for U' in (0, 1].
+    U' = 1 gives E = +0 and an infinite key (computed as 0 - ln U', so that the zero is
+    not negative); ids with w_j = 0 never win (key -inf)."""
+    weights = np.asarray(weights, dtype=np.float64)
+    e = 0.0 - np.log(np.asarray(u, dtype=np.float64))
+    with np.errstate(divide="ignore", invalid="ignore"):
+        return np.where(weights > 0, weights / e, -np.inf)
+
+
 def exponential_race(weights, seed, b, position):
     """Categorical draw proportional to `weights` (R14): argmax_j w_j / E_j with
     E_j = -ln U'_j, U' from the tag-1 stream of (seed, b, position); ties -> lowest id.
     Returns (token, relative gap between the two best keys)."""
     weights = np.asarray(weights, dtype=np.float64)
     u = philox.race_uniforms(seed, b, position, np.arange(weights.size, dtype=np.uint64))
-    e = -np.log(u)
-    with np.errstate(divide="ignore", invalid="ignore"):
-        keys = np.where(weights > 0, weights / e, -np.inf)
+    keys = race_keys(weights, u)
     tok = int(np.argmax(keys))
     order = np.sort(keys)[::-1]
     best, second = order[0], (order[1] if order.size > 1 else -np.inf)

@@ -317,6 +317,20 @@ def test_exponential_race_is_categorical():
     assert _chi2_ok(toks, w / w.sum()) > 1e-3
 
 
+def test_race_uniform_one_gives_infinite_key():
+    """U' = 1 means E = -ln 1 = 0: the id's key is +inf and it wins over any finite key
+    (ties among such ids go to the lowest id); a zero weight still never wins."""
+    w = np.array([5.0, 0.5, 0.0, 0.25])
+    u = np.array([0.3, 1.0, 1.0, 1.0])
+    keys = sampling.race_keys(w, u)
+    assert np.isposinf(keys[1]) and np.isposinf(keys[3]) and np.isneginf(keys[2])
+    assert int(np.argmax(keys)) == 1
+    u2 = np.array([0.3, 0.99, 0.7, 0.5])          # all < 1: plain w / (-ln u)
+    np.testing.assert_array_equal(sampling.race_keys(w, u2),
+                                  np.where(w > 0, w / -np.log(u2), -np.inf))
+    assert int(np.argmax(sampling.race_keys(w, u2))) == 1
+
+
 def test_planted_residual_mistake_is_caught(monkeypatch):
     """If the resample ignored q (used p instead of max(0, p - q)), the first emitted token
     would be biased towards the draft; the same chi-square must reject it."""

@@ -10,7 +10,7 @@ namespace {
 constexpr int kMaxRowsPerSeq = kMaxSeqRows;
 constexpr int kMaxTopK = kKeep;
 constexpr int kMaxTopLogprobs = 32;
-constexpr int kMaxVocab = 256 * kChunk;   // per-wave chunk tables hold 256 entries
+constexpr int kMaxVocab = kMaxChunks * kChunk;
 
 bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
 

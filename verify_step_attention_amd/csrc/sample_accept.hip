@@ -35,6 +35,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kEpt = kChunk / kThreads;        // ids per thread per chunk (8)
+constexpr int kQuads = kChunk / 1024;          // float4 groups per thread per chunk
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kBigIdx = 0x7FFFFFFF;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -360,7 +361,7 @@ __device__ __forceinline__ void load_chunk(const float* row, int base, int vocab
     const int tid = threadIdx.x;
     if (VEC) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
+        for (int q = 0; q < kQuads; ++q) {
             const int j = base + 1024 * q + 4 * tid;
             float4 v = make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
             if (j < vocab) v = *reinterpret_cast<const float4*>(row + j);
@@ -389,7 +390,7 @@ __device__ __forceinline__ void load_counts(const int32_t* row, int base, int vo
     }
     if (VEC) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
+        for (int q = 0; q < kQuads; ++q) {
             const int j = base + 1024 * q + 4 * tid;
             int4 v = make_int4(0, 0, 0, 0);
             if (j < vocab) v = *reinterpret_cast<const int4*>(row + j);
@@ -411,25 +412,23 @@ __device__ __forceinline__ int elem_id(int base, int e) {
     return base + 1024 * (e >> 2) + 4 * (int)threadIdx.x + (e & 3);
 }
 
-// Bits of this thread's ids that equal one of the first `k` drafts.
-__device__ __forceinline__ uint32_t special_mask(const int* s_draft, int k, int base) {
-    uint32_t mask = 0;
+// Per id of this thread: bit t set when draft t + 1 equals the id (the penalty count at
+// target row i is then the base count plus popcount(mask & (2^i - 1))).
+__device__ __forceinline__ void draft_masks(const int* s_draft, int k, int base,
+                                            uint32_t (&dm)[kEpt]) {
+#pragma unroll
+    for (int e = 0; e < kEpt; ++e) dm[e] = 0u;
     for (int t = 0; t < k; ++t) {
         const int off = s_draft[t] - base;
-        if (off >= 0 && off < kChunk && ((off & 1023) >> 2) == (int)threadIdx.x)
-            mask |= 1u << ((off >> 10) * 4 + (off & 3));
+        if (off >= 0 && off < kChunk && ((off & 1023) >> 2) == (int)threadIdx.x) {
+            const int ee = (off >> 10) * 4 + (off & 3);
+#pragma unroll
+            for (int e = 0; e < kEpt; ++e) dm[e] |= (e == ee) ? (1u << t) : 0u;
+        }
     }
-    return mask;
 }
 
-// Penalty count of id j at target row i: base count plus drafts d_1..d_i equal to j.
-__device__ __forceinline__ int row_count(int base_count, bool special, const int* s_draft, int i,
-                                         int j) {
-    int c = base_count;
-    if (special)
-        for (int t = 0; t < i; ++t) c += (s_draft[t] == j) ? 1 : 0;
-    return c;
-}
+__device__ __forceinline__ uint32_t low_bits(int i) { return i >= 32 ? ~0u : (1u << i) - 1u; }
 
 // ------------------------------------------------------------------ finalize helpers
 // Probability of id d under row `slot`'s truncated distribution (its kept list).
@@ -460,13 +459,15 @@ __device__ int keep_race(const SampArgs& a, int pslot, int np, int qslot, int nq
                 if (kq[t].idx == j) q = kq[t].p;
         const double r = kq ? fmax(0.0, p - q) : p;
         const uint4 w = philox_block(a.seed, (uint32_t)j >> 2, (uint32_t)pos, (uint32_t)b, 1u);
-        const double e = -log((double)race_u(pick(w, j & 3)));
+        // U' = 1 is E = 0: an infinite key (selected explicitly, not through -log(1))
+        const float uu = race_u(pick(w, j & 3));
+        const double inv_e = uu < 1.f ? 1.0 / -log((double)uu) : __builtin_inf();
         if (r > 0.0) {
-            const double key = r / e;
+            const double key = r * inv_e;
             if (key > best || (key == best && j < bi)) { best = key; bi = j; }
         }
         if (p > 0.0) {
-            const double key = p / e;
+            const double key = p * inv_e;
             if (key > fbest || (key == fbest && j < fbi)) { fbest = key; fbi = j; }
         }
     }
@@ -487,7 +488,7 @@ struct FinalShared {
     uint32_t lkey[4][kKeep];
     int lidx[4][kKeep];
     double lp[4][kKeep];
-    int ccount[4][256];
+    int ccount[4][kMaxChunks];
     int drafts[kMaxSeqRows];
 };
 
@@ -498,16 +499,16 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
     uint32_t ebits = 0;
 
     // ---- A: merge the chunk statistics of every row. One wave per row, rows q = wave,
-    //      wave + 4, ...; the (<= 256) chunk entries of up to 3 rows per wave are loaded in
-    //      one round (4 per lane per row).
+    //      wave + 4, ...; the (<= kMaxChunks) chunk entries of up to 3 rows per wave are
+    //      loaded in one round (up to kChunkLoads per lane per row).
     for (int q0 = wave; q0 < nrows; q0 += 12) {
-        float4 st[3][4];
+        float4 st[3][kChunkLoads];
 #pragma unroll
         for (int x = 0; x < 3; ++x) {
             const int q = q0 + 4 * x;
             const int slot = q < nrows ? row_ref(a, m, q).slot : 0;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < kChunkLoads; ++u) {
                 const int c = lane + 64 * u;
                 st[x][u] = (q < nrows && c < a.nchunk)
                                ? handoff_load4(a.stats + (size_t)slot * a.nchunk + c)
@@ -523,7 +524,7 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
             float bm = kNegInf, bv = kNegInf;
             int bi = kBigIdx;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < kChunkLoads; ++u) {
                 if (greedy_row) {
                     const int ci = __float_as_int(st[x][u].w);
                     if (better(st[x][u].z, ci, bv, bi)) { bv = st[x][u].z; bi = ci; }
@@ -538,7 +539,7 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
             if (!greedy_row && bm != kNegInf) {
                 const float cs = r.kind == 2 ? kLog2e : kLog2e / m.temp;
 #pragma unroll
-                for (int u = 0; u < 4; ++u)
+                for (int u = 0; u < kChunkLoads; ++u)
                     if (st[x][u].x != kNegInf)
                         z += (double)st[x][u].y * (double)exp2f((st[x][u].x - bm) * cs);
                 z = wave_sum_d(z);
@@ -829,13 +830,26 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
     const int base = c * kChunk;
     int cnt[kEpt];
     load_counts<VEC>(a.counts ? a.counts + (size_t)b * a.vocab : nullptr, base, a.vocab, cnt);
-    uint32_t special = 0;
     uint32_t valid = 0;
 #pragma unroll
     for (int e = 0; e < kEpt; ++e) valid |= (elem_id(base, e) < a.vocab ? 1u : 0u) << e;
+    // penalty terms of the base counts, each rounded as in z = (x - fp c) - pp [c > 0]
+    const bool has_pen = m.pp != 0.f || m.fp != 0.f;
+    float fpc[kEpt], ppc[kEpt];
+#pragma unroll
+    for (int e = 0; e < kEpt; ++e) {
+        fpc[e] = __fmul_rn(m.fp, (float)cnt[e]);
+        ppc[e] = cnt[e] > 0 ? m.pp : 0.f;
+    }
+    uint32_t dm[kEpt];              // drafts equal to each id (see draft_masks)
+    uint32_t dmo = 0;               // their union
 
     const int nrows = seq_nrows(m);
-    // ---- per-row statistics of this chunk (loads of kRowBatch rows in flight at once)
+    const int nd = m.sampled ? m.k : 0;
+    // ---- per-row statistics of this chunk (loads of kRowBatch rows in flight at once).
+    // Values: z (penalized target), w (draft) or x (raw); softmax statistics are taken as
+    // (max v, sum 2^((v - max) c)) with c = log2(e) / T, greedy target rows as argmax.
+    // Each phase runs over the batch's rows so that independent reductions interleave.
     for (int q0 = 0; q0 < nrows; q0 += kRowBatch) {
         float xv[kRowBatch][kEpt];
 #pragma unroll
@@ -845,54 +859,74 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
         if (q0 == 0) {
             if (tid < m.k) s_draft[tid] = dreg;
             __syncthreads();
-            special = special_mask(s_draft, m.k, base);
+            draft_masks(s_draft, m.k, base, dm);
+#pragma unroll
+            for (int e = 0; e < kEpt; ++e) dmo |= dm[e];
         }
+        float rmax[kRowBatch];
+        int ridx[kRowBatch];
+        // phase 1: penalties, per-thread max / argmax
 #pragma unroll
         for (int u = 0; u < kRowBatch; ++u) {
             const int q = q0 + u;
             if (q >= nrows) break;
-            const RowRef r = row_ref(a, m, q);
-            const bool greedy_row = r.kind == 0 && !m.sampled;
-            // values: z (penalized target), w (draft) or x (raw); the softmax statistics
-            // are taken as (max v, sum 2^((v - max) c)) with c = log2(e) / T
-            float v[kEpt];
+            const bool target = q < m.rows;
+            if (target && has_pen) {
+                const uint32_t lm = low_bits(q);
+                if (__ballot((dmo & lm) != 0u)) {
+                    // a draft of an earlier position is among this wave's ids
 #pragma unroll
-            for (int e = 0; e < kEpt; ++e) {
-                float val = xv[u][e];
-                if (r.kind == 0) {
-                    const int cc = row_count(cnt[e], (special >> e) & 1u, s_draft, r.i,
-                                             elem_id(base, e));
-                    val = penalize(val, cc, m.pp, m.fp);
+                    for (int e = 0; e < kEpt; ++e)
+                        xv[u][e] = penalize(xv[u][e], cnt[e] + __popc(dm[e] & lm), m.pp, m.fp);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < kEpt; ++e)
+                        xv[u][e] = __fsub_rn(__fsub_rn(xv[u][e], fpc[e]), ppc[e]);
                 }
-                v[e] = ((valid >> e) & 1u) ? val : kNegInf;
             }
-            float4 res;
-            if (greedy_row) {
-                float bv = kNegInf;
-                int bi = kBigIdx;
+            float bv = kNegInf;
+            int bi = kBigIdx;
+            if (target && !m.sampled) {
 #pragma unroll
                 for (int e = 0; e < kEpt; ++e)
-                    if (((valid >> e) & 1u) && better(v[e], elem_id(base, e), bv, bi)) {
-                        bv = v[e];
+                    if (((valid >> e) & 1u) && better(xv[u][e], elem_id(base, e), bv, bi)) {
+                        bv = xv[u][e];
                         bi = elem_id(base, e);
                     }
-                wave_argmax(bv, bi);
-                res = make_float4(0.f, 0.f, bv, __int_as_float(bi));
             } else {
-                const float cs = r.kind == 2 ? kLog2e : kLog2e / m.temp;
-                float mx = kNegInf;
 #pragma unroll
-                for (int e = 0; e < kEpt; ++e) mx = fmaxf(mx, v[e]);
-                mx = wave_max(mx);
+                for (int e = 0; e < kEpt; ++e) bv = fmaxf(bv, xv[u][e]);
+            }
+            rmax[u] = bv;
+            ridx[u] = bi;
+        }
+        // phase 2: wave maxima
+#pragma unroll
+        for (int u = 0; u < kRowBatch; ++u) {
+            const int q = q0 + u;
+            if (q >= nrows) break;
+            if (q < m.rows && !m.sampled) wave_argmax(rmax[u], ridx[u]);
+            else rmax[u] = wave_max(rmax[u]);
+        }
+        // phase 3: sums of exp2 ((v - max) c) (arguments <= 0: the hardware exp2 is exact
+        // enough, and terms below 2^-126 add nothing), wave sums, partials to LDS
+#pragma unroll
+        for (int u = 0; u < kRowBatch; ++u) {
+            const int q = q0 + u;
+            if (q >= nrows) break;
+            float4 res;
+            if (q < m.rows && !m.sampled) {
+                res = make_float4(0.f, 0.f, rmax[u], __int_as_float(ridx[u]));
+            } else {
+                const float cs = q >= m.rows + nd ? kLog2e : kLog2e / m.temp;
+                const float mx = rmax[u];
                 float sm = 0.f;
                 if (mx != kNegInf) {
-                    // arguments are <= 0: the hardware exp2 (v_exp_f32) is exact enough and
-                    // terms below 2^-126 add nothing
 #pragma unroll
-                    for (int e = 0; e < kEpt; ++e) sm += __builtin_amdgcn_exp2f((v[e] - mx) * cs);
+                    for (int e = 0; e < kEpt; ++e)
+                        sm += __builtin_amdgcn_exp2f((xv[u][e] - mx) * cs);
                 }
-                sm = wave_sum(sm);
-                res = make_float4(mx, sm, 0.f, 0.f);
+                res = make_float4(mx, wave_sum(sm), 0.f, 0.f);
             }
             if (lane == 0) s_part[q][wave] = res;
         }
@@ -940,8 +974,7 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
             for (int e = 0; e < kEpt; ++e) {
                 float val = x[e];
                 if (r.kind == 0)
-                    val = penalize(val, row_count(cnt[e], (special >> e) & 1u, s_draft, r.i,
-                                                  elem_id(base, e)), m.pp, m.fp);
+                    val = penalize(val, cnt[e] + __popc(dm[e] & low_bits(r.i)), m.pp, m.fp);
                 key[e] = ord_key(val);
             }
             const int n_valid = min(kChunk, a.vocab - base);
@@ -1000,16 +1033,20 @@ __global__ __launch_bounds__(kThreads) void race_kernel(const SampArgs a) {
     if (rq.kind == 1) load_chunk<VEC>(a.dl + (size_t)(m.d0 + rq.a) * a.vocab, base, a.vocab, xq);
     if (tid < m.k) s_draft[tid] = dreg;
     __syncthreads();
-    const uint32_t special = special_mask(s_draft, rq.a, base);
+    uint32_t dm[kEpt];
+    draft_masks(s_draft, rq.a, base, dm);
     const float inv_zp = (float)(1.0 / rq.z_p);
     const float inv_zq = rq.kind == 1 ? (float)(1.0 / rq.z_q) : 0.f;
     const float cs = kLog2e / m.temp;
 
-    // residual race and, in case every residual weight is 0, the race on p itself
+    // residual race and, in case every residual weight is 0, the race on p itself.
+    // Keys are w / (-log2 U') (the race's w / (-ln U') times ln 2, the same argmax), with
+    // the hardware exp2 / log2 / reciprocal (about one ulp each: the keys stay well inside
+    // the relative gap below which two ids count as tied).
     float best = 0.f, fbest = 0.f;
     int bi = kBigIdx, fbi = kBigIdx;
 #pragma unroll
-    for (int qd = 0; qd < 2; ++qd) {
+    for (int qd = 0; qd < kQuads; ++qd) {
         const int j0 = base + 1024 * qd + 4 * tid;
         if (j0 >= a.vocab) continue;
         const uint4 w = philox_block(a.seed, (uint32_t)j0 >> 2, (uint32_t)rq.pos, (uint32_t)b, 1u);
@@ -1018,21 +1055,24 @@ __global__ __launch_bounds__(kThreads) void race_kernel(const SampArgs a) {
             const int e = 4 * qd + r;
             const int j = j0 + r;
             if (j >= a.vocab) continue;
-            const int cc = row_count(cnt[e], (special >> e) & 1u, s_draft, rq.a, j);
-            const float zp = penalize(xp[e], cc, m.pp, m.fp);
-            const float p = exp2f((zp - rq.m_p) * cs) * inv_zp;
+            const float zp = penalize(xp[e], cnt[e] + __popc(dm[e]), m.pp, m.fp);
+            const float p = __builtin_amdgcn_exp2f((zp - rq.m_p) * cs) * inv_zp;
             float rr = p;
             if (rq.kind == 1) {
-                const float q = exp2f((xq[e] - rq.m_q) * cs) * inv_zq;
+                const float q = __builtin_amdgcn_exp2f((xq[e] - rq.m_q) * cs) * inv_zq;
                 rr = fmaxf(0.f, p - q);
             }
-            const float ex = -logf(race_u(pick(w, r)));
+            // 1 / (-log2 U'); U' = 1 is E = 0 in the exact race, an infinite key (selected
+            // explicitly: -log2(1) may come out as -0, whose reciprocal is -inf)
+            const float uu = race_u(pick(w, r));
+            const float inv_e = uu < 1.f ? __builtin_amdgcn_rcpf(-__builtin_amdgcn_logf(uu))
+                                         : __builtin_inff();
             if (rr > 0.f) {
-                const float key = rr / ex;
+                const float key = rr * inv_e;
                 if (key > best || (key == best && j < bi)) { best = key; bi = j; }
             }
             if (p > 0.f) {
-                const float key = p / ex;
+                const float key = p * inv_e;
                 if (key > fbest || (key == fbest && j < fbi)) { fbest = key; fbi = j; }
             }
         }
@@ -1062,16 +1102,16 @@ __global__ __launch_bounds__(kThreads) void race_kernel(const SampArgs a) {
     if (tid < 64) {
         float bb = 0.f, fb = 0.f;
         int bbi = kBigIdx, fbi2 = kBigIdx;
-        float4 part[4];                                   // <= 256 chunks, one round
+        float4 part[kChunkLoads];                         // <= kMaxChunks chunks, one round
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < kChunkLoads; ++u) {
             const int cc = lane + 64 * u;
             part[u] = cc < a.nchunk ? handoff_load4(a.race_part + (size_t)b * a.nchunk + cc)
                                     : make_float4(0.f, __int_as_float(kBigIdx), 0.f,
                                                   __int_as_float(kBigIdx));
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < kChunkLoads; ++u) {
             const float4 o = part[u];
             const int oi = __float_as_int(o.y), ofi = __float_as_int(o.w);
             if (o.x > bb || (o.x == bb && oi < bbi)) { bb = o.x; bbi = oi; }

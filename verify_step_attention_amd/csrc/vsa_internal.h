@@ -206,6 +206,8 @@ hipError_t launch_attention(const AttnArgs& a, const AttnPlan& p, vsa_dtype dtyp
 
 // ---------------------------------------------------------------- vocabulary stage
 constexpr int kChunk = 2048;         // vocabulary ids per workgroup chunk (8 per thread)
+constexpr int kMaxChunks = 256;      // chunks per row (vocabulary <= kMaxChunks * kChunk)
+constexpr int kChunkLoads = kMaxChunks / 64;   // per-lane loads when a wave reads a row's chunks
 constexpr int kKeep = 256;           // kept-set capacity of one truncated row
 constexpr int kMaxSeqRows = 32;      // verify rows per sequence (K <= 31)
 
