@@ -232,86 +232,6 @@ __device__ uint32_t wg_select_kth(const uint32_t (&key)[kEpt], uint32_t valid, i
 }
 
 // ------------------------------------------------------------------ wave-level pieces
-// The k-th largest candidate key of one row (candidates of every chunk, `ccount` valid
-// entries each, counts in LDS). hist: per-wave LDS[256].
-__device__ uint32_t wave_select_kth(const uint2* cand, const int* ccount, int nchunk, int capc,
-                                    int k, uint32_t* hist) {
-    const int lane = threadIdx.x & 63;
-    uint32_t prefix = 0, mask = 0;
-    int need = k;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        for (int i = lane; i < 256; i += 64) hist[i] = 0;
-        wave_sync();
-        for (int c = 0; c < nchunk; ++c) {
-            const uint2* cc = cand + (size_t)c * capc;
-            const int n = ccount[c];
-            for (int i = lane; i < n; i += 64) {
-                const uint32_t key = handoff_load_u2(cc + i).x;
-                if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-            }
-        }
-        wave_sync();
-        const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1];
-        const uint32_t h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
-        const uint32_t sl = h0 + h1 + h2 + h3;
-        uint32_t incl = sl;
-        for (int off = 1; off < 64; off <<= 1) {
-            const uint32_t v = __shfl_down(incl, off);
-            if (lane + off < 64) incl += v;
-        }
-        const uint32_t above = incl - sl;
-        int digit = -1, nneed = 0;
-        if (above < (uint32_t)need && (uint32_t)need <= incl) {
-            uint32_t cum = above;
-            if (cum + h3 >= (uint32_t)need) digit = 4 * lane + 3;
-            else if ((cum += h3) + h2 >= (uint32_t)need) digit = 4 * lane + 2;
-            else if ((cum += h2) + h1 >= (uint32_t)need) digit = 4 * lane + 1;
-            else { cum += h1; digit = 4 * lane; }
-            nneed = need - (int)cum;
-        }
-        const uint64_t found = __ballot(digit >= 0);
-        const int src = __ffsll((unsigned long long)found) - 1;
-        digit = __shfl(digit, src);
-        nneed = __shfl(nneed, src);
-        prefix |= (uint32_t)digit << shift;
-        mask |= 0xFFu << shift;
-        need = nneed;
-        wave_sync();
-    }
-    return prefix;
-}
-
-// Collects the candidates with key >= theta into a per-wave list (at most kKeep kept);
-// returns how many there are in total.
-__device__ int wave_collect(const uint2* cand, const int* ccount, int nchunk, int capc,
-                            uint32_t theta, uint32_t* lkey, int* lidx) {
-    const int lane = threadIdx.x & 63;
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    int n_s = 0;
-    for (int c = 0; c < nchunk; ++c) {
-        const uint2* cc = cand + (size_t)c * capc;
-        const int n = ccount[c];
-        for (int i0 = 0; i0 < n; i0 += 64) {
-            const int i = i0 + lane;
-            uint2 e = make_uint2(0, 0);
-            bool take = false;
-            if (i < n) {
-                e = handoff_load_u2(cc + i);
-                take = e.x >= theta;
-            }
-            const uint64_t m = __ballot(take);
-            const int pos = n_s + __popcll(m & below);
-            if (take && pos < kKeep) {
-                lkey[pos] = e.x;
-                lidx[pos] = (int)e.y;
-            }
-            n_s += __popcll(m);
-        }
-    }
-    wave_sync();
-    return n_s;
-}
-
 // Bitonic sort of n <= kKeep (key, id) pairs: key descending, id ascending.
 __device__ void wave_sort(uint32_t* lkey, int* lidx, int n) {
     const int lane = threadIdx.x & 63;
@@ -430,6 +350,118 @@ __device__ __forceinline__ void draft_masks(const int* s_draft, int k, int base,
 
 __device__ __forceinline__ uint32_t low_bits(int i) { return i >= 32 ? ~0u : (1u << i) - 1u; }
 
+// ------------------------------------------------------------------ workgroup selection
+constexpr int kSelTile = 32;     // candidate slots per thread held in registers at once
+
+__device__ __forceinline__ int wg_sum_i(int v, int* sh /* LDS[4] */) {
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+    __syncthreads();
+    const int r = sh[0] + sh[1] + sh[2] + sh[3];
+    __syncthreads();
+    return r;
+}
+
+__device__ __forceinline__ uint32_t wg_max_u(uint32_t v, int* sh /* LDS[4] */) {
+    for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off));
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = (int)v;
+    __syncthreads();
+    const uint32_t r = max(max((uint32_t)sh[0], (uint32_t)sh[1]),
+                           max((uint32_t)sh[2], (uint32_t)sh[3]));
+    __syncthreads();
+    return r;
+}
+
+// Keys of the candidate slots s0 + tid + 256 j (j < kSelTile) of one row's padded table
+// [chunk][capc]; returns the bit mask of the slots that hold a candidate (slot i of chunk c
+// is one when i < ccount[c]). All loads are issued before any is used.
+__device__ __forceinline__ uint32_t load_slot_keys(const uint2* cand, const int* ccount,
+                                                   int capc, int nslots, int s0,
+                                                   uint32_t (&kt)[kSelTile]) {
+    const float rc = 1.f / (float)capc;
+    uint32_t vm = 0u;
+#pragma unroll
+    for (int j = 0; j < kSelTile; ++j) {
+        const int sl = s0 + (int)threadIdx.x + kThreads * j;
+        // chunk = sl / capc, from a float quotient corrected by one step (sl < 2^24)
+        int c = (int)((float)sl * rc);
+        int i = sl - c * capc;
+        if (i < 0) { --c; i += capc; }
+        else if (i >= capc) { ++c; i -= capc; }
+        c = c < 0 ? 0 : c < kMaxChunks - 1 ? c : kMaxChunks - 1;   // in the table
+        const bool v = sl < nslots && i < ccount[c];
+        vm |= (v ? 1u : 0u) << j;
+    }
+#pragma unroll
+    for (int j = 0; j < kSelTile; ++j)
+        kt[j] = ((vm >> j) & 1u) ? cand[s0 + (int)threadIdx.x + kThreads * j].x : 0u;
+    return vm;
+}
+
+// After a histogram pass: the digit whose bin holds the `need`-th largest key, and how many
+// of the keys in that bin are still needed (sh[0], sh[1]). Wave 0 does the scan.
+__device__ __forceinline__ void hist_digit(const uint32_t* hist, int need, int* sh) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    if (tid < 64) {
+        const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1];
+        const uint32_t h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+        const uint32_t sl = h0 + h1 + h2 + h3;
+        uint32_t incl = sl;
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t v = __shfl_down(incl, off);
+            if (lane + off < 64) incl += v;
+        }
+        const uint32_t above = incl - sl;
+        if (above < (uint32_t)need && (uint32_t)need <= incl) {
+            uint32_t cum = above;
+            int digit;
+            if (cum + h3 >= (uint32_t)need) digit = 4 * lane + 3;
+            else if ((cum += h3) + h2 >= (uint32_t)need) digit = 4 * lane + 2;
+            else if ((cum += h2) + h1 >= (uint32_t)need) digit = 4 * lane + 1;
+            else { cum += h1; digit = 4 * lane; }
+            sh[0] = digit;
+            sh[1] = need - (int)cum;
+        }
+    }
+}
+
+// The k-th largest candidate key of one row (1-based), 8 bits at a time over every valid
+// slot; `kt` / `vm0` hold the first tile, reloaded per pass only when the table is larger.
+__device__ uint32_t wg_select_slots(const uint2* cand, const int* ccount, int capc, int nslots,
+                                    int k, const uint32_t (&kt0)[kSelTile], uint32_t vm0,
+                                    uint32_t* hist, int* sh) {
+    const int tid = threadIdx.x;
+    const bool one_tile = nslots <= kThreads * kSelTile;
+    uint32_t prefix = 0, mask = 0;
+    int need = k;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        hist[tid] = 0;
+        __syncthreads();
+        for (int s0 = 0; s0 < nslots; s0 += kThreads * kSelTile) {
+            uint32_t kt[kSelTile];
+            uint32_t vm = vm0;
+            if (one_tile) {
+#pragma unroll
+                for (int j = 0; j < kSelTile; ++j) kt[j] = kt0[j];
+            } else {
+                vm = load_slot_keys(cand, ccount, capc, nslots, s0, kt);
+            }
+#pragma unroll
+            for (int j = 0; j < kSelTile; ++j)
+                if (((vm >> j) & 1u) && (kt[j] & mask) == prefix)
+                    atomicAdd(&hist[(kt[j] >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        hist_digit(hist, need, sh);
+        __syncthreads();
+        prefix |= (uint32_t)sh[0] << shift;
+        mask |= 0xFFu << shift;
+        need = sh[1];
+        __syncthreads();
+    }
+    return prefix;
+}
+
 // ------------------------------------------------------------------ finalize helpers
 // Probability of id d under row `slot`'s truncated distribution (its kept list).
 __device__ double keep_lookup(const SampArgs& a, int kslot, int n, int d) {
@@ -484,14 +516,253 @@ __device__ int keep_race(const SampArgs& a, int pslot, int np, int qslot, int nq
 
 // ------------------------------------------------------------------ finalize
 struct FinalShared {
-    uint32_t hist[4][256];
-    uint32_t lkey[4][kKeep];
-    int lidx[4][kKeep];
-    double lp[4][kKeep];
-    int ccount[4][kMaxChunks];
+    int sel[8];                  // selection scratch: counter, sums, digit + remaining k
+    uint32_t hist[256];
+    uint32_t lkey[kKeep];
+    int lidx[kKeep];
+    double lp[kKeep];
+    int ccount[kMaxChunks];
+    __attribute__((aligned(16))) uint32_t cmk[kMaxChunks];   // chunk maxima as ordered keys
     int drafts[kMaxSeqRows];
 };
 
+// ------------------------------------------------------------------ per-row selection
+// (max, normalizer) of one row from its chunk statistics, by one wave (every lane returns it).
+__device__ RowInfo row_stats_wave(const SampArgs& a, const SeqMode& m, const RowRef& r) {
+    const int lane = threadIdx.x & 63;
+    float4 st[kChunkLoads];
+#pragma unroll
+    for (int u = 0; u < kChunkLoads; ++u) {
+        const int c = lane + 64 * u;
+        st[u] = c < a.nchunk ? a.stats[(size_t)r.slot * a.nchunk + c]
+                             : make_float4(kNegInf, 0.f, 0.f, 0.f);
+    }
+    float bm = kNegInf;
+#pragma unroll
+    for (int u = 0; u < kChunkLoads; ++u) bm = fmaxf(bm, st[u].x);
+    bm = wave_max(bm);
+    double z = 0.0;
+    if (bm != kNegInf) {
+        const float cs = r.kind == 2 ? kLog2e : kLog2e / m.temp;
+#pragma unroll
+        for (int u = 0; u < kChunkLoads; ++u)
+            if (st[u].x != kNegInf) z += (double)st[u].y * (double)exp2f((st[u].x - bm) * cs);
+        z = wave_sum_d(z);
+    }
+    RowInfo ri{};
+    ri.m = bm;
+    ri.z = z;
+    return ri;
+}
+
+// Truncated row (top-k threshold, kept set, nucleus; results to the row's workspace RowInfo
+// and kept list) or raw top-n row (top ids and their logprobs to the outputs), by one
+// workgroup, after the sweep (stream order makes its tables visible). A row's candidates sit
+// in a padded table [chunk][capc] (first ccount[c] valid); each thread loads the keys of its
+// slots tid + 256 j (coalesced, one round trip per tile of kSelTile slots per thread).
+// Lower bounds of the row's k-th largest key usually leave a few dozen candidates, sorted
+// exactly; otherwise a radix select over the registers decides. The kept ids (key >= theta)
+// go to an LDS list that wave 0 sorts.
+__device__ void select_row(const SampArgs& a, const SeqMode& m, int q, FinalShared& fs) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int* const ccount = fs.ccount;
+    const RowRef r = row_ref(a, m, q);
+    const bool trunc = m.topk && r.kind != 2;
+    const bool topn = r.kind == 2 && m.ntop > 0;
+    if (!trunc && !topn) return;
+    const int kk = trunc ? m.topk_k : m.ntop;
+    const uint2* cand = a.cand + (size_t)r.slot * a.nchunk * a.capc;
+    uint32_t ovf_key = 0u;                         // a chunk's k-th key where ties were cut
+    bool ovf = false;
+    uint32_t cmax = 0u;
+    if (tid < a.nchunk) {
+        const uint2 meta = a.cand_meta[(size_t)r.slot * a.nchunk + tid];
+        const float4 st = a.stats[(size_t)r.slot * a.nchunk + tid];
+        ccount[tid] = min((int)meta.x, a.capc);
+        ovf = (int)meta.x > a.capc;
+        ovf_key = meta.y;
+        cmax = ord_key(st.x);
+        fs.cmk[tid] = cmax;
+    } else if (tid < (a.nchunk + 15) / 16 * 16) {
+        fs.cmk[tid] = 0u;                          // padding: ranks below every maximum
+    }
+    if (tid == 0) {
+        fs.sel[0] = 0;
+        fs.sel[7] = 0;
+    }
+    __syncthreads();
+    const int nslots = a.nchunk * a.capc;
+    int tot = 0;
+    for (int c = tid; c < a.nchunk; c += kThreads) tot += ccount[c];
+    tot = wg_sum_i(tot, fs.sel + 1);
+    const int ksel = min(kk, tot);
+    if (ksel < 1) {
+        if (tid == 0 && trunc) {
+            a.rows[r.slot].kept_k = 0;
+            a.rows[r.slot].kept_p = 0;
+            a.rows[r.slot].theta = kNegInf;
+        }
+        return;
+    }
+    // Lower bounds of the row's ksel-th largest key theta: every chunk holds at least k
+    // values >= its own k-th key (meta.y), and the ksel largest chunk maxima are ksel
+    // distinct values. Usually only a few dozen candidates reach the larger bound; they
+    // are sorted exactly. Otherwise a radix select over every candidate decides.
+    uint32_t lb = wg_max_u(tid < a.nchunk ? ovf_key : 0u, fs.sel + 1);
+    if (a.nchunk >= ksel && tid < a.nchunk) {
+        // rank of this chunk's maximum; the table is padded with zeros to a multiple
+        // of 16 entries, read 16 at a time
+        int rank = 0;
+        const uint4* cm4 = reinterpret_cast<const uint4*>(fs.cmk);
+        for (int c4 = 0; c4 < (a.nchunk + 15) / 16 * 4; c4 += 4) {
+            uint4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = cm4[c4 + u];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int c = 4 * (c4 + u);
+                rank += (v[u].x > cmax || (v[u].x == cmax && c < tid)) ? 1 : 0;
+                rank += (v[u].y > cmax || (v[u].y == cmax && c + 1 < tid)) ? 1 : 0;
+                rank += (v[u].z > cmax || (v[u].z == cmax && c + 2 < tid)) ? 1 : 0;
+                rank += (v[u].w > cmax || (v[u].w == cmax && c + 3 < tid)) ? 1 : 0;
+            }
+        }
+        if (rank == ksel - 1) fs.sel[7] = (int)cmax;
+    }
+    __syncthreads();
+    lb = max(lb, (uint32_t)fs.sel[7]);
+    uint32_t kt0[kSelTile];
+    const uint32_t vm0 = load_slot_keys(cand, ccount, a.capc, nslots, 0, kt0);
+    // every candidate >= bound goes to the LDS list (ids loaded for those only)
+    auto collect = [&](uint32_t bound) {
+        for (int s0 = 0; s0 < nslots; s0 += kThreads * kSelTile) {
+            uint32_t kt[kSelTile];
+            uint32_t vmask = vm0;
+            if (s0 == 0) {
+#pragma unroll
+                for (int j = 0; j < kSelTile; ++j) kt[j] = kt0[j];
+            } else {
+                vmask = load_slot_keys(cand, ccount, a.capc, nslots, s0, kt);
+            }
+#pragma unroll
+            for (int j = 0; j < kSelTile; ++j) {
+                if (((vmask >> j) & 1u) && kt[j] >= bound) {
+                    const int sl = s0 + tid + kThreads * j;
+                    const int pos = atomicAdd(&fs.sel[0], 1);
+                    if (pos < kKeep) {
+                        fs.lkey[pos] = kt[j];
+                        fs.lidx[pos] = (int)cand[sl].y;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    };
+    collect(lb);
+    int n_all = fs.sel[0];
+    uint32_t theta;
+    bool sorted = false;
+    if (n_all >= ksel && n_all <= kKeep) {
+        if (wave == 0) wave_sort(fs.lkey, fs.lidx, n_all);
+        __syncthreads();
+        theta = fs.lkey[ksel - 1];
+        int cnt = 0;
+        for (int i = tid; i < n_all; i += kThreads) cnt += fs.lkey[i] >= theta ? 1 : 0;
+        n_all = wg_sum_i(cnt, fs.sel + 1);          // the sorted list's first n_all
+        sorted = true;
+    } else {
+        theta = wg_select_slots(cand, ccount, a.capc, nslots, ksel, kt0, vm0, fs.hist,
+                                fs.sel + 5);
+        if (tid == 0) fs.sel[0] = 0;
+        __syncthreads();
+        collect(theta);
+        n_all = fs.sel[0];
+    }
+    if (__syncthreads_or(ovf && ovf_key == theta) && tid == 0)
+        atomicOr(a.err, VSA_DEVERR_TIE_OVERFLOW);
+    if (n_all > kKeep && tid == 0) atomicOr(a.err, VSA_DEVERR_TIE_OVERFLOW);
+    if (wave != 0) return;
+    const int n = min(n_all, kKeep);
+    if (!sorted) wave_sort(fs.lkey, fs.lidx, n);
+    if (topn) {
+        // raw top-n ids with their log-softmax values
+        const RowInfo ri = row_stats_wave(a, m, r);
+        const int grow = m.r0 + r.i;
+        const double lz = log(ri.z);
+        for (int i = lane; i < a.max_top_lp; i += 64) {
+            const bool has = i < m.ntop && i < n;
+            if (a.top_ids) a.top_ids[(size_t)grow * a.max_top_lp + i] = has ? fs.lidx[i] : -1;
+            if (a.top_vals)
+                a.top_vals[(size_t)grow * a.max_top_lp + i] =
+                    has ? (float)((double)key_float(fs.lkey[i]) - (double)ri.m - lz)
+                        : 0.f;
+        }
+        return;
+    }
+    // probabilities over the kept set, fp64, in sorted order
+    const double ymax = (double)__fdiv_rn(key_float(fs.lkey[0]), m.temp);
+    double part = 0.0;
+    for (int i = lane; i < n; i += 64) {
+        const double y = (double)__fdiv_rn(key_float(fs.lkey[i]), m.temp);
+        const double w = exp(y - ymax);
+        fs.lp[i] = w;
+        part += w;
+    }
+    const double zs = wave_sum_d(part);
+    wave_sync();
+    for (int i = lane; i < n; i += 64) fs.lp[i] /= zs;
+    wave_sync();
+    int n_keep = n;
+    if (m.top_p < 1.f) {
+        // inclusive scan in sorted order: lane owns a contiguous run
+        const int per = (n + 63) / 64;
+        const int i0 = min(lane * per, n), i1 = min(i0 + per, n);
+        double run = 0.0;
+        for (int i = i0; i < i1; ++i) run += fs.lp[i];
+        double excl = run;
+        for (int off = 1; off < 64; off <<= 1) {
+            const double v = __shfl_up(excl, off);
+            if (lane >= off) excl += v;
+        }
+        excl -= run;
+        int first = kBigIdx;
+        double cum = excl;
+        for (int i = i0; i < i1; ++i) {
+            cum += fs.lp[i];
+            if (cum >= (double)m.top_p && first == kBigIdx) first = i;
+        }
+        int mstar = wave_min_i(first);
+        if (mstar == kBigIdx) mstar = n - 1;
+        const double cutoff = fs.lp[mstar];
+        int cnt = 0;
+        for (int i = lane; i < n; i += 64) cnt += fs.lp[i] >= cutoff ? 1 : 0;
+        n_keep = wave_sum_i(cnt);
+        double ks = 0.0;
+        for (int i = lane; i < n_keep; i += 64) ks += fs.lp[i];
+        ks = wave_sum_d(ks);
+        wave_sync();
+        for (int i = lane; i < n_keep; i += 64) fs.lp[i] /= ks;
+        wave_sync();
+    }
+    KeepEntry* keep = a.keep + (size_t)r.slot * a.keepcap;
+    for (int i = lane; i < n_keep; i += 64) {
+        KeepEntry e;
+        e.idx = fs.lidx[i];
+        e.pad = 0;
+        e.p = fs.lp[i];
+        keep[i] = e;
+    }
+    if (lane == 0) {
+        a.rows[r.slot].theta = key_float(theta);
+        a.rows[r.slot].kept_k = n_all;
+        a.rows[r.slot].kept_p = n_keep;
+    }
+}
+
+// AFTER_SELECT: run as its own kernel after the sweep and select_kernel (plain loads; the
+// truncated rows' thresholds and kept lists come from select_kernel); otherwise inside the
+// sweep's last workgroup of the sequence (hand-off loads; no truncated rows).
+template <bool AFTER_SELECT>
 __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, FinalShared& fs,
                                   RowInfo* rinfo /* LDS, one per row of the list */) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -510,8 +781,9 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
 #pragma unroll
             for (int u = 0; u < kChunkLoads; ++u) {
                 const int c = lane + 64 * u;
+                const float4* src = a.stats + (size_t)slot * a.nchunk + c;
                 st[x][u] = (q < nrows && c < a.nchunk)
-                               ? handoff_load4(a.stats + (size_t)slot * a.nchunk + c)
+                               ? (AFTER_SELECT ? *src : handoff_load4(src))
                                : make_float4(kNegInf, 0.f, kNegInf, __int_as_float(kBigIdx));
             }
         }
@@ -558,114 +830,18 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
     }
     __syncthreads();
 
-    // ---- B: truncated rows (top-k threshold, kept set, nucleus) and raw top-n rows
-    for (int q = wave; q < nrows; q += 4) {
-        const RowRef r = row_ref(a, m, q);
-        const bool trunc = m.topk && r.kind != 2;
-        const bool topn = r.kind == 2 && m.ntop > 0;
-        if (!trunc && !topn) continue;
-        const int kk = trunc ? m.topk_k : m.ntop;
-        int* ccount = fs.ccount[wave];
-        bool overflow_risk = false;
-        for (int c = lane; c < a.nchunk; c += 64) {
-            const uint2 meta = handoff_load_u2(a.cand_meta + (size_t)r.slot * a.nchunk + c);
-            ccount[c] = min((int)meta.x, a.capc);
-        }
-        wave_sync();
-        const uint2* cand = a.cand + (size_t)r.slot * a.nchunk * a.capc;
-        int total = 0;
-        for (int c = lane; c < a.nchunk; c += 64) total += ccount[c];
-        total = wave_sum_i(total);
-        const int ksel = min(kk, total);
-        if (ksel < 1) {
-            if (lane == 0 && trunc) rinfo[q].kept_k = rinfo[q].kept_p = 0;
-            continue;
-        }
-        const uint32_t theta = wave_select_kth(cand, ccount, a.nchunk, a.capc, ksel, fs.hist[wave]);
-        for (int c = lane; c < a.nchunk; c += 64) {
-            const uint2 meta = handoff_load_u2(a.cand_meta + (size_t)r.slot * a.nchunk + c);
-            if ((int)meta.x > a.capc && meta.y == theta) overflow_risk = true;
-        }
-        const int n_all = wave_collect(cand, ccount, a.nchunk, a.capc, theta, fs.lkey[wave],
-                                       fs.lidx[wave]);
-        if ((__ballot(overflow_risk) || n_all > kKeep) && lane == 0)
-            atomicOr(a.err, VSA_DEVERR_TIE_OVERFLOW);
-        const int n = min(n_all, kKeep);
-        wave_sort(fs.lkey[wave], fs.lidx[wave], n);
-        if (topn) {
-            // raw top-n ids with their log-softmax values
-            const RowInfo ri = rinfo[q];
-            const int grow = m.r0 + r.i;
-            const double lz = log(ri.z);
-            for (int i = lane; i < a.max_top_lp; i += 64) {
-                const bool has = i < m.ntop && i < n;
-                if (a.top_ids) a.top_ids[(size_t)grow * a.max_top_lp + i] = has ? fs.lidx[wave][i] : -1;
-                if (a.top_vals)
-                    a.top_vals[(size_t)grow * a.max_top_lp + i] =
-                        has ? (float)((double)key_float(fs.lkey[wave][i]) - (double)ri.m - lz)
-                            : 0.f;
+    // ---- B: selection results of truncated rows (select_kernel, a kernel earlier)
+    if (AFTER_SELECT) {
+        for (int q = tid; q < nrows; q += kThreads) {
+            const RowRef r = row_ref(a, m, q);
+            if (m.topk && r.kind != 2) {
+                const RowInfo sr = a.rows[r.slot];
+                rinfo[q].theta = sr.theta;
+                rinfo[q].kept_k = sr.kept_k;
+                rinfo[q].kept_p = sr.kept_p;
             }
-            continue;
         }
-        // probabilities over the kept set, fp64, in sorted order
-        const double ymax = (double)__fdiv_rn(key_float(fs.lkey[wave][0]), m.temp);
-        double part = 0.0;
-        for (int i = lane; i < n; i += 64) {
-            const double y = (double)__fdiv_rn(key_float(fs.lkey[wave][i]), m.temp);
-            const double w = exp(y - ymax);
-            fs.lp[wave][i] = w;
-            part += w;
-        }
-        const double zs = wave_sum_d(part);
-        wave_sync();
-        for (int i = lane; i < n; i += 64) fs.lp[wave][i] /= zs;
-        wave_sync();
-        int n_keep = n;
-        if (m.top_p < 1.f) {
-            // inclusive scan in sorted order: lane owns a contiguous run
-            const int per = (n + 63) / 64;
-            const int i0 = min(lane * per, n), i1 = min(i0 + per, n);
-            double run = 0.0;
-            for (int i = i0; i < i1; ++i) run += fs.lp[wave][i];
-            double excl = run;
-            for (int off = 1; off < 64; off <<= 1) {
-                const double v = __shfl_up(excl, off);
-                if (lane >= off) excl += v;
-            }
-            excl -= run;
-            int first = kBigIdx;
-            double cum = excl;
-            for (int i = i0; i < i1; ++i) {
-                cum += fs.lp[wave][i];
-                if (cum >= (double)m.top_p && first == kBigIdx) first = i;
-            }
-            int mstar = wave_min_i(first);
-            if (mstar == kBigIdx) mstar = n - 1;
-            const double cutoff = fs.lp[wave][mstar];
-            int cnt = 0;
-            for (int i = lane; i < n; i += 64) cnt += fs.lp[wave][i] >= cutoff ? 1 : 0;
-            n_keep = wave_sum_i(cnt);
-            double ks = 0.0;
-            for (int i = lane; i < n_keep; i += 64) ks += fs.lp[wave][i];
-            ks = wave_sum_d(ks);
-            wave_sync();
-            for (int i = lane; i < n_keep; i += 64) fs.lp[wave][i] /= ks;
-            wave_sync();
-        }
-        KeepEntry* keep = a.keep + (size_t)r.slot * a.keepcap;
-        for (int i = lane; i < n_keep; i += 64) {
-            KeepEntry e;
-            e.idx = fs.lidx[wave][i];
-            e.pad = 0;
-            e.p = fs.lp[wave][i];
-            keep[i] = e;
-        }
-        if (lane == 0) {
-            rinfo[q].theta = key_float(theta);
-            rinfo[q].kept_k = n_all;
-            rinfo[q].kept_p = n_keep;
-        }
-        wave_sync();
+        __syncthreads();
     }
     if (tid < m.k) fs.drafts[tid] = a.drafts[m.d0 + tid];
     __threadfence_block();        // kept lists written above are read by wave 0 below
@@ -809,11 +985,12 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
 }
 
 // ------------------------------------------------------------------ sweep kernel
-template <bool VEC>
+template <bool VEC, bool TOPK>
 __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
     __shared__ float4 s_part[3 * kMaxSeqRows][4];
     __shared__ int s_draft[kMaxSeqRows];
     __shared__ uint32_t s_hist[256];
+    __shared__ __attribute__((aligned(16))) uint32_t s_tm[kThreads];
     __shared__ int s_sh[4];
     __shared__ FinalShared s_final;
     __shared__ RowInfo s_rinfo[3 * kMaxSeqRows];
@@ -956,11 +1133,12 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
             acc.x = mx;
             acc.y = sm;
         }
-        handoff_store4(a.stats + (size_t)r.slot * a.nchunk + c, acc);
+        if (TOPK) a.stats[(size_t)r.slot * a.nchunk + c] = acc;   // read by later kernels
+        else handoff_store4(a.stats + (size_t)r.slot * a.nchunk + c, acc);
     }
 
     // ---- candidates for the k-th-largest threshold of truncated / top-n rows
-    if (m.topk || m.ntop > 0) {
+    if (TOPK && (m.topk || m.ntop > 0)) {
         for (int q = 0; q < nrows; ++q) {
             const RowRef r = row_ref(a, m, q);
             const bool trunc = m.topk && r.kind != 2;
@@ -978,38 +1156,106 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
                 key[e] = ord_key(val);
             }
             const int n_valid = min(kChunk, a.vocab - base);
+            uint2* out = a.cand + ((size_t)r.slot * a.nchunk + c) * a.capc;
+            // The chunk's candidates are all keys >= vk for a vk <= its kk-th largest key.
+            // First vk is the kk-th largest of the threads' maxima (kk distinct values, or 0
+            // when fewer threads hold ids): a cheap bound that usually leaves a few more
+            // than kk keys. If those do not fit in capc slots, vk becomes the exact kk-th key
+            // (radix select) and ties at it are cut at capc (the count says so).
             uint32_t vk = 0u;
-            if (n_valid > kk) vk = wg_select_kth(key, valid, kk, s_hist, s_sh);
+            if (n_valid > kk) {
+                uint32_t tmax = 0u;
+#pragma unroll
+                for (int e = 0; e < kEpt; ++e)
+                    if ((valid >> e) & 1u) tmax = max(tmax, key[e]);
+                s_tm[tid] = tmax;
+                __syncthreads();
+                int rank = 0;
+                const uint4* tm4 = reinterpret_cast<const uint4*>(s_tm);
+                for (int t4 = 0; t4 < kThreads / 4; t4 += 4) {     // 16 values per round
+                    uint4 v[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) v[u] = tm4[t4 + u];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int t = 4 * (t4 + u);
+                        rank += (v[u].x > tmax || (v[u].x == tmax && t < tid)) ? 1 : 0;
+                        rank += (v[u].y > tmax || (v[u].y == tmax && t + 1 < tid)) ? 1 : 0;
+                        rank += (v[u].z > tmax || (v[u].z == tmax && t + 2 < tid)) ? 1 : 0;
+                        rank += (v[u].w > tmax || (v[u].w == tmax && t + 3 < tid)) ? 1 : 0;
+                    }
+                }
+                if (rank == kk - 1) s_sh[3] = (int)tmax;
+                __syncthreads();
+                vk = (uint32_t)s_sh[3];
+            }
             if (tid == 0) s_sh[2] = 0;
             __syncthreads();
-            uint2* out = a.cand + ((size_t)r.slot * a.nchunk + c) * a.capc;
 #pragma unroll
             for (int e = 0; e < kEpt; ++e)
-                if (((valid >> e) & 1u) && key[e] > vk) {
-                    const int pos = atomicAdd(&s_sh[2], 1);
-                    handoff_store_u2(out + pos, make_uint2(key[e], (uint32_t)elem_id(base, e)));
-                }
-            __syncthreads();
-#pragma unroll
-            for (int e = 0; e < kEpt; ++e)
-                if (((valid >> e) & 1u) && key[e] == vk) {
+                if (((valid >> e) & 1u) && key[e] >= vk) {
                     const int pos = atomicAdd(&s_sh[2], 1);
                     if (pos < a.capc)
-                        handoff_store_u2(out + pos, make_uint2(key[e], (uint32_t)elem_id(base, e)));
+                        out[pos] = make_uint2(key[e], (uint32_t)elem_id(base, e));
                 }
             __syncthreads();
+            int ncand = s_sh[2];
+            if (ncand > a.capc) {
+                vk = wg_select_kth(key, valid, kk, s_hist, s_sh);
+                if (tid == 0) s_sh[2] = 0;
+                __syncthreads();
+#pragma unroll
+                for (int e = 0; e < kEpt; ++e)
+                    if (((valid >> e) & 1u) && key[e] > vk) {
+                        const int pos = atomicAdd(&s_sh[2], 1);
+                        out[pos] = make_uint2(key[e], (uint32_t)elem_id(base, e));
+                    }
+                __syncthreads();
+#pragma unroll
+                for (int e = 0; e < kEpt; ++e)
+                    if (((valid >> e) & 1u) && key[e] == vk) {
+                        const int pos = atomicAdd(&s_sh[2], 1);
+                        if (pos < a.capc)
+                            out[pos] = make_uint2(key[e], (uint32_t)elem_id(base, e));
+                    }
+                __syncthreads();
+                ncand = s_sh[2];
+            }
             if (tid == 0)
-                handoff_store_u2(a.cand_meta + (size_t)r.slot * a.nchunk + c,
-                                 make_uint2((uint32_t)s_sh[2], vk));
+                a.cand_meta[(size_t)r.slot * a.nchunk + c] = make_uint2((uint32_t)ncand, vk);
             __syncthreads();
         }
     }
 
 
     // ---- the last chunk of the sequence to finish merges and accepts (fence-free)
+    if (TOPK) return;                              // select_kernel and finalize_kernel follow
     __shared__ int s_last;
     if (handoff_arrive(a.cnt_sweep + b, (uint32_t)a.nchunk, &s_last))
-        finalize_sequence(a, m, b, s_final, s_rinfo);
+        finalize_sequence<false>(a, m, b, s_final, s_rinfo);
+}
+
+// ------------------------------------------------------------------ top-k pipeline kernels
+// grid (B x rows_cap): workgroup (b, q) selects row q of sequence b when it is a truncated
+// or top-n row; every other workgroup returns at once.
+__global__ __launch_bounds__(kThreads) void select_kernel(const SampArgs a, int rows_cap) {
+    __shared__ FinalShared s_final;
+    const int b = blockIdx.x / rows_cap, q = blockIdx.x % rows_cap;
+    uint32_t ebits = 0;
+    const SeqMode m = seq_mode(a, b, &ebits);
+    if (!m.valid || q >= seq_nrows(m)) return;
+    select_row(a, m, q, s_final);
+}
+
+// grid (B): merges the chunk statistics and runs the acceptance of one sequence.
+__global__ __launch_bounds__(kThreads) void finalize_kernel(const SampArgs a) {
+    __shared__ FinalShared s_final;
+    __shared__ RowInfo s_rinfo[3 * kMaxSeqRows];
+    const int b = blockIdx.x;
+    uint32_t ebits = 0;
+    const SeqMode m = seq_mode(a, b, &ebits);
+    if (!m.valid) return;
+    finalize_sequence<true>(a, m, b, s_final, s_rinfo);
 }
 
 // ------------------------------------------------------------------ race kernel
@@ -1169,10 +1415,30 @@ SampPlan plan_sample(int B, int total_rows, int V, int max_top_k, int max_top_lp
 hipError_t launch_sample(const SampArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)a.batch * a.nchunk), block(kThreads);
     const bool vec = (a.vocab % 4) == 0;
-    if (vec) hipLaunchKernelGGL(sweep_kernel<true>, grid, block, 0, stream, a);
-    else hipLaunchKernelGGL(sweep_kernel<false>, grid, block, 0, stream, a);
+    // Truncated (top-k) and top-n rows need the candidate tables and the selection code,
+    // which only the TOPK variant carries (a parameter asking for them is rejected when
+    // max_top_k and max_top_logprobs are 0).
+    const bool topk = a.max_top_k > 0 || a.max_top_lp > 0;
+    if (vec) {
+        if (topk) hipLaunchKernelGGL((sweep_kernel<true, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((sweep_kernel<true, false>), grid, block, 0, stream, a);
+    } else {
+        if (topk) hipLaunchKernelGGL((sweep_kernel<false, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((sweep_kernel<false, false>), grid, block, 0, stream, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (topk) {
+        // one workgroup per (sequence, row of its row list), then one per sequence
+        const int rows_cap = 3 * a.max_rows;
+        hipLaunchKernelGGL(select_kernel, dim3((unsigned)a.batch * rows_cap), block, 0, stream,
+                           a, rows_cap);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)a.batch), block, 0, stream, a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     // Always launched: only the device knows which sequences end in a full-vocabulary
     // draw; every other workgroup returns at once.
     if (vec) hipLaunchKernelGGL(race_kernel<true>, grid, block, 0, stream, a);
