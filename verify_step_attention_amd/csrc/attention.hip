@@ -30,6 +30,7 @@ constexpr int kThreads = 256;        // threads per workgroup (every kernel here
                                      // so loops do not load the size from the dispatch packet)
 constexpr int kMaxSplits = 32;       // key splits per (sequence, KV head)
 constexpr int kMergeGroup = 8;       // splits whose partials a merge thread loads together
+constexpr float kLazyLog2 = 8.f;     // online softmax: rescale only past this growth (log2)
 
 // Block index -> (unit, split). Consecutive block ids go to different XCDs (round-robin
 // dispatch), so units are dealt out across XCDs and all splits of one unit land on one XCD,
@@ -195,6 +196,11 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const AttnArgs a) {
     __shared__ __attribute__((aligned(1024))) char v0s[TILEB];
     __shared__ __attribute__((aligned(1024))) char k1s[TILEB];
     __shared__ __attribute__((aligned(1024))) char v1s[TILEB];
+    // tail: the last L mod TK keys of a sequence, <= 32 per split (see below)
+    constexpr int TAILB = 32 * ROWB;
+    constexpr int TPW = TAILB / 1024 / 4 > 0 ? TAILB / 1024 / 4 : 1;   // tail blocks per wave
+    __shared__ __attribute__((aligned(1024))) char kts[TAILB];
+    __shared__ __attribute__((aligned(1024))) char vts[TAILB];
     __shared__ float stats[kStatFloats];
 
     int unit, split;
@@ -202,7 +208,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const AttnArgs a) {
     if (unit >= a.units) return;
     const int b = unit / a.hkv, g = unit % a.hkv;
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const size_t kv_off = ((size_t)b * a.hkv + g) * (size_t)a.s_max * D;
     const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k) + kv_off;
     const uint16_t* vbase = reinterpret_cast<const uint16_t*>(a.v) + kv_off;
@@ -210,8 +216,25 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const AttnArgs a) {
     // DMA of tile t: wave w fills blocks w, w + 4, ... of K and of V (so a wave only ever
     // waits for its own blocks). Keys at or past key_lim read key key_lim - 1.
     const int dma_ri = lane / CH, dma_pos = lane % CH;
+    // the permutation of a row depends only on its index mod 16, which for the rows this
+    // lane fills (blocks wave, wave + 4, ...) is the same in every block
+    const int dma_off = dma_ri * ROWB + ((dma_pos ^ kv_swz<D>(wave * RPI + dma_ri)) << 4);
     int key_lim;
-    auto issue_tile = [&](int t, char* kt, char* vt) {
+    auto issue_tile = [&](int t, char* kt, char* vt) __attribute__((always_inline)) {
+        if ((t + 1) * TK <= key_lim) {
+            // whole tile inside the sequence: uniform base + the lane's fixed offset
+            const char* kb = reinterpret_cast<const char*>(kbase) + (size_t)t * TILEB;
+            const char* vb = reinterpret_cast<const char*>(vbase) + (size_t)t * TILEB;
+#pragma unroll
+            for (int i = 0; i < BPW; ++i) {
+                const int blk = i * 4 + wave;
+                __builtin_amdgcn_global_load_lds(kb + blk * 1024 + dma_off,
+                                                 (lds_void*)(kt + blk * 1024), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(vb + blk * 1024 + dma_off,
+                                                 (lds_void*)(vt + blk * 1024), 16, 0, 0);
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < BPW; ++i) {
             const int blk = i * 4 + wave;
@@ -223,13 +246,26 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const AttnArgs a) {
             __builtin_amdgcn_global_load_lds(vbase + src, (lds_void*)(vt + blk * 1024), 16, 0, 0);
         }
     };
+    // Key ranges. With >= 4 splits, split s owns full tiles [F s / n, F (s + 1) / n) of the
+    // F = L / TK full tiles, and a tail of the last L mod TK keys, spread so that each split
+    // gets <= 32 of them (prefetched into a small buffer and computed alongside its first
+    // tile): every split then streams the same number of full tiles, where handing the
+    // remainder to one split would cost it a whole extra tile. With fewer splits the tiles
+    // are ceil(L / TK), the last one partial, and there is no tail.
+    const bool tails = a.nsplit >= 4;
+    auto tile_range = [&](int len, int* tb, int* te) __attribute__((always_inline)) {
+        const long nt = tails ? len / TK : (len + TK - 1) / TK;
+        *tb = (int)((long)split * nt / a.nsplit);
+        *te = (int)((long)(split + 1) * nt / a.nsplit);
+    };
     // The first tile is requested before the sequence geometry arrives, as if the sequence
     // held all kv_cap keys (the split's first tile is then the same whenever the sequence
     // spans as many tiles as kv_cap). Rows past the true end are fixed up below.
     const int kv_cap = a.max_kv_len < a.s_max ? a.max_kv_len : a.s_max;
-    const int t_spec = (int)((long)split * ((kv_cap + TK - 1) / TK) / a.nsplit);
+    int t_spec, t_spec_end;
+    tile_range(kv_cap, &t_spec, &t_spec_end);
     key_lim = kv_cap;
-    issue_tile(t_spec, k0s, v0s);
+    if (t_spec < t_spec_end) issue_tile(t_spec, k0s, v0s);
 
     const SeqGeom s = seq_geometry(a, b, tid == 0 && split == 0 && g == 0);
     if (!s.ok) {
@@ -237,16 +273,23 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const AttnArgs a) {
         return;
     }
     const int L = s.ctx + s.rows;                      // keys of this sequence
-    const int ntiles = (L + TK - 1) / TK;
-    const int t_begin = (int)((long)split * ntiles / a.nsplit);
-    const int t_end = (int)((long)(split + 1) * ntiles / a.nsplit);
+    int t_begin, t_end;
+    tile_range(L, &t_begin, &t_end);
+    int tail_b = 0, tail_e = 0;
+    if (tails) {
+        const int f = L / TK * TK, rem = L - f;
+        tail_b = f + (int)((long)split * rem / a.nsplit);
+        tail_e = f + (int)((long)(split + 1) * rem / a.nsplit);
+    }
     key_lim = L;
-    if (t_begin >= t_end) {
+    if (t_begin >= t_end && tail_b >= tail_e) {
         __builtin_amdgcn_s_waitcnt(0);                 // no DMA outlives the workgroup
         attn_empty_split<D>(a, unit, split, s);
         return;
     }
-    if (t_begin != t_spec) {
+    if (t_begin >= t_end) {
+        // tail only
+    } else if (t_begin != t_spec || t_spec >= t_spec_end) {
         __builtin_amdgcn_s_waitcnt(0);                 // this wave's blocks are free again
         issue_tile(t_begin, k0s, v0s);
     } else if ((t_begin + 1) * TK > L) {
@@ -257,6 +300,21 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const AttnArgs a) {
         const int r0 = L - t_begin * TK;
         for (int e = r0 * CH + tid; e < TK * CH; e += kThreads)
             *reinterpret_cast<uint4*>(v0s + (size_t)e * 16) = make_uint4(0, 0, 0, 0);
+    }
+
+    if (tail_b < tail_e) {
+        // rows past the tail end read its last key (finite data, masked)
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            const int blk = i * 4 + wave;
+            if (blk * 1024 >= TAILB) break;
+            const int r = blk * RPI + dma_ri;
+            int key = tail_b + r;
+            key = key < tail_e ? key : tail_e - 1;
+            const size_t src = (size_t)key * D + (size_t)((dma_pos ^ kv_swz<D>(r)) * 8);
+            __builtin_amdgcn_global_load_lds(kbase + src, (lds_void*)(kts + blk * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vbase + src, (lds_void*)(vts + blk * 1024), 16, 0, 0);
+        }
     }
 
     const int nb = wave % NB, kg = wave / NB;
@@ -291,10 +349,11 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const AttnArgs a) {
     const int i16 = lane & 15;
     const int half = (lane >> 4) & 1;
 
-    auto compute_tile = [&](int t, const char* ktile, const char* vtile) {
-#pragma unroll
-        for (int st = 0; st < NB; ++st) {
-            const int kl0 = kg * (TK / KG) + st * 32;       // first key of this sub-tile
+    // One 32-key sub-tile: buffer rows kl0 .. kl0 + 31 hold keys kbase0 + row; keys at or
+    // past khi are masked.
+    auto compute_sub = [&](const char* ktile, const char* vtile, int kl0, int kbase0,
+                           int khi) __attribute__((always_inline)) {
+        {
             // ---- S^T = K Q^T  (A operand: row kl0 + col, chunk 2 kk + h)
             f32x16 sacc;
 #pragma unroll
@@ -310,40 +369,54 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const AttnArgs a) {
                     sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], sacc, 0, 0, 0);
                 }
             }
-            // ---- mask + online softmax (lane owns column n; keys 8(r/4)+4h+r%4)
+            // ---- mask + online softmax (lane owns column n; keys 8(r/4)+4h+r%4). A
+            // sub-tile whose keys all precede the sequence's first verify row is visible to
+            // every row and needs no mask.
             float sv[16];
             float mt = kNegInf;
+            if (kbase0 + kl0 + 31 <= s.ctx && kbase0 + kl0 + 31 < khi) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int tg = t * TK + kl0 + 8 * (r >> 2) + 4 * h + (r & 3);
-                const bool vis = col_valid && tg < L && tg <= causal_lim;
-                sv[r] = vis ? sacc[r] * a.scale_log2 : kNegInf;
-                mt = fmaxf(mt, sv[r]);
+                for (int r = 0; r < 16; ++r) {
+                    sv[r] = sacc[r] * a.scale_log2;
+                    mt = fmaxf(mt, sv[r]);
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int tg = kbase0 + kl0 + 8 * (r >> 2) + 4 * h + (r & 3);
+                    const bool vis = col_valid && tg < khi && tg <= causal_lim;
+                    sv[r] = vis ? sacc[r] * a.scale_log2 : kNegInf;
+                    mt = fmaxf(mt, sv[r]);
+                }
             }
             mt = fmaxf(mt, __shfl_xor(mt, 32));
-            const float m_new = fmaxf(m_run, mt);
-            const float alpha = (m_new == kNegInf) ? 1.f : exp2f(m_run - m_new);
+            // Lazy rescale: the reference max m_run moves only when a score exceeds it by
+            // more than kLazyLog2 (or at the first finite score), so P stays <= 2^kLazyLog2
+            // and the O rescale (64 accumulators) runs rarely instead of at most tiles.
+            const bool grow = mt > m_run + kLazyLog2;
+            if (__ballot(grow)) {
+                const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mt) : 1.f;  // -inf -> 0
+                if (grow) m_run = mt;
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+            }
             // P goes into the PV product as a bf16 pair hi + lo (about 16 significant
             // bits): a single bf16 rounding of P would perturb the weights by up to 2^-8.
             bf16x8 pb_hi[2], pb_lo[2];
             float ls = 0.f;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float pf = (sv[r] == kNegInf) ? 0.f : exp2f(sv[r] - m_new);
-                const uint32_t hi = f32_to_bf16_bits(pf);
-                const uint32_t lo = f32_to_bf16_bits(pf - bf16_bits_to_f32(hi));
+                const float pf = (sv[r] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(sv[r] - m_run);
+                const __bf16 hi = (__bf16)pf;
+                const __bf16 lo = (__bf16)(pf - (float)hi);
                 ls += pf;
-                pb_hi[r >> 3][r & 7] = (short)hi;
-                pb_lo[r >> 3][r & 7] = (short)lo;
+                pb_hi[r >> 3][r & 7] = __builtin_bit_cast(short, hi);
+                pb_lo[r >> 3][r & 7] = __builtin_bit_cast(short, lo);
             }
-            l_run = l_run * alpha + ls;
-            m_run = m_new;
-            if (alpha != 1.f) {
-#pragma unroll
-                for (int db = 0; db < DB; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-            }
+            l_run += ls;
             // ---- O^T += V^T P^T  (two 16-key k-steps; rows vrow and vrow + 8)
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
@@ -365,14 +438,29 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const AttnArgs a) {
             }
         }
     };
+    auto compute_tile = [&](int t, const char* ktile,
+                            const char* vtile) __attribute__((always_inline)) {
+#pragma unroll
+        for (int st = 0; st < NB; ++st) compute_sub(ktile, vtile, kg * (TK / KG) + st * 32, t * TK, L);
+    };
+    // the tail (<= 32 keys) is one sub-tile, for the waves of key group 0
+    auto compute_tail = [&]() __attribute__((always_inline)) {
+        if (tail_b < tail_e && kg == 0) compute_sub(kts, vts, 0, tail_b, tail_e);
+    };
 
     // Tile t + 1 is in flight while tile t is computed. Before each tile: this wave's DMA
     // landed (s_waitcnt), then every wave's, and every wave is done with the other buffer.
-    for (int t = t_begin; t < t_end; t += 2) {
+    if (t_begin >= t_end) {
         __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        compute_tail();
+    }
+    for (int t = t_begin; t < t_end; t += 2) {
+        __builtin_amdgcn_s_waitcnt(0);                 // first time: the tail landed too
         __syncthreads();
         if (t + 1 < t_end) issue_tile(t + 1, k1s, v1s);
         compute_tile(t, k0s, v0s);
+        if (t == t_begin) compute_tail();
         if (t + 1 >= t_end) break;
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
