@@ -764,10 +764,26 @@ __device__ void select_row(const SampArgs& a, const SeqMode& m, int q, FinalShar
 // sweep's last workgroup of the sequence (hand-off loads; no truncated rows).
 template <bool AFTER_SELECT>
 __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, FinalShared& fs,
-                                  RowInfo* rinfo /* LDS, one per row of the list */) {
+                                  RowInfo* rinfo /* LDS, one per row of the list */,
+                                  const int* drafts_lds /* the K draft ids in LDS, or null */) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nrows = seq_nrows(m);
     uint32_t ebits = 0;
+    // The draft ids, and for sampled rows without top-k each draft's target logit, draft
+    // logit and base count (wave 0, lane t - 1), are requested before the statistics merge
+    // so that they arrive with it.
+    const int* const drafts = drafts_lds ? drafts_lds : fs.drafts;
+    if (!drafts_lds && tid < m.k) fs.drafts[tid] = a.drafts[m.d0 + tid];
+    int pre_d = -1, pre_c = 0;
+    float pre_xt = 0.f, pre_xd = 0.f;
+    if (wave == 0 && lane < m.k) {
+        pre_d = drafts_lds ? drafts_lds[lane] : a.drafts[m.d0 + lane];
+        if (m.sampled && !m.topk && pre_d >= 0 && pre_d < a.vocab) {
+            pre_c = a.counts ? a.counts[(size_t)b * a.vocab + pre_d] : 0;
+            pre_xt = a.tl[(size_t)(m.r0 + lane) * a.vocab + pre_d];
+            pre_xd = a.dl[(size_t)(m.d0 + lane) * a.vocab + pre_d];
+        }
+    }
 
     // ---- A: merge the chunk statistics of every row. One wave per row, rows q = wave,
     //      wave + 4, ...; the (<= kMaxChunks) chunk entries of up to 3 rows per wave are
@@ -843,9 +859,6 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
         }
         __syncthreads();
     }
-    if (tid < m.k) fs.drafts[tid] = a.drafts[m.d0 + tid];
-    __threadfence_block();        // kept lists written above are read by wave 0 below
-    __syncthreads();
 
     // ---- C: acceptance (wave 0)
     if (wave == 0) {
@@ -855,7 +868,7 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
         RaceReq rq{};
         if (!m.sampled) {
             while (acc < m.k) {
-                const int d = fs.drafts[acc];
+                const int d = drafts[acc];
                 if (d < 0 || d >= a.vocab) ebits |= VSA_DEVERR_DRAFT_ID;
                 if (d != rinfo[acc].argmax) break;
                 ++acc;
@@ -868,15 +881,15 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
             double pd_l = 0.0, qd_l = 0.0;
             if (lane < m.k) {
                 const int t = lane + 1;
-                const int d = fs.drafts[lane];
+                const int d = pre_d;
                 if (d >= 0 && d < a.vocab) {
                     if (m.topk) {
                         // filled below, with the whole wave scanning the kept lists
                     } else {
-                        int c = a.counts ? a.counts[(size_t)b * a.vocab + d] : 0;
-                        const float xt = a.tl[(size_t)(m.r0 + t - 1) * a.vocab + d];
-                        const float xd = a.dl[(size_t)(m.d0 + t - 1) * a.vocab + d];
-                        for (int s2 = 0; s2 < t - 1; ++s2) c += fs.drafts[s2] == d ? 1 : 0;
+                        int c = pre_c;
+                        const float xt = pre_xt;
+                        const float xd = pre_xd;
+                        for (int s2 = 0; s2 < t - 1; ++s2) c += drafts[s2] == d ? 1 : 0;
                         const float cs = kLog2e / m.temp;
                         const float zt = penalize(xt, c, m.pp, m.fp);
                         pd_l = (double)exp2f((zt - rinfo[t - 1].m) * cs) / rinfo[t - 1].z;
@@ -888,7 +901,7 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
             bool all = true;
             for (int t = 1; t <= m.k; ++t) {
                 const int pos = base_pos + t - 1;
-                const int d = fs.drafts[t - 1];
+                const int d = drafts[t - 1];
                 const bool valid = d >= 0 && d < a.vocab;
                 if (!valid) ebits |= VSA_DEVERR_DRAFT_ID;
                 double pd = 0.0, qd = 0.0;
@@ -956,7 +969,7 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
         for (int s = lane; s < m.rows; s += 64) {
             const int grow = m.r0 + s;
             int out = -1;
-            if (s < acc) out = fs.drafts[s];
+            if (s < acc) out = drafts[s];
             else if (s == acc) out = pending ? -1 : tok;
             a.out_tokens[grow] = out;
             if (a.chosen_lp) {
@@ -1232,7 +1245,7 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
     if (TOPK) return;                              // select_kernel and finalize_kernel follow
     __shared__ int s_last;
     if (handoff_arrive(a.cnt_sweep + b, (uint32_t)a.nchunk, &s_last))
-        finalize_sequence<false>(a, m, b, s_final, s_rinfo);
+        finalize_sequence<false>(a, m, b, s_final, s_rinfo, s_draft);
 }
 
 // ------------------------------------------------------------------ top-k pipeline kernels
@@ -1255,7 +1268,7 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(const SampArgs a) {
     uint32_t ebits = 0;
     const SeqMode m = seq_mode(a, b, &ebits);
     if (!m.valid) return;
-    finalize_sequence<true>(a, m, b, s_final, s_rinfo);
+    finalize_sequence<true>(a, m, b, s_final, s_rinfo, nullptr);
 }
 
 // ------------------------------------------------------------------ race kernel
