@@ -8,6 +8,10 @@ verify_sample_accept on the same stream, on one of R distinct input sets in HBM 
 > 1 GB, so the 256 MB last-level cache cannot hold the working set between steps).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--static-splits]
+
+Attention runs with dynamic key splits (VSA_ATTN_DYNAMIC_SPLITS: splits claim key tiles
+at run time) unless --static-splits asks for fixed, bitwise reproducible ranges.
 
 Prints one JSON line. Roofline: the dominant stage (attention: its main kernel and the
 split merge kernel) is timed per call with HIP events on the stream it runs on; its
@@ -28,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 WORKLOAD = "verify_b4k4_ctx8192"
+ATTN_FLAGS = 0                   # set in main(): dynamic splits unless --static-splits
 PEAK_HBM_GBPS = 8000.0
 COUNTERS = os.path.join(ROOT, "profiles", "attention_b4k4_ctx8192_counters.json")
 ATTN_SRC = os.path.join(ROOT, "verify_step_attention_amd", "csrc", "attention.hip")
@@ -171,6 +176,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=7)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--static-splits", action="store_true",
+                    help="attention with fixed key ranges per split (bitwise reproducible) "
+                         "instead of tiles claimed at run time")
     ap.add_argument("--eager", action="store_true",
                     help="launch every call from Python instead of replaying HIP graphs")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -186,6 +194,8 @@ def main():
     import torch
     import verify_step_attention_amd as vsa
     from verify_step_attention_amd import workloads as wl
+    global ATTN_FLAGS
+    ATTN_FLAGS = 0 if args.static_splits else vsa.ATTN_DYNAMIC_SPLITS
 
     print(f"[bench] building inputs for {WORKLOAD}", file=sys.stderr, flush=True)
     w = wl.make_workload(WORKLOAD)
@@ -211,7 +221,7 @@ def main():
     def attention(d, s=None):
         vsa.verify_attention(d["q"], d["k_cache"], d["v_cache"], d["cu_rows"], d["ctx_lens"],
                              out, ws_a, max_rows_per_seq=w.max_rows, max_kv_len=w.max_kv_len,
-                             stream=stream if s is None else s)
+                             flags=ATTN_FLAGS, stream=stream if s is None else s)
 
     def sample(d, s=None):
         vsa.verify_sample_accept(d["target_logits"], d["draft_logits"], d["draft_tokens"],
@@ -363,6 +373,7 @@ def main():
                                      round(float(np.percentile(attn_ms, 90)) * 1e3, 2)],
             "sample_accept_us": round(float(np.mean(samp_ms)) * 1e3, 2),
             "logits_dtype": "f32",
+            "attention_splits": "dynamic" if ATTN_FLAGS else "static",
         },
         "roofline": {
             "bound": "hbm",

@@ -117,17 +117,30 @@ const char* vsa_status_string(vsa_status status);
  *   max_rows_per_seq  host bound >= every R_b (at most 32)
  *   max_kv_len host bound >= every ctx_b + R_b (sizes the key split; <= S_max)
  *   scale      softmax scale; 0 => 1/sqrt(D)
+ *   flags      0, or VSA_ATTN_DYNAMIC_SPLITS (other bits: VSA_ERR_INVALID_ARG)
  *   out        [total_rows, Hq, D] float32, written for every row
  * Limits: (Hq / Hkv) * max_rows_per_seq <= 128.
+ *
+ * The keys of each (sequence, KV head) are split over several workgroups whose partial
+ * softmax states are merged. With flags = 0 every split owns a fixed key range, so the
+ * output is bitwise reproducible run to run and identical for identical sequences in one
+ * batch. With VSA_ATTN_DYNAMIC_SPLITS the splits claim key tiles at run time (the ones
+ * that start early or stream fast take more), which shortens the call when workgroups
+ * start at different times; the output then differs between runs at the level of fp32
+ * rounding order, within the same error bound to the exact result. The flag applies to
+ * the bf16 path; the fp32 path always uses fixed ranges.
  * ------------------------------------------------------------------------------------ */
+#define VSA_ATTN_DYNAMIC_SPLITS 1u
+
 size_t verify_attention_workspace_size(int B, int Hq, int Hkv, int D, int max_rows_per_seq,
                                        int max_kv_len);
 
 vsa_status verify_attention(const void* q, const void* k_cache, const void* v_cache,
                             vsa_dtype dtype, const int32_t* cu_rows, const int32_t* ctx_lens,
                             int B, int total_rows, int Hq, int Hkv, int D, int S_max,
-                            int max_rows_per_seq, int max_kv_len, float scale, float* out,
-                            void* workspace, size_t workspace_bytes, void* stream);
+                            int max_rows_per_seq, int max_kv_len, float scale,
+                            uint32_t flags, float* out, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------
  * verify_sample_accept

@@ -6,7 +6,7 @@ import verify_step_attention_amd as vsa
 from verify_step_attention_amd import workloads as wl
 
 
-def attention_gpu(w, dev=None, max_kv_len=None, workspace=None, stream=None):
+def attention_gpu(w, dev=None, max_kv_len=None, workspace=None, stream=None, flags=0):
     """Returns (out float32 numpy [T, Hq, D], device error word)."""
     dev = dev or wl.device_tensors(w)
     mkv = max_kv_len or w.max_kv_len
@@ -20,7 +20,7 @@ def attention_gpu(w, dev=None, max_kv_len=None, workspace=None, stream=None):
                      dtype=torch.float32, device="cuda")
     vsa.verify_attention(dev["q"], dev["k_cache"], dev["v_cache"], dev["cu_rows"],
                          dev["ctx_lens"], out, ws, max_rows_per_seq=w.max_rows,
-                         max_kv_len=mkv, stream=stream)
+                         max_kv_len=mkv, flags=flags, stream=stream)
     torch.cuda.synchronize()
     err = int(ws[:4].view(torch.int32).item())
     return out.cpu().numpy(), err

@@ -9,6 +9,7 @@ torch = pytest.importorskip("torch")
 if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
 
+import verify_step_attention_amd as vsa  # noqa: E402
 from verify_step_attention_amd import workloads as wl  # noqa: E402
 from gpu_helpers import attention_gpu, attention_oracle, assert_attention_close  # noqa: E402
 
@@ -17,12 +18,16 @@ def _log(msg):
     print(msg, flush=True)
 
 
+FLAGS = [0, vsa.ATTN_DYNAMIC_SPLITS]
+
+
+@pytest.mark.parametrize("flags", FLAGS)
 @pytest.mark.parametrize("name", ["tiny", "qwen3_4b", "batched", "verify_b4k4_ctx8192",
                                   "long", "swarm"])
-def test_workload_parity(name):
-    _log(f"attention parity: workload {name}")
+def test_workload_parity(name, flags):
+    _log(f"attention parity: workload {name} flags {flags}")
     w = wl.make_workload(name)
-    got, err = attention_gpu(w)
+    got, err = attention_gpu(w, flags=flags)
     assert err == 0
     assert_attention_close(got, attention_oracle(w))
 
@@ -36,13 +41,14 @@ def test_workload_parity(name):
     (16, 2, 64, wl.F32, [333, 40], [3, 9], None),                       # fp32, ragged
     (32, 8, 128, wl.BF16, [5], [4], 8192),                              # mostly empty splits
 ])
-def test_edge_shapes(case):
+@pytest.mark.parametrize("flags", FLAGS)
+def test_edge_shapes(case, flags):
     hq, hkv, d, dtype, ctxs, drafts, mkv = case
-    _log(f"attention edge case {case}")
+    _log(f"attention edge case {case} flags {flags}")
     w = _custom(hq, hkv, d, dtype, ctxs, drafts)
     if mkv is not None:
         mkv = min(mkv, w.s_max)
-    got, err = attention_gpu(w, max_kv_len=mkv)
+    got, err = attention_gpu(w, max_kv_len=mkv, flags=flags)
     assert err == 0
     assert_attention_close(got, attention_oracle(w))
 
@@ -92,6 +98,27 @@ def test_batch_invariance_and_workspace_reuse():
     x, _ = attention_gpu(w1, workspace=ws)
     y, _ = attention_gpu(w1, workspace=ws)
     assert np.array_equal(x, y)
+
+
+def test_dynamic_splits_reuse_workspace():
+    """Dynamic splits: the tile counters return to zero, so calls that reuse one workspace
+    (different sequences in between) all cover every key; results agree up to rounding."""
+    _log("attention dynamic splits: workspace reuse")
+    a = wl.make_workload("batched")
+    b = wl.make_workload("qwen3_4b")
+    ws = torch.zeros(1 << 24, dtype=torch.uint8, device="cuda")
+    ref_a, ref_b = attention_oracle(a), attention_oracle(b)
+    first = None
+    for rep in range(3):
+        x, err = attention_gpu(a, workspace=ws, flags=vsa.ATTN_DYNAMIC_SPLITS)
+        assert err == 0
+        assert_attention_close(x, ref_a)
+        if first is None:
+            first = x
+        assert np.allclose(x, first, rtol=1e-5, atol=1e-6)
+        y, err = attention_gpu(b, workspace=ws, flags=vsa.ATTN_DYNAMIC_SPLITS)
+        assert err == 0
+        assert_attention_close(y, ref_b)
 
 
 def test_device_error_word_on_bad_context():

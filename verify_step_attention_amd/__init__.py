@@ -21,6 +21,9 @@ DEVERR_PARAMS = 0x04
 DEVERR_NO_DRAFT_LOGITS = 0x08
 DEVERR_TIE_OVERFLOW = 0x10
 
+# verify_attention flags
+ATTN_DYNAMIC_SPLITS = 0x1
+
 # vsa_row_params, field for field
 ROW_PARAMS_DTYPE = np.dtype([("temperature", "<f4"), ("top_k", "<i4"), ("top_p", "<f4"),
                              ("presence_penalty", "<f4"), ("frequency_penalty", "<f4"),
@@ -57,7 +60,8 @@ def _lib():
         lib.verify_attention.restype = c_int
         lib.verify_attention.argtypes = [c_void, c_void, c_void, c_int, c_void, c_void,
                                          c_int, c_int, c_int, c_int, c_int, c_int, c_int,
-                                         c_int, c_float, c_void, c_void, c_size, c_void]
+                                         c_int, c_float, ctypes.c_uint32, c_void, c_void,
+                                         c_size, c_void]
         lib.verify_sample_accept_workspace_size.restype = c_size
         lib.verify_sample_accept_workspace_size.argtypes = [c_int] * 6
         lib.verify_sample_accept.restype = c_int
@@ -106,9 +110,10 @@ def verify_attention_workspace_size(B, Hq, Hkv, D, max_rows_per_seq, max_kv_len)
 
 
 def verify_attention(q, k_cache, v_cache, cu_rows, ctx_lens, out, workspace, *,
-                     max_rows_per_seq, max_kv_len, scale=0.0, stream=None):
+                     max_rows_per_seq, max_kv_len, scale=0.0, flags=0, stream=None):
     """q [T, Hq, D], k_cache / v_cache [B, Hkv, S_max, D] (bf16 or float32 tensors on the
-    GPU), cu_rows [B+1] / ctx_lens [B] int32, out [T, Hq, D] float32, workspace uint8."""
+    GPU), cu_rows [B+1] / ctx_lens [B] int32, out [T, Hq, D] float32, workspace uint8;
+    flags 0 or ATTN_DYNAMIC_SPLITS."""
     import torch
     total, hq, d = q.shape
     batch, hkv, s_max, d2 = k_cache.shape
@@ -128,7 +133,7 @@ def verify_attention(q, k_cache, v_cache, cu_rows, ctx_lens, out, workspace, *,
     st = _lib().verify_attention(_ptr(q), _ptr(k_cache), _ptr(v_cache), dtype, _ptr(cu_rows),
                                  _ptr(ctx_lens), batch, total, hq, hkv, d, s_max,
                                  int(max_rows_per_seq), int(max_kv_len), float(scale),
-                                 _ptr(out), _ptr(workspace), workspace.numel(),
+                                 int(flags), _ptr(out), _ptr(workspace), workspace.numel(),
                                  _stream(stream))
     _check(st, "verify_attention")
 

@@ -43,9 +43,11 @@ size_t verify_attention_workspace_size(int B, int Hq, int Hkv, int D, int max_ro
 vsa_status verify_attention(const void* q, const void* k_cache, const void* v_cache,
                             vsa_dtype dtype, const int32_t* cu_rows, const int32_t* ctx_lens,
                             int B, int total_rows, int Hq, int Hkv, int D, int S_max,
-                            int max_rows_per_seq, int max_kv_len, float scale, float* out,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+                            int max_rows_per_seq, int max_kv_len, float scale,
+                            uint32_t flags, float* out, void* workspace,
+                            size_t workspace_bytes, void* stream) {
     if (!q || !k_cache || !v_cache || !cu_rows || !ctx_lens || !out) return VSA_ERR_INVALID_ARG;
+    if (flags & ~VSA_ATTN_DYNAMIC_SPLITS) return VSA_ERR_INVALID_ARG;
     if (dtype != VSA_F32 && dtype != VSA_BF16) return VSA_ERR_INVALID_ARG;
     if (B < 1 || total_rows < B || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || S_max < 1 ||
         max_rows_per_seq < 1 || max_kv_len < 1 || max_kv_len > S_max ||
@@ -68,6 +70,7 @@ vsa_status verify_attention(const void* q, const void* k_cache, const void* v_ca
     a.out = out;
     a.part_o = reinterpret_cast<float*>(ws + plan.off_o);
     a.part_ml = reinterpret_cast<float2*>(ws + plan.off_ml);
+    a.tile_ctr = reinterpret_cast<uint32_t*>(ws + plan.off_ctr);
     a.err = reinterpret_cast<uint32_t*>(ws);
     a.batch = B;
     a.total_rows = total_rows;
@@ -79,6 +82,7 @@ vsa_status verify_attention(const void* q, const void* k_cache, const void* v_ca
     a.max_rows = max_rows_per_seq;
     a.max_kv_len = max_kv_len;
     a.nsplit = plan.nsplit;
+    a.dyn = (flags & VSA_ATTN_DYNAMIC_SPLITS) != 0 && plan.nsplit >= 2 && dtype == VSA_BF16;
     a.units = plan.units;
     a.mcap = plan.mcap;
     const float sc = scale == 0.f ? 1.f / sqrtf((float)D) : scale;

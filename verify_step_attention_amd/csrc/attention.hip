@@ -33,14 +33,12 @@ constexpr int kMergeGroup = 8;       // splits whose partials a merge thread loa
 constexpr float kLazyLog2 = 8.f;     // online softmax: rescale only past this growth (log2)
 
 // Block index -> (unit, split). Consecutive block ids go to different XCDs (round-robin
-// dispatch), so units are dealt out across XCDs and all splits of one unit land on one XCD,
-// where the partial states merged at the end stay in that XCD's L2.
-__device__ __forceinline__ void map_block(int bid, int units, int nsplit, int* unit,
-                                          int* split) {
-    const int xcd = bid & 7;
-    const int slot = bid >> 3;
-    *unit = (slot / nsplit) * 8 + xcd;
-    *split = slot % nsplit;
+// dispatch), so the splits of one unit are spread over the XCDs: the XCDs start their
+// workgroups microseconds apart, and splits that start early claim more of the unit's
+// tiles (see the tile loop of the bf16 kernel).
+__device__ __forceinline__ void map_block(int bid, int nsplit, int* unit, int* split) {
+    *unit = bid / nsplit;
+    *split = bid % nsplit;
 }
 
 struct SeqGeom {
@@ -203,9 +201,14 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const AttnArgs a) {
     __shared__ __attribute__((aligned(1024))) char vts[TAILB];
     __shared__ float stats[kStatFloats];
 
+    // every kernel argument in one round of scalar loads (the compiler would otherwise
+    // spread them over several dependent round trips before the first DMA)
+    asm volatile("" ::"s"(a.k), "s"(a.v), "s"(a.tile_ctr), "s"(a.cu_rows), "s"(a.ctx_lens),
+                 "s"(a.nsplit), "s"(a.hkv), "s"(a.s_max), "s"(a.max_kv_len), "s"(a.dyn),
+                 "s"(a.max_rows), "s"(a.q), "s"(a.out), "s"(a.part_o), "s"(a.part_ml),
+                 "s"(a.err), "s"(a.total_rows), "s"(a.group), "s"(a.mcap), "s"(a.scale_log2));
     int unit, split;
-    map_block(blockIdx.x, a.units, a.nsplit, &unit, &split);
-    if (unit >= a.units) return;
+    map_block(blockIdx.x, a.nsplit, &unit, &split);    // the grid is units x nsplit
     const int b = unit / a.hkv, g = unit % a.hkv;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -246,26 +249,40 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const AttnArgs a) {
             __builtin_amdgcn_global_load_lds(vbase + src, (lds_void*)(vt + blk * 1024), 16, 0, 0);
         }
     };
-    // Key ranges. With >= 4 splits, split s owns full tiles [F s / n, F (s + 1) / n) of the
-    // F = L / TK full tiles, and a tail of the last L mod TK keys, spread so that each split
-    // gets <= 32 of them (prefetched into a small buffer and computed alongside its first
-    // tile): every split then streams the same number of full tiles, where handing the
-    // remainder to one split would cost it a whole extra tile. With fewer splits the tiles
-    // are ceil(L / TK), the last one partial, and there is no tail.
+    // Tiles. With >= 4 splits the streamed tiles are the F = L / TK full ones, and the last
+    // L mod TK keys form a tail spread so that each split gets <= 32 of them (prefetched
+    // into a small buffer and computed alongside its first tile); with fewer splits the
+    // tiles are ceil(L / TK), the last one partial, and there is no tail.
+    // Static schedule: split s streams tiles [nt s / n, nt (s + 1) / n) in order, so the
+    // result does not depend on timing. Dynamic schedule (a.dyn): split s streams tile s
+    // first, and every later tile is claimed from the unit's counter (tile nsplit + the
+    // counter's old value), one claim ahead of the DMA, so splits that start early or
+    // stream fast take more tiles and the splits of a unit end together; the partial states
+    // then cover timing-dependent tile sets and the merged output varies in rounding only.
     const bool tails = a.nsplit >= 4;
-    auto tile_range = [&](int len, int* tb, int* te) __attribute__((always_inline)) {
-        const long nt = tails ? len / TK : (len + TK - 1) / TK;
-        *tb = (int)((long)split * nt / a.nsplit);
-        *te = (int)((long)(split + 1) * nt / a.nsplit);
+    const bool dyn = a.dyn != 0;
+    auto tile_count = [&](int len) __attribute__((always_inline)) {
+        return tails ? len / TK : (len + TK - 1) / TK;
+    };
+    auto static_end = [&](int nt) __attribute__((always_inline)) {
+        return (int)((uint32_t)((split + 1) * nt) / (uint32_t)a.nsplit);
+    };
+    auto first_tile = [&](int nt) __attribute__((always_inline)) {
+        const int t = dyn ? split : (int)((uint32_t)(split * nt) / (uint32_t)a.nsplit);
+        return t < (dyn ? nt : static_end(nt)) ? t : -1;
     };
     // The first tile is requested before the sequence geometry arrives, as if the sequence
     // held all kv_cap keys (the split's first tile is then the same whenever the sequence
-    // spans as many tiles as kv_cap). Rows past the true end are fixed up below.
+    // spans as many tiles as kv_cap, and always in the dynamic schedule). Rows past the
+    // true end are fixed up below.
     const int kv_cap = a.max_kv_len < a.s_max ? a.max_kv_len : a.s_max;
-    int t_spec, t_spec_end;
-    tile_range(kv_cap, &t_spec, &t_spec_end);
+    const int t_spec = first_tile(tile_count(kv_cap));
     key_lim = kv_cap;
-    if (t_spec < t_spec_end) issue_tile(t_spec, k0s, v0s);
+    if (t_spec >= 0) issue_tile(t_spec, k0s, v0s);
+    uint32_t* const ctr = a.tile_ctr + unit;
+    uint32_t claim = 0;                                // thread 0: the pending claim
+    if (dyn && tid == 0) claim = atomicAdd(ctr, 1u);
+    __shared__ int s_next[2];
 
     const SeqGeom s = seq_geometry(a, b, tid == 0 && split == 0 && g == 0);
     if (!s.ok) {
@@ -273,31 +290,31 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const AttnArgs a) {
         return;
     }
     const int L = s.ctx + s.rows;                      // keys of this sequence
-    int t_begin, t_end;
-    tile_range(L, &t_begin, &t_end);
+    const int nt = tile_count(L);
+    const int t_first = first_tile(nt);
+    const int t_last = dyn ? nt : static_end(nt);      // tiles below this one are streamed
     int tail_b = 0, tail_e = 0;
     if (tails) {
         const int f = L / TK * TK, rem = L - f;
-        tail_b = f + (int)((long)split * rem / a.nsplit);
-        tail_e = f + (int)((long)(split + 1) * rem / a.nsplit);
+        tail_b = f + (int)((uint32_t)(split * rem) / (uint32_t)a.nsplit);
+        tail_e = f + (int)((uint32_t)((split + 1) * rem) / (uint32_t)a.nsplit);
     }
     key_lim = L;
-    if (t_begin >= t_end && tail_b >= tail_e) {
+    // a split without a first tile has no tile at all (dynamic: nsplit + c > split >= nt)
+    if (t_first < 0 && tail_b >= tail_e) {
         __builtin_amdgcn_s_waitcnt(0);                 // no DMA outlives the workgroup
         attn_empty_split<D>(a, unit, split, s);
         return;
     }
-    if (t_begin >= t_end) {
-        // tail only
-    } else if (t_begin != t_spec || t_spec >= t_spec_end) {
+    if (t_first >= 0 && t_first != t_spec) {
         __builtin_amdgcn_s_waitcnt(0);                 // this wave's blocks are free again
-        issue_tile(t_begin, k0s, v0s);
-    } else if ((t_begin + 1) * TK > L) {
+        issue_tile(t_first, k0s, v0s);
+    } else if (t_first >= 0 && (t_first + 1) * TK > L) {
         // the speculative tile runs past the sequence end: rows from L on may hold
         // anything, and a V row is multiplied by P = 0, so those rows become zeros
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        const int r0 = L - t_begin * TK;
+        const int r0 = L - t_first * TK;
         for (int e = r0 * CH + tid; e < TK * CH; e += kThreads)
             *reinterpret_cast<uint4*>(v0s + (size_t)e * 16) = make_uint4(0, 0, 0, 0);
     }
@@ -450,22 +467,33 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const AttnArgs a) {
 
     // Tile t + 1 is in flight while tile t is computed. Before each tile: this wave's DMA
     // landed (s_waitcnt), then every wave's, and every wave is done with the other buffer.
-    if (t_begin >= t_end) {
+    // Thread 0 publishes the next tile (its claim has returned by then) in s_next[parity]:
+    // a slot is rewritten only two barriers after it was read.
+    auto next_tile = [&](int t, int par) __attribute__((always_inline)) {
+        if (tid == 0) s_next[par] = dyn ? a.nsplit + (int)claim : t + 1;
+        __syncthreads();
+        const int tn = s_next[par];
+        if (tn >= t_last) return -1;
+        if (dyn && tid == 0) claim = atomicAdd(ctr, 1u);
+        return tn;
+    };
+    if (t_first < 0) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         compute_tail();
     }
-    for (int t = t_begin; t < t_end; t += 2) {
+    for (int t = t_first; t >= 0;) {
         __builtin_amdgcn_s_waitcnt(0);                 // first time: the tail landed too
-        __syncthreads();
-        if (t + 1 < t_end) issue_tile(t + 1, k1s, v1s);
+        const int t1 = next_tile(t, 0);
+        if (t1 >= 0) issue_tile(t1, k1s, v1s);
         compute_tile(t, k0s, v0s);
-        if (t == t_begin) compute_tail();
-        if (t + 1 >= t_end) break;
+        if (t == t_first) compute_tail();
+        if (t1 < 0) break;
         __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (t + 2 < t_end) issue_tile(t + 2, k0s, v0s);
-        compute_tile(t + 1, k1s, v1s);
+        const int t2 = next_tile(t1, 1);
+        if (t2 >= 0) issue_tile(t2, k0s, v0s);
+        compute_tile(t1, k1s, v1s);
+        t = t2;
     }
 
     // ---- combine the key groups: wave w stores its 32 columns of O in tile buffer w,
@@ -508,7 +536,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const AttnArgs a) {
     __shared__ __attribute__((aligned(16))) char smem[SMEM];
 
     int unit, split;
-    map_block(blockIdx.x, a.units, a.nsplit, &unit, &split);
+    map_block(blockIdx.x, a.nsplit, &unit, &split);
     if (unit >= a.units) return;
     const int b = unit / a.hkv, g = unit % a.hkv;
     const int tid = threadIdx.x;
@@ -611,7 +639,10 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const AttnArgs a) {
     const int chunks = (a.mcap * D4 + kThreads - 1) / kThreads;
     const int unit = blockIdx.x / chunks;
     const int e = (blockIdx.x % chunks) * kThreads + threadIdx.x;
-    if (unit >= a.units || e >= a.mcap * D4) return;
+    if (unit >= a.units) return;
+    // the attention kernel has finished: its tile counter returns to zero for the next call
+    if (a.dyn && e == 0) __hip_atomic_store(a.tile_ctr + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (e >= a.mcap * D4) return;
     const int b = unit / a.hkv, g = unit % a.hkv;
     const int n = e / D4, d4 = e % D4;
     const int ns = a.nsplit;
@@ -677,6 +708,8 @@ AttnPlan plan_attention(int B, int Hq, int Hkv, int D, int max_rows, int max_kv_
     if (nsplit < 1) nsplit = 1;
     p.nsplit = nsplit;
     size_t off = 256;                                            // error word + pad
+    p.off_ctr = off;
+    off += ((size_t)p.units * 4 + 255) / 256 * 256;
     p.off_ml = off;
     off += ((size_t)p.units * nsplit * p.mcap * 8 + 255) / 256 * 256;
     p.off_o = off;
@@ -687,8 +720,7 @@ AttnPlan plan_attention(int B, int Hq, int Hkv, int D, int max_rows, int max_kv_
 
 hipError_t launch_attention(const AttnArgs& a, const AttnPlan& p, vsa_dtype dtype,
                             hipStream_t stream) {
-    const int groups = (p.units + 7) / 8;
-    const dim3 grid(groups * 8 * p.nsplit), block(kThreads);
+    const dim3 grid(p.units * p.nsplit), block(kThreads);
     if (dtype == VSA_BF16) {
         if (a.d == 128) {
             if (p.nb == 1) hipLaunchKernelGGL((attn_bf16_kernel<128, 1>), grid, block, 0, stream, a);

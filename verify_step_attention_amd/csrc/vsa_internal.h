@@ -176,17 +176,23 @@ __device__ __forceinline__ bool handoff_arrive(uint32_t* counter, uint32_t total
 
 // ---------------------------------------------------------------- attention launch args
 struct AttnArgs {
-    const void* q;
+    // what the first tile's DMA and the sequence geometry need, in the first 64 bytes (one
+    // scalar cache line of the kernel arguments)
     const void* k;
     const void* v;
+    uint32_t* tile_ctr;     // [units] tile claim counters (zero between calls)
     const int32_t* cu_rows;
     const int32_t* ctx_lens;
+    int nsplit, hkv, s_max, max_kv_len;
+    int dyn;                // splits claim tiles from tile_ctr (needs nsplit >= 2)
+    int max_rows;
+    // the rest
+    const void* q;
     float* out;
     float* part_o;          // [units][nsplit][mcap][D]
     float2* part_ml;        // [units][nsplit][mcap]   (running max (log2 units), sum)
     uint32_t* err;
-    int batch, total_rows, hq, hkv, group, d, s_max, max_rows, max_kv_len;
-    int nsplit, units, mcap;
+    int batch, total_rows, hq, group, d, units, mcap;
     float scale_log2;       // softmax scale * log2(e)
 };
 
@@ -197,7 +203,7 @@ struct AttnPlan {
     int nsplit;      // key splits per (sequence, KV head)
     int units;       // B * Hkv
     int tile;        // keys per workgroup tile
-    size_t off_ml, off_o, bytes;
+    size_t off_ctr, off_ml, off_o, bytes;
 };
 
 AttnPlan plan_attention(int B, int Hq, int Hkv, int D, int max_rows, int max_kv_len);
