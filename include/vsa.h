@@ -76,6 +76,11 @@ typedef enum vsa_dtype {
 #define VSA_DEVERR_TIE_OVERFLOW   0x10u /* more ids tie at a top-k threshold than the
                                            candidate capacity holds: the kept set is
                                            truncated to the capacity */
+#define VSA_DEVERR_WAIT_TIMEOUT   0x20u /* a workgroup waited about 0.2 s for its
+                                           sequence's acceptance result (the call's
+                                           workgroups could not all run at once, e.g.
+                                           other work held the GPU): the token drawn for
+                                           that sequence is unreliable */
 
 /* Per-sequence sampling parameters: the request parameters the pages list (temperature,
  * top_p, top_k, presence/frequency penalty, logprobs, top_logprobs; release v0.1.0 and

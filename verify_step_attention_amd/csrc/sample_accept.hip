@@ -57,9 +57,11 @@ __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1
             k0 += 0x9E3779B9u;
             k1 += 0xBB67AE85u;
         }
-        const uint32_t lo0 = 0xD2511F53u * c.x, hi0 = __umulhi(0xD2511F53u, c.x);
-        const uint32_t lo1 = 0xCD9E8D57u * c.z, hi1 = __umulhi(0xCD9E8D57u, c.z);
-        c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+        // each 32 x 32 -> 64-bit product in one instruction (v_mad_u64_u32)
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
+        c = make_uint4((uint32_t)(p1 >> 32) ^ c.y ^ k0, (uint32_t)p1,
+                       (uint32_t)(p0 >> 32) ^ c.w ^ k1, (uint32_t)p0);
     }
     return c;
 }
@@ -114,8 +116,11 @@ struct SeqMode {
 
 __device__ SeqMode seq_mode(const SampArgs& a, int b, uint32_t* errbits) {
     SeqMode m{};
-    m.r0 = a.cu_rows[b];
-    m.rows = a.cu_rows[b + 1] - m.r0;
+    // the row range and the parameters are requested together (b < B: both in bounds)
+    const int c0 = a.cu_rows[b], c1 = a.cu_rows[b + 1];
+    const vsa_row_params p = a.params[b];
+    m.r0 = c0;
+    m.rows = c1 - c0;
     m.k = m.rows - 1;
     m.d0 = m.r0 - b;
     m.valid = m.rows >= 1 && m.rows <= a.max_rows && m.r0 >= 0 &&
@@ -125,7 +130,6 @@ __device__ SeqMode seq_mode(const SampArgs& a, int b, uint32_t* errbits) {
         *errbits |= VSA_DEVERR_SEQ_SHAPE;
         return m;
     }
-    const vsa_row_params p = a.params[b];
     const bool bad = !(p.temperature >= 0.f) || !isfinite(p.temperature) || p.top_k < 0 ||
                      p.top_k > a.max_top_k || !(p.top_p > 0.f && p.top_p <= 1.f) ||
                      p.top_logprobs < 0 || p.top_logprobs > a.max_top_lp ||
@@ -762,10 +766,51 @@ __device__ void select_row(const SampArgs& a, const SeqMode& m, int q, FinalShar
 // AFTER_SELECT: run as its own kernel after the sweep and select_kernel (plain loads; the
 // truncated rows' thresholds and kept lists come from select_kernel); otherwise inside the
 // sweep's last workgroup of the sequence (hand-off loads; no truncated rows).
+// (max, normalizer) of a softmax row from its per-chunk (max, sum) entries, one wave: lane
+// holds entries lane, lane + 64, ... Every caller uses this same order of operations, so
+// every workgroup that merges a row gets the same bits.
+__device__ __forceinline__ void merge_row_wave(const float4 (&st)[kChunkLoads], float cs,
+                                               float* m_out, double* z_out) {
+    float bm = kNegInf;
+#pragma unroll
+    for (int u = 0; u < kChunkLoads; ++u) bm = fmaxf(bm, st[u].x);
+    bm = wave_max(bm);
+    // normalizer sum_j 2^((v_j - m) c) over the row, c = log2(e) / T (raw: T = 1)
+    double z = 0.0;
+    if (bm != kNegInf) {
+#pragma unroll
+        for (int u = 0; u < kChunkLoads; ++u)
+            if (st[u].x != kNegInf) z += (double)st[u].y * (double)exp2f((st[u].x - bm) * cs);
+        z = wave_sum_d(z);
+    }
+    *m_out = bm;
+    *z_out = z;
+}
+
+// A row's merged (max, normalizer) in its RowInfo slot, as hand-off words (fused race).
+__device__ __forceinline__ void publish_row_mz(RowInfo* ri, float m, double z) {
+    float2* w = reinterpret_cast<float2*>(ri);           // word 0: z, word 1: (m, argmax)
+    handoff_store(w, __builtin_bit_cast(float2, z));
+    handoff_store(w + 1, make_float2(m, 0.f));
+}
+__device__ __forceinline__ void read_row_mz(const RowInfo* ri, float* m, double* z) {
+    const float2* w = reinterpret_cast<const float2*>(ri);
+    const float2 w0 = handoff_load(w), w1 = handoff_load(w + 1);
+    *z = __builtin_bit_cast(double, w0);
+    *m = w1.x;
+}
+
+// Fused race hand-off word of a sequence: 0 = not yet; else 1 | kind << 1 | accepted << 8.
+__device__ __forceinline__ uint32_t race_word(int kind, int acc) {
+    return 1u | ((uint32_t)kind << 1) | ((uint32_t)acc << 8);
+}
+
 template <bool AFTER_SELECT>
 __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, FinalShared& fs,
                                   RowInfo* rinfo /* LDS, one per row of the list */,
-                                  const int* drafts_lds /* the K draft ids in LDS, or null */) {
+                                  const int* drafts_lds /* the K draft ids in LDS, or null */,
+                                  uint32_t* word_lds /* fused race: its hand-off word in LDS,
+                                                        or null */) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nrows = seq_nrows(m);
     uint32_t ebits = 0;
@@ -776,6 +821,7 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
     if (!drafts_lds && tid < m.k) fs.drafts[tid] = a.drafts[m.d0 + tid];
     int pre_d = -1, pre_c = 0;
     float pre_xt = 0.f, pre_xd = 0.f;
+    const int base_pos = (wave == 0 && m.sampled) ? a.positions[b] : 0;
     if (wave == 0 && lane < m.k) {
         pre_d = drafts_lds ? drafts_lds[lane] : a.drafts[m.d0 + lane];
         if (m.sampled && !m.topk && pre_d >= 0 && pre_d < a.vocab) {
@@ -811,26 +857,16 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
             const bool greedy_row = r.kind == 0 && !m.sampled;
             float bm = kNegInf, bv = kNegInf;
             int bi = kBigIdx;
+            double z = 0.0;
+            if (greedy_row) {
 #pragma unroll
-            for (int u = 0; u < kChunkLoads; ++u) {
-                if (greedy_row) {
+                for (int u = 0; u < kChunkLoads; ++u) {
                     const int ci = __float_as_int(st[x][u].w);
                     if (better(st[x][u].z, ci, bv, bi)) { bv = st[x][u].z; bi = ci; }
-                } else {
-                    bm = fmaxf(bm, st[x][u].x);
                 }
-            }
-            if (greedy_row) wave_argmax(bv, bi);
-            else bm = wave_max(bm);
-            // normalizer sum_j 2^((v_j - m) c) over the row, c = log2(e) / T (raw: T = 1)
-            double z = 0.0;
-            if (!greedy_row && bm != kNegInf) {
-                const float cs = r.kind == 2 ? kLog2e : kLog2e / m.temp;
-#pragma unroll
-                for (int u = 0; u < kChunkLoads; ++u)
-                    if (st[x][u].x != kNegInf)
-                        z += (double)st[x][u].y * (double)exp2f((st[x][u].x - bm) * cs);
-                z = wave_sum_d(z);
+                wave_argmax(bv, bi);
+            } else {
+                merge_row_wave(st[x], r.kind == 2 ? kLog2e : kLog2e / m.temp, &bm, &z);
             }
             if (lane == 0) {
                 RowInfo ri{};
@@ -841,6 +877,7 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
                 ri.kept_k = a.vocab;
                 ri.kept_p = a.vocab;
                 rinfo[q] = ri;
+                if (word_lds && !greedy_row) publish_row_mz(a.rows + r.slot, bm, z);
             }
         }
     }
@@ -861,11 +898,11 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
     }
 
     // ---- C: acceptance (wave 0)
+    int acc = 0;
+    int tok = -1;
+    bool pending = false;
+    RaceReq rq{};
     if (wave == 0) {
-        int acc = 0;
-        int tok = -1;
-        bool pending = false;
-        RaceReq rq{};
         if (!m.sampled) {
             while (acc < m.k) {
                 const int d = drafts[acc];
@@ -876,79 +913,76 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
             tok = rinfo[acc].argmax;
             if (tok < 0 || tok >= a.vocab) tok = 0;      // a row with no ordered value
         } else {
-            const int base_pos = a.positions[b];
-            // p_{t-1}(d_t) and q_t(d_t) of every draft, one lane per draft, loads in parallel
+            // p_{t-1}(d_t) and q_t(d_t) of every draft, one lane per draft (t = lane + 1)
             double pd_l = 0.0, qd_l = 0.0;
-            if (lane < m.k) {
+            const int d_l = lane < m.k ? pre_d : -1;
+            const bool valid_l = d_l >= 0 && d_l < a.vocab;
+            if (!m.topk && lane < m.k && valid_l) {
                 const int t = lane + 1;
-                const int d = pre_d;
-                if (d >= 0 && d < a.vocab) {
-                    if (m.topk) {
-                        // filled below, with the whole wave scanning the kept lists
-                    } else {
-                        int c = pre_c;
-                        const float xt = pre_xt;
-                        const float xd = pre_xd;
-                        for (int s2 = 0; s2 < t - 1; ++s2) c += drafts[s2] == d ? 1 : 0;
-                        const float cs = kLog2e / m.temp;
-                        const float zt = penalize(xt, c, m.pp, m.fp);
-                        pd_l = (double)exp2f((zt - rinfo[t - 1].m) * cs) / rinfo[t - 1].z;
-                        qd_l = (double)exp2f((xd - rinfo[m.rows + t - 1].m) * cs) /
-                               rinfo[m.rows + t - 1].z;
-                    }
-                }
+                int c = pre_c;
+                for (int s2 = 0; s2 < t - 1; ++s2) c += drafts[s2] == d_l ? 1 : 0;
+                const float cs = kLog2e / m.temp;
+                const float zt = penalize(pre_xt, c, m.pp, m.fp);
+                pd_l = (double)exp2f((zt - rinfo[t - 1].m) * cs) / rinfo[t - 1].z;
+                qd_l = (double)exp2f((pre_xd - rinfo[m.rows + t - 1].m) * cs) /
+                       rinfo[m.rows + t - 1].z;
             }
-            bool all = true;
-            for (int t = 1; t <= m.k; ++t) {
-                const int pos = base_pos + t - 1;
-                const int d = drafts[t - 1];
-                const bool valid = d >= 0 && d < a.vocab;
-                if (!valid) ebits |= VSA_DEVERR_DRAFT_ID;
-                double pd = 0.0, qd = 0.0;
-                const int pq = t - 1;            // target row t-1 in the row list
-                const int qq = m.rows + t - 1;   // draft row t
-                const RowRef rp = row_ref(a, m, pq), rqr = row_ref(a, m, qq);
-                if (valid) {
-                    if (m.topk) {
-                        pd = keep_lookup(a, rp.slot, rinfo[pq].kept_p, d);
-                        qd = keep_lookup(a, rqr.slot, rinfo[qq].kept_p, d);
-                    } else {
-                        pd = __shfl(pd_l, t - 1);
-                        qd = __shfl(qd_l, t - 1);
-                    }
+            if (!m.topk) {
+                // every draft's test at once (u_t from the stream (b, its position, tag 0));
+                // the accepted prefix ends at the first lane that rejects
+                bool ok = false;
+                if (lane < m.k) {
+                    const uint4 wu =
+                        philox_block(a.seed, 0u, (uint32_t)(base_pos + lane), (uint32_t)b, 0u);
+                    const double u = (double)(wu.x >> 8) * 5.9604644775390625e-08;
+                    ok = valid_l && u * qd_l < pd_l;
                 }
-                const uint4 wu = philox_block(a.seed, 0u, (uint32_t)pos, (uint32_t)b, 0u);
-                const double u = (double)(wu.x >> 8) * 5.9604644775390625e-08;
-                if (u * qd < pd) { ++acc; continue; }
-                all = false;
-                if (m.topk) {
-                    tok = keep_race(a, rp.slot, rinfo[pq].kept_p, rqr.slot, rinfo[qq].kept_p, b, pos);
-                    if (tok < 0 || tok >= a.vocab) tok = 0;
-                } else {
-                    pending = true;
+                const unsigned long long rej = __ballot(lane < m.k && !ok);
+                acc = rej ? __ffsll(rej) - 1 : m.k;
+                if (__ballot(lane < m.k && lane <= acc && !valid_l)) ebits |= VSA_DEVERR_DRAFT_ID;
+                pending = true;
+                rq.a = acc;
+                rq.pos = base_pos + acc;
+                if (acc < m.k) {                 // residual of target row acc, draft row acc+1
                     rq.kind = 1;
-                    rq.a = acc;
-                    rq.pos = pos;
-                    rq.m_p = rinfo[pq].m;
-                    rq.z_p = rinfo[pq].z;
-                    rq.m_q = rinfo[qq].m;
-                    rq.z_q = rinfo[qq].z;
-                }
-                break;
-            }
-            if (all) {
-                const int pos = base_pos + m.k;
-                const RowRef rp = row_ref(a, m, m.k);
-                if (m.topk) {
-                    tok = keep_race(a, rp.slot, rinfo[m.k].kept_p, -1, 0, b, pos);
-                    if (tok < 0 || tok >= a.vocab) tok = 0;
-                } else {
-                    pending = true;
+                    rq.m_p = rinfo[acc].m;
+                    rq.z_p = rinfo[acc].z;
+                    rq.m_q = rinfo[m.rows + acc].m;
+                    rq.z_q = rinfo[m.rows + acc].z;
+                } else {                         // bonus draw from target row K
                     rq.kind = 2;
-                    rq.a = acc;
-                    rq.pos = pos;
                     rq.m_p = rinfo[m.k].m;
                     rq.z_p = rinfo[m.k].z;
+                }
+            } else {
+                // truncated rows: probabilities from the kept lists, one draft at a time
+                bool all = true;
+                for (int t = 1; t <= m.k; ++t) {
+                    const int pos = base_pos + t - 1;
+                    const int d = drafts[t - 1];
+                    const bool valid = d >= 0 && d < a.vocab;
+                    if (!valid) ebits |= VSA_DEVERR_DRAFT_ID;
+                    double pd = 0.0, qd = 0.0;
+                    const int pq = t - 1;            // target row t-1 in the row list
+                    const int qq = m.rows + t - 1;   // draft row t
+                    const RowRef rp = row_ref(a, m, pq), rqr = row_ref(a, m, qq);
+                    if (valid) {
+                        pd = keep_lookup(a, rp.slot, rinfo[pq].kept_p, d);
+                        qd = keep_lookup(a, rqr.slot, rinfo[qq].kept_p, d);
+                    }
+                    const uint4 wu = philox_block(a.seed, 0u, (uint32_t)pos, (uint32_t)b, 0u);
+                    const double u = (double)(wu.x >> 8) * 5.9604644775390625e-08;
+                    if (u * qd < pd) { ++acc; continue; }
+                    all = false;
+                    tok = keep_race(a, rp.slot, rinfo[pq].kept_p, rqr.slot, rinfo[qq].kept_p, b,
+                                    pos);
+                    if (tok < 0 || tok >= a.vocab) tok = 0;
+                    break;
+                }
+                if (all) {
+                    const RowRef rp = row_ref(a, m, m.k);
+                    tok = keep_race(a, rp.slot, rinfo[m.k].kept_p, -1, 0, b, base_pos + m.k);
+                    if (tok < 0 || tok >= a.vocab) tok = 0;
                 }
             }
         }
@@ -961,18 +995,36 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
                 rq.z_x = rinfo[xq].z;
             }
         }
+    }
+    if (word_lds) {
+        // every wave's published row statistics have landed before the hand-off word
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+    if (wave == 0) {
         if (lane == 0) {
-            a.race[b] = rq;
+            if (word_lds) {
+                // fused race: the sequence's other workgroups wait for this word, then read
+                // the published statistics of the rows it names
+                const uint32_t wd = race_word(pending ? rq.kind : 0, acc);
+                __hip_atomic_store(a.race_flag + b, wd, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+                *word_lds = wd;
+            } else {
+                a.race[b] = rq;
+            }
             a.accepted[b] = acc;
         }
-        // emitted tokens, logprobs, diagnostics
+        // emitted tokens, logprobs, diagnostics. The token and logprob of a pending draw
+        // are the race's to write: no address gets plain stores from two workgroups of one
+        // kernel (their L2 write-backs could land in either order).
         for (int s = lane; s < m.rows; s += 64) {
             const int grow = m.r0 + s;
             int out = -1;
             if (s < acc) out = drafts[s];
-            else if (s == acc) out = pending ? -1 : tok;
-            a.out_tokens[grow] = out;
-            if (a.chosen_lp) {
+            else if (s == acc) out = tok;
+            if (!(pending && s == acc)) a.out_tokens[grow] = out;
+            if (a.chosen_lp && !(pending && s == acc)) {
                 float lpv = __builtin_nanf("");
                 if (m.logprobs && out >= 0) {
                     const int xq = m.rows + (m.sampled ? m.k : 0) + s;
@@ -998,6 +1050,162 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
 }
 
 // ------------------------------------------------------------------ sweep kernel
+// ------------------------------------------------------------------ full-vocabulary race
+// A categorical draw over the whole vocabulary as an exponential race: id j wins when its
+// key w_j / E_j is the largest, E_j = -ln U'_j standard exponential, U'_j from the draw's
+// Philox stream (tag 1), w = max(0, p - q) for a residual draw (kind 1) or p (kind 2);
+// when every residual weight is 0 the draw falls back to the race on p itself. Each chunk
+// of kChunk ids finds its two winners; the last chunk to arrive merges them.
+
+// The winners of this wave's ids of chunk c for request rq: (key, id, fallback key,
+// fallback id), valid in every lane. xp / xq hold the chunk of the target row (m.r0 + rq.a)
+// and, for kind 1, of the draft row (m.d0 + rq.a); dm[e] marks the drafts before row rq.a
+// that equal id e. Ids past the vocabulary hold -inf logits (weight 0: never a winner).
+__device__ float4 race_chunk(const SampArgs& a, const SeqMode& m, const RaceReq& rq, int b,
+                             int c, const int (&cnt)[kEpt], const uint32_t (&dm)[kEpt],
+                             const float (&xp)[kEpt], const float (&xq)[kEpt]) {
+    const int tid = threadIdx.x;
+    const int base = c * kChunk;
+    const float inv_zp = (float)(1.0 / rq.z_p);
+    const float inv_zq = rq.kind == 1 ? (float)(1.0 / rq.z_q) : 0.f;
+    const float cs = kLog2e / m.temp;
+    // Keys are w / (-log2 U') (the race's w / (-ln U') times ln 2, the same argmax), with
+    // the hardware exp2 / log2 / reciprocal (about one ulp each: the keys stay well inside
+    // the relative gap below which two ids count as tied). A thread visits its ids in
+    // increasing order, so a strict > keeps the lower id of a tie; w = 0 gives a key of 0,
+    // or NaN against an infinite 1 / E, neither of which wins.
+    float best = 0.f, fbest = 0.f;
+    int bi = kBigIdx, fbi = kBigIdx;
+#pragma unroll
+    for (int qd = 0; qd < kQuads; ++qd) {
+        const int j0 = base + 1024 * qd + 4 * tid;
+        const uint4 w = philox_block(a.seed, (uint32_t)j0 >> 2, (uint32_t)rq.pos, (uint32_t)b, 1u);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int e = 4 * qd + r;
+            const int j = j0 + r;
+            const float zp = penalize(xp[e], cnt[e] + __popc(dm[e]), m.pp, m.fp);
+            const float p = __builtin_amdgcn_exp2f((zp - rq.m_p) * cs) * inv_zp;
+            float rr = p;
+            if (rq.kind == 1) {
+                const float q = __builtin_amdgcn_exp2f((xq[e] - rq.m_q) * cs) * inv_zq;
+                rr = fmaxf(0.f, p - q);
+            }
+            // 1 / (-log2 U'); U' = 1 is E = 0 in the exact race, an infinite key (selected
+            // explicitly: -log2(1) may come out as -0, whose reciprocal is -inf)
+            const float uu = race_u(pick(w, r));
+            const float inv_e = uu < 1.f ? __builtin_amdgcn_rcpf(-__builtin_amdgcn_logf(uu))
+                                         : __builtin_inff();
+            const float key = rr * inv_e, fkey = p * inv_e;
+            const bool up = key > best, fup = fkey > fbest;
+            best = up ? key : best;
+            bi = up ? j : bi;
+            fbest = fup ? fkey : fbest;
+            fbi = fup ? j : fbi;
+        }
+    }
+    wave_argmax(best, bi);
+    // the race on p itself only decides when no residual weight anywhere is positive, so a
+    // wave that found one leaves its fallback out
+    if (best > 0.f) {
+        fbest = 0.f;
+        fbi = kBigIdx;
+    } else {
+        wave_argmax(fbest, fbi);
+    }
+    return make_float4(best, __int_as_float(bi), fbest, __int_as_float(fbi));
+}
+
+__device__ __forceinline__ float4 race_none() {
+    return make_float4(0.f, __int_as_float(kBigIdx), 0.f, __int_as_float(kBigIdx));
+}
+
+// The drawn id of sequence b from its chunk winners (one hand-off slot per chunk: atomics
+// on a shared winner serialize badly), merged by one wave; valid in lane 0.
+__device__ int race_winner(const SampArgs& a, int b, int lane) {
+    float bb = 0.f, fb = 0.f;
+    int bbi = kBigIdx, fbi2 = kBigIdx;
+    constexpr int kLoads = 4 * kChunkLoads;               // 4 waves x <= kMaxChunks chunks
+    float4 pt[kLoads];                                    // one round
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) {
+        const int cc = lane + 64 * u;
+        pt[u] = cc < 4 * a.nchunk
+                    ? handoff_load4(a.race_part + (size_t)b * a.nchunk * 4 + cc)
+                    : race_none();
+    }
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) {
+        const float4 o = pt[u];
+        const int oi = __float_as_int(o.y), ofi = __float_as_int(o.w);
+        if (o.x > bb || (o.x == bb && oi < bbi)) { bb = o.x; bbi = oi; }
+        if (o.z > fb || (o.z == fb && ofi < fbi2)) { fb = o.z; fbi2 = ofi; }
+    }
+    wave_argmax(bb, bbi);
+    wave_argmax(fb, fbi2);
+    int tok = bb > 0.f ? bbi : fbi2;
+    if (tok < 0 || tok >= a.vocab) tok = 0;               // a row with no ordered value
+    return tok;
+}
+
+// Fused race: thread 0 waits for the hand-off word that the sequence's last sweep
+// workgroup publishes. The sweep grid is launched fused only when all of its workgroups
+// fit on the GPU at once, so the publisher always runs; the wait still gives up after
+// kWaitTicks of the 100 MHz clock (error bit; the workgroup then joins with no winner).
+constexpr uint64_t kWaitTicks = 20000000ull;              // 0.2 s
+__device__ uint32_t wait_race_word(const SampArgs& a, int b) {
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    uint32_t w;
+    while (((w = __hip_atomic_load(a.race_flag + b, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT)) & 1u) == 0u) {
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
+            atomicOr(a.err, VSA_DEVERR_WAIT_TIMEOUT);
+            return 0u;
+        }
+        __builtin_amdgcn_s_sleep(4);
+    }
+    return w;
+}
+
+// Separate race kernel (top-k pipeline, or a sweep grid too large to be resident at once).
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void race_kernel(const SampArgs a) {
+    __shared__ int s_draft[kMaxSeqRows];
+    __shared__ int s_last;
+    preload_args(a);
+    const int b = blockIdx.x / a.nchunk, c = blockIdx.x % a.nchunk;
+    const int tid = threadIdx.x;
+    const RaceReq rq = a.race[b];                  // requested with the sequence's shape
+    uint32_t ebits = 0;
+    const SeqMode m = seq_mode(a, b, &ebits);
+    if (!m.valid || !m.sampled || m.topk || rq.kind == 0) return;
+    const int dreg = tid < m.k ? a.drafts[m.d0 + tid] : 0;
+    const int base = c * kChunk;
+    int cnt[kEpt];
+    load_counts<VEC>(a.counts ? a.counts + (size_t)b * a.vocab : nullptr, base, a.vocab, cnt);
+    float xp[kEpt], xq[kEpt];
+    load_chunk<VEC>(a.tl + (size_t)(m.r0 + rq.a) * a.vocab, base, a.vocab, xp);
+    if (rq.kind == 1) load_chunk<VEC>(a.dl + (size_t)(m.d0 + rq.a) * a.vocab, base, a.vocab, xq);
+    else
+#pragma unroll
+        for (int e = 0; e < kEpt; ++e) xq[e] = 0.f;
+    if (tid < m.k) s_draft[tid] = dreg;
+    __syncthreads();
+    uint32_t dm[kEpt];
+    draft_masks(s_draft, rq.a, base, dm);
+    const float4 part = race_chunk(a, m, rq, b, c, cnt, dm, xp, xq);
+    if ((tid & 63) == 0) handoff_store4(a.race_part + ((size_t)b * a.nchunk + c) * 4 + (tid >> 6), part);
+    if (!handoff_arrive(a.cnt_race + b, (uint32_t)a.nchunk, &s_last) || tid >= 64) return;
+    const int tok = race_winner(a, b, tid);
+    if (tid != 0) return;
+    const int grow = m.r0 + rq.a;
+    a.out_tokens[grow] = tok;
+    if (a.chosen_lp)
+        a.chosen_lp[grow] = rq.logprobs ? (float)((double)a.tl[(size_t)grow * a.vocab + tok] -
+                                                  (double)rq.m_x - log(rq.z_x))
+                                        : __builtin_nanf("");
+}
+
 template <bool VEC, bool TOPK>
 __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
     __shared__ float4 s_part[3 * kMaxSeqRows][4];
@@ -1008,18 +1216,19 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
     __shared__ FinalShared s_final;
     __shared__ RowInfo s_rinfo[3 * kMaxSeqRows];
 
+    preload_args(a);
     const int b = blockIdx.x / a.nchunk, c = blockIdx.x % a.nchunk;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the counts go out with the sequence's geometry and parameters; the draft ids and the
+    // first batch of rows are requested together once those arrive
+    const int base = c * kChunk;
+    int cnt[kEpt];
+    load_counts<VEC>(a.counts ? a.counts + (size_t)b * a.vocab : nullptr, base, a.vocab, cnt);
     uint32_t ebits = 0;
     const SeqMode m = seq_mode(a, b, &ebits);
     if (c == 0 && tid == 0 && ebits) atomicOr(a.err, ebits);
     if (!m.valid) return;
-    // the draft ids, the counts and the first batch of rows are all requested before any of
-    // them is waited for
     const int dreg = tid < m.k ? a.drafts[m.d0 + tid] : 0;
-    const int base = c * kChunk;
-    int cnt[kEpt];
-    load_counts<VEC>(a.counts ? a.counts + (size_t)b * a.vocab : nullptr, base, a.vocab, cnt);
     uint32_t valid = 0;
 #pragma unroll
     for (int e = 0; e < kEpt; ++e) valid |= (elem_id(base, e) < a.vocab ? 1u : 0u) << e;
@@ -1244,8 +1453,77 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
     // ---- the last chunk of the sequence to finish merges and accepts (fence-free)
     if (TOPK) return;                              // select_kernel and finalize_kernel follow
     __shared__ int s_last;
-    if (handoff_arrive(a.cnt_sweep + b, (uint32_t)a.nchunk, &s_last))
-        finalize_sequence<false>(a, m, b, s_final, s_rinfo, s_draft);
+    __shared__ uint32_t s_word;
+    __shared__ float s_mrow[2];
+    __shared__ double s_zrow[2];
+    const bool last = handoff_arrive(a.cnt_sweep + b, (uint32_t)a.nchunk, &s_last);
+    // a fused sampled sequence ends in a race (residual or bonus draw) that every chunk of
+    // it joins: its finalize publishes the hand-off word, the race's last arriver clears it
+    const bool race_here = a.fused && m.sampled && !m.topk;
+    if (last) finalize_sequence<false>(a, m, b, s_final, s_rinfo, s_draft, race_here ? &s_word : nullptr);
+    if (!race_here) return;
+    // ---- fused race over this chunk: the sweep's counts and draft masks, L2-warm rows
+    const int pos0 = a.positions[b];
+    if (tid == 0 && !last) s_word = wait_race_word(a, b);
+    __syncthreads();
+    const uint32_t wd = s_word;
+    const int kind = (int)((wd >> 1) & 3u), ra = (int)(wd >> 8);
+    float4 part = race_none();
+    if (kind != 0) {
+        float xp[kEpt], xq[kEpt];
+        load_chunk<VEC>(a.tl + (size_t)(m.r0 + ra) * a.vocab, base, a.vocab, xp);
+        if (kind == 1) load_chunk<VEC>(a.dl + (size_t)(m.d0 + ra) * a.vocab, base, a.vocab, xq);
+        else
+#pragma unroll
+            for (int e = 0; e < kEpt; ++e) xq[e] = 0.f;
+        // the finalize's (max, normalizer) of p's row (target row ra) and q's row (draft
+        // row ra + 1)
+        if (tid < (kind == 1 ? 2 : 1)) {
+            float mm;
+            double zz;
+            read_row_mz(a.rows + (tid == 0 ? m.r0 + ra : a.total_rows + m.d0 + ra), &mm, &zz);
+            s_mrow[tid] = mm;
+            s_zrow[tid] = zz;
+        }
+        __syncthreads();
+        RaceReq rq{};
+        rq.kind = kind;
+        rq.a = ra;
+        rq.pos = pos0 + ra;
+        rq.m_p = s_mrow[0];
+        rq.z_p = s_zrow[0];
+        if (kind == 1) {
+            rq.m_q = s_mrow[1];
+            rq.z_q = s_zrow[1];
+        }
+        uint32_t dmr[kEpt];
+        const uint32_t lm = low_bits(ra);
+#pragma unroll
+        for (int e = 0; e < kEpt; ++e) dmr[e] = dm[e] & lm;
+        part = race_chunk(a, m, rq, b, c, cnt, dmr, xp, xq);
+    }
+    if (lane == 0) handoff_store4(a.race_part + ((size_t)b * a.nchunk + c) * 4 + wave, part);
+    if (!handoff_arrive(a.cnt_race + b, (uint32_t)a.nchunk, &s_last) || tid >= 64) return;
+    // ---- the last chunk to arrive: the drawn token and its logprob
+    uint32_t w2 = wd;
+    if ((w2 & 1u) == 0u)                                  // this workgroup's wait gave up
+        w2 = __hip_atomic_load(a.race_flag + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int kind2 = (int)((w2 >> 1) & 3u), ra2 = (int)(w2 >> 8);
+    const int tok = race_winner(a, b, lane);
+    float lp = __builtin_nanf("");
+    if (kind2 != 0 && a.chosen_lp && m.logprobs && lane == 0) {
+        float mx;
+        double zx;
+        read_row_mz(a.rows + row_ref(a, m, m.rows + m.k + ra2).slot, &mx, &zx);
+        const int grow = m.r0 + ra2;
+        lp = (float)((double)a.tl[(size_t)grow * a.vocab + tok] - (double)mx - log(zx));
+    }
+    if (lane != 0) return;
+    __hip_atomic_store(a.race_flag + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (kind2 == 0) return;                               // the finalize emitted the token
+    const int grow = m.r0 + ra2;
+    a.out_tokens[grow] = tok;
+    if (a.chosen_lp) a.chosen_lp[grow] = lp;
 }
 
 // ------------------------------------------------------------------ top-k pipeline kernels
@@ -1253,6 +1531,7 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
 // or top-n row; every other workgroup returns at once.
 __global__ __launch_bounds__(kThreads) void select_kernel(const SampArgs a, int rows_cap) {
     __shared__ FinalShared s_final;
+    preload_args(a);
     const int b = blockIdx.x / rows_cap, q = blockIdx.x % rows_cap;
     uint32_t ebits = 0;
     const SeqMode m = seq_mode(a, b, &ebits);
@@ -1264,129 +1543,12 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const SampArgs a, int 
 __global__ __launch_bounds__(kThreads) void finalize_kernel(const SampArgs a) {
     __shared__ FinalShared s_final;
     __shared__ RowInfo s_rinfo[3 * kMaxSeqRows];
+    preload_args(a);
     const int b = blockIdx.x;
     uint32_t ebits = 0;
     const SeqMode m = seq_mode(a, b, &ebits);
     if (!m.valid) return;
-    finalize_sequence<true>(a, m, b, s_final, s_rinfo, nullptr);
-}
-
-// ------------------------------------------------------------------ race kernel
-template <bool VEC>
-__global__ __launch_bounds__(kThreads) void race_kernel(const SampArgs a) {
-    __shared__ int s_draft[kMaxSeqRows];
-    __shared__ float4 s_part[4];
-    __shared__ int s_last;
-    const int b = blockIdx.x / a.nchunk, c = blockIdx.x % a.nchunk;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const RaceReq rq = a.race[b];                  // requested with the sequence's shape
-    uint32_t ebits = 0;
-    const SeqMode m = seq_mode(a, b, &ebits);
-    if (!m.valid || !m.sampled || m.topk || rq.kind == 0) return;
-    const int dreg = tid < m.k ? a.drafts[m.d0 + tid] : 0;
-    const int base = c * kChunk;
-    int cnt[kEpt];
-    load_counts<VEC>(a.counts ? a.counts + (size_t)b * a.vocab : nullptr, base, a.vocab, cnt);
-    float xp[kEpt], xq[kEpt];
-    load_chunk<VEC>(a.tl + (size_t)(m.r0 + rq.a) * a.vocab, base, a.vocab, xp);
-    if (rq.kind == 1) load_chunk<VEC>(a.dl + (size_t)(m.d0 + rq.a) * a.vocab, base, a.vocab, xq);
-    if (tid < m.k) s_draft[tid] = dreg;
-    __syncthreads();
-    uint32_t dm[kEpt];
-    draft_masks(s_draft, rq.a, base, dm);
-    const float inv_zp = (float)(1.0 / rq.z_p);
-    const float inv_zq = rq.kind == 1 ? (float)(1.0 / rq.z_q) : 0.f;
-    const float cs = kLog2e / m.temp;
-
-    // residual race and, in case every residual weight is 0, the race on p itself.
-    // Keys are w / (-log2 U') (the race's w / (-ln U') times ln 2, the same argmax), with
-    // the hardware exp2 / log2 / reciprocal (about one ulp each: the keys stay well inside
-    // the relative gap below which two ids count as tied).
-    float best = 0.f, fbest = 0.f;
-    int bi = kBigIdx, fbi = kBigIdx;
-#pragma unroll
-    for (int qd = 0; qd < kQuads; ++qd) {
-        const int j0 = base + 1024 * qd + 4 * tid;
-        if (j0 >= a.vocab) continue;
-        const uint4 w = philox_block(a.seed, (uint32_t)j0 >> 2, (uint32_t)rq.pos, (uint32_t)b, 1u);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int e = 4 * qd + r;
-            const int j = j0 + r;
-            if (j >= a.vocab) continue;
-            const float zp = penalize(xp[e], cnt[e] + __popc(dm[e]), m.pp, m.fp);
-            const float p = __builtin_amdgcn_exp2f((zp - rq.m_p) * cs) * inv_zp;
-            float rr = p;
-            if (rq.kind == 1) {
-                const float q = __builtin_amdgcn_exp2f((xq[e] - rq.m_q) * cs) * inv_zq;
-                rr = fmaxf(0.f, p - q);
-            }
-            // 1 / (-log2 U'); U' = 1 is E = 0 in the exact race, an infinite key (selected
-            // explicitly: -log2(1) may come out as -0, whose reciprocal is -inf)
-            const float uu = race_u(pick(w, r));
-            const float inv_e = uu < 1.f ? __builtin_amdgcn_rcpf(-__builtin_amdgcn_logf(uu))
-                                         : __builtin_inff();
-            if (rr > 0.f) {
-                const float key = rr * inv_e;
-                if (key > best || (key == best && j < bi)) { best = key; bi = j; }
-            }
-            if (p > 0.f) {
-                const float key = p * inv_e;
-                if (key > fbest || (key == fbest && j < fbi)) { fbest = key; fbi = j; }
-            }
-        }
-    }
-    wave_argmax(best, bi);
-    wave_argmax(fbest, fbi);
-    // one (key, id, fallback key, fallback id) per chunk, merged by the last chunk to finish
-    // (one slot per workgroup: atomics on a shared winner serialize badly)
-    if (lane == 0) s_part[wave] = make_float4(best, __int_as_float(bi), fbest, __int_as_float(fbi));
-    __syncthreads();
-    if (tid == 0) {
-        float4 acc = s_part[0];
-        for (int w = 1; w < 4; ++w) {
-            const float4 o = s_part[w];
-            if (o.x > acc.x || (o.x == acc.x && __float_as_int(o.y) < __float_as_int(acc.y))) {
-                acc.x = o.x;
-                acc.y = o.y;
-            }
-            if (o.z > acc.z || (o.z == acc.z && __float_as_int(o.w) < __float_as_int(acc.w))) {
-                acc.z = o.z;
-                acc.w = o.w;
-            }
-        }
-        handoff_store4(a.race_part + (size_t)b * a.nchunk + c, acc);
-    }
-    if (!handoff_arrive(a.cnt_race + b, (uint32_t)a.nchunk, &s_last)) return;
-    if (tid < 64) {
-        float bb = 0.f, fb = 0.f;
-        int bbi = kBigIdx, fbi2 = kBigIdx;
-        float4 part[kChunkLoads];                         // <= kMaxChunks chunks, one round
-#pragma unroll
-        for (int u = 0; u < kChunkLoads; ++u) {
-            const int cc = lane + 64 * u;
-            part[u] = cc < a.nchunk ? handoff_load4(a.race_part + (size_t)b * a.nchunk + cc)
-                                    : make_float4(0.f, __int_as_float(kBigIdx), 0.f,
-                                                  __int_as_float(kBigIdx));
-        }
-#pragma unroll
-        for (int u = 0; u < kChunkLoads; ++u) {
-            const float4 o = part[u];
-            const int oi = __float_as_int(o.y), ofi = __float_as_int(o.w);
-            if (o.x > bb || (o.x == bb && oi < bbi)) { bb = o.x; bbi = oi; }
-            if (o.z > fb || (o.z == fb && ofi < fbi2)) { fb = o.z; fbi2 = ofi; }
-        }
-        wave_argmax(bb, bbi);
-        wave_argmax(fb, fbi2);
-        if (lane != 0) return;
-        int tok = bb > 0.f ? bbi : fbi2;
-        if (tok < 0 || tok >= a.vocab) tok = 0;          // a row with no ordered value
-        const int grow = m.r0 + rq.a;
-        a.out_tokens[grow] = tok;
-        if (a.chosen_lp && rq.logprobs)
-            a.chosen_lp[grow] = (float)((double)a.tl[(size_t)grow * a.vocab + tok] -
-                                        (double)rq.m_x - log(rq.z_x));
-    }
+    finalize_sequence<true>(a, m, b, s_final, s_rinfo, nullptr, nullptr);
 }
 
 }  // namespace
@@ -1420,18 +1582,42 @@ SampPlan plan_sample(int B, int total_rows, int V, int max_top_k, int max_top_lp
     p.off_race = off;
     off += up((size_t)B * sizeof(RaceReq));
     p.off_race_part = off;
-    off += up((size_t)B * p.nchunk * 16);
+    off += up((size_t)B * p.nchunk * 4 * 16);
+    p.off_race_flag = off;
+    off += up((size_t)B * 4);
     p.bytes = off;
     return p;
 }
 
-hipError_t launch_sample(const SampArgs& a, hipStream_t stream) {
+// Workgroups of the lean sweep kernel that the device holds at once (cached per device).
+static int sweep_capacity(bool vec) {
+    static int cache[2][64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int& c = cache[vec ? 1 : 0][dev];
+    if (c == 0) {
+        int per_cu = 0, cus = 0;
+        const void* k = vec ? reinterpret_cast<const void*>(&sweep_kernel<true, false>)
+                            : reinterpret_cast<const void*>(&sweep_kernel<false, false>);
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kThreads, 0) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            per_cu = cus = 0;
+        c = per_cu * cus > 0 ? per_cu * cus : -1;
+    }
+    return c;
+}
+
+hipError_t launch_sample(const SampArgs& args, hipStream_t stream) {
+    SampArgs a = args;
     const dim3 grid((unsigned)a.batch * a.nchunk), block(kThreads);
     const bool vec = (a.vocab % 4) == 0;
     // Truncated (top-k) and top-n rows need the candidate tables and the selection code,
     // which only the TOPK variant carries (a parameter asking for them is rejected when
     // max_top_k and max_top_logprobs are 0).
     const bool topk = a.max_top_k > 0 || a.max_top_lp > 0;
+    // Without them the sweep workgroups run the full-vocabulary race themselves, waiting
+    // for their sequence's acceptance step, when the whole grid is resident at once.
+    a.fused = !topk && (long)a.batch * a.nchunk <= (long)sweep_capacity(vec);
     if (vec) {
         if (topk) hipLaunchKernelGGL((sweep_kernel<true, true>), grid, block, 0, stream, a);
         else hipLaunchKernelGGL((sweep_kernel<true, false>), grid, block, 0, stream, a);
@@ -1452,8 +1638,9 @@ hipError_t launch_sample(const SampArgs& a, hipStream_t stream) {
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    // Always launched: only the device knows which sequences end in a full-vocabulary
-    // draw; every other workgroup returns at once.
+    if (a.fused) return hipSuccess;
+    // Only the device knows which sequences end in a full-vocabulary draw; every other
+    // workgroup returns at once.
     if (vec) hipLaunchKernelGGL(race_kernel<true>, grid, block, 0, stream, a);
     else hipLaunchKernelGGL(race_kernel<false>, grid, block, 0, stream, a);
     return hipGetLastError();

@@ -269,13 +269,29 @@ struct SampArgs {
     RowInfo* rows;                 // [slots]
     KeepEntry* keep;               // [2T - B][keepcap]
     RaceReq* race;                 // [B]
-    float4* race_part;             // [B][nchunk] per-chunk race winners
+    float4* race_part;             // [B][nchunk][4] race winners per (chunk, wave)
+    uint32_t* race_flag;           // [B] race request published (zero between calls)
+    int fused;                     // the sweep workgroups run the race themselves
 };
+
+// Every kernel argument in one round of scalar loads: the compiler otherwise spreads them
+// over several dependent round trips ahead of the first memory request.
+__device__ __forceinline__ void preload_args(const SampArgs& a) {
+    asm volatile("" ::"s"(a.tl), "s"(a.dl), "s"(a.drafts), "s"(a.cu_rows), "s"(a.counts),
+                 "s"(a.params), "s"(a.positions), "s"(a.seed), "s"(a.batch),
+                 "s"(a.total_rows), "s"(a.vocab), "s"(a.max_rows), "s"(a.max_top_k),
+                 "s"(a.max_top_lp), "s"(a.nchunk), "s"(a.capc), "s"(a.keepcap));
+    asm volatile("" ::"s"(a.accepted), "s"(a.out_tokens), "s"(a.chosen_lp), "s"(a.top_vals),
+                 "s"(a.top_ids), "s"(a.diag_thr), "s"(a.diag_kept), "s"(a.err),
+                 "s"(a.cnt_sweep), "s"(a.cnt_race), "s"(a.stats), "s"(a.cand),
+                 "s"(a.cand_meta), "s"(a.rows), "s"(a.keep), "s"(a.race), "s"(a.race_part),
+                 "s"(a.race_flag), "s"(a.fused));
+}
 
 struct SampPlan {
     int nchunk, capc, keepcap, slots;
     size_t off_cnt_sweep, off_cnt_race, off_stats, off_cand, off_meta, off_rows, off_keep,
-        off_race, off_race_part, bytes;
+        off_race, off_race_part, off_race_flag, bytes;
 };
 
 SampPlan plan_sample(int B, int total_rows, int V, int max_top_k, int max_top_lp);
