@@ -57,3 +57,50 @@ def verify_attention(q, k_cache, v_cache, cu_rows, ctx_lens, num_q_heads, num_kv
                 out[r0 + i, heads] = ((w @ vals) / w.sum(axis=1, keepdims=True)).astype(
                     np.float32)
     return out
+
+
+# ---------------------------------------------------------------------- quantized K/V cache
+# The pages' --kv-bits 4|8 option keeps the target's K/V cache quantized from token 0
+# (mlx-dspark Changelog [0.3.0] "Added": KV-cache quantization; [0.13.1]: 8 bits halve and
+# 4 bits quarter the per-token cache). They do not give the format; the reading used here
+# is affine quantization in groups of 64 consecutive head dimensions, the grouping the pages
+# name for weights:
+#   value = scale * code + bias,   code unsigned (8 bits: 0..255, 4 bits: 0..15),
+#   one (scale, bias) pair of fp16 per group.
+# Layouts (row-major):
+#   codes  [B, Hkv, S_max, D]       uint8 (8 bits)
+#          [B, Hkv, S_max, D / 2]   uint8 (4 bits: element 2i in the low nibble, 2i + 1 in
+#                                   the high nibble)
+#   sb     [B, Hkv, S_max, D / 64, 2]  float16 (scale, bias)
+# Attention over a quantized cache is the definition above applied to the dequantized
+# values, each computed exactly in fp64 (an fp16 times an integer below 2^8, plus an fp16).
+
+KV_GROUP = 64
+
+
+def dequantize_kv(codes, sb, bits):
+    """Quantized cache -> float64 [B, Hkv, S, D] (the exact values scale * code + bias)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    sb = np.asarray(sb, dtype=np.float16)
+    if bits == 8:
+        c = codes.astype(np.float64)
+    elif bits == 4:
+        lo = (codes & 0x0F).astype(np.float64)
+        hi = (codes >> 4).astype(np.float64)
+        c = np.stack([lo, hi], axis=-1).reshape(codes.shape[:-1] + (codes.shape[-1] * 2,))
+    else:
+        raise ValueError(f"bits must be 4 or 8, got {bits}")
+    d = c.shape[-1]
+    assert d % KV_GROUP == 0 and sb.shape[-2:] == (d // KV_GROUP, 2)
+    scale = np.repeat(sb[..., 0].astype(np.float64), KV_GROUP, axis=-1)
+    bias = np.repeat(sb[..., 1].astype(np.float64), KV_GROUP, axis=-1)
+    return scale * c + bias
+
+
+def verify_attention_kvq(q, k_codes, k_sb, v_codes, v_sb, bits, cu_rows, ctx_lens,
+                         num_q_heads, num_kv_heads, scale=None):
+    """Verify attention over a quantized K/V cache: the same definition on the dequantized
+    keys and values."""
+    return verify_attention(q, dequantize_kv(k_codes, k_sb, bits),
+                            dequantize_kv(v_codes, v_sb, bits), cu_rows, ctx_lens,
+                            num_q_heads, num_kv_heads, scale=scale)

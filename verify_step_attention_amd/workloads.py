@@ -159,6 +159,56 @@ def _default_params(name, batch):
     raise KeyError(name)
 
 
+def quantize_kv(x, bits, group=64):
+    """Input generator for the quantized K/V cache format: float32 [..., D] -> (codes uint8,
+    (scale, bias) float16 pairs [..., D / group, 2]). Per group of `group` dimensions:
+    bias = fp16(min), scale = fp16((max - min) / (2^bits - 1)), code = the nearest level,
+    clamped; 4-bit codes pack two to a byte, element 2i in the low nibble. A group holding
+    NaN (poison past a sequence's keys) gets codes of all ones and NaN scale and bias."""
+    x = np.asarray(x, dtype=np.float32)
+    d = x.shape[-1]
+    assert d % group == 0 and bits in (4, 8)
+    g = x.reshape(x.shape[:-1] + (d // group, group))
+    lo = np.nanmin(np.where(np.isnan(g), np.inf, g), axis=-1)
+    hi = np.nanmax(np.where(np.isnan(g), -np.inf, g), axis=-1)
+    bad = np.isnan(g).any(axis=-1)
+    lo = np.where(bad, 0.0, lo)
+    hi = np.where(bad, 0.0, hi)
+    qmax = (1 << bits) - 1
+    scale = ((hi - lo) / qmax).astype(np.float16)
+    bias = lo.astype(np.float16)
+    s32 = scale.astype(np.float32)[..., None]
+    b32 = bias.astype(np.float32)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        c = np.where(s32 > 0, np.rint((g - b32) / s32), 0.0)
+    c = np.clip(np.nan_to_num(c), 0, qmax).astype(np.uint8)
+    c = np.where(bad[..., None], np.uint8(qmax), c).reshape(x.shape)
+    sb = np.stack([scale, bias], axis=-1)
+    sb[bad] = np.float16(np.nan)
+    if bits == 4:
+        c = (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+    return np.ascontiguousarray(c), np.ascontiguousarray(sb)
+
+
+@dataclass
+class KvQuant:
+    """A workload's K/V cache in the quantized format (see quantize_kv)."""
+    bits: int
+    k_codes: np.ndarray
+    k_sb: np.ndarray
+    v_codes: np.ndarray
+    v_sb: np.ndarray
+
+
+def quantized_cache(w, bits):
+    """The workload's K/V cache (its bf16 or fp32 values, NaN past each sequence's keys)
+    in the quantized format."""
+    k, v = w.kv_f32()
+    kc, ks = quantize_kv(k, bits)
+    vc, vs = quantize_kv(v, bits)
+    return KvQuant(bits=bits, k_codes=kc, k_sb=ks, v_codes=vc, v_sb=vs)
+
+
 def make_workload(name, *, batch=None, drafts=None, ctx=None, vocab=None, with_kv=True,
                   seed_offset=0):
     """Build the named workload. Overrides (batch, drafts per sequence, context, vocab)
