@@ -148,6 +148,33 @@ vsa_status verify_attention(const void* q, const void* k_cache, const void* v_ca
                             size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------
+ * verify_attention_kvq
+ *
+ * verify_attention over a quantized K/V cache (Changelog [0.3.0] "Added": KV-cache
+ * quantization, --kv-bits 4|8, the target's cache quantized from token 0; [0.13.1]: 8 bits
+ * halve and 4 bits quarter the per-token cache). The pages do not give the format; this
+ * library reads it as affine quantization in groups of 64 consecutive head dimensions:
+ *     value = scale * code + bias,  one (scale, bias) pair of fp16 per group,
+ *     code unsigned: 8 bits (0..255) or 4 bits (0..15, two per byte, element 2i in the
+ *     low nibble).
+ * The result is the definition above applied to those exact values (fp32 accumulation).
+ *
+ *   q          [total_rows, Hq, D]               bf16
+ *   k_codes    [B, Hkv, S_max, D * bits / 8]     uint8   (v_codes the same)
+ *   k_sb       [B, Hkv, S_max, D / 64, 2]        fp16 (scale, bias)   (v_sb the same)
+ *   bits       8 or 4
+ *   every other argument as for verify_attention (same workspace size query)
+ * Codes and (scale, bias) of positions >= ctx_b + R_b are never used in the result.
+ * ------------------------------------------------------------------------------------ */
+vsa_status verify_attention_kvq(const void* q, const uint8_t* k_codes, const void* k_sb,
+                                const uint8_t* v_codes, const void* v_sb, int bits,
+                                const int32_t* cu_rows, const int32_t* ctx_lens, int B,
+                                int total_rows, int Hq, int Hkv, int D, int S_max,
+                                int max_rows_per_seq, int max_kv_len, float scale,
+                                uint32_t flags, float* out, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------
  * verify_sample_accept
  *
  * Row i of sequence b (i = 0..K_b, K_b = R_b - 1) holds the target logits that decide the

@@ -88,6 +88,22 @@ def test_attention_host_checks(lib):
     assert _attention(lib, ws_bytes=1024) == WORKSPACE
 
 
+def _attention_kvq(lib, *, q=FAKE, bits=8, d=128, flags=0, ws_bytes=1 << 30, sb=FAKE):
+    return lib.verify_attention_kvq(q, FAKE, sb, FAKE, FAKE, bits, FAKE, FAKE, 4, 20, 32, 8,
+                                    d, 8256, 5, 8197, 0.0, flags, FAKE, FAKE * 256, ws_bytes,
+                                    None)
+
+
+def test_attention_kvq_host_checks(lib):
+    assert _attention_kvq(lib, q=None) == INVALID_ARG
+    assert _attention_kvq(lib, sb=None) == INVALID_ARG
+    assert _attention_kvq(lib, bits=6) == INVALID_ARG
+    assert _attention_kvq(lib, bits=16) == INVALID_ARG
+    assert _attention_kvq(lib, flags=4) == INVALID_ARG
+    assert _attention_kvq(lib, d=96) == UNSUPPORTED
+    assert _attention_kvq(lib, bits=4, ws_bytes=1024) == WORKSPACE
+
+
 def test_sample_workspace_size_limits(lib):
     ok = lib.verify_sample_accept_workspace_size(4, 20, 151936, 5, 0, 0)
     assert ok > 0

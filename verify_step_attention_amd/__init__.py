@@ -30,8 +30,8 @@ ROW_PARAMS_DTYPE = np.dtype([("temperature", "<f4"), ("top_k", "<i4"), ("top_p",
                              ("logprobs", "<i4"), ("top_logprobs", "<i4")])
 
 EXPORTED_SYMBOLS = ("vsa_version", "vsa_status_string", "verify_attention_workspace_size",
-                    "verify_attention", "verify_sample_accept_workspace_size",
-                    "verify_sample_accept")
+                    "verify_attention", "verify_attention_kvq",
+                    "verify_sample_accept_workspace_size", "verify_sample_accept")
 
 
 class VsaError(RuntimeError):
@@ -62,6 +62,11 @@ def _lib():
                                          c_int, c_int, c_int, c_int, c_int, c_int, c_int,
                                          c_int, c_float, ctypes.c_uint32, c_void, c_void,
                                          c_size, c_void]
+        lib.verify_attention_kvq.restype = c_int
+        lib.verify_attention_kvq.argtypes = [c_void, c_void, c_void, c_void, c_void, c_int,
+                                             c_void, c_void, c_int, c_int, c_int, c_int,
+                                             c_int, c_int, c_int, c_int, c_float,
+                                             ctypes.c_uint32, c_void, c_void, c_size, c_void]
         lib.verify_sample_accept_workspace_size.restype = c_size
         lib.verify_sample_accept_workspace_size.argtypes = [c_int] * 6
         lib.verify_sample_accept.restype = c_int
@@ -136,6 +141,38 @@ def verify_attention(q, k_cache, v_cache, cu_rows, ctx_lens, out, workspace, *,
                                  int(flags), _ptr(out), _ptr(workspace), workspace.numel(),
                                  _stream(stream))
     _check(st, "verify_attention")
+
+
+def verify_attention_kvq(q, k_codes, k_sb, v_codes, v_sb, bits, cu_rows, ctx_lens, out,
+                         workspace, *, max_rows_per_seq, max_kv_len, scale=0.0, flags=0,
+                         stream=None):
+    """verify_attention over a quantized K/V cache: q [T, Hq, D] bf16, k_codes / v_codes
+    [B, Hkv, S_max, D * bits / 8] uint8, k_sb / v_sb [B, Hkv, S_max, D / 64, 2] float16
+    (scale, bias), bits 8 or 4; the rest as verify_attention (same workspace size)."""
+    import torch
+    total, hq, d = q.shape
+    if bits not in (4, 8):
+        raise ValueError("bits must be 4 or 8")
+    batch, hkv, s_max, rowb = k_codes.shape
+    if q.dtype != torch.bfloat16 or out.dtype != torch.float32:
+        raise ValueError("q must be bfloat16 and out float32")
+    if rowb * 8 != d * bits or tuple(v_codes.shape) != tuple(k_codes.shape):
+        raise ValueError("code arrays disagree with q / bits")
+    if k_codes.dtype != torch.uint8 or v_codes.dtype != torch.uint8:
+        raise ValueError("codes must be uint8")
+    if tuple(k_sb.shape) != (batch, hkv, s_max, d // 64, 2) or \
+            tuple(v_sb.shape) != tuple(k_sb.shape) or k_sb.dtype != torch.float16 or \
+            v_sb.dtype != torch.float16:
+        raise ValueError("scale / bias arrays must be float16 [B, Hkv, S_max, D/64, 2]")
+    for t in (q, k_codes, k_sb, v_codes, v_sb, cu_rows, ctx_lens, out, workspace):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    st = _lib().verify_attention_kvq(_ptr(q), _ptr(k_codes), _ptr(k_sb), _ptr(v_codes),
+                                     _ptr(v_sb), int(bits), _ptr(cu_rows), _ptr(ctx_lens),
+                                     batch, total, hq, hkv, d, s_max, int(max_rows_per_seq),
+                                     int(max_kv_len), float(scale), int(flags), _ptr(out),
+                                     _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "verify_attention_kvq")
 
 
 # ----------------------------------------------------------------------------- sampling

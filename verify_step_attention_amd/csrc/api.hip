@@ -92,6 +92,63 @@ vsa_status verify_attention(const void* q, const void* k_cache, const void* v_ca
     return VSA_OK;
 }
 
+vsa_status verify_attention_kvq(const void* q, const uint8_t* k_codes, const void* k_sb,
+                                const uint8_t* v_codes, const void* v_sb, int bits,
+                                const int32_t* cu_rows, const int32_t* ctx_lens, int B,
+                                int total_rows, int Hq, int Hkv, int D, int S_max,
+                                int max_rows_per_seq, int max_kv_len, float scale,
+                                uint32_t flags, float* out, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    if (!q || !k_codes || !k_sb || !v_codes || !v_sb || !cu_rows || !ctx_lens || !out)
+        return VSA_ERR_INVALID_ARG;
+    if (bits != 8 && bits != 4) return VSA_ERR_INVALID_ARG;
+    if (flags & ~VSA_ATTN_DYNAMIC_SPLITS) return VSA_ERR_INVALID_ARG;
+    if (B < 1 || total_rows < B || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || S_max < 1 ||
+        max_rows_per_seq < 1 || max_kv_len < 1 || max_kv_len > S_max ||
+        total_rows > B * max_rows_per_seq || !(scale >= 0.f) || !isfinite(scale))
+        return VSA_ERR_INVALID_ARG;
+    if ((D != 64 && D != 128) || max_rows_per_seq > kMaxRowsPerSeq ||
+        (Hq / Hkv) * max_rows_per_seq > 128)
+        return VSA_ERR_UNSUPPORTED;
+    const AttnPlan plan = plan_attention(B, Hq, Hkv, D, max_rows_per_seq, max_kv_len);
+    if (!workspace || !aligned256(workspace) || workspace_bytes < plan.bytes)
+        return VSA_ERR_WORKSPACE;
+
+    char* ws = static_cast<char*>(workspace);
+    AttnArgs a{};
+    a.q = q;
+    a.k = k_codes;
+    a.v = v_codes;
+    a.ksb = k_sb;
+    a.vsb = v_sb;
+    a.bits = bits;
+    a.cu_rows = cu_rows;
+    a.ctx_lens = ctx_lens;
+    a.out = out;
+    a.part_o = reinterpret_cast<float*>(ws + plan.off_o);
+    a.part_ml = reinterpret_cast<float2*>(ws + plan.off_ml);
+    a.tile_ctr = reinterpret_cast<uint32_t*>(ws + plan.off_ctr);
+    a.err = reinterpret_cast<uint32_t*>(ws);
+    a.batch = B;
+    a.total_rows = total_rows;
+    a.hq = Hq;
+    a.hkv = Hkv;
+    a.group = Hq / Hkv;
+    a.d = D;
+    a.s_max = S_max;
+    a.max_rows = max_rows_per_seq;
+    a.max_kv_len = max_kv_len;
+    a.nsplit = plan.nsplit;
+    a.dyn = (flags & VSA_ATTN_DYNAMIC_SPLITS) != 0 && plan.nsplit >= 2;
+    a.units = plan.units;
+    a.mcap = plan.mcap;
+    const float sc = scale == 0.f ? 1.f / sqrtf((float)D) : scale;
+    a.scale_log2 = sc * 1.4426950408889634f;
+    if (launch_attention(a, plan, VSA_BF16, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return VSA_ERR_LAUNCH;
+    return VSA_OK;
+}
+
 }  // extern "C"
 
 extern "C" {

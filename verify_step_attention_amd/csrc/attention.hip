@@ -521,6 +521,554 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const AttnArgs a) {
     attn_epilogue<D, KG, NB>(a, ob, stats, unit, split, g, s, OS);
 }
 
+// ------------------------------------------------------------- bf16 Q x quantized K / V
+// K and V arrive as unsigned codes (8 or 4 bits) with an fp16 (scale, bias) pair per group
+// of 64 dimensions: value = scale * code + bias. The codes go to the MFMAs as exact
+// integers (at most 255), so no dequantized value is ever rounded:
+//   S[t][n] = sum_g ( s_g[t] * sum_{d in g} code[t][d] q[n][d] + b_g[t] * sum_{d in g} q[n][d] )
+//   O[n][d] = sum_t (P[n][t] s_g[t]) code[t][d] + sum_t P[n][t] b_g[t]      (g = group of d)
+// QK^T runs in fp16 (K codes built from their bits, q scaled by a power of two per column
+// so that it converts exactly); PV runs in bf16 on P s_g split into two bf16 terms (16
+// significant bits). The fp16 (scale, bias) enter fp32 arithmetic through mixed fma.
+// The same tile schedule as the bf16 kernel (static or claimed tiles, tails, speculative
+// first tile). Code rows (D * bits / 8 bytes) are staged by DMA with their 16-byte chunks
+// permuted per row (chunk c at c ^ swz(r)) so the QK^T operand reads (32 lanes, 8 codes of
+// 32 consecutive rows) hit at most two lanes per bank; the (scale, bias) rows follow the
+// codes of each buffer. V codes are expanded once per tile into bf16 integers in the bf16
+// kernel's V layout, so the transposed PV operand reads are the same.
+template <int ROWB>
+__device__ __forceinline__ int code_swz(int r) {
+    return (r / (256 / ROWB)) & (ROWB / 16 - 1);
+}
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// K codes -> fp16 operands of the QK^T MFMA, exact: a code c (< 1024) under the exponent
+// bits of 1024 is the fp16 number 1024 + c, and one packed subtraction of 1024 leaves c.
+// 8-bit: dwords w0, w1 hold codes 0..7 in byte order. 4-bit: dword w holds codes 0..7 in
+// nibble order; the result holds them as (0, 4, 1, 5, 2, 6, 3, 7), and the Q operand is
+// permuted the same way.
+__device__ __forceinline__ f16x2 f16_pair_minus_1024(uint32_t d) {
+    return __builtin_bit_cast(f16x2, d) - f16x2{(_Float16)1024.f, (_Float16)1024.f};
+}
+__device__ __forceinline__ f16x8 kcodes8_to_f16(uint32_t w0, uint32_t w1) {
+    // byte select over {0x64646464 : w}: selectors 0..3 pick bytes of w, 4 picks 0x64
+    constexpr uint32_t kExp = 0x64646464u;
+    const f16x2 p0 = f16_pair_minus_1024(__builtin_amdgcn_perm(kExp, w0, 0x04010400u));
+    const f16x2 p1 = f16_pair_minus_1024(__builtin_amdgcn_perm(kExp, w0, 0x04030402u));
+    const f16x2 p2 = f16_pair_minus_1024(__builtin_amdgcn_perm(kExp, w1, 0x04010400u));
+    const f16x2 p3 = f16_pair_minus_1024(__builtin_amdgcn_perm(kExp, w1, 0x04030402u));
+    return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+__device__ __forceinline__ f16x8 kcodes4_to_f16(uint32_t w) {
+    const f16x2 p0 = f16_pair_minus_1024((w & 0x000F000Fu) | 0x64006400u);
+    const f16x2 p1 = f16_pair_minus_1024(((w >> 4) & 0x000F000Fu) | 0x64006400u);
+    const f16x2 p2 = f16_pair_minus_1024(((w >> 8) & 0x000F000Fu) | 0x64006400u);
+    const f16x2 p3 = f16_pair_minus_1024(((w >> 12) & 0x000F000Fu) | 0x64006400u);
+    return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// V codes -> 8 bf16 (exact small integers). 8-bit: two dwords; 4-bit: one dword, element
+// 2i in the low nibble of byte i.
+__device__ __forceinline__ bf16x8 codes8_to_bf16(uint32_t w0, uint32_t w1) {
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r[i] = __builtin_bit_cast(short, (__bf16)(float)((w0 >> (8 * i)) & 0xFFu));
+        r[4 + i] = __builtin_bit_cast(short, (__bf16)(float)((w1 >> (8 * i)) & 0xFFu));
+    }
+    return r;
+}
+__device__ __forceinline__ bf16x8 codes4_to_bf16(uint32_t w) {
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        r[i] = __builtin_bit_cast(short, (__bf16)(float)((w >> (4 * i)) & 0xFu));
+    return r;
+}
+
+template <int D, int NB, int BITS>
+__global__ __launch_bounds__(256, 1) void attn_kvq_kernel(const AttnArgs a) {
+    constexpr int TK = 128;                  // keys per tile
+    constexpr int NG = D / 64;               // quantization groups per row
+    constexpr int KPG = 4;                   // QK^T k-steps (16 dims) per group
+    constexpr int ROWB = D * BITS / 8;       // code bytes per key row
+    constexpr int CH = ROWB / 16;            // 16-byte chunks per code row
+    constexpr int RPI = 1024 / ROWB;         // rows per 1 KB DMA block
+    constexpr int CODEB = TK * ROWB;         // code bytes of one matrix tile
+    constexpr int BPW = CODEB / 1024 / 4;    // DMA blocks per wave
+    constexpr int SBROW = NG * 4;            // (scale, bias) bytes per row
+    constexpr int SBB = TK * SBROW;          // ... per tile
+    constexpr int VROWB = D * 2;             // expanded V row (bf16)
+    constexpr int KSTEPS = D / 16;
+    constexpr int DB = D / 32;
+    constexpr int KG = 4 / NB;
+    constexpr int OS = D + 4;
+    constexpr int OBB = 32 * OS * 4;         // one wave's O in the epilogue
+    constexpr int BUFB0 = CODEB + SBB;
+    constexpr int BUFB = ((BUFB0 > OBB ? BUFB0 : OBB) + 1023) / 1024 * 1024;
+    static_assert(CODEB % 4096 == 0 && SBB % 256 == 0, "whole DMA blocks per wave");
+    // two stages of (K codes + sb), (V codes + sb): four distinct LDS objects
+    __shared__ __attribute__((aligned(1024))) char k0s[BUFB];
+    __shared__ __attribute__((aligned(1024))) char v0s[BUFB];
+    __shared__ __attribute__((aligned(1024))) char k1s[BUFB];
+    __shared__ __attribute__((aligned(1024))) char v1s[BUFB];
+    __shared__ __attribute__((aligned(1024))) char vdq[TK * VROWB];   // expanded V tile
+    // tail (<= 32 keys per split): codes + sb of K and V, and its expanded V
+    constexpr int TCODEB = 32 * ROWB, TSBB = 32 * SBROW;
+    __shared__ __attribute__((aligned(1024))) char kts[TCODEB + TSBB];
+    __shared__ __attribute__((aligned(1024))) char vts[TCODEB + TSBB];
+    __shared__ __attribute__((aligned(1024))) char vtdq[32 * VROWB];
+    __shared__ float stats[kStatFloats];
+    __shared__ int s_next[2];
+
+    asm volatile("" ::"s"(a.k), "s"(a.v), "s"(a.tile_ctr), "s"(a.cu_rows), "s"(a.ctx_lens),
+                 "s"(a.nsplit), "s"(a.hkv), "s"(a.s_max), "s"(a.max_kv_len), "s"(a.dyn),
+                 "s"(a.max_rows), "s"(a.ksb), "s"(a.vsb), "s"(a.q), "s"(a.out),
+                 "s"(a.part_o), "s"(a.part_ml), "s"(a.err), "s"(a.total_rows), "s"(a.group),
+                 "s"(a.mcap), "s"(a.scale_log2));
+    int unit, split;
+    map_block(blockIdx.x, a.nsplit, &unit, &split);    // the grid is units x nsplit
+    const int b = unit / a.hkv, g = unit % a.hkv;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const size_t row0 = ((size_t)b * a.hkv + g) * (size_t)a.s_max;     // first key row
+    const char* kbase = reinterpret_cast<const char*>(a.k) + row0 * ROWB;
+    const char* vbase = reinterpret_cast<const char*>(a.v) + row0 * ROWB;
+    const char* ksbase = reinterpret_cast<const char*>(a.ksb) + row0 * SBROW;
+    const char* vsbase = reinterpret_cast<const char*>(a.vsb) + row0 * SBROW;
+
+    // DMA of tile t: wave w fills code blocks w, w + 4, ... of K and of V and the dwords
+    // [256 w, 256 w + 256) of each (scale, bias) tile. Keys at or past key_lim read key
+    // key_lim - 1.
+    const int dma_ri = lane / CH, dma_pos = lane % CH;
+    const int dma_off = dma_ri * ROWB + ((dma_pos ^ code_swz<ROWB>(wave * RPI + dma_ri)) << 4);
+    const int sb_byte = wave * 256 + lane * 4;         // this lane's dword of an sb tile
+    int key_lim;
+    auto issue_tile = [&](int t, char* kt, char* vt) __attribute__((always_inline)) {
+        if ((t + 1) * TK <= key_lim) {
+            const char* kb = kbase + (size_t)t * CODEB;
+            const char* vb = vbase + (size_t)t * CODEB;
+#pragma unroll
+            for (int i = 0; i < BPW; ++i) {
+                const int blk = i * 4 + wave;
+                __builtin_amdgcn_global_load_lds(kb + blk * 1024 + dma_off,
+                                                 (lds_void*)(kt + blk * 1024), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(vb + blk * 1024 + dma_off,
+                                                 (lds_void*)(vt + blk * 1024), 16, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < BPW; ++i) {
+                const int blk = i * 4 + wave;
+                const int r = blk * RPI + dma_ri;
+                int key = t * TK + r;
+                key = key < key_lim ? key : key_lim - 1;
+                const size_t src = (size_t)key * ROWB + (size_t)((dma_pos ^ code_swz<ROWB>(r)) << 4);
+                __builtin_amdgcn_global_load_lds(kbase + src, (lds_void*)(kt + blk * 1024), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(vbase + src, (lds_void*)(vt + blk * 1024), 16, 0, 0);
+            }
+        }
+        if (wave * 256 < SBB) {
+            const int r = sb_byte / SBROW;
+            int key = t * TK + r;
+            key = key < key_lim ? key : key_lim - 1;
+            const size_t src = (size_t)key * SBROW + sb_byte % SBROW;
+            __builtin_amdgcn_global_load_lds(ksbase + src, (lds_void*)(kt + CODEB + wave * 256), 4, 0, 0);
+            __builtin_amdgcn_global_load_lds(vsbase + src, (lds_void*)(vt + CODEB + wave * 256), 4, 0, 0);
+        }
+    };
+
+    const bool tails = a.nsplit >= 4;
+    const bool dyn = a.dyn != 0;
+    auto tile_count = [&](int len) __attribute__((always_inline)) {
+        return tails ? len / TK : (len + TK - 1) / TK;
+    };
+    auto static_end = [&](int nt) __attribute__((always_inline)) {
+        return (int)((uint32_t)((split + 1) * nt) / (uint32_t)a.nsplit);
+    };
+    auto first_tile = [&](int nt) __attribute__((always_inline)) {
+        const int t = dyn ? split : (int)((uint32_t)(split * nt) / (uint32_t)a.nsplit);
+        return t < (dyn ? nt : static_end(nt)) ? t : -1;
+    };
+    const int kv_cap = a.max_kv_len < a.s_max ? a.max_kv_len : a.s_max;
+    const int t_spec = first_tile(tile_count(kv_cap));
+    key_lim = kv_cap;
+    if (t_spec >= 0) issue_tile(t_spec, k0s, v0s);
+    uint32_t* const ctr = a.tile_ctr + unit;
+    uint32_t claim = 0;
+    if (dyn && tid == 0) claim = atomicAdd(ctr, 1u);
+
+    const SeqGeom s = seq_geometry(a, b, tid == 0 && split == 0 && g == 0);
+    if (!s.ok) {
+        __builtin_amdgcn_s_waitcnt(0);
+        return;
+    }
+    const int L = s.ctx + s.rows;
+    const int nt = tile_count(L);
+    const int t_first = first_tile(nt);
+    const int t_last = dyn ? nt : static_end(nt);
+    int tail_b = 0, tail_e = 0;
+    if (tails) {
+        const int f = L / TK * TK, rem = L - f;
+        tail_b = f + (int)((uint32_t)(split * rem) / (uint32_t)a.nsplit);
+        tail_e = f + (int)((uint32_t)((split + 1) * rem) / (uint32_t)a.nsplit);
+    }
+    key_lim = L;
+    if (t_first < 0 && tail_b >= tail_e) {
+        __builtin_amdgcn_s_waitcnt(0);
+        attn_empty_split<D>(a, unit, split, s);
+        return;
+    }
+    // The speculative tile is kept as it landed: rows past the sequence hold finite codes
+    // (any byte is a code), and their (scale, bias), which may not be finite, are zeroed
+    // before use. Every other DMA repeats the last key of its range in such rows.
+    if (t_first >= 0 && t_first != t_spec) {
+        __builtin_amdgcn_s_waitcnt(0);
+        issue_tile(t_first, k0s, v0s);
+    }
+    if (tail_b < tail_e) {
+        // rows past the tail end read its last key
+        if (wave * 1024 < TCODEB) {
+            const int r = wave * RPI + dma_ri;
+            int key = tail_b + r;
+            key = key < tail_e ? key : tail_e - 1;
+            const size_t src = (size_t)key * ROWB + (size_t)((dma_pos ^ code_swz<ROWB>(r)) << 4);
+            __builtin_amdgcn_global_load_lds(kbase + src, (lds_void*)(kts + wave * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vbase + src, (lds_void*)(vts + wave * 1024), 16, 0, 0);
+        }
+        if (wave == 0 && lane * 4 < TSBB) {
+            int key = tail_b + lane * 4 / SBROW;
+            key = key < tail_e ? key : tail_e - 1;
+            const size_t src = (size_t)key * SBROW + (lane * 4) % SBROW;
+            __builtin_amdgcn_global_load_lds(ksbase + src, (lds_void*)(kts + TCODEB), 4, 0, 0);
+            __builtin_amdgcn_global_load_lds(vsbase + src, (lds_void*)(vts + TCODEB), 4, 0, 0);
+        }
+    }
+
+    const int nb = wave % NB, kg = wave / NB;
+    const int h = lane >> 5, col = lane & 31;
+    const int n = nb * 32 + col;
+    const int M = s.rows * a.group;
+    const bool col_valid = n < M;
+    const int ri = col_valid ? n / a.group : 0;
+    const int hh = col_valid ? n % a.group : 0;
+    const int causal_lim = s.ctx + ri;
+
+    // This column's q as fp16, scaled by 2^qe so that its largest magnitude lies in
+    // [2^14, 2^15): every bf16 value within 2^24 of that maximum converts exactly (the
+    // smaller ones, if any, round at 2^-24 of the fp16 range, far below the score
+    // tolerance); the scores are scaled back by 2^-qe, folded into qfac.
+    f16x8 qh[KSTEPS];
+    float qfac;
+    {
+        const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
+                             ((size_t)(s.r0 + ri) * a.hq + g * a.group + hh) * D;
+        float qv[KSTEPS][8];
+        float qmax = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) {
+            bf16x8 w = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+            if (col_valid) w = *reinterpret_cast<const bf16x8*>(qp + 16 * kk + 8 * h);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                qv[kk][e] = (float)__builtin_bit_cast(__bf16, (short)w[e]);
+                qmax = fmaxf(qmax, fabsf(qv[kk][e]));
+            }
+        }
+        qmax = fmaxf(qmax, __shfl_xor(qmax, 32));
+        int qe = 0;
+        if (qmax > 0.f && qmax <= 3.0e38f) {
+            int ex;
+            (void)__builtin_frexpf(qmax, &ex);
+            qe = 15 - ex;
+        }
+        qfac = __builtin_ldexpf(a.scale_log2, -qe);
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                // 4-bit K operands hold dims (0, 4, 1, 5, 2, 6, 3, 7) of each 8
+                const int pos = BITS == 4 ? (e < 4 ? 2 * e : 2 * (e - 4) + 1) : e;
+                qh[kk][pos] = (_Float16)__builtin_ldexpf(qv[kk][e], qe);
+            }
+    }
+    // per-group sums of this column's (scaled, fp16) q: the bias term of the scores
+    float qsum[NG];
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+        float sm = 0.f;
+#pragma unroll
+        for (int kk = gi * KPG; kk < (gi + 1) * KPG; ++kk)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sm += (float)qh[kk][e];
+        qsum[gi] = sm + __shfl_xor(sm, 32);
+    }
+
+    f32x16 o[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+    float m_run = kNegInf, l_run = 0.f;
+    const int i16 = lane & 15;
+    const int half = (lane >> 4) & 1;
+
+    // The bias term of O, sum_t P[n][t] b_g[t], is kept per group as one running value per
+    // lane (column n), rescaled with O, and added to O once after the last tile.
+    float bacc[NG];
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) bacc[gi] = 0.f;
+
+    // (scale, bias) fp16 pairs of group gi for this lane's keys kl0 + 8 j + 4 h + (0..3),
+    // as packed dwords (every lane of a half-wave reads the same ones)
+    auto load_sb = [&](const char* sbt, int kl0, int gi, uint32_t (&w)[16])
+        __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int k4 = 0; k4 < 4; ++k4)
+                w[4 * j + k4] = *reinterpret_cast<const uint32_t*>(
+                    sbt + (kl0 + 8 * j + 4 * h + k4) * SBROW + gi * 4);
+    };
+    auto lo_f16 = [](uint32_t w) __attribute__((always_inline)) {
+        return (float)__builtin_bit_cast(_Float16, (unsigned short)(w & 0xFFFFu));
+    };
+    auto hi_f16 = [](uint32_t w) __attribute__((always_inline)) {
+        return (float)__builtin_bit_cast(_Float16, (unsigned short)(w >> 16));
+    };
+
+    // One 32-key sub-tile: code rows kl0 .. kl0 + 31 of ktile (their (scale, bias) rows in
+    // ksbt) and expanded V rows of vtile (scale, bias in vsbt) hold keys kbase0 + row; keys
+    // at or past khi are masked.
+    auto compute_sub = [&](const char* ktile, const char* ksbt, const char* vtile,
+                           const char* vsbt, int kl0, int kbase0, int khi)
+        __attribute__((always_inline)) {
+        f32x16 sacc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+        {
+            const int krow = kl0 + col;
+            const int ksw = code_swz<ROWB>(krow);
+            const char* kr = ktile + krow * ROWB;
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) {
+                f32x16 acc;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+                for (int kk = gi * KPG; kk < (gi + 1) * KPG; ++kk) {
+                    f16x8 ka;
+                    if constexpr (BITS == 8) {
+                        // dims 16 kk + 8 h .. + 8: half h of chunk kk
+                        const uint2 w = *reinterpret_cast<const uint2*>(
+                            kr + ((kk ^ ksw) << 4) + 8 * h);
+                        ka = kcodes8_to_f16(w.x, w.y);
+                    } else {
+                        // 4 bytes at 8 kk + 4 h: chunk kk / 2, byte 8 (kk & 1) + 4 h
+                        const uint32_t w = *reinterpret_cast<const uint32_t*>(
+                            kr + (((kk >> 1) ^ ksw) << 4) + 8 * (kk & 1) + 4 * h);
+                        ka = kcodes4_to_f16(w);
+                    }
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qh[kk], acc, 0, 0, 0);
+                }
+                uint32_t sbw[16];
+                load_sb(ksbt, kl0, gi, sbw);
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    sacc[r] = __builtin_fmaf(lo_f16(sbw[r]), acc[r],
+                                             __builtin_fmaf(hi_f16(sbw[r]), qsum[gi], sacc[r]));
+            }
+        }
+        float sv[16];
+        float mt = kNegInf;
+        if (kbase0 + kl0 + 31 <= s.ctx && kbase0 + kl0 + 31 < khi) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                sv[r] = sacc[r] * qfac;
+                mt = fmaxf(mt, sv[r]);
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int tg = kbase0 + kl0 + 8 * (r >> 2) + 4 * h + (r & 3);
+                const bool vis = col_valid && tg < khi && tg <= causal_lim;
+                sv[r] = vis ? sacc[r] * qfac : kNegInf;
+                mt = fmaxf(mt, sv[r]);
+            }
+        }
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const bool grow = mt > m_run + kLazyLog2;
+        if (__ballot(grow)) {
+            const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mt) : 1.f;
+            if (grow) m_run = mt;
+            l_run *= alpha;
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) bacc[gi] *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+        }
+        float pf[16];
+        float ls = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            pf[r] = (sv[r] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(sv[r] - m_run);
+            ls += pf[r];
+        }
+        l_run += ls;
+        // ---- O^T += V^T (P s_g)^T per group; the bias term into bacc (every (scale, bias)
+        // of the tile is finite: rows past the sequence were zeroed or repeat a key of it)
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+            uint32_t sbw[16];
+            load_sb(vsbt, kl0, gi, sbw);
+            bf16x8 pb_hi[2], pb_lo[2];
+            float bsum = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float pw = __builtin_fmaf(pf[r], lo_f16(sbw[r]), 0.f);
+                bsum = __builtin_fmaf(pf[r], hi_f16(sbw[r]), bsum);
+                const __bf16 hi = (__bf16)pw;
+                const __bf16 lo = (__bf16)(pw - (float)hi);
+                pb_hi[r >> 3][r & 7] = __builtin_bit_cast(short, hi);
+                pb_lo[r >> 3][r & 7] = __builtin_bit_cast(short, lo);
+            }
+            bacc[gi] += bsum;
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const int vrow = kl0 + 16 * s2 + 4 * h + (i16 >> 2);
+                const int sw0 = kv_swz<D>(vrow), sw1 = kv_swz<D>(vrow + 8);
+                const char* r0p = vtile + vrow * VROWB + 8 * (i16 & 1);
+                const char* r1p = r0p + 8 * VROWB;
+#pragma unroll
+                for (int db = gi * (DB / NG); db < (gi + 1) * (DB / NG); ++db) {
+                    const int chunk = 4 * db + 2 * half + ((i16 & 3) >> 1);
+                    const bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_bf16x4*)(const lds_char*)(r0p + ((chunk ^ sw0) << 4)));
+                    const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_bf16x4*)(const lds_char*)(r1p + ((chunk ^ sw1) << 4)));
+                    const bf16x8 va = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb_hi[s2], o[db], 0, 0, 0);
+                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb_lo[s2], o[db], 0, 0, 0);
+                }
+            }
+        }
+    };
+
+    // (scale, bias) rows of keys at or past L in the speculative tile t -> 0 (after every
+    // wave's DMA of the tile landed)
+    auto zero_sb = [&](int t, char* kt, char* vt) __attribute__((always_inline)) {
+        if (t == t_spec && (t + 1) * TK > L && tid < TK && t * TK + tid >= L) {
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) {
+                *reinterpret_cast<uint32_t*>(kt + CODEB + tid * SBROW + gi * 4) = 0u;
+                *reinterpret_cast<uint32_t*>(vt + CODEB + tid * SBROW + gi * 4) = 0u;
+            }
+        }
+    };
+    // V codes of `rows` rows -> bf16 integers in the bf16 kernel's V layout
+    auto expand_v = [&](const char* vcodes, char* vexp, int rows) __attribute__((always_inline)) {
+        for (int ci = tid; ci < rows * CH; ci += kThreads) {
+            const int r = ci / CH, c = ci % CH;
+            const uint4 w = *reinterpret_cast<const uint4*>(
+                vcodes + r * ROWB + ((c ^ code_swz<ROWB>(r)) << 4));
+            char* dst = vexp + r * VROWB;
+            const int sw = kv_swz<D>(r);
+            if constexpr (BITS == 8) {
+                *reinterpret_cast<bf16x8*>(dst + (((2 * c) ^ sw) << 4)) = codes8_to_bf16(w.x, w.y);
+                *reinterpret_cast<bf16x8*>(dst + (((2 * c + 1) ^ sw) << 4)) = codes8_to_bf16(w.z, w.w);
+            } else {
+                *reinterpret_cast<bf16x8*>(dst + (((4 * c) ^ sw) << 4)) = codes4_to_bf16(w.x);
+                *reinterpret_cast<bf16x8*>(dst + (((4 * c + 1) ^ sw) << 4)) = codes4_to_bf16(w.y);
+                *reinterpret_cast<bf16x8*>(dst + (((4 * c + 2) ^ sw) << 4)) = codes4_to_bf16(w.z);
+                *reinterpret_cast<bf16x8*>(dst + (((4 * c + 3) ^ sw) << 4)) = codes4_to_bf16(w.w);
+            }
+        }
+    };
+    auto compute_tile = [&](int t, const char* kt, const char* vt) __attribute__((always_inline)) {
+#pragma unroll
+        for (int st = 0; st < NB; ++st)
+            compute_sub(kt, kt + CODEB, vdq, vt + CODEB, kg * (TK / KG) + st * 32, t * TK, L);
+    };
+    auto compute_tail = [&]() __attribute__((always_inline)) {
+        if (tail_b < tail_e && kg == 0)
+            compute_sub(kts, kts + TCODEB, vtdq, vts + TCODEB, 0, tail_b, tail_e);
+    };
+    auto next_tile = [&](int t, int par) __attribute__((always_inline)) {
+        if (tid == 0) s_next[par] = dyn ? a.nsplit + (int)claim : t + 1;
+        __syncthreads();
+        const int tn = s_next[par];
+        if (tn >= t_last) return -1;
+        if (dyn && tid == 0) claim = atomicAdd(ctr, 1u);
+        return tn;
+    };
+
+    // Tile t + 1 is in flight while tile t is expanded and computed. Before each tile: this
+    // wave's DMA landed (s_waitcnt), then every wave's, and every wave is done with the
+    // other buffers and with the expanded V of the previous tile.
+    if (t_first < 0) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        expand_v(vts, vtdq, 32);
+        __syncthreads();
+        compute_tail();
+    }
+    for (int t = t_first; t >= 0;) {
+        __builtin_amdgcn_s_waitcnt(0);                 // first time: the tail landed too
+        const int t1 = next_tile(t, 0);
+        if (t1 >= 0) issue_tile(t1, k1s, v1s);
+        if (t == t_first) zero_sb(t, k0s, v0s);
+        expand_v(v0s, vdq, TK);
+        if (t == t_first && tail_b < tail_e) expand_v(vts, vtdq, 32);
+        __syncthreads();
+        compute_tile(t, k0s, v0s);
+        if (t == t_first) compute_tail();
+        if (t1 < 0) break;
+        __builtin_amdgcn_s_waitcnt(0);
+        const int t2 = next_tile(t1, 1);
+        if (t2 >= 0) issue_tile(t2, k0s, v0s);
+        expand_v(v1s, vdq, TK);
+        __syncthreads();
+        compute_tile(t1, k1s, v1s);
+        t = t2;
+    }
+
+    // ---- the bias term (this lane's keys; the other half-wave holds the rest of the
+    // column's), then combine the key groups as in the bf16 kernel
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+        const float bt = bacc[gi] + __shfl_xor(bacc[gi], 32);
+#pragma unroll
+        for (int db = gi * (DB / NG); db < (gi + 1) * (DB / NG); ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[db][r] += bt;
+    }
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    __syncthreads();                                    // buffers no longer needed
+    LdsQuad ob;
+    ob.p0 = reinterpret_cast<float*>(k0s);
+    ob.p1 = reinterpret_cast<float*>(v0s);
+    ob.p2 = reinterpret_cast<float*>(k1s);
+    ob.p3 = reinterpret_cast<float*>(v1s);
+    float* mine = ob[wave];
+    if (h == 0) {
+        stats[kg * a.mcap + n] = m_run;
+        stats[kStatCap + kg * a.mcap + n] = l_tot;
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int d = 32 * db + 8 * (r >> 2) + 4 * h + (r & 3);
+            mine[col * OS + d] = o[db][r];
+        }
+    __syncthreads();
+    attn_epilogue<D, KG, NB>(a, ob, stats, unit, split, g, s, OS);
+}
+
 // -------------------------------------------------------------------------- fp32 / FMA
 // Same split and merge as the bf16 kernel; per tile of 32 keys: scores S[n][key] (one dot
 // product per thread task), an online-softmax update per column, then O[n][d] += P V. All
@@ -721,7 +1269,23 @@ AttnPlan plan_attention(int B, int Hq, int Hkv, int D, int max_rows, int max_kv_
 hipError_t launch_attention(const AttnArgs& a, const AttnPlan& p, vsa_dtype dtype,
                             hipStream_t stream) {
     const dim3 grid(p.units * p.nsplit), block(kThreads);
-    if (dtype == VSA_BF16) {
+    if (a.bits == 8 || a.bits == 4) {
+#define VSA_KVQ(DD, NBB, BB) hipLaunchKernelGGL((attn_kvq_kernel<DD, NBB, BB>), grid, block, 0, stream, a)
+        if (a.bits == 8) {
+            if (a.d == 128) {
+                if (p.nb == 1) VSA_KVQ(128, 1, 8); else if (p.nb == 2) VSA_KVQ(128, 2, 8); else VSA_KVQ(128, 4, 8);
+            } else {
+                if (p.nb == 1) VSA_KVQ(64, 1, 8); else if (p.nb == 2) VSA_KVQ(64, 2, 8); else VSA_KVQ(64, 4, 8);
+            }
+        } else {
+            if (a.d == 128) {
+                if (p.nb == 1) VSA_KVQ(128, 1, 4); else if (p.nb == 2) VSA_KVQ(128, 2, 4); else VSA_KVQ(128, 4, 4);
+            } else {
+                if (p.nb == 1) VSA_KVQ(64, 1, 4); else if (p.nb == 2) VSA_KVQ(64, 2, 4); else VSA_KVQ(64, 4, 4);
+            }
+        }
+#undef VSA_KVQ
+    } else if (dtype == VSA_BF16) {
         if (a.d == 128) {
             if (p.nb == 1) hipLaunchKernelGGL((attn_bf16_kernel<128, 1>), grid, block, 0, stream, a);
             else if (p.nb == 2) hipLaunchKernelGGL((attn_bf16_kernel<128, 2>), grid, block, 0, stream, a);

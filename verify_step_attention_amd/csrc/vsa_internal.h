@@ -187,6 +187,9 @@ struct AttnArgs {
     int dyn;                // splits claim tiles from tile_ctr (needs nsplit >= 2)
     int max_rows;
     // the rest
+    const void* ksb;        // quantized caches: (scale, bias) fp16 pairs per 64 dims
+    const void* vsb;
+    int bits;               // 0: bf16 / fp32 K and V; 8 or 4: quantized codes in k / v
     const void* q;
     float* out;
     float* part_o;          // [units][nsplit][mcap][D]
