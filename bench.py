@@ -8,10 +8,13 @@ verify_sample_accept on the same stream, on one of R distinct input sets in HBM 
 > 1 GB, so the 256 MB last-level cache cannot hold the working set between steps).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--static-splits]
+                    [--static-splits] [--kv-bits 16|8|4]
 
 Attention runs with dynamic key splits (VSA_ATTN_DYNAMIC_SPLITS: splits claim key tiles
 at run time) unless --static-splits asks for fixed, bitwise reproducible ranges.
+--kv-bits 8 or 4 runs the same step over a quantized copy of the cache (affine codes per
+group of 64 dimensions with fp16 scale and bias) through verify_attention_kvq; the default
+16 is the bf16 cache.
 
 Prints one JSON line. Roofline: the dominant stage (attention: its main kernel and the
 split merge kernel) is timed per call with HIP events on the stream it runs on; its
@@ -38,10 +41,14 @@ COUNTERS = os.path.join(ROOT, "profiles", "attention_b4k4_ctx8192_counters.json"
 ATTN_SRC = os.path.join(ROOT, "verify_step_attention_amd", "csrc", "attention.hip")
 
 
-def algorithmic_bytes(w):
-    """Bytes each kernel must move at least once (inputs read once, outputs written once)."""
+def algorithmic_bytes(w, kv_bits=16):
+    """Bytes each kernel must move at least once (inputs read once, outputs written once).
+    A quantized key row is D * bits / 8 code bytes and 4 bytes of (scale, bias) per group
+    of 64 dimensions."""
     rows = np.diff(w.cu_rows)
-    kv = int(((w.ctx_lens + rows) * w.num_kv_heads * w.head_dim * 2 * 2).sum())
+    per_key = (w.head_dim * 2 if kv_bits == 16 else
+               w.head_dim * kv_bits // 8 + 4 * (w.head_dim // 64))
+    kv = int(((w.ctx_lens + rows) * w.num_kv_heads * per_key * 2).sum())
     q = w.total_rows * w.num_q_heads * w.head_dim * 2
     o = w.total_rows * w.num_q_heads * w.head_dim * 4
     sampled = [b for b in range(w.batch) if w.params[b].temperature > 0]
@@ -68,22 +75,32 @@ def counters_traffic():
         return None
 
 
-def cpu_baseline(w, budget_s=12.0):
+def cpu_baseline(w, kq=None, budget_s=12.0):
     """The oracle as it stands, timed on the host on whole verify steps of the same workload
-    until about budget_s seconds have passed (at least one step)."""
+    until about budget_s seconds have passed (at least one step). kq: the quantized cache,
+    when the step reads one."""
     from oracle import attention as oatt, sampling as osamp
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         cores = 1
-    k, v = w.kv_f32()
     q = w.q_f32()
+    if kq is None:
+        k, v = w.kv_f32()
+
+        def attend():
+            oatt.verify_attention(q, k, v, w.cu_rows, w.ctx_lens, w.num_q_heads,
+                                  w.num_kv_heads)
+    else:
+        def attend():
+            oatt.verify_attention_kvq(q, kq.k_codes, kq.k_sb, kq.v_codes, kq.v_sb, kq.bits,
+                                      w.cu_rows, w.ctx_lens, w.num_q_heads, w.num_kv_heads)
     prm = [osamp.RowParams(p.temperature, p.top_k, p.top_p, p.presence_penalty,
                            p.frequency_penalty, p.logprobs, p.top_logprobs) for p in w.params]
     steps, t0 = 0, time.perf_counter()
     while True:
-        oatt.verify_attention(q, k, v, w.cu_rows, w.ctx_lens, w.num_q_heads, w.num_kv_heads)
+        attend()
         osamp.verify_sample_accept(w.target_logits, w.draft_logits, w.draft_tokens, w.cu_rows,
                                    w.token_counts, prm, w.positions, w.seed)
         steps += 1
@@ -92,8 +109,9 @@ def cpu_baseline(w, budget_s=12.0):
     dt = time.perf_counter() - t0
     return {"value": round(steps * w.total_rows / dt, 3), "unit": "rows/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"{steps} whole verify step(s) of {WORKLOAD} (attention of all 20 rows "
-                      f"+ sample/accept of all 4 sequences), {dt:.1f} s on the host, numpy "
+            "sample": f"{steps} whole verify step(s) of {WORKLOAD} (attention of all 20 rows"
+                      f"{'' if kq is None else f' over the {kq.bits}-bit cache'} + "
+                      f"sample/accept of all 4 sequences), {dt:.1f} s on the host, numpy "
                       f"BLAS threads = {cores}"}
 
 
@@ -179,6 +197,8 @@ def main():
     ap.add_argument("--static-splits", action="store_true",
                     help="attention with fixed key ranges per split (bitwise reproducible) "
                          "instead of tiles claimed at run time")
+    ap.add_argument("--kv-bits", type=int, default=16, choices=(16, 8, 4),
+                    help="K/V cache: bf16 (16) or affine codes of 8 or 4 bits")
     ap.add_argument("--eager", action="store_true",
                     help="launch every call from Python instead of replaying HIP graphs")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -199,9 +219,16 @@ def main():
 
     print(f"[bench] building inputs for {WORKLOAD}", file=sys.stderr, flush=True)
     w = wl.make_workload(WORKLOAD)
-    nbytes = algorithmic_bytes(w)
+    nbytes = algorithmic_bytes(w, args.kv_bits)
     step_bytes = nbytes["attention"] + nbytes["sample"]
     dev0 = wl.device_tensors(w)
+    kq = None
+    if args.kv_bits != 16:
+        kq = wl.quantized_cache(w, args.kv_bits)
+        dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()  # noqa: E731
+        dev0.update(k_codes=dev(kq.k_codes), k_sb=dev(kq.k_sb), v_codes=dev(kq.v_codes),
+                    v_sb=dev(kq.v_sb))
+        del dev0["k_cache"], dev0["v_cache"]
     sets = [dev0] + [{k: (None if t is None else t.clone()) for k, t in dev0.items()}
                      for _ in range(args.sets - 1)]
     params = torch.from_numpy(vsa.pack_row_params(w.params).view(np.uint8)).cuda()
@@ -219,9 +246,16 @@ def main():
     stream = torch.cuda.current_stream()
 
     def attention(d, s=None):
-        vsa.verify_attention(d["q"], d["k_cache"], d["v_cache"], d["cu_rows"], d["ctx_lens"],
-                             out, ws_a, max_rows_per_seq=w.max_rows, max_kv_len=w.max_kv_len,
-                             flags=ATTN_FLAGS, stream=stream if s is None else s)
+        if kq is None:
+            vsa.verify_attention(d["q"], d["k_cache"], d["v_cache"], d["cu_rows"],
+                                 d["ctx_lens"], out, ws_a, max_rows_per_seq=w.max_rows,
+                                 max_kv_len=w.max_kv_len, flags=ATTN_FLAGS,
+                                 stream=stream if s is None else s)
+        else:
+            vsa.verify_attention_kvq(d["q"], d["k_codes"], d["k_sb"], d["v_codes"], d["v_sb"],
+                                     kq.bits, d["cu_rows"], d["ctx_lens"], out, ws_a,
+                                     max_rows_per_seq=w.max_rows, max_kv_len=w.max_kv_len,
+                                     flags=ATTN_FLAGS, stream=stream if s is None else s)
 
     def sample(d, s=None):
         vsa.verify_sample_accept(d["target_logits"], d["draft_logits"], d["draft_tokens"],
@@ -344,7 +378,7 @@ def main():
 
     attn_us = float(np.mean(attn_ms)) * 1e3
     achieved = nbytes["attention"] / (attn_us * 1e-6) / 1e9
-    traffic = counters_traffic()
+    traffic = counters_traffic() if kq is None else None
     rows_per_s = w.total_rows / (ms_step * 1e-3)
     line = {
         "metric": "verified draft-block rows/sec + achieved HBM GB/s, B=4 K=4 ctx 8192",
@@ -357,7 +391,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if kq is None else f"bf16 q, u{kq.bits} kv codes",
         "data": "synthetic",
         "achieved_hbm_GBps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "launch": "eager" if not graphs else "hip_graph_replay",
@@ -374,10 +408,14 @@ def main():
             "sample_accept_us": round(float(np.mean(samp_ms)) * 1e3, 2),
             "logits_dtype": "f32",
             "attention_splits": "dynamic" if ATTN_FLAGS else "static",
+            "kv_bits": args.kv_bits,
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "verify_attention call (attn_bf16_kernel<128,1> + attn_merge_kernel<128>)",
+            "kernel": ("verify_attention call (attn_bf16_kernel<128,1> + attn_merge_kernel<128>)"
+                       if kq is None else
+                       f"verify_attention_kvq call (attn_kvq_kernel<128,1,{kq.bits}> + "
+                       "attn_merge_kernel<128>)"),
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
@@ -388,7 +426,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on the host", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(w)
+        line["cpu_baseline"] = cpu_baseline(w, kq)
     print(json.dumps(line), flush=True)
 
 
