@@ -59,6 +59,65 @@ def verify_attention(q, k_cache, v_cache, cu_rows, ctx_lens, num_q_heads, num_kv
     return out
 
 
+# ------------------------------------------------------------- a drafter's block, windowed
+# The same multi-row attention also serves a drafter's block over its context (Changelog
+# [0.20.0] "Added"). Around it the pages give: the drafter's context K/V lives in one buffer
+# with the block written into its tail ([0.20.0] "Changed"), i.e. the block's keys sit right
+# after the context, as in verify; the drafter attends only the last N context rows
+# (--drafter-window N, 0 = the whole context), while heads with a trained sliding window
+# keep theirs ([0.20.0] "Changed"); DFlash-lineage heads are causal inside the block (a row
+# never sees later block positions) and DeepSpec-native heads are bidirectional there
+# ([0.8.1] "Changed"). The reading used here, for block row i at position p = ctx_b + i:
+#   first visible key  lo_i = 0                          no window (window = 0)
+#                           = max(0, ctx_b - window)     recent window of context rows
+#                           = max(0, p - window + 1)     sliding window ending at p
+#   last visible key   hi_i = p                          causal block
+#                           = ctx_b + R_b - 1            bidirectional block
+# and row i attends keys lo_i .. hi_i (never empty: lo_i <= p <= hi_i).
+
+
+def block_visible_range(ctx, rows, i, window=0, sliding=False, bidirectional=False):
+    """(lo, hi): the keys row i of a block of `rows` rows after `ctx` context keys sees."""
+    p = ctx + i
+    if window == 0:
+        lo = 0
+    elif sliding:
+        lo = max(0, p - window + 1)
+    else:
+        lo = max(0, ctx - window)
+    hi = ctx + rows - 1 if bidirectional else p
+    return lo, hi
+
+
+def block_attention(q, k_cache, v_cache, cu_rows, ctx_lens, num_q_heads, num_kv_heads,
+                    scale=None, window=0, sliding=False, bidirectional=False):
+    """Attention of each sequence's block rows over keys lo_i .. hi_i (above), in fp64,
+    rounded once to fp32. window = 0, causal: the verify definition."""
+    q = np.asarray(q)
+    total_rows, hq, d = q.shape
+    assert hq == num_q_heads and num_q_heads % num_kv_heads == 0 and window >= 0
+    assert not (sliding and window == 0)
+    group = num_q_heads // num_kv_heads
+    if scale is None or scale == 0:
+        scale = 1.0 / math.sqrt(d)
+    out = np.zeros((total_rows, hq, d), dtype=np.float32)
+    for b in range(len(ctx_lens)):
+        r0, r1 = int(cu_rows[b]), int(cu_rows[b + 1])
+        ctx = int(ctx_lens[b])
+        for i in range(r1 - r0):
+            lo, hi = block_visible_range(ctx, r1 - r0, i, window, sliding, bidirectional)
+            for g in range(num_kv_heads):
+                keys = np.asarray(k_cache[b, g, lo:hi + 1], dtype=np.float64)
+                vals = np.asarray(v_cache[b, g, lo:hi + 1], dtype=np.float64)
+                heads = slice(g * group, (g + 1) * group)
+                qg = np.asarray(q[r0 + i, heads], dtype=np.float64)
+                s = scale * (qg @ keys.T)
+                w = np.exp(s - s.max(axis=1, keepdims=True))
+                out[r0 + i, heads] = ((w @ vals) / w.sum(axis=1, keepdims=True)).astype(
+                    np.float32)
+    return out
+
+
 # ---------------------------------------------------------------------- quantized K/V cache
 # The pages' --kv-bits 4|8 option keeps the target's K/V cache quantized from token 0
 # (mlx-dspark Changelog [0.3.0] "Added": KV-cache quantization; [0.13.1]: 8 bits halve and
