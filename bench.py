@@ -16,6 +16,12 @@ at run time) unless --static-splits asks for fixed, bitwise reproducible ranges.
 group of 64 dimensions with fp16 scale and bias) through verify_attention_kvq; the default
 16 is the bf16 cache.
 
+    python bench.py --drafter-block [--window W] [--bidirectional] [--sliding]
+
+times block_attention alone on a drafter's block instead: B=4 blocks of 8 rows over a
+32768-token context (32 q / 8 kv heads, D=128, bf16), attending the last W = 4096 context
+rows by default; one JSON line in the same form, rows = block rows.
+
 Prints one JSON line. Roofline: the dominant stage (attention: its main kernel and the
 split merge kernel) is timed per call with HIP events on the stream it runs on; its
 algorithmic bytes are the K/V of every sequence (ctx + R keys x Hkv x D x 2 bytes x 2), Q
@@ -115,6 +121,110 @@ def cpu_baseline(w, kq=None, budget_s=12.0):
                       f"BLAS threads = {cores}"}
 
 
+def drafter_block_main(args):
+    """block_attention on drafter_b4r8_ctx32768: HIP-event timing over graph replays of the
+    call on R input sets, roofline against the keys the rows attend, the oracle as the CPU
+    baseline."""
+    import torch
+    import verify_step_attention_amd as vsa
+    from verify_step_attention_amd import workloads as wl
+    name = "drafter_b4r8_ctx32768"
+    flags = (0 if args.static_splits else vsa.ATTN_DYNAMIC_SPLITS) | \
+        (vsa.ATTN_BIDIRECTIONAL if args.bidirectional else 0) | \
+        (vsa.ATTN_SLIDING_WINDOW if args.sliding else 0)
+    print(f"[bench] building inputs for {name}", file=sys.stderr, flush=True)
+    w = wl.make_workload(name)
+    rows = np.diff(w.cu_rows)
+    win = args.window
+    # keys some row of the block attends (context window + block), each read once
+    first = np.maximum(0, w.ctx_lens - (win - (1 if args.sliding else 0))) if win else \
+        np.zeros_like(w.ctx_lens)
+    kv = int(((w.ctx_lens + rows - first) * w.num_kv_heads * w.head_dim * 2 * 2).sum())
+    nbytes = kv + w.total_rows * w.num_q_heads * w.head_dim * (2 + 4)
+    dev0 = wl.device_tensors(w, with_kv=True)
+    sets = [dev0] + [{k: (None if t is None else t.clone()) for k, t in dev0.items()}
+                     for _ in range(args.sets - 1)]
+    ws = torch.zeros(vsa.verify_attention_workspace_size(
+        w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.max_rows, w.max_kv_len),
+        dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.total_rows, w.num_q_heads, w.head_dim), dtype=torch.float32,
+                      device="cuda")
+
+    def call(d, s):
+        vsa.block_attention(d["q"], d["k_cache"], d["v_cache"], d["cu_rows"], d["ctx_lens"],
+                            out, ws, max_rows_per_seq=w.max_rows, max_kv_len=w.max_kv_len,
+                            window=win, flags=flags, stream=s)
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        call(sets[i % len(sets)], stream)
+    torch.cuda.synchronize()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(stream)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cs):
+        with torch.cuda.graph(g, stream=cs):
+            for d in sets:
+                call(d, torch.cuda.current_stream())
+    stream.wait_stream(cs)
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, args.steps // len(sets))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * len(sets))
+    err = int(ws[:4].view(torch.int32).item())
+    if err:
+        print(f"[bench] device error word {err:#x}", file=sys.stderr)
+    achieved = nbytes / (us * 1e-6) / 1e9
+    mode = ("bidirectional" if args.bidirectional else "causal") + \
+        (", sliding" if args.sliding else "")
+    line = {
+        "metric": f"drafter block attention rows/sec + achieved HBM GB/s, B=4 block 8 "
+                  f"ctx 32768 window {win}",
+        "value": round(w.total_rows / (us * 1e-6), 1), "unit": "rows/s", "n_gpus": 1,
+        "steps": reps * len(sets), "warmup": args.warmup, "ms_per_step": round(us / 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic", "launch": "hip_graph_replay",
+        "config": {"workload": name, "batch": w.batch, "block_rows": 8, "ctx": 32768,
+                   "window": win, "mask": mode, "q_heads": w.num_q_heads,
+                   "kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "input_sets": len(sets), "attention_us": round(us, 2),
+                   "attention_splits": "static" if args.static_splits else "dynamic"},
+        "roofline": {"bound": "hbm", "kernel": "block_attention call (attn_bf16_kernel<128,"
+                     "1,true> + attn_merge_kernel<128>)", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": nbytes},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import attention as oatt
+        k, v = w.kv_f32()
+        q = w.q_f32()
+        n, t0 = 0, time.perf_counter()
+        while True:
+            oatt.block_attention(q, k, v, w.cu_rows, w.ctx_lens, w.num_q_heads,
+                                 w.num_kv_heads, window=win, sliding=args.sliding,
+                                 bidirectional=args.bidirectional)
+            n += 1
+            if time.perf_counter() - t0 >= 10.0:
+                break
+        dt = time.perf_counter() - t0
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        except Exception:
+            cores = 1
+        line["cpu_baseline"] = {"value": round(n * w.total_rows / dt, 3), "unit": "rows/s",
+                                "cores": cores, "kind": "oracle",
+                                "sample": f"{n} whole block_attention call(s) of {name} on "
+                                          f"the host, {dt:.1f} s"}
+    print(json.dumps(line), flush=True)
+
+
 def _counter_rows(d, counter):
     """Per-kernel values of one rocprofv3 --pmc counter (KiB per dispatch) under folder d."""
     import csv
@@ -199,6 +309,11 @@ def main():
                          "instead of tiles claimed at run time")
     ap.add_argument("--kv-bits", type=int, default=16, choices=(16, 8, 4),
                     help="K/V cache: bf16 (16) or affine codes of 8 or 4 bits")
+    ap.add_argument("--drafter-block", action="store_true",
+                    help="time block_attention on a drafter's block instead of the step")
+    ap.add_argument("--window", type=int, default=4096)
+    ap.add_argument("--bidirectional", action="store_true")
+    ap.add_argument("--sliding", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="launch every call from Python instead of replaying HIP graphs")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -210,6 +325,9 @@ def main():
               "the verify step's sharding across GPUs is a design note, not a run.",
               file=sys.stderr)
         sys.exit(2)
+    if args.drafter_block:
+        drafter_block_main(args)
+        return
 
     import torch
     import verify_step_attention_amd as vsa
@@ -412,7 +530,8 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": ("verify_attention call (attn_bf16_kernel<128,1> + attn_merge_kernel<128>)"
+            "kernel": ("verify_attention call (attn_bf16_kernel<128,1,false> + "
+                       "attn_merge_kernel<128>)"
                        if kq is None else
                        f"verify_attention_kvq call (attn_kvq_kernel<128,1,{kq.bits}> + "
                        "attn_merge_kernel<128>)"),

@@ -113,7 +113,8 @@ const char* vsa_status_string(vsa_status status);
  * computed with fp32 accumulation (bf16 products are exact in fp32).
  *
  *   q          [total_rows, Hq, D]     dtype
- *   k_cache    [B, Hkv, S_max, D]      dtype (positions >= ctx_b + R_b are never read)
+ *   k_cache    [B, Hkv, S_max, D]      dtype (positions >= ctx_b + R_b never enter the
+ *                                      result; reads stay below max_kv_len)
  *   v_cache    [B, Hkv, S_max, D]      dtype
  *   dtype      VSA_BF16 (MFMA path) or VSA_F32
  *   cu_rows    [B + 1] int32           0 = cu_rows[0] < cu_rows[1] < ... = total_rows
@@ -146,6 +147,41 @@ vsa_status verify_attention(const void* q, const void* k_cache, const void* v_ca
                             int max_rows_per_seq, int max_kv_len, float scale,
                             uint32_t flags, float* out, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * block_attention
+ *
+ * The same multi-row attention for a drafter's block over its context (Changelog
+ * [0.20.0] "Added": the kernel serves verify widths and a drafter's block; "Changed": the
+ * drafter's context K/V sits in one buffer with the block written at its tail, the
+ * drafter attends only the last N context rows (0 = all), heads with a trained sliding
+ * window keep it; [0.8.1] "Changed": causal-block heads never see later block positions,
+ * DeepSpec-native heads are bidirectional in the block). Layout as verify_attention: the
+ * block's R_b rows have their K/V at positions ctx_b .. ctx_b + R_b - 1. Row i, at
+ * position p = ctx_b + i, attends keys lo .. hi:
+ *     lo = 0                         window == 0
+ *        = max(0, ctx_b - window)    window > 0 (the last `window` context rows)
+ *        = max(0, p - window + 1)    window > 0 and VSA_ATTN_SLIDING_WINDOW
+ *     hi = p                         (causal in the block)
+ *        = ctx_b + R_b - 1           VSA_ATTN_BIDIRECTIONAL
+ * window = 0 with flags 0 is exactly verify_attention.
+ *
+ *   window     >= 0; VSA_ATTN_SLIDING_WINDOW needs window > 0 (else VSA_ERR_INVALID_ARG)
+ *   flags      any of VSA_ATTN_DYNAMIC_SPLITS, VSA_ATTN_BIDIRECTIONAL,
+ *              VSA_ATTN_SLIDING_WINDOW (other bits: VSA_ERR_INVALID_ARG)
+ *   every other argument as for verify_attention (same workspace size query; a window
+ *   only lowers the split count). Keys below lo are not read from HBM beyond the tile
+ *   (128 keys; 32 on the fp32 path) that holds the first one any row sees.
+ * ------------------------------------------------------------------------------------ */
+#define VSA_ATTN_BIDIRECTIONAL 2u
+#define VSA_ATTN_SLIDING_WINDOW 4u
+
+vsa_status block_attention(const void* q, const void* k_cache, const void* v_cache,
+                           vsa_dtype dtype, const int32_t* cu_rows, const int32_t* ctx_lens,
+                           int B, int total_rows, int Hq, int Hkv, int D, int S_max,
+                           int max_rows_per_seq, int max_kv_len, float scale, int window,
+                           uint32_t flags, float* out, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------
  * verify_attention_kvq

@@ -44,7 +44,10 @@ def test_header_enums_match_binding():
                         ("VSA_ERR_UNSUPPORTED", UNSUPPORTED), ("VSA_ERR_WORKSPACE", WORKSPACE),
                         ("VSA_BF16", BF16), ("VSA_F32", F32)]:
         assert re.search(rf"\b{name}\s*=\s*{value}\b", text), name
-    assert re.search(rf"#define VSA_ATTN_DYNAMIC_SPLITS\s+{vsa.ATTN_DYNAMIC_SPLITS}u", text)
+    for name, value in [("VSA_ATTN_DYNAMIC_SPLITS", vsa.ATTN_DYNAMIC_SPLITS),
+                        ("VSA_ATTN_BIDIRECTIONAL", vsa.ATTN_BIDIRECTIONAL),
+                        ("VSA_ATTN_SLIDING_WINDOW", vsa.ATTN_SLIDING_WINDOW)]:
+        assert re.search(rf"#define {name}\s+{value}u", text), name
 
 
 def test_version_and_status_strings(lib):
@@ -86,6 +89,21 @@ def test_attention_host_checks(lib):
     assert _attention(lib, ws=None) == WORKSPACE
     assert _attention(lib, ws=FAKE * 256 + 64) == WORKSPACE   # not 256-byte aligned
     assert _attention(lib, ws_bytes=1024) == WORKSPACE
+
+
+def _block(lib, *, window=0, flags=0, d=128, ws_bytes=1 << 30):
+    return lib.block_attention(FAKE, FAKE, FAKE, BF16, FAKE, FAKE, 4, 20, 32, 8, d, 8256, 5,
+                               8197, 0.0, window, flags, FAKE, FAKE * 256, ws_bytes, None)
+
+
+def test_block_attention_host_checks(lib):
+    assert _block(lib, window=-1) == INVALID_ARG
+    assert _block(lib, flags=vsa.ATTN_SLIDING_WINDOW) == INVALID_ARG     # needs a window
+    assert _block(lib, flags=8) == INVALID_ARG
+    assert _block(lib, window=4096, d=96) == UNSUPPORTED
+    assert _block(lib, window=4096, flags=vsa.ATTN_BIDIRECTIONAL, ws_bytes=1024) == WORKSPACE
+    # verify_attention takes no mask flags
+    assert _attention(lib, flags=vsa.ATTN_BIDIRECTIONAL) == INVALID_ARG
 
 
 def _attention_kvq(lib, *, q=FAKE, bits=8, d=128, flags=0, ws_bytes=1 << 30, sb=FAKE):

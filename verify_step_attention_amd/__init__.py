@@ -21,8 +21,10 @@ DEVERR_PARAMS = 0x04
 DEVERR_NO_DRAFT_LOGITS = 0x08
 DEVERR_TIE_OVERFLOW = 0x10
 
-# verify_attention flags
+# attention flags (verify_attention: only ATTN_DYNAMIC_SPLITS)
 ATTN_DYNAMIC_SPLITS = 0x1
+ATTN_BIDIRECTIONAL = 0x2
+ATTN_SLIDING_WINDOW = 0x4
 
 # vsa_row_params, field for field
 ROW_PARAMS_DTYPE = np.dtype([("temperature", "<f4"), ("top_k", "<i4"), ("top_p", "<f4"),
@@ -30,7 +32,7 @@ ROW_PARAMS_DTYPE = np.dtype([("temperature", "<f4"), ("top_k", "<i4"), ("top_p",
                              ("logprobs", "<i4"), ("top_logprobs", "<i4")])
 
 EXPORTED_SYMBOLS = ("vsa_version", "vsa_status_string", "verify_attention_workspace_size",
-                    "verify_attention", "verify_attention_kvq",
+                    "verify_attention", "block_attention", "verify_attention_kvq",
                     "verify_sample_accept_workspace_size", "verify_sample_accept")
 
 
@@ -62,6 +64,11 @@ def _lib():
                                          c_int, c_int, c_int, c_int, c_int, c_int, c_int,
                                          c_int, c_float, ctypes.c_uint32, c_void, c_void,
                                          c_size, c_void]
+        lib.block_attention.restype = c_int
+        lib.block_attention.argtypes = [c_void, c_void, c_void, c_int, c_void, c_void,
+                                        c_int, c_int, c_int, c_int, c_int, c_int, c_int,
+                                        c_int, c_float, c_int, ctypes.c_uint32, c_void,
+                                        c_void, c_size, c_void]
         lib.verify_attention_kvq.restype = c_int
         lib.verify_attention_kvq.argtypes = [c_void, c_void, c_void, c_void, c_void, c_int,
                                              c_void, c_void, c_int, c_int, c_int, c_int,
@@ -114,11 +121,7 @@ def verify_attention_workspace_size(B, Hq, Hkv, D, max_rows_per_seq, max_kv_len)
                                                       max_kv_len))
 
 
-def verify_attention(q, k_cache, v_cache, cu_rows, ctx_lens, out, workspace, *,
-                     max_rows_per_seq, max_kv_len, scale=0.0, flags=0, stream=None):
-    """q [T, Hq, D], k_cache / v_cache [B, Hkv, S_max, D] (bf16 or float32 tensors on the
-    GPU), cu_rows [B+1] / ctx_lens [B] int32, out [T, Hq, D] float32, workspace uint8;
-    flags 0 or ATTN_DYNAMIC_SPLITS."""
+def _attention_dtype(q, k_cache, v_cache, out, cu_rows, ctx_lens, workspace):
     import torch
     total, hq, d = q.shape
     batch, hkv, s_max, d2 = k_cache.shape
@@ -135,6 +138,33 @@ def verify_attention(q, k_cache, v_cache, cu_rows, ctx_lens, out, workspace, *,
     for t in (q, k_cache, v_cache, cu_rows, ctx_lens, out, workspace):
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
+    return dtype
+
+
+def block_attention(q, k_cache, v_cache, cu_rows, ctx_lens, out, workspace, *,
+                    max_rows_per_seq, max_kv_len, window=0, scale=0.0, flags=0, stream=None):
+    """A drafter's block over its context: verify_attention's arguments plus window (0 =
+    the whole context) and flags (ATTN_DYNAMIC_SPLITS | ATTN_BIDIRECTIONAL |
+    ATTN_SLIDING_WINDOW)."""
+    dtype = _attention_dtype(q, k_cache, v_cache, out, cu_rows, ctx_lens, workspace)
+    total, hq, d = q.shape
+    batch, hkv, s_max, _ = k_cache.shape
+    st = _lib().block_attention(_ptr(q), _ptr(k_cache), _ptr(v_cache), dtype, _ptr(cu_rows),
+                                _ptr(ctx_lens), batch, total, hq, hkv, d, s_max,
+                                int(max_rows_per_seq), int(max_kv_len), float(scale),
+                                int(window), int(flags), _ptr(out), _ptr(workspace),
+                                workspace.numel(), _stream(stream))
+    _check(st, "block_attention")
+
+
+def verify_attention(q, k_cache, v_cache, cu_rows, ctx_lens, out, workspace, *,
+                     max_rows_per_seq, max_kv_len, scale=0.0, flags=0, stream=None):
+    """q [T, Hq, D], k_cache / v_cache [B, Hkv, S_max, D] (bf16 or float32 tensors on the
+    GPU), cu_rows [B+1] / ctx_lens [B] int32, out [T, Hq, D] float32, workspace uint8;
+    flags 0 or ATTN_DYNAMIC_SPLITS."""
+    dtype = _attention_dtype(q, k_cache, v_cache, out, cu_rows, ctx_lens, workspace)
+    total, hq, d = q.shape
+    batch, hkv, s_max, _ = k_cache.shape
     st = _lib().verify_attention(_ptr(q), _ptr(k_cache), _ptr(v_cache), dtype, _ptr(cu_rows),
                                  _ptr(ctx_lens), batch, total, hq, hkv, d, s_max,
                                  int(max_rows_per_seq), int(max_kv_len), float(scale),

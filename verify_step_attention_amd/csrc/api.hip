@@ -46,8 +46,23 @@ vsa_status verify_attention(const void* q, const void* k_cache, const void* v_ca
                             int max_rows_per_seq, int max_kv_len, float scale,
                             uint32_t flags, float* out, void* workspace,
                             size_t workspace_bytes, void* stream) {
-    if (!q || !k_cache || !v_cache || !cu_rows || !ctx_lens || !out) return VSA_ERR_INVALID_ARG;
     if (flags & ~VSA_ATTN_DYNAMIC_SPLITS) return VSA_ERR_INVALID_ARG;
+    return block_attention(q, k_cache, v_cache, dtype, cu_rows, ctx_lens, B, total_rows, Hq,
+                           Hkv, D, S_max, max_rows_per_seq, max_kv_len, scale, 0, flags, out,
+                           workspace, workspace_bytes, stream);
+}
+
+vsa_status block_attention(const void* q, const void* k_cache, const void* v_cache,
+                           vsa_dtype dtype, const int32_t* cu_rows, const int32_t* ctx_lens,
+                           int B, int total_rows, int Hq, int Hkv, int D, int S_max,
+                           int max_rows_per_seq, int max_kv_len, float scale, int window,
+                           uint32_t flags, float* out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    if (!q || !k_cache || !v_cache || !cu_rows || !ctx_lens || !out) return VSA_ERR_INVALID_ARG;
+    if (flags & ~(VSA_ATTN_DYNAMIC_SPLITS | VSA_ATTN_BIDIRECTIONAL | VSA_ATTN_SLIDING_WINDOW))
+        return VSA_ERR_INVALID_ARG;
+    if (window < 0 || ((flags & VSA_ATTN_SLIDING_WINDOW) && window == 0))
+        return VSA_ERR_INVALID_ARG;
     if (dtype != VSA_F32 && dtype != VSA_BF16) return VSA_ERR_INVALID_ARG;
     if (B < 1 || total_rows < B || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || S_max < 1 ||
         max_rows_per_seq < 1 || max_kv_len < 1 || max_kv_len > S_max ||
@@ -56,7 +71,13 @@ vsa_status verify_attention(const void* q, const void* k_cache, const void* v_ca
     if ((D != 64 && D != 128) || max_rows_per_seq > kMaxRowsPerSeq ||
         (Hq / Hkv) * max_rows_per_seq > 128)
         return VSA_ERR_UNSUPPORTED;
-    const AttnPlan plan = plan_attention(B, Hq, Hkv, D, max_rows_per_seq, max_kv_len);
+    // A window bounds the keys of every sequence by window + rows (plus one tile of
+    // rounding), so the split count is planned for that; it never exceeds the one the
+    // workspace size query plans for max_kv_len.
+    int plan_len = max_kv_len;
+    if (window > 0 && (long)window + max_rows_per_seq + 128 < (long)max_kv_len)
+        plan_len = window + max_rows_per_seq + 128;
+    const AttnPlan plan = plan_attention(B, Hq, Hkv, D, max_rows_per_seq, plan_len);
     if (!workspace || !aligned256(workspace) || workspace_bytes < plan.bytes)
         return VSA_ERR_WORKSPACE;
 
@@ -87,6 +108,9 @@ vsa_status verify_attention(const void* q, const void* k_cache, const void* v_ca
     a.mcap = plan.mcap;
     const float sc = scale == 0.f ? 1.f / sqrtf((float)D) : scale;
     a.scale_log2 = sc * 1.4426950408889634f;
+    a.window = window;
+    a.mask = ((flags & VSA_ATTN_BIDIRECTIONAL) ? kMaskBidirectional : 0) |
+             ((flags & VSA_ATTN_SLIDING_WINDOW) ? kMaskSliding : 0);
     if (launch_attention(a, plan, dtype, static_cast<hipStream_t>(stream)) != hipSuccess)
         return VSA_ERR_LAUNCH;
     return VSA_OK;

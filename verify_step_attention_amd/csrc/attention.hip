@@ -64,6 +64,21 @@ __device__ __forceinline__ SeqGeom seq_geometry(const AttnArgs& a, int b, bool r
     return s;
 }
 
+// Keys a block row sees. Verify: window 0, causal, so row i sees keys 0 .. ctx + i. A
+// drafter's block (mlx-dspark Changelog [0.20.0] "Changed": only the last `window` context
+// rows, or a trained sliding window; [0.8.1] "Changed": causal or bidirectional in the
+// block): row i at position p = ctx + i sees keys key_lo .. key_hi,
+//   key_lo = 0 | max(0, ctx - window) | max(0, p - window + 1) (sliding),
+//   key_hi = p | ctx + rows - 1 (bidirectional).
+__device__ __forceinline__ int key_lo(const AttnArgs& a, const SeqGeom& s, int i) {
+    if (a.window <= 0) return 0;
+    const int lo = (a.mask & kMaskSliding) ? s.ctx + i - a.window + 1 : s.ctx - a.window;
+    return lo > 0 ? lo : 0;
+}
+__device__ __forceinline__ int key_hi(const AttnArgs& a, const SeqGeom& s, int i) {
+    return (a.mask & kMaskBidirectional) ? s.ctx + s.rows - 1 : s.ctx + i;
+}
+
 // Workgroup statistics of the epilogue, in LDS: kStatCap floats each of
 //   gm[KGX][MC] key-group running max (log2 units) | gl[KGX][MC] key-group sum
 //   | fac[KGX][MC] factor 2^(m_kg - m_wg) | wm[MC] workgroup max | wl[MC] workgroup sum
@@ -172,7 +187,9 @@ __device__ __forceinline__ int kv_swz(int r) {
     else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
-template <int D, int NB>
+// WIN: the call has a window or a bidirectional block (block_attention); without it the
+// kernel is compiled for window 0, causal (verify) and carries none of the extra bounds.
+template <int D, int NB, bool WIN>
 __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const AttnArgs a) {
     constexpr int TK = 128;                  // keys per tile
     constexpr int ROWB = D * 2;              // LDS bytes per key row
@@ -206,7 +223,8 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const AttnArgs a) {
     asm volatile("" ::"s"(a.k), "s"(a.v), "s"(a.tile_ctr), "s"(a.cu_rows), "s"(a.ctx_lens),
                  "s"(a.nsplit), "s"(a.hkv), "s"(a.s_max), "s"(a.max_kv_len), "s"(a.dyn),
                  "s"(a.max_rows), "s"(a.q), "s"(a.out), "s"(a.part_o), "s"(a.part_ml),
-                 "s"(a.err), "s"(a.total_rows), "s"(a.group), "s"(a.mcap), "s"(a.scale_log2));
+                 "s"(a.err), "s"(a.total_rows), "s"(a.group), "s"(a.mcap), "s"(a.scale_log2),
+                 "s"(a.window), "s"(a.mask));
     int unit, split;
     map_block(blockIdx.x, a.nsplit, &unit, &split);    // the grid is units x nsplit
     const int b = unit / a.hkv, g = unit % a.hkv;
@@ -290,12 +308,18 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const AttnArgs a) {
         return;
     }
     const int L = s.ctx + s.rows;                      // keys of this sequence
-    const int nt = tile_count(L);
+    // Streamed keys: from the first key any row sees, rounded down to a tile (key tile t0),
+    // to L; schedule tile t is key tile t0 + t.
+    const int lo_first = WIN ? key_lo(a, s, 0) : 0;
+    const int lo_all = WIN ? key_lo(a, s, s.rows - 1) : 0;
+    const int hi_all = WIN ? key_hi(a, s, 0) : s.ctx;  // every row sees lo_all .. hi_all
+    const int t0 = lo_first / TK;
+    const int nt = tile_count(L - t0 * TK);
     const int t_first = first_tile(nt);
     const int t_last = dyn ? nt : static_end(nt);      // tiles below this one are streamed
     int tail_b = 0, tail_e = 0;
     if (tails) {
-        const int f = L / TK * TK, rem = L - f;
+        const int f = t0 * TK + (L - t0 * TK) / TK * TK, rem = L - f;
         tail_b = f + (int)((uint32_t)(split * rem) / (uint32_t)a.nsplit);
         tail_e = f + (int)((uint32_t)((split + 1) * rem) / (uint32_t)a.nsplit);
     }
@@ -306,9 +330,9 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const AttnArgs a) {
         attn_empty_split<D>(a, unit, split, s);
         return;
     }
-    if (t_first >= 0 && t_first != t_spec) {
+    if (t_first >= 0 && (t0 != 0 || t_first != t_spec)) {
         __builtin_amdgcn_s_waitcnt(0);                 // this wave's blocks are free again
-        issue_tile(t_first, k0s, v0s);
+        issue_tile(t0 + t_first, k0s, v0s);
     } else if (t_first >= 0 && (t_first + 1) * TK > L) {
         // the speculative tile runs past the sequence end: rows from L on may hold
         // anything, and a V row is multiplied by P = 0, so those rows become zeros
@@ -333,6 +357,19 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const AttnArgs a) {
             __builtin_amdgcn_global_load_lds(vbase + src, (lds_void*)(vts + blk * 1024), 16, 0, 0);
         }
     }
+    // Keys below the first one any row sees (a window) may share its tile; a V row is
+    // multiplied by P = 0 there, so those rows become zeros whatever they hold.
+    const bool tail_low = tail_b < tail_e && tail_b < lo_first;
+    if (WIN && lo_first > t0 * TK && (t_first == 0 || tail_low)) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (t_first == 0)
+            for (int e = tid; e < (lo_first - t0 * TK) * CH; e += kThreads)
+                *reinterpret_cast<uint4*>(v0s + (size_t)e * 16) = make_uint4(0, 0, 0, 0);
+        if (tail_low)
+            for (int e = tid; e < (lo_first - tail_b) * CH && e < 32 * CH; e += kThreads)
+                *reinterpret_cast<uint4*>(vts + (size_t)e * 16) = make_uint4(0, 0, 0, 0);
+    }
 
     const int nb = wave % NB, kg = wave / NB;
     const int h = lane >> 5, col = lane & 31;
@@ -341,7 +378,8 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const AttnArgs a) {
     const bool col_valid = n < M;
     const int ri = col_valid ? n / a.group : 0;
     const int hh = col_valid ? n % a.group : 0;
-    const int causal_lim = s.ctx + ri;                 // key t visible iff t <= causal_lim
+    const int lo_c = WIN ? key_lo(a, s, ri) : 0;                  // this column's keys
+    const int hi_c = WIN ? key_hi(a, s, ri) : s.ctx + ri;
 
     // Q^T fragment (B operand): lane holds column n, dims 16*kk + 8*h .. +8
     bf16x8 qf[KSTEPS];
@@ -387,11 +425,11 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const AttnArgs a) {
                 }
             }
             // ---- mask + online softmax (lane owns column n; keys 8(r/4)+4h+r%4). A
-            // sub-tile whose keys all precede the sequence's first verify row is visible to
-            // every row and needs no mask.
+            // sub-tile whose keys every row sees needs no mask.
             float sv[16];
             float mt = kNegInf;
-            if (kbase0 + kl0 + 31 <= s.ctx && kbase0 + kl0 + 31 < khi) {
+            if ((!WIN || kbase0 + kl0 >= lo_all) && kbase0 + kl0 + 31 <= hi_all &&
+                kbase0 + kl0 + 31 < khi) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     sv[r] = sacc[r] * a.scale_log2;
@@ -401,7 +439,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const AttnArgs a) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int tg = kbase0 + kl0 + 8 * (r >> 2) + 4 * h + (r & 3);
-                    const bool vis = col_valid && tg < khi && tg <= causal_lim;
+                    const bool vis = col_valid && tg < khi && tg <= hi_c && (!WIN || tg >= lo_c);
                     sv[r] = vis ? sacc[r] * a.scale_log2 : kNegInf;
                     mt = fmaxf(mt, sv[r]);
                 }
@@ -485,14 +523,14 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const AttnArgs a) {
     for (int t = t_first; t >= 0;) {
         __builtin_amdgcn_s_waitcnt(0);                 // first time: the tail landed too
         const int t1 = next_tile(t, 0);
-        if (t1 >= 0) issue_tile(t1, k1s, v1s);
-        compute_tile(t, k0s, v0s);
+        if (t1 >= 0) issue_tile(t0 + t1, k1s, v1s);
+        compute_tile(t0 + t, k0s, v0s);
         if (t == t_first) compute_tail();
         if (t1 < 0) break;
         __builtin_amdgcn_s_waitcnt(0);
         const int t2 = next_tile(t1, 1);
-        if (t2 >= 0) issue_tile(t2, k0s, v0s);
-        compute_tile(t1, k1s, v1s);
+        if (t2 >= 0) issue_tile(t0 + t2, k0s, v0s);
+        compute_tile(t0 + t1, k1s, v1s);
         t = t2;
     }
 
@@ -1092,7 +1130,9 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const AttnArgs a) {
     if (!s.ok) return;
     const int M = s.rows * a.group;
     const int L = s.ctx + s.rows;
-    const int ntiles = (L + TK - 1) / TK;
+    const int lo_first = key_lo(a, s, 0);
+    const int k0 = lo_first / TK * TK;                   // first streamed key
+    const int ntiles = (L - k0 + TK - 1) / TK;
     const int t_begin = (int)((long)split * ntiles / a.nsplit);
     const int t_end = (int)((long)(split + 1) * ntiles / a.nsplit);
     float* os = reinterpret_cast<float*>(smem);          // [MC][D]   (epilogue O)
@@ -1121,20 +1161,21 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const AttnArgs a) {
         __syncthreads();
         for (int e = tid; e < TK * D; e += kThreads) {
             const int kr = e / D, d = e % D;
-            const int key = t * TK + kr;
-            const bool in = key < L;
+            const int key = k0 + t * TK + kr;
+            const bool in = key < L && key >= lo_first;
             ks[kr * KROW + d] = in ? kb[(size_t)key * D + d] : 0.f;
             vs[e] = in ? vb[(size_t)key * D + d] : 0.f;
         }
         __syncthreads();
         for (int e = tid; e < M * TK; e += kThreads) {
             const int n = e / TK, kr = e % TK;
-            const int key = t * TK + kr;
+            const int key = k0 + t * TK + kr;
             const float* qrow = qg + ((size_t)(s.r0 + n / a.group) * a.hq + g * a.group +
                                       n % a.group) * D;
             float dot = 0.f;
             for (int d = 0; d < D; ++d) dot = fmaf(qrow[d], ks[kr * KROW + d], dot);
-            const bool vis = key < L && key <= s.ctx + n / a.group;
+            const int ri = n / a.group;
+            const bool vis = key < L && key <= key_hi(a, s, ri) && key >= key_lo(a, s, ri);
             ss[n * TK + kr] = vis ? dot * a.scale_log2 : kNegInf;
         }
         __syncthreads();
@@ -1286,15 +1327,21 @@ hipError_t launch_attention(const AttnArgs& a, const AttnPlan& p, vsa_dtype dtyp
         }
 #undef VSA_KVQ
     } else if (dtype == VSA_BF16) {
+#define VSA_BF16K(DD, NBB, WW) hipLaunchKernelGGL((attn_bf16_kernel<DD, NBB, WW>), grid, block, 0, stream, a)
+#define VSA_BF16D(DD, WW)                                                      \
+    do {                                                                       \
+        if (p.nb == 1) VSA_BF16K(DD, 1, WW);                                   \
+        else if (p.nb == 2) VSA_BF16K(DD, 2, WW);                              \
+        else VSA_BF16K(DD, 4, WW);                                             \
+    } while (0)
+        const bool win = a.window > 0 || a.mask != 0;
         if (a.d == 128) {
-            if (p.nb == 1) hipLaunchKernelGGL((attn_bf16_kernel<128, 1>), grid, block, 0, stream, a);
-            else if (p.nb == 2) hipLaunchKernelGGL((attn_bf16_kernel<128, 2>), grid, block, 0, stream, a);
-            else hipLaunchKernelGGL((attn_bf16_kernel<128, 4>), grid, block, 0, stream, a);
+            if (win) VSA_BF16D(128, true); else VSA_BF16D(128, false);
         } else {
-            if (p.nb == 1) hipLaunchKernelGGL((attn_bf16_kernel<64, 1>), grid, block, 0, stream, a);
-            else if (p.nb == 2) hipLaunchKernelGGL((attn_bf16_kernel<64, 2>), grid, block, 0, stream, a);
-            else hipLaunchKernelGGL((attn_bf16_kernel<64, 4>), grid, block, 0, stream, a);
+            if (win) VSA_BF16D(64, true); else VSA_BF16D(64, false);
         }
+#undef VSA_BF16D
+#undef VSA_BF16K
     } else {
         if (a.d == 128) hipLaunchKernelGGL((attn_f32_kernel<128>), grid, block, 0, stream, a);
         else hipLaunchKernelGGL((attn_f32_kernel<64>), grid, block, 0, stream, a);

@@ -197,7 +197,11 @@ struct AttnArgs {
     uint32_t* err;
     int batch, total_rows, hq, group, d, units, mcap;
     float scale_log2;       // softmax scale * log2(e)
+    int window;             // > 0: context keys seen per row are limited (see mask)
+    int mask;               // kMaskBidirectional | kMaskSliding
 };
+constexpr int kMaskBidirectional = 1;   // block rows see every block row
+constexpr int kMaskSliding = 2;         // the window ends at each row's own position
 
 // Host-side plan shared by the size query and the launcher.
 struct AttnPlan {

@@ -120,6 +120,8 @@ _SPECS = {
     "batched": (1003, 4, (2, 7), (750, 8192), 32, 8, 128, BF16, 151936),
     "long": (1004, 1, 8, 32768, 48, 8, 128, BF16, 262144),
     "swarm": (1005, 16, 4, (2048, 16384), 32, 8, 128, BF16, 151936),
+    # a drafter's block of 8 rows over a 32k context (attention only; tiny vocabulary)
+    "drafter_b4r8_ctx32768": (1006, 4, 7, 32768, 32, 8, 128, BF16, 1024),
 }
 
 WORKLOAD_NAMES = tuple(_SPECS)
@@ -142,8 +144,8 @@ def _zipf_counts(rng, batch, vocab):
 
 
 def _default_params(name, batch):
-    if name == "tiny":
-        return [Params()]
+    if name in ("tiny", "drafter_b4r8_ctx32768"):
+        return [Params()] * batch
     if name == "qwen3_4b":
         return [Params(temperature=0.7, top_k=20, top_p=0.8)]
     if name in ("batched", "verify_b4k4_ctx8192"):
