@@ -357,3 +357,27 @@ def sample_proposals(draft_logits, cu_rows, params, positions, seed):
                 out[r0 - b + t - 1] = exponential_race(q.probs, seed, b,
                                                        int(positions[b]) + t - 1)[0]
     return out
+
+
+def widen_draft_logits(draft_logits, d2t, vocab):
+    """Reduced draft vocabulary (Changelog [0.8.0] "Added", reduced draft vocabularies): the
+    draft head scores only a subset of V_d target tokens, and an offset table maps draft id
+    j to target id j + d2t[j]. Before the accept test the draft distribution is widened
+    onto the target vocabulary, so the residual still runs over every target id. Written
+    out on logits: [rows, V_d] -> [rows, V], target id j + d2t[j] takes draft logit j and
+    every other target id -inf (probability 0 after any softmax, truncation or race). The
+    widened rows then enter verify_sample_accept unchanged. The table must map the draft
+    ids to distinct target ids in [0, V)."""
+    dl = np.asarray(draft_logits, dtype=np.float32)
+    d2t = np.asarray(d2t, dtype=np.int64)
+    rows, dvocab = dl.shape if dl.ndim == 2 else (0, len(d2t))
+    if d2t.shape != (dvocab,):
+        raise ValueError("d2t must hold one offset per draft id")
+    target = np.arange(dvocab, dtype=np.int64) + d2t
+    if target.size and (target.min() < 0 or target.max() >= vocab):
+        raise ValueError("d2t maps a draft id outside the target vocabulary")
+    if len(np.unique(target)) != dvocab:
+        raise ValueError("d2t maps two draft ids to one target id")
+    out = np.full((rows, vocab), -np.inf, dtype=np.float32)
+    out[:, target] = dl.reshape(rows, dvocab)
+    return out
