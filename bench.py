@@ -16,6 +16,10 @@ at run time) unless --static-splits asks for fixed, bitwise reproducible ranges.
 group of 64 dimensions with fp16 scale and bias) through verify_attention_kvq; the default
 16 is the bf16 cache.
 
+--draft-vocab N gives the step's drafts a reduced vocabulary of N ids (a seeded subset of the
+target vocabulary and its offset table, as EAGLE-3-style heads ship): draft logits are
+[rows, N] and verify_sample_accept_reduced_draft reads them through the inverse table.
+
     python bench.py --drafter-block [--window W] [--bidirectional] [--sliding]
 
 times block_attention alone on a drafter's block instead: B=4 blocks of 8 rows over a
@@ -47,7 +51,7 @@ COUNTERS = os.path.join(ROOT, "profiles", "attention_b4k4_ctx8192_counters.json"
 ATTN_SRC = os.path.join(ROOT, "verify_step_attention_amd", "csrc", "attention.hip")
 
 
-def algorithmic_bytes(w, kv_bits=16):
+def algorithmic_bytes(w, kv_bits=16, draft_vocab=0):
     """Bytes each kernel must move at least once (inputs read once, outputs written once).
     A quantized key row is D * bits / 8 code bytes and 4 bytes of (scale, bias) per group
     of 64 dimensions."""
@@ -59,7 +63,9 @@ def algorithmic_bytes(w, kv_bits=16):
     o = w.total_rows * w.num_q_heads * w.head_dim * 4
     sampled = [b for b in range(w.batch) if w.params[b].temperature > 0]
     tl = w.total_rows * w.vocab * 4
-    dl = sum(int(rows[b] - 1) for b in sampled) * w.vocab * 4
+    dl = sum(int(rows[b] - 1) for b in sampled) * (draft_vocab or w.vocab) * 4
+    if draft_vocab and sampled:
+        dl += w.vocab * 4                                   # the inverse table, once
     cnt = w.batch * w.vocab * 4 if w.token_counts is not None else 0
     small = w.total_rows * 4 * 2 + w.batch * 4 * 4          # drafts, tokens, lengths, params
     return {"attention": kv + q + o, "sample": tl + dl + cnt + small,
@@ -309,6 +315,8 @@ def main():
                          "instead of tiles claimed at run time")
     ap.add_argument("--kv-bits", type=int, default=16, choices=(16, 8, 4),
                     help="K/V cache: bf16 (16) or affine codes of 8 or 4 bits")
+    ap.add_argument("--draft-vocab", type=int, default=0,
+                    help="reduced draft vocabulary size (0: drafts over the whole vocabulary)")
     ap.add_argument("--drafter-block", action="store_true",
                     help="time block_attention on a drafter's block instead of the step")
     ap.add_argument("--window", type=int, default=4096)
@@ -337,7 +345,7 @@ def main():
 
     print(f"[bench] building inputs for {WORKLOAD}", file=sys.stderr, flush=True)
     w = wl.make_workload(WORKLOAD)
-    nbytes = algorithmic_bytes(w, args.kv_bits)
+    nbytes = algorithmic_bytes(w, args.kv_bits, args.draft_vocab)
     step_bytes = nbytes["attention"] + nbytes["sample"]
     dev0 = wl.device_tensors(w)
     kq = None
@@ -347,6 +355,17 @@ def main():
         dev0.update(k_codes=dev(kq.k_codes), k_sb=dev(kq.k_sb), v_codes=dev(kq.v_codes),
                     v_sb=dev(kq.v_sb))
         del dev0["k_cache"], dev0["v_cache"]
+    t2d = None
+    if args.draft_vocab:
+        rng = np.random.default_rng(77)
+        subset = np.sort(rng.choice(w.vocab, size=args.draft_vocab, replace=False))
+        d2t = torch.from_numpy((subset - np.arange(args.draft_vocab)).astype(np.int32)).cuda()
+        t2d = torch.empty(w.vocab, dtype=torch.int32, device="cuda")
+        vsa.draft_vocab_inverse(d2t, w.vocab, t2d)
+        idx = torch.from_numpy(subset).cuda()
+        # draft rows over the subset; the step's drafts are ids of the subset
+        dev0["draft_logits"] = dev0["draft_logits"][:, idx].contiguous()
+        dev0["draft_tokens"] = idx[torch.argmax(dev0["draft_logits"], dim=1)].to(torch.int32)
     sets = [dev0] + [{k: (None if t is None else t.clone()) for k, t in dev0.items()}
                      for _ in range(args.sets - 1)]
     params = torch.from_numpy(vsa.pack_row_params(w.params).view(np.uint8)).cuda()
@@ -376,10 +395,18 @@ def main():
                                      flags=ATTN_FLAGS, stream=stream if s is None else s)
 
     def sample(d, s=None):
-        vsa.verify_sample_accept(d["target_logits"], d["draft_logits"], d["draft_tokens"],
-                                 d["cu_rows"], d["token_counts"], params, d["positions"], 0,
-                                 acc, toks, ws_s, max_rows_per_seq=w.max_rows, max_top_k=mtk,
-                                 max_top_logprobs=mtl, stream=stream if s is None else s)
+        if t2d is None:
+            vsa.verify_sample_accept(d["target_logits"], d["draft_logits"], d["draft_tokens"],
+                                     d["cu_rows"], d["token_counts"], params, d["positions"],
+                                     0, acc, toks, ws_s, max_rows_per_seq=w.max_rows,
+                                     max_top_k=mtk, max_top_logprobs=mtl,
+                                     stream=stream if s is None else s)
+        else:
+            vsa.verify_sample_accept_reduced_draft(
+                d["target_logits"], d["draft_logits"], t2d, d["draft_tokens"], d["cu_rows"],
+                d["token_counts"], params, d["positions"], 0, acc, toks, ws_s,
+                max_rows_per_seq=w.max_rows, max_top_k=mtk, max_top_logprobs=mtl,
+                stream=stream if s is None else s)
 
     if args.copy_probe_mib:
         src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device="cuda")
@@ -527,6 +554,7 @@ def main():
             "logits_dtype": "f32",
             "attention_splits": "dynamic" if ATTN_FLAGS else "static",
             "kv_bits": args.kv_bits,
+            "draft_vocab": args.draft_vocab or w.vocab,
         },
         "roofline": {
             "bound": "hbm",
@@ -545,7 +573,14 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on the host", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(w, kq)
+        wc = w
+        if t2d is not None:
+            from oracle.sampling import widen_draft_logits
+            wc = w.with_params(w.params)
+            wc.draft_logits = widen_draft_logits(dev0["draft_logits"].cpu().numpy(),
+                                                 d2t.cpu().numpy(), w.vocab)
+            wc.draft_tokens = dev0["draft_tokens"].cpu().numpy()
+        line["cpu_baseline"] = cpu_baseline(wc, kq)
     print(json.dumps(line), flush=True)
 
 

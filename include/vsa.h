@@ -81,6 +81,8 @@ typedef enum vsa_dtype {
                                            workgroups could not all run at once, e.g.
                                            other work held the GPU): the token drawn for
                                            that sequence is unreliable */
+#define VSA_DEVERR_DRAFT_MAP      0x40u /* a t2d entry outside [-1, draft_vocab): read as
+                                           "no draft id" (probability 0) */
 
 /* Per-sequence sampling parameters: the request parameters the pages list (temperature,
  * top_p, top_k, presence/frequency penalty, logprobs, top_logprobs; release v0.1.0 and
@@ -271,6 +273,40 @@ vsa_status verify_sample_accept(const float* target_logits, const float* draft_l
                                 int32_t* out_tokens, float* chosen_logprob, float* top_lp_vals,
                                 int32_t* top_lp_ids, float* diag_threshold, int32_t* diag_kept,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * Reduced draft vocabularies (Changelog [0.8.0] "Added": EAGLE-3-style heads score a
+ * frequent-token subset of draft_vocab ids and ship an offset table d2t, draft id j
+ * standing for target id j + d2t[j]; temperature sampling widens the draft distribution
+ * onto the target vocabulary before the accept test, so the residual runs over every
+ * target id).
+ *
+ * draft_vocab_inverse builds, once per drafter, the inverse table the verify call reads:
+ *   d2t    [draft_vocab] int32 offsets (device); entries mapping outside [0, V) are
+ *          skipped; the map must be one-to-one (if two draft ids share a target id the
+ *          higher one is kept)
+ *   t2d    [V] int32 output (device, 16-byte aligned): the draft id of each target id,
+ *          -1 where none maps. Two kernels on `stream`; nothing is allocated.
+ *
+ * verify_sample_accept_reduced_draft is verify_sample_accept with
+ *   draft_logits  [total_rows - B, draft_vocab] float32 (draft ids), or NULL
+ *   draft_vocab   1 <= draft_vocab <= V
+ *   t2d           [V] int32 from draft_vocab_inverse (16-byte aligned when V % 4 == 0)
+ * and computes exactly what verify_sample_accept computes on the widened draft rows
+ * (target id x takes the draft logit of t2d[x], or -inf when t2d[x] = -1). Draft tokens,
+ * outputs and every other argument are in target ids as before.
+ * ------------------------------------------------------------------------------------ */
+vsa_status draft_vocab_inverse(const int32_t* d2t, int draft_vocab, int V, int32_t* t2d,
+                               void* stream);
+
+vsa_status verify_sample_accept_reduced_draft(
+    const float* target_logits, const float* draft_logits, int draft_vocab, const int32_t* t2d,
+    const int32_t* draft_tokens, const int32_t* cu_rows, const int32_t* token_counts,
+    const vsa_row_params* params, const int32_t* positions, uint64_t seed, int B,
+    int total_rows, int V, int max_rows_per_seq, int max_top_k, int max_top_logprobs,
+    int32_t* accepted_len, int32_t* out_tokens, float* chosen_logprob, float* top_lp_vals,
+    int32_t* top_lp_ids, float* diag_threshold, int32_t* diag_kept, void* workspace,
+    size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -59,7 +59,10 @@ def q_distributed_drafts(w, seed=1):
                             seed).astype(np.int32)
 
 
-def sample_gpu(w, seed=0, max_top_k=None, max_top_lp=None, workspace=None, dev=None):
+def sample_gpu(w, seed=0, max_top_k=None, max_top_lp=None, workspace=None, dev=None,
+               reduced=None):
+    """reduced: (draft logits [T-B, V_d] device tensor, t2d [V] device tensor) to call
+    verify_sample_accept_reduced_draft instead."""
     dev = dev or wl.device_tensors(w, with_kv=False)
     mtk = max_top_k if max_top_k is not None else max([p.top_k for p in w.params] + [0])
     mtl = max_top_lp if max_top_lp is not None else max([p.top_logprobs for p in w.params] + [0])
@@ -80,14 +83,22 @@ def sample_gpu(w, seed=0, max_top_k=None, max_top_lp=None, workspace=None, dev=N
         "diag_threshold": torch.full((t,), 7.0, dtype=torch.float32, device="cuda"),
         "diag_kept": torch.full((t, 2), -7, dtype=torch.int32, device="cuda"),
     }
-    draft_logits = dev["draft_logits"] if any(p.temperature > 0 for p in w.params) else None
-    vsa.verify_sample_accept(dev["target_logits"], draft_logits, dev["draft_tokens"],
-                             dev["cu_rows"], dev["token_counts"], params, dev["positions"],
-                             seed, out["accepted_len"], out["out_tokens"], ws,
-                             max_rows_per_seq=w.max_rows, max_top_k=mtk, max_top_logprobs=mtl,
-                             chosen_logprob=out["chosen_logprob"],
-                             top_lp_vals=out["top_lp_vals"], top_lp_ids=out["top_lp_ids"],
-                             diag_threshold=out["diag_threshold"], diag_kept=out["diag_kept"])
+    sampled = any(p.temperature > 0 for p in w.params)
+    opt = dict(max_rows_per_seq=w.max_rows, max_top_k=mtk, max_top_logprobs=mtl,
+               chosen_logprob=out["chosen_logprob"], top_lp_vals=out["top_lp_vals"],
+               top_lp_ids=out["top_lp_ids"], diag_threshold=out["diag_threshold"],
+               diag_kept=out["diag_kept"])
+    if reduced is None:
+        draft_logits = dev["draft_logits"] if sampled else None
+        vsa.verify_sample_accept(dev["target_logits"], draft_logits, dev["draft_tokens"],
+                                 dev["cu_rows"], dev["token_counts"], params, dev["positions"],
+                                 seed, out["accepted_len"], out["out_tokens"], ws, **opt)
+    else:
+        draft_logits, t2d = reduced
+        vsa.verify_sample_accept_reduced_draft(
+            dev["target_logits"], draft_logits if sampled else None, t2d, dev["draft_tokens"],
+            dev["cu_rows"], dev["token_counts"], params, dev["positions"], seed,
+            out["accepted_len"], out["out_tokens"], ws, **opt)
     torch.cuda.synchronize()
     res = {k: v.cpu().numpy() for k, v in out.items()}
     res["top_lp_vals"] = res["top_lp_vals"][:, :mtl]

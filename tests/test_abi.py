@@ -151,3 +151,17 @@ def test_sample_host_checks(lib):
     assert _sample(lib, rows=40, total=20) == UNSUPPORTED
     assert _sample(lib, ws=None) == WORKSPACE
     assert _sample(lib, ws_bytes=256) == WORKSPACE
+
+
+def test_reduced_draft_host_checks(lib):
+    def call(dvocab=32000, t2d=FAKE * 256, V=151936):
+        return lib.verify_sample_accept_reduced_draft(
+            FAKE, FAKE, dvocab, t2d, FAKE, FAKE, None, FAKE, FAKE, 0, 4, 20, V, 5, 0, 0, FAKE,
+            FAKE, None, None, None, None, None, FAKE * 256, 1 << 30, None)
+    assert call(t2d=None) == INVALID_ARG                      # a reduced vocab needs t2d
+    assert call(dvocab=0) == INVALID_ARG
+    assert call(dvocab=151937) == INVALID_ARG                 # larger than V
+    assert call(t2d=FAKE * 256 + 4) == INVALID_ARG            # t2d not 16-byte aligned
+    assert lib.draft_vocab_inverse(None, 10, 100, FAKE * 256, None) == INVALID_ARG
+    assert lib.draft_vocab_inverse(FAKE, 101, 100, FAKE * 256, None) == INVALID_ARG
+    assert lib.draft_vocab_inverse(FAKE, 10, 100, FAKE * 256 + 8, None) == INVALID_ARG

@@ -20,6 +20,8 @@ DEVERR_DRAFT_ID = 0x02
 DEVERR_PARAMS = 0x04
 DEVERR_NO_DRAFT_LOGITS = 0x08
 DEVERR_TIE_OVERFLOW = 0x10
+DEVERR_WAIT_TIMEOUT = 0x20
+DEVERR_DRAFT_MAP = 0x40
 
 # attention flags (verify_attention: only ATTN_DYNAMIC_SPLITS)
 ATTN_DYNAMIC_SPLITS = 0x1
@@ -33,7 +35,8 @@ ROW_PARAMS_DTYPE = np.dtype([("temperature", "<f4"), ("top_k", "<i4"), ("top_p",
 
 EXPORTED_SYMBOLS = ("vsa_version", "vsa_status_string", "verify_attention_workspace_size",
                     "verify_attention", "block_attention", "verify_attention_kvq",
-                    "verify_sample_accept_workspace_size", "verify_sample_accept")
+                    "verify_sample_accept_workspace_size", "verify_sample_accept",
+                    "draft_vocab_inverse", "verify_sample_accept_reduced_draft")
 
 
 class VsaError(RuntimeError):
@@ -82,6 +85,13 @@ def _lib():
                                              c_int, c_int, c_int, c_void, c_void, c_void,
                                              c_void, c_void, c_void, c_void, c_void, c_size,
                                              c_void]
+        lib.draft_vocab_inverse.restype = c_int
+        lib.draft_vocab_inverse.argtypes = [c_void, c_int, c_int, c_void, c_void]
+        lib.verify_sample_accept_reduced_draft.restype = c_int
+        lib.verify_sample_accept_reduced_draft.argtypes = [
+            c_void, c_void, c_int, c_void, c_void, c_void, c_void, c_void, c_void,
+            ctypes.c_uint64, c_int, c_int, c_int, c_int, c_int, c_int, c_void, c_void, c_void,
+            c_void, c_void, c_void, c_void, c_void, c_size, c_void]
         _lib_handle = lib
     return _lib_handle
 
@@ -241,3 +251,35 @@ def verify_sample_accept(target_logits, draft_logits, draft_tokens, cu_rows, tok
         _ptr(diag_threshold), _ptr(diag_kept), _ptr(workspace), workspace.numel(),
         _stream(stream))
     _check(st, "verify_sample_accept")
+
+
+def draft_vocab_inverse(d2t, vocab, t2d, stream=None):
+    """Reduced draft vocabulary: d2t [V_d] int32 offsets (target id = j + d2t[j]) -> t2d [V]
+    int32 (draft id of each target id, -1 where none), both device tensors."""
+    if d2t.dtype != t2d.dtype or t2d.numel() != vocab or not d2t.is_contiguous() or \
+            not t2d.is_contiguous():
+        raise ValueError("d2t / t2d must be contiguous int32 tensors, t2d of size V")
+    _check(_lib().draft_vocab_inverse(_ptr(d2t), d2t.numel(), int(vocab), _ptr(t2d),
+                                      _stream(stream)), "draft_vocab_inverse")
+
+
+def verify_sample_accept_reduced_draft(target_logits, draft_logits, t2d, draft_tokens, cu_rows,
+                                       token_counts, params, positions, seed, accepted_len,
+                                       out_tokens, workspace, *, max_rows_per_seq, max_top_k,
+                                       max_top_logprobs, chosen_logprob=None, top_lp_vals=None,
+                                       top_lp_ids=None, diag_threshold=None, diag_kept=None,
+                                       stream=None):
+    """verify_sample_accept with draft_logits [T-B, V_d] over a reduced draft vocabulary and
+    t2d [V] int32 from draft_vocab_inverse; everything else in target ids as before."""
+    total, vocab = target_logits.shape
+    batch = cu_rows.numel() - 1
+    dvocab = draft_logits.shape[1] if draft_logits is not None else vocab
+    st = _lib().verify_sample_accept_reduced_draft(
+        _ptr(target_logits), _ptr(draft_logits), int(dvocab), _ptr(t2d), _ptr(draft_tokens),
+        _ptr(cu_rows), _ptr(token_counts), _ptr(params), _ptr(positions),
+        ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF), batch, total, vocab,
+        int(max_rows_per_seq), int(max_top_k), int(max_top_logprobs), _ptr(accepted_len),
+        _ptr(out_tokens), _ptr(chosen_logprob), _ptr(top_lp_vals), _ptr(top_lp_ids),
+        _ptr(diag_threshold), _ptr(diag_kept), _ptr(workspace), workspace.numel(),
+        _stream(stream))
+    _check(st, "verify_sample_accept_reduced_draft")

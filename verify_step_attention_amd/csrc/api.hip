@@ -196,12 +196,41 @@ vsa_status verify_sample_accept(const float* target_logits, const float* draft_l
                                 int32_t* out_tokens, float* chosen_logprob, float* top_lp_vals,
                                 int32_t* top_lp_ids, float* diag_threshold, int32_t* diag_kept,
                                 void* workspace, size_t workspace_bytes, void* stream) {
+    return verify_sample_accept_reduced_draft(
+        target_logits, draft_logits, V, nullptr, draft_tokens, cu_rows, token_counts, params,
+        positions, seed, B, total_rows, V, max_rows_per_seq, max_top_k, max_top_logprobs,
+        accepted_len, out_tokens, chosen_logprob, top_lp_vals, top_lp_ids, diag_threshold,
+        diag_kept, workspace, workspace_bytes, stream);
+}
+
+vsa_status draft_vocab_inverse(const int32_t* d2t, int draft_vocab, int V, int32_t* t2d,
+                               void* stream) {
+    if (!d2t || !t2d || draft_vocab < 1 || V < 1 || draft_vocab > V) return VSA_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(t2d) & 15u) != 0) return VSA_ERR_INVALID_ARG;
+    if (launch_draft_vocab_inverse(d2t, draft_vocab, V, t2d,
+                                   static_cast<hipStream_t>(stream)) != hipSuccess)
+        return VSA_ERR_LAUNCH;
+    return VSA_OK;
+}
+
+vsa_status verify_sample_accept_reduced_draft(
+    const float* target_logits, const float* draft_logits, int draft_vocab, const int32_t* t2d,
+    const int32_t* draft_tokens, const int32_t* cu_rows, const int32_t* token_counts,
+    const vsa_row_params* params, const int32_t* positions, uint64_t seed, int B,
+    int total_rows, int V, int max_rows_per_seq, int max_top_k, int max_top_logprobs,
+    int32_t* accepted_len, int32_t* out_tokens, float* chosen_logprob, float* top_lp_vals,
+    int32_t* top_lp_ids, float* diag_threshold, int32_t* diag_kept, void* workspace,
+    size_t workspace_bytes, void* stream) {
     if (!target_logits || !cu_rows || !params || !positions || !accepted_len || !out_tokens)
         return VSA_ERR_INVALID_ARG;
     if (B < 1 || total_rows < B || V < 1 || max_rows_per_seq < 1 || max_top_k < 0 ||
         max_top_logprobs < 0 || total_rows > B * max_rows_per_seq)
         return VSA_ERR_INVALID_ARG;
     if (total_rows > B && !draft_tokens) return VSA_ERR_INVALID_ARG;
+    if (draft_vocab < 1 || draft_vocab > V || (draft_vocab != V && !t2d))
+        return VSA_ERR_INVALID_ARG;
+    if (t2d && (V % 4) == 0 && (reinterpret_cast<uintptr_t>(t2d) & 15u) != 0)
+        return VSA_ERR_INVALID_ARG;
     if (V > kMaxVocab || max_rows_per_seq > kMaxRowsPerSeq || max_top_k > kMaxTopK ||
         max_top_logprobs > kMaxTopLogprobs)
         return VSA_ERR_UNSUPPORTED;
@@ -212,6 +241,8 @@ vsa_status verify_sample_accept(const float* target_logits, const float* draft_l
     SampArgs a{};
     a.tl = target_logits;
     a.dl = draft_logits;
+    a.t2d = t2d;
+    a.dvocab = t2d ? draft_vocab : V;
     a.drafts = draft_tokens;
     a.cu_rows = cu_rows;
     a.counts = token_counts;

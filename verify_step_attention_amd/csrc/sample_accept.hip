@@ -183,11 +183,6 @@ __device__ __forceinline__ RowRef row_ref(const SampArgs& a, const SeqMode& m, i
     return r;
 }
 
-__device__ __forceinline__ const float* row_ptr(const SampArgs& a, const SeqMode& m,
-                                                const RowRef& r) {
-    if (r.kind == 1) return a.dl + (size_t)(m.d0 + r.i - 1) * a.vocab;
-    return a.tl + (size_t)(m.r0 + r.i) * a.vocab;
-}
 
 // ------------------------------------------------------------------ workgroup radix select
 // The k-th largest key (1-based) among the valid keys of the workgroup, 8 bits at a time.
@@ -300,6 +295,78 @@ __device__ __forceinline__ void load_chunk(const float* row, int base, int vocab
             const int j = base + 1024 * (e >> 2) + 4 * tid + (e & 3);
             x[e] = j < vocab ? row[j] : kNegInf;
         }
+    }
+}
+
+// A draft row's logits at the chunk's target ids. With a reduced draft vocabulary
+// (mlx-dspark Changelog [0.8.0] "Added": draft id j stands for target id j + d2t[j], and
+// the draft distribution is widened onto the target vocabulary before the accept test)
+// a target id takes the logit of its draft id through the inverse table t2d, and -inf
+// (probability 0) when no draft id maps to it; an entry outside [-1, dvocab) reads as
+// -inf and sets VSA_DEVERR_DRAFT_MAP.
+__device__ __forceinline__ float mapped_logit(const SampArgs& a, const float* row, int m,
+                                              uint32_t* ebits) {
+    if ((uint32_t)m < (uint32_t)a.dvocab) return row[m];
+    if (m != -1) *ebits |= VSA_DEVERR_DRAFT_MAP;
+    return kNegInf;
+}
+// MAP: the call has a reduced draft vocabulary (kernels are compiled both ways, so the
+// full-vocabulary path carries none of this).
+template <bool VEC, bool MAP>
+__device__ __forceinline__ void load_draft_chunk(const SampArgs& a, int drow, int base,
+                                                 float (&x)[kEpt]) {
+    if constexpr (!MAP) {
+        load_chunk<VEC>(a.dl + (size_t)drow * a.vocab, base, a.vocab, x);
+        return;
+    }
+    const float* row = a.dl + (size_t)drow * a.dvocab;
+    const int tid = threadIdx.x;
+    int map[kEpt];
+    if (VEC) {
+#pragma unroll
+        for (int q = 0; q < kQuads; ++q) {
+            const int j = base + 1024 * q + 4 * tid;
+            int4 v = make_int4(-1, -1, -1, -1);
+            if (j < a.vocab) v = *reinterpret_cast<const int4*>(a.t2d + j);
+            map[4 * q] = v.x;
+            map[4 * q + 1] = v.y;
+            map[4 * q + 2] = v.z;
+            map[4 * q + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < kEpt; ++e) {
+            const int j = base + 1024 * (e >> 2) + 4 * tid + (e & 3);
+            map[e] = j < a.vocab ? a.t2d[j] : -1;
+        }
+    }
+    uint32_t ebits = 0;
+#pragma unroll
+    for (int e = 0; e < kEpt; ++e) x[e] = mapped_logit(a, row, map[e], &ebits);
+    if (ebits) atomicOr(a.err, ebits);
+}
+// The draft logit of target id `id` in draft row drow (id inside [0, V)).
+template <bool MAP>
+__device__ __forceinline__ float draft_logit(const SampArgs& a, int drow, int id) {
+    if constexpr (!MAP) return a.dl[(size_t)drow * a.vocab + id];
+    const float* row = a.dl + (size_t)drow * a.dvocab;
+    uint32_t ebits = 0;
+    const float v = mapped_logit(a, row, a.t2d[id], &ebits);
+    if (ebits) atomicOr(a.err, ebits);
+    return v;
+}
+// Row q of a sequence's row list (target, draft or raw) at the chunk's ids.
+template <bool VEC, bool MAP>
+__device__ __forceinline__ void load_row_chunk(const SampArgs& a, const SeqMode& m,
+                                               const RowRef& r, int base, float (&x)[kEpt]) {
+    if constexpr (!MAP) {
+        // one load path for every row kind: only the row's address differs
+        const float* row = r.kind == 1 ? a.dl + (size_t)(m.d0 + r.i - 1) * a.vocab
+                                       : a.tl + (size_t)(m.r0 + r.i) * a.vocab;
+        load_chunk<VEC>(row, base, a.vocab, x);
+    } else {
+        if (r.kind == 1) load_draft_chunk<VEC, MAP>(a, m.d0 + r.i - 1, base, x);
+        else load_chunk<VEC>(a.tl + (size_t)(m.r0 + r.i) * a.vocab, base, a.vocab, x);
     }
 }
 
@@ -805,7 +872,7 @@ __device__ __forceinline__ uint32_t race_word(int kind, int acc) {
     return 1u | ((uint32_t)kind << 1) | ((uint32_t)acc << 8);
 }
 
-template <bool AFTER_SELECT>
+template <bool AFTER_SELECT, bool MAP>
 __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, FinalShared& fs,
                                   RowInfo* rinfo /* LDS, one per row of the list */,
                                   const int* drafts_lds /* the K draft ids in LDS, or null */,
@@ -827,7 +894,7 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
         if (m.sampled && !m.topk && pre_d >= 0 && pre_d < a.vocab) {
             pre_c = a.counts ? a.counts[(size_t)b * a.vocab + pre_d] : 0;
             pre_xt = a.tl[(size_t)(m.r0 + lane) * a.vocab + pre_d];
-            pre_xd = a.dl[(size_t)(m.d0 + lane) * a.vocab + pre_d];
+            pre_xd = draft_logit<MAP>(a, m.d0 + lane, pre_d);
         }
     }
 
@@ -1168,7 +1235,7 @@ __device__ uint32_t wait_race_word(const SampArgs& a, int b) {
 }
 
 // Separate race kernel (top-k pipeline, or a sweep grid too large to be resident at once).
-template <bool VEC>
+template <bool VEC, bool MAP>
 __global__ __launch_bounds__(kThreads) void race_kernel(const SampArgs a) {
     __shared__ int s_draft[kMaxSeqRows];
     __shared__ int s_last;
@@ -1185,7 +1252,7 @@ __global__ __launch_bounds__(kThreads) void race_kernel(const SampArgs a) {
     load_counts<VEC>(a.counts ? a.counts + (size_t)b * a.vocab : nullptr, base, a.vocab, cnt);
     float xp[kEpt], xq[kEpt];
     load_chunk<VEC>(a.tl + (size_t)(m.r0 + rq.a) * a.vocab, base, a.vocab, xp);
-    if (rq.kind == 1) load_chunk<VEC>(a.dl + (size_t)(m.d0 + rq.a) * a.vocab, base, a.vocab, xq);
+    if (rq.kind == 1) load_draft_chunk<VEC, MAP>(a, m.d0 + rq.a, base, xq);
     else
 #pragma unroll
         for (int e = 0; e < kEpt; ++e) xq[e] = 0.f;
@@ -1206,7 +1273,7 @@ __global__ __launch_bounds__(kThreads) void race_kernel(const SampArgs a) {
                                         : __builtin_nanf("");
 }
 
-template <bool VEC, bool TOPK>
+template <bool VEC, bool TOPK, bool MAP>
 __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
     __shared__ float4 s_part[3 * kMaxSeqRows][4];
     __shared__ int s_draft[kMaxSeqRows];
@@ -1253,8 +1320,7 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
         float xv[kRowBatch][kEpt];
 #pragma unroll
         for (int u = 0; u < kRowBatch; ++u)
-            if (q0 + u < nrows) load_chunk<VEC>(row_ptr(a, m, row_ref(a, m, q0 + u)), base,
-                                                a.vocab, xv[u]);
+            if (q0 + u < nrows) load_row_chunk<VEC, MAP>(a, m, row_ref(a, m, q0 + u), base, xv[u]);
         if (q0 == 0) {
             if (tid < m.k) s_draft[tid] = dreg;
             __syncthreads();
@@ -1368,7 +1434,7 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
             if (!trunc && !topn) continue;
             const int kk = trunc ? m.topk_k : m.ntop;
             float x[kEpt];
-            load_chunk<VEC>(row_ptr(a, m, r), base, a.vocab, x);
+            load_row_chunk<VEC, MAP>(a, m, r, base, x);
             uint32_t key[kEpt];
 #pragma unroll
             for (int e = 0; e < kEpt; ++e) {
@@ -1460,7 +1526,9 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
     // a fused sampled sequence ends in a race (residual or bonus draw) that every chunk of
     // it joins: its finalize publishes the hand-off word, the race's last arriver clears it
     const bool race_here = a.fused && m.sampled && !m.topk;
-    if (last) finalize_sequence<false>(a, m, b, s_final, s_rinfo, s_draft, race_here ? &s_word : nullptr);
+    if (last)
+        finalize_sequence<false, MAP>(a, m, b, s_final, s_rinfo, s_draft,
+                                      race_here ? &s_word : nullptr);
     if (!race_here) return;
     // ---- fused race over this chunk: the sweep's counts and draft masks, L2-warm rows
     const int pos0 = a.positions[b];
@@ -1472,7 +1540,7 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
     if (kind != 0) {
         float xp[kEpt], xq[kEpt];
         load_chunk<VEC>(a.tl + (size_t)(m.r0 + ra) * a.vocab, base, a.vocab, xp);
-        if (kind == 1) load_chunk<VEC>(a.dl + (size_t)(m.d0 + ra) * a.vocab, base, a.vocab, xq);
+        if (kind == 1) load_draft_chunk<VEC, MAP>(a, m.d0 + ra, base, xq);
         else
 #pragma unroll
             for (int e = 0; e < kEpt; ++e) xq[e] = 0.f;
@@ -1540,6 +1608,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const SampArgs a, int 
 }
 
 // grid (B): merges the chunk statistics and runs the acceptance of one sequence.
+template <bool MAP>
 __global__ __launch_bounds__(kThreads) void finalize_kernel(const SampArgs a) {
     __shared__ FinalShared s_final;
     __shared__ RowInfo s_rinfo[3 * kMaxSeqRows];
@@ -1548,7 +1617,7 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(const SampArgs a) {
     uint32_t ebits = 0;
     const SeqMode m = seq_mode(a, b, &ebits);
     if (!m.valid) return;
-    finalize_sequence<true>(a, m, b, s_final, s_rinfo, nullptr, nullptr);
+    finalize_sequence<true, MAP>(a, m, b, s_final, s_rinfo, nullptr, nullptr);
 }
 
 }  // namespace
@@ -1589,22 +1658,52 @@ SampPlan plan_sample(int B, int total_rows, int V, int max_top_k, int max_top_lp
     return p;
 }
 
-// Workgroups of the lean sweep kernel that the device holds at once (cached per device).
-static int sweep_capacity(bool vec) {
-    static int cache[2][64];
+// Workgroups of the lean sweep kernel (the form launched: vector loads or not, reduced
+// draft vocabulary or not) that the device holds at once (cached per device).
+static int sweep_capacity(bool vec, bool map) {
+    static int cache[2][2][64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    int& c = cache[vec ? 1 : 0][dev];
+    int& c = cache[vec ? 1 : 0][map ? 1 : 0][dev];
     if (c == 0) {
         int per_cu = 0, cus = 0;
-        const void* k = vec ? reinterpret_cast<const void*>(&sweep_kernel<true, false>)
-                            : reinterpret_cast<const void*>(&sweep_kernel<false, false>);
+        const void* k =
+            map ? (vec ? reinterpret_cast<const void*>(&sweep_kernel<true, false, true>)
+                       : reinterpret_cast<const void*>(&sweep_kernel<false, false, true>))
+                : (vec ? reinterpret_cast<const void*>(&sweep_kernel<true, false, false>)
+                       : reinterpret_cast<const void*>(&sweep_kernel<false, false, false>));
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kThreads, 0) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             per_cu = cus = 0;
         c = per_cu * cus > 0 ? per_cu * cus : -1;
     }
     return c;
+}
+
+// Inverse of a reduced draft vocabulary's offset table: t2d[x] = the draft id j with
+// j + d2t[j] = x, or -1. Two launches in stream order: fill, then scatter (an entry outside
+// [0, V) is skipped; if two draft ids share a target id the higher one is kept).
+__global__ __launch_bounds__(256) void t2d_fill_kernel(int32_t* t2d, int vocab) {
+    const int i = blockIdx.x * kThreads + threadIdx.x;
+    if (i < vocab) t2d[i] = -1;
+}
+__global__ __launch_bounds__(256) void t2d_scatter_kernel(const int32_t* d2t, int dvocab,
+                                                          int vocab, int32_t* t2d) {
+    const int j = blockIdx.x * kThreads + threadIdx.x;
+    if (j >= dvocab) return;
+    const long x = (long)j + d2t[j];
+    if (x >= 0 && x < vocab) atomicMax(t2d + x, j);
+}
+
+hipError_t launch_draft_vocab_inverse(const int32_t* d2t, int dvocab, int vocab, int32_t* t2d,
+                                      hipStream_t stream) {
+    hipLaunchKernelGGL(t2d_fill_kernel, dim3((unsigned)((vocab + kThreads - 1) / kThreads)),
+                       dim3(kThreads), 0, stream, t2d, vocab);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(t2d_scatter_kernel, dim3((unsigned)((dvocab + kThreads - 1) / kThreads)),
+                       dim3(kThreads), 0, stream, d2t, dvocab, vocab, t2d);
+    return hipGetLastError();
 }
 
 hipError_t launch_sample(const SampArgs& args, hipStream_t stream) {
@@ -1617,14 +1716,17 @@ hipError_t launch_sample(const SampArgs& args, hipStream_t stream) {
     const bool topk = a.max_top_k > 0 || a.max_top_lp > 0;
     // Without them the sweep workgroups run the full-vocabulary race themselves, waiting
     // for their sequence's acceptance step, when the whole grid is resident at once.
-    a.fused = !topk && (long)a.batch * a.nchunk <= (long)sweep_capacity(vec);
-    if (vec) {
-        if (topk) hipLaunchKernelGGL((sweep_kernel<true, true>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((sweep_kernel<true, false>), grid, block, 0, stream, a);
+    const bool map = a.t2d != nullptr;
+    a.fused = !topk && (long)a.batch * a.nchunk <= (long)sweep_capacity(vec, map);
+#define VSA_SWEEP(V, T, M) hipLaunchKernelGGL((sweep_kernel<V, T, M>), grid, block, 0, stream, a)
+    if (map) {
+        if (vec) { if (topk) VSA_SWEEP(true, true, true); else VSA_SWEEP(true, false, true); }
+        else { if (topk) VSA_SWEEP(false, true, true); else VSA_SWEEP(false, false, true); }
     } else {
-        if (topk) hipLaunchKernelGGL((sweep_kernel<false, true>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((sweep_kernel<false, false>), grid, block, 0, stream, a);
+        if (vec) { if (topk) VSA_SWEEP(true, true, false); else VSA_SWEEP(true, false, false); }
+        else { if (topk) VSA_SWEEP(false, true, false); else VSA_SWEEP(false, false, false); }
     }
+#undef VSA_SWEEP
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (topk) {
@@ -1634,15 +1736,21 @@ hipError_t launch_sample(const SampArgs& args, hipStream_t stream) {
                            a, rows_cap);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)a.batch), block, 0, stream, a);
+        if (map) hipLaunchKernelGGL(finalize_kernel<true>, dim3((unsigned)a.batch), block, 0, stream, a);
+        else hipLaunchKernelGGL(finalize_kernel<false>, dim3((unsigned)a.batch), block, 0, stream, a);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (a.fused) return hipSuccess;
     // Only the device knows which sequences end in a full-vocabulary draw; every other
     // workgroup returns at once.
-    if (vec) hipLaunchKernelGGL(race_kernel<true>, grid, block, 0, stream, a);
-    else hipLaunchKernelGGL(race_kernel<false>, grid, block, 0, stream, a);
+    if (map) {
+        if (vec) hipLaunchKernelGGL((race_kernel<true, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((race_kernel<false, true>), grid, block, 0, stream, a);
+    } else {
+        if (vec) hipLaunchKernelGGL((race_kernel<true, false>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((race_kernel<false, false>), grid, block, 0, stream, a);
+    }
     return hipGetLastError();
 }
 

@@ -252,7 +252,7 @@ struct RaceReq {       // a categorical draw over the whole vocabulary, done by 
 
 struct SampArgs {
     const float* tl;               // target logits [T, V]
-    const float* dl;               // draft logits [T - B, V] or null
+    const float* dl;               // draft logits [T - B, dvocab] or null
     const int32_t* drafts;         // [T - B]
     const int32_t* cu_rows;        // [B + 1]
     const int32_t* counts;         // [B, V] or null
@@ -279,6 +279,9 @@ struct SampArgs {
     float4* race_part;             // [B][nchunk][4] race winners per (chunk, wave)
     uint32_t* race_flag;           // [B] race request published (zero between calls)
     int fused;                     // the sweep workgroups run the race themselves
+    // reduced draft vocabulary (after the rest, so the common fields keep their offsets)
+    const int32_t* t2d;            // [V] draft id of each target id (-1: none) or null
+    int dvocab;                    // draft vocabulary (V unless t2d is given)
 };
 
 // Every kernel argument in one round of scalar loads: the compiler otherwise spreads them
@@ -303,5 +306,7 @@ struct SampPlan {
 
 SampPlan plan_sample(int B, int total_rows, int V, int max_top_k, int max_top_lp);
 hipError_t launch_sample(const SampArgs& a, hipStream_t stream);
+hipError_t launch_draft_vocab_inverse(const int32_t* d2t, int dvocab, int vocab, int32_t* t2d,
+                                      hipStream_t stream);
 
 }  // namespace vsa
