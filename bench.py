@@ -20,6 +20,13 @@ group of 64 dimensions with fp16 scale and bias) through verify_attention_kvq; t
 target vocabulary and its offset table, as EAGLE-3-style heads ship): draft logits are
 [rows, N] and verify_sample_accept_reduced_draft reads them through the inverse table.
 
+    python bench.py --verify-matmul [--rows M] [--weight-bits 4|8]
+
+times small_m_qmm instead: the four weight matmuls of one 27B-class decoder layer (hidden
+5120, 64 q / 8 kv heads of 128, MLP 25600: qkv 10240x5120, o 5120x8192, gate+up 51200x5120,
+down 5120x25600) on M verify rows, with synthetic quantized weights (random codes, scale
+and bias) resident in HBM; one JSON line, value = layers per second.
+
     python bench.py --drafter-block [--window W] [--bidirectional] [--sliding]
 
 times block_attention alone on a drafter's block instead: B=4 blocks of 8 rows over a
@@ -231,6 +238,115 @@ def drafter_block_main(args):
     print(json.dumps(line), flush=True)
 
 
+LAYER_27B = (("qkv", 10240, 5120), ("o", 5120, 8192), ("gate_up", 51200, 5120),
+             ("down", 5120, 25600))
+
+
+def verify_matmul_main(args):
+    """small_m_qmm over one 27B-class layer's projections; HIP-event timing of graph replays
+    rotating over weight sets (more than the 256 MB last-level cache); the oracle timed on a
+    sample of output features as the CPU baseline."""
+    import torch
+    import verify_step_attention_amd as vsa
+    bits, m = args.weight_bits, args.rows
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1234)
+    layer_bytes = sum(n * k * bits // 8 + n * (k // 64) * 4 for _, n, k in LAYER_27B)
+    nsets = max(2, -(-(1 << 30) // layer_bytes))           # > 1 GB of distinct weights
+    print(f"[bench] {nsets} weight sets of {layer_bytes / 1e6:.1f} MB", file=sys.stderr,
+          flush=True)
+    sets = []
+    for _ in range(nsets):
+        mats = []
+        for name, n, k in LAYER_27B:
+            codes = torch.randint(0, 256, (n, k * bits // 8), dtype=torch.uint8, device="cuda",
+                                  generator=gen)
+            sb = torch.empty((n, k // 64, 2), dtype=torch.float16, device="cuda")
+            sb[..., 0].uniform_(1e-4, 2e-3, generator=gen)
+            sb[..., 1].uniform_(-0.2, 0.0, generator=gen)
+            mats.append((codes, sb))
+        sets.append(mats)
+    xs = {k: torch.randn((m, k), dtype=torch.float32, device="cuda", generator=gen).to(
+        torch.bfloat16) for k in {k for _, _, k in LAYER_27B}}
+    ys = [torch.empty((m, n), dtype=torch.float32, device="cuda") for _, n, _ in LAYER_27B]
+    wss = [torch.zeros(vsa.small_m_qmm_workspace_size(m, n, k), dtype=torch.uint8,
+                       device="cuda") for _, n, k in LAYER_27B]
+
+    def layer(mats, s):
+        for i, (name, n, k) in enumerate(LAYER_27B):
+            vsa.small_m_qmm(xs[k], mats[i][0], mats[i][1], bits, ys[i], wss[i], stream=s)
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        layer(sets[i % nsets], stream)
+    torch.cuda.synchronize()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(stream)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cs):
+        with torch.cuda.graph(g, stream=cs):
+            for mats in sets:
+                layer(mats, torch.cuda.current_stream())
+    stream.wait_stream(cs)
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, args.steps // nsets)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * nsets)
+    nbytes = layer_bytes + sum(m * k * 2 + m * n * 4 for _, n, k in LAYER_27B)
+    achieved = nbytes / (us * 1e-6) / 1e9
+    line = {
+        "metric": f"verify matmul layers/sec + achieved HBM GB/s, 27B-class layer, {m} rows, "
+                  f"{bits}-bit weights",
+        "value": round(1e6 / us, 1), "unit": "layers/s", "n_gpus": 1,
+        "steps": reps * nsets, "warmup": args.warmup, "ms_per_step": round(us / 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": f"bf16 x, u{bits} weight codes", "data": "synthetic",
+        "launch": "hip_graph_replay",
+        "config": {"workload": "layer27b_small_m_qmm", "rows": m, "weight_bits": bits,
+                   "matmuls": [f"{name} {n}x{k}" for name, n, k in LAYER_27B],
+                   "weight_sets": nsets, "layer_us": round(us, 2),
+                   "algorithmic_bytes_per_layer": nbytes},
+        "roofline": {"bound": "hbm", "kernel": f"small_m_qmm x4 (qmm_kernel<{bits}> + "
+                     "qmm_reduce_kernel)", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": nbytes},
+    }
+    if not args.no_cpu_baseline:
+        from oracle.qmm import small_m_qmm
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        except Exception:
+            cores = 1
+        # a bounded sample: 256 output features of each projection, whole input width
+        feats, t0, done = 256, time.perf_counter(), 0
+        mats = sets[0]
+        while True:
+            for i, (name, n, k) in enumerate(LAYER_27B):
+                small_m_qmm(xs[k].float().cpu().numpy(), mats[i][0][:feats].cpu().numpy(),
+                            mats[i][1][:feats].cpu().numpy(), bits)
+            done += 1
+            if time.perf_counter() - t0 >= 10.0:
+                break
+        dt = time.perf_counter() - t0
+        frac = feats * len(LAYER_27B) / sum(n for _, n, _ in LAYER_27B)
+        per_layer = dt / done / (sum(feats * k for _, n, k in LAYER_27B) /
+                                 sum(n * k for _, n, k in LAYER_27B))
+        line["cpu_baseline"] = {"value": round(1.0 / per_layer, 4), "unit": "layers/s",
+                                "cores": cores, "kind": "oracle",
+                                "sample": f"{done} pass(es) over 256 output features of each "
+                                          f"projection ({frac:.4f} of the layer's features, "
+                                          f"weighted by input width), {dt:.1f} s on the host, "
+                                          "scaled to whole layers"}
+    print(json.dumps(line), flush=True)
+
+
 def _counter_rows(d, counter):
     """Per-kernel values of one rocprofv3 --pmc counter (KiB per dispatch) under folder d."""
     import csv
@@ -317,6 +433,10 @@ def main():
                     help="K/V cache: bf16 (16) or affine codes of 8 or 4 bits")
     ap.add_argument("--draft-vocab", type=int, default=0,
                     help="reduced draft vocabulary size (0: drafts over the whole vocabulary)")
+    ap.add_argument("--verify-matmul", action="store_true",
+                    help="time small_m_qmm on a 27B-class layer instead of the step")
+    ap.add_argument("--rows", type=int, default=8)
+    ap.add_argument("--weight-bits", type=int, default=4, choices=(4, 8))
     ap.add_argument("--drafter-block", action="store_true",
                     help="time block_attention on a drafter's block instead of the step")
     ap.add_argument("--window", type=int, default=4096)
@@ -335,6 +455,9 @@ def main():
         sys.exit(2)
     if args.drafter_block:
         drafter_block_main(args)
+        return
+    if args.verify_matmul:
+        verify_matmul_main(args)
         return
 
     import torch

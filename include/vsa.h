@@ -308,6 +308,33 @@ vsa_status verify_sample_accept_reduced_draft(
     int32_t* top_lp_ids, float* diag_threshold, int32_t* diag_kept, void* workspace,
     size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------------------
+ * small_m_qmm
+ *
+ * The few-row quantized matmul of the verify forward (Changelog [0.20.0] "Changed": a
+ * small-M verify matmul for verify widths up to 16, the weights as the matrix operand
+ * shared by every row; [0.12.0] "Changed": 4-bit and 8-bit weights in groups of 64):
+ *     y[m][n] = sum_k x[m][k] * (scale[n][k / 64] * code[n][k] + bias[n][k / 64])
+ * with fp32 accumulation of exact products (codes and x enter the matrix units exactly).
+ *
+ *   x          [M, K] bf16 (16-byte aligned)
+ *   codes      [N, K * bits / 8] uint8 (16-byte aligned); 4 bits: element 2i in the low
+ *              nibble of byte i
+ *   sb         [N, K / 64, 2] fp16 (scale, bias)
+ *   bits       8 or 4
+ *   M, N, K    1 <= M <= 16; K a multiple of 64 (else VSA_ERR_UNSUPPORTED)
+ *   y          [M, N] float32 (16-byte aligned when N % 4 == 0), fully written
+ *   workspace  small_m_qmm_workspace_size(M, N, K) bytes, 256-byte aligned: partial sums
+ *              of the input splits (no state kept between calls)
+ * The inputs are split over workgroups for parallelism and the partials summed in a fixed
+ * order, so the result is bitwise reproducible.
+ * ------------------------------------------------------------------------------------ */
+size_t small_m_qmm_workspace_size(int M, int N, int K);
+
+vsa_status small_m_qmm(const void* x, const uint8_t* codes, const void* sb, int bits, int M,
+                       int N, int K, float* y, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -165,3 +165,19 @@ def test_reduced_draft_host_checks(lib):
     assert lib.draft_vocab_inverse(None, 10, 100, FAKE * 256, None) == INVALID_ARG
     assert lib.draft_vocab_inverse(FAKE, 101, 100, FAKE * 256, None) == INVALID_ARG
     assert lib.draft_vocab_inverse(FAKE, 10, 100, FAKE * 256 + 8, None) == INVALID_ARG
+
+
+def test_small_m_qmm_host_checks(lib):
+    assert lib.small_m_qmm_workspace_size(17, 1024, 4096) == 0     # more than 16 rows
+    assert lib.small_m_qmm_workspace_size(8, 1024, 100) == 0       # K not a multiple of 64
+    assert lib.small_m_qmm_workspace_size(8, 1024, 4096) > 0
+    call = lambda **kw: lib.small_m_qmm(kw.get("x", FAKE * 256), FAKE * 256, FAKE * 256,
+                                        kw.get("bits", 4), kw.get("M", 8), 1024,
+                                        kw.get("K", 4096), FAKE * 256, kw.get("ws", FAKE * 256),
+                                        kw.get("ws_bytes", 1 << 30), None)
+    assert call(x=None) == INVALID_ARG
+    assert call(bits=6) == INVALID_ARG
+    assert call(x=FAKE * 256 + 2) == INVALID_ARG                    # x not 16-byte aligned
+    assert call(M=17) == UNSUPPORTED
+    assert call(K=4000) == UNSUPPORTED
+    assert call(ws=None) == WORKSPACE                               # splits need partials

@@ -36,7 +36,8 @@ ROW_PARAMS_DTYPE = np.dtype([("temperature", "<f4"), ("top_k", "<i4"), ("top_p",
 EXPORTED_SYMBOLS = ("vsa_version", "vsa_status_string", "verify_attention_workspace_size",
                     "verify_attention", "block_attention", "verify_attention_kvq",
                     "verify_sample_accept_workspace_size", "verify_sample_accept",
-                    "draft_vocab_inverse", "verify_sample_accept_reduced_draft")
+                    "draft_vocab_inverse", "verify_sample_accept_reduced_draft",
+                    "small_m_qmm_workspace_size", "small_m_qmm")
 
 
 class VsaError(RuntimeError):
@@ -92,6 +93,11 @@ def _lib():
             c_void, c_void, c_int, c_void, c_void, c_void, c_void, c_void, c_void,
             ctypes.c_uint64, c_int, c_int, c_int, c_int, c_int, c_int, c_void, c_void, c_void,
             c_void, c_void, c_void, c_void, c_void, c_size, c_void]
+        lib.small_m_qmm_workspace_size.restype = c_size
+        lib.small_m_qmm_workspace_size.argtypes = [c_int, c_int, c_int]
+        lib.small_m_qmm.restype = c_int
+        lib.small_m_qmm.argtypes = [c_void, c_void, c_void, c_int, c_int, c_int, c_int, c_void,
+                                    c_void, c_size, c_void]
         _lib_handle = lib
     return _lib_handle
 
@@ -283,3 +289,29 @@ def verify_sample_accept_reduced_draft(target_logits, draft_logits, t2d, draft_t
         _ptr(diag_threshold), _ptr(diag_kept), _ptr(workspace), workspace.numel(),
         _stream(stream))
     _check(st, "verify_sample_accept_reduced_draft")
+
+
+# ----------------------------------------------------------------------------- verify matmul
+def small_m_qmm_workspace_size(M, N, K):
+    return int(_lib().small_m_qmm_workspace_size(int(M), int(N), int(K)))
+
+
+def small_m_qmm(x, codes, sb, bits, y, workspace, stream=None):
+    """y [M, N] float32 = x [M, K] bf16 times the quantized weights' transpose: codes
+    [N, K * bits / 8] uint8, sb [N, K / 64, 2] float16 (scale, bias), bits 8 or 4; M <= 16.
+    workspace: uint8 device tensor of small_m_qmm_workspace_size(M, N, K) bytes."""
+    import torch
+    m, k = x.shape
+    n = codes.shape[0]
+    if x.dtype != torch.bfloat16 or y.dtype != torch.float32 or codes.dtype != torch.uint8 \
+            or sb.dtype != torch.float16:
+        raise ValueError("x bf16, codes uint8, sb float16, y float32")
+    if tuple(codes.shape) != (n, k * bits // 8) or tuple(sb.shape) != (n, k // 64, 2) or \
+            tuple(y.shape) != (m, n):
+        raise ValueError("shapes disagree")
+    for t in (x, codes, sb, y, workspace):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    st = _lib().small_m_qmm(_ptr(x), _ptr(codes), _ptr(sb), int(bits), m, n, k, _ptr(y),
+                            _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "small_m_qmm")

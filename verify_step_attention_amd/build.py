@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libvsa.so")
-SOURCES = ["api.hip", "attention.hip", "sample_accept.hip"]
+SOURCES = ["api.hip", "attention.hip", "sample_accept.hip", "qmm.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -280,4 +280,43 @@ vsa_status verify_sample_accept_reduced_draft(
     return VSA_OK;
 }
 
+size_t small_m_qmm_workspace_size(int M, int N, int K) {
+    if (M < 1 || M > 16 || N < 1 || K < 64 || K % 64 != 0) return 0;
+    const QmmPlan p = plan_qmm(M, N, K);
+    return p.bytes > 0 ? p.bytes : 256;
+}
+
+vsa_status small_m_qmm(const void* x, const uint8_t* codes, const void* sb, int bits, int M,
+                       int N, int K, float* y, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+    if (!x || !codes || !sb || !y) return VSA_ERR_INVALID_ARG;
+    if (bits != 8 && bits != 4) return VSA_ERR_INVALID_ARG;
+    if (M < 1 || N < 1 || K < 1) return VSA_ERR_INVALID_ARG;
+    if (M > 16 || K % 64 != 0) return VSA_ERR_UNSUPPORTED;
+    const uintptr_t ax = reinterpret_cast<uintptr_t>(x), ac = reinterpret_cast<uintptr_t>(codes);
+    const uintptr_t as = reinterpret_cast<uintptr_t>(sb), ay = reinterpret_cast<uintptr_t>(y);
+    if ((ax & 15u) || (ac & 15u) || (as & 3u) || (ay & ((N % 4) == 0 ? 15u : 3u)))
+        return VSA_ERR_INVALID_ARG;
+    const QmmPlan plan = plan_qmm(M, N, K);
+    if (plan.bytes > 0 && (!workspace || !aligned256(workspace) || workspace_bytes < plan.bytes))
+        return VSA_ERR_WORKSPACE;
+    QmmArgs a{};
+    a.x = static_cast<const uint16_t*>(x);
+    a.codes = codes;
+    a.sb = sb;
+    a.y = y;
+    a.part = plan.bytes > 0 ? static_cast<float*>(workspace) : nullptr;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.bits = bits;
+    a.rowbytes = K * bits / 8;
+    a.sbrow = K / 64;
+    a.nsplit = plan.nsplit;
+    a.ksplit = plan.ksplit;
+    a.tiles = plan.tiles;
+    if (launch_qmm(a, static_cast<hipStream_t>(stream)) != hipSuccess) return VSA_ERR_LAUNCH;
+    return VSA_OK;
+}
+
 }  // extern "C"

@@ -217,6 +217,22 @@ AttnPlan plan_attention(int B, int Hq, int Hkv, int D, int max_rows, int max_kv_
 hipError_t launch_attention(const AttnArgs& a, const AttnPlan& p, vsa_dtype dtype,
                             hipStream_t stream);
 
+// ---------------------------------------------------------------- few-row quantized matmul
+struct QmmArgs {
+    const uint16_t* x;      // [M, K] bf16
+    const uint8_t* codes;   // [N, rowbytes]
+    const void* sb;         // [N, sbrow] fp16 (scale, bias) pairs
+    float* y;               // [M, N]
+    float* part;            // [nsplit, M, N] partials (nsplit > 1)
+    int M, N, K, bits, rowbytes, sbrow, nsplit, ksplit, tiles;
+};
+struct QmmPlan {
+    int tiles, nsplit, ksplit;
+    size_t bytes;           // workspace (partials), 0 with one split
+};
+QmmPlan plan_qmm(int M, int N, int K);
+hipError_t launch_qmm(const QmmArgs& a, hipStream_t stream);
+
 // ---------------------------------------------------------------- vocabulary stage
 constexpr int kChunk = 2048;         // vocabulary ids per workgroup chunk (8 per thread)
 constexpr int kMaxChunks = 256;      // chunks per row (vocabulary <= kMaxChunks * kChunk)
