@@ -275,7 +275,6 @@ vsa_status verify_sample_accept_reduced_draft(
     a.keep = reinterpret_cast<KeepEntry*>(ws + plan.off_keep);
     a.race = reinterpret_cast<RaceReq*>(ws + plan.off_race);
     a.race_part = reinterpret_cast<float4*>(ws + plan.off_race_part);
-    a.race_flag = reinterpret_cast<uint32_t*>(ws + plan.off_race_flag);
     if (launch_sample(a, static_cast<hipStream_t>(stream)) != hipSuccess) return VSA_ERR_LAUNCH;
     return VSA_OK;
 }

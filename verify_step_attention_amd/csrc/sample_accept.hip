@@ -836,7 +836,7 @@ __device__ void select_row(const SampArgs& a, const SeqMode& m, int q, FinalShar
 // (max, normalizer) of a softmax row from its per-chunk (max, sum) entries, one wave: lane
 // holds entries lane, lane + 64, ... Every caller uses this same order of operations, so
 // every workgroup that merges a row gets the same bits.
-__device__ __forceinline__ void merge_row_wave(const float4 (&st)[kChunkLoads], float cs,
+__device__ __forceinline__ void merge_row_wave(const float2 (&st)[kChunkLoads], float cs,
                                                float* m_out, double* z_out) {
     float bm = kNegInf;
 #pragma unroll
@@ -854,20 +854,7 @@ __device__ __forceinline__ void merge_row_wave(const float4 (&st)[kChunkLoads], 
     *z_out = z;
 }
 
-// A row's merged (max, normalizer) in its RowInfo slot, as hand-off words (fused race).
-__device__ __forceinline__ void publish_row_mz(RowInfo* ri, float m, double z) {
-    float2* w = reinterpret_cast<float2*>(ri);           // word 0: z, word 1: (m, argmax)
-    handoff_store(w, __builtin_bit_cast(float2, z));
-    handoff_store(w + 1, make_float2(m, 0.f));
-}
-__device__ __forceinline__ void read_row_mz(const RowInfo* ri, float* m, double* z) {
-    const float2* w = reinterpret_cast<const float2*>(ri);
-    const float2 w0 = handoff_load(w), w1 = handoff_load(w + 1);
-    *z = __builtin_bit_cast(double, w0);
-    *m = w1.x;
-}
-
-// Fused race hand-off word of a sequence: 0 = not yet; else 1 | kind << 1 | accepted << 8.
+// Fused race word of a sequence (in LDS): 1 | kind << 1 | accepted << 8.
 __device__ __forceinline__ uint32_t race_word(int kind, int acc) {
     return 1u | ((uint32_t)kind << 1) | ((uint32_t)acc << 8);
 }
@@ -876,8 +863,9 @@ template <bool AFTER_SELECT, bool MAP>
 __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, FinalShared& fs,
                                   RowInfo* rinfo /* LDS, one per row of the list */,
                                   const int* drafts_lds /* the K draft ids in LDS, or null */,
-                                  uint32_t* word_lds /* fused race: its hand-off word in LDS,
-                                                        or null */) {
+                                  uint32_t* word_lds /* fused race: the draw's word in LDS,
+                                                        or null */,
+                                  bool emit /* write the sequence's outputs */) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nrows = seq_nrows(m);
     uint32_t ebits = 0;
@@ -900,20 +888,24 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
 
     // ---- A: merge the chunk statistics of every row. One wave per row, rows q = wave,
     //      wave + 4, ...; the (<= kMaxChunks) chunk entries of up to 3 rows per wave are
-    //      loaded in one round (up to kChunkLoads per lane per row).
+    //      loaded in one round (up to kChunkLoads per lane per row), only the half of each
+    //      entry the row uses: (max, sum) of a softmax row, (value, id) of a greedy row.
     for (int q0 = wave; q0 < nrows; q0 += 12) {
-        float4 st[3][kChunkLoads];
+        float2 st[3][kChunkLoads];
 #pragma unroll
         for (int x = 0; x < 3; ++x) {
             const int q = q0 + 4 * x;
-            const int slot = q < nrows ? row_ref(a, m, q).slot : 0;
+            const RowRef rr = row_ref(a, m, q < nrows ? q : 0);
+            const int half = rr.kind == 0 && !m.sampled ? 1 : 0;
 #pragma unroll
             for (int u = 0; u < kChunkLoads; ++u) {
                 const int c = lane + 64 * u;
-                const float4* src = a.stats + (size_t)slot * a.nchunk + c;
+                const float2* src =
+                    reinterpret_cast<const float2*>(a.stats + (size_t)rr.slot * a.nchunk + c) +
+                    half;
                 st[x][u] = (q < nrows && c < a.nchunk)
-                               ? (AFTER_SELECT ? *src : handoff_load4(src))
-                               : make_float4(kNegInf, 0.f, kNegInf, __int_as_float(kBigIdx));
+                               ? (AFTER_SELECT ? *src : handoff_load(src))
+                               : make_float2(kNegInf, __int_as_float(kBigIdx));
             }
         }
 #pragma unroll
@@ -928,8 +920,8 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
             if (greedy_row) {
 #pragma unroll
                 for (int u = 0; u < kChunkLoads; ++u) {
-                    const int ci = __float_as_int(st[x][u].w);
-                    if (better(st[x][u].z, ci, bv, bi)) { bv = st[x][u].z; bi = ci; }
+                    const int ci = __float_as_int(st[x][u].y);
+                    if (better(st[x][u].x, ci, bv, bi)) { bv = st[x][u].x; bi = ci; }
                 }
                 wave_argmax(bv, bi);
             } else {
@@ -944,7 +936,6 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
                 ri.kept_k = a.vocab;
                 ri.kept_p = a.vocab;
                 rinfo[q] = ri;
-                if (word_lds && !greedy_row) publish_row_mz(a.rows + r.slot, bm, z);
             }
         }
     }
@@ -1063,25 +1054,15 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
             }
         }
     }
-    if (word_lds) {
-        // every wave's published row statistics have landed before the hand-off word
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+    if (wave == 0 && lane == 0) {
+        // fused race: the draw this workgroup joins (every workgroup of the sequence decides
+        // the same); otherwise the request for race_kernel
+        if (word_lds) *word_lds = race_word(pending ? rq.kind : 0, acc);
+        else if (emit) a.race[b] = rq;
+        if (emit) a.accepted[b] = acc;
     }
+    if (!emit) return;
     if (wave == 0) {
-        if (lane == 0) {
-            if (word_lds) {
-                // fused race: the sequence's other workgroups wait for this word, then read
-                // the published statistics of the rows it names
-                const uint32_t wd = race_word(pending ? rq.kind : 0, acc);
-                __hip_atomic_store(a.race_flag + b, wd, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-                *word_lds = wd;
-            } else {
-                a.race[b] = rq;
-            }
-            a.accepted[b] = acc;
-        }
         // emitted tokens, logprobs, diagnostics. The token and logprob of a pending draw
         // are the race's to write: no address gets plain stores from two workgroups of one
         // kernel (their L2 write-backs could land in either order).
@@ -1215,23 +1196,21 @@ __device__ int race_winner(const SampArgs& a, int b, int lane) {
     return tok;
 }
 
-// Fused race: thread 0 waits for the hand-off word that the sequence's last sweep
-// workgroup publishes. The sweep grid is launched fused only when all of its workgroups
-// fit on the GPU at once, so the publisher always runs; the wait still gives up after
-// kWaitTicks of the 100 MHz clock (error bit; the workgroup then joins with no winner).
+// Fused race: thread 0 waits until all `total` workgroups of the sequence have counted in.
+// The sweep grid is launched fused only when all of its workgroups fit on the GPU at once,
+// so every one of them arrives; the wait still gives up after kWaitTicks of the 100 MHz
+// clock (error bit; the workgroup then goes on with what it reads).
 constexpr uint64_t kWaitTicks = 20000000ull;              // 0.2 s
-__device__ uint32_t wait_race_word(const SampArgs& a, int b) {
+__device__ void wait_arrivals(const SampArgs& a, const uint32_t* counter, uint32_t total) {
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    uint32_t w;
-    while (((w = __hip_atomic_load(a.race_flag + b, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT)) & 1u) == 0u) {
+    while (__hip_atomic_load(const_cast<uint32_t*>(counter), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT) < total) {
         if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
             atomicOr(a.err, VSA_DEVERR_WAIT_TIMEOUT);
-            return 0u;
+            return;
         }
         __builtin_amdgcn_s_sleep(4);
     }
-    return w;
 }
 
 // Separate race kernel (top-k pipeline, or a sweep grid too large to be resident at once).
@@ -1262,7 +1241,7 @@ __global__ __launch_bounds__(kThreads) void race_kernel(const SampArgs a) {
     draft_masks(s_draft, rq.a, base, dm);
     const float4 part = race_chunk(a, m, rq, b, c, cnt, dm, xp, xq);
     if ((tid & 63) == 0) handoff_store4(a.race_part + ((size_t)b * a.nchunk + c) * 4 + (tid >> 6), part);
-    if (!handoff_arrive(a.cnt_race + b, (uint32_t)a.nchunk, &s_last) || tid >= 64) return;
+    if (!handoff_arrive(a.cnt_race + b * kCtrStride, (uint32_t)a.nchunk, &s_last) || tid >= 64) return;
     const int tok = race_winner(a, b, tid);
     if (tid != 0) return;
     const int grow = m.r0 + rq.a;
@@ -1520,20 +1499,24 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
     if (TOPK) return;                              // select_kernel and finalize_kernel follow
     __shared__ int s_last;
     __shared__ uint32_t s_word;
-    __shared__ float s_mrow[2];
-    __shared__ double s_zrow[2];
-    const bool last = handoff_arrive(a.cnt_sweep + b, (uint32_t)a.nchunk, &s_last);
-    // a fused sampled sequence ends in a race (residual or bonus draw) that every chunk of
-    // it joins: its finalize publishes the hand-off word, the race's last arriver clears it
+    // A fused sampled sequence ends in a race (residual or bonus draw) that every chunk of it
+    // joins. Each of its workgroups waits until all of them have counted in, then merges
+    // the statistics and runs the acceptance itself: the same values in the same order, so
+    // every workgroup reaches the same decision, with no round trips to publish it. Only
+    // the last arriver writes the outputs; the race's last arriver clears both counters.
     const bool race_here = a.fused && m.sampled && !m.topk;
-    if (last)
-        finalize_sequence<false, MAP>(a, m, b, s_final, s_rinfo, s_draft,
-                                      race_here ? &s_word : nullptr);
+    const int pos0 = race_here ? a.positions[b] : 0;
+    const bool last = handoff_arrive(a.cnt_sweep + b * kCtrStride, (uint32_t)a.nchunk, &s_last, !race_here);
+    if (!race_here && !last) return;
+    if (race_here) {
+        if (!last && tid == 0) wait_arrivals(a, a.cnt_sweep + b * kCtrStride, (uint32_t)a.nchunk);
+        __syncthreads();
+    }
+    finalize_sequence<false, MAP>(a, m, b, s_final, s_rinfo, s_draft,
+                                  race_here ? &s_word : nullptr, last);
     if (!race_here) return;
-    // ---- fused race over this chunk: the sweep's counts and draft masks, L2-warm rows
-    const int pos0 = a.positions[b];
-    if (tid == 0 && !last) s_word = wait_race_word(a, b);
     __syncthreads();
+    // ---- race over this chunk: the sweep's counts and draft masks, L2-warm rows
     const uint32_t wd = s_word;
     const int kind = (int)((wd >> 1) & 3u), ra = (int)(wd >> 8);
     float4 part = race_none();
@@ -1544,25 +1527,16 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
         else
 #pragma unroll
             for (int e = 0; e < kEpt; ++e) xq[e] = 0.f;
-        // the finalize's (max, normalizer) of p's row (target row ra) and q's row (draft
-        // row ra + 1)
-        if (tid < (kind == 1 ? 2 : 1)) {
-            float mm;
-            double zz;
-            read_row_mz(a.rows + (tid == 0 ? m.r0 + ra : a.total_rows + m.d0 + ra), &mm, &zz);
-            s_mrow[tid] = mm;
-            s_zrow[tid] = zz;
-        }
-        __syncthreads();
+        // p is target row ra, q draft row ra + 1 (row list index m.rows + ra)
         RaceReq rq{};
         rq.kind = kind;
         rq.a = ra;
         rq.pos = pos0 + ra;
-        rq.m_p = s_mrow[0];
-        rq.z_p = s_zrow[0];
+        rq.m_p = s_rinfo[ra].m;
+        rq.z_p = s_rinfo[ra].z;
         if (kind == 1) {
-            rq.m_q = s_mrow[1];
-            rq.z_q = s_zrow[1];
+            rq.m_q = s_rinfo[m.rows + ra].m;
+            rq.z_q = s_rinfo[m.rows + ra].z;
         }
         uint32_t dmr[kEpt];
         const uint32_t lm = low_bits(ra);
@@ -1571,27 +1545,23 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
         part = race_chunk(a, m, rq, b, c, cnt, dmr, xp, xq);
     }
     if (lane == 0) handoff_store4(a.race_part + ((size_t)b * a.nchunk + c) * 4 + wave, part);
-    if (!handoff_arrive(a.cnt_race + b, (uint32_t)a.nchunk, &s_last) || tid >= 64) return;
-    // ---- the last chunk to arrive: the drawn token and its logprob
-    uint32_t w2 = wd;
-    if ((w2 & 1u) == 0u)                                  // this workgroup's wait gave up
-        w2 = __hip_atomic_load(a.race_flag + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int kind2 = (int)((w2 >> 1) & 3u), ra2 = (int)(w2 >> 8);
+    if (!handoff_arrive(a.cnt_race + b * kCtrStride, (uint32_t)a.nchunk, &s_last) || tid >= 64) return;
+    // ---- the last chunk to arrive: the drawn token and its logprob. Every workgroup of the
+    // sequence has passed its wait, so the sweep counter can go back to zero.
+    if (lane == 0)
+        __hip_atomic_store(a.cnt_sweep + b * kCtrStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int tok = race_winner(a, b, lane);
-    float lp = __builtin_nanf("");
-    if (kind2 != 0 && a.chosen_lp && m.logprobs && lane == 0) {
-        float mx;
-        double zx;
-        read_row_mz(a.rows + row_ref(a, m, m.rows + m.k + ra2).slot, &mx, &zx);
-        const int grow = m.r0 + ra2;
-        lp = (float)((double)a.tl[(size_t)grow * a.vocab + tok] - (double)mx - log(zx));
-    }
-    if (lane != 0) return;
-    __hip_atomic_store(a.race_flag + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (kind2 == 0) return;                               // the finalize emitted the token
-    const int grow = m.r0 + ra2;
+    if (lane != 0 || kind == 0) return;
+    const int grow = m.r0 + ra;
     a.out_tokens[grow] = tok;
-    if (a.chosen_lp) a.chosen_lp[grow] = lp;
+    if (a.chosen_lp) {
+        float lp = __builtin_nanf("");
+        if (m.logprobs) {                         // raw row ra (row list m.rows + K + ra)
+            const RowInfo& rx = s_rinfo[m.rows + m.k + ra];
+            lp = (float)((double)a.tl[(size_t)grow * a.vocab + tok] - (double)rx.m - log(rx.z));
+        }
+        a.chosen_lp[grow] = lp;
+    }
 }
 
 // ------------------------------------------------------------------ top-k pipeline kernels
@@ -1617,7 +1587,7 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(const SampArgs a) {
     uint32_t ebits = 0;
     const SeqMode m = seq_mode(a, b, &ebits);
     if (!m.valid) return;
-    finalize_sequence<true, MAP>(a, m, b, s_final, s_rinfo, nullptr, nullptr);
+    finalize_sequence<true, MAP>(a, m, b, s_final, s_rinfo, nullptr, nullptr, true);
 }
 
 }  // namespace
@@ -1635,9 +1605,9 @@ SampPlan plan_sample(int B, int total_rows, int V, int max_top_k, int max_top_lp
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     size_t off = 256;
     p.off_cnt_sweep = off;
-    off += up((size_t)B * 4);
+    off += up((size_t)B * 4 * kCtrStride);
     p.off_cnt_race = off;
-    off += up((size_t)B * 4);
+    off += up((size_t)B * 4 * kCtrStride);
     p.off_stats = off;
     off += up((size_t)p.slots * p.nchunk * 16);
     p.off_cand = off;
@@ -1652,8 +1622,6 @@ SampPlan plan_sample(int B, int total_rows, int V, int max_top_k, int max_top_lp
     off += up((size_t)B * sizeof(RaceReq));
     p.off_race_part = off;
     off += up((size_t)B * p.nchunk * 4 * 16);
-    p.off_race_flag = off;
-    off += up((size_t)B * 4);
     p.bytes = off;
     return p;
 }

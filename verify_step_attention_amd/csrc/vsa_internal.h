@@ -159,15 +159,17 @@ __device__ __forceinline__ float4 handoff_load4(const float4* p) {
 
 // Every thread's hand-off stores are complete before thread 0 counts the workgroup in;
 // returns true (in every thread) in the last of `total` workgroups to arrive, which also
-// resets the counter for the next call.
+// resets the counter for the next call unless `reset` is false (then whoever else reads
+// the count clears it).
 __device__ __forceinline__ bool handoff_arrive(uint32_t* counter, uint32_t total,
-                                               int* s_flag) {
+                                               int* s_flag, bool reset = true) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0) {
         const uint32_t prev = atomicAdd(counter, 1u);
         const bool last = prev == total - 1;
-        if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (last && reset)
+            __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         *s_flag = last;
     }
     __syncthreads();
@@ -239,6 +241,7 @@ constexpr int kMaxChunks = 256;      // chunks per row (vocabulary <= kMaxChunks
 constexpr int kChunkLoads = kMaxChunks / 64;   // per-lane loads when a wave reads a row's chunks
 constexpr int kKeep = 256;           // kept-set capacity of one truncated row
 constexpr int kMaxSeqRows = 32;      // verify rows per sequence (K <= 31)
+constexpr int kCtrStride = 64;       // uint32 between two sequences' arrival counters (256 B)
 
 // Merged statistics of one row (finalize results, also handed to the race kernel).
 struct RowInfo {
@@ -284,8 +287,8 @@ struct SampArgs {
     float* diag_thr;
     int32_t* diag_kept;
     uint32_t* err;
-    uint32_t* cnt_sweep;           // [B] arrival counters (zero between calls)
-    uint32_t* cnt_race;            // [B]
+    uint32_t* cnt_sweep;           // [B][kCtrStride] arrival counters (zero between calls)
+    uint32_t* cnt_race;            // [B][kCtrStride]
     float4* stats;                 // [slots][nchunk] (m, s, best value, best id bits)
     uint2* cand;                   // [slots][nchunk][capc] (ordered key, id)
     uint2* cand_meta;              // [slots][nchunk] (count, k-th key)
@@ -293,7 +296,6 @@ struct SampArgs {
     KeepEntry* keep;               // [2T - B][keepcap]
     RaceReq* race;                 // [B]
     float4* race_part;             // [B][nchunk][4] race winners per (chunk, wave)
-    uint32_t* race_flag;           // [B] race request published (zero between calls)
     int fused;                     // the sweep workgroups run the race themselves
     // reduced draft vocabulary (after the rest, so the common fields keep their offsets)
     const int32_t* t2d;            // [V] draft id of each target id (-1: none) or null
@@ -311,13 +313,13 @@ __device__ __forceinline__ void preload_args(const SampArgs& a) {
                  "s"(a.top_ids), "s"(a.diag_thr), "s"(a.diag_kept), "s"(a.err),
                  "s"(a.cnt_sweep), "s"(a.cnt_race), "s"(a.stats), "s"(a.cand),
                  "s"(a.cand_meta), "s"(a.rows), "s"(a.keep), "s"(a.race), "s"(a.race_part),
-                 "s"(a.race_flag), "s"(a.fused));
+                 "s"(a.fused));
 }
 
 struct SampPlan {
     int nchunk, capc, keepcap, slots;
     size_t off_cnt_sweep, off_cnt_race, off_stats, off_cand, off_meta, off_rows, off_keep,
-        off_race, off_race_part, off_race_flag, bytes;
+        off_race, off_race_part, bytes;
 };
 
 SampPlan plan_sample(int B, int total_rows, int V, int max_top_k, int max_top_lp);
