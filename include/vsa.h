@@ -32,10 +32,13 @@
  *     in and never cleared by the library; the caller reads (and may zero) it after the
  *     stream completes.
  *   - Workspace: caller-owned device memory of at least *_workspace_size() bytes, 256-byte
- *     aligned, ZERO-FILLED BEFORE ITS FIRST USE. It holds arrival counters that every call
- *     returns to zero, so one workspace serves any number of calls in stream order. Two
- *     calls that share a workspace must not run concurrently (different streams), and a
- *     workspace sized for one problem serves any problem whose size query is not larger.
+ *     aligned, ZERO-FILLED BEFORE ITS FIRST USE. Every workspace starts with the same header:
+ *     the error word (byte 0) and, from byte 256, a 64 KB region of counters that every call
+ *     returns to zero and no call uses for anything else (a call that needs more than 16384
+ *     counters keeps the rest in its own area and clears them first). So one workspace
+ *     serves any number of calls of any of these functions and shapes in stream order. Two calls that
+ *     share a workspace must not run concurrently (different streams), and a workspace
+ *     sized for one problem serves any problem whose size query is not larger.
  *   - No call keeps state between calls; the library is reentrant across workspaces.
  */
 #ifndef VSA_H

@@ -67,6 +67,9 @@ def test_attention_workspace_size_limits(lib):
                 (4, 64, 2, 128, 5, 8197),       # (Hq / Hkv) * R > 128
                 (0, 32, 8, 128, 5, 8197)]:      # no sequence
         assert lib.verify_attention_workspace_size(*bad) == 0, bad
+    # (sequence, KV head) units past the workspace's counter region add their own area
+    assert lib.verify_attention_workspace_size(2049, 32, 8, 128, 5, 64) >= \
+        lib.verify_attention_workspace_size(2048, 32, 8, 128, 5, 64) + 8 * 4
 
 
 def _attention(lib, *, q=FAKE, dtype=BF16, B=4, total=20, hq=32, hkv=8, d=128, s_max=8256,

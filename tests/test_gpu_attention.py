@@ -11,7 +11,8 @@ if not torch.cuda.is_available():
 
 import verify_step_attention_amd as vsa  # noqa: E402
 from verify_step_attention_amd import workloads as wl  # noqa: E402
-from gpu_helpers import attention_gpu, attention_oracle, assert_attention_close  # noqa: E402
+from gpu_helpers import (attention_gpu, attention_oracle, assert_attention_close,  # noqa: E402
+                         compare_sample, q_distributed_drafts, sample_gpu, sample_oracle)
 
 
 def _log(msg):
@@ -119,6 +120,77 @@ def test_dynamic_splits_reuse_workspace():
         y, err = attention_gpu(b, workspace=ws, flags=vsa.ATTN_DYNAMIC_SPLITS)
         assert err == 0
         assert_attention_close(y, ref_b)
+
+
+def test_shared_workspace_across_shapes_and_calls():
+    """One workspace serves calls of different shapes and different functions in stream
+    order: a call over more (sequence, KV head) units than the previous one must still find
+    its tile counters at zero, and a sampling call in between must not disturb them."""
+    _log("shared workspace: 8 units, 96 units, sampling, 8 units, 96 units")
+    small = wl.make_workload("qwen3_4b", ctx=300)                  # 8 units
+    big = wl.make_workload("batched", batch=12, ctx=(200, 700))    # 96 units
+    samp = wl.make_workload("batched", with_kv=False, vocab=8192)
+    samp.draft_tokens = q_distributed_drafts(samp)
+    sizes = [vsa.verify_attention_workspace_size(w.batch, w.num_q_heads, w.num_kv_heads,
+                                                 w.head_dim, w.max_rows, w.max_kv_len)
+             for w in (small, big)]
+    sizes.append(vsa.verify_sample_accept_workspace_size(samp.batch, samp.total_rows,
+                                                         samp.vocab, samp.max_rows, 0, 0))
+    ws = torch.zeros(max(sizes), dtype=torch.uint8, device="cuda")
+    ref_s, ref_b = attention_oracle(small), attention_oracle(big)
+    want = sample_oracle(samp, seed=0)
+    for rep in range(2):
+        x, err = attention_gpu(small, workspace=ws, flags=vsa.ATTN_DYNAMIC_SPLITS)
+        assert err == 0
+        assert_attention_close(x, ref_s)
+        y, err = attention_gpu(big, workspace=ws, flags=vsa.ATTN_DYNAMIC_SPLITS)
+        assert err == 0
+        assert_attention_close(y, ref_b)
+        got = sample_gpu(samp, seed=0, workspace=ws)
+        assert got["err"] == 0
+        compare_sample(samp, got, want)
+
+
+def test_units_past_the_counter_region():
+    """More (sequence, KV head) units than the workspace's counter region holds: the rest of
+    the tile counters live in the call's own area, cleared first; dynamic splits still cover
+    every key, twice in a row on one workspace."""
+    _log("attention: 2100 x 8 units, dynamic splits")
+    rng = np.random.default_rng(9)
+    batch, hkv, hq, d = 2100, 8, 8, 64
+    ctxs = rng.integers(0, 100, size=batch)
+    drafts = rng.integers(0, 3, size=batch)
+    w = _custom_small(hq, hkv, d, ctxs, drafts, rng)
+    ref = attention_oracle(w)
+    size = vsa.verify_attention_workspace_size(batch, hq, hkv, d, w.max_rows, w.max_kv_len)
+    ws = torch.zeros(size, dtype=torch.uint8, device="cuda")
+    for rep in range(2):
+        x, err = attention_gpu(w, workspace=ws, flags=vsa.ATTN_DYNAMIC_SPLITS)
+        assert err == 0
+        assert_attention_close(x, ref)
+
+
+def _custom_small(hq, hkv, d, ctxs, drafts, rng):
+    batch = len(ctxs)
+    rows = np.asarray(drafts) + 1
+    cu = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
+    kv_len = np.asarray(ctxs) + rows
+    s_max = int(-(-int(kv_len.max() + 8) // 64) * 64)
+    qf = rng.standard_normal((cu[-1], hq, d), dtype=np.float32)
+    kf = rng.standard_normal((batch, hkv, s_max, d), dtype=np.float32)
+    vf = rng.standard_normal((batch, hkv, s_max, d), dtype=np.float32)
+    for b in range(batch):
+        kf[b, :, kv_len[b]:] = np.nan
+        vf[b, :, kv_len[b]:] = np.nan
+    z = np.zeros((cu[-1], 4), np.float32)
+    return wl.Workload(name="custom", batch=batch, num_q_heads=hq, num_kv_heads=hkv,
+                       head_dim=d, dtype=wl.BF16, vocab=4,
+                       ctx_lens=np.asarray(ctxs, np.int32), cu_rows=cu, s_max=s_max,
+                       q=wl.bf16_bits(qf), k_cache=wl.bf16_bits(kf), v_cache=wl.bf16_bits(vf),
+                       target_logits=z, draft_logits=z[:cu[-1] - batch],
+                       draft_tokens=np.zeros(cu[-1] - batch, np.int32), token_counts=None,
+                       params=[wl.Params()] * batch,
+                       positions=np.asarray(ctxs, np.int32) + 1)
 
 
 def test_device_error_word_on_bad_context():

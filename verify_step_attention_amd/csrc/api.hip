@@ -14,7 +14,19 @@ constexpr int kMaxVocab = kMaxChunks * kChunk;
 
 bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
 
+__global__ __launch_bounds__(256) void zero_u32_kernel(uint32_t* p, size_t n) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
 }  // namespace
+
+// Clears counters past the workspace's counter region (calls with that many of them).
+hipError_t vsa::launch_zero_u32(uint32_t* p, size_t n, hipStream_t stream) {
+    hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                       p, n);
+    return hipGetLastError();
+}
 
 extern "C" {
 
@@ -91,7 +103,8 @@ vsa_status block_attention(const void* q, const void* k_cache, const void* v_cac
     a.out = out;
     a.part_o = reinterpret_cast<float*>(ws + plan.off_o);
     a.part_ml = reinterpret_cast<float2*>(ws + plan.off_ml);
-    a.tile_ctr = reinterpret_cast<uint32_t*>(ws + plan.off_ctr);
+    a.tile_ctr = reinterpret_cast<uint32_t*>(ws + kWsCounters);
+    a.tile_ctr_x = reinterpret_cast<uint32_t*>(ws + plan.off_ctr_x);
     a.err = reinterpret_cast<uint32_t*>(ws);
     a.batch = B;
     a.total_rows = total_rows;
@@ -111,6 +124,9 @@ vsa_status block_attention(const void* q, const void* k_cache, const void* v_cac
     a.window = window;
     a.mask = ((flags & VSA_ATTN_BIDIRECTIONAL) ? kMaskBidirectional : 0) |
              ((flags & VSA_ATTN_SLIDING_WINDOW) ? kMaskSliding : 0);
+    if (plan.n_ctr_x &&
+        launch_zero_u32(a.tile_ctr_x, plan.n_ctr_x, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return VSA_ERR_LAUNCH;
     if (launch_attention(a, plan, dtype, static_cast<hipStream_t>(stream)) != hipSuccess)
         return VSA_ERR_LAUNCH;
     return VSA_OK;
@@ -151,7 +167,8 @@ vsa_status verify_attention_kvq(const void* q, const uint8_t* k_codes, const voi
     a.out = out;
     a.part_o = reinterpret_cast<float*>(ws + plan.off_o);
     a.part_ml = reinterpret_cast<float2*>(ws + plan.off_ml);
-    a.tile_ctr = reinterpret_cast<uint32_t*>(ws + plan.off_ctr);
+    a.tile_ctr = reinterpret_cast<uint32_t*>(ws + kWsCounters);
+    a.tile_ctr_x = reinterpret_cast<uint32_t*>(ws + plan.off_ctr_x);
     a.err = reinterpret_cast<uint32_t*>(ws);
     a.batch = B;
     a.total_rows = total_rows;
@@ -168,6 +185,9 @@ vsa_status verify_attention_kvq(const void* q, const uint8_t* k_codes, const voi
     a.mcap = plan.mcap;
     const float sc = scale == 0.f ? 1.f / sqrtf((float)D) : scale;
     a.scale_log2 = sc * 1.4426950408889634f;
+    if (plan.n_ctr_x &&
+        launch_zero_u32(a.tile_ctr_x, plan.n_ctr_x, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return VSA_ERR_LAUNCH;
     if (launch_attention(a, plan, VSA_BF16, static_cast<hipStream_t>(stream)) != hipSuccess)
         return VSA_ERR_LAUNCH;
     return VSA_OK;
@@ -266,8 +286,8 @@ vsa_status verify_sample_accept_reduced_draft(
     a.diag_thr = diag_threshold;
     a.diag_kept = diag_kept;
     a.err = reinterpret_cast<uint32_t*>(ws);
-    a.cnt_sweep = reinterpret_cast<uint32_t*>(ws + plan.off_cnt_sweep);
-    a.cnt_race = reinterpret_cast<uint32_t*>(ws + plan.off_cnt_race);
+    a.ctr = reinterpret_cast<uint32_t*>(ws + kWsCounters);
+    a.ctr_x = reinterpret_cast<uint32_t*>(ws + plan.off_ctr_x);
     a.stats = reinterpret_cast<float4*>(ws + plan.off_stats);
     a.cand = reinterpret_cast<uint2*>(ws + plan.off_cand);
     a.cand_meta = reinterpret_cast<uint2*>(ws + plan.off_meta);
@@ -275,6 +295,9 @@ vsa_status verify_sample_accept_reduced_draft(
     a.keep = reinterpret_cast<KeepEntry*>(ws + plan.off_keep);
     a.race = reinterpret_cast<RaceReq*>(ws + plan.off_race);
     a.race_part = reinterpret_cast<float4*>(ws + plan.off_race_part);
+    if (plan.n_ctr_x &&
+        launch_zero_u32(a.ctr_x, plan.n_ctr_x, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return VSA_ERR_LAUNCH;
     if (launch_sample(a, static_cast<hipStream_t>(stream)) != hipSuccess) return VSA_ERR_LAUNCH;
     return VSA_OK;
 }
@@ -304,7 +327,8 @@ vsa_status small_m_qmm(const void* x, const uint8_t* codes, const void* sb, int 
     a.codes = codes;
     a.sb = sb;
     a.y = y;
-    a.part = plan.bytes > 0 ? static_cast<float*>(workspace) : nullptr;
+    a.part = plan.bytes > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + kWsHeader)
+                            : nullptr;
     a.M = M;
     a.N = N;
     a.K = K;

@@ -297,7 +297,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const AttnArgs a) {
     const int t_spec = first_tile(tile_count(kv_cap));
     key_lim = kv_cap;
     if (t_spec >= 0) issue_tile(t_spec, k0s, v0s);
-    uint32_t* const ctr = a.tile_ctr + unit;
+    uint32_t* const ctr = counter_at(a.tile_ctr, a.tile_ctr_x, unit);
     uint32_t claim = 0;                                // thread 0: the pending claim
     if (dyn && tid == 0) claim = atomicAdd(ctr, 1u);
     __shared__ int s_next[2];
@@ -734,7 +734,7 @@ __global__ __launch_bounds__(256, 1) void attn_kvq_kernel(const AttnArgs a) {
     const int t_spec = first_tile(tile_count(kv_cap));
     key_lim = kv_cap;
     if (t_spec >= 0) issue_tile(t_spec, k0s, v0s);
-    uint32_t* const ctr = a.tile_ctr + unit;
+    uint32_t* const ctr = counter_at(a.tile_ctr, a.tile_ctr_x, unit);
     uint32_t claim = 0;
     if (dyn && tid == 0) claim = atomicAdd(ctr, 1u);
 
@@ -1230,7 +1230,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const AttnArgs a) {
     const int e = (blockIdx.x % chunks) * kThreads + threadIdx.x;
     if (unit >= a.units) return;
     // the attention kernel has finished: its tile counter returns to zero for the next call
-    if (a.dyn && e == 0) __hip_atomic_store(a.tile_ctr + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (a.dyn && e == 0) __hip_atomic_store(counter_at(a.tile_ctr, a.tile_ctr_x, unit), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (e >= a.mcap * D4) return;
     const int b = unit / a.hkv, g = unit % a.hkv;
     const int n = e / D4, d4 = e % D4;
@@ -1296,9 +1296,10 @@ AttnPlan plan_attention(int B, int Hq, int Hkv, int D, int max_rows, int max_kv_
     if (nsplit > kMaxSplits) nsplit = kMaxSplits;
     if (nsplit < 1) nsplit = 1;
     p.nsplit = nsplit;
-    size_t off = 256;                                            // error word + pad
-    p.off_ctr = off;
-    off += ((size_t)p.units * 4 + 255) / 256 * 256;
+    size_t off = kWsHeader;                                      // error word, counters
+    p.n_ctr_x = extra_counters(p.units);
+    p.off_ctr_x = off;
+    off += (p.n_ctr_x * 4 + 255) / 256 * 256;
     p.off_ml = off;
     off += ((size_t)p.units * nsplit * p.mcap * 8 + 255) / 256 * 256;
     p.off_o = off;

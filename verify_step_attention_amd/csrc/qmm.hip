@@ -268,8 +268,9 @@ QmmPlan plan_qmm(int M, int N, int K) {
     const int gps = (groups + nsplit - 1) / nsplit;          // groups per split
     p.ksplit = gps * 64;
     p.nsplit = (groups + gps - 1) / gps;
-    p.bytes = p.nsplit > 1 ? (size_t)p.nsplit * M * N * 4 : 0;
-    p.bytes = (p.bytes + 255) / 256 * 256;
+    // partial sums after the common workspace header (error word and counters), so the
+    // workspace may be shared with the other calls
+    p.bytes = p.nsplit > 1 ? kWsHeader + ((size_t)p.nsplit * M * N * 4 + 255) / 256 * 256 : 0;
     return p;
 }
 

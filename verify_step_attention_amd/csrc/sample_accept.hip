@@ -1241,7 +1241,7 @@ __global__ __launch_bounds__(kThreads) void race_kernel(const SampArgs a) {
     draft_masks(s_draft, rq.a, base, dm);
     const float4 part = race_chunk(a, m, rq, b, c, cnt, dm, xp, xq);
     if ((tid & 63) == 0) handoff_store4(a.race_part + ((size_t)b * a.nchunk + c) * 4 + (tid >> 6), part);
-    if (!handoff_arrive(a.cnt_race + b * kCtrStride, (uint32_t)a.nchunk, &s_last) || tid >= 64) return;
+    if (!handoff_arrive(counter_at(a.ctr, a.ctr_x, 2 * b + 1), (uint32_t)a.nchunk, &s_last) || tid >= 64) return;
     const int tok = race_winner(a, b, tid);
     if (tid != 0) return;
     const int grow = m.r0 + rq.a;
@@ -1506,10 +1506,10 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
     // the last arriver writes the outputs; the race's last arriver clears both counters.
     const bool race_here = a.fused && m.sampled && !m.topk;
     const int pos0 = race_here ? a.positions[b] : 0;
-    const bool last = handoff_arrive(a.cnt_sweep + b * kCtrStride, (uint32_t)a.nchunk, &s_last, !race_here);
+    const bool last = handoff_arrive(counter_at(a.ctr, a.ctr_x, 2 * b), (uint32_t)a.nchunk, &s_last, !race_here);
     if (!race_here && !last) return;
     if (race_here) {
-        if (!last && tid == 0) wait_arrivals(a, a.cnt_sweep + b * kCtrStride, (uint32_t)a.nchunk);
+        if (!last && tid == 0) wait_arrivals(a, counter_at(a.ctr, a.ctr_x, 2 * b), (uint32_t)a.nchunk);
         __syncthreads();
     }
     finalize_sequence<false, MAP>(a, m, b, s_final, s_rinfo, s_draft,
@@ -1545,11 +1545,11 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
         part = race_chunk(a, m, rq, b, c, cnt, dmr, xp, xq);
     }
     if (lane == 0) handoff_store4(a.race_part + ((size_t)b * a.nchunk + c) * 4 + wave, part);
-    if (!handoff_arrive(a.cnt_race + b * kCtrStride, (uint32_t)a.nchunk, &s_last) || tid >= 64) return;
+    if (!handoff_arrive(counter_at(a.ctr, a.ctr_x, 2 * b + 1), (uint32_t)a.nchunk, &s_last) || tid >= 64) return;
     // ---- the last chunk to arrive: the drawn token and its logprob. Every workgroup of the
     // sequence has passed its wait, so the sweep counter can go back to zero.
     if (lane == 0)
-        __hip_atomic_store(a.cnt_sweep + b * kCtrStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(counter_at(a.ctr, a.ctr_x, 2 * b), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int tok = race_winner(a, b, lane);
     if (lane != 0 || kind == 0) return;
     const int grow = m.r0 + ra;
@@ -1603,11 +1603,10 @@ SampPlan plan_sample(int B, int total_rows, int V, int max_top_k, int max_top_lp
     p.keepcap = V < kKeep ? V : kKeep;
     p.slots = 3 * total_rows - B;
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-    size_t off = 256;
-    p.off_cnt_sweep = off;
-    off += up((size_t)B * 4 * kCtrStride);
-    p.off_cnt_race = off;
-    off += up((size_t)B * 4 * kCtrStride);
+    size_t off = kWsHeader;                         // error word, counters
+    p.n_ctr_x = extra_counters(2L * B);
+    p.off_ctr_x = off;
+    off += up(p.n_ctr_x * 4);
     p.off_stats = off;
     off += up((size_t)p.slots * p.nchunk * 16);
     p.off_cand = off;

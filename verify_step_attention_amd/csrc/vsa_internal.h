@@ -19,6 +19,25 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kWave = 64;
+// Every workspace starts with the same header: the device error word (byte 0), then from
+// byte 256 a region of kCtrLines 256-byte lines of counters that workgroups update
+// atomically. Every call returns its counters to zero and no call keeps anything else
+// there, so any mix of calls and shapes can share one workspace in stream order. Counter i
+// has a line of its own for i < kCtrLines (counters sharing a line serialize each other's
+// atomics); beyond that, lines are shared round-robin.
+constexpr int kCtrLines = 256;
+constexpr int kMaxCounters = kCtrLines * 64;
+constexpr size_t kWsCounters = 256;                                // byte offset
+constexpr size_t kWsHeader = kWsCounters + (size_t)kCtrLines * 256; // first data byte
+__host__ __device__ __forceinline__ size_t ctr_slot(int i) {
+    return (size_t)(i % kCtrLines) * 64 + (size_t)(i / kCtrLines);
+}
+// A call that needs more than kMaxCounters counters keeps the rest in its own workspace
+// area (`extra`, compact), which a fill kernel clears at the start of the call.
+__device__ __forceinline__ uint32_t* counter_at(uint32_t* head, uint32_t* extra, int i) {
+    return i < kMaxCounters ? head + ctr_slot(i) : extra + (i - kMaxCounters);
+}
+inline size_t extra_counters(long n) { return n > kMaxCounters ? (size_t)(n - kMaxCounters) : 0; }
 
 // ---------------------------------------------------------------- small helpers
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
@@ -182,13 +201,14 @@ struct AttnArgs {
     // scalar cache line of the kernel arguments)
     const void* k;
     const void* v;
-    uint32_t* tile_ctr;     // [units] tile claim counters (zero between calls)
+    uint32_t* tile_ctr;     // counter region; unit u claims tiles at counter_at(u)
     const int32_t* cu_rows;
     const int32_t* ctx_lens;
     int nsplit, hkv, s_max, max_kv_len;
     int dyn;                // splits claim tiles from tile_ctr (needs nsplit >= 2)
     int max_rows;
     // the rest
+    uint32_t* tile_ctr_x;   // tile claim counters past the counter region (or unused)
     const void* ksb;        // quantized caches: (scale, bias) fp16 pairs per 64 dims
     const void* vsb;
     int bits;               // 0: bf16 / fp32 K and V; 8 or 4: quantized codes in k / v
@@ -212,7 +232,7 @@ struct AttnPlan {
     int nsplit;      // key splits per (sequence, KV head)
     int units;       // B * Hkv
     int tile;        // keys per workgroup tile
-    size_t off_ctr, off_ml, off_o, bytes;
+    size_t off_ctr_x, n_ctr_x, off_ml, off_o, bytes;
 };
 
 AttnPlan plan_attention(int B, int Hq, int Hkv, int D, int max_rows, int max_kv_len);
@@ -241,7 +261,6 @@ constexpr int kMaxChunks = 256;      // chunks per row (vocabulary <= kMaxChunks
 constexpr int kChunkLoads = kMaxChunks / 64;   // per-lane loads when a wave reads a row's chunks
 constexpr int kKeep = 256;           // kept-set capacity of one truncated row
 constexpr int kMaxSeqRows = 32;      // verify rows per sequence (K <= 31)
-constexpr int kCtrStride = 64;       // uint32 between two sequences' arrival counters (256 B)
 
 // Merged statistics of one row (finalize results, also handed to the race kernel).
 struct RowInfo {
@@ -287,8 +306,9 @@ struct SampArgs {
     float* diag_thr;
     int32_t* diag_kept;
     uint32_t* err;
-    uint32_t* cnt_sweep;           // [B][kCtrStride] arrival counters (zero between calls)
-    uint32_t* cnt_race;            // [B][kCtrStride]
+    uint32_t* ctr;                 // counter region: sequence b's sweep arrivals at
+                                   // counter_at(2b), its race arrivals at counter_at(2b + 1)
+    uint32_t* ctr_x;               // counters past the region (or unused)
     float4* stats;                 // [slots][nchunk] (m, s, best value, best id bits)
     uint2* cand;                   // [slots][nchunk][capc] (ordered key, id)
     uint2* cand_meta;              // [slots][nchunk] (count, k-th key)
@@ -311,19 +331,20 @@ __device__ __forceinline__ void preload_args(const SampArgs& a) {
                  "s"(a.max_top_lp), "s"(a.nchunk), "s"(a.capc), "s"(a.keepcap));
     asm volatile("" ::"s"(a.accepted), "s"(a.out_tokens), "s"(a.chosen_lp), "s"(a.top_vals),
                  "s"(a.top_ids), "s"(a.diag_thr), "s"(a.diag_kept), "s"(a.err),
-                 "s"(a.cnt_sweep), "s"(a.cnt_race), "s"(a.stats), "s"(a.cand),
+                 "s"(a.ctr), "s"(a.ctr_x), "s"(a.stats), "s"(a.cand),
                  "s"(a.cand_meta), "s"(a.rows), "s"(a.keep), "s"(a.race), "s"(a.race_part),
                  "s"(a.fused));
 }
 
 struct SampPlan {
     int nchunk, capc, keepcap, slots;
-    size_t off_cnt_sweep, off_cnt_race, off_stats, off_cand, off_meta, off_rows, off_keep,
+    size_t off_ctr_x, n_ctr_x, off_stats, off_cand, off_meta, off_rows, off_keep,
         off_race, off_race_part, bytes;
 };
 
 SampPlan plan_sample(int B, int total_rows, int V, int max_top_k, int max_top_lp);
 hipError_t launch_sample(const SampArgs& a, hipStream_t stream);
+hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t stream);
 hipError_t launch_draft_vocab_inverse(const int32_t* d2t, int dvocab, int vocab, int32_t* t2d,
                                       hipStream_t stream);
 
