@@ -73,8 +73,9 @@ typedef enum vsa_dtype {
 #define VSA_DEVERR_PARAMS         0x04u /* a sequence's parameters are out of range
                                            (T < 0 or not finite, top_p outside (0, 1],
                                            top_k < 0 or > max_top_k, top_logprobs outside
-                                           [0, max_top_logprobs]): the sequence is
-                                           verified greedily with no logprobs */
+                                           [0, max_top_logprobs], a nucleus without top-k
+                                           when max_top_k = 0): the sequence is verified
+                                           greedily with no logprobs */
 #define VSA_DEVERR_NO_DRAFT_LOGITS 0x08u /* T > 0 but draft_logits is NULL: greedy */
 #define VSA_DEVERR_TIE_OVERFLOW   0x10u /* more ids tie at a top-k threshold than the
                                            candidate capacity holds: the kept set is
@@ -94,7 +95,8 @@ typedef struct vsa_row_params {
     float temperature;        /* 0 => greedy; > 0 => sampled at this temperature */
     int32_t top_k;            /* 0 => off; else keep every id whose penalized logit is >= the
                                  k-th largest (ties at the threshold are kept) */
-    float top_p;              /* 1 => off; in (0, 1): nucleus over the top-k set */
+    float top_p;              /* 1 => off; in (0, 1): nucleus over the top-k set, or
+                                 over the whole vocabulary when top-k is off */
     float presence_penalty;   /* subtracted once from every id with count > 0 */
     float frequency_penalty;  /* subtracted count times from every id */
     int32_t logprobs;         /* nonzero => write the chosen token's raw logprob */
@@ -245,7 +247,8 @@ vsa_status verify_attention_kvq(const void* q, const uint8_t* k_codes, const voi
  *   positions      [B] int32 absolute position decided by row 0
  *   seed           64-bit Philox key
  *   max_rows_per_seq host bound >= every R_b (at most 32)
- *   max_top_k      host bound >= every top_k in use (0 if no sequence uses top-k); <= 256
+ *   max_top_k      host bound >= every top_k in use, and >= 1 when any sampled sequence
+ *                  has top_p < 1 without top-k (0 when no sequence truncates); <= 256
  *   max_top_logprobs host bound >= every top_logprobs (<= 32); the width of top_lp_*
  * Outputs (each may be NULL when not wanted, except accepted_len and out_tokens):
  *   accepted_len   [B] int32   accepted drafts a_b
@@ -259,10 +262,11 @@ vsa_status verify_attention_kvq(const void* q, const uint8_t* k_codes, const voi
  *                  sequence (-inf when top-k is off), NaN for greedy sequences
  *   diag_kept      [total_rows, 2] int32 kept-set sizes after top-k and after top-p of
  *                  each target row of a sampled sequence (0 for greedy sequences)
- * Limits: 1 <= V <= 524288; K_b <= 31; top_k <= 256; a sampled sequence with top_p < 1
- * needs 0 < top_k < V (a nucleus over the whole vocabulary is not supported:
- * VSA_DEVERR_PARAMS); at most 256 ids may tie into one kept set
- * (VSA_DEVERR_TIE_OVERFLOW beyond).
+ * Limits: 1 <= V <= 524288; K_b <= 31; top_k <= 256; at most 256 ids may tie into one
+ * top-k kept set (VSA_DEVERR_TIE_OVERFLOW beyond). A nucleus without top-k (top_p < 1 and
+ * top_k 0 or >= V) keeps {j : z_j / T >= y*} over the whole vocabulary, y* found by a
+ * weighted selection rather than a sort; it runs in the truncation pipeline, so a call
+ * with such a sequence and max_top_k = 0 sets VSA_DEVERR_PARAMS for it (decoded greedily).
  * ------------------------------------------------------------------------------------ */
 size_t verify_sample_accept_workspace_size(int B, int total_rows, int V, int max_rows_per_seq,
                                            int max_top_k, int max_top_logprobs);

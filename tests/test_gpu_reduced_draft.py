@@ -42,17 +42,18 @@ def _inverse_gpu(d2t, vocab):
     return t2d
 
 
-def _run_reduced(w, subset, d2t, reduced, seed=0):
+def _run_reduced(w, subset, d2t, reduced, seed=0, max_top_k=None, nucleus_margin=None):
     from oracle.sampling import widen_draft_logits
     t2d = _inverse_gpu(d2t, w.vocab)
     ref = np.full(w.vocab, -1, np.int32)
     ref[subset] = np.arange(len(subset))
     assert np.array_equal(t2d.cpu().numpy(), ref)
-    gpu = sample_gpu(w, seed=seed, reduced=(torch.from_numpy(reduced).cuda(), t2d))
+    gpu = sample_gpu(w, seed=seed, reduced=(torch.from_numpy(reduced).cuda(), t2d),
+                     max_top_k=max_top_k)
     wide = w.with_params(w.params)
     wide.draft_logits = widen_draft_logits(reduced, d2t, w.vocab)
     ora = sample_oracle(wide, seed=seed)
-    return gpu, compare_sample(w, gpu, ora)
+    return gpu, compare_sample(w, gpu, ora, nucleus_margin=nucleus_margin)
 
 
 @pytest.mark.parametrize("name,dvocab", [("qwen3_4b", 32000), ("batched", 32000),
@@ -109,3 +110,15 @@ def test_bad_inverse_entries_set_error_bit():
     bad[7] = -9
     gpu = sample_gpu(w, reduced=(torch.from_numpy(reduced).cuda(), bad))
     assert gpu["err"] & vsa.DEVERR_DRAFT_MAP
+
+
+def test_reduced_draft_with_nucleus_without_top_k():
+    """Nucleus rows without top-k whose draft rows come through the inverse table."""
+    w = wl.make_workload("verify_b4k4_ctx8192", with_kv=False, seed_offset=3)
+    w = w.with_params([wl.Params(temperature=0.6, top_p=0.85)] * w.batch)
+    w.draft_tokens = q_distributed_drafts(w)
+    subset, d2t, reduced = _reduce(w, 32000, 12)
+    _log("reduced draft vocabulary 32000 with nuclei without top-k")
+    _, flagged = _run_reduced(w, subset, d2t, reduced, seed=2, max_top_k=1,
+                              nucleus_margin=1e-6)
+    assert flagged <= 1

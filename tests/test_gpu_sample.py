@@ -22,11 +22,14 @@ def _log(msg):
     print(msg, flush=True)
 
 
-def _run(w, seed=0, expect_err=0):
-    gpu = sample_gpu(w, seed=seed)
+NUC_MARGIN = 1e-6      # E2 margin for nuclei without top-k (see compare_sample)
+
+
+def _run(w, seed=0, expect_err=0, nucleus_margin=None, max_top_k=None):
+    gpu = sample_gpu(w, seed=seed, max_top_k=max_top_k)
     assert gpu["err"] == expect_err, hex(gpu["err"])
     ora = sample_oracle(w, seed=seed)
-    flagged = compare_sample(w, gpu, ora)
+    flagged = compare_sample(w, gpu, ora, nucleus_margin=nucleus_margin)
     return gpu, ora, flagged
 
 
@@ -51,8 +54,9 @@ def test_tiny_sampled_variant():
         _run(w2, seed=off)
 
 
-def _mixed_batch(batch, vocab, seed, kmax=7):
-    """Many sequences with every parameter combination, ragged K, random counts."""
+def _mixed_batch(batch, vocab, seed, kmax=7, nucleus=False):
+    """Many sequences with every parameter combination, ragged K, random counts; with
+    `nucleus`, also sequences with a nucleus and no top-k."""
     rng = np.random.default_rng(seed)
     k_per = rng.integers(0, kmax + 1, size=batch)
     rows = k_per + 1
@@ -67,13 +71,11 @@ def _mixed_batch(batch, vocab, seed, kmax=7):
         (rng.random((batch, vocab)) < 0.02)
     params = []
     for b in range(batch):
-        kind = b % 6
-        temp = [0.0, 0.8, 1.0, 0.6, 1.3, 0.7][kind]
-        top_k = [0, 0, 20, 5, 64, 40][kind]
-        top_p = [1.0, 1.0, 0.8, 0.95, 1.0, 0.9][kind]
+        kind = b % (8 if nucleus else 6)       # kinds 6, 7: a nucleus without top-k
+        temp = [0.0, 0.8, 1.0, 0.6, 1.3, 0.7, 0.9, 0.7][kind]
+        top_k = [0, 0, 20, 5, 64, 40, 0, 0][kind]
+        top_p = [1.0, 1.0, 0.8, 0.95, 1.0, 0.9, 0.9, 0.5][kind]
         pen = b % 4 == 1
-        if top_k >= vocab:
-            top_p = 1.0                 # a nucleus needs 0 < top_k < V on the GPU
         params.append(wl.Params(temperature=temp, top_k=top_k, top_p=top_p,
                                 presence_penalty=0.5 if pen else 0.0,
                                 frequency_penalty=0.3 if pen else 0.0,
@@ -101,24 +103,74 @@ def test_odd_vocab_scalar_path_and_ties():
     """V not a multiple of 4 (scalar loads), integer logits with ties at the top-k
     threshold and at the greedy argmax."""
     rng = np.random.default_rng(3)
-    w = _mixed_batch(60, 37, 9, kmax=4)
+    w = _mixed_batch(60, 37, 9, kmax=4, nucleus=True)
     w.target_logits = rng.integers(-3, 4, size=w.target_logits.shape).astype(np.float32)
     w.draft_logits = rng.integers(-3, 4, size=w.draft_logits.shape).astype(np.float32)
     w.draft_tokens = q_distributed_drafts(w, seed=4)
     _log("odd vocab 37 with ties")
-    _run(w, seed=1)
+    _run(w, seed=1, nucleus_margin=NUC_MARGIN)
 
 
 def test_edge_cases_k0_and_small_vocab():
     for vocab in (1, 2, 5, 8, 2048, 2049, 4096 + 3):
-        w = _mixed_batch(24, vocab, 100 + vocab, kmax=3)
+        w = _mixed_batch(24, vocab, 100 + vocab, kmax=3, nucleus=True)
         for p in w.params:
-            p.top_k = min(p.top_k, vocab)
-            if p.top_k >= vocab:
-                p.top_p = 1.0          # a nucleus needs 0 < top_k < V on the GPU
+            p.top_k = min(p.top_k, vocab)          # top_k = V: a nucleus without top-k
             p.top_logprobs = min(p.top_logprobs, 5)
         _log(f"small vocab {vocab}")
-        _run(w, seed=vocab)
+        _run(w, seed=vocab, nucleus_margin=NUC_MARGIN)
+
+
+def test_nucleus_mixed_batch():
+    """600 sequences, V=3000, every parameter kind including nuclei without top-k."""
+    w = _mixed_batch(600, 3000, 23, nucleus=True)
+    _log("mixed batch with nuclei: 600 sequences, V=3000")
+    _, _, flagged = _run(w, seed=6, nucleus_margin=NUC_MARGIN)
+    assert flagged <= 6, flagged
+
+
+@pytest.mark.parametrize("temp,top_p,pen", [(0.7, 0.8, False), (0.5, 0.9, True),
+                                              (0.6, 0.3, True), (1.0, 0.95, True)])
+def test_nucleus_without_top_k(temp, top_p, pen):
+    """top_p < 1 and no top-k over the full 151936 vocabulary: the GPU's weighted selection
+    gives the full-sort nucleus (kept counts exact), acceptance and draws equal. At T=1.0,
+    top_p=0.95 the ids near the cutoff carry ~4e-6 each, so most rows sit inside even the
+    tighter margin and are counted, not compared."""
+    w = wl.make_workload("verify_b4k4_ctx8192", with_kv=False, seed_offset=int(top_p * 100))
+    w = w.with_params([wl.Params(temperature=temp, top_p=top_p,
+                                 presence_penalty=0.5 if pen else 0.0,
+                                 frequency_penalty=0.3 if pen else 0.0,
+                                 logprobs=1)] * w.batch)
+    w.draft_tokens = q_distributed_drafts(w)
+    _log(f"nucleus without top-k: T={temp} top_p={top_p} penalties={pen}")
+    gpu, _, flagged = _run(w, seed=3, nucleus_margin=NUC_MARGIN, max_top_k=1)
+    if temp < 1.0:
+        assert flagged <= 1
+    kept = gpu["diag_kept"]
+    assert (kept[:, 0] == w.vocab).all() and (kept[:, 1] > 0).all()
+
+
+def test_nucleus_without_top_k_heavy_ties():
+    """Integer logits over the full vocabulary: tens of thousands of ids share the crossing
+    value (more than the selection's list holds), all kept or all dropped together."""
+    w = wl.make_workload("verify_b4k4_ctx8192", with_kv=False, seed_offset=7)
+    rng = np.random.default_rng(8)
+    w.target_logits = rng.integers(-3, 4, size=w.target_logits.shape).astype(np.float32)
+    w.draft_logits = rng.integers(-3, 4, size=w.draft_logits.shape).astype(np.float32)
+    w = w.with_params([wl.Params(temperature=1.0, top_p=0.7)] * w.batch)
+    w.draft_tokens = q_distributed_drafts(w)
+    _log("nucleus without top-k: integer logits")
+    _run(w, seed=4, nucleus_margin=NUC_MARGIN, max_top_k=1)
+
+
+def test_nucleus_without_top_k_needs_the_truncation_pipeline():
+    """With max_top_k = 0 the caller promised no truncation: a nucleus row is refused
+    (parameter error bit) and the sequence decodes greedily."""
+    w = wl.make_workload("tiny", with_kv=False)
+    w = w.with_params([wl.Params(temperature=1.0, top_p=0.9)])
+    w.draft_tokens = q_distributed_drafts(w)
+    gpu = sample_gpu(w, seed=0, max_top_k=0)
+    assert gpu["err"] & 0x04
 
 
 def test_invalid_inputs_set_error_bits():
@@ -147,6 +199,7 @@ def test_workspace_reuse_is_stateless():
 @pytest.mark.parametrize("cfg", [
     dict(temperature=1.0, top_k=0, top_p=1.0, pen=False),
     dict(temperature=1.3, top_k=6, top_p=0.95, pen=True),
+    dict(temperature=1.0, top_k=0, top_p=0.85, pen=True),      # nucleus without top-k
 ])
 def test_chi_square_losslessness_on_gpu(cfg):
     """The GPU's emitted tokens follow the (penalized, truncated) target: first token ~ p0,
@@ -173,7 +226,7 @@ def test_chi_square_losslessness_on_gpu(cfg):
                     token_counts=None if counts is None else np.tile(counts, (n, 1)),
                     params=[prm] * n, positions=np.full(n, 1000, np.int32), seed=0)
     _log(f"chi-square on GPU: {cfg}")
-    gpu = sample_gpu(w, seed=11)
+    gpu = sample_gpu(w, seed=11, max_top_k=max(cfg["top_k"], int(cfg["top_p"] < 1.0)))
     assert gpu["err"] == 0
     z0 = sampling.penalized_logits(target[0], ctr, pp, fp)
     p0 = sampling.truncated_distribution(z0, prm.temperature, prm.top_k, prm.top_p).probs

@@ -96,6 +96,18 @@ __device__ __forceinline__ float penalize(float x, int c, float pp, float fp) {
     return __fsub_rn(z, c > 0 ? pp : 0.f);
 }
 
+// Nucleus rows (sampled, top_p < 1, no top-k): mass e^(y - ymax) of a value y = v / T
+// relative to the row's maximum, in the same form in the selection, the acceptance and the
+// race. The difference and its base-2 split are exact or fp64, only 2^f (0 <= f < 1) is the
+// fp32 hardware power, so the relative error (~1e-7) does not grow with the distance to the
+// maximum; cumulative masses then sit within ~1e-7 of the fp64 definition.
+__device__ __forceinline__ double nuc_mass(float y, float ymax) {
+    const double t = ((double)y - (double)ymax) * 1.4426950408889634;
+    if (!(t > -1100.0)) return 0.0;                  // -inf, NaN or below every double
+    const double n = floor(t);
+    return ldexp((double)__builtin_amdgcn_exp2f((float)(t - n)), (int)n);
+}
+
 __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -110,6 +122,7 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
 struct SeqMode {
     int r0, rows, k, d0;
     bool valid, sampled, topk, raw;
+    bool nucleus;    // sampled, top_p < 1 without top-k: full-vocabulary nucleus rows
     int ntop, topk_k, logprobs;
     float temp, top_p, pp, fp;
 };
@@ -134,7 +147,7 @@ __device__ SeqMode seq_mode(const SampArgs& a, int b, uint32_t* errbits) {
                      p.top_k > a.max_top_k || !(p.top_p > 0.f && p.top_p <= 1.f) ||
                      p.top_logprobs < 0 || p.top_logprobs > a.max_top_lp ||
                      (p.top_p < 1.f && p.temperature > 0.f &&
-                      !(p.top_k > 0 && p.top_k < a.vocab));
+                      !(p.top_k > 0 && p.top_k < a.vocab) && a.max_top_k == 0);
     if (bad) *errbits |= VSA_DEVERR_PARAMS;
     m.temp = p.temperature;
     m.sampled = !bad && p.temperature > 0.f;
@@ -143,6 +156,7 @@ __device__ SeqMode seq_mode(const SampArgs& a, int b, uint32_t* errbits) {
         m.sampled = false;
     }
     m.topk = m.sampled && p.top_k > 0 && p.top_k < a.vocab;
+    m.nucleus = m.sampled && !m.topk && p.top_p < 1.f;
     m.topk_k = p.top_k;
     m.top_p = p.top_p;
     m.pp = p.presence_penalty;
@@ -935,6 +949,7 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
                 ri.theta = kNegInf;
                 ri.kept_k = a.vocab;
                 ri.kept_p = a.vocab;
+                ri.ythr = kNegInf;
                 rinfo[q] = ri;
             }
         }
@@ -945,11 +960,16 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
     if (AFTER_SELECT) {
         for (int q = tid; q < nrows; q += kThreads) {
             const RowRef r = row_ref(a, m, q);
-            if (m.topk && r.kind != 2) {
+            if ((m.topk || m.nucleus) && r.kind != 2) {
                 const RowInfo sr = a.rows[r.slot];
                 rinfo[q].theta = sr.theta;
                 rinfo[q].kept_k = sr.kept_k;
                 rinfo[q].kept_p = sr.kept_p;
+                if (m.nucleus) {
+                    rinfo[q].ythr = sr.ythr;
+                    rinfo[q].ymax = sr.ymax;
+                    rinfo[q].zk = sr.zk;
+                }
             }
         }
         __syncthreads();
@@ -981,9 +1001,18 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
                 for (int s2 = 0; s2 < t - 1; ++s2) c += drafts[s2] == d_l ? 1 : 0;
                 const float cs = kLog2e / m.temp;
                 const float zt = penalize(pre_xt, c, m.pp, m.fp);
-                pd_l = (double)exp2f((zt - rinfo[t - 1].m) * cs) / rinfo[t - 1].z;
-                qd_l = (double)exp2f((pre_xd - rinfo[m.rows + t - 1].m) * cs) /
-                       rinfo[m.rows + t - 1].z;
+                if (m.nucleus) {
+                    // kept iff y >= y* of the row; renormalized over the kept mass
+                    const RowInfo& ip = rinfo[t - 1];
+                    const RowInfo& iq = rinfo[m.rows + t - 1];
+                    const float yp = __fdiv_rn(zt, m.temp), yq = __fdiv_rn(pre_xd, m.temp);
+                    pd_l = yp >= ip.ythr ? nuc_mass(yp, ip.ymax) / ip.zk : 0.0;
+                    qd_l = yq >= iq.ythr ? nuc_mass(yq, iq.ymax) / iq.zk : 0.0;
+                } else {
+                    pd_l = (double)exp2f((zt - rinfo[t - 1].m) * cs) / rinfo[t - 1].z;
+                    qd_l = (double)exp2f((pre_xd - rinfo[m.rows + t - 1].m) * cs) /
+                           rinfo[m.rows + t - 1].z;
+                }
             }
             if (!m.topk) {
                 // every draft's test at once (u_t from the stream (b, its position, tag 0));
@@ -1011,6 +1040,17 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
                     rq.kind = 2;
                     rq.m_p = rinfo[m.k].m;
                     rq.z_p = rinfo[m.k].z;
+                }
+                if (m.nucleus) {                 // the rows' nuclei and kept masses
+                    rq.nucleus = 1;
+                    rq.z_p = rinfo[acc].zk;
+                    rq.ythr_p = rinfo[acc].ythr;
+                    rq.ymax_p = rinfo[acc].ymax;
+                    if (acc < m.k) {
+                        rq.z_q = rinfo[m.rows + acc].zk;
+                        rq.ythr_q = rinfo[m.rows + acc].ythr;
+                        rq.ymax_q = rinfo[m.rows + acc].ymax;
+                    }
                 }
             } else {
                 // truncated rows: probabilities from the kept lists, one draft at a time
@@ -1109,6 +1149,7 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
 // fallback id), valid in every lane. xp / xq hold the chunk of the target row (m.r0 + rq.a)
 // and, for kind 1, of the draft row (m.d0 + rq.a); dm[e] marks the drafts before row rq.a
 // that equal id e. Ids past the vocabulary hold -inf logits (weight 0: never a winner).
+template <bool NUC>
 __device__ float4 race_chunk(const SampArgs& a, const SeqMode& m, const RaceReq& rq, int b,
                              int c, const int (&cnt)[kEpt], const uint32_t (&dm)[kEpt],
                              const float (&xp)[kEpt], const float (&xq)[kEpt]) {
@@ -1133,11 +1174,25 @@ __device__ float4 race_chunk(const SampArgs& a, const SeqMode& m, const RaceReq&
             const int e = 4 * qd + r;
             const int j = j0 + r;
             const float zp = penalize(xp[e], cnt[e] + __popc(dm[e]), m.pp, m.fp);
-            const float p = __builtin_amdgcn_exp2f((zp - rq.m_p) * cs) * inv_zp;
-            float rr = p;
-            if (rq.kind == 1) {
-                const float q = __builtin_amdgcn_exp2f((xq[e] - rq.m_q) * cs) * inv_zq;
-                rr = fmaxf(0.f, p - q);
+            float p, rr;
+            if constexpr (NUC) {
+                // nucleus rows: ids below the row's y* have probability 0
+                const float y = __fdiv_rn(zp, m.temp);
+                p = y >= rq.ythr_p ? (float)(nuc_mass(y, rq.ymax_p) / rq.z_p) : 0.f;
+                rr = p;
+                if (rq.kind == 1) {
+                    const float yq = __fdiv_rn(xq[e], m.temp);
+                    const float q =
+                        yq >= rq.ythr_q ? (float)(nuc_mass(yq, rq.ymax_q) / rq.z_q) : 0.f;
+                    rr = fmaxf(0.f, p - q);
+                }
+            } else {
+                p = __builtin_amdgcn_exp2f((zp - rq.m_p) * cs) * inv_zp;
+                rr = p;
+                if (rq.kind == 1) {
+                    const float q = __builtin_amdgcn_exp2f((xq[e] - rq.m_q) * cs) * inv_zq;
+                    rr = fmaxf(0.f, p - q);
+                }
             }
             // 1 / (-log2 U'); U' = 1 is E = 0 in the exact race, an infinite key (selected
             // explicitly: -log2(1) may come out as -0, whose reciprocal is -inf)
@@ -1239,7 +1294,8 @@ __global__ __launch_bounds__(kThreads) void race_kernel(const SampArgs a) {
     __syncthreads();
     uint32_t dm[kEpt];
     draft_masks(s_draft, rq.a, base, dm);
-    const float4 part = race_chunk(a, m, rq, b, c, cnt, dm, xp, xq);
+    const float4 part = rq.nucleus ? race_chunk<true>(a, m, rq, b, c, cnt, dm, xp, xq)
+                                   : race_chunk<false>(a, m, rq, b, c, cnt, dm, xp, xq);
     if ((tid & 63) == 0) handoff_store4(a.race_part + ((size_t)b * a.nchunk + c) * 4 + (tid >> 6), part);
     if (!handoff_arrive(counter_at(a.ctr, a.ctr_x, 2 * b + 1), (uint32_t)a.nchunk, &s_last) || tid >= 64) return;
     const int tok = race_winner(a, b, tid);
@@ -1542,7 +1598,7 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
         const uint32_t lm = low_bits(ra);
 #pragma unroll
         for (int e = 0; e < kEpt; ++e) dmr[e] = dm[e] & lm;
-        part = race_chunk(a, m, rq, b, c, cnt, dmr, xp, xq);
+        part = race_chunk<false>(a, m, rq, b, c, cnt, dmr, xp, xq);
     }
     if (lane == 0) handoff_store4(a.race_part + ((size_t)b * a.nchunk + c) * 4 + wave, part);
     if (!handoff_arrive(counter_at(a.ctr, a.ctr_x, 2 * b + 1), (uint32_t)a.nchunk, &s_last) || tid >= 64) return;
@@ -1564,17 +1620,290 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
     }
 }
 
+// ------------------------------------------------------------------ nucleus without top-k
+// A sampled row with top_p < 1 and no top-k keeps {j : y_j >= y*}, y = v / T (fp32 IEEE
+// division, as the definition), where y* is the value at which the mass of the ids sorted
+// by y (descending) first reaches top_p of the row's mass; ties at y* are kept (mlx-dspark
+// release v0.1.0 "Lossless top-p / top-k sampling": the nucleus truncates draft and target).
+// No sort: one workgroup per row finds y* by a weighted selection. Pass 1 over the row
+// histograms the mass by (ymax - y) in steps of 1/16 and finds the bucket where the mass
+// from the top crosses the target; pass 2 lists that bucket's ids (usually a few hundred);
+// a radix selection on their ordered keys, 8 bits at a time, weighted by mass, finds y*.
+
+constexpr int kNucBuckets = 2048;
+constexpr int kNucList = 4096;
+__device__ __forceinline__ int nuc_bucket(float y, float ymax) {
+    const float u = (ymax - y) * 16.f;        // monotone in y: ties share a bucket
+    return u < (float)(kNucBuckets - 1) ? (int)u : kNucBuckets - 1;
+}
+struct NucShared {
+    double hm[kNucBuckets];                   // mass per bucket / digit
+    int hn[kNucBuckets];                      // ids per bucket / digit
+    uint32_t lkey[kNucList];                  // the crossing bucket's ids: ordered key of y
+    double lw[kNucList];                      // and mass
+    int drafts[kMaxSeqRows];
+    int cnt;
+    int pos, cnt_before;
+    double mass_before;
+};
+
+__device__ __forceinline__ double wave_scan_d(double v) {
+    const int lane = threadIdx.x & 63;
+    for (int off = 1; off < 64; off <<= 1) {
+        const double o = __shfl_up(v, off);
+        if (lane >= off) v += o;
+    }
+    return v;
+}
+__device__ __forceinline__ int wave_scan_i(int v) {
+    const int lane = threadIdx.x & 63;
+    for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(v, off);
+        if (lane >= off) v += o;
+    }
+    return v;
+}
+
+// Wave 0: walks positions 0..nb-1 of a histogram (bucket nb - 1 - p when rev) from `base`
+// and stores in ns the first position whose running mass reaches `target`, the running
+// mass before it (base included) and the ids of this histogram before it; when none does
+// (rounding at the very end), the last non-empty position.
+__device__ void nuc_crossing(NucShared& ns, int nb, bool rev, double base, double target) {
+    const int lane = threadIdx.x & 63;
+    const int per = nb / 64;
+    double ms = 0.0;
+    int cs = 0;
+    for (int i = 0; i < per; ++i) {
+        const int p = lane * per + i, idx = rev ? nb - 1 - p : p;
+        ms += ns.hm[idx];
+        cs += ns.hn[idx];
+    }
+    const double incl = wave_scan_d(ms);
+    const int incl_n = wave_scan_i(cs);
+    double excl = __shfl_up(incl, 1);
+    int excl_n = __shfl_up(incl_n, 1);
+    if (lane == 0) {
+        excl = 0.0;
+        excl_n = 0;
+    }
+    const unsigned long long hit = __ballot(base + incl >= target);
+    const unsigned long long nz = __ballot(cs > 0);
+    const int L = hit ? __ffsll(hit) - 1 : (nz ? 63 - __clzll(nz) : 0);
+    if (lane != L) return;
+    double acc = base + excl;
+    int an = excl_n;
+    int pos = -1, last = -1, last_n = 0;
+    double last_m = 0.0;
+    for (int i = 0; i < per; ++i) {
+        const int p = lane * per + i, idx = rev ? nb - 1 - p : p;
+        if (hit && acc + ns.hm[idx] >= target) {
+            pos = p;
+            break;
+        }
+        if (ns.hn[idx] > 0) {
+            last = p;
+            last_m = acc;
+            last_n = an;
+        }
+        acc += ns.hm[idx];
+        an += ns.hn[idx];
+    }
+    if (pos < 0) {                                  // no crossing here: last non-empty
+        pos = last < 0 ? lane * per : last;
+        acc = last_m;
+        an = last_n;
+    }
+    ns.pos = pos;
+    ns.mass_before = acc;
+    ns.cnt_before = an;
+}
+
+// One pass over row r's values y = v / T, f(y) per id (ids past the vocabulary skipped).
+// Target rows carry their penalties (base counts plus the drafts before the row).
+template <bool VEC, bool MAP, class F>
+__device__ void nuc_pass(const SampArgs& a, const SeqMode& m, const RowRef& r, int b,
+                         const int* drafts, F&& f) {
+    constexpr int kB = 4;                           // chunks whose loads are in flight together
+    const bool pen = r.kind == 0 && (m.pp != 0.f || m.fp != 0.f);
+    const int32_t* crow = a.counts ? a.counts + (size_t)b * a.vocab : nullptr;
+    for (int c0 = 0; c0 < a.nchunk; c0 += kB) {
+        float x[kB][kEpt];
+        int cnt[kB][kEpt];
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+            if (c0 + u >= a.nchunk) break;
+            load_row_chunk<VEC, MAP>(a, m, r, (c0 + u) * kChunk, x[u]);
+            if (pen) load_counts<VEC>(crow, (c0 + u) * kChunk, a.vocab, cnt[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+            if (c0 + u >= a.nchunk) break;
+            const int base = (c0 + u) * kChunk;
+            if (pen) {
+                uint32_t dm[kEpt];
+                draft_masks(drafts, r.i, base, dm);   // drafts d_1 .. d_i
+#pragma unroll
+                for (int e = 0; e < kEpt; ++e)
+                    x[u][e] = penalize(x[u][e], cnt[u][e] + __popc(dm[e]), m.pp, m.fp);
+            }
+#pragma unroll
+            for (int e = 0; e < kEpt; ++e)
+                if (elem_id(base, e) < a.vocab) f(__fdiv_rn(x[u][e], m.temp));
+        }
+    }
+}
+
+// Per-thread run-length aggregation of (bucket, mass) before the LDS atomics: ids of one
+// thread that fall in the same bucket in a row cost one atomic.
+struct NucRun {
+    int cur = -1;
+    double acc = 0.0;
+    int n = 0;
+    __device__ void add(NucShared& ns, int k, double w) {
+        if (k != cur) {
+            flush(ns);
+            cur = k;
+        }
+        acc += w;
+        ++n;
+    }
+    __device__ void flush(NucShared& ns) {
+        if (cur >= 0) {
+            atomicAdd(&ns.hm[cur], acc);
+            atomicAdd(&ns.hn[cur], n);
+        }
+        cur = -1;
+        acc = 0.0;
+        n = 0;
+    }
+};
+
+// Nucleus row q of sequence b (target or draft row of a sampled sequence with top_p < 1
+// and no top-k): y*, its kept mass and count to the row's workspace RowInfo.
+template <bool VEC, bool MAP>
+__device__ void nucleus_row(const SampArgs& a, const SeqMode& m, int b, int q, NucShared& ns) {
+    const int tid = threadIdx.x, wave = tid >> 6;
+    const RowRef r = row_ref(a, m, q);
+    if (tid < m.k) ns.drafts[tid] = a.drafts[m.d0 + tid];
+    for (int i = tid; i < kNucBuckets; i += kThreads) {
+        ns.hm[i] = 0.0;
+        ns.hn[i] = 0;
+    }
+    if (tid == 0) ns.cnt = 0;
+    const RowInfo st = row_stats_wave(a, m, r);      // the row's max of v (every wave)
+    const float ymax = __fdiv_rn(st.m, m.temp);        // division is monotone: max of y
+    __syncthreads();
+    RowInfo* out = a.rows + r.slot;
+    if (ymax == kNegInf) {                             // no orderable value in the row
+        if (tid == 0) {
+            out->theta = kNegInf;
+            out->kept_k = a.vocab;
+            out->kept_p = 0;
+            out->ythr = kNegInf;
+            out->ymax = ymax;
+            out->zk = 0.0;
+        }
+        return;
+    }
+    // ---- pass 1: mass per bucket of (ymax - y)
+    {
+        NucRun run;
+        nuc_pass<VEC, MAP>(a, m, r, b, ns.drafts, [&](float y) {
+            run.add(ns, nuc_bucket(y, ymax), nuc_mass(y, ymax));
+        });
+        run.flush(ns);
+    }
+    __syncthreads();
+    __shared__ double s_target;
+    if (wave == 0) {
+        double t = 0.0;
+        for (int i = tid; i < kNucBuckets; i += 64) t += ns.hm[i];
+        t = wave_sum_d(t);
+        const double target = (double)m.top_p * t;
+        if (tid == 0) s_target = target;
+        nuc_crossing(ns, kNucBuckets, false, 0.0, target);
+    }
+    __syncthreads();
+    const double target = s_target;
+    const int bstar = ns.pos;
+    double base = ns.mass_before;
+    int cbase = ns.cnt_before;
+    const int nb = ns.hn[bstar];
+    __syncthreads();
+    // ---- pass 2: the crossing bucket's ids (when they fit the list)
+    const bool listed = nb <= kNucList;
+    if (listed) {
+        nuc_pass<VEC, MAP>(a, m, r, b, ns.drafts, [&](float y) {
+            if (nuc_bucket(y, ymax) == bstar) {
+                const int p = atomicAdd(&ns.cnt, 1);
+                if (p < kNucList) {
+                    ns.lkey[p] = ord_key(y);
+                    ns.lw[p] = nuc_mass(y, ymax);
+                }
+            }
+        });
+        __syncthreads();
+    }
+    const int nl = min(ns.cnt, kNucList);
+    // ---- radix selection on the ordered keys of the bucket's ids, weighted by mass
+    uint32_t prefix = 0u;
+    double last_m = 0.0;
+    int last_n = 0;
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+        for (int i = tid; i < 256; i += kThreads) {
+            ns.hm[i] = 0.0;
+            ns.hn[i] = 0;
+        }
+        __syncthreads();
+        auto visit = [&](uint32_t key, double w, NucRun& run) {
+            if (pass > 0 && (key >> (shift + 8)) != prefix) return;
+            run.add(ns, (int)((key >> shift) & 255u), w);
+        };
+        NucRun run;
+        if (listed) {
+            for (int i = tid; i < nl; i += kThreads) visit(ns.lkey[i], ns.lw[i], run);
+        } else {
+            nuc_pass<VEC, MAP>(a, m, r, b, ns.drafts, [&](float y) {
+                if (nuc_bucket(y, ymax) == bstar) visit(ord_key(y), nuc_mass(y, ymax), run);
+            });
+        }
+        run.flush(ns);
+        __syncthreads();
+        if (wave == 0) nuc_crossing(ns, 256, true, base, target);
+        __syncthreads();
+        const int digit = 255 - ns.pos;
+        base = ns.mass_before;                         // includes the earlier mass
+        cbase += ns.cnt_before;                        // ids of this pass before the digit
+        last_m = ns.hm[digit];
+        last_n = ns.hn[digit];
+        prefix = (prefix << 8) | (uint32_t)digit;
+        __syncthreads();
+    }
+    if (tid == 0) {
+        out->theta = kNegInf;                          // no top-k
+        out->kept_k = a.vocab;
+        out->kept_p = cbase + last_n;
+        out->ythr = key_float(prefix);
+        out->ymax = ymax;
+        out->zk = base + last_m;
+    }
+}
+
 // ------------------------------------------------------------------ top-k pipeline kernels
 // grid (B x rows_cap): workgroup (b, q) selects row q of sequence b when it is a truncated
 // or top-n row; every other workgroup returns at once.
+template <bool VEC, bool MAP>
 __global__ __launch_bounds__(kThreads) void select_kernel(const SampArgs a, int rows_cap) {
     __shared__ FinalShared s_final;
+    __shared__ NucShared s_nuc;
     preload_args(a);
     const int b = blockIdx.x / rows_cap, q = blockIdx.x % rows_cap;
     uint32_t ebits = 0;
     const SeqMode m = seq_mode(a, b, &ebits);
     if (!m.valid || q >= seq_nrows(m)) return;
-    select_row(a, m, q, s_final);
+    if (m.nucleus && row_ref(a, m, q).kind != 2) nucleus_row<VEC, MAP>(a, m, b, q, s_nuc);
+    else select_row(a, m, q, s_final);
 }
 
 // grid (B): merges the chunk statistics and runs the acceptance of one sequence.
@@ -1699,8 +2028,14 @@ hipError_t launch_sample(const SampArgs& args, hipStream_t stream) {
     if (topk) {
         // one workgroup per (sequence, row of its row list), then one per sequence
         const int rows_cap = 3 * a.max_rows;
-        hipLaunchKernelGGL(select_kernel, dim3((unsigned)a.batch * rows_cap), block, 0, stream,
-                           a, rows_cap);
+        const dim3 sgrid((unsigned)a.batch * rows_cap);
+        if (map) {
+            if (vec) hipLaunchKernelGGL((select_kernel<true, true>), sgrid, block, 0, stream, a, rows_cap);
+            else hipLaunchKernelGGL((select_kernel<false, true>), sgrid, block, 0, stream, a, rows_cap);
+        } else {
+            if (vec) hipLaunchKernelGGL((select_kernel<true, false>), sgrid, block, 0, stream, a, rows_cap);
+            else hipLaunchKernelGGL((select_kernel<false, false>), sgrid, block, 0, stream, a, rows_cap);
+        }
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (map) hipLaunchKernelGGL(finalize_kernel<true>, dim3((unsigned)a.batch), block, 0, stream, a);

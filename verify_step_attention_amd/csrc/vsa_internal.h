@@ -269,7 +269,12 @@ struct RowInfo {
     int argmax;        // greedy argmax (lowest id on ties)
     float theta;       // top-k threshold (value of the k-th largest)
     int kept_k, kept_p;
+    // nucleus without top-k: the kept set is {y >= ythr}, y = v / T (fp32 division), with
+    // mass zk = sum over it of 2^((y - ymax) log2 e); ythr = -inf otherwise
+    float ythr;
+    float ymax;
     int pad;
+    double zk;
 };
 
 struct KeepEntry {     // one id of a truncated, renormalized distribution
@@ -284,8 +289,9 @@ struct RaceReq {       // a categorical draw over the whole vocabulary, done by 
     int pos;           // absolute position of the draw
     int logprobs;
     float m_p, m_q, m_x;
-    int pad;
+    int nucleus;       // p and q are nucleus rows: (ythr, ymax) below, z_p / z_q their kept mass
     double z_p, z_q, z_x;
+    float ythr_p, ymax_p, ythr_q, ymax_q;
 };
 
 struct SampArgs {
