@@ -449,7 +449,7 @@ def main():
                          "reference for rocprofv3 byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}); "
               "the verify step's sharding across GPUs is a design note, not a run.",
               file=sys.stderr)
         sys.exit(2)
