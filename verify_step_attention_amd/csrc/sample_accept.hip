@@ -102,8 +102,9 @@ __device__ __forceinline__ float penalize(float x, int c, float pp, float fp) {
 // fp32 hardware power, so the relative error (~1e-7) does not grow with the distance to the
 // maximum; cumulative masses then sit within ~1e-7 of the fp64 definition.
 __device__ __forceinline__ double nuc_mass(float y, float ymax) {
-    const double t = ((double)y - (double)ymax) * 1.4426950408889634;
+    double t = ((double)y - (double)ymax) * 1.4426950408889634;
     if (!(t > -1100.0)) return 0.0;                  // -inf, NaN or below every double
+    if (!(t <= 0.0)) t = 0.0;                        // y <= ymax; an empty row gives +inf
     const double n = floor(t);
     return ldexp((double)__builtin_amdgcn_exp2f((float)(t - n)), (int)n);
 }
@@ -1794,12 +1795,12 @@ __device__ void nucleus_row(const SampArgs& a, const SeqMode& m, int b, int q, N
     const float ymax = __fdiv_rn(st.m, m.temp);        // division is monotone: max of y
     __syncthreads();
     RowInfo* out = a.rows + r.slot;
-    if (ymax == kNegInf) {                             // no orderable value in the row
+    if (ymax == kNegInf) {                             // no orderable value: nothing kept
         if (tid == 0) {
             out->theta = kNegInf;
             out->kept_k = a.vocab;
             out->kept_p = 0;
-            out->ythr = kNegInf;
+            out->ythr = __builtin_inff();
             out->ymax = ymax;
             out->zk = 0.0;
         }
