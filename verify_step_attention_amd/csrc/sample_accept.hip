@@ -247,6 +247,43 @@ __device__ uint32_t wg_select_kth(const uint32_t (&key)[kEpt], uint32_t valid, i
 
 // ------------------------------------------------------------------ wave-level pieces
 // Bitonic sort of n <= kKeep (key, id) pairs: key descending, id ascending.
+// A lower bound of the k-th largest (1-based, k <= 256) of the 256 threads' values v, in
+// every thread: a radix selection on the top 16 bits, 4 bits a round, whose result with
+// the low 16 bits cleared has at least k values at or above it (for ordered float keys,
+// within 2^-7 relative of the k-th largest). Per round each wave counts in its own LDS
+// table the values that carry the prefix chosen so far, per nibble; lanes 0..15 of every
+// wave add the four waves' counts (descending nibble order), scan them with row shifts and
+// pick the nibble where the running count reaches the remaining k. One barrier a round
+// (the count tables are double-buffered by round).
+__device__ uint32_t wg_kth_bound(uint32_t v, int k, int (&cnt)[2][4][16]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t prefix = 0u, pmask = 0u;
+    int need = k;
+    for (int shift = 28, par = 0; shift >= 16; shift -= 4, par ^= 1) {
+        // this wave's counts per nibble: its own table, cleared and filled by the wave
+        // alone (its LDS operations complete in order)
+        if (lane < 16) cnt[par][wave][lane] = 0;
+        if ((v & pmask) == prefix) atomicAdd(&cnt[par][wave][(v >> shift) & 15u], 1);
+        __syncthreads();
+        int t = 0;
+        if (lane < 16) {
+            const int c = 15 - lane;
+            t = cnt[par][0][c] + cnt[par][1][c] + cnt[par][2][c] + cnt[par][3][c];
+        }
+        int incl = t;                                  // inclusive scan in lanes 0..15
+        incl += __builtin_amdgcn_update_dpp(0, incl, 0x111, 0xF, 0xF, false);   // row_shr:1
+        incl += __builtin_amdgcn_update_dpp(0, incl, 0x112, 0xF, 0xF, false);   // row_shr:2
+        incl += __builtin_amdgcn_update_dpp(0, incl, 0x114, 0xF, 0xF, false);   // row_shr:4
+        incl += __builtin_amdgcn_update_dpp(0, incl, 0x118, 0xF, 0xF, false);   // row_shr:8
+        const unsigned long long hit = __ballot(lane < 16 && incl >= need);
+        const int L = __ffsll(hit) - 1;             // the prefix's values number >= need
+        need -= __builtin_amdgcn_readlane(incl - t, L);
+        prefix |= (uint32_t)(15 - L) << shift;
+        pmask |= 15u << shift;
+    }
+    return prefix;
+}
+
 __device__ void wave_sort(uint32_t* lkey, int* lidx, int n) {
     const int lane = threadIdx.x & 63;
     int np = 1;
@@ -1314,7 +1351,7 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
     __shared__ float4 s_part[3 * kMaxSeqRows][4];
     __shared__ int s_draft[kMaxSeqRows];
     __shared__ uint32_t s_hist[256];
-    __shared__ __attribute__((aligned(16))) uint32_t s_tm[kThreads];
+    __shared__ int s_nib[2][4][16];
     __shared__ int s_sh[4];
     __shared__ FinalShared s_final;
     __shared__ RowInfo s_rinfo[3 * kMaxSeqRows];
@@ -1482,36 +1519,18 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
             const int n_valid = min(kChunk, a.vocab - base);
             uint2* out = a.cand + ((size_t)r.slot * a.nchunk + c) * a.capc;
             // The chunk's candidates are all keys >= vk for a vk <= its kk-th largest key.
-            // First vk is the kk-th largest of the threads' maxima (kk distinct values, or 0
-            // when fewer threads hold ids): a cheap bound that usually leaves a few more
-            // than kk keys. If those do not fit in capc slots, vk becomes the exact kk-th key
-            // (radix select) and ties at it are cut at capc (the count says so).
+            // First vk is a bound at or below the kk-th largest of the threads' maxima (kk
+            // distinct values, or 0 when fewer threads hold ids), within 2^-7 of it: a cheap
+            // bound that usually leaves a few more than kk keys. If those do not fit in capc
+            // slots, vk becomes the exact kk-th key (radix select) and ties at it are cut at
+            // capc (the count says so).
             uint32_t vk = 0u;
             if (n_valid > kk) {
                 uint32_t tmax = 0u;
 #pragma unroll
                 for (int e = 0; e < kEpt; ++e)
                     if ((valid >> e) & 1u) tmax = max(tmax, key[e]);
-                s_tm[tid] = tmax;
-                __syncthreads();
-                int rank = 0;
-                const uint4* tm4 = reinterpret_cast<const uint4*>(s_tm);
-                for (int t4 = 0; t4 < kThreads / 4; t4 += 4) {     // 16 values per round
-                    uint4 v[4];
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) v[u] = tm4[t4 + u];
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const int t = 4 * (t4 + u);
-                        rank += (v[u].x > tmax || (v[u].x == tmax && t < tid)) ? 1 : 0;
-                        rank += (v[u].y > tmax || (v[u].y == tmax && t + 1 < tid)) ? 1 : 0;
-                        rank += (v[u].z > tmax || (v[u].z == tmax && t + 2 < tid)) ? 1 : 0;
-                        rank += (v[u].w > tmax || (v[u].w == tmax && t + 3 < tid)) ? 1 : 0;
-                    }
-                }
-                if (rank == kk - 1) s_sh[3] = (int)tmax;
-                __syncthreads();
-                vk = (uint32_t)s_sh[3];
+                vk = wg_kth_bound(tmax, kk, s_nib);
             }
             if (tid == 0) s_sh[2] = 0;
             __syncthreads();
