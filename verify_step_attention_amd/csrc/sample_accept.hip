@@ -284,7 +284,39 @@ __device__ uint32_t wg_kth_bound(uint32_t v, int k, int (&cnt)[2][4][16]) {
     return prefix;
 }
 
-__device__ void wave_sort(uint32_t* lkey, int* lidx, int n) {
+// Sorts n <= kKeep (key, id) pairs in LDS by key descending, id ascending (one wave). Up to
+// 64 pairs: each pair's rank is the number of pairs before it in that order (ids are
+// distinct, so ranks are a permutation) and the pairs move through `tmp` to their ranks:
+// n independent LDS reads per lane instead of a bitonic network's log^2 n dependent
+// stages. Larger lists take the bitonic network.
+__device__ void wave_sort_bitonic(uint32_t* lkey, int* lidx, int n);
+__device__ void wave_sort(uint32_t* lkey, int* lidx, int n, uint2* tmp) {
+    if (n > 64) {
+        wave_sort_bitonic(lkey, lidx, n);
+        return;
+    }
+    const int lane = threadIdx.x & 63;
+    for (int i = lane; i < n; i += 64) {
+        const uint32_t k = lkey[i];
+        const int id = lidx[i];
+        int rank = 0;
+        for (int t = 0; t < n; ++t) {
+            const uint32_t kt = lkey[t];
+            const int it = lidx[t];
+            rank += (kt > k || (kt == k && it < id)) ? 1 : 0;
+        }
+        tmp[rank] = make_uint2(k, (uint32_t)id);
+    }
+    wave_sync();
+    for (int i = lane; i < n; i += 64) {
+        const uint2 e = tmp[i];
+        lkey[i] = e.x;
+        lidx[i] = (int)e.y;
+    }
+    wave_sync();
+}
+
+__device__ void wave_sort_bitonic(uint32_t* lkey, int* lidx, int n) {
     const int lane = threadIdx.x & 63;
     int np = 1;
     while (np < n) np <<= 1;
@@ -515,9 +547,13 @@ __device__ __forceinline__ uint32_t load_slot_keys(const uint2* cand, const int*
         const bool v = sl < nslots && i < ccount[c];
         vm |= (v ? 1u : 0u) << j;
     }
+    // every load issued (clamped into the row's table), then masked: no load waits behind
+    // the branch of another
 #pragma unroll
     for (int j = 0; j < kSelTile; ++j)
-        kt[j] = ((vm >> j) & 1u) ? cand[s0 + (int)threadIdx.x + kThreads * j].x : 0u;
+        kt[j] = cand[min(s0 + (int)threadIdx.x + kThreads * j, nslots - 1)].x;
+#pragma unroll
+    for (int j = 0; j < kSelTile; ++j) kt[j] = ((vm >> j) & 1u) ? kt[j] : 0u;
     return vm;
 }
 
@@ -645,7 +681,7 @@ struct FinalShared {
     int lidx[kKeep];
     double lp[kKeep];
     int ccount[kMaxChunks];
-    __attribute__((aligned(16))) uint32_t cmk[kMaxChunks];   // chunk maxima as ordered keys
+    int nib[2][4][16];           // radix-bound counts (wg_kth_bound)
     int drafts[kMaxSeqRows];
 };
 
@@ -705,14 +741,8 @@ __device__ void select_row(const SampArgs& a, const SeqMode& m, int q, FinalShar
         ovf = (int)meta.x > a.capc;
         ovf_key = meta.y;
         cmax = ord_key(st.x);
-        fs.cmk[tid] = cmax;
-    } else if (tid < (a.nchunk + 15) / 16 * 16) {
-        fs.cmk[tid] = 0u;                          // padding: ranks below every maximum
     }
-    if (tid == 0) {
-        fs.sel[0] = 0;
-        fs.sel[7] = 0;
-    }
+    if (tid == 0) fs.sel[0] = 0;
     __syncthreads();
     const int nslots = a.nchunk * a.capc;
     int tot = 0;
@@ -729,31 +759,11 @@ __device__ void select_row(const SampArgs& a, const SeqMode& m, int q, FinalShar
     }
     // Lower bounds of the row's ksel-th largest key theta: every chunk holds at least k
     // values >= its own k-th key (meta.y), and the ksel largest chunk maxima are ksel
-    // distinct values. Usually only a few dozen candidates reach the larger bound; they
+    // distinct values (a radix bound at or below the ksel-th largest of them serves). Usually only a few dozen candidates reach the larger bound; they
     // are sorted exactly. Otherwise a radix select over every candidate decides.
     uint32_t lb = wg_max_u(tid < a.nchunk ? ovf_key : 0u, fs.sel + 1);
-    if (a.nchunk >= ksel && tid < a.nchunk) {
-        // rank of this chunk's maximum; the table is padded with zeros to a multiple
-        // of 16 entries, read 16 at a time
-        int rank = 0;
-        const uint4* cm4 = reinterpret_cast<const uint4*>(fs.cmk);
-        for (int c4 = 0; c4 < (a.nchunk + 15) / 16 * 4; c4 += 4) {
-            uint4 v[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) v[u] = cm4[c4 + u];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int c = 4 * (c4 + u);
-                rank += (v[u].x > cmax || (v[u].x == cmax && c < tid)) ? 1 : 0;
-                rank += (v[u].y > cmax || (v[u].y == cmax && c + 1 < tid)) ? 1 : 0;
-                rank += (v[u].z > cmax || (v[u].z == cmax && c + 2 < tid)) ? 1 : 0;
-                rank += (v[u].w > cmax || (v[u].w == cmax && c + 3 < tid)) ? 1 : 0;
-            }
-        }
-        if (rank == ksel - 1) fs.sel[7] = (int)cmax;
-    }
-    __syncthreads();
-    lb = max(lb, (uint32_t)fs.sel[7]);
+    if (a.nchunk >= ksel) lb = max(lb, wg_kth_bound(cmax, ksel, fs.nib));
+
     uint32_t kt0[kSelTile];
     const uint32_t vm0 = load_slot_keys(cand, ccount, a.capc, nslots, 0, kt0);
     // every candidate >= bound goes to the LDS list (ids loaded for those only)
@@ -769,12 +779,18 @@ __device__ void select_row(const SampArgs& a, const SeqMode& m, int q, FinalShar
             }
 #pragma unroll
             for (int j = 0; j < kSelTile; ++j) {
-                if (((vmask >> j) & 1u) && kt[j] >= bound) {
-                    const int sl = s0 + tid + kThreads * j;
-                    const int pos = atomicAdd(&fs.sel[0], 1);
+                // one list reservation per wave and slot column, not one per candidate
+                const bool take = ((vmask >> j) & 1u) && kt[j] >= bound;
+                const unsigned long long bal = __ballot(take);
+                if (bal == 0ull) continue;
+                int pos0 = 0;
+                if (lane == 0) pos0 = atomicAdd(&fs.sel[0], __popcll(bal));
+                pos0 = __builtin_amdgcn_readfirstlane(pos0);
+                if (take) {
+                    const int pos = pos0 + __popcll(bal & ((1ull << lane) - 1ull));
                     if (pos < kKeep) {
                         fs.lkey[pos] = kt[j];
-                        fs.lidx[pos] = (int)cand[sl].y;
+                        fs.lidx[pos] = (int)cand[s0 + tid + kThreads * j].y;
                     }
                 }
             }
@@ -786,7 +802,7 @@ __device__ void select_row(const SampArgs& a, const SeqMode& m, int q, FinalShar
     uint32_t theta;
     bool sorted = false;
     if (n_all >= ksel && n_all <= kKeep) {
-        if (wave == 0) wave_sort(fs.lkey, fs.lidx, n_all);
+        if (wave == 0) wave_sort(fs.lkey, fs.lidx, n_all, reinterpret_cast<uint2*>(fs.lp));
         __syncthreads();
         theta = fs.lkey[ksel - 1];
         int cnt = 0;
@@ -806,7 +822,7 @@ __device__ void select_row(const SampArgs& a, const SeqMode& m, int q, FinalShar
     if (n_all > kKeep && tid == 0) atomicOr(a.err, VSA_DEVERR_TIE_OVERFLOW);
     if (wave != 0) return;
     const int n = min(n_all, kKeep);
-    if (!sorted) wave_sort(fs.lkey, fs.lidx, n);
+    if (!sorted) wave_sort(fs.lkey, fs.lidx, n, reinterpret_cast<uint2*>(fs.lp));
     if (topn) {
         // raw top-n ids with their log-softmax values
         const RowInfo ri = row_stats_wave(a, m, r);
