@@ -682,6 +682,8 @@ struct FinalShared {
     double lp[kKeep];
     int ccount[kMaxChunks];
     int nib[2][4][16];           // radix-bound counts (wg_kth_bound)
+    int live[kMaxChunks];        // chunks whose maximum reaches the bound, and their count
+    int nlive;
     int drafts[kMaxSeqRows];
 };
 
@@ -742,7 +744,10 @@ __device__ void select_row(const SampArgs& a, const SeqMode& m, int q, FinalShar
         ovf_key = meta.y;
         cmax = ord_key(st.x);
     }
-    if (tid == 0) fs.sel[0] = 0;
+    if (tid == 0) {
+        fs.sel[0] = 0;
+        fs.nlive = 0;
+    }
     __syncthreads();
     const int nslots = a.nchunk * a.capc;
     int tot = 0;
@@ -765,7 +770,7 @@ __device__ void select_row(const SampArgs& a, const SeqMode& m, int q, FinalShar
     if (a.nchunk >= ksel) lb = max(lb, wg_kth_bound(cmax, ksel, fs.nib));
 
     uint32_t kt0[kSelTile];
-    const uint32_t vm0 = load_slot_keys(cand, ccount, a.capc, nslots, 0, kt0);
+    uint32_t vm0 = 0u;                             // loaded only if the exact path runs
     // every candidate >= bound goes to the LDS list (ids loaded for those only)
     auto collect = [&](uint32_t bound) {
         for (int s0 = 0; s0 < nslots; s0 += kThreads * kSelTile) {
@@ -797,7 +802,56 @@ __device__ void select_row(const SampArgs& a, const SeqMode& m, int q, FinalShar
         }
         __syncthreads();
     };
-    collect(lb);
+    // First pass: only chunks whose maximum reaches lb can hold a candidate >= lb (usually a
+    // few dozen of them); their slots are read as (key, id) pairs in one round.
+    {
+        const bool live = tid < a.nchunk && cmax >= lb && ccount[tid] > 0;
+        const unsigned long long bal = __ballot(live);
+        int p0 = 0;
+        if (lane == 0 && bal) p0 = atomicAdd(&fs.nlive, __popcll(bal));
+        p0 = __builtin_amdgcn_readfirstlane(p0);
+        if (live) fs.live[p0 + __popcll(bal & ((1ull << lane) - 1ull))] = tid;
+    }
+    __syncthreads();
+    {
+        constexpr int kLiveTile = 16;
+        const int nlive = fs.nlive;
+        const int nls = nlive * a.capc;
+        const float rc = 1.f / (float)a.capc;
+        for (int s0 = 0; s0 < nls; s0 += kThreads * kLiveTile) {
+            uint2 kv[kLiveTile];
+            uint32_t vm = 0u;
+#pragma unroll
+            for (int j = 0; j < kLiveTile; ++j) {
+                const int sl = s0 + tid + kThreads * j;
+                int li = (int)((float)sl * rc);          // corrected by one step (sl < 2^24)
+                int i = sl - li * a.capc;
+                if (i < 0) { --li; i += a.capc; }
+                else if (i >= a.capc) { ++li; i -= a.capc; }
+                li = li < 0 ? 0 : li < nlive - 1 ? li : nlive - 1;
+                const int c = fs.live[li];
+                vm |= (sl < nls && i < ccount[c] ? 1u : 0u) << j;
+                kv[j] = cand[c * a.capc + i];
+            }
+#pragma unroll
+            for (int j = 0; j < kLiveTile; ++j) {
+                const bool take = ((vm >> j) & 1u) && kv[j].x >= lb;
+                const unsigned long long bal = __ballot(take);
+                if (bal == 0ull) continue;
+                int pos0 = 0;
+                if (lane == 0) pos0 = atomicAdd(&fs.sel[0], __popcll(bal));
+                pos0 = __builtin_amdgcn_readfirstlane(pos0);
+                if (take) {
+                    const int pos = pos0 + __popcll(bal & ((1ull << lane) - 1ull));
+                    if (pos < kKeep) {
+                        fs.lkey[pos] = kv[j].x;
+                        fs.lidx[pos] = (int)kv[j].y;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
     int n_all = fs.sel[0];
     uint32_t theta;
     bool sorted = false;
@@ -810,6 +864,7 @@ __device__ void select_row(const SampArgs& a, const SeqMode& m, int q, FinalShar
         n_all = wg_sum_i(cnt, fs.sel + 1);          // the sorted list's first n_all
         sorted = true;
     } else {
+        vm0 = load_slot_keys(cand, ccount, a.capc, nslots, 0, kt0);
         theta = wg_select_slots(cand, ccount, a.capc, nslots, ksel, kt0, vm0, fs.hist,
                                 fs.sel + 5);
         if (tid == 0) fs.sel[0] = 0;
