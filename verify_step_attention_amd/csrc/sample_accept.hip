@@ -685,6 +685,7 @@ struct FinalShared {
     int live[kMaxChunks];        // chunks whose maximum reaches the bound, and their count
     int nlive;
     int drafts[kMaxSeqRows];
+    double pq[2][kMaxSeqRows];   // p_{t-1}(d_t), q_t(d_t) of truncated rows (finalize)
 };
 
 // ------------------------------------------------------------------ per-row selection
@@ -1082,6 +1083,25 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
             }
         }
         __syncthreads();
+        // every draft's p_{t-1}(d_t) and q_t(d_t) from the truncated rows' kept lists, draft
+        // t by wave (t - 1) mod 4, so the lists are read in parallel rather than one draft
+        // after another in the acceptance loop
+        if (m.topk) {
+            for (int t = 1 + wave; t <= m.k; t += 4) {
+                const int d = drafts[t - 1];
+                double pd = 0.0, qd = 0.0;
+                if (d >= 0 && d < a.vocab) {
+                    pd = keep_lookup(a, row_ref(a, m, t - 1).slot, rinfo[t - 1].kept_p, d);
+                    qd = keep_lookup(a, row_ref(a, m, m.rows + t - 1).slot,
+                                     rinfo[m.rows + t - 1].kept_p, d);
+                }
+                if (lane == 0) {
+                    fs.pq[0][t - 1] = pd;
+                    fs.pq[1][t - 1] = qd;
+                }
+            }
+            __syncthreads();
+        }
     }
 
     // ---- C: acceptance (wave 0)
@@ -1169,14 +1189,10 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
                     const int d = drafts[t - 1];
                     const bool valid = d >= 0 && d < a.vocab;
                     if (!valid) ebits |= VSA_DEVERR_DRAFT_ID;
-                    double pd = 0.0, qd = 0.0;
                     const int pq = t - 1;            // target row t-1 in the row list
                     const int qq = m.rows + t - 1;   // draft row t
                     const RowRef rp = row_ref(a, m, pq), rqr = row_ref(a, m, qq);
-                    if (valid) {
-                        pd = keep_lookup(a, rp.slot, rinfo[pq].kept_p, d);
-                        qd = keep_lookup(a, rqr.slot, rinfo[qq].kept_p, d);
-                    }
+                    const double pd = fs.pq[0][t - 1], qd = fs.pq[1][t - 1];   // 0 if invalid
                     const uint4 wu = philox_block(a.seed, 0u, (uint32_t)pos, (uint32_t)b, 0u);
                     const double u = (double)(wu.x >> 8) * 5.9604644775390625e-08;
                     if (u * qd < pd) { ++acc; continue; }
