@@ -27,6 +27,11 @@ times small_m_qmm instead: the four weight matmuls of one 27B-class decoder laye
 down 5120x25600) on M verify rows, with synthetic quantized weights (random codes, scale
 and bias) resident in HBM; one JSON line, value = layers per second.
 
+    python bench.py --sampling WORKLOAD [--top-p P --temperature T]
+
+times verify_sample_accept alone on a workload's logits (qwen3_4b, long, swarm, ...), with
+its own parameters or, given --top-p, a nucleus without top-k on every sequence.
+
     python bench.py --drafter-block [--window W] [--bidirectional] [--sliding]
 
 times block_attention alone on a drafter's block instead: B=4 blocks of 8 rows over a
@@ -132,6 +137,80 @@ def cpu_baseline(w, kq=None, budget_s=12.0):
                       f"{'' if kq is None else f' over the {kq.bits}-bit cache'} + "
                       f"sample/accept of all 4 sequences), {dt:.1f} s on the host, numpy "
                       f"BLAS threads = {cores}"}
+
+
+def sampling_main(args):
+    """verify_sample_accept alone on a named workload's logits (its own parameters, or a
+    nucleus without top-k when --top-p is given): HIP-event timing of graph replays of the
+    call over 3 input sets. Drafts are the stand-in greedy drafter's (argmax of each draft
+    row)."""
+    import torch
+    import verify_step_attention_amd as vsa
+    from verify_step_attention_amd import workloads as wl
+    name = args.sampling
+    w = wl.make_workload(name, with_kv=False)
+    if args.top_p < 1.0:
+        w = w.with_params([wl.Params(temperature=args.temperature, top_p=args.top_p)] *
+                          w.batch)
+    mtk = max([p.top_k for p in w.params] + [1 if args.top_p < 1.0 else 0])
+    mtl = max(p.top_logprobs for p in w.params)
+    dev0 = wl.device_tensors(w, with_kv=False)
+    sets = [dev0] + [{k: (None if t is None else t.clone()) for k, t in dev0.items()}
+                     for _ in range(2)]
+    params = torch.from_numpy(vsa.pack_row_params(w.params).view(np.uint8)).cuda()
+    ws = torch.zeros(vsa.verify_sample_accept_workspace_size(
+        w.batch, w.total_rows, w.vocab, w.max_rows, mtk, mtl), dtype=torch.uint8, device="cuda")
+    acc = torch.empty(w.batch, dtype=torch.int32, device="cuda")
+    toks = torch.empty(w.total_rows, dtype=torch.int32, device="cuda")
+    lp = torch.empty(w.total_rows, dtype=torch.float32, device="cuda")
+    tv = torch.empty((w.total_rows, max(mtl, 1)), dtype=torch.float32, device="cuda")
+    ti = torch.empty((w.total_rows, max(mtl, 1)), dtype=torch.int32, device="cuda")
+
+    def call(d, s):
+        vsa.verify_sample_accept(d["target_logits"], d["draft_logits"], d["draft_tokens"],
+                                 d["cu_rows"], d["token_counts"], params, d["positions"], 0,
+                                 acc, toks, ws, max_rows_per_seq=w.max_rows, max_top_k=mtk,
+                                 max_top_logprobs=mtl, chosen_logprob=lp,
+                                 top_lp_vals=tv if mtl else None,
+                                 top_lp_ids=ti if mtl else None, stream=s)
+    stream = torch.cuda.current_stream()
+    for d in sets:
+        call(d, stream)
+    torch.cuda.synchronize()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(stream)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cs):
+        with torch.cuda.graph(g, stream=cs):
+            for d in sets:
+                call(d, torch.cuda.current_stream())
+    stream.wait_stream(cs)
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, args.steps // len(sets))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * len(sets))
+    err = int(ws[:4].view(torch.int32).item())
+    if err:
+        print(f"[bench] device error word {err:#x}", file=sys.stderr)
+    nbytes = (w.total_rows + (w.total_rows - w.batch)) * w.vocab * 4 + \
+        (0 if w.token_counts is None else w.batch * w.vocab * 4)
+    print(json.dumps({
+        "metric": f"verify_sample_accept calls/sec, {name}" +
+                  (f", nucleus T={args.temperature} top_p={args.top_p}"
+                   if args.top_p < 1.0 else ""),
+        "value": round(1e6 / us, 1), "unit": "calls/s", "n_gpus": 1,
+        "steps": reps * len(sets), "warmup": len(sets), "ms_per_step": round(us / 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic", "launch": "hip_graph_replay",
+        "config": {"workload": name, "batch": w.batch, "rows": w.total_rows,
+                   "vocab": w.vocab, "call_us": round(us, 2),
+                   "logit_bytes": nbytes}}), flush=True)
 
 
 def drafter_block_main(args):
@@ -437,6 +516,11 @@ def main():
                     help="time small_m_qmm on a 27B-class layer instead of the step")
     ap.add_argument("--rows", type=int, default=8)
     ap.add_argument("--weight-bits", type=int, default=4, choices=(4, 8))
+    ap.add_argument("--sampling", default="",
+                    help="time verify_sample_accept alone on this workload's logits")
+    ap.add_argument("--top-p", type=float, default=1.0,
+                    help="with --sampling: every sequence a nucleus without top-k")
+    ap.add_argument("--temperature", type=float, default=1.0)
     ap.add_argument("--drafter-block", action="store_true",
                     help="time block_attention on a drafter's block instead of the step")
     ap.add_argument("--window", type=int, default=4096)
@@ -453,6 +537,9 @@ def main():
               "the verify step's sharding across GPUs is a design note, not a run.",
               file=sys.stderr)
         sys.exit(2)
+    if args.sampling:
+        sampling_main(args)
+        return
     if args.drafter_block:
         drafter_block_main(args)
         return
