@@ -1825,11 +1825,12 @@ __device__ void nuc_crossing(NucShared& ns, int nb, bool rev, double base, doubl
     ns.cnt_before = an;
 }
 
-// One pass over row r's values y = v / T, f(y) per id (ids past the vocabulary skipped).
+// One pass over row r's values y = v / T, f(y) per id whose v lies in [vlo, vhi] (ids past
+// the vocabulary skipped; the interval spares the division for ids that cannot matter).
 // Target rows carry their penalties (base counts plus the drafts before the row).
 template <bool VEC, bool MAP, class F>
 __device__ void nuc_pass(const SampArgs& a, const SeqMode& m, const RowRef& r, int b,
-                         const int* drafts, F&& f) {
+                         const int* drafts, float vlo, float vhi, F&& f) {
     constexpr int kB = 4;                           // chunks whose loads are in flight together
     const bool pen = r.kind == 0 && (m.pp != 0.f || m.fp != 0.f);
     const int32_t* crow = a.counts ? a.counts + (size_t)b * a.vocab : nullptr;
@@ -1855,7 +1856,8 @@ __device__ void nuc_pass(const SampArgs& a, const SeqMode& m, const RowRef& r, i
             }
 #pragma unroll
             for (int e = 0; e < kEpt; ++e)
-                if (elem_id(base, e) < a.vocab) f(__fdiv_rn(x[u][e], m.temp));
+                if (elem_id(base, e) < a.vocab && x[u][e] >= vlo && x[u][e] <= vhi)
+                    f(__fdiv_rn(x[u][e], m.temp));
         }
     }
 }
@@ -1915,7 +1917,7 @@ __device__ void nucleus_row(const SampArgs& a, const SeqMode& m, int b, int q, N
     // ---- pass 1: mass per bucket of (ymax - y)
     {
         NucRun run;
-        nuc_pass<VEC, MAP>(a, m, r, b, ns.drafts, [&](float y) {
+        nuc_pass<VEC, MAP>(a, m, r, b, ns.drafts, kNegInf, __builtin_inff(), [&](float y) {
             run.add(ns, nuc_bucket(y, ymax), nuc_mass(y, ymax));
         });
         run.flush(ns);
@@ -1939,8 +1941,20 @@ __device__ void nucleus_row(const SampArgs& a, const SeqMode& m, int b, int q, N
     __syncthreads();
     // ---- pass 2: the crossing bucket's ids (when they fit the list)
     const bool listed = nb <= kNucList;
+    // values v whose y = v / T can fall in bucket bstar, with a wide margin (the bucket test
+    // itself decides): y in [ymax - (bstar + 1) / 16, ymax - bstar / 16], widened by 1e-3 of
+    // the magnitudes, and v = y T within 1e-5 relative
+    float vlo = kNegInf, vhi = __builtin_inff();
+    {
+        const double slack = 1e-3 * (fabs((double)ymax) + (bstar + 1) / 16.0) + 1e-30;
+        const double ylo = (double)ymax - (bstar + 1) / 16.0 - slack;
+        const double yhi = (double)ymax - bstar / 16.0 + slack;
+        const double t = (double)m.temp;
+        if (bstar < kNucBuckets - 1) vlo = (float)fmin(ylo * t * (1 - 1e-5), ylo * t * (1 + 1e-5));
+        vhi = (float)fmax(yhi * t * (1 - 1e-5), yhi * t * (1 + 1e-5));
+    }
     if (listed) {
-        nuc_pass<VEC, MAP>(a, m, r, b, ns.drafts, [&](float y) {
+        nuc_pass<VEC, MAP>(a, m, r, b, ns.drafts, vlo, vhi, [&](float y) {
             if (nuc_bucket(y, ymax) == bstar) {
                 const int p = atomicAdd(&ns.cnt, 1);
                 if (p < kNucList) {
@@ -1971,7 +1985,7 @@ __device__ void nucleus_row(const SampArgs& a, const SeqMode& m, int b, int q, N
         if (listed) {
             for (int i = tid; i < nl; i += kThreads) visit(ns.lkey[i], ns.lw[i], run);
         } else {
-            nuc_pass<VEC, MAP>(a, m, r, b, ns.drafts, [&](float y) {
+            nuc_pass<VEC, MAP>(a, m, r, b, ns.drafts, vlo, vhi, [&](float y) {
                 if (nuc_bucket(y, ymax) == bstar) visit(ord_key(y), nuc_mass(y, ymax), run);
             });
         }
