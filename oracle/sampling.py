@@ -16,6 +16,8 @@ Sources on the pages (mlx-dspark):
   * sampled acceptance: release v0.0.2 "Highlights" (sample the draft, accept with
     probability min(1, p/q), resample the residual on rejection; output distribution equals
     the target's; default greedy);
+  * one-hot proposals (prompt-lookup drafts carry no draft distribution; sampling stays an
+    exact target sample): Changelog [0.2.0] "Added" (--mode lookup);
   * greedy acceptance: Changelog [0.2.0] "Decode-path performance" (accepted-prefix length
     as a cumulative product of positionwise matches); greedy output equals plain greedy
     decoding (release v0.0.2).
@@ -26,22 +28,38 @@ Readings where the pages are silent (each also listed in the design notes):
   R7  argmax ties go to the lowest token id.
   R8  top-k is a threshold: theta = k-th largest z (sorted by z desc, id asc); every id with
       z >= theta is kept, so ties at theta are all kept.  R9  top-k selects on z, before /T.
-  R10 top-p acts on the temperature-scaled probabilities renormalized over the top-k set:
+  R10 probabilities are the softmax of z / T over the kept set, evaluated in fp64 from the
+      fp32 z as exp((z_j - z_max) / T) (no rounding of z / T to fp32); top-p acts on them:
       sort by P desc (id asc), m* = first m whose cumulative sum reaches top_p, cutoff
       c = P_(m*), keep every id with P >= c (the crossing id and ties at it are kept).
   R11 greedy emits the accepted drafts and then the target argmax of the first unmatched
       row (or of the last row when every draft matched).
   R12 a draft whose p and q are both 0 is rejected.  R13 if the residual max(0, p-q) sums
       to 0 the draw falls back to p.
-  R14 categorical draws are exponential races: argmax_j r_j / E_j, E_j = -ln U'_j.
+  R14 categorical draws are exponential races: argmax_j r_j / E_j, E_j = -ln U_j with the
+      64-bit open-interval uniforms of oracle/philox.py; ties go to the lowest id.
   R15 randoms are keyed (seed, sequence b, absolute position, tag); row i of sequence b
       decides the token at position positions[b] + i.
   R16 logprobs are of the raw target logits (before penalties, temperature, truncation).
 
-Precision: penalized logits z and y = z / T are fp32 (IEEE, one rounding per operation);
-probabilities, cumulative sums, acceptance tests and races are fp64; logprobs fp64.
+Precision: penalized logits z are fp32 (IEEE, one rounding per operation); probabilities,
+cumulative sums, acceptance tests and races are fp64; logprobs fp64.
+
+Exception accounting. The GPU takes the same decisions in its own arithmetic; a decision
+whose fp64 value lies within the GPU's error bound of the boundary can legitimately go
+either way. Every such decision is an exception point with a list of admissible outcomes;
+`enumerate_outcomes` follows every combination, so a flagged sequence is still checked: the
+GPU's result must equal one of them. The error bounds (ERROR MODEL below) state how far the
+GPU's values may sit from the fp64 ones, per precision class of a row:
+  "kept"  a row truncated by top-k: the GPU evaluates the same fp64 formulas over the kept
+          list (only the summation order differs);
+  "full"  a full-vocabulary softmax row: per-id exp2 of fp32 exponents, fp32 chunk sums
+          merged in fp64;
+  "nuc"   a nucleus over the whole vocabulary (top_p < 1, no top-k): fp64 exponents split
+          into integer and fraction, fp32 exp2 of the fraction, fp64 sums;
+  "onehot" a one-hot proposal (q(d) = 1 exactly).
 """
-from dataclasses import dataclass
+from dataclasses import dataclass, field
 
 import numpy as np
 
@@ -61,11 +79,31 @@ class RowParams:
     top_logprobs: int = 0
 
 
-# Exception margins (fp64) inside which the GPU's fp32 arithmetic may legitimately decide
-# the other way; sequences touching one are counted rather than compared.
-ACCEPT_MARGIN = 1e-5     # E1: |u - p/q|
-NUCLEUS_MARGIN = 1e-5    # E2: |C_m - top_p| at the crossing
-RACE_MARGIN = 1e-5       # E3: (best - second) / best of the race keys
+# ----------------------------------------------------------------------------- ERROR MODEL
+# Relative error bounds of the GPU's probabilities against the fp64 values (per class), and
+# of its race keys; absolute bounds of its cumulative nucleus sums. Stated generously (about
+# ten times what the arithmetic gives) and used with a factor 2 below.
+REL_KEPT = 1e-12          # fp64 over <= 256 kept ids
+REL_FULL_BASE = 2e-6      # full rows: normalizer (fp32 chunk sums) + exp2 + roundings
+REL_FULL_PER_LOG2 = 2.4e-7  # ... + per unit of |exponent| in log2 units (its fp32 rounding)
+REL_NUC = 2e-6            # whole-vocabulary nuclei: fraction exp2 + fp64 sums
+REL_RACE_KEY = 1e-6       # fp32 -log2 U, reciprocal and product of a key
+CUM_KEPT = 1e-12          # nucleus cumulative sums over a kept list (fp64)
+CUM_NUC = 1e-6            # nucleus cumulative sums over the whole vocabulary
+SAFETY = 2.0
+
+
+def rel_error(cls, z, z_max, temperature):
+    """Per-id relative error bound of the GPU's probability in a row of class `cls`."""
+    if cls == "kept":
+        return np.full(z.shape, REL_KEPT)
+    if cls == "nuc":
+        return np.full(z.shape, REL_NUC)
+    if cls == "onehot":
+        return np.zeros(z.shape)
+    t = np.abs((z.astype(np.float64) - float(z_max)) / float(temperature)) / np.log(2.0)
+    t = np.where(np.isfinite(t), t, 0.0)
+    return REL_FULL_BASE + REL_FULL_PER_LOG2 * t
 
 
 # ----------------------------------------------------------------------------- penalties
@@ -109,66 +147,113 @@ class Truncated:
     theta: float             # top-k threshold on z (-inf when top-k is off)
     kept_topk: int           # |S|
     kept_nucleus: int        # |S'|
-    nucleus_margin: float    # min distance of the crossing cumulative sums to top_p (inf if off)
+    cls: str                 # precision class of the GPU's values for this row
+    rel_err: np.ndarray      # per-id relative error bound of the GPU's probability
+    m_star: int = -1         # nucleus crossing rank used (-1: no nucleus)
+    m_options: tuple = ()    # crossing ranks within the GPU's error of the boundary
 
 
-def truncated_distribution(z, temperature, top_k, top_p):
-    """Temperature softmax of z truncated by top-k then top-p (R8-R10), fp64 result."""
+def row_class(vocab, top_k, top_p):
+    if 0 < top_k < vocab:
+        return "kept"
+    return "nuc" if top_p < 1.0 else "full"
+
+
+def truncated_distribution(z, temperature, top_k, top_p, m_star=None):
+    """Softmax of z / T truncated by top-k then top-p (R8-R10), fp64 result. `m_star` forces
+    the nucleus crossing rank (an admissible alternative of an exception point)."""
     z = np.asarray(z, dtype=np.float32)
     vocab = z.size
-    if 0 < top_k < vocab:
+    cls = row_class(vocab, top_k, top_p)
+    if cls == "kept":
         theta = np.float32(z[order_desc(z)[top_k - 1]])
         kept = z >= theta
     else:
         theta = np.float32(-np.inf)
         kept = np.ones(vocab, dtype=bool)
     kept_topk = int(np.count_nonzero(kept))
-    y = (z / np.float32(temperature)).astype(np.float32)          # IEEE fp32 division
-    y64 = y.astype(np.float64)
-    w = np.where(kept, np.exp(y64 - y64[kept].max()), 0.0)
-    probs = w / w.sum()
-    margin = np.inf
-    if top_p < 1.0:
+    z64 = z.astype(np.float64)
+    zmax = z64[kept].max() if kept.any() else -np.inf
+    with np.errstate(invalid="ignore", over="ignore"):
+        w = np.where(kept, np.exp((z64 - zmax) / float(np.float32(temperature))), 0.0)
+    w = np.where(np.isnan(w), 0.0, w)
+    tot = w.sum()
+    probs = w / tot if tot > 0 else w
+    used_m, options = -1, ()
+    if top_p < 1.0 and tot > 0:
         ids = np.flatnonzero(kept)
         ranked = ids[order_desc(probs[ids])]
         cum = np.cumsum(probs[ranked])
         reach = np.flatnonzero(cum >= top_p)
-        m_star = int(reach[0]) if reach.size else ranked.size - 1
-        cutoff = probs[ranked[m_star]]
-        margin = abs(cum[m_star] - top_p)
-        if m_star > 0:
-            margin = min(margin, abs(cum[m_star - 1] - top_p))
+        m_def = int(reach[0]) if reach.size else ranked.size - 1
+        eps = SAFETY * (CUM_KEPT if cls == "kept" else CUM_NUC)
+        opts = [m_def]
+        if reach.size and cum[m_def] - top_p <= eps and m_def + 1 < ranked.size:
+            opts.append(m_def + 1)          # the GPU may see C_m* just below top_p
+        if m_def > 0 and top_p - cum[m_def - 1] <= eps:
+            opts.append(m_def - 1)          # ... or C_(m*-1) already at top_p
+        options = tuple(opts) if len(opts) > 1 else ()
+        used_m = m_def if m_star is None else int(m_star)
+        cutoff = probs[ranked[used_m]]
         kept = kept & (probs >= cutoff)
         probs = np.where(kept, probs, 0.0)
         probs = probs / probs.sum()
-    return Truncated(probs, float(theta), kept_topk, int(np.count_nonzero(kept)), margin)
+    rel = rel_error(cls, z, zmax, temperature)
+    return Truncated(probs, float(theta), kept_topk, int(np.count_nonzero(kept)), cls, rel,
+                     used_m, options)
+
+
+def one_hot(d, vocab):
+    """A one-hot proposal at draft id d (prompt lookup): q(d) = 1, q = 0 elsewhere."""
+    probs = np.zeros(vocab)
+    if 0 <= d < vocab:
+        probs[d] = 1.0
+    return Truncated(probs, float("-inf"), vocab, 1, "onehot", np.zeros(vocab))
 
 
 # ----------------------------------------------------------------------------- race
-def race_keys(weights, u):
-    """Keys w_j / E_j of the exponential race (R14), E_j = -ln U'_j >= 0 for U' in (0, 1].
-    U' = 1 gives E = +0 and an infinite key (computed as 0 - ln U', so that the zero is
-    not negative); ids with w_j = 0 never win (key -inf)."""
+ANY = -2                  # a race outcome that admits any token (see race_candidates)
+MAX_CANDIDATES = 512
+
+
+def race_keys(weights, e):
+    """Keys w_j / E_j of the exponential race (R14); E_j > 0 always (the uniforms lie in
+    the open interval), ids with w_j = 0 never win (key -inf)."""
     weights = np.asarray(weights, dtype=np.float64)
-    e = 0.0 - np.log(np.asarray(u, dtype=np.float64))
+    e = np.asarray(e, dtype=np.float64)
     with np.errstate(divide="ignore", invalid="ignore"):
         return np.where(weights > 0, weights / e, -np.inf)
 
 
-def exponential_race(weights, seed, b, position):
-    """Categorical draw proportional to `weights` (R14): argmax_j w_j / E_j with
-    E_j = -ln U'_j, U' from the tag-1 stream of (seed, b, position); ties -> lowest id.
-    Returns (token, relative gap between the two best keys)."""
+def race_candidates(weights, delta, e, key_step):
+    """The race winner (largest key w / E, lowest id on ties) and every id whose key may
+    reach the winner's on the GPU: its weight may sit `delta` (absolute, per id) from the
+    fp64 one and its key a further `key_step` (relative) away. An id of weight 0 whose
+    delta is positive can thus be a candidate. More than MAX_CANDIDATES candidates (a
+    race on weights all within rounding of zero) admit any token (ANY)."""
     weights = np.asarray(weights, dtype=np.float64)
-    u = philox.race_uniforms(seed, b, position, np.arange(weights.size, dtype=np.uint64))
-    keys = race_keys(weights, u)
+    keys = race_keys(weights, e)
     tok = int(np.argmax(keys))
-    order = np.sort(keys)[::-1]
-    best, second = order[0], (order[1] if order.size > 1 else -np.inf)
-    # A key is +inf only when U' == 1 exactly (E = 0); both sides then break ties by id,
-    # so such a draw is exact and carries no margin.
-    gap = np.inf if (np.isinf(best) or best <= 0) else (best - second) / best
-    return tok, gap
+    if delta is None:
+        return tok, [tok]
+    w_lo = np.maximum(0.0, weights - SAFETY * delta)
+    w_hi = weights + SAFETY * delta
+    lo_best = w_lo[tok] / e[tok] * (1.0 - SAFETY * key_step)
+    hi = w_hi / e * (1.0 + SAFETY * key_step)
+    hi[tok] = -np.inf
+    others = np.flatnonzero((hi >= lo_best) & (w_hi > 0))
+    if others.size > MAX_CANDIDATES:
+        return tok, [tok, ANY]
+    return tok, [tok] + [int(j) for j in others]
+
+
+def exponential_race(weights, seed, b, position, delta=None, key_step=0.0):
+    """Categorical draw proportional to `weights` (R14): argmax_j w_j / E_j with E_j from
+    the tag-1 stream of (seed, b, position); ties -> lowest id. Returns (token, the ids the
+    GPU may pick given per-id weight errors `delta`; [token] when delta is None)."""
+    weights = np.asarray(weights, dtype=np.float64)
+    e = philox.race_exponentials(seed, b, position, np.arange(weights.size, dtype=np.uint64))
+    return race_candidates(weights, delta, e, key_step)
 
 
 def residual_distribution(p, q):
@@ -178,12 +263,36 @@ def residual_distribution(p, q):
     return p if resid.sum() == 0.0 else resid
 
 
+def key_step(cls):
+    """Relative error of the GPU's race key beyond that of its weight: fp32 -log2 U,
+    reciprocal and product for full rows and nuclei; fp64 for kept lists."""
+    return 1e-12 if cls == "kept" else REL_RACE_KEY
+
+
+def weight_delta(p, q=None):
+    """Absolute error bound of the GPU's race weights: p alone, or p - q (whose error is the
+    sum of both, however much they cancel)."""
+    d = p.rel_err * p.probs
+    return d if q is None else d + q.rel_err * q.probs
+
+
 # ----------------------------------------------------------------------------- logprobs
 def raw_logprobs(x):
     """log-softmax of the raw target logits in fp64 (R16)."""
     x = np.asarray(x, dtype=np.float64)
     m = x.max()
     return x - m - np.log(np.exp(x - m).sum())
+
+
+# ----------------------------------------------------------------------------- acceptance
+def accept_test(u, pd, qd, e_p, e_q):
+    """Accept the draft iff u q(d) < p(d) (u < min(1, p/q); p = q = 0 rejects, R12).
+    Returns (accepted, ambiguous): ambiguous when the GPU's p and q, each within its
+    relative error, could put u q(d) on the other side of p(d)."""
+    acc = u * qd < pd
+    slack = SAFETY * (e_p * pd + e_q * u * qd)
+    amb = (pd > 0 or qd > 0) and abs(u * qd - pd) <= slack
+    return bool(acc), bool(amb)
 
 
 # ----------------------------------------------------------------------------- one sequence
@@ -197,15 +306,35 @@ class SequenceResult:
     theta: np.ndarray       # [R] top-k threshold per target row (nan for greedy)
     kept_topk: np.ndarray   # [R]
     kept_nucleus: np.ndarray  # [R]
-    row_nucleus_margin: np.ndarray  # [R] E2 margin per target row (inf if n/a)
-    excepted: bool          # an E1/E2/E3 margin was hit on a row that decided the output
-    margins: dict           # the smallest margin of each class met on the used rows
+    points: list = field(default_factory=list)   # exception points met: (key, options)
+
+    @property
+    def excepted(self):
+        return bool(self.points)
+
+
+class _Decisions:
+    """Forced outcomes of exception points (for enumerate_outcomes) and the record of the
+    points met on the way."""
+
+    def __init__(self, forced=None):
+        self.forced = dict(forced or {})
+        self.points = []
+
+    def take(self, key, default, options):
+        """The outcome of decision `key`: the forced one if any, else `default`; the point
+        is recorded when more than one outcome is admissible."""
+        if len(options) > 1:
+            self.points.append((key, tuple(options)))
+        return self.forced.get(key, default)
 
 
 def verify_sequence(b, target_rows, draft_rows, drafts, base_counts, params, position,
-                    seed, n_top):
-    """Verify one sequence: R = K+1 target rows, K draft rows (or None if greedy),
-    K drafted tokens. Returns the emitted tokens and diagnostics."""
+                    seed, n_top, forced=None, one_hot_drafts=False):
+    """Verify one sequence: R = K+1 target rows, K draft rows (or None if greedy or one-hot),
+    K drafted tokens. Returns the emitted tokens and diagnostics. `forced` maps exception
+    points to chosen outcomes (see enumerate_outcomes)."""
+    dec = _Decisions(forced)
     target_rows = np.asarray(target_rows, dtype=np.float32)
     rows, vocab = target_rows.shape
     k = rows - 1
@@ -215,11 +344,18 @@ def verify_sequence(b, target_rows, draft_rows, drafts, base_counts, params, pos
     theta = np.full(rows, np.nan)
     kept_topk = np.zeros(rows, dtype=np.int64)
     kept_nucleus = np.zeros(rows, dtype=np.int64)
-    row_margin = np.full(rows, np.inf)
-    margins = {"accept": np.inf, "nucleus": np.inf, "race": np.inf}
 
     def valid(d):
         return 0 <= int(d) < vocab
+
+    def truncated(logits, kind, i):
+        tr = truncated_distribution(logits, params.temperature, params.top_k, params.top_p)
+        if tr.m_star >= 0:
+            m = dec.take(("nuc", kind, i), tr.m_star, tr.m_options or (tr.m_star,))
+            if m != tr.m_star:
+                tr = truncated_distribution(logits, params.temperature, params.top_k,
+                                            params.top_p, m_star=m)
+        return tr
 
     if params.temperature == 0.0:
         g = [greedy_token(z[i]) for i in range(rows)]
@@ -228,14 +364,14 @@ def verify_sequence(b, target_rows, draft_rows, drafts, base_counts, params, pos
             a += 1
         tokens = [int(d) for d in drafts[:a]] + [g[a]]
     else:
-        p = [truncated_distribution(z[i], params.temperature, params.top_k, params.top_p)
-             for i in range(rows)]
-        q = [None] + [truncated_distribution(draft_rows[t - 1], params.temperature,
-                                             params.top_k, params.top_p)
-                      for t in range(1, k + 1)]
+        p = [truncated(z[i], "p", i) for i in range(rows)]
+        if one_hot_drafts:
+            q = [None] + [one_hot(int(drafts[t - 1]), vocab) for t in range(1, k + 1)]
+        else:
+            q = [None] + [truncated(draft_rows[t - 1], "q", t) for t in range(1, k + 1)]
         for i in range(rows):
             theta[i], kept_topk[i] = p[i].theta, p[i].kept_topk
-            kept_nucleus[i], row_margin[i] = p[i].kept_nucleus, p[i].nucleus_margin
+            kept_nucleus[i] = p[i].kept_nucleus
         tokens = None
         a = k
         for t in range(1, k + 1):
@@ -244,23 +380,38 @@ def verify_sequence(b, target_rows, draft_rows, drafts, base_counts, params, pos
             d = int(drafts[t - 1])
             pd = p[t - 1].probs[d] if valid(d) else 0.0
             qd = q[t].probs[d] if valid(d) else 0.0
-            margins["nucleus"] = min(margins["nucleus"], p[t - 1].nucleus_margin,
-                                     q[t].nucleus_margin)
-            if qd > 0:
-                margins["accept"] = min(margins["accept"], abs(u - pd / qd))
-            if u * qd < pd:                                      # u < min(1, p/q)
+            e_p = p[t - 1].rel_err[d] if valid(d) else 0.0
+            e_q = q[t].rel_err[d] if valid(d) else 0.0
+            acc, amb = accept_test(u, pd, qd, e_p, e_q)
+            acc = dec.take(("acc", t), acc, (acc, not acc) if amb else (acc,))
+            if acc:
                 continue
-            tok, gap = exponential_race(residual_distribution(p[t - 1].probs, q[t].probs),
-                                        seed, b, pos)
-            margins["race"] = min(margins["race"], gap)
-            tokens = [int(x) for x in drafts[:t - 1]] + [tok]
+            resid = residual_distribution(p[t - 1].probs, q[t].probs)
+            step = key_step(p[t - 1].cls)
+            if resid is p[t - 1].probs:
+                # R13: the residual is zero everywhere and the draw falls back to p; the GPU's
+                # residual may instead hold rounding-level weights, a race on noise
+                tok, cand = exponential_race(resid, seed, b, pos, weight_delta(p[t - 1]), step)
+                if np.any(weight_delta(p[t - 1], q[t]) > 0):
+                    cand = cand + [ANY]
+            else:
+                delta = weight_delta(p[t - 1], q[t])
+                tok, cand = exponential_race(resid, seed, b, pos, delta, step)
+                if not np.any(resid > SAFETY * delta):
+                    # every residual weight may round to zero on the GPU: its fallback race
+                    # on p is admissible too
+                    _, fcand = exponential_race(p[t - 1].probs, seed, b, pos,
+                                                weight_delta(p[t - 1]), step)
+                    cand = cand + [c for c in fcand if c not in cand]
+            tok = dec.take(("race", t), tok, cand)
+            tokens = [int(x) for x in drafts[:t - 1]] + [int(tok)]
             a = t - 1
             break
         if tokens is None:
-            margins["nucleus"] = min(margins["nucleus"], p[k].nucleus_margin)
-            tok, gap = exponential_race(p[k].probs, seed, b, position + k)
-            margins["race"] = min(margins["race"], gap)
-            tokens = [int(x) for x in drafts[:k]] + [tok]
+            tok, cand = exponential_race(p[k].probs, seed, b, position + k,
+                                         weight_delta(p[k]), key_step(p[k].cls))
+            tok = dec.take(("race", k + 1), tok, cand)
+            tokens = [int(x) for x in drafts[:k]] + [int(tok)]
 
     lp_rows = [raw_logprobs(target_rows[i]) for i in range(len(tokens))]
     chosen = [float(lp_rows[i][tok]) for i, tok in enumerate(tokens)]
@@ -272,23 +423,46 @@ def verify_sequence(b, target_rows, draft_rows, drafts, base_counts, params, pos
             ids = order_desc(target_rows[i])[:n_top]
             top_ids[i, :ids.size] = ids
             top_vals[i, :ids.size] = lp[ids]
-    excepted = (margins["accept"] < ACCEPT_MARGIN or margins["nucleus"] < NUCLEUS_MARGIN
-                or margins["race"] < RACE_MARGIN)
     return SequenceResult(a, tokens, chosen, top_ids, top_vals, theta, kept_topk,
-                          kept_nucleus, row_margin, excepted, margins)
+                          kept_nucleus, dec.points)
+
+
+def enumerate_outcomes(run, limit=4096):
+    """Every result that some admissible combination of outcomes at the exception points
+    gives. `run(forced)` returns a result with `.points`; the first exception point not yet
+    forced is branched over each of its outcomes, recursively."""
+    out = []
+
+    def explore(forced):
+        res = run(forced)
+        free = [(key, opts) for key, opts in res.points if key not in forced]
+        if not free:
+            out.append(res)
+            if len(out) > limit:
+                raise RuntimeError("too many admissible outcomes")
+            return
+        key, opts = free[0]
+        for o in opts:
+            explore({**forced, key: o})
+
+    explore({})
+    return out
 
 
 # ----------------------------------------------------------------------------- the batch
 def verify_sample_accept(target_logits, draft_logits, draft_tokens, cu_rows, token_counts,
-                         params, positions, seed, max_top_logprobs=0):
+                         params, positions, seed, max_top_logprobs=0, one_hot_drafts=False,
+                         alternatives=True):
     """Batched verify acceptance with the same argument semantics as the library call.
 
     target_logits [total_rows, V] f32; draft_logits [total_rows - B, V] f32 or None;
     draft_tokens [total_rows - B] int; cu_rows [B+1]; token_counts [B, V] int or None;
     params: list of RowParams (one per sequence); positions [B] (absolute index of the token
-    that row 0 of the sequence decides); seed: 64-bit integer.
-    Returns a dict of numpy arrays shaped like the library's outputs, plus per-sequence
-    exception flags.
+    that row 0 of the sequence decides); seed: 64-bit integer. one_hot_drafts: the drafts
+    are one-hot proposals (draft_logits unused).
+    Returns a dict of numpy arrays shaped like the library's outputs (the fp64 decisions),
+    per-sequence exception flags, and for each flagged sequence the list of admissible
+    results (`alternatives[b]`, each a SequenceResult; None when not flagged).
     """
     target_logits = np.asarray(target_logits, dtype=np.float32)
     total_rows, vocab = target_logits.shape
@@ -302,9 +476,9 @@ def verify_sample_accept(target_logits, draft_logits, draft_tokens, cu_rows, tok
     theta = np.full(total_rows, np.nan)
     kept_topk = np.zeros(total_rows, dtype=np.int64)
     kept_nucleus = np.zeros(total_rows, dtype=np.int64)
-    row_margin = np.full(total_rows, np.inf)
     excepted = np.zeros(batch, dtype=bool)
-    margins = []
+    alts = [None] * batch
+    points = [None] * batch
     for b in range(batch):
         r0, r1 = int(cu_rows[b]), int(cu_rows[b + 1])
         d0 = r0 - b
@@ -312,12 +486,17 @@ def verify_sample_accept(target_logits, draft_logits, draft_tokens, cu_rows, tok
         prm = params[b]
         drafts = np.asarray(draft_tokens[d0:d0 + k]) if k else np.zeros(0, np.int64)
         drows = None
-        if prm.temperature > 0 and k:
+        if prm.temperature > 0 and k and not one_hot_drafts:
             drows = np.asarray(draft_logits[d0:d0 + k], dtype=np.float32)
         counts = None if token_counts is None else token_counts[b]
         n_req = min(n_top, int(prm.top_logprobs))
-        res = verify_sequence(b, target_logits[r0:r1], drows, drafts, counts, prm,
-                              int(positions[b]), seed, n_req)
+
+        def run(forced, b=b, r0=r0, r1=r1, drows=drows, drafts=drafts, counts=counts,
+                prm=prm, n_req=n_req):
+            return verify_sequence(b, target_logits[r0:r1], drows, drafts, counts, prm,
+                                   int(positions[b]), seed, n_req, forced, one_hot_drafts)
+
+        res = run({})
         accepted[b] = res.accepted
         for i, tok in enumerate(res.tokens):
             out_tokens[r0 + i] = tok
@@ -329,13 +508,14 @@ def verify_sample_accept(target_logits, draft_logits, draft_tokens, cu_rows, tok
         theta[r0:r1] = res.theta
         kept_topk[r0:r1] = res.kept_topk
         kept_nucleus[r0:r1] = res.kept_nucleus
-        row_margin[r0:r1] = res.row_nucleus_margin
         excepted[b] = res.excepted
-        margins.append(res.margins)
+        points[b] = res.points
+        if res.excepted and alternatives:
+            alts[b] = enumerate_outcomes(run)
     return {"accepted_len": accepted, "out_tokens": out_tokens,
             "chosen_logprob": chosen_lp, "top_lp_ids": top_ids, "top_lp_vals": top_vals,
             "topk_threshold": theta, "kept_topk": kept_topk, "kept_nucleus": kept_nucleus,
-            "row_nucleus_margin": row_margin, "excepted": excepted, "margins": margins}
+            "excepted": excepted, "alternatives": alts, "points": points}
 
 
 # ----------------------------------------------------------------------------- draft proposals

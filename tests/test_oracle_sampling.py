@@ -13,15 +13,17 @@ mathematics rather than against the oracle's own formulas:
   * a planted mistake in the residual is caught by the same chi-square;
   * logprob identities (Changelog [0.2.0]: raw target log-softmax).
 """
+import concurrent.futures
 import json
 import math
+import multiprocessing as mp
 import os
 
 import numpy as np
 import pytest
 from scipy import stats
 
-from oracle import sampling
+from oracle import philox, sampling
 from oracle.sampling import RowParams, truncated_distribution, verify_sample_accept
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -317,18 +319,145 @@ def test_exponential_race_is_categorical():
     assert _chi2_ok(toks, w / w.sum()) > 1e-3
 
 
-def test_race_uniform_one_gives_infinite_key():
-    """U' = 1 means E = -ln 1 = 0: the id's key is +inf and it wins over any finite key
-    (ties among such ids go to the lowest id); a zero weight still never wins."""
-    w = np.array([5.0, 0.5, 0.0, 0.25])
-    u = np.array([0.3, 1.0, 1.0, 1.0])
-    keys = sampling.race_keys(w, u)
-    assert np.isposinf(keys[1]) and np.isposinf(keys[3]) and np.isneginf(keys[2])
-    assert int(np.argmax(keys)) == 1
-    u2 = np.array([0.3, 0.99, 0.7, 0.5])          # all < 1: plain w / (-ln u)
-    np.testing.assert_array_equal(sampling.race_keys(w, u2),
-                                  np.where(w > 0, w / -np.log(u2), -np.inf))
-    assert int(np.argmax(sampling.race_keys(w, u2))) == 1
+def test_race_keys_are_finite_for_every_variate():
+    """E lies in [2^-65, 65 ln 2] (open-interval uniforms), so a positive weight always has
+    a finite positive key and a zero weight never wins, whatever the variate."""
+    m = 0xFFFFFFFF
+    e = philox.exponential64(np.array([0, m, m, 2 ** 31], np.uint64),
+                             np.array([0, m, 0, 0], np.uint64))
+    keys = sampling.race_keys(np.array([1.0, 1e-300, 0.0, 2.0]), e)
+    assert np.all(np.isfinite(keys[[0, 1, 3]])) and keys[2] == -np.inf
+    assert e.min() == 2.0 ** -65 and e.max() < 45.06
+
+
+def _dominant_draws(args):
+    lo, hi = args
+    w = np.full(151936, 1e-12)
+    w[777] = 1.0
+    return sum(int(sampling.exponential_race(w, 42, 0, p)[0] != 777) for p in range(lo, hi))
+
+
+def test_dominant_weight_at_full_vocabulary():
+    """V = 151936, one id of weight 1, every other 1e-12: the exact chance that the draw
+    leaves the dominant id is sum_j w_j / sum w ~ 1.5e-7 per draw, so in 20000 draws the
+    count must be 0 (binomial, P(0) ~ 0.997). A uniform that can reach 1 (an infinite key
+    for whichever id draws it) would leave it in ~0.9% of draws (V 2^-24), ~180 times."""
+    n, parts = 20000, 16
+    step = n // parts
+    with concurrent.futures.ProcessPoolExecutor(max_workers=min(8, os.cpu_count() or 1),
+                                                mp_context=mp.get_context("fork")) as ex:
+        bad = sum(ex.map(_dominant_draws, [(i * step, (i + 1) * step) for i in range(parts)]))
+    assert bad == 0
+
+
+# ----------------------------------------------------------------------------- exception points
+def test_accept_margin_pins():
+    """E1: u q(d) within the GPU's relative error of p(d) is ambiguous; clearly apart is
+    not. Here e_p = e_q = 2e-6 (full rows) and SAFETY = 2: slack ~ 8e-6 p."""
+    p, q = 0.4, 0.5
+    u_edge = p / q
+    for rel, amb in [(5e-7, True), (-5e-7, True), (3e-6, True), (-1e-3, False),
+                     (1e-3, False), (2e-5, False)]:
+        u = u_edge * (1 + rel)
+        acc, a = sampling.accept_test(u, p, q, 2e-6, 2e-6)
+        assert acc == (u * q < p)
+        assert a == amb, (rel, a)
+    # kept-list rows (fp64 on the GPU): only rounding-level distances are ambiguous
+    assert sampling.accept_test(u_edge * (1 + 1e-13), p, q, 1e-12, 1e-12)[1]
+    assert not sampling.accept_test(u_edge * (1 + 1e-9), p, q, 1e-12, 1e-12)[1]
+    # p = q = 0 rejects, unambiguously (R12)
+    assert sampling.accept_test(0.3, 0.0, 0.0, 2e-6, 2e-6) == (False, False)
+
+
+def _nucleus_row(cum_at_cross, top_p, v=64):
+    """fp32 logits whose sorted probabilities put the cumulative mass after the first two
+    ids at `cum_at_cross`; T = 1. Returns z."""
+    rest = (1.0 - cum_at_cross) / (v - 2)
+    pr = np.array([cum_at_cross * 0.6, cum_at_cross * 0.4] + [rest] * (v - 2))
+    return np.log(pr).astype(np.float32)
+
+
+def test_nucleus_margin_pins():
+    """E2: the crossing cumulative sum within the GPU's error of top_p offers the
+    neighbouring crossing rank; a distance of 1e-3 does not. Whole-vocabulary nucleus rows
+    (GPU error 1e-6, x2) and top-k rows (fp64 kept lists, 1e-12, x2)."""
+    for d, opts in [(5e-7, True), (1.5e-6, True), (1e-3, False), (-1e-3, False)]:
+        z = _nucleus_row(0.5, 0.5)
+        c2 = float(np.cumsum(np.sort(np.exp(z.astype(np.float64)) /
+                                     np.exp(z.astype(np.float64)).sum())[::-1])[1])
+        top_p = np.float32(c2 - d)
+        tr = truncated_distribution(z, 1.0, 0, float(top_p))
+        assert tr.cls == "nuc"
+        assert bool(tr.m_options) == opts, (d, tr.m_options)
+    z = _nucleus_row(0.5, 0.5)
+    zk = np.concatenate([z, np.full(8, -30, np.float32)])
+    pr = np.exp(zk.astype(np.float64) - zk.max())
+    top = np.sort(pr[pr > np.exp(-29.0)])[::-1]
+    for d, opts in [(1e-13, True), (1e-9, False)]:
+        c = float(np.cumsum(top / top.sum())[1])
+        tr = truncated_distribution(zk, 1.0, 64, c - d)
+        assert tr.cls == "kept" and bool(tr.m_options) == opts, (d, tr.m_options)
+
+
+def test_race_margin_pins():
+    """E3: two keys within the GPU's key error are both candidates; 1e-3 apart, only the
+    winner. Explicit exponentials, so the keys are known."""
+    e = np.array([1.0, 1.0, 2.0])
+    w_tie = np.array([1.0, 1.0 - 1e-7, 0.1])
+    tok, cand = sampling.race_candidates(w_tie, 2e-6 * w_tie, e, 1e-6)
+    assert tok == 0 and sorted(cand) == [0, 1]
+    w_far = np.array([1.0, 1.0 - 1e-3, 0.1])
+    tok, cand = sampling.race_candidates(w_far, 2e-6 * w_far, e, 1e-6)
+    assert tok == 0 and cand == [0]
+    # a zero-weight id whose GPU weight may be positive competes only through its bound
+    w0 = np.array([1e-6, 0.0])
+    tok, cand = sampling.race_candidates(w0, np.array([0.0, 1e-6]), np.array([1.0, 0.5]), 0)
+    assert tok == 0 and cand == [0, 1]
+    tok, cand = sampling.race_candidates(w0, None, np.array([1.0, 0.5]), 0)
+    assert cand == [0]
+
+
+def test_enumerate_outcomes_follows_every_ambiguous_decision():
+    """A sequence whose first acceptance test sits on the boundary: both branches are
+    admissible results (accept: the second draft is tested too; reject: a residual draw)."""
+    rng = np.random.default_rng(30)
+    v = 16
+    target = _rows(rng, 3, v)
+    draft = (target[:2] + 0.5 * rng.standard_normal((2, v))).astype(np.float32)
+    prm = RowParams(temperature=1.0)
+    drafts = np.array([3, 5])
+    base = sampling.verify_sequence(0, target, draft, drafts, None, prm, 10, 7, 0)
+    forced_runs = []
+
+    def run(forced):
+        forced_runs.append(dict(forced))
+        res = sampling.verify_sequence(0, target, draft, drafts, None, prm, 10, 7, 0, forced)
+        res.points = [(("acc", 1), (True, False))] + res.points
+        return res
+    outs = sampling.enumerate_outcomes(run)
+    accs = sorted({o.accepted for o in outs})
+    assert accs[0] == 0 and accs[-1] >= 1
+    assert any(o.tokens == base.tokens for o in outs)
+
+
+def test_one_hot_proposals_accept_and_resample():
+    """One-hot proposals (prompt lookup, Changelog [0.2.0]): P(accept) = p(d), and after a
+    rejection the token follows p without d (the residual max(0, p - delta_d))."""
+    rng = np.random.default_rng(31)
+    v, n = 8, 12000
+    target = _rows(rng, 2, v)
+    tl = np.tile(target, (n, 1))
+    cu = np.arange(0, 2 * n + 1, 2)
+    out = verify_sample_accept(tl, None, np.full(n, 3, np.int32), cu, None,
+                               [RowParams(temperature=1.0)] * n, np.arange(n) * 2, 0,
+                               one_hot_drafts=True)
+    p = truncated_distribution(target[0], 1.0, 0, 1.0).probs
+    hits = int(np.count_nonzero(out["accepted_len"] == 1))
+    assert stats.binomtest(hits, n, p[3]).pvalue > 1e-3
+    rej = out["accepted_len"] == 0
+    resid = p.copy()
+    resid[3] = 0.0
+    assert _chi2_ok(out["out_tokens"][0::2][rej], resid / resid.sum()) > 1e-3
 
 
 def test_planted_residual_mistake_is_caught(monkeypatch):
