@@ -80,11 +80,11 @@ typedef enum vsa_dtype {
 #define VSA_DEVERR_TIE_OVERFLOW   0x10u /* more ids tie at a top-k threshold than the
                                            candidate capacity holds: the kept set is
                                            truncated to the capacity */
-#define VSA_DEVERR_WAIT_TIMEOUT   0x20u /* a workgroup waited about 0.2 s for its
-                                           sequence's acceptance result (the call's
-                                           workgroups could not all run at once, e.g.
-                                           other work held the GPU): the token drawn for
-                                           that sequence is unreliable */
+#define VSA_DEVERR_WAIT_TIMEOUT   0x20u /* a workgroup gave up waiting for its sequence's
+                                           statistics (the call's workgroups did not all
+                                           run at once, e.g. other work held the GPU) and
+                                           handed its share of the draw to another: the
+                                           outputs are still exact, the call was slower */
 #define VSA_DEVERR_DRAFT_MAP      0x40u /* a t2d entry outside [-1, draft_vocab): read as
                                            "no draft id" (probability 0) */
 
@@ -228,14 +228,17 @@ vsa_status verify_attention_kvq(const void* q, const uint8_t* k_codes, const voi
  *         c_i = token_counts[b] + the counts of drafts d_1..d_i
  *   greedy (T == 0): a = length of the longest prefix with d_{t} = argmax z_{t-1} (lowest
  *         id on ties); emit d_1..d_a and argmax z_a.
- *   sampled (T > 0): p_i = softmax(z_i / T) truncated to {z >= k-th largest z} (top-k)
- *         then to the smallest prefix by probability reaching top_p (ties kept), and
- *         renormalized; q_t likewise from draft row t (no penalties). For t = 1..K_b draw
- *         u (Philox4x32-10 keyed by seed, stream (b, position, tag 0)); accept d_t iff
- *         u * q_t(d_t) < p_{t-1}(d_t); at the first rejection emit a draw from
+ *   sampled (T > 0): p_i = softmax(z_i / T) (exp((z - z_max) / T) in fp64 from the fp32
+ *         z) truncated to {z >= k-th largest z} (top-k) then to the smallest prefix by z
+ *         (descending) whose probability reaches top_p (ties of z kept), and renormalized;
+ *         q_t likewise from draft row t (no penalties). For t = 1..K_b draw u
+ *         (Philox4x32-10 keyed by seed, counter (0, position, b, 0), words 0 and 1); accept
+ *         d_t iff u * q_t(d_t) < p_{t-1}(d_t); at the first rejection emit a draw from
  *         max(0, p_{t-1} - q_t) and stop; if all are accepted emit a draw from p_{K_b}.
- *         Draws are exponential races argmax_j w_j / E_j with E_j = -ln U'_j from the
- *         (b, position, tag 1) stream.
+ *         Draws are exponential races argmax_j w_j / E_j, E_j = -ln U_j, U_j from words
+ *         2 (j & 1) and 2 (j & 1) + 1 of counter (j >> 1, position, b, 1). Every uniform
+ *         is a 64-bit one on the open interval: U = (hi 2^32 + lo + 1/2) 2^-64, so no E is
+ *         0 or infinite and the draw is an exact sample up to the rounding of the weights.
  *   logprobs: raw log-softmax of x (no penalties, temperature or truncation).
  *
  *   target_logits  [total_rows, V] float32
@@ -264,9 +267,14 @@ vsa_status verify_attention_kvq(const void* q, const uint8_t* k_codes, const voi
  *                  each target row of a sampled sequence (0 for greedy sequences)
  * Limits: 1 <= V <= 524288; K_b <= 31; top_k <= 256; at most 256 ids may tie into one
  * top-k kept set (VSA_DEVERR_TIE_OVERFLOW beyond). A nucleus without top-k (top_p < 1 and
- * top_k 0 or >= V) keeps {j : z_j / T >= y*} over the whole vocabulary, y* found by a
+ * top_k 0 or >= V) keeps {j : z_j >= z*} over the whole vocabulary, z* found by a
  * weighted selection rather than a sort; it runs in the truncation pipeline, so a call
  * with such a sequence and max_top_k = 0 sets VSA_DEVERR_PARAMS for it (decoded greedily).
+ * A call with max_top_k = 0 and max_top_logprobs = 0 runs as one kernel whose workgroups
+ * wait for each other (it is launched that way only when they all fit on the device at
+ * once); a workgroup that waits longer than VSA_FUSED_WAIT_US microseconds (environment,
+ * default 2000) hands its share of the draw to another one and sets
+ * VSA_DEVERR_WAIT_TIMEOUT. The outputs stay exact; only the call is slower.
  * ------------------------------------------------------------------------------------ */
 size_t verify_sample_accept_workspace_size(int B, int total_rows, int V, int max_rows_per_seq,
                                            int max_top_k, int max_top_logprobs);
@@ -314,6 +322,23 @@ vsa_status verify_sample_accept_reduced_draft(
     int32_t* accepted_len, int32_t* out_tokens, float* chosen_logprob, float* top_lp_vals,
     int32_t* top_lp_ids, float* diag_threshold, int32_t* diag_kept, void* workspace,
     size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * verify_sample_accept_onehot
+ * verify_sample_accept for one-hot proposals (Changelog [0.2.0] "Added": --mode lookup,
+ * prompt-lookup drafts with no draft distribution; temperature > 0 through one-hot-proposal
+ * speculative sampling, still an exact target sample): q_t = 1 at d_t and 0 elsewhere
+ * (truncation leaves it so). Draft t is accepted iff u < p_{t-1}(d_t); after a rejection
+ * the draw is from max(0, p_{t-1} - q_t), i.e. p_{t-1} without d_t. No draft logits are
+ * read. Arguments, outputs, workspace size query and limits as verify_sample_accept.
+ * ------------------------------------------------------------------------------------ */
+vsa_status verify_sample_accept_onehot(
+    const float* target_logits, const int32_t* draft_tokens, const int32_t* cu_rows,
+    const int32_t* token_counts, const vsa_row_params* params, const int32_t* positions,
+    uint64_t seed, int B, int total_rows, int V, int max_rows_per_seq, int max_top_k,
+    int max_top_logprobs, int32_t* accepted_len, int32_t* out_tokens, float* chosen_logprob,
+    float* top_lp_vals, int32_t* top_lp_ids, float* diag_threshold, int32_t* diag_kept,
+    void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------
  * small_m_qmm

@@ -30,8 +30,9 @@ Readings where the pages are silent (each also listed in the design notes):
       z >= theta is kept, so ties at theta are all kept.  R9  top-k selects on z, before /T.
   R10 probabilities are the softmax of z / T over the kept set, evaluated in fp64 from the
       fp32 z as exp((z_j - z_max) / T) (no rounding of z / T to fp32); top-p acts on them:
-      sort by P desc (id asc), m* = first m whose cumulative sum reaches top_p, cutoff
-      c = P_(m*), keep every id with P >= c (the crossing id and ties at it are kept).
+      sort by z desc (id asc), which is the order of P, m* = first m whose cumulative sum of
+      P reaches top_p, keep every id whose z is at least the crossing id's (the crossing id
+      and ties with it are kept; ties are ties of z).
   R11 greedy emits the accepted drafts and then the target argmax of the first unmatched
       row (or of the last row when every draft matched).
   R12 a draft whose p and q are both 0 is rejected.  R13 if the residual max(0, p-q) sums
@@ -182,7 +183,7 @@ def truncated_distribution(z, temperature, top_k, top_p, m_star=None):
     used_m, options = -1, ()
     if top_p < 1.0 and tot > 0:
         ids = np.flatnonzero(kept)
-        ranked = ids[order_desc(probs[ids])]
+        ranked = ids[order_desc(z[ids])]
         cum = np.cumsum(probs[ranked])
         reach = np.flatnonzero(cum >= top_p)
         m_def = int(reach[0]) if reach.size else ranked.size - 1
@@ -194,8 +195,7 @@ def truncated_distribution(z, temperature, top_k, top_p, m_star=None):
             opts.append(m_def - 1)          # ... or C_(m*-1) already at top_p
         options = tuple(opts) if len(opts) > 1 else ()
         used_m = m_def if m_star is None else int(m_star)
-        cutoff = probs[ranked[used_m]]
-        kept = kept & (probs >= cutoff)
+        kept = kept & (z >= z[ranked[used_m]])
         probs = np.where(kept, probs, 0.0)
         probs = probs / probs.sum()
     rel = rel_error(cls, z, zmax, temperature)
@@ -305,12 +305,13 @@ class SequenceResult:
     top_vals: np.ndarray    # [R, n] their raw logprobs
     theta: np.ndarray       # [R] top-k threshold per target row (nan for greedy)
     kept_topk: np.ndarray   # [R]
-    kept_nucleus: np.ndarray  # [R]
+    kept_nucleus: np.ndarray  # [R] (the fp64 decision)
+    kept_options: list = field(default_factory=list)  # [R] admissible |S'| per target row
     points: list = field(default_factory=list)   # exception points met: (key, options)
 
     @property
     def excepted(self):
-        return bool(self.points)
+        return bool(self.points) or any(len(o) > 1 for o in self.kept_options)
 
 
 class _Decisions:
@@ -329,11 +330,38 @@ class _Decisions:
         return self.forced.get(key, default)
 
 
+def truncated_versions(logits, params):
+    """The row's truncated distribution (first) and, when its nucleus crossing lies within
+    the GPU's error of top_p, the distribution at each admissible neighbouring crossing."""
+    tr = truncated_distribution(logits, params.temperature, params.top_k, params.top_p)
+    out = [tr]
+    for m in tr.m_options:
+        if m != tr.m_star:
+            out.append(truncated_distribution(logits, params.temperature, params.top_k,
+                                              params.top_p, m_star=m))
+    return out
+
+
+def _race_over(weights_fn, versions, e, step):
+    """Winner under the first version combination and the union of every combination's
+    candidates. weights_fn(v) -> (weights, delta) for one combination v."""
+    tok, cand = None, []
+    for v in versions:
+        w, delta = weights_fn(v)
+        t, c = race_candidates(w, delta, e, step)
+        if tok is None:
+            tok = t
+        cand += [x for x in c if x not in cand]
+    return tok, cand
+
+
 def verify_sequence(b, target_rows, draft_rows, drafts, base_counts, params, position,
                     seed, n_top, forced=None, one_hot_drafts=False):
     """Verify one sequence: R = K+1 target rows, K draft rows (or None if greedy or one-hot),
     K drafted tokens. Returns the emitted tokens and diagnostics. `forced` maps exception
-    points to chosen outcomes (see enumerate_outcomes)."""
+    points to chosen outcomes (see enumerate_outcomes). A nucleus row whose crossing is
+    within the GPU's error of top_p contributes its admissible versions: each decision that
+    uses the row is taken under every version, and only a disagreement is a point."""
     dec = _Decisions(forced)
     target_rows = np.asarray(target_rows, dtype=np.float32)
     rows, vocab = target_rows.shape
@@ -344,18 +372,10 @@ def verify_sequence(b, target_rows, draft_rows, drafts, base_counts, params, pos
     theta = np.full(rows, np.nan)
     kept_topk = np.zeros(rows, dtype=np.int64)
     kept_nucleus = np.zeros(rows, dtype=np.int64)
+    kept_options = [(0,)] * rows
 
     def valid(d):
         return 0 <= int(d) < vocab
-
-    def truncated(logits, kind, i):
-        tr = truncated_distribution(logits, params.temperature, params.top_k, params.top_p)
-        if tr.m_star >= 0:
-            m = dec.take(("nuc", kind, i), tr.m_star, tr.m_options or (tr.m_star,))
-            if m != tr.m_star:
-                tr = truncated_distribution(logits, params.temperature, params.top_k,
-                                            params.top_p, m_star=m)
-        return tr
 
     if params.temperature == 0.0:
         g = [greedy_token(z[i]) for i in range(rows)]
@@ -364,57 +384,73 @@ def verify_sequence(b, target_rows, draft_rows, drafts, base_counts, params, pos
             a += 1
         tokens = [int(d) for d in drafts[:a]] + [g[a]]
     else:
-        p = [truncated(z[i], "p", i) for i in range(rows)]
+        p = [truncated_versions(z[i], params) for i in range(rows)]
         if one_hot_drafts:
-            q = [None] + [one_hot(int(drafts[t - 1]), vocab) for t in range(1, k + 1)]
+            q = [None] + [[one_hot(int(drafts[t - 1]), vocab)] for t in range(1, k + 1)]
         else:
-            q = [None] + [truncated(draft_rows[t - 1], "q", t) for t in range(1, k + 1)]
+            q = [None] + [truncated_versions(draft_rows[t - 1], params)
+                          for t in range(1, k + 1)]
         for i in range(rows):
-            theta[i], kept_topk[i] = p[i].theta, p[i].kept_topk
-            kept_nucleus[i] = p[i].kept_nucleus
+            theta[i], kept_topk[i] = p[i][0].theta, p[i][0].kept_topk
+            kept_nucleus[i] = p[i][0].kept_nucleus
+            kept_options[i] = tuple(sorted({v.kept_nucleus for v in p[i]}))
         tokens = None
         a = k
         for t in range(1, k + 1):
             pos = position + t - 1
             u = philox.acceptance_uniform(seed, b, pos)
             d = int(drafts[t - 1])
-            pd = p[t - 1].probs[d] if valid(d) else 0.0
-            qd = q[t].probs[d] if valid(d) else 0.0
-            e_p = p[t - 1].rel_err[d] if valid(d) else 0.0
-            e_q = q[t].rel_err[d] if valid(d) else 0.0
-            acc, amb = accept_test(u, pd, qd, e_p, e_q)
-            acc = dec.take(("acc", t), acc, (acc, not acc) if amb else (acc,))
+            outcomes = []
+            for pv in p[t - 1]:
+                for qv in q[t]:
+                    pd = pv.probs[d] if valid(d) else 0.0
+                    qd = qv.probs[d] if valid(d) else 0.0
+                    e_p = pv.rel_err[d] if valid(d) else 0.0
+                    e_q = qv.rel_err[d] if valid(d) else 0.0
+                    acc, amb = accept_test(u, pd, qd, e_p, e_q)
+                    outcomes += [acc, not acc] if amb else [acc]
+            opts = [outcomes[0]] + [o for o in (True, False) if o in outcomes[1:] and
+                                    o != outcomes[0]]
+            acc = dec.take(("acc", t), outcomes[0], tuple(opts))
             if acc:
                 continue
-            resid = residual_distribution(p[t - 1].probs, q[t].probs)
-            step = key_step(p[t - 1].cls)
-            if resid is p[t - 1].probs:
-                # R13: the residual is zero everywhere and the draw falls back to p; the GPU's
-                # residual may instead hold rounding-level weights, a race on noise
-                tok, cand = exponential_race(resid, seed, b, pos, weight_delta(p[t - 1]), step)
-                if np.any(weight_delta(p[t - 1], q[t]) > 0):
-                    cand = cand + [ANY]
-            else:
-                delta = weight_delta(p[t - 1], q[t])
-                tok, cand = exponential_race(resid, seed, b, pos, delta, step)
-                if not np.any(resid > SAFETY * delta):
+            e = philox.race_exponentials(seed, b, pos, np.arange(vocab, dtype=np.uint64))
+            step = key_step(p[t - 1][0].cls)
+            combos = [(pv, qv) for pv in p[t - 1] for qv in q[t]]
+
+            def resid_race(pq):
+                pv, qv = pq
+                resid = residual_distribution(pv.probs, qv.probs)
+                if resid is pv.probs:
+                    return resid, weight_delta(pv)
+                return resid, weight_delta(pv, qv)
+            tok, cand = _race_over(resid_race, combos, e, step)
+            for pv, qv in combos:
+                resid = residual_distribution(pv.probs, qv.probs)
+                if resid is pv.probs:
+                    # R13: the residual is zero everywhere and the draw falls back to p; the
+                    # GPU's residual may instead hold rounding-level weights, a race on noise
+                    if np.any(weight_delta(pv, qv) > 0) and ANY not in cand:
+                        cand.append(ANY)
+                elif not np.any(resid > SAFETY * weight_delta(pv, qv)):
                     # every residual weight may round to zero on the GPU: its fallback race
                     # on p is admissible too
-                    _, fcand = exponential_race(p[t - 1].probs, seed, b, pos,
-                                                weight_delta(p[t - 1]), step)
-                    cand = cand + [c for c in fcand if c not in cand]
+                    _, fcand = race_candidates(pv.probs, weight_delta(pv), e, step)
+                    cand += [c for c in fcand if c not in cand]
             tok = dec.take(("race", t), tok, cand)
             tokens = [int(x) for x in drafts[:t - 1]] + [int(tok)]
             a = t - 1
             break
         if tokens is None:
-            tok, cand = exponential_race(p[k].probs, seed, b, position + k,
-                                         weight_delta(p[k]), key_step(p[k].cls))
+            e = philox.race_exponentials(seed, b, position + k, np.arange(vocab, dtype=np.uint64))
+            tok, cand = _race_over(lambda pv: (pv.probs, weight_delta(pv)), p[k], e,
+                                   key_step(p[k][0].cls))
             tok = dec.take(("race", k + 1), tok, cand)
             tokens = [int(x) for x in drafts[:k]] + [int(tok)]
 
     lp_rows = [raw_logprobs(target_rows[i]) for i in range(len(tokens))]
-    chosen = [float(lp_rows[i][tok]) for i, tok in enumerate(tokens)]
+    chosen = [float(lp_rows[i][tok]) if tok >= 0 else float("nan")
+              for i, tok in enumerate(tokens)]
     top_ids = np.full((rows, n_top), -1, dtype=np.int64)
     top_vals = np.zeros((rows, n_top), dtype=np.float64)
     if n_top:
@@ -424,7 +460,7 @@ def verify_sequence(b, target_rows, draft_rows, drafts, base_counts, params, pos
             top_ids[i, :ids.size] = ids
             top_vals[i, :ids.size] = lp[ids]
     return SequenceResult(a, tokens, chosen, top_ids, top_vals, theta, kept_topk,
-                          kept_nucleus, dec.points)
+                          kept_nucleus, kept_options, dec.points)
 
 
 def enumerate_outcomes(run, limit=4096):
@@ -479,6 +515,7 @@ def verify_sample_accept(target_logits, draft_logits, draft_tokens, cu_rows, tok
     excepted = np.zeros(batch, dtype=bool)
     alts = [None] * batch
     points = [None] * batch
+    kept_opts = [(0,)] * total_rows
     for b in range(batch):
         r0, r1 = int(cu_rows[b]), int(cu_rows[b + 1])
         d0 = r0 - b
@@ -510,12 +547,14 @@ def verify_sample_accept(target_logits, draft_logits, draft_tokens, cu_rows, tok
         kept_nucleus[r0:r1] = res.kept_nucleus
         excepted[b] = res.excepted
         points[b] = res.points
+        kept_opts[r0:r1] = res.kept_options
         if res.excepted and alternatives:
-            alts[b] = enumerate_outcomes(run)
+            alts[b] = enumerate_outcomes(run) if res.points else [res]
     return {"accepted_len": accepted, "out_tokens": out_tokens,
             "chosen_logprob": chosen_lp, "top_lp_ids": top_ids, "top_lp_vals": top_vals,
             "topk_threshold": theta, "kept_topk": kept_topk, "kept_nucleus": kept_nucleus,
-            "excepted": excepted, "alternatives": alts, "points": points}
+            "kept_options": kept_opts, "excepted": excepted, "alternatives": alts,
+            "points": points}
 
 
 # ----------------------------------------------------------------------------- draft proposals

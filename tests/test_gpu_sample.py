@@ -1,9 +1,9 @@
 """GPU parity of verify_sample_accept against the CPU oracle, through the C ABI.
 
-Bar: accepted lengths, emitted tokens, top-k thresholds and kept-set sizes bit-exact;
-sequences whose acceptance test, nucleus boundary or race lies within 1e-5 of flipping in
-the oracle's fp64 are counted, not compared, and must stay under 0.1% of a large batch;
-logprobs within 2e-5."""
+Bar: top-k thresholds and kept-set sizes bit-exact; accepted lengths and emitted tokens
+equal to the oracle's fp64 decisions, or, for a sequence with a decision inside the GPU's
+stated arithmetic error (the oracle's exception points), equal to one of the outcomes the
+oracle admits there; logprobs within 2e-5."""
 import numpy as np
 import pytest
 
@@ -22,14 +22,11 @@ def _log(msg):
     print(msg, flush=True)
 
 
-NUC_MARGIN = 1e-6      # E2 margin for nuclei without top-k (see compare_sample)
-
-
-def _run(w, seed=0, expect_err=0, nucleus_margin=None, max_top_k=None):
-    gpu = sample_gpu(w, seed=seed, max_top_k=max_top_k)
+def _run(w, seed=0, expect_err=0, max_top_k=None, onehot=False):
+    gpu = sample_gpu(w, seed=seed, max_top_k=max_top_k, onehot=onehot)
     assert gpu["err"] == expect_err, hex(gpu["err"])
-    ora = sample_oracle(w, seed=seed)
-    flagged = compare_sample(w, gpu, ora, nucleus_margin=nucleus_margin)
+    ora = sample_oracle(w, seed=seed, onehot=onehot)
+    flagged = compare_sample(w, gpu, ora)
     return gpu, ora, flagged
 
 
@@ -40,7 +37,7 @@ def test_workload_parity(name):
     w = wl.make_workload(name, with_kv=False)
     w.draft_tokens = q_distributed_drafts(w)
     _, _, flagged = _run(w)
-    assert flagged <= max(1, w.batch // 8)
+    _log(f"  flagged sequences (compared against admissible outcomes): {flagged}")
 
 
 def test_tiny_sampled_variant():
@@ -96,7 +93,8 @@ def test_large_mixed_batch_exception_rate():
     w = _mixed_batch(1200, 3000, 21)
     _log("mixed batch: 1200 sequences, V=3000")
     _, _, flagged = _run(w, seed=5)
-    assert flagged / w.batch < 1e-3 or flagged <= 1
+    _log(f"  flagged {flagged} of {w.batch}")
+    assert flagged / w.batch < 1e-3
 
 
 def test_odd_vocab_scalar_path_and_ties():
@@ -108,7 +106,7 @@ def test_odd_vocab_scalar_path_and_ties():
     w.draft_logits = rng.integers(-3, 4, size=w.draft_logits.shape).astype(np.float32)
     w.draft_tokens = q_distributed_drafts(w, seed=4)
     _log("odd vocab 37 with ties")
-    _run(w, seed=1, nucleus_margin=NUC_MARGIN)
+    _run(w, seed=1)
 
 
 def test_edge_cases_k0_and_small_vocab():
@@ -118,15 +116,15 @@ def test_edge_cases_k0_and_small_vocab():
             p.top_k = min(p.top_k, vocab)          # top_k = V: a nucleus without top-k
             p.top_logprobs = min(p.top_logprobs, 5)
         _log(f"small vocab {vocab}")
-        _run(w, seed=vocab, nucleus_margin=NUC_MARGIN)
+        _run(w, seed=vocab)
 
 
 def test_nucleus_mixed_batch():
     """600 sequences, V=3000, every parameter kind including nuclei without top-k."""
     w = _mixed_batch(600, 3000, 23, nucleus=True)
     _log("mixed batch with nuclei: 600 sequences, V=3000")
-    _, _, flagged = _run(w, seed=6, nucleus_margin=NUC_MARGIN)
-    assert flagged <= 6, flagged
+    _, _, flagged = _run(w, seed=6)
+    _log(f"  flagged {flagged} of {w.batch}")
 
 
 @pytest.mark.parametrize("temp,top_p,pen", [(0.7, 0.8, False), (0.5, 0.9, True),
@@ -143,9 +141,8 @@ def test_nucleus_without_top_k(temp, top_p, pen):
                                  logprobs=1)] * w.batch)
     w.draft_tokens = q_distributed_drafts(w)
     _log(f"nucleus without top-k: T={temp} top_p={top_p} penalties={pen}")
-    gpu, _, flagged = _run(w, seed=3, nucleus_margin=NUC_MARGIN, max_top_k=1)
-    if temp < 1.0:
-        assert flagged <= 1
+    gpu, _, flagged = _run(w, seed=3, max_top_k=1)
+    _log(f"  flagged {flagged} of {w.batch} (compared against admissible outcomes)")
     kept = gpu["diag_kept"]
     assert (kept[:, 0] == w.vocab).all() and (kept[:, 1] > 0).all()
 
@@ -160,7 +157,7 @@ def test_nucleus_without_top_k_heavy_ties():
     w = w.with_params([wl.Params(temperature=1.0, top_p=0.7)] * w.batch)
     w.draft_tokens = q_distributed_drafts(w)
     _log("nucleus without top-k: integer logits")
-    _run(w, seed=4, nucleus_margin=NUC_MARGIN, max_top_k=1)
+    _run(w, seed=4, max_top_k=1)
 
 
 def test_nucleus_without_top_k_needs_the_truncation_pipeline():
@@ -250,3 +247,98 @@ def test_chi_square_losslessness_on_gpu(cfg):
     sup1 = p1 > 0
     assert obs2[~sup1].sum() == 0
     assert stats.chisquare(obs2[sup1], p1[sup1] * sel.sum()).pvalue > 1e-4
+
+
+def test_wait_budget_zero_hands_the_draw_over(monkeypatch):
+    """VSA_FUSED_WAIT_US = 0: every workgroup of the fused kernel that is not the last of
+    its sequence gives up waiting at once and hands its chunk of the draw to the last
+    arriver. Every kernel still ends, the error word says so, and the outputs equal the
+    oracle's (the hand-over changes who races a chunk, not the race)."""
+    monkeypatch.setenv("VSA_FUSED_WAIT_US", "0")
+    for name in ("verify_b4k4_ctx8192", "tiny"):
+        w = wl.make_workload(name, with_kv=False)
+        if name == "tiny":
+            w = w.with_params([wl.Params(temperature=1.0)])
+        w.draft_tokens = q_distributed_drafts(w)
+        _log(f"wait budget 0: {name}")
+        gpu = sample_gpu(w, seed=9)
+        assert gpu["err"] & ~0x20 == 0, hex(gpu["err"])
+        compare_sample(w, gpu, sample_oracle(w, seed=9))
+        # the state the kernel returns to zero serves the next call as usual
+        monkeypatch.setenv("VSA_FUSED_WAIT_US", "2000")
+        again = sample_gpu(w, seed=9)
+        assert again["err"] == 0
+        assert np.array_equal(again["out_tokens"], gpu["out_tokens"])
+        monkeypatch.setenv("VSA_FUSED_WAIT_US", "0")
+
+
+@pytest.mark.parametrize("name", ["verify_b4k4_ctx8192", "qwen3_4b", "tiny"])
+def test_onehot_proposals_parity(name):
+    """One-hot proposals (prompt lookup): the same comparison against the oracle with
+    q_t = delta(d_t); fused kernel (no truncation) and truncation pipeline (qwen3_4b)."""
+    w = wl.make_workload(name, with_kv=False)
+    if name == "tiny":
+        w = w.with_params([wl.Params(temperature=1.0)])
+    if name == "verify_b4k4_ctx8192":
+        w = w.with_params([wl.Params(temperature=0.8, presence_penalty=0.5,
+                                     frequency_penalty=0.3, logprobs=1)] * w.batch)
+    w.draft_tokens = q_distributed_drafts(w)
+    _log(f"one-hot proposals: {name}")
+    _run(w, seed=2, onehot=True)
+
+
+def test_onehot_accept_rate_is_target_probability():
+    """P(accept d) = p(d) for a one-hot proposal (binomial over 20000 sequences), and the
+    token after a rejection never equals d (the residual is p without d)."""
+    from scipy import stats
+    from oracle import sampling
+    rng = np.random.default_rng(5)
+    v, n = 64, 20000
+    target = (1.2 * rng.standard_normal((2, v))).astype(np.float32)
+    d = int(np.argsort(target[0])[-3])
+    p0 = sampling.truncated_distribution(target[0], 1.0, 0, 1.0).probs
+    w = wl.Workload(name="onehot", batch=n, num_q_heads=1, num_kv_heads=1, head_dim=64,
+                    dtype=wl.BF16, vocab=v, ctx_lens=np.zeros(n, np.int32),
+                    cu_rows=np.arange(0, 2 * n + 1, 2, dtype=np.int32), s_max=0, q=None,
+                    k_cache=None, v_cache=None, target_logits=np.tile(target, (n, 1)),
+                    draft_logits=None, draft_tokens=np.full(n, d, np.int32),
+                    token_counts=None, params=[wl.Params(temperature=1.0)] * n,
+                    positions=np.arange(n, dtype=np.int32) * 3, seed=0)
+    gpu = sample_gpu(w, seed=4, onehot=True)
+    assert gpu["err"] == 0
+    hits = int(np.count_nonzero(gpu["accepted_len"] == 1))
+    assert stats.binomtest(hits, n, p0[d]).pvalue > 1e-4
+    first = gpu["out_tokens"][0::2]
+    rej = gpu["accepted_len"] == 0
+    assert np.all(first[rej] != d)
+
+
+@pytest.mark.parametrize("batch", [4, 64])
+def test_dominant_weight_full_vocabulary_draws(batch):
+    """V = 151936, one id at logit 0 and every other at ln(1e-12): the chance that a draw
+    leaves the dominant id is ~1.5e-7, so 20480 draws (no drafts: every draw is a race over
+    the whole vocabulary) must all return it. A race variate that could reach U = 1 (an
+    infinite key) would miss in ~0.9% of draws. B = 4 runs the fused kernel, B = 64 the
+    separate race kernel."""
+    v = 151936
+    rng = np.random.default_rng(6)
+    dom = int(rng.integers(0, v))
+    row = np.full(v, np.log(1e-12), np.float32)
+    row[dom] = 0.0
+    calls = 20480 // batch
+    w = wl.Workload(name="dominant", batch=batch, num_q_heads=1, num_kv_heads=1,
+                    head_dim=64, dtype=wl.BF16, vocab=v, ctx_lens=np.zeros(batch, np.int32),
+                    cu_rows=np.arange(batch + 1, dtype=np.int32), s_max=0, q=None,
+                    k_cache=None, v_cache=None, target_logits=np.tile(row, (batch, 1)),
+                    draft_logits=None, draft_tokens=np.zeros(0, np.int32), token_counts=None,
+                    params=[wl.Params(temperature=1.0)] * batch,
+                    positions=np.zeros(batch, np.int32), seed=0)
+    dev = wl.device_tensors(w, with_kv=False)
+    miss = 0
+    for c in range(calls):
+        dev["positions"].copy_(torch.arange(batch, dtype=torch.int32) * 7 + c * 100003)
+        gpu = sample_gpu(w, seed=c, dev=dev)
+        assert gpu["err"] == 0
+        miss += int(np.count_nonzero(gpu["out_tokens"] != dom))
+    _log(f"dominant-weight draws: {calls * batch}, misses {miss}")
+    assert miss == 0

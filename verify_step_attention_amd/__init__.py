@@ -37,6 +37,7 @@ EXPORTED_SYMBOLS = ("vsa_version", "vsa_status_string", "verify_attention_worksp
                     "verify_attention", "block_attention", "verify_attention_kvq",
                     "verify_sample_accept_workspace_size", "verify_sample_accept",
                     "draft_vocab_inverse", "verify_sample_accept_reduced_draft",
+                    "verify_sample_accept_onehot",
                     "small_m_qmm_workspace_size", "small_m_qmm")
 
 
@@ -93,6 +94,12 @@ def _lib():
             c_void, c_void, c_int, c_void, c_void, c_void, c_void, c_void, c_void,
             ctypes.c_uint64, c_int, c_int, c_int, c_int, c_int, c_int, c_void, c_void, c_void,
             c_void, c_void, c_void, c_void, c_void, c_size, c_void]
+        lib.verify_sample_accept_onehot.restype = c_int
+        lib.verify_sample_accept_onehot.argtypes = [c_void, c_void, c_void, c_void, c_void,
+                                                    c_void, ctypes.c_uint64, c_int, c_int,
+                                                    c_int, c_int, c_int, c_int, c_void, c_void,
+                                                    c_void, c_void, c_void, c_void, c_void,
+                                                    c_void, c_size, c_void]
         lib.small_m_qmm_workspace_size.restype = c_size
         lib.small_m_qmm_workspace_size.argtypes = [c_int, c_int, c_int]
         lib.small_m_qmm.restype = c_int
@@ -257,6 +264,25 @@ def verify_sample_accept(target_logits, draft_logits, draft_tokens, cu_rows, tok
         _ptr(diag_threshold), _ptr(diag_kept), _ptr(workspace), workspace.numel(),
         _stream(stream))
     _check(st, "verify_sample_accept")
+
+
+def verify_sample_accept_onehot(target_logits, draft_tokens, cu_rows, token_counts, params,
+                                positions, seed, accepted_len, out_tokens, workspace, *,
+                                max_rows_per_seq, max_top_k, max_top_logprobs,
+                                chosen_logprob=None, top_lp_vals=None, top_lp_ids=None,
+                                diag_threshold=None, diag_kept=None, stream=None):
+    """verify_sample_accept for one-hot proposals (prompt-lookup drafts): no draft logits,
+    q_t = 1 at d_t and 0 elsewhere; arguments otherwise as verify_sample_accept."""
+    total, vocab = target_logits.shape
+    batch = cu_rows.numel() - 1
+    st = _lib().verify_sample_accept_onehot(
+        _ptr(target_logits), _ptr(draft_tokens), _ptr(cu_rows), _ptr(token_counts),
+        _ptr(params), _ptr(positions), ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF), batch,
+        total, vocab, int(max_rows_per_seq), int(max_top_k), int(max_top_logprobs),
+        _ptr(accepted_len), _ptr(out_tokens), _ptr(chosen_logprob), _ptr(top_lp_vals),
+        _ptr(top_lp_ids), _ptr(diag_threshold), _ptr(diag_kept), _ptr(workspace),
+        workspace.numel(), _stream(stream))
+    _check(st, "verify_sample_accept_onehot")
 
 
 def draft_vocab_inverse(d2t, vocab, t2d, stream=None):

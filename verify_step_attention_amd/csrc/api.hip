@@ -1,5 +1,6 @@
 // C-ABI entry points: host-side validation, workspace layout and launches.
 #include <math.h>
+#include <stdlib.h>
 
 #include "vsa_internal.h"
 
@@ -30,7 +31,7 @@ hipError_t vsa::launch_zero_u32(uint32_t* p, size_t n, hipStream_t stream) {
 
 extern "C" {
 
-int vsa_version(void) { return 100; }
+int vsa_version(void) { return 200; }
 
 const char* vsa_status_string(vsa_status status) {
     switch (status) {
@@ -233,14 +234,33 @@ vsa_status draft_vocab_inverse(const int32_t* d2t, int draft_vocab, int V, int32
     return VSA_OK;
 }
 
-vsa_status verify_sample_accept_reduced_draft(
-    const float* target_logits, const float* draft_logits, int draft_vocab, const int32_t* t2d,
-    const int32_t* draft_tokens, const int32_t* cu_rows, const int32_t* token_counts,
-    const vsa_row_params* params, const int32_t* positions, uint64_t seed, int B,
-    int total_rows, int V, int max_rows_per_seq, int max_top_k, int max_top_logprobs,
-    int32_t* accepted_len, int32_t* out_tokens, float* chosen_logprob, float* top_lp_vals,
-    int32_t* top_lp_ids, float* diag_threshold, int32_t* diag_kept, void* workspace,
-    size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// How long (microseconds) a fused-kernel workgroup waits for its sequence's statistics
+// before it hands its chunk of the draw to the last arriver: VSA_FUSED_WAIT_US, else 2 ms.
+// Tests set it to 0 to drive the hand-over path from the host.
+uint32_t fused_wait_ticks() {
+    const char* e = getenv("VSA_FUSED_WAIT_US");
+    long us = 2000;
+    if (e && *e) {
+        char* end = nullptr;
+        const long v = strtol(e, &end, 10);
+        if (end && *end == '\0' && v >= 0 && v <= 10000000) us = v;
+    }
+    return (uint32_t)(us * 100);                  // s_memrealtime runs at 100 MHz
+}
+
+vsa_status sample_call(const float* target_logits, const float* draft_logits, int draft_vocab,
+                       const int32_t* t2d, bool onehot, const int32_t* draft_tokens,
+                       const int32_t* cu_rows, const int32_t* token_counts,
+                       const vsa_row_params* params, const int32_t* positions, uint64_t seed,
+                       int B, int total_rows, int V, int max_rows_per_seq, int max_top_k,
+                       int max_top_logprobs, int32_t* accepted_len, int32_t* out_tokens,
+                       float* chosen_logprob, float* top_lp_vals, int32_t* top_lp_ids,
+                       float* diag_threshold, int32_t* diag_kept, void* workspace,
+                       size_t workspace_bytes, void* stream) {
     if (!target_logits || !cu_rows || !params || !positions || !accepted_len || !out_tokens)
         return VSA_ERR_INVALID_ARG;
     if (B < 1 || total_rows < B || V < 1 || max_rows_per_seq < 1 || max_top_k < 0 ||
@@ -260,9 +280,11 @@ vsa_status verify_sample_accept_reduced_draft(
     char* ws = static_cast<char*>(workspace);
     SampArgs a{};
     a.tl = target_logits;
-    a.dl = draft_logits;
-    a.t2d = t2d;
-    a.dvocab = t2d ? draft_vocab : V;
+    a.dl = onehot ? nullptr : draft_logits;
+    a.t2d = onehot ? nullptr : t2d;
+    a.dvocab = (t2d && !onehot) ? draft_vocab : V;
+    a.onehot = onehot ? 1 : 0;
+    a.wait_ticks = fused_wait_ticks();
     a.drafts = draft_tokens;
     a.cu_rows = cu_rows;
     a.counts = token_counts;
@@ -300,6 +322,39 @@ vsa_status verify_sample_accept_reduced_draft(
         return VSA_ERR_LAUNCH;
     if (launch_sample(a, static_cast<hipStream_t>(stream)) != hipSuccess) return VSA_ERR_LAUNCH;
     return VSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+vsa_status verify_sample_accept_reduced_draft(
+    const float* target_logits, const float* draft_logits, int draft_vocab, const int32_t* t2d,
+    const int32_t* draft_tokens, const int32_t* cu_rows, const int32_t* token_counts,
+    const vsa_row_params* params, const int32_t* positions, uint64_t seed, int B,
+    int total_rows, int V, int max_rows_per_seq, int max_top_k, int max_top_logprobs,
+    int32_t* accepted_len, int32_t* out_tokens, float* chosen_logprob, float* top_lp_vals,
+    int32_t* top_lp_ids, float* diag_threshold, int32_t* diag_kept, void* workspace,
+    size_t workspace_bytes, void* stream) {
+    return sample_call(target_logits, draft_logits, draft_vocab, t2d, false, draft_tokens,
+                       cu_rows, token_counts, params, positions, seed, B, total_rows, V,
+                       max_rows_per_seq, max_top_k, max_top_logprobs, accepted_len, out_tokens,
+                       chosen_logprob, top_lp_vals, top_lp_ids, diag_threshold, diag_kept,
+                       workspace, workspace_bytes, stream);
+}
+
+vsa_status verify_sample_accept_onehot(
+    const float* target_logits, const int32_t* draft_tokens, const int32_t* cu_rows,
+    const int32_t* token_counts, const vsa_row_params* params, const int32_t* positions,
+    uint64_t seed, int B, int total_rows, int V, int max_rows_per_seq, int max_top_k,
+    int max_top_logprobs, int32_t* accepted_len, int32_t* out_tokens, float* chosen_logprob,
+    float* top_lp_vals, int32_t* top_lp_ids, float* diag_threshold, int32_t* diag_kept,
+    void* workspace, size_t workspace_bytes, void* stream) {
+    return sample_call(target_logits, nullptr, V, nullptr, true, draft_tokens, cu_rows,
+                       token_counts, params, positions, seed, B, total_rows, V,
+                       max_rows_per_seq, max_top_k, max_top_logprobs, accepted_len, out_tokens,
+                       chosen_logprob, top_lp_vals, top_lp_ids, diag_threshold, diag_kept,
+                       workspace, workspace_bytes, stream);
 }
 
 size_t small_m_qmm_workspace_size(int M, int N, int K) {

@@ -1,203 +1,41 @@
-// Vocabulary stage of the verify step (gfx950): presence/frequency penalties, temperature,
-// top-k threshold and nucleus cutoff, greedy or sampled acceptance, logprobs.
+// Truncation pipeline of the vocabulary stage (gfx950): top-k thresholds, nuclei, raw top
+// logprobs, then the acceptance and the draws, for calls whose sequences need them (and
+// for calls too large for the fused kernel of sample_fused.hip to be resident at once).
 //
-// Pages (mlx-dspark): penalties per verify position from base counts plus the position's
-// own draft prefix, and raw logprobs (Changelog [0.2.0] "Added"); top-k threshold and
-// nucleus cutoff from small grouped selections instead of full-vocabulary sorts, with the
-// same truncated distribution (Changelog [0.20.2] "Changed"); truncation of draft and
-// target (release v0.1.0); accept with probability min(1, p/q) and resample the residual
-// (release v0.0.2); greedy acceptance as the product of positionwise matches with one sync
-// per round (Changelog [0.2.0] "Decode-path performance").
+// Pages (mlx-dspark): top-k threshold and nucleus cutoff from small grouped selections
+// instead of full-vocabulary sorts, with the same truncated distribution (Changelog
+// [0.20.2] "Changed"); truncation of draft and target (release v0.1.0); accept with
+// probability min(1, p/q) and resample the residual (release v0.0.2); penalties and raw
+// logprobs (Changelog [0.2.0] "Added"); one-hot proposals (Changelog [0.2.0] "Added",
+// --mode lookup).
 //
-// Kernels (two launches; within each, workgroups hand results to the last one to finish
-// through agent-scope stores and loads rather than a fence):
-//   sweep_kernel  grid (B x chunks of 2048 ids). One workgroup reads one chunk of every row
-//                 of one sequence with coalesced loads: the count histogram once, then each
-//                 target row (penalized z, and y = z / T when sampled), draft row and raw
-//                 row. Per (row, chunk) it writes max / sum-of-exp / argmax, and for
-//                 truncated rows the chunk's candidate set for the k-th-largest threshold
-//                 (radix select on order-preserving uint32 keys). The last workgroup of a
-//                 sequence to finish (arrival counter) merges the chunks, derives each
-//                 truncated row's threshold, kept set and nucleus (wave-level selection,
-//                 a small bitonic sort, an fp64 scan), and runs the acceptance loop.
-//   race_kernel   grid (B x chunks). For sampled rows without top-k, the final draw is an
-//                 exponential race over the whole vocabulary; the workgroups of the chunks
-//                 compute it in one more coalesced pass and the last one picks the winner.
-//                 Every other sequence returns at once.
-// Random numbers: Philox4x32-10 (Salmon et al., SC'11), keyed (seed), counter
-// (id >> 2, position, sequence, tag).
-#include <math.h>
-
-#include "vsa_internal.h"
+// Kernels, in stream order (each reads what the previous ones wrote):
+//   sweep_kernel     grid (B x chunks of 2048 ids). One workgroup reads one chunk of every
+//                    row of one sequence with coalesced loads: the count histogram once, then
+//                    each target row (penalized z), draft row and raw row. Per (row, chunk)
+//                    it writes max / sum-of-exp / argmax, and for truncated and top-n rows
+//                    the chunk's candidates for the k-th-largest threshold (keys at or above
+//                    a cheap bound on the chunk's k-th largest, or the exact k-th key from a
+//                    radix select).
+//   select_kernel    one workgroup per truncated or top-n row: the row's threshold and kept
+//                    list (sort of the few candidates above a bound on the row's k-th
+//                    largest), its nucleus, or the raw top-n logprobs; a nucleus without
+//                    top-k by a weighted selection over the whole row.
+//   finalize_kernel  one workgroup per sequence: merged statistics, the acceptance tests,
+//                    the draws over kept lists, the outputs, and a race request for draws
+//                    over the whole vocabulary.
+//   race_kernel      grid (B x chunks): the exponential race over the whole vocabulary for
+//                    those requests; the last chunk to finish writes the token.
+// Random numbers: Philox4x32-10 (Salmon et al., SC'11), see sample_common.h.
+#include "sample_common.h"
 
 namespace vsa {
+
+using namespace samp;
+
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kEpt = kChunk / kThreads;        // ids per thread per chunk (8)
-constexpr int kQuads = kChunk / 1024;          // float4 groups per thread per chunk
-constexpr float kNegInf = -__builtin_inff();
-constexpr int kBigIdx = 0x7FFFFFFF;
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kRowBatch = 12;                  // rows whose chunk loads are in flight together
-
-__device__ __forceinline__ void handoff_store_u2(uint2* p, uint2 v) {
-    handoff_store(reinterpret_cast<float2*>(p), *reinterpret_cast<float2*>(&v));
-}
-__device__ __forceinline__ uint2 handoff_load_u2(const uint2* p) {
-    const float2 f = handoff_load(reinterpret_cast<const float2*>(p));
-    return *reinterpret_cast<const uint2*>(&f);
-}
-
-// ------------------------------------------------------------------ small device helpers
-__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
-#pragma unroll
-    for (int r = 0; r < 10; ++r) {
-        if (r) {
-            k0 += 0x9E3779B9u;
-            k1 += 0xBB67AE85u;
-        }
-        // each 32 x 32 -> 64-bit product in one instruction (v_mad_u64_u32)
-        const uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
-        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
-        c = make_uint4((uint32_t)(p1 >> 32) ^ c.y ^ k0, (uint32_t)p1,
-                       (uint32_t)(p0 >> 32) ^ c.w ^ k1, (uint32_t)p0);
-    }
-    return c;
-}
-
-__device__ __forceinline__ uint4 philox_block(uint64_t seed, uint32_t block, uint32_t pos,
-                                              uint32_t seq, uint32_t tag) {
-    return philox4x32_10(make_uint4(block, pos, seq, tag), (uint32_t)seed,
-                         (uint32_t)(seed >> 32));
-}
-
-__device__ __forceinline__ uint32_t pick(uint4 w, int i) {
-    return i == 0 ? w.x : i == 1 ? w.y : i == 2 ? w.z : w.w;
-}
-
-// U' = ((word >> 8) + 1) 2^-24 in (0, 1]
-__device__ __forceinline__ float race_u(uint32_t w) {
-    return (float)((w >> 8) + 1u) * 5.9604644775390625e-08f;
-}
-
-// order-preserving map float -> uint32 (larger float, larger key); -0 is folded into +0
-__device__ __forceinline__ uint32_t ord_key(float f) {
-    const uint32_t u = __float_as_uint(f + 0.0f);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float key_float(uint32_t k) {
-    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-}
-
-// z = (x - fp * c) - pp * [c > 0], each operation rounded once (no contraction)
-__device__ __forceinline__ float penalize(float x, int c, float pp, float fp) {
-    const float z = __fsub_rn(x, __fmul_rn(fp, (float)c));
-    return __fsub_rn(z, c > 0 ? pp : 0.f);
-}
-
-// Nucleus rows (sampled, top_p < 1, no top-k): mass e^(y - ymax) of a value y = v / T
-// relative to the row's maximum, in the same form in the selection, the acceptance and the
-// race. The difference and its base-2 split are exact or fp64, only 2^f (0 <= f < 1) is the
-// fp32 hardware power, so the relative error (~1e-7) does not grow with the distance to the
-// maximum; cumulative masses then sit within ~1e-7 of the fp64 definition.
-__device__ __forceinline__ double nuc_mass(float y, float ymax) {
-    double t = ((double)y - (double)ymax) * 1.4426950408889634;
-    if (!(t > -1100.0)) return 0.0;                  // -inf, NaN or below every double
-    if (!(t <= 0.0)) t = 0.0;                        // y <= ymax; an empty row gives +inf
-    const double n = floor(t);
-    return ldexp((double)__builtin_amdgcn_exp2f((float)(t - n)), (int)n);
-}
-
-__device__ __forceinline__ void wave_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
-    return v > bv || (v == bv && i < bi);
-}
-
-// ------------------------------------------------------------------ per-sequence mode
-struct SeqMode {
-    int r0, rows, k, d0;
-    bool valid, sampled, topk, raw;
-    bool nucleus;    // sampled, top_p < 1 without top-k: full-vocabulary nucleus rows
-    int ntop, topk_k, logprobs;
-    float temp, top_p, pp, fp;
-};
-
-__device__ SeqMode seq_mode(const SampArgs& a, int b, uint32_t* errbits) {
-    SeqMode m{};
-    // the row range and the parameters are requested together (b < B: both in bounds)
-    const int c0 = a.cu_rows[b], c1 = a.cu_rows[b + 1];
-    const vsa_row_params p = a.params[b];
-    m.r0 = c0;
-    m.rows = c1 - c0;
-    m.k = m.rows - 1;
-    m.d0 = m.r0 - b;
-    m.valid = m.rows >= 1 && m.rows <= a.max_rows && m.r0 >= 0 &&
-              m.r0 + m.rows <= a.total_rows && m.d0 >= 0 &&
-              m.d0 + m.k <= a.total_rows - a.batch;
-    if (!m.valid) {
-        *errbits |= VSA_DEVERR_SEQ_SHAPE;
-        return m;
-    }
-    const bool bad = !(p.temperature >= 0.f) || !isfinite(p.temperature) || p.top_k < 0 ||
-                     p.top_k > a.max_top_k || !(p.top_p > 0.f && p.top_p <= 1.f) ||
-                     p.top_logprobs < 0 || p.top_logprobs > a.max_top_lp ||
-                     (p.top_p < 1.f && p.temperature > 0.f &&
-                      !(p.top_k > 0 && p.top_k < a.vocab) && a.max_top_k == 0);
-    if (bad) *errbits |= VSA_DEVERR_PARAMS;
-    m.temp = p.temperature;
-    m.sampled = !bad && p.temperature > 0.f;
-    if (m.sampled && m.k > 0 && a.dl == nullptr) {
-        *errbits |= VSA_DEVERR_NO_DRAFT_LOGITS;
-        m.sampled = false;
-    }
-    m.topk = m.sampled && p.top_k > 0 && p.top_k < a.vocab;
-    m.nucleus = m.sampled && !m.topk && p.top_p < 1.f;
-    m.topk_k = p.top_k;
-    m.top_p = p.top_p;
-    m.pp = p.presence_penalty;
-    m.fp = p.frequency_penalty;
-    m.logprobs = bad ? 0 : p.logprobs;
-    m.ntop = bad ? 0 : p.top_logprobs;
-    m.raw = (m.logprobs != 0) || m.ntop > 0;
-    return m;
-}
-
-// Row q of a sequence's row list: target rows, then draft rows (sampled), then raw rows.
-struct RowRef {
-    int kind;   // 0 target, 1 draft, 2 raw
-    int i;      // target / raw: row 0..R-1; draft: t = 1..K
-    int slot;   // workspace slot
-};
-
-__device__ __forceinline__ int seq_nrows(const SeqMode& m) {
-    return m.rows + (m.sampled ? m.k : 0) + (m.raw ? m.rows : 0);
-}
-
-__device__ __forceinline__ RowRef row_ref(const SampArgs& a, const SeqMode& m, int q) {
-    RowRef r;
-    const int nd = m.sampled ? m.k : 0;
-    if (q < m.rows) {
-        r.kind = 0;
-        r.i = q;
-        r.slot = m.r0 + q;
-    } else if (q < m.rows + nd) {
-        r.kind = 1;
-        r.i = q - m.rows + 1;
-        r.slot = a.total_rows + m.d0 + r.i - 1;
-    } else {
-        r.kind = 2;
-        r.i = q - m.rows - nd;
-        r.slot = 2 * a.total_rows - a.batch + m.r0 + r.i;
-    }
-    return r;
-}
-
 
 // ------------------------------------------------------------------ workgroup radix select
 // The k-th largest key (1-based) among the valid keys of the workgroup, 8 bits at a time.
@@ -356,155 +194,6 @@ __device__ __forceinline__ int wave_sum_i(int v) {
     for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
     return v;
 }
-
-// ------------------------------------------------------------------ chunk loads
-template <bool VEC>
-__device__ __forceinline__ void load_chunk(const float* row, int base, int vocab,
-                                           float (&x)[kEpt]) {
-    const int tid = threadIdx.x;
-    if (VEC) {
-#pragma unroll
-        for (int q = 0; q < kQuads; ++q) {
-            const int j = base + 1024 * q + 4 * tid;
-            float4 v = make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
-            if (j < vocab) v = *reinterpret_cast<const float4*>(row + j);
-            x[4 * q] = v.x;
-            x[4 * q + 1] = v.y;
-            x[4 * q + 2] = v.z;
-            x[4 * q + 3] = v.w;
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < kEpt; ++e) {
-            const int j = base + 1024 * (e >> 2) + 4 * tid + (e & 3);
-            x[e] = j < vocab ? row[j] : kNegInf;
-        }
-    }
-}
-
-// A draft row's logits at the chunk's target ids. With a reduced draft vocabulary
-// (mlx-dspark Changelog [0.8.0] "Added": draft id j stands for target id j + d2t[j], and
-// the draft distribution is widened onto the target vocabulary before the accept test)
-// a target id takes the logit of its draft id through the inverse table t2d, and -inf
-// (probability 0) when no draft id maps to it; an entry outside [-1, dvocab) reads as
-// -inf and sets VSA_DEVERR_DRAFT_MAP.
-__device__ __forceinline__ float mapped_logit(const SampArgs& a, const float* row, int m,
-                                              uint32_t* ebits) {
-    if ((uint32_t)m < (uint32_t)a.dvocab) return row[m];
-    if (m != -1) *ebits |= VSA_DEVERR_DRAFT_MAP;
-    return kNegInf;
-}
-// MAP: the call has a reduced draft vocabulary (kernels are compiled both ways, so the
-// full-vocabulary path carries none of this).
-template <bool VEC, bool MAP>
-__device__ __forceinline__ void load_draft_chunk(const SampArgs& a, int drow, int base,
-                                                 float (&x)[kEpt]) {
-    if constexpr (!MAP) {
-        load_chunk<VEC>(a.dl + (size_t)drow * a.vocab, base, a.vocab, x);
-        return;
-    }
-    const float* row = a.dl + (size_t)drow * a.dvocab;
-    const int tid = threadIdx.x;
-    int map[kEpt];
-    if (VEC) {
-#pragma unroll
-        for (int q = 0; q < kQuads; ++q) {
-            const int j = base + 1024 * q + 4 * tid;
-            int4 v = make_int4(-1, -1, -1, -1);
-            if (j < a.vocab) v = *reinterpret_cast<const int4*>(a.t2d + j);
-            map[4 * q] = v.x;
-            map[4 * q + 1] = v.y;
-            map[4 * q + 2] = v.z;
-            map[4 * q + 3] = v.w;
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < kEpt; ++e) {
-            const int j = base + 1024 * (e >> 2) + 4 * tid + (e & 3);
-            map[e] = j < a.vocab ? a.t2d[j] : -1;
-        }
-    }
-    uint32_t ebits = 0;
-#pragma unroll
-    for (int e = 0; e < kEpt; ++e) x[e] = mapped_logit(a, row, map[e], &ebits);
-    if (ebits) atomicOr(a.err, ebits);
-}
-// The draft logit of target id `id` in draft row drow (id inside [0, V)).
-template <bool MAP>
-__device__ __forceinline__ float draft_logit(const SampArgs& a, int drow, int id) {
-    if constexpr (!MAP) return a.dl[(size_t)drow * a.vocab + id];
-    const float* row = a.dl + (size_t)drow * a.dvocab;
-    uint32_t ebits = 0;
-    const float v = mapped_logit(a, row, a.t2d[id], &ebits);
-    if (ebits) atomicOr(a.err, ebits);
-    return v;
-}
-// Row q of a sequence's row list (target, draft or raw) at the chunk's ids.
-template <bool VEC, bool MAP>
-__device__ __forceinline__ void load_row_chunk(const SampArgs& a, const SeqMode& m,
-                                               const RowRef& r, int base, float (&x)[kEpt]) {
-    if constexpr (!MAP) {
-        // one load path for every row kind: only the row's address differs
-        const float* row = r.kind == 1 ? a.dl + (size_t)(m.d0 + r.i - 1) * a.vocab
-                                       : a.tl + (size_t)(m.r0 + r.i) * a.vocab;
-        load_chunk<VEC>(row, base, a.vocab, x);
-    } else {
-        if (r.kind == 1) load_draft_chunk<VEC, MAP>(a, m.d0 + r.i - 1, base, x);
-        else load_chunk<VEC>(a.tl + (size_t)(m.r0 + r.i) * a.vocab, base, a.vocab, x);
-    }
-}
-
-template <bool VEC>
-__device__ __forceinline__ void load_counts(const int32_t* row, int base, int vocab,
-                                            int (&c)[kEpt]) {
-    const int tid = threadIdx.x;
-    if (row == nullptr) {
-#pragma unroll
-        for (int e = 0; e < kEpt; ++e) c[e] = 0;
-        return;
-    }
-    if (VEC) {
-#pragma unroll
-        for (int q = 0; q < kQuads; ++q) {
-            const int j = base + 1024 * q + 4 * tid;
-            int4 v = make_int4(0, 0, 0, 0);
-            if (j < vocab) v = *reinterpret_cast<const int4*>(row + j);
-            c[4 * q] = v.x;
-            c[4 * q + 1] = v.y;
-            c[4 * q + 2] = v.z;
-            c[4 * q + 3] = v.w;
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < kEpt; ++e) {
-            const int j = base + 1024 * (e >> 2) + 4 * tid + (e & 3);
-            c[e] = j < vocab ? row[j] : 0;
-        }
-    }
-}
-
-__device__ __forceinline__ int elem_id(int base, int e) {
-    return base + 1024 * (e >> 2) + 4 * (int)threadIdx.x + (e & 3);
-}
-
-// Per id of this thread: bit t set when draft t + 1 equals the id (the penalty count at
-// target row i is then the base count plus popcount(mask & (2^i - 1))).
-__device__ __forceinline__ void draft_masks(const int* s_draft, int k, int base,
-                                            uint32_t (&dm)[kEpt]) {
-#pragma unroll
-    for (int e = 0; e < kEpt; ++e) dm[e] = 0u;
-    for (int t = 0; t < k; ++t) {
-        const int off = s_draft[t] - base;
-        if (off >= 0 && off < kChunk && ((off & 1023) >> 2) == (int)threadIdx.x) {
-            const int ee = (off >> 10) * 4 + (off & 3);
-#pragma unroll
-            for (int e = 0; e < kEpt; ++e) dm[e] |= (e == ee) ? (1u << t) : 0u;
-        }
-    }
-}
-
-__device__ __forceinline__ uint32_t low_bits(int i) { return i >= 32 ? ~0u : (1u << i) - 1u; }
-
 // ------------------------------------------------------------------ workgroup selection
 constexpr int kSelTile = 32;     // candidate slots per thread held in registers at once
 
@@ -631,14 +320,15 @@ __device__ double keep_lookup(const SampArgs& a, int kslot, int n, int d) {
         if (k[i].idx == d) p = k[i].p;
     return wave_sum_d(p);
 }
-
-// Exponential race over a kept list: weights max(0, p - q) (q from another kept list, or
-// none) with a fallback to p if every weight is 0. fp64, ties to the lowest id.
-__device__ int keep_race(const SampArgs& a, int pslot, int np, int qslot, int nq, int b,
-                         int pos) {
+// Exponential race over a kept list: weights max(0, p - q) (q from another kept list, a
+// one-hot proposal at `onehot_d`, or none) with a fallback to p if every weight is 0. fp64
+// keys w / E with E = -ln U from the two race words of the id; ties to the lowest id.
+__device__ int keep_race(const SampArgs& a, int pslot, int np, int qslot, int nq, int onehot_d,
+                         int b, int pos) {
     const int lane = threadIdx.x & 63;
     const KeepEntry* kp = a.keep + (size_t)pslot * a.keepcap;
     const KeepEntry* kq = qslot >= 0 ? a.keep + (size_t)qslot * a.keepcap : nullptr;
+    const bool resid = kq != nullptr || onehot_d >= 0;
     double best = -1.0, fbest = -1.0;
     int bi = kBigIdx, fbi = kBigIdx;
     for (int i = lane; i < np; i += 64) {
@@ -648,11 +338,10 @@ __device__ int keep_race(const SampArgs& a, int pslot, int np, int qslot, int nq
         if (kq)
             for (int t = 0; t < nq; ++t)
                 if (kq[t].idx == j) q = kq[t].p;
-        const double r = kq ? fmax(0.0, p - q) : p;
-        const uint4 w = philox_block(a.seed, (uint32_t)j >> 2, (uint32_t)pos, (uint32_t)b, 1u);
-        // U' = 1 is E = 0: an infinite key (selected explicitly, not through -log(1))
-        const float uu = race_u(pick(w, j & 3));
-        const double inv_e = uu < 1.f ? 1.0 / -log((double)uu) : __builtin_inf();
+        if (j == onehot_d) q = 1.0;
+        const double r = resid ? fmax(0.0, p - q) : p;
+        const uint4 w = philox_block(a.seed, (uint32_t)j >> 1, (uint32_t)pos, (uint32_t)b, 1u);
+        const double inv_e = 1.0 / race_e64((j & 1) ? w.z : w.x, (j & 1) ? w.w : w.y);
         if (r > 0.0) {
             const double key = r * inv_e;
             if (key > best || (key == best && j < bi)) { best = key; bi = j; }
@@ -673,7 +362,6 @@ __device__ int keep_race(const SampArgs& a, int pslot, int np, int qslot, int nq
     return best > 0.0 ? bi : fbi;
 }
 
-// ------------------------------------------------------------------ finalize
 struct FinalShared {
     int sel[8];                  // selection scratch: counter, sums, digit + remaining k
     uint32_t hist[256];
@@ -894,12 +582,11 @@ __device__ void select_row(const SampArgs& a, const SeqMode& m, int q, FinalShar
         }
         return;
     }
-    // probabilities over the kept set, fp64, in sorted order
-    const double ymax = (double)__fdiv_rn(key_float(fs.lkey[0]), m.temp);
+    // probabilities over the kept set, fp64, in sorted order: exp((v - vmax) / T)
+    const float vmax = key_float(fs.lkey[0]);
     double part = 0.0;
     for (int i = lane; i < n; i += 64) {
-        const double y = (double)__fdiv_rn(key_float(fs.lkey[i]), m.temp);
-        const double w = exp(y - ymax);
+        const double w = weight64(key_float(fs.lkey[i]), vmax, m.temp);
         fs.lp[i] = w;
         part += w;
     }
@@ -928,9 +615,10 @@ __device__ void select_row(const SampArgs& a, const SeqMode& m, int q, FinalShar
         }
         int mstar = wave_min_i(first);
         if (mstar == kBigIdx) mstar = n - 1;
-        const double cutoff = fs.lp[mstar];
+        // kept: every id whose value is at least the crossing id's (ties of the value kept)
+        const uint32_t kcut = fs.lkey[mstar];
         int cnt = 0;
-        for (int i = lane; i < n; i += 64) cnt += fs.lp[i] >= cutoff ? 1 : 0;
+        for (int i = lane; i < n; i += 64) cnt += fs.lkey[i] >= kcut ? 1 : 0;
         n_keep = wave_sum_i(cnt);
         double ks = 0.0;
         for (int i = lane; i < n_keep; i += 64) ks += fs.lp[i];
@@ -953,60 +641,32 @@ __device__ void select_row(const SampArgs& a, const SeqMode& m, int q, FinalShar
         a.rows[r.slot].kept_p = n_keep;
     }
 }
-
-// AFTER_SELECT: run as its own kernel after the sweep and select_kernel (plain loads; the
-// truncated rows' thresholds and kept lists come from select_kernel); otherwise inside the
-// sweep's last workgroup of the sequence (hand-off loads; no truncated rows).
-// (max, normalizer) of a softmax row from its per-chunk (max, sum) entries, one wave: lane
-// holds entries lane, lane + 64, ... Every caller uses this same order of operations, so
-// every workgroup that merges a row gets the same bits.
-__device__ __forceinline__ void merge_row_wave(const float2 (&st)[kChunkLoads], float cs,
-                                               float* m_out, double* z_out) {
-    float bm = kNegInf;
-#pragma unroll
-    for (int u = 0; u < kChunkLoads; ++u) bm = fmaxf(bm, st[u].x);
-    bm = wave_max(bm);
-    // normalizer sum_j 2^((v_j - m) c) over the row, c = log2(e) / T (raw: T = 1)
-    double z = 0.0;
-    if (bm != kNegInf) {
-#pragma unroll
-        for (int u = 0; u < kChunkLoads; ++u)
-            if (st[u].x != kNegInf) z += (double)st[u].y * (double)exp2f((st[u].x - bm) * cs);
-        z = wave_sum_d(z);
-    }
-    *m_out = bm;
-    *z_out = z;
-}
-
-// Fused race word of a sequence (in LDS): 1 | kind << 1 | accepted << 8.
-__device__ __forceinline__ uint32_t race_word(int kind, int acc) {
-    return 1u | ((uint32_t)kind << 1) | ((uint32_t)acc << 8);
-}
-
-template <bool AFTER_SELECT, bool MAP>
+// The acceptance of one sequence after the sweep and select_kernel (stream order makes
+// their tables visible): the merged statistics of every row, the truncated rows' thresholds
+// and kept lists, the acceptance tests, the draws over kept lists, the outputs, and a race
+// request for a draw over the whole vocabulary (race_kernel, next in the stream).
+template <bool MAP>
 __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, FinalShared& fs,
-                                  RowInfo* rinfo /* LDS, one per row of the list */,
-                                  const int* drafts_lds /* the K draft ids in LDS, or null */,
-                                  uint32_t* word_lds /* fused race: the draw's word in LDS,
-                                                        or null */,
-                                  bool emit /* write the sequence's outputs */) {
+                                  RowInfo* rinfo /* LDS, one per row of the list */) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int nrows = seq_nrows(m);
+    const int nrows = seq_nrows(a, m);
+    const int nd = seq_ndraft(a, m);
+    const bool onehot = a.onehot != 0;
     uint32_t ebits = 0;
     // The draft ids, and for sampled rows without top-k each draft's target logit, draft
     // logit and base count (wave 0, lane t - 1), are requested before the statistics merge
     // so that they arrive with it.
-    const int* const drafts = drafts_lds ? drafts_lds : fs.drafts;
-    if (!drafts_lds && tid < m.k) fs.drafts[tid] = a.drafts[m.d0 + tid];
+    const int* const drafts = fs.drafts;
+    if (tid < m.k) fs.drafts[tid] = a.drafts[m.d0 + tid];
     int pre_d = -1, pre_c = 0;
     float pre_xt = 0.f, pre_xd = 0.f;
     const int base_pos = (wave == 0 && m.sampled) ? a.positions[b] : 0;
     if (wave == 0 && lane < m.k) {
-        pre_d = drafts_lds ? drafts_lds[lane] : a.drafts[m.d0 + lane];
+        pre_d = a.drafts[m.d0 + lane];
         if (m.sampled && !m.topk && pre_d >= 0 && pre_d < a.vocab) {
             pre_c = a.counts ? a.counts[(size_t)b * a.vocab + pre_d] : 0;
             pre_xt = a.tl[(size_t)(m.r0 + lane) * a.vocab + pre_d];
-            pre_xd = draft_logit<MAP>(a, m.d0 + lane, pre_d);
+            if (!onehot) pre_xd = draft_logit<MAP>(a, m.d0 + lane, pre_d);
         }
     }
 
@@ -1027,9 +687,8 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
                 const float2* src =
                     reinterpret_cast<const float2*>(a.stats + (size_t)rr.slot * a.nchunk + c) +
                     half;
-                st[x][u] = (q < nrows && c < a.nchunk)
-                               ? (AFTER_SELECT ? *src : handoff_load(src))
-                               : make_float2(kNegInf, __int_as_float(kBigIdx));
+                st[x][u] = (q < nrows && c < a.nchunk) ? *src
+                                                       : make_float2(kNegInf, __int_as_float(kBigIdx));
             }
         }
 #pragma unroll
@@ -1067,41 +726,40 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
     __syncthreads();
 
     // ---- B: selection results of truncated rows (select_kernel, a kernel earlier)
-    if (AFTER_SELECT) {
-        for (int q = tid; q < nrows; q += kThreads) {
-            const RowRef r = row_ref(a, m, q);
-            if ((m.topk || m.nucleus) && r.kind != 2) {
-                const RowInfo sr = a.rows[r.slot];
-                rinfo[q].theta = sr.theta;
-                rinfo[q].kept_k = sr.kept_k;
-                rinfo[q].kept_p = sr.kept_p;
-                if (m.nucleus) {
-                    rinfo[q].ythr = sr.ythr;
-                    rinfo[q].ymax = sr.ymax;
-                    rinfo[q].zk = sr.zk;
-                }
+    for (int q = tid; q < nrows; q += kThreads) {
+        const RowRef r = row_ref(a, m, q);
+        if ((m.topk || m.nucleus) && r.kind != 2) {
+            const RowInfo sr = a.rows[r.slot];
+            rinfo[q].theta = sr.theta;
+            rinfo[q].kept_k = sr.kept_k;
+            rinfo[q].kept_p = sr.kept_p;
+            if (m.nucleus) {
+                rinfo[q].ythr = sr.ythr;
+                rinfo[q].ymax = sr.ymax;
+                rinfo[q].zk = sr.zk;
+            }
+        }
+    }
+    __syncthreads();
+    // every draft's p_{t-1}(d_t) and q_t(d_t) from the truncated rows' kept lists, draft
+    // t by wave (t - 1) mod 4, so the lists are read in parallel rather than one draft
+    // after another in the acceptance loop (a one-hot proposal has q_t(d_t) = 1)
+    if (m.topk) {
+        for (int t = 1 + wave; t <= m.k; t += 4) {
+            const int d = drafts[t - 1];
+            double pd = 0.0, qd = 0.0;
+            if (d >= 0 && d < a.vocab) {
+                pd = keep_lookup(a, row_ref(a, m, t - 1).slot, rinfo[t - 1].kept_p, d);
+                qd = onehot ? 1.0
+                            : keep_lookup(a, row_ref(a, m, m.rows + t - 1).slot,
+                                          rinfo[m.rows + t - 1].kept_p, d);
+            }
+            if (lane == 0) {
+                fs.pq[0][t - 1] = pd;
+                fs.pq[1][t - 1] = qd;
             }
         }
         __syncthreads();
-        // every draft's p_{t-1}(d_t) and q_t(d_t) from the truncated rows' kept lists, draft
-        // t by wave (t - 1) mod 4, so the lists are read in parallel rather than one draft
-        // after another in the acceptance loop
-        if (m.topk) {
-            for (int t = 1 + wave; t <= m.k; t += 4) {
-                const int d = drafts[t - 1];
-                double pd = 0.0, qd = 0.0;
-                if (d >= 0 && d < a.vocab) {
-                    pd = keep_lookup(a, row_ref(a, m, t - 1).slot, rinfo[t - 1].kept_p, d);
-                    qd = keep_lookup(a, row_ref(a, m, m.rows + t - 1).slot,
-                                     rinfo[m.rows + t - 1].kept_p, d);
-                }
-                if (lane == 0) {
-                    fs.pq[0][t - 1] = pd;
-                    fs.pq[1][t - 1] = qd;
-                }
-            }
-            __syncthreads();
-        }
     }
 
     // ---- C: acceptance (wave 0)
@@ -1109,6 +767,7 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
     int tok = -1;
     bool pending = false;
     RaceReq rq{};
+    rq.onehot_d = -1;
     if (wave == 0) {
         if (!m.sampled) {
             while (acc < m.k) {
@@ -1119,118 +778,113 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
             }
             tok = rinfo[acc].argmax;
             if (tok < 0 || tok >= a.vocab) tok = 0;      // a row with no ordered value
-        } else {
-            // p_{t-1}(d_t) and q_t(d_t) of every draft, one lane per draft (t = lane + 1)
+        } else if (!m.topk) {
+            // p_{t-1}(d_t) and q_t(d_t) of every draft, one lane per draft (t = lane + 1), fp64
             double pd_l = 0.0, qd_l = 0.0;
             const int d_l = lane < m.k ? pre_d : -1;
             const bool valid_l = d_l >= 0 && d_l < a.vocab;
-            if (!m.topk && lane < m.k && valid_l) {
+            if (lane < m.k && valid_l) {
                 const int t = lane + 1;
                 int c = pre_c;
                 for (int s2 = 0; s2 < t - 1; ++s2) c += drafts[s2] == d_l ? 1 : 0;
-                const float cs = kLog2e / m.temp;
                 const float zt = penalize(pre_xt, c, m.pp, m.fp);
                 if (m.nucleus) {
-                    // kept iff y >= y* of the row; renormalized over the kept mass
+                    // kept iff v >= the row's threshold; renormalized over the kept mass
                     const RowInfo& ip = rinfo[t - 1];
-                    const RowInfo& iq = rinfo[m.rows + t - 1];
-                    const float yp = __fdiv_rn(zt, m.temp), yq = __fdiv_rn(pre_xd, m.temp);
-                    pd_l = yp >= ip.ythr ? nuc_mass(yp, ip.ymax) / ip.zk : 0.0;
-                    qd_l = yq >= iq.ythr ? nuc_mass(yq, iq.ymax) / iq.zk : 0.0;
+                    pd_l = zt >= ip.ythr ? nuc_mass(zt, ip.ymax, m.temp) / ip.zk : 0.0;
+                    if (!onehot) {
+                        const RowInfo& iq = rinfo[m.rows + t - 1];
+                        qd_l = pre_xd >= iq.ythr ? nuc_mass(pre_xd, iq.ymax, m.temp) / iq.zk : 0.0;
+                    }
                 } else {
-                    pd_l = (double)exp2f((zt - rinfo[t - 1].m) * cs) / rinfo[t - 1].z;
-                    qd_l = (double)exp2f((pre_xd - rinfo[m.rows + t - 1].m) * cs) /
-                           rinfo[m.rows + t - 1].z;
+                    pd_l = weight64(zt, rinfo[t - 1].m, m.temp) / rinfo[t - 1].z;
+                    if (!onehot)
+                        qd_l = weight64(pre_xd, rinfo[m.rows + t - 1].m, m.temp) /
+                               rinfo[m.rows + t - 1].z;
                 }
+                if (onehot) qd_l = 1.0;
             }
-            if (!m.topk) {
-                // every draft's test at once (u_t from the stream (b, its position, tag 0));
-                // the accepted prefix ends at the first lane that rejects
-                bool ok = false;
-                if (lane < m.k) {
-                    const uint4 wu =
-                        philox_block(a.seed, 0u, (uint32_t)(base_pos + lane), (uint32_t)b, 0u);
-                    const double u = (double)(wu.x >> 8) * 5.9604644775390625e-08;
-                    ok = valid_l && u * qd_l < pd_l;
-                }
-                const unsigned long long rej = __ballot(lane < m.k && !ok);
-                acc = rej ? __ffsll(rej) - 1 : m.k;
-                if (__ballot(lane < m.k && lane <= acc && !valid_l)) ebits |= VSA_DEVERR_DRAFT_ID;
-                pending = true;
-                rq.a = acc;
-                rq.pos = base_pos + acc;
-                if (acc < m.k) {                 // residual of target row acc, draft row acc+1
-                    rq.kind = 1;
-                    rq.m_p = rinfo[acc].m;
-                    rq.z_p = rinfo[acc].z;
+            // every draft's test at once (u_t from the stream (b, its position, tag 0));
+            // the accepted prefix ends at the first lane that rejects
+            bool ok = false;
+            if (lane < m.k) ok = valid_l && accept_uniform(a.seed, b, base_pos + lane) * qd_l < pd_l;
+            const unsigned long long rej = __ballot(lane < m.k && !ok);
+            acc = rej ? __ffsll(rej) - 1 : m.k;
+            if (__ballot(lane < m.k && lane <= acc && !valid_l)) ebits |= VSA_DEVERR_DRAFT_ID;
+            pending = true;
+            rq.a = acc;
+            rq.pos = base_pos + acc;
+            if (acc < m.k) {                 // residual of target row acc, draft row acc+1
+                rq.kind = 1;
+                rq.m_p = rinfo[acc].m;
+                rq.z_p = rinfo[acc].z;
+                if (onehot) {
+                    rq.onehot_d = drafts[acc];
+                } else {
                     rq.m_q = rinfo[m.rows + acc].m;
                     rq.z_q = rinfo[m.rows + acc].z;
-                } else {                         // bonus draw from target row K
-                    rq.kind = 2;
-                    rq.m_p = rinfo[m.k].m;
-                    rq.z_p = rinfo[m.k].z;
                 }
-                if (m.nucleus) {                 // the rows' nuclei and kept masses
-                    rq.nucleus = 1;
-                    rq.z_p = rinfo[acc].zk;
-                    rq.ythr_p = rinfo[acc].ythr;
-                    rq.ymax_p = rinfo[acc].ymax;
-                    if (acc < m.k) {
-                        rq.z_q = rinfo[m.rows + acc].zk;
-                        rq.ythr_q = rinfo[m.rows + acc].ythr;
-                        rq.ymax_q = rinfo[m.rows + acc].ymax;
-                    }
+            } else {                         // bonus draw from target row K
+                rq.kind = 2;
+                rq.m_p = rinfo[m.k].m;
+                rq.z_p = rinfo[m.k].z;
+            }
+            if (m.nucleus) {                 // the rows' nuclei and kept masses
+                rq.nucleus = 1;
+                rq.z_p = rinfo[acc].zk;
+                rq.ythr_p = rinfo[acc].ythr;
+                rq.ymax_p = rinfo[acc].ymax;
+                if (acc < m.k && !onehot) {
+                    rq.z_q = rinfo[m.rows + acc].zk;
+                    rq.ythr_q = rinfo[m.rows + acc].ythr;
+                    rq.ymax_q = rinfo[m.rows + acc].ymax;
                 }
-            } else {
-                // truncated rows: probabilities from the kept lists, one draft at a time
-                bool all = true;
-                for (int t = 1; t <= m.k; ++t) {
-                    const int pos = base_pos + t - 1;
-                    const int d = drafts[t - 1];
-                    const bool valid = d >= 0 && d < a.vocab;
-                    if (!valid) ebits |= VSA_DEVERR_DRAFT_ID;
-                    const int pq = t - 1;            // target row t-1 in the row list
-                    const int qq = m.rows + t - 1;   // draft row t
-                    const RowRef rp = row_ref(a, m, pq), rqr = row_ref(a, m, qq);
-                    const double pd = fs.pq[0][t - 1], qd = fs.pq[1][t - 1];   // 0 if invalid
-                    const uint4 wu = philox_block(a.seed, 0u, (uint32_t)pos, (uint32_t)b, 0u);
-                    const double u = (double)(wu.x >> 8) * 5.9604644775390625e-08;
-                    if (u * qd < pd) { ++acc; continue; }
-                    all = false;
-                    tok = keep_race(a, rp.slot, rinfo[pq].kept_p, rqr.slot, rinfo[qq].kept_p, b,
-                                    pos);
-                    if (tok < 0 || tok >= a.vocab) tok = 0;
-                    break;
+            }
+        } else {
+            // truncated rows: probabilities from the kept lists, one draft at a time
+            bool all = true;
+            for (int t = 1; t <= m.k; ++t) {
+                const int pos = base_pos + t - 1;
+                const int d = drafts[t - 1];
+                const bool valid = d >= 0 && d < a.vocab;
+                if (!valid) ebits |= VSA_DEVERR_DRAFT_ID;
+                const double pd = fs.pq[0][t - 1], qd = fs.pq[1][t - 1];   // 0 if invalid
+                if (accept_uniform(a.seed, b, pos) * qd < pd) { ++acc; continue; }
+                all = false;
+                const RowRef rp = row_ref(a, m, t - 1);
+                if (onehot) {
+                    tok = keep_race(a, rp.slot, rinfo[t - 1].kept_p, -1, 0, d, b, pos);
+                } else {
+                    const RowRef rqr = row_ref(a, m, m.rows + t - 1);
+                    tok = keep_race(a, rp.slot, rinfo[t - 1].kept_p, rqr.slot,
+                                    rinfo[m.rows + t - 1].kept_p, -1, b, pos);
                 }
-                if (all) {
-                    const RowRef rp = row_ref(a, m, m.k);
-                    tok = keep_race(a, rp.slot, rinfo[m.k].kept_p, -1, 0, b, base_pos + m.k);
-                    if (tok < 0 || tok >= a.vocab) tok = 0;
-                }
+                if (tok < 0 || tok >= a.vocab) tok = 0;
+                break;
+            }
+            if (all) {
+                const RowRef rp = row_ref(a, m, m.k);
+                tok = keep_race(a, rp.slot, rinfo[m.k].kept_p, -1, 0, -1, b, base_pos + m.k);
+                if (tok < 0 || tok >= a.vocab) tok = 0;
             }
         }
         // raw statistics of the row whose token the race kernel will pick
         if (pending) {
             rq.logprobs = m.logprobs;
             if (m.raw) {
-                const int xq = m.rows + (m.sampled ? m.k : 0) + acc;
+                const int xq = m.rows + nd + acc;
                 rq.m_x = rinfo[xq].m;
                 rq.z_x = rinfo[xq].z;
             }
         }
     }
     if (wave == 0 && lane == 0) {
-        // fused race: the draw this workgroup joins (every workgroup of the sequence decides
-        // the same); otherwise the request for race_kernel
-        if (word_lds) *word_lds = race_word(pending ? rq.kind : 0, acc);
-        else if (emit) a.race[b] = rq;
-        if (emit) a.accepted[b] = acc;
+        a.race[b] = rq;
+        a.accepted[b] = acc;
     }
-    if (!emit) return;
     if (wave == 0) {
         // emitted tokens, logprobs, diagnostics. The token and logprob of a pending draw
-        // are the race's to write: no address gets plain stores from two workgroups of one
-        // kernel (their L2 write-backs could land in either order).
+        // are the race kernel's to write.
         for (int s = lane; s < m.rows; s += 64) {
             const int grow = m.r0 + s;
             int out = -1;
@@ -1240,7 +894,7 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
             if (a.chosen_lp && !(pending && s == acc)) {
                 float lpv = __builtin_nanf("");
                 if (m.logprobs && out >= 0) {
-                    const int xq = m.rows + (m.sampled ? m.k : 0) + s;
+                    const int xq = m.rows + nd + s;
                     lpv = (float)((double)a.tl[(size_t)grow * a.vocab + out] -
                                   (double)rinfo[xq].m - log(rinfo[xq].z));
                 }
@@ -1262,68 +916,56 @@ __device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, Fi
     }
 }
 
-// ------------------------------------------------------------------ sweep kernel
 // ------------------------------------------------------------------ full-vocabulary race
 // A categorical draw over the whole vocabulary as an exponential race: id j wins when its
-// key w_j / E_j is the largest, E_j = -ln U'_j standard exponential, U'_j from the draw's
-// Philox stream (tag 1), w = max(0, p - q) for a residual draw (kind 1) or p (kind 2);
-// when every residual weight is 0 the draw falls back to the race on p itself. Each chunk
-// of kChunk ids finds its two winners; the last chunk to arrive merges them.
+// key w_j / E_j is the largest, E_j = -ln U_j standard exponential from the draw's Philox
+// stream (tag 1), w = max(0, p - q) for a residual draw (kind 1) or p (kind 2); when every
+// residual weight is 0 the draw falls back to the race on p itself. Each chunk of kChunk
+// ids finds its two winners; the last chunk to arrive merges them.
 
 // The winners of this wave's ids of chunk c for request rq: (key, id, fallback key,
 // fallback id), valid in every lane. xp / xq hold the chunk of the target row (m.r0 + rq.a)
-// and, for kind 1, of the draft row (m.d0 + rq.a); dm[e] marks the drafts before row rq.a
-// that equal id e. Ids past the vocabulary hold -inf logits (weight 0: never a winner).
+// and, for kind 1 with a draft row, of the draft row (m.d0 + rq.a); dm[e] marks the drafts
+// before row rq.a that equal id e. Ids past the vocabulary hold -inf logits (weight 0).
 template <bool NUC>
 __device__ float4 race_chunk(const SampArgs& a, const SeqMode& m, const RaceReq& rq, int b,
                              int c, const int (&cnt)[kEpt], const uint32_t (&dm)[kEpt],
                              const float (&xp)[kEpt], const float (&xq)[kEpt]) {
     const int tid = threadIdx.x;
     const int base = c * kChunk;
+    const bool draft_q = rq.kind == 1 && rq.onehot_d < 0;
     const float inv_zp = (float)(1.0 / rq.z_p);
-    const float inv_zq = rq.kind == 1 ? (float)(1.0 / rq.z_q) : 0.f;
+    const float inv_zq = draft_q ? (float)(1.0 / rq.z_q) : 0.f;
     const float cs = kLog2e / m.temp;
-    // Keys are w / (-log2 U') (the race's w / (-ln U') times ln 2, the same argmax), with
-    // the hardware exp2 / log2 / reciprocal (about one ulp each: the keys stay well inside
-    // the relative gap below which two ids count as tied). A thread visits its ids in
+    // Keys are w / (-log2 U) (the race's w / E times ln 2, the same argmax), with the
+    // hardware exp2 / log2 / reciprocal (a few ulps each). A thread visits its ids in
     // increasing order, so a strict > keeps the lower id of a tie; w = 0 gives a key of 0,
-    // or NaN against an infinite 1 / E, neither of which wins.
+    // which never wins.
     float best = 0.f, fbest = 0.f;
     int bi = kBigIdx, fbi = kBigIdx;
 #pragma unroll
     for (int qd = 0; qd < kQuads; ++qd) {
         const int j0 = base + 1024 * qd + 4 * tid;
-        const uint4 w = philox_block(a.seed, (uint32_t)j0 >> 2, (uint32_t)rq.pos, (uint32_t)b, 1u);
+        const RaceWords w = race_words4(a.seed, j0, rq.pos, b);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int e = 4 * qd + r;
             const int j = j0 + r;
             const float zp = penalize(xp[e], cnt[e] + __popc(dm[e]), m.pp, m.fp);
-            float p, rr;
+            float p, q = 0.f;
             if constexpr (NUC) {
-                // nucleus rows: ids below the row's y* have probability 0
-                const float y = __fdiv_rn(zp, m.temp);
-                p = y >= rq.ythr_p ? (float)(nuc_mass(y, rq.ymax_p) / rq.z_p) : 0.f;
-                rr = p;
-                if (rq.kind == 1) {
-                    const float yq = __fdiv_rn(xq[e], m.temp);
-                    const float q =
-                        yq >= rq.ythr_q ? (float)(nuc_mass(yq, rq.ymax_q) / rq.z_q) : 0.f;
-                    rr = fmaxf(0.f, p - q);
-                }
+                // nucleus rows: ids below the row's threshold have probability 0
+                p = zp >= rq.ythr_p ? (float)(nuc_mass(zp, rq.ymax_p, m.temp) / rq.z_p) : 0.f;
+                if (draft_q)
+                    q = xq[e] >= rq.ythr_q ? (float)(nuc_mass(xq[e], rq.ymax_q, m.temp) / rq.z_q)
+                                           : 0.f;
             } else {
                 p = __builtin_amdgcn_exp2f((zp - rq.m_p) * cs) * inv_zp;
-                rr = p;
-                if (rq.kind == 1) {
-                    const float q = __builtin_amdgcn_exp2f((xq[e] - rq.m_q) * cs) * inv_zq;
-                    rr = fmaxf(0.f, p - q);
-                }
+                if (draft_q) q = __builtin_amdgcn_exp2f((xq[e] - rq.m_q) * cs) * inv_zq;
             }
-            // 1 / (-log2 U'); U' = 1 is E = 0 in the exact race, an infinite key (selected
-            // explicitly: -log2(1) may come out as -0, whose reciprocal is -inf)
-            const float uu = race_u(pick(w, r));
-            const float inv_e = uu < 1.f ? __builtin_amdgcn_rcpf(-__builtin_amdgcn_logf(uu))
-                                         : __builtin_inff();
+            if (rq.kind == 1 && j == rq.onehot_d) q = 1.f;
+            const float rr = rq.kind == 1 ? fmaxf(0.f, p - q) : p;
+            const float inv_e = __builtin_amdgcn_rcpf(race_e2(w.hi(r), w.lo(r)));
             const float key = rr * inv_e, fkey = p * inv_e;
             const bool up = key > best, fup = fkey > fbest;
             best = up ? key : best;
@@ -1375,25 +1017,7 @@ __device__ int race_winner(const SampArgs& a, int b, int lane) {
     if (tok < 0 || tok >= a.vocab) tok = 0;               // a row with no ordered value
     return tok;
 }
-
-// Fused race: thread 0 waits until all `total` workgroups of the sequence have counted in.
-// The sweep grid is launched fused only when all of its workgroups fit on the GPU at once,
-// so every one of them arrives; the wait still gives up after kWaitTicks of the 100 MHz
-// clock (error bit; the workgroup then goes on with what it reads).
-constexpr uint64_t kWaitTicks = 20000000ull;              // 0.2 s
-__device__ void wait_arrivals(const SampArgs& a, const uint32_t* counter, uint32_t total) {
-    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    while (__hip_atomic_load(const_cast<uint32_t*>(counter), __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT) < total) {
-        if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
-            atomicOr(a.err, VSA_DEVERR_WAIT_TIMEOUT);
-            return;
-        }
-        __builtin_amdgcn_s_sleep(4);
-    }
-}
-
-// Separate race kernel (top-k pipeline, or a sweep grid too large to be resident at once).
+// The race kernel: only sequences whose draw is over the whole vocabulary do work.
 template <bool VEC, bool MAP>
 __global__ __launch_bounds__(kThreads) void race_kernel(const SampArgs a) {
     __shared__ int s_draft[kMaxSeqRows];
@@ -1411,7 +1035,7 @@ __global__ __launch_bounds__(kThreads) void race_kernel(const SampArgs a) {
     load_counts<VEC>(a.counts ? a.counts + (size_t)b * a.vocab : nullptr, base, a.vocab, cnt);
     float xp[kEpt], xq[kEpt];
     load_chunk<VEC>(a.tl + (size_t)(m.r0 + rq.a) * a.vocab, base, a.vocab, xp);
-    if (rq.kind == 1) load_draft_chunk<VEC, MAP>(a, m.d0 + rq.a, base, xq);
+    if (rq.kind == 1 && rq.onehot_d < 0) load_draft_chunk<VEC, MAP>(a, m.d0 + rq.a, base, xq);
     else
 #pragma unroll
         for (int e = 0; e < kEpt; ++e) xq[e] = 0.f;
@@ -1422,7 +1046,7 @@ __global__ __launch_bounds__(kThreads) void race_kernel(const SampArgs a) {
     const float4 part = rq.nucleus ? race_chunk<true>(a, m, rq, b, c, cnt, dm, xp, xq)
                                    : race_chunk<false>(a, m, rq, b, c, cnt, dm, xp, xq);
     if ((tid & 63) == 0) handoff_store4(a.race_part + ((size_t)b * a.nchunk + c) * 4 + (tid >> 6), part);
-    if (!handoff_arrive(counter_at(a.ctr, a.ctr_x, 2 * b + 1), (uint32_t)a.nchunk, &s_last) || tid >= 64) return;
+    if (!handoff_arrive(counter_at(a.ctr, a.ctr_x, 4 * b + 1), (uint32_t)a.nchunk, &s_last) || tid >= 64) return;
     const int tok = race_winner(a, b, tid);
     if (tid != 0) return;
     const int grow = m.r0 + rq.a;
@@ -1433,15 +1057,13 @@ __global__ __launch_bounds__(kThreads) void race_kernel(const SampArgs a) {
                                         : __builtin_nanf("");
 }
 
-template <bool VEC, bool TOPK, bool MAP>
+template <bool VEC, bool MAP>
 __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
     __shared__ float4 s_part[3 * kMaxSeqRows][4];
     __shared__ int s_draft[kMaxSeqRows];
     __shared__ uint32_t s_hist[256];
     __shared__ int s_nib[2][4][16];
     __shared__ int s_sh[4];
-    __shared__ FinalShared s_final;
-    __shared__ RowInfo s_rinfo[3 * kMaxSeqRows];
 
     preload_args(a);
     const int b = blockIdx.x / a.nchunk, c = blockIdx.x % a.nchunk;
@@ -1470,8 +1092,8 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
     uint32_t dm[kEpt];              // drafts equal to each id (see draft_masks)
     uint32_t dmo = 0;               // their union
 
-    const int nrows = seq_nrows(m);
-    const int nd = m.sampled ? m.k : 0;
+    const int nrows = seq_nrows(a, m);
+    const int nd = seq_ndraft(a, m);
     // ---- per-row statistics of this chunk (loads of kRowBatch rows in flight at once).
     // Values: z (penalized target), w (draft) or x (raw); softmax statistics are taken as
     // (max v, sum 2^((v - max) c)) with c = log2(e) / T, greedy target rows as argmax.
@@ -1581,12 +1203,11 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
             acc.x = mx;
             acc.y = sm;
         }
-        if (TOPK) a.stats[(size_t)r.slot * a.nchunk + c] = acc;   // read by later kernels
-        else handoff_store4(a.stats + (size_t)r.slot * a.nchunk + c, acc);
+        a.stats[(size_t)r.slot * a.nchunk + c] = acc;   // read by later kernels
     }
 
     // ---- candidates for the k-th-largest threshold of truncated / top-n rows
-    if (TOPK && (m.topk || m.ntop > 0)) {
+    if (m.topk || m.ntop > 0) {
         for (int q = 0; q < nrows; ++q) {
             const RowRef r = row_ref(a, m, q);
             const bool trunc = m.topk && r.kind != 2;
@@ -1656,91 +1277,23 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
             __syncthreads();
         }
     }
-
-
-    // ---- the last chunk of the sequence to finish merges and accepts (fence-free)
-    if (TOPK) return;                              // select_kernel and finalize_kernel follow
-    __shared__ int s_last;
-    __shared__ uint32_t s_word;
-    // A fused sampled sequence ends in a race (residual or bonus draw) that every chunk of it
-    // joins. Each of its workgroups waits until all of them have counted in, then merges
-    // the statistics and runs the acceptance itself: the same values in the same order, so
-    // every workgroup reaches the same decision, with no round trips to publish it. Only
-    // the last arriver writes the outputs; the race's last arriver clears both counters.
-    const bool race_here = a.fused && m.sampled && !m.topk;
-    const int pos0 = race_here ? a.positions[b] : 0;
-    const bool last = handoff_arrive(counter_at(a.ctr, a.ctr_x, 2 * b), (uint32_t)a.nchunk, &s_last, !race_here);
-    if (!race_here && !last) return;
-    if (race_here) {
-        if (!last && tid == 0) wait_arrivals(a, counter_at(a.ctr, a.ctr_x, 2 * b), (uint32_t)a.nchunk);
-        __syncthreads();
-    }
-    finalize_sequence<false, MAP>(a, m, b, s_final, s_rinfo, s_draft,
-                                  race_here ? &s_word : nullptr, last);
-    if (!race_here) return;
-    __syncthreads();
-    // ---- race over this chunk: the sweep's counts and draft masks, L2-warm rows
-    const uint32_t wd = s_word;
-    const int kind = (int)((wd >> 1) & 3u), ra = (int)(wd >> 8);
-    float4 part = race_none();
-    if (kind != 0) {
-        float xp[kEpt], xq[kEpt];
-        load_chunk<VEC>(a.tl + (size_t)(m.r0 + ra) * a.vocab, base, a.vocab, xp);
-        if (kind == 1) load_draft_chunk<VEC, MAP>(a, m.d0 + ra, base, xq);
-        else
-#pragma unroll
-            for (int e = 0; e < kEpt; ++e) xq[e] = 0.f;
-        // p is target row ra, q draft row ra + 1 (row list index m.rows + ra)
-        RaceReq rq{};
-        rq.kind = kind;
-        rq.a = ra;
-        rq.pos = pos0 + ra;
-        rq.m_p = s_rinfo[ra].m;
-        rq.z_p = s_rinfo[ra].z;
-        if (kind == 1) {
-            rq.m_q = s_rinfo[m.rows + ra].m;
-            rq.z_q = s_rinfo[m.rows + ra].z;
-        }
-        uint32_t dmr[kEpt];
-        const uint32_t lm = low_bits(ra);
-#pragma unroll
-        for (int e = 0; e < kEpt; ++e) dmr[e] = dm[e] & lm;
-        part = race_chunk<false>(a, m, rq, b, c, cnt, dmr, xp, xq);
-    }
-    if (lane == 0) handoff_store4(a.race_part + ((size_t)b * a.nchunk + c) * 4 + wave, part);
-    if (!handoff_arrive(counter_at(a.ctr, a.ctr_x, 2 * b + 1), (uint32_t)a.nchunk, &s_last) || tid >= 64) return;
-    // ---- the last chunk to arrive: the drawn token and its logprob. Every workgroup of the
-    // sequence has passed its wait, so the sweep counter can go back to zero.
-    if (lane == 0)
-        __hip_atomic_store(counter_at(a.ctr, a.ctr_x, 2 * b), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int tok = race_winner(a, b, lane);
-    if (lane != 0 || kind == 0) return;
-    const int grow = m.r0 + ra;
-    a.out_tokens[grow] = tok;
-    if (a.chosen_lp) {
-        float lp = __builtin_nanf("");
-        if (m.logprobs) {                         // raw row ra (row list m.rows + K + ra)
-            const RowInfo& rx = s_rinfo[m.rows + m.k + ra];
-            lp = (float)((double)a.tl[(size_t)grow * a.vocab + tok] - (double)rx.m - log(rx.z));
-        }
-        a.chosen_lp[grow] = lp;
-    }
 }
 
 // ------------------------------------------------------------------ nucleus without top-k
-// A sampled row with top_p < 1 and no top-k keeps {j : y_j >= y*}, y = v / T (fp32 IEEE
-// division, as the definition), where y* is the value at which the mass of the ids sorted
-// by y (descending) first reaches top_p of the row's mass; ties at y* are kept (mlx-dspark
-// release v0.1.0 "Lossless top-p / top-k sampling": the nucleus truncates draft and target).
-// No sort: one workgroup per row finds y* by a weighted selection. Pass 1 over the row
-// histograms the mass by (ymax - y) in steps of 1/16 and finds the bucket where the mass
-// from the top crosses the target; pass 2 lists that bucket's ids (usually a few hundred);
-// a radix selection on their ordered keys, 8 bits at a time, weighted by mass, finds y*.
+// A sampled row with top_p < 1 and no top-k keeps {j : v_j >= v*} (v the penalized target
+// logit z, or the draft logit), where v* is the value at which the mass e^((v - vmax) / T)
+// of the ids sorted by v (descending) first reaches top_p of the row's mass; ties at v* are
+// kept (mlx-dspark release v0.1.0 "Lossless top-p / top-k sampling": the nucleus truncates
+// draft and target). No sort: one workgroup per row finds v* by a weighted selection. Pass
+// 1 over the row histograms the mass by (vmax - v) / T in steps of 1/16 and finds the
+// bucket where the mass from the top crosses the target; pass 2 lists that bucket's ids
+// (usually a few hundred); a radix selection on their ordered keys, 8 bits at a time,
+// weighted by mass, finds v*.
 
 constexpr int kNucBuckets = 2048;
 constexpr int kNucList = 4096;
-__device__ __forceinline__ int nuc_bucket(float y, float ymax) {
-    const float u = (ymax - y) * 16.f;        // monotone in y: ties share a bucket
+__device__ __forceinline__ int nuc_bucket(float v, float vmax, float s16) {
+    const float u = (vmax - v) * s16;         // monotone in v: ties share a bucket (s16 = 16/T)
     return u < (float)(kNucBuckets - 1) ? (int)u : kNucBuckets - 1;
 }
 struct NucShared {
@@ -1825,8 +1378,8 @@ __device__ void nuc_crossing(NucShared& ns, int nb, bool rev, double base, doubl
     ns.cnt_before = an;
 }
 
-// One pass over row r's values y = v / T, f(y) per id whose v lies in [vlo, vhi] (ids past
-// the vocabulary skipped; the interval spares the division for ids that cannot matter).
+// One pass over row r's values v, f(v) per id whose v lies in [vlo, vhi] (ids past the
+// vocabulary skipped; the interval spares the mass for ids that cannot matter).
 // Target rows carry their penalties (base counts plus the drafts before the row).
 template <bool VEC, bool MAP, class F>
 __device__ void nuc_pass(const SampArgs& a, const SeqMode& m, const RowRef& r, int b,
@@ -1857,7 +1410,7 @@ __device__ void nuc_pass(const SampArgs& a, const SeqMode& m, const RowRef& r, i
 #pragma unroll
             for (int e = 0; e < kEpt; ++e)
                 if (elem_id(base, e) < a.vocab && x[u][e] >= vlo && x[u][e] <= vhi)
-                    f(__fdiv_rn(x[u][e], m.temp));
+                    f(x[u][e]);
         }
     }
 }
@@ -1900,16 +1453,17 @@ __device__ void nucleus_row(const SampArgs& a, const SeqMode& m, int b, int q, N
     }
     if (tid == 0) ns.cnt = 0;
     const RowInfo st = row_stats_wave(a, m, r);      // the row's max of v (every wave)
-    const float ymax = __fdiv_rn(st.m, m.temp);        // division is monotone: max of y
+    const float vmax = st.m;
+    const float s16 = 16.f / m.temp;
     __syncthreads();
     RowInfo* out = a.rows + r.slot;
-    if (ymax == kNegInf) {                             // no orderable value: nothing kept
+    if (vmax == kNegInf) {                             // no orderable value: nothing kept
         if (tid == 0) {
             out->theta = kNegInf;
             out->kept_k = a.vocab;
             out->kept_p = 0;
             out->ythr = __builtin_inff();
-            out->ymax = ymax;
+            out->ymax = vmax;
             out->zk = 0.0;
         }
         return;
@@ -1917,8 +1471,8 @@ __device__ void nucleus_row(const SampArgs& a, const SeqMode& m, int b, int q, N
     // ---- pass 1: mass per bucket of (ymax - y)
     {
         NucRun run;
-        nuc_pass<VEC, MAP>(a, m, r, b, ns.drafts, kNegInf, __builtin_inff(), [&](float y) {
-            run.add(ns, nuc_bucket(y, ymax), nuc_mass(y, ymax));
+        nuc_pass<VEC, MAP>(a, m, r, b, ns.drafts, kNegInf, __builtin_inff(), [&](float v) {
+            run.add(ns, nuc_bucket(v, vmax, s16), nuc_mass(v, vmax, m.temp));
         });
         run.flush(ns);
     }
@@ -1941,25 +1495,23 @@ __device__ void nucleus_row(const SampArgs& a, const SeqMode& m, int b, int q, N
     __syncthreads();
     // ---- pass 2: the crossing bucket's ids (when they fit the list)
     const bool listed = nb <= kNucList;
-    // values v whose y = v / T can fall in bucket bstar, with a wide margin (the bucket test
-    // itself decides): y in [ymax - (bstar + 1) / 16, ymax - bstar / 16], widened by 1e-3 of
-    // the magnitudes, and v = y T within 1e-5 relative
+    // values v that can fall in bucket bstar, with a wide margin (the bucket test itself
+    // decides): v in [vmax - (bstar + 1) T / 16, vmax - bstar T / 16], widened by 1e-3 of
+    // the magnitudes
     float vlo = kNegInf, vhi = __builtin_inff();
     {
-        const double slack = 1e-3 * (fabs((double)ymax) + (bstar + 1) / 16.0) + 1e-30;
-        const double ylo = (double)ymax - (bstar + 1) / 16.0 - slack;
-        const double yhi = (double)ymax - bstar / 16.0 + slack;
         const double t = (double)m.temp;
-        if (bstar < kNucBuckets - 1) vlo = (float)fmin(ylo * t * (1 - 1e-5), ylo * t * (1 + 1e-5));
-        vhi = (float)fmax(yhi * t * (1 - 1e-5), yhi * t * (1 + 1e-5));
+        const double slack = 1e-3 * (fabs((double)vmax) + (bstar + 1) * t / 16.0) + 1e-30;
+        if (bstar < kNucBuckets - 1) vlo = (float)((double)vmax - (bstar + 1) * t / 16.0 - slack);
+        vhi = (float)((double)vmax - bstar * t / 16.0 + slack);
     }
     if (listed) {
-        nuc_pass<VEC, MAP>(a, m, r, b, ns.drafts, vlo, vhi, [&](float y) {
-            if (nuc_bucket(y, ymax) == bstar) {
+        nuc_pass<VEC, MAP>(a, m, r, b, ns.drafts, vlo, vhi, [&](float v) {
+            if (nuc_bucket(v, vmax, s16) == bstar) {
                 const int p = atomicAdd(&ns.cnt, 1);
                 if (p < kNucList) {
-                    ns.lkey[p] = ord_key(y);
-                    ns.lw[p] = nuc_mass(y, ymax);
+                    ns.lkey[p] = ord_key(v);
+                    ns.lw[p] = nuc_mass(v, vmax, m.temp);
                 }
             }
         });
@@ -1985,8 +1537,9 @@ __device__ void nucleus_row(const SampArgs& a, const SeqMode& m, int b, int q, N
         if (listed) {
             for (int i = tid; i < nl; i += kThreads) visit(ns.lkey[i], ns.lw[i], run);
         } else {
-            nuc_pass<VEC, MAP>(a, m, r, b, ns.drafts, vlo, vhi, [&](float y) {
-                if (nuc_bucket(y, ymax) == bstar) visit(ord_key(y), nuc_mass(y, ymax), run);
+            nuc_pass<VEC, MAP>(a, m, r, b, ns.drafts, vlo, vhi, [&](float v) {
+                if (nuc_bucket(v, vmax, s16) == bstar)
+                    visit(ord_key(v), nuc_mass(v, vmax, m.temp), run);
             });
         }
         run.flush(ns);
@@ -2006,11 +1559,10 @@ __device__ void nucleus_row(const SampArgs& a, const SeqMode& m, int b, int q, N
         out->kept_k = a.vocab;
         out->kept_p = cbase + last_n;
         out->ythr = key_float(prefix);
-        out->ymax = ymax;
+        out->ymax = vmax;
         out->zk = base + last_m;
     }
 }
-
 // ------------------------------------------------------------------ top-k pipeline kernels
 // grid (B x rows_cap): workgroup (b, q) selects row q of sequence b when it is a truncated
 // or top-n row; every other workgroup returns at once.
@@ -2022,10 +1574,11 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const SampArgs a, int 
     const int b = blockIdx.x / rows_cap, q = blockIdx.x % rows_cap;
     uint32_t ebits = 0;
     const SeqMode m = seq_mode(a, b, &ebits);
-    if (!m.valid || q >= seq_nrows(m)) return;
+    if (!m.valid || q >= seq_nrows(a, m)) return;
     if (m.nucleus && row_ref(a, m, q).kind != 2) nucleus_row<VEC, MAP>(a, m, b, q, s_nuc);
     else select_row(a, m, q, s_final);
 }
+
 
 // grid (B): merges the chunk statistics and runs the acceptance of one sequence.
 template <bool MAP>
@@ -2037,7 +1590,7 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(const SampArgs a) {
     uint32_t ebits = 0;
     const SeqMode m = seq_mode(a, b, &ebits);
     if (!m.valid) return;
-    finalize_sequence<true, MAP>(a, m, b, s_final, s_rinfo, nullptr, nullptr, true);
+    finalize_sequence<MAP>(a, m, b, s_final, s_rinfo);
 }
 
 }  // namespace
@@ -2054,7 +1607,7 @@ SampPlan plan_sample(int B, int total_rows, int V, int max_top_k, int max_top_lp
     p.slots = 3 * total_rows - B;
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     size_t off = kWsHeader;                         // error word, counters
-    p.n_ctr_x = extra_counters(2L * B);
+    p.n_ctr_x = extra_counters(4L * B);
     p.off_ctr_x = off;
     off += up(p.n_ctr_x * 4);
     p.off_stats = off;
@@ -2073,28 +1626,6 @@ SampPlan plan_sample(int B, int total_rows, int V, int max_top_k, int max_top_lp
     off += up((size_t)B * p.nchunk * 4 * 16);
     p.bytes = off;
     return p;
-}
-
-// Workgroups of the lean sweep kernel (the form launched: vector loads or not, reduced
-// draft vocabulary or not) that the device holds at once (cached per device).
-static int sweep_capacity(bool vec, bool map) {
-    static int cache[2][2][64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    int& c = cache[vec ? 1 : 0][map ? 1 : 0][dev];
-    if (c == 0) {
-        int per_cu = 0, cus = 0;
-        const void* k =
-            map ? (vec ? reinterpret_cast<const void*>(&sweep_kernel<true, false, true>)
-                       : reinterpret_cast<const void*>(&sweep_kernel<false, false, true>))
-                : (vec ? reinterpret_cast<const void*>(&sweep_kernel<true, false, false>)
-                       : reinterpret_cast<const void*>(&sweep_kernel<false, false, false>));
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kThreads, 0) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            per_cu = cus = 0;
-        c = per_cu * cus > 0 ? per_cu * cus : -1;
-    }
-    return c;
 }
 
 // Inverse of a reduced draft vocabulary's offset table: t2d[x] = the draft id j with
@@ -2125,46 +1656,37 @@ hipError_t launch_draft_vocab_inverse(const int32_t* d2t, int dvocab, int vocab,
 
 hipError_t launch_sample(const SampArgs& args, hipStream_t stream) {
     SampArgs a = args;
+    // Without truncation, top-n logprobs or a grid too large to be resident at once, the
+    // whole stage is the fused kernel (sample_fused.hip).
+    if (fused_fits(a)) return launch_fused(a, stream);
     const dim3 grid((unsigned)a.batch * a.nchunk), block(kThreads);
     const bool vec = (a.vocab % 4) == 0;
-    // Truncated (top-k) and top-n rows need the candidate tables and the selection code,
-    // which only the TOPK variant carries (a parameter asking for them is rejected when
-    // max_top_k and max_top_logprobs are 0).
-    const bool topk = a.max_top_k > 0 || a.max_top_lp > 0;
-    // Without them the sweep workgroups run the full-vocabulary race themselves, waiting
-    // for their sequence's acceptance step, when the whole grid is resident at once.
     const bool map = a.t2d != nullptr;
-    a.fused = !topk && (long)a.batch * a.nchunk <= (long)sweep_capacity(vec, map);
-#define VSA_SWEEP(V, T, M) hipLaunchKernelGGL((sweep_kernel<V, T, M>), grid, block, 0, stream, a)
+#define VSA_SWEEP(V, M) hipLaunchKernelGGL((sweep_kernel<V, M>), grid, block, 0, stream, a)
     if (map) {
-        if (vec) { if (topk) VSA_SWEEP(true, true, true); else VSA_SWEEP(true, false, true); }
-        else { if (topk) VSA_SWEEP(false, true, true); else VSA_SWEEP(false, false, true); }
+        if (vec) VSA_SWEEP(true, true); else VSA_SWEEP(false, true);
     } else {
-        if (vec) { if (topk) VSA_SWEEP(true, true, false); else VSA_SWEEP(true, false, false); }
-        else { if (topk) VSA_SWEEP(false, true, false); else VSA_SWEEP(false, false, false); }
+        if (vec) VSA_SWEEP(true, false); else VSA_SWEEP(false, false);
     }
 #undef VSA_SWEEP
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (topk) {
-        // one workgroup per (sequence, row of its row list), then one per sequence
-        const int rows_cap = 3 * a.max_rows;
-        const dim3 sgrid((unsigned)a.batch * rows_cap);
-        if (map) {
-            if (vec) hipLaunchKernelGGL((select_kernel<true, true>), sgrid, block, 0, stream, a, rows_cap);
-            else hipLaunchKernelGGL((select_kernel<false, true>), sgrid, block, 0, stream, a, rows_cap);
-        } else {
-            if (vec) hipLaunchKernelGGL((select_kernel<true, false>), sgrid, block, 0, stream, a, rows_cap);
-            else hipLaunchKernelGGL((select_kernel<false, false>), sgrid, block, 0, stream, a, rows_cap);
-        }
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        if (map) hipLaunchKernelGGL(finalize_kernel<true>, dim3((unsigned)a.batch), block, 0, stream, a);
-        else hipLaunchKernelGGL(finalize_kernel<false>, dim3((unsigned)a.batch), block, 0, stream, a);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
+    // one workgroup per (sequence, row of its row list), then one per sequence
+    const int rows_cap = 3 * a.max_rows;
+    const dim3 sgrid((unsigned)a.batch * rows_cap);
+    if (map) {
+        if (vec) hipLaunchKernelGGL((select_kernel<true, true>), sgrid, block, 0, stream, a, rows_cap);
+        else hipLaunchKernelGGL((select_kernel<false, true>), sgrid, block, 0, stream, a, rows_cap);
+    } else {
+        if (vec) hipLaunchKernelGGL((select_kernel<true, false>), sgrid, block, 0, stream, a, rows_cap);
+        else hipLaunchKernelGGL((select_kernel<false, false>), sgrid, block, 0, stream, a, rows_cap);
     }
-    if (a.fused) return hipSuccess;
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (map) hipLaunchKernelGGL(finalize_kernel<true>, dim3((unsigned)a.batch), block, 0, stream, a);
+    else hipLaunchKernelGGL(finalize_kernel<false>, dim3((unsigned)a.batch), block, 0, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
     // Only the device knows which sequences end in a full-vocabulary draw; every other
     // workgroup returns at once.
     if (map) {

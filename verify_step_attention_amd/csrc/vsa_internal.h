@@ -25,12 +25,18 @@ constexpr int kWave = 64;
 // there, so any mix of calls and shapes can share one workspace in stream order. Counter i
 // has a line of its own for i < kCtrLines (counters sharing a line serialize each other's
 // atomics); beyond that, lines are shared round-robin.
+// The last 8 bytes of each line are a 64-bit word of its own (word64_at), so 32-bit
+// counters use the first 62 words of each line.
 constexpr int kCtrLines = 256;
-constexpr int kMaxCounters = kCtrLines * 64;
+constexpr int kMaxCounters = kCtrLines * 62;
 constexpr size_t kWsCounters = 256;                                // byte offset
 constexpr size_t kWsHeader = kWsCounters + (size_t)kCtrLines * 256; // first data byte
 __host__ __device__ __forceinline__ size_t ctr_slot(int i) {
     return (size_t)(i % kCtrLines) * 64 + (size_t)(i / kCtrLines);
+}
+// 64-bit word i (i < kCtrLines: one per line) of the counter region.
+__device__ __forceinline__ unsigned long long* word64_at(uint32_t* head, int i) {
+    return reinterpret_cast<unsigned long long*>(head + (size_t)(i % kCtrLines) * 64 + 62);
 }
 // A call that needs more than kMaxCounters counters keeps the rest in its own workspace
 // area (`extra`, compact), which a fill kernel clears at the start of the call.
@@ -105,10 +111,9 @@ template <int CTRL, int ROWS = 0xF>
 __device__ __forceinline__ void argmax_step(float& v, int& i) {
     const float ov = dpp_f<CTRL, ROWS>(v, v);
     const int oi = dpp_i<CTRL, ROWS>(i, i);
-    if (ov > v || (ov == v && oi < i)) {
-        v = ov;
-        i = oi;
-    }
+    const bool take = (ov > v) | ((ov == v) & (oi < i));  // selects, no divergent branch
+    v = take ? ov : v;
+    i = take ? oi : i;
 }
 __device__ __forceinline__ void wave_argmax(float& v, int& i) {
     argmax_step<kDppSwap1>(v, i);
@@ -264,13 +269,13 @@ constexpr int kMaxSeqRows = 32;      // verify rows per sequence (K <= 31)
 
 // Merged statistics of one row (finalize results, also handed to the race kernel).
 struct RowInfo {
-    double z;          // sum of exp(v - m) over the row (softmax normalizer)
+    double z;          // sum of exp((v - m) / T) over the row (softmax normalizer)
     float m;           // max of v over the row
     int argmax;        // greedy argmax (lowest id on ties)
     float theta;       // top-k threshold (value of the k-th largest)
     int kept_k, kept_p;
-    // nucleus without top-k: the kept set is {y >= ythr}, y = v / T (fp32 division), with
-    // mass zk = sum over it of 2^((y - ymax) log2 e); ythr = -inf otherwise
+    // nucleus without top-k: the kept set is {v >= ythr}, with mass zk = sum over it of
+    // e^((v - ymax) / T), ymax the row's max of v; ythr = -inf otherwise
     float ythr;
     float ymax;
     int pad;
@@ -285,6 +290,7 @@ struct KeepEntry {     // one id of a truncated, renormalized distribution
 
 struct RaceReq {       // a categorical draw over the whole vocabulary, done by race_kernel
     int kind;          // 0 none, 1 residual max(0, p - q), 2 bonus (p)
+    int onehot_d;      // kind 1 with a one-hot proposal: q = 1 at this id, 0 elsewhere; else -1
     int a;             // accepted drafts (the draw decides row a)
     int pos;           // absolute position of the draw
     int logprobs;
@@ -312,8 +318,8 @@ struct SampArgs {
     float* diag_thr;
     int32_t* diag_kept;
     uint32_t* err;
-    uint32_t* ctr;                 // counter region: sequence b's sweep arrivals at
-                                   // counter_at(2b), its race arrivals at counter_at(2b + 1)
+    uint32_t* ctr;                 // counter region: sequence b's arrivals at counter_at(4b)
+                                   // and counter_at(4b + 1) (see the kernels)
     uint32_t* ctr_x;               // counters past the region (or unused)
     float4* stats;                 // [slots][nchunk] (m, s, best value, best id bits)
     uint2* cand;                   // [slots][nchunk][capc] (ordered key, id)
@@ -322,11 +328,17 @@ struct SampArgs {
     KeepEntry* keep;               // [2T - B][keepcap]
     RaceReq* race;                 // [B]
     float4* race_part;             // [B][nchunk][4] race winners per (chunk, wave)
-    int fused;                     // the sweep workgroups run the race themselves
     // reduced draft vocabulary (after the rest, so the common fields keep their offsets)
     const int32_t* t2d;            // [V] draft id of each target id (-1: none) or null
     int dvocab;                    // draft vocabulary (V unless t2d is given)
+    int onehot;                    // the drafts are one-hot proposals (no draft rows)
+    uint32_t wait_ticks;           // fused kernel: how long (100 MHz ticks) a workgroup waits
+                                   // for its sequence's statistics before it hands its chunk
+                                   // of the draw to the last arriver
 };
+// The fused kernel keeps each sequence's counters and race words on lines 4b .. 4b + 3 and
+// its claim words on the lines after the first 4B.
+constexpr int kFusedMaxBatch = 60;
 
 // Every kernel argument in one round of scalar loads: the compiler otherwise spreads them
 // over several dependent round trips ahead of the first memory request.
@@ -339,7 +351,7 @@ __device__ __forceinline__ void preload_args(const SampArgs& a) {
                  "s"(a.top_ids), "s"(a.diag_thr), "s"(a.diag_kept), "s"(a.err),
                  "s"(a.ctr), "s"(a.ctr_x), "s"(a.stats), "s"(a.cand),
                  "s"(a.cand_meta), "s"(a.rows), "s"(a.keep), "s"(a.race), "s"(a.race_part),
-                 "s"(a.fused));
+                 "s"(a.onehot), "s"(a.wait_ticks));
 }
 
 struct SampPlan {
@@ -350,6 +362,8 @@ struct SampPlan {
 
 SampPlan plan_sample(int B, int total_rows, int V, int max_top_k, int max_top_lp);
 hipError_t launch_sample(const SampArgs& a, hipStream_t stream);
+bool fused_fits(const SampArgs& a);
+hipError_t launch_fused(const SampArgs& a, hipStream_t stream);
 hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t stream);
 hipError_t launch_draft_vocab_inverse(const int32_t* d2t, int dvocab, int vocab, int32_t* t2d,
                                       hipStream_t stream);

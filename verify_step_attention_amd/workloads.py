@@ -299,7 +299,8 @@ def device_tensors(w, device="cuda", with_kv=True):
     out["cu_rows"] = t(w.cu_rows.astype(np.int32))
     out["ctx_lens"] = t(w.ctx_lens.astype(np.int32))
     out["target_logits"] = t(w.target_logits)
-    out["draft_logits"] = t(w.draft_logits) if w.draft_logits.size else None
+    out["draft_logits"] = (t(w.draft_logits) if w.draft_logits is not None and w.draft_logits.size
+                           else None)
     out["draft_tokens"] = t(w.draft_tokens.astype(np.int32)) if w.draft_tokens.size else None
     out["token_counts"] = None if w.token_counts is None else t(w.token_counts.astype(np.int32))
     out["positions"] = t(w.positions.astype(np.int32))
