@@ -156,6 +156,34 @@ vsa_status verify_attention(const void* q, const void* k_cache, const void* v_ca
                             size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------
+ * verify_attention_noalloc
+ *
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): verify_attention without a workspace
+ * argument. Its partial results and counters live in a static device array of the library,
+ * VSA_NOALLOC_SCRATCH_BYTES (16 MiB) on each GPU, present from the library's load until the
+ * process ends. The call allocates nothing; its first call on a device looks up that
+ * device's copy and enqueues a kernel on `stream` that clears the copy's counters.
+ *
+ *   device_error  device pointer to a uint32 into which the device error bits are ORed
+ *                 (as in the workspace's error word), or NULL to drop them
+ *   every other argument as for verify_attention; the stream must belong to the current
+ *   device.
+ * Returns VSA_ERR_WORKSPACE when verify_attention_workspace_size() of the problem exceeds
+ * VSA_NOALLOC_SCRATCH_BYTES. Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (different streams, or different host threads without ordering)
+ * race and give undefined results; calls in stream order are safe.
+ * ------------------------------------------------------------------------------------ */
+#define VSA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+vsa_status verify_attention_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                    vsa_dtype dtype, const int32_t* cu_rows,
+                                    const int32_t* ctx_lens, int B, int total_rows, int Hq,
+                                    int Hkv, int D, int S_max, int max_rows_per_seq,
+                                    int max_kv_len, float scale, uint32_t flags, float* out,
+                                    uint32_t* device_error, void* stream);
+
+/* ------------------------------------------------------------------------------------
  * block_attention
  *
  * The same multi-row attention for a drafter's block over its context (Changelog

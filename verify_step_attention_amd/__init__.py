@@ -38,7 +38,7 @@ EXPORTED_SYMBOLS = ("vsa_version", "vsa_status_string", "verify_attention_worksp
                     "verify_sample_accept_workspace_size", "verify_sample_accept",
                     "draft_vocab_inverse", "verify_sample_accept_reduced_draft",
                     "verify_sample_accept_onehot",
-                    "small_m_qmm_workspace_size", "small_m_qmm")
+                    "small_m_qmm_workspace_size", "small_m_qmm", "verify_attention_noalloc")
 
 
 class VsaError(RuntimeError):
@@ -69,6 +69,11 @@ def _lib():
                                          c_int, c_int, c_int, c_int, c_int, c_int, c_int,
                                          c_int, c_float, ctypes.c_uint32, c_void, c_void,
                                          c_size, c_void]
+        lib.verify_attention_noalloc.restype = c_int
+        lib.verify_attention_noalloc.argtypes = [c_void, c_void, c_void, c_int, c_void, c_void,
+                                                 c_int, c_int, c_int, c_int, c_int, c_int,
+                                                 c_int, c_int, c_float, ctypes.c_uint32, c_void,
+                                                 c_void, c_void]
         lib.block_attention.restype = c_int
         lib.block_attention.argtypes = [c_void, c_void, c_void, c_int, c_void, c_void,
                                         c_int, c_int, c_int, c_int, c_int, c_int, c_int,
@@ -194,6 +199,28 @@ def verify_attention(q, k_cache, v_cache, cu_rows, ctx_lens, out, workspace, *,
                                  int(flags), _ptr(out), _ptr(workspace), workspace.numel(),
                                  _stream(stream))
     _check(st, "verify_attention")
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def verify_attention_noalloc(q, k_cache, v_cache, cu_rows, ctx_lens, out, device_error=None,
+                             *, max_rows_per_seq, max_kv_len, scale=0.0, flags=0, stream=None):
+    """verify_attention without a workspace: the library's static per-GPU scratch holds the
+    partial results. device_error: None or a one-element int32/uint32 device tensor that
+    receives the device error bits."""
+    dtype = _attention_dtype(q, k_cache, v_cache, out, cu_rows, ctx_lens, out)
+    if device_error is not None and (device_error.numel() < 1 or
+                                     device_error.element_size() != 4):
+        raise ValueError("device_error must hold one 32-bit word")
+    total, hq, d = q.shape
+    batch, hkv, s_max, _ = k_cache.shape
+    st = _lib().verify_attention_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), dtype,
+                                         _ptr(cu_rows), _ptr(ctx_lens), batch, total, hq, hkv,
+                                         d, s_max, int(max_rows_per_seq), int(max_kv_len),
+                                         float(scale), int(flags), _ptr(out),
+                                         _ptr(device_error), _stream(stream))
+    _check(st, "verify_attention_noalloc")
 
 
 def verify_attention_kvq(q, k_codes, k_sb, v_codes, v_sb, bits, cu_rows, ctx_lens, out,

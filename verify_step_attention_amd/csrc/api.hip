@@ -2,6 +2,8 @@
 #include <math.h>
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "vsa_internal.h"
 
 using namespace vsa;
@@ -65,12 +67,19 @@ vsa_status verify_attention(const void* q, const void* k_cache, const void* v_ca
                            workspace, workspace_bytes, stream);
 }
 
-vsa_status block_attention(const void* q, const void* k_cache, const void* v_cache,
-                           vsa_dtype dtype, const int32_t* cu_rows, const int32_t* ctx_lens,
-                           int B, int total_rows, int Hq, int Hkv, int D, int S_max,
-                           int max_rows_per_seq, int max_kv_len, float scale, int window,
-                           uint32_t flags, float* out, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The multi-row attention behind verify_attention, block_attention and
+// verify_attention_noalloc. err_word receives the device error bits; NULL means the
+// workspace's own error word (byte 0).
+vsa_status attention_call(const void* q, const void* k_cache, const void* v_cache,
+                          vsa_dtype dtype, const int32_t* cu_rows, const int32_t* ctx_lens,
+                          int B, int total_rows, int Hq, int Hkv, int D, int S_max,
+                          int max_rows_per_seq, int max_kv_len, float scale, int window,
+                          uint32_t flags, float* out, void* workspace, size_t workspace_bytes,
+                          uint32_t* err_word, void* stream) {
     if (!q || !k_cache || !v_cache || !cu_rows || !ctx_lens || !out) return VSA_ERR_INVALID_ARG;
     if (flags & ~(VSA_ATTN_DYNAMIC_SPLITS | VSA_ATTN_BIDIRECTIONAL | VSA_ATTN_SLIDING_WINDOW))
         return VSA_ERR_INVALID_ARG;
@@ -106,7 +115,7 @@ vsa_status block_attention(const void* q, const void* k_cache, const void* v_cac
     a.part_ml = reinterpret_cast<float2*>(ws + plan.off_ml);
     a.tile_ctr = reinterpret_cast<uint32_t*>(ws + kWsCounters);
     a.tile_ctr_x = reinterpret_cast<uint32_t*>(ws + plan.off_ctr_x);
-    a.err = reinterpret_cast<uint32_t*>(ws);
+    a.err = err_word ? err_word : reinterpret_cast<uint32_t*>(ws);
     a.batch = B;
     a.total_rows = total_rows;
     a.hq = Hq;
@@ -131,6 +140,76 @@ vsa_status block_attention(const void* q, const void* k_cache, const void* v_cac
     if (launch_attention(a, plan, dtype, static_cast<hipStream_t>(stream)) != hipSuccess)
         return VSA_ERR_LAUNCH;
     return VSA_OK;
+}
+
+// Scratch of verify_attention_noalloc: one copy per GPU, zero when the code object loads,
+// held until the process ends. Host code never passes `scratch` itself to a kernel (on the
+// host it is only a stand-in for the symbol); it uses the per-device address that
+// hipGetSymbolAddress returns.
+constexpr size_t kNoallocScratchBytes = VSA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's scratch address, looked up (and its header of error word and
+// counters cleared, by a kernel on `stream`) on the first call on that device.
+vsa_status device_scratch(hipStream_t stream, char** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return VSA_ERR_LAUNCH;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr ||
+            !aligned256(ptr))
+            return VSA_ERR_LAUNCH;
+        if (launch_zero_u32(static_cast<uint32_t*>(ptr), kWsHeader / 4, stream) != hipSuccess)
+            return VSA_ERR_LAUNCH;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = static_cast<char*>(g_scratch_ptr[dev]);
+    return VSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+vsa_status block_attention(const void* q, const void* k_cache, const void* v_cache,
+                           vsa_dtype dtype, const int32_t* cu_rows, const int32_t* ctx_lens,
+                           int B, int total_rows, int Hq, int Hkv, int D, int S_max,
+                           int max_rows_per_seq, int max_kv_len, float scale, int window,
+                           uint32_t flags, float* out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    return attention_call(q, k_cache, v_cache, dtype, cu_rows, ctx_lens, B, total_rows, Hq,
+                          Hkv, D, S_max, max_rows_per_seq, max_kv_len, scale, window, flags,
+                          out, workspace, workspace_bytes, nullptr, stream);
+}
+
+vsa_status verify_attention_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                    vsa_dtype dtype, const int32_t* cu_rows,
+                                    const int32_t* ctx_lens, int B, int total_rows, int Hq,
+                                    int Hkv, int D, int S_max, int max_rows_per_seq,
+                                    int max_kv_len, float scale, uint32_t flags, float* out,
+                                    uint32_t* device_error, void* stream) {
+    if (flags & ~VSA_ATTN_DYNAMIC_SPLITS) return VSA_ERR_INVALID_ARG;
+    const size_t need = verify_attention_workspace_size(B, Hq, Hkv, D, max_rows_per_seq,
+                                                        max_kv_len);
+    if (need > kNoallocScratchBytes) return VSA_ERR_WORKSPACE;
+    if (need == 0) {
+        // Not a supported problem: the regular checks name the reason before any set-up.
+        return attention_call(q, k_cache, v_cache, dtype, cu_rows, ctx_lens, B, total_rows,
+                              Hq, Hkv, D, S_max, max_rows_per_seq, max_kv_len, scale, 0,
+                              flags, out, nullptr, 0, device_error, stream);
+    }
+    char* ws = nullptr;
+    const vsa_status st = device_scratch(static_cast<hipStream_t>(stream), &ws);
+    if (st != VSA_OK) return st;
+    return attention_call(q, k_cache, v_cache, dtype, cu_rows, ctx_lens, B, total_rows, Hq,
+                          Hkv, D, S_max, max_rows_per_seq, max_kv_len, scale, 0, flags, out,
+                          ws, kNoallocScratchBytes, device_error, stream);
 }
 
 vsa_status verify_attention_kvq(const void* q, const uint8_t* k_codes, const void* k_sb,
