@@ -38,8 +38,8 @@ times block_attention alone on a drafter's block instead: B=4 blocks of 8 rows o
 32768-token context (32 q / 8 kv heads, D=128, bf16), attending the last W = 4096 context
 rows by default; one JSON line in the same form, rows = block rows.
 
-Prints one JSON line. Roofline: the dominant stage (attention: its main kernel and the
-split merge kernel) is timed per call with HIP events on the stream it runs on; its
+Prints one JSON line. Roofline: the dominant stage (attention: one kernel, which also
+merges its key splits) is timed per call with HIP events on the stream it runs on; its
 algorithmic bytes are the K/V of every sequence (ctx + R keys x Hkv x D x 2 bytes x 2), Q
 and the fp32 output. HBM traffic counters come from rocprofv3 runs recorded under profiles/
 and are reported only while the attention source still matches the one they were taken on.
@@ -287,7 +287,7 @@ def drafter_block_main(args):
                    "input_sets": len(sets), "attention_us": round(us, 2),
                    "attention_splits": "static" if args.static_splits else "dynamic"},
         "roofline": {"bound": "hbm", "kernel": "block_attention call (attn_bf16_kernel<128,"
-                     "1,true> + attn_merge_kernel<128>)", "achieved": round(achieved, 1),
+                     "1,true>)", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
                      "algorithmic_bytes_per_launch": nbytes},
@@ -443,8 +443,7 @@ def _counter_rows(d, counter):
 
 def record_traffic(fetch_dir, write_dir, copy_mib, command):
     """Turn two rocprofv3 --pmc runs of `bench.py --eager --copy-probe-mib M` (FETCH_SIZE, then
-    WRITE_SIZE) into bytes per verify_attention call (its main kernel plus the split merge
-    kernel). Each counter is scaled by what it reads for the plain copy of M MiB that the
+    WRITE_SIZE) into bytes per verify_attention call (its one kernel). Each counter is scaled by what it reads for the plain copy of M MiB that the
     run starts with (read M MiB, write M MiB)."""
     fetch = _counter_rows(fetch_dir, "FETCH_SIZE")
     write = _counter_rows(write_dir, "WRITE_SIZE")
@@ -460,7 +459,7 @@ def record_traffic(fetch_dir, write_dir, copy_mib, command):
         wb = float(np.median(write.get(k, [0.0]))) * 1024 / w_scale
         kernels[k] = {"fetch_bytes": round(fb), "write_bytes": round(wb),
                       "dispatches": len(fetch[k])}
-    attn = [k for k in kernels if "attn_bf16_kernel" in k or "attn_merge_kernel" in k]
+    attn = [k for k in kernels if "attn_bf16_kernel" in k]
     if not any("attn_bf16_kernel" in k for k in attn):
         raise SystemExit(f"no attention kernel in the counters: {list(kernels)}")
     a = {"fetch_bytes": sum(kernels[k]["fetch_bytes"] for k in attn),
@@ -768,11 +767,9 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": ("verify_attention call (attn_bf16_kernel<128,1,false> + "
-                       "attn_merge_kernel<128>)"
+            "kernel": ("verify_attention call (attn_bf16_kernel<128,1,false>)"
                        if kq is None else
-                       f"verify_attention_kvq call (attn_kvq_kernel<128,1,{kq.bits}> + "
-                       "attn_merge_kernel<128>)"),
+                       f"verify_attention_kvq call (attn_kvq_kernel<128,1,{kq.bits}>)"),
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",

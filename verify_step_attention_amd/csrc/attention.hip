@@ -31,6 +31,11 @@ constexpr int kThreads = 256;        // threads per workgroup (every kernel here
 constexpr int kMaxSplits = 32;       // key splits per (sequence, KV head)
 constexpr int kMergeGroup = 8;       // splits whose partials a merge thread loads together
 constexpr float kLazyLog2 = 8.f;     // online softmax: rescale only past this growth (log2)
+#ifndef VSA_ATTN_DMA_CPOL
+#define VSA_ATTN_DMA_CPOL 2
+#endif
+// Cache policy of the K/V tile DMAs: 2 = nt (streaming; each byte is read once per call).
+constexpr int kKvPolicy = VSA_ATTN_DMA_CPOL;
 
 // Block index -> (unit, split). Consecutive block ids go to different XCDs (round-robin
 // dispatch), so the splits of one unit are spread over the XCDs: the XCDs start their
@@ -41,16 +46,41 @@ __device__ __forceinline__ void map_block(int bid, int nsplit, int* unit, int* s
     *split = bid % nsplit;
 }
 
+// One tile claim of the dynamic schedule: thread 0 reads the result only at the next
+// barrier, so the claim's round trip overlaps the tile in flight. atomicInc with the
+// largest limit is a plain increment; unlike atomicAdd, the compiler does not rewrite it
+// into a wave-wide form that reads the result (and so waits for every earlier load of the
+// wave, DMAs included, which complete in issue order) right after issuing it.
+__device__ __forceinline__ uint32_t claim_tile(uint32_t* ctr) {
+    return atomicInc(ctr, 0xFFFFFFFFu);
+}
+
 struct SeqGeom {
     int r0, rows, ctx;
     bool ok;
 };
 
-__device__ __forceinline__ SeqGeom seq_geometry(const AttnArgs& a, int b, bool report) {
+// The raw geometry words of sequence b: cu_rows[b], cu_rows[b + 1], ctx_lens[b].
+struct GeomWords {
+    int r0, r1, ctx;
+};
+
+// Read through the constant address space: scalar loads, whose completion does not wait
+// for the vector loads and DMAs issued before them (those complete in issue order). The
+// arrays are inputs that no kernel of the call writes.
+typedef __attribute__((address_space(4))) const int const_int;
+
+__device__ __forceinline__ GeomWords load_geometry(const AttnArgs& a, int b) {
+    const const_int* cu = (const const_int*)a.cu_rows;
+    const const_int* cl = (const const_int*)a.ctx_lens;
+    return GeomWords{cu[b], cu[b + 1], cl[b]};
+}
+
+__device__ __forceinline__ SeqGeom seq_geometry(const AttnArgs& a, GeomWords w, bool report) {
     SeqGeom s;
-    s.r0 = a.cu_rows[b];
-    s.rows = a.cu_rows[b + 1] - s.r0;
-    s.ctx = a.ctx_lens[b];
+    s.r0 = w.r0;
+    s.rows = w.r1 - w.r0;
+    s.ctx = w.ctx;
     bool bad = false;
     if (s.rows > a.max_rows) { s.rows = a.max_rows; bad = true; }
     if (s.ctx < 0) { s.ctx = 0; bad = true; }
@@ -62,6 +92,10 @@ __device__ __forceinline__ SeqGeom seq_geometry(const AttnArgs& a, int b, bool r
     if (!s.ok) bad = true;
     if (bad && report) set_device_error(a.err, VSA_DEVERR_SEQ_SHAPE);
     return s;
+}
+
+__device__ __forceinline__ SeqGeom seq_geometry(const AttnArgs& a, int b, bool report) {
+    return seq_geometry(a, load_geometry(a, b), report);
 }
 
 // Keys a block row sees. Verify: window 0, causal, so row i sees keys 0 .. ctx + i. A
@@ -97,11 +131,102 @@ struct LdsQuad {
     }
 };
 
+// The end of every split of a (sequence, KV head) unit when the keys are split: the split
+// counts itself in on the unit's arrival counter after its partial state is stored (with
+// the hand-off stores: written through to the device-coherent level), and the last of the
+// unit's splits to arrive merges them,
+//   out = sum_s w_s O_s,   w_s = 2^(m_s - m) / sum_s' 2^(m_s' - m) l_s',   m = max_s m_s,
+// the (max, sum) and O of up to kMergeGroup splits loaded together. It also returns the unit's tile-claim and arrival counters to zero. A unit
+// whose geometry is invalid (merge = false) only counts in, so that its counters return to
+// zero as well.
+template <int D>
+__device__ void attn_finish_unit(const AttnArgs& a, int unit, int g, const SeqGeom& s,
+                                 bool merge) {
+    constexpr int D4 = D / 4;
+    constexpr int SG = kMergeGroup;
+    __shared__ int s_last;
+    uint32_t* const arrive = counter_at(a.tile_ctr, a.tile_ctr_x, a.units + unit);
+    if (!handoff_arrive(arrive, (uint32_t)a.nsplit, &s_last)) return;
+    if (a.dyn && threadIdx.x == 0)
+        __hip_atomic_store(counter_at(a.tile_ctr, a.tile_ctr_x, unit), 0u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    if (!merge) return;
+    // Thread tasks: output float4s e, e + 256, e + 512 (column e / (D/4), consecutive
+    // lanes on consecutive float4s); the loads of all three tasks and up to kMergeGroup
+    // splits are in flight together.
+    constexpr int TPT = 3;
+    const int M = s.rows * a.group;
+    const int ntask = M * D4;
+    const int ns = a.nsplit;
+    const size_t base = (size_t)unit * ns;
+    const size_t sstride = (size_t)a.mcap * D4;              // float4s between splits
+    const float2* pml = a.part_ml + base * a.mcap;
+    const float4* po = reinterpret_cast<const float4*>(a.part_o) + base * a.mcap * D4;
+    for (int e0 = threadIdx.x; e0 < ntask; e0 += TPT * kThreads) {
+        float m_run[TPT], l_run[TPT];
+        float4 acc[TPT];
+#pragma unroll
+        for (int t = 0; t < TPT; ++t) {
+            m_run[t] = kNegInf;
+            l_run[t] = 0.f;
+            acc[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        for (int s0 = 0; s0 < ns; s0 += SG) {
+            float2 ml[TPT][SG];
+            float4 v[TPT][SG];
+#pragma unroll
+            for (int t = 0; t < TPT; ++t) {
+                int e = e0 + t * kThreads;
+                e = e < ntask ? e : ntask - 1;                   // in bounds; dropped below
+                const int n = e / D4;
+#pragma unroll
+                for (int u = 0; u < SG; ++u) {
+                    const int sp = s0 + u < ns ? s0 + u : ns - 1;
+                    ml[t][u] = handoff_load(pml + (size_t)sp * a.mcap + n);
+                    v[t][u] = handoff_load4(po + sp * sstride + e);
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < TPT; ++t) {
+                float m = m_run[t];
+#pragma unroll
+                for (int u = 0; u < SG; ++u)
+                    if (s0 + u < ns) m = fmaxf(m, ml[t][u].x);
+                if (m == kNegInf) continue;
+                const float c = exp2f(m_run[t] - m);             // m_run = -inf gives 0
+                l_run[t] *= c;
+                acc[t] = make_float4(acc[t].x * c, acc[t].y * c, acc[t].z * c, acc[t].w * c);
+#pragma unroll
+                for (int u = 0; u < SG; ++u) {
+                    const float f =
+                        (s0 + u < ns && ml[t][u].x != kNegInf) ? exp2f(ml[t][u].x - m) : 0.f;
+                    l_run[t] += f * ml[t][u].y;
+                    acc[t].x += f * v[t][u].x;
+                    acc[t].y += f * v[t][u].y;
+                    acc[t].z += f * v[t][u].z;
+                    acc[t].w += f * v[t][u].w;
+                }
+                m_run[t] = m;
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < TPT; ++t) {
+            const int e = e0 + t * kThreads;
+            if (e >= ntask) break;
+            const int n = e / D4, d4 = e % D4;
+            const float il = 1.f / l_run[t];
+            const int row = s.r0 + n / a.group, head = g * a.group + n % a.group;
+            *(reinterpret_cast<float4*>(a.out + ((size_t)row * a.hq + head) * D) + d4) =
+                make_float4(acc[t].x * il, acc[t].y * il, acc[t].z * il, acc[t].w * il);
+        }
+    }
+}
+
 // Combines the key groups of one workgroup and writes either the final output (single
 // split) or this split's partial state (O relative to the split's max, unnormalized; max in
-// log2 units; sum), which the merge kernel combines after this kernel. The O of key group k
-// (relative to its own max) for columns 32 j .. 32 j + 31 is at ob[k * NBX + j], rows OS
-// floats apart.
+// log2 units; sum), which the unit's last split to finish merges (attn_finish_unit). The
+// O of key group k (relative to its own max) for columns 32 j .. 32 j + 31 is at
+// ob[k * NBX + j], rows OS floats apart.
 template <int D, int KGX, int NBX>
 __device__ void attn_epilogue(const AttnArgs& a, LdsQuad ob, float* st, int unit, int split,
                               int g, const SeqGeom& s, int OS) {
@@ -149,25 +274,28 @@ __device__ void attn_epilogue(const AttnArgs& a, LdsQuad ob, float* st, int unit
             *reinterpret_cast<float4*>(a.out + ((size_t)row * a.hq + head) * D + d) =
                 make_float4(o.x * il, o.y * il, o.z * il, o.w * il);
         } else {
-            *reinterpret_cast<float4*>(a.part_o + (pslot * a.mcap + n) * D + d) = o;
+            handoff_store4(reinterpret_cast<float4*>(a.part_o + (pslot * a.mcap + n) * D + d), o);
         }
     }
     if (a.nsplit == 1) return;
     for (int n = tid; n < M; n += kThreads)
-        a.part_ml[pslot * a.mcap + n] = make_float2(wm[n], wl[n]);
+        handoff_store(a.part_ml + pslot * a.mcap + n, make_float2(wm[n], wl[n]));
+    attn_finish_unit<D>(a, unit, g, s, true);
 }
 
 // A split that owns no tile publishes an empty state (m = -inf, l = 0, O = 0), which
 // adds nothing in the merge.
 template <int D>
-__device__ void attn_empty_split(const AttnArgs& a, int unit, int split, const SeqGeom& s) {
+__device__ void attn_empty_split(const AttnArgs& a, int unit, int split, int g,
+                                 const SeqGeom& s) {
     const int M = s.rows * a.group;
     const size_t pslot = (size_t)unit * a.nsplit + split;
     for (int e = threadIdx.x; e < M * (D / 4); e += kThreads)
-        reinterpret_cast<float4*>(a.part_o + (pslot * a.mcap) * D)[e] =
-            make_float4(0.f, 0.f, 0.f, 0.f);
+        handoff_store4(reinterpret_cast<float4*>(a.part_o + (pslot * a.mcap) * D) + e,
+                       make_float4(0.f, 0.f, 0.f, 0.f));
     for (int n = threadIdx.x; n < M; n += kThreads)
-        a.part_ml[pslot * a.mcap + n] = make_float2(kNegInf, 0.f);
+        handoff_store(a.part_ml + pslot * a.mcap + n, make_float2(kNegInf, 0.f));
+    attn_finish_unit<D>(a, unit, g, s, true);
 }
 
 // -------------------------------------------------------------------------- bf16 / MFMA
@@ -233,6 +361,9 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const AttnArgs a) {
     const size_t kv_off = ((size_t)b * a.hkv + g) * (size_t)a.s_max * D;
     const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k) + kv_off;
     const uint16_t* vbase = reinterpret_cast<const uint16_t*>(a.v) + kv_off;
+    // The geometry words go out before the first tile's DMA: vector loads complete in
+    // issue order, so issued after it they would wait for the whole tile.
+    const GeomWords geo = load_geometry(a, b);
 
     // DMA of tile t: wave w fills blocks w, w + 4, ... of K and of V (so a wave only ever
     // waits for its own blocks). Keys at or past key_lim read key key_lim - 1.
@@ -250,9 +381,9 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const AttnArgs a) {
             for (int i = 0; i < BPW; ++i) {
                 const int blk = i * 4 + wave;
                 __builtin_amdgcn_global_load_lds(kb + blk * 1024 + dma_off,
-                                                 (lds_void*)(kt + blk * 1024), 16, 0, 0);
+                                                 (lds_void*)(kt + blk * 1024), 16, 0, kKvPolicy);
                 __builtin_amdgcn_global_load_lds(vb + blk * 1024 + dma_off,
-                                                 (lds_void*)(vt + blk * 1024), 16, 0, 0);
+                                                 (lds_void*)(vt + blk * 1024), 16, 0, kKvPolicy);
             }
             return;
         }
@@ -263,8 +394,8 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const AttnArgs a) {
             int key = t * TK + r;
             key = key < key_lim ? key : key_lim - 1;
             const size_t src = (size_t)key * D + (size_t)((dma_pos ^ kv_swz<D>(r)) * 8);
-            __builtin_amdgcn_global_load_lds(kbase + src, (lds_void*)(kt + blk * 1024), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(vbase + src, (lds_void*)(vt + blk * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(kbase + src, (lds_void*)(kt + blk * 1024), 16, 0, kKvPolicy);
+            __builtin_amdgcn_global_load_lds(vbase + src, (lds_void*)(vt + blk * 1024), 16, 0, kKvPolicy);
         }
     };
     // Tiles. With >= 4 splits the streamed tiles are the F = L / TK full ones, and the last
@@ -298,13 +429,17 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const AttnArgs a) {
     key_lim = kv_cap;
     if (t_spec >= 0) issue_tile(t_spec, k0s, v0s);
     uint32_t* const ctr = counter_at(a.tile_ctr, a.tile_ctr_x, unit);
-    uint32_t claim = 0;                                // thread 0: the pending claim
-    if (dyn && tid == 0) claim = atomicAdd(ctr, 1u);
+    // thread 0: the pending claim. Left undefined in the other threads (which never read
+    // it): a constant there would be a second write to the register the atomic returns
+    // into, and the compiler would wait for the atomic (queued behind the DMA) at once.
+    uint32_t claim;
+    if (dyn && tid == 0) claim = claim_tile(ctr);
     __shared__ int s_next[2];
 
-    const SeqGeom s = seq_geometry(a, b, tid == 0 && split == 0 && g == 0);
+    const SeqGeom s = seq_geometry(a, geo, tid == 0 && split == 0 && g == 0);
     if (!s.ok) {
         __builtin_amdgcn_s_waitcnt(0);                 // no DMA outlives the workgroup
+        if (a.nsplit > 1) attn_finish_unit<D>(a, unit, g, s, false);
         return;
     }
     const int L = s.ctx + s.rows;                      // keys of this sequence
@@ -327,7 +462,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const AttnArgs a) {
     // a split without a first tile has no tile at all (dynamic: nsplit + c > split >= nt)
     if (t_first < 0 && tail_b >= tail_e) {
         __builtin_amdgcn_s_waitcnt(0);                 // no DMA outlives the workgroup
-        attn_empty_split<D>(a, unit, split, s);
+        attn_empty_split<D>(a, unit, split, g, s);
         return;
     }
     if (t_first >= 0 && (t0 != 0 || t_first != t_spec)) {
@@ -353,8 +488,8 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const AttnArgs a) {
             int key = tail_b + r;
             key = key < tail_e ? key : tail_e - 1;
             const size_t src = (size_t)key * D + (size_t)((dma_pos ^ kv_swz<D>(r)) * 8);
-            __builtin_amdgcn_global_load_lds(kbase + src, (lds_void*)(kts + blk * 1024), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(vbase + src, (lds_void*)(vts + blk * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(kbase + src, (lds_void*)(kts + blk * 1024), 16, 0, kKvPolicy);
+            __builtin_amdgcn_global_load_lds(vbase + src, (lds_void*)(vts + blk * 1024), 16, 0, kKvPolicy);
         }
     }
     // Keys below the first one any row sees (a window) may share its tile; a V row is
@@ -512,7 +647,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const AttnArgs a) {
         __syncthreads();
         const int tn = s_next[par];
         if (tn >= t_last) return -1;
-        if (dyn && tid == 0) claim = atomicAdd(ctr, 1u);
+        if (dyn && tid == 0) claim = claim_tile(ctr);
         return tn;
     };
     if (t_first < 0) {
@@ -736,11 +871,12 @@ __global__ __launch_bounds__(256, 1) void attn_kvq_kernel(const AttnArgs a) {
     if (t_spec >= 0) issue_tile(t_spec, k0s, v0s);
     uint32_t* const ctr = counter_at(a.tile_ctr, a.tile_ctr_x, unit);
     uint32_t claim = 0;
-    if (dyn && tid == 0) claim = atomicAdd(ctr, 1u);
+    if (dyn && tid == 0) claim = claim_tile(ctr);
 
     const SeqGeom s = seq_geometry(a, b, tid == 0 && split == 0 && g == 0);
     if (!s.ok) {
         __builtin_amdgcn_s_waitcnt(0);
+        if (a.nsplit > 1) attn_finish_unit<D>(a, unit, g, s, false);
         return;
     }
     const int L = s.ctx + s.rows;
@@ -756,7 +892,7 @@ __global__ __launch_bounds__(256, 1) void attn_kvq_kernel(const AttnArgs a) {
     key_lim = L;
     if (t_first < 0 && tail_b >= tail_e) {
         __builtin_amdgcn_s_waitcnt(0);
-        attn_empty_split<D>(a, unit, split, s);
+        attn_empty_split<D>(a, unit, split, g, s);
         return;
     }
     // The speculative tile is kept as it landed: rows past the sequence hold finite codes
@@ -1040,7 +1176,7 @@ __global__ __launch_bounds__(256, 1) void attn_kvq_kernel(const AttnArgs a) {
         __syncthreads();
         const int tn = s_next[par];
         if (tn >= t_last) return -1;
-        if (dyn && tid == 0) claim = atomicAdd(ctr, 1u);
+        if (dyn && tid == 0) claim = claim_tile(ctr);
         return tn;
     };
 
@@ -1127,7 +1263,10 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const AttnArgs a) {
     const int b = unit / a.hkv, g = unit % a.hkv;
     const int tid = threadIdx.x;
     const SeqGeom s = seq_geometry(a, b, tid == 0 && split == 0 && g == 0);
-    if (!s.ok) return;
+    if (!s.ok) {
+        if (a.nsplit > 1) attn_finish_unit<D>(a, unit, g, s, false);
+        return;
+    }
     const int M = s.rows * a.group;
     const int L = s.ctx + s.rows;
     const int lo_first = key_lo(a, s, 0);
@@ -1141,7 +1280,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const AttnArgs a) {
     float* ls = st + kStatCap;                           // [MC]      (epilogue gl)
     float* ss = os + MCOLS * D + 5 * MCOLS;              // [MCOLS][TK]
     if (t_begin >= t_end) {
-        attn_empty_split<D>(a, unit, split, s);
+        attn_empty_split<D>(a, unit, split, g, s);
         return;
     }
 
@@ -1213,72 +1352,6 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const AttnArgs a) {
 }
 
 
-// -------------------------------------------------------------------------- split merge
-// Runs after the attention kernel (stream order makes every partial visible):
-//   out = sum_s w_s O_s,   w_s = 2^(m_s - m) / sum_s' 2^(m_s' - m) l_s',   m = max_s m_s
-// over the key splits s of one (sequence, KV head) unit. Thread e of the unit's slice owns
-// column n = e / (D/4) and 4 consecutive d; the geometry, (max, sum) and O loads of up to
-// kMergeGroup splits are issued together, so one memory round trip covers <= 8 splits.
-// Columns past the sequence's M read workspace slots nobody wrote this call; their
-// results are computed and dropped.
-template <int D>
-__global__ __launch_bounds__(256) void attn_merge_kernel(const AttnArgs a) {
-    constexpr int D4 = D / 4;
-    constexpr int SG = kMergeGroup;
-    const int chunks = (a.mcap * D4 + kThreads - 1) / kThreads;
-    const int unit = blockIdx.x / chunks;
-    const int e = (blockIdx.x % chunks) * kThreads + threadIdx.x;
-    if (unit >= a.units) return;
-    // the attention kernel has finished: its tile counter returns to zero for the next call
-    if (a.dyn && e == 0) __hip_atomic_store(counter_at(a.tile_ctr, a.tile_ctr_x, unit), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (e >= a.mcap * D4) return;
-    const int b = unit / a.hkv, g = unit % a.hkv;
-    const int n = e / D4, d4 = e % D4;
-    const int ns = a.nsplit;
-    const size_t base = (size_t)unit * ns;
-    const float2* pml = a.part_ml + base * a.mcap + n;
-    const float4* po = reinterpret_cast<const float4*>(a.part_o) + (base * a.mcap + n) * D4 + d4;
-    const size_t sstride = (size_t)a.mcap * D4;              // float4s between splits
-
-    float m_run = kNegInf, l_run = 0.f;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    SeqGeom s{};
-    for (int s0 = 0; s0 < ns; s0 += SG) {
-        float2 ml[SG];
-        float4 v[SG];
-#pragma unroll
-        for (int u = 0; u < SG; ++u) {
-            const int sp = s0 + u < ns ? s0 + u : ns - 1;    // in bounds; dropped below
-            ml[u] = pml[(size_t)sp * a.mcap];
-            v[u] = po[sp * sstride];
-        }
-        if (s0 == 0) s = seq_geometry(a, b, false);
-        float m = m_run;
-#pragma unroll
-        for (int u = 0; u < SG; ++u)
-            if (s0 + u < ns) m = fmaxf(m, ml[u].x);
-        if (m == kNegInf) continue;
-        const float c = exp2f(m_run - m);                    // m_run = -inf gives 0
-        l_run *= c;
-        acc = make_float4(acc.x * c, acc.y * c, acc.z * c, acc.w * c);
-#pragma unroll
-        for (int u = 0; u < SG; ++u) {
-            const float f = (s0 + u < ns && ml[u].x != kNegInf) ? exp2f(ml[u].x - m) : 0.f;
-            l_run += f * ml[u].y;
-            acc.x += f * v[u].x;
-            acc.y += f * v[u].y;
-            acc.z += f * v[u].z;
-            acc.w += f * v[u].w;
-        }
-        m_run = m;
-    }
-    if (!s.ok || n >= s.rows * a.group) return;
-    const float il = 1.f / l_run;
-    const int row = s.r0 + n / a.group, head = g * a.group + n % a.group;
-    *reinterpret_cast<float4*>(a.out + ((size_t)row * a.hq + head) * D + 4 * d4) =
-        make_float4(acc.x * il, acc.y * il, acc.z * il, acc.w * il);
-}
-
 }  // namespace
 
 AttnPlan plan_attention(int B, int Hq, int Hkv, int D, int max_rows, int max_kv_len) {
@@ -1297,7 +1370,7 @@ AttnPlan plan_attention(int B, int Hq, int Hkv, int D, int max_rows, int max_kv_
     if (nsplit < 1) nsplit = 1;
     p.nsplit = nsplit;
     size_t off = kWsHeader;                                      // error word, counters
-    p.n_ctr_x = extra_counters(p.units);
+    p.n_ctr_x = extra_counters(2L * p.units);       // tile claims, then arrivals
     p.off_ctr_x = off;
     off += (p.n_ctr_x * 4 + 255) / 256 * 256;
     p.off_ml = off;
@@ -1346,11 +1419,6 @@ hipError_t launch_attention(const AttnArgs& a, const AttnPlan& p, vsa_dtype dtyp
     } else {
         if (a.d == 128) hipLaunchKernelGGL((attn_f32_kernel<128>), grid, block, 0, stream, a);
         else hipLaunchKernelGGL((attn_f32_kernel<64>), grid, block, 0, stream, a);
-    }
-    if (p.nsplit > 1) {
-        const dim3 mgrid(p.units * ((p.mcap * (a.d / 4) + kThreads - 1) / kThreads));
-        if (a.d == 128) hipLaunchKernelGGL((attn_merge_kernel<128>), mgrid, block, 0, stream, a);
-        else hipLaunchKernelGGL((attn_merge_kernel<64>), mgrid, block, 0, stream, a);
     }
     return hipGetLastError();
 }
