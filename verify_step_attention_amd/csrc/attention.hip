@@ -827,9 +827,9 @@ __global__ __launch_bounds__(256, 1) void attn_kvq_kernel(const AttnArgs a) {
             for (int i = 0; i < BPW; ++i) {
                 const int blk = i * 4 + wave;
                 __builtin_amdgcn_global_load_lds(kb + blk * 1024 + dma_off,
-                                                 (lds_void*)(kt + blk * 1024), 16, 0, 0);
+                                                 (lds_void*)(kt + blk * 1024), 16, 0, kKvPolicy);
                 __builtin_amdgcn_global_load_lds(vb + blk * 1024 + dma_off,
-                                                 (lds_void*)(vt + blk * 1024), 16, 0, 0);
+                                                 (lds_void*)(vt + blk * 1024), 16, 0, kKvPolicy);
             }
         } else {
 #pragma unroll
@@ -839,8 +839,8 @@ __global__ __launch_bounds__(256, 1) void attn_kvq_kernel(const AttnArgs a) {
                 int key = t * TK + r;
                 key = key < key_lim ? key : key_lim - 1;
                 const size_t src = (size_t)key * ROWB + (size_t)((dma_pos ^ code_swz<ROWB>(r)) << 4);
-                __builtin_amdgcn_global_load_lds(kbase + src, (lds_void*)(kt + blk * 1024), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(vbase + src, (lds_void*)(vt + blk * 1024), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(kbase + src, (lds_void*)(kt + blk * 1024), 16, 0, kKvPolicy);
+                __builtin_amdgcn_global_load_lds(vbase + src, (lds_void*)(vt + blk * 1024), 16, 0, kKvPolicy);
             }
         }
         if (wave * 256 < SBB) {
@@ -848,8 +848,8 @@ __global__ __launch_bounds__(256, 1) void attn_kvq_kernel(const AttnArgs a) {
             int key = t * TK + r;
             key = key < key_lim ? key : key_lim - 1;
             const size_t src = (size_t)key * SBROW + sb_byte % SBROW;
-            __builtin_amdgcn_global_load_lds(ksbase + src, (lds_void*)(kt + CODEB + wave * 256), 4, 0, 0);
-            __builtin_amdgcn_global_load_lds(vsbase + src, (lds_void*)(vt + CODEB + wave * 256), 4, 0, 0);
+            __builtin_amdgcn_global_load_lds(ksbase + src, (lds_void*)(kt + CODEB + wave * 256), 4, 0, kKvPolicy);
+            __builtin_amdgcn_global_load_lds(vsbase + src, (lds_void*)(vt + CODEB + wave * 256), 4, 0, kKvPolicy);
         }
     };
 
@@ -870,7 +870,7 @@ __global__ __launch_bounds__(256, 1) void attn_kvq_kernel(const AttnArgs a) {
     key_lim = kv_cap;
     if (t_spec >= 0) issue_tile(t_spec, k0s, v0s);
     uint32_t* const ctr = counter_at(a.tile_ctr, a.tile_ctr_x, unit);
-    uint32_t claim = 0;
+    uint32_t claim;                                    // thread 0 only (see the bf16 kernel)
     if (dyn && tid == 0) claim = claim_tile(ctr);
 
     const SeqGeom s = seq_geometry(a, b, tid == 0 && split == 0 && g == 0);
@@ -909,15 +909,15 @@ __global__ __launch_bounds__(256, 1) void attn_kvq_kernel(const AttnArgs a) {
             int key = tail_b + r;
             key = key < tail_e ? key : tail_e - 1;
             const size_t src = (size_t)key * ROWB + (size_t)((dma_pos ^ code_swz<ROWB>(r)) << 4);
-            __builtin_amdgcn_global_load_lds(kbase + src, (lds_void*)(kts + wave * 1024), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(vbase + src, (lds_void*)(vts + wave * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(kbase + src, (lds_void*)(kts + wave * 1024), 16, 0, kKvPolicy);
+            __builtin_amdgcn_global_load_lds(vbase + src, (lds_void*)(vts + wave * 1024), 16, 0, kKvPolicy);
         }
         if (wave == 0 && lane * 4 < TSBB) {
             int key = tail_b + lane * 4 / SBROW;
             key = key < tail_e ? key : tail_e - 1;
             const size_t src = (size_t)key * SBROW + (lane * 4) % SBROW;
-            __builtin_amdgcn_global_load_lds(ksbase + src, (lds_void*)(kts + TCODEB), 4, 0, 0);
-            __builtin_amdgcn_global_load_lds(vsbase + src, (lds_void*)(vts + TCODEB), 4, 0, 0);
+            __builtin_amdgcn_global_load_lds(ksbase + src, (lds_void*)(kts + TCODEB), 4, 0, kKvPolicy);
+            __builtin_amdgcn_global_load_lds(vsbase + src, (lds_void*)(vts + TCODEB), 4, 0, kKvPolicy);
         }
     }
 

@@ -1057,16 +1057,165 @@ __global__ __launch_bounds__(kThreads) void race_kernel(const SampArgs a) {
                                         : __builtin_nanf("");
 }
 
+// ------------------------------------------------------------------ wave-layout chunk
+// A whole chunk of one row in one wave: lane l holds the float4s l + 64 j (j < 8), that is
+// ids base + 4 (l + 64 j) + i (i < 4) as element e = 4 j + i. The candidate phase of the
+// sweep gives each truncated row to one wave: rows proceed side by side without workgroup
+// barriers, each wave loads its next row while it works on the current one, and the code
+// of one row is reused for the next (straight-line code that runs once per workgroup is
+// bound by instruction fetch).
+constexpr int kWj = kChunk / 256;                 // float4s per lane
+constexpr int kWe = 4 * kWj;                      // ids per lane
+__device__ __forceinline__ int welem_id(int base, int lane, int e) {
+    return base + 4 * (lane + 64 * (e >> 2)) + (e & 3);
+}
+template <bool VEC, class T>
+__device__ __forceinline__ void wload4(const T* row, int base, int vocab, int lane, T fill,
+                                       T (&x)[kWe]) {
+    if (VEC) {
+#pragma unroll
+        for (int j = 0; j < kWj; ++j) {
+            const int id0 = base + 4 * (lane + 64 * j);
+            if (id0 < vocab) {
+                const auto v = *reinterpret_cast<const decltype(make_float4(0, 0, 0, 0))*>(
+                    reinterpret_cast<const float*>(row) + id0);
+                x[4 * j] = __builtin_bit_cast(T, v.x);
+                x[4 * j + 1] = __builtin_bit_cast(T, v.y);
+                x[4 * j + 2] = __builtin_bit_cast(T, v.z);
+                x[4 * j + 3] = __builtin_bit_cast(T, v.w);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x[4 * j + i] = fill;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < kWe; ++e) {
+            const int id = welem_id(base, lane, e);
+            x[e] = id < vocab ? row[id] : fill;
+        }
+    }
+}
+// Row r's values at the chunk's ids in the wave layout (draft rows through t2d when MAP),
+// and for target rows the base counts.
+template <bool VEC, bool MAP>
+__device__ __forceinline__ void wload_row(const SampArgs& a, const SeqMode& m, const RowRef& r,
+                                          int b, int base, int lane, float (&x)[kWe],
+                                          int (&cnt)[kWe]) {
+    if (r.kind != 1 || !MAP) {
+        const float* row = r.kind == 1 ? a.dl + (size_t)(m.d0 + r.i - 1) * a.vocab
+                                       : a.tl + (size_t)(m.r0 + r.i) * a.vocab;
+        wload4<VEC>(row, base, a.vocab, lane, kNegInf, x);
+    } else {
+        const float* row = a.dl + (size_t)(m.d0 + r.i - 1) * a.dvocab;
+        int map[kWe];
+        wload4<VEC>(a.t2d, base, a.vocab, lane, -1, map);
+        uint32_t ebits = 0;
+#pragma unroll
+        for (int e = 0; e < kWe; ++e) x[e] = mapped_logit(a, row, map[e], &ebits);
+        if (ebits) atomicOr(a.err, ebits);
+    }
+    if (r.kind == 0 && a.counts)
+        wload4<VEC>(a.counts + (size_t)b * a.vocab, base, a.vocab, lane, 0, cnt);
+    else {
+#pragma unroll
+        for (int e = 0; e < kWe; ++e) cnt[e] = 0;
+    }
+}
+
+// Candidates of one truncated or top-n row in this chunk, by one wave, from its loaded
+// values: every key >= vk for a vk at or below the chunk's kk-th largest key. vk is the
+// largest 16-bit-prefixed value T such that at least kk of the lanes' group maxima (the
+// maxima of 1, 2 or 4 disjoint groups of each lane's ids as kk needs: distinct ids) are
+// >= T, found by a binary search with ballot counts; it lies within 2^-7 of the kk-th
+// largest of those maxima, so the candidates are usually the kk largest and a few more.
+// Returns false when they do not fit in capc slots (the workgroup path then takes the row
+// and rewrites its slots).
+__device__ bool wave_row_candidates(const SampArgs& a, const SeqMode& m, const RowRef& r,
+                                    int c, int base, const int* s_draft, int kk,
+                                    const float (&x)[kWe], int (&cnt)[kWe]) {
+    const int lane = threadIdx.x & 63;
+    if (r.kind == 0) {
+        // the drafts d_1 .. d_i before target row i add to the counts
+        for (int t = 0; t < r.i; ++t) {
+            const int off = s_draft[t] - base;
+            if (off < 0 || off >= kChunk || ((off >> 2) & 63) != lane) continue;
+            const int ee = 4 * (off >> 8) + (off & 3);
+#pragma unroll
+            for (int e = 0; e < kWe; ++e) cnt[e] += e == ee ? 1 : 0;
+        }
+    }
+    uint32_t key[kWe];
+    uint32_t valid = 0u;
+#pragma unroll
+    for (int e = 0; e < kWe; ++e) {
+        const bool in = welem_id(base, lane, e) < a.vocab;
+        const float val = r.kind == 0 ? penalize(x[e], cnt[e], m.pp, m.fp) : x[e];
+        key[e] = in ? ord_key(val) : 0u;
+        valid |= (in ? 1u : 0u) << e;
+    }
+    const int n_valid = min(kChunk, a.vocab - base);
+    uint32_t vk = 0u;
+    if (n_valid > kk) {
+        // the maxima of 1, 2 or 4 disjoint groups of the lane's ids (distinct ids; invalid
+        // ids are 0, below every key), as kk needs
+        const int ng = kk <= 16 ? 1 : kk <= 32 ? 2 : 4;
+        uint32_t g8[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) g8[i] = max(max(key[i], key[i + 8]), max(key[i + 16], key[i + 24]));
+        uint32_t gm[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) gm[i] = max(g8[i], g8[i + 4]);      // groups e mod 4
+        if (ng <= 2) {
+            gm[0] = max(gm[0], gm[2]);
+            gm[1] = max(gm[1], gm[3]);
+            gm[2] = gm[3] = 0u;
+        }
+        if (ng == 1) {
+            gm[0] = max(gm[0], gm[1]);
+            gm[1] = 0u;
+        }
+        uint32_t t = 0u;
+        for (int bit = 31; bit >= 16; --bit) {
+            const uint32_t cand = t | (1u << bit);
+            int n = __popcll(__ballot(gm[0] >= cand));
+            if (ng > 1) n += __popcll(__ballot(gm[1] >= cand));
+            if (ng > 2) n += __popcll(__ballot(gm[2] >= cand)) + __popcll(__ballot(gm[3] >= cand));
+            if (n >= kk) t = cand;
+        }
+        vk = t;
+    }
+    uint2* out = a.cand + ((size_t)r.slot * a.nchunk + c) * a.capc;
+    int total = 0;
+#pragma unroll
+    for (int e = 0; e < kWe; ++e) {
+        const bool take = ((valid >> e) & 1u) && key[e] >= vk;
+        const unsigned long long bal = __ballot(take);
+        if (take) {
+            const int pos = total + __popcll(bal & ((1ull << lane) - 1ull));
+            if (pos < a.capc) out[pos] = make_uint2(key[e], (uint32_t)welem_id(base, lane, e));
+        }
+        total += __popcll(bal);
+    }
+    if (total > a.capc) return false;                  // the workgroup path rewrites the slots
+    if (lane == 0) a.cand_meta[(size_t)r.slot * a.nchunk + c] = make_uint2((uint32_t)total, vk);
+    return true;
+}
+
 template <bool VEC, bool MAP>
 __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
     __shared__ float4 s_part[3 * kMaxSeqRows][4];
     __shared__ int s_draft[kMaxSeqRows];
     __shared__ uint32_t s_hist[256];
     __shared__ int s_nib[2][4][16];
+    __shared__ int s_ovf[3 * kMaxSeqRows];
+    __shared__ int s_novf;
     __shared__ int s_sh[4];
 
     preload_args(a);
-    const int b = blockIdx.x / a.nchunk, c = blockIdx.x % a.nchunk;
+    // workgroup (b, c, s): chunk c of the rows q = s, s + S, ... of sequence b (S = rsplit)
+    const int s_row = blockIdx.x % a.rsplit, bc = blockIdx.x / a.rsplit;
+    const int b = bc / a.nchunk, c = bc % a.nchunk;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // the counts go out with the sequence's geometry and parameters; the draft ids and the
     // first batch of rows are requested together once those arrive
@@ -1094,16 +1243,25 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
 
     const int nrows = seq_nrows(a, m);
     const int nd = seq_ndraft(a, m);
+    // this workgroup's rows: list index q = s_row + rsplit j, j < nloc
+    const int nloc = s_row < nrows ? (nrows - s_row + a.rsplit - 1) / a.rsplit : 0;
+    if (nloc == 0) return;
+    const bool cand_any = m.topk || m.ntop > 0;
+    const int n_valid = min(kChunk, a.vocab - base);
+    if (tid == 0) s_novf = 0;
     // ---- per-row statistics of this chunk (loads of kRowBatch rows in flight at once).
     // Values: z (penalized target), w (draft) or x (raw); softmax statistics are taken as
     // (max v, sum 2^((v - max) c)) with c = log2(e) / T, greedy target rows as argmax.
     // Each phase runs over the batch's rows so that independent reductions interleave.
-    for (int q0 = 0; q0 < nrows; q0 += kRowBatch) {
+    for (int j0 = 0; j0 < nloc; j0 += kRowBatch) {
         float xv[kRowBatch][kEpt];
 #pragma unroll
         for (int u = 0; u < kRowBatch; ++u)
-            if (q0 + u < nrows) load_row_chunk<VEC, MAP>(a, m, row_ref(a, m, q0 + u), base, xv[u]);
-        if (q0 == 0) {
+            // plain loads: truncated rows are read again by the candidate phase
+            if (j0 + u < nloc)
+                load_row_chunk<VEC, MAP, false>(a, m, row_ref(a, m, s_row + a.rsplit * (j0 + u)),
+                                                base, xv[u]);
+        if (j0 == 0) {
             if (tid < m.k) s_draft[tid] = dreg;
             __syncthreads();
             draft_masks(s_draft, m.k, base, dm);
@@ -1115,8 +1273,9 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
         // phase 1: penalties, per-thread max / argmax
 #pragma unroll
         for (int u = 0; u < kRowBatch; ++u) {
-            const int q = q0 + u;
-            if (q >= nrows) break;
+            const int j = j0 + u;
+            if (j >= nloc) break;
+            const int q = s_row + a.rsplit * j;
             const bool target = q < m.rows;
             if (target && has_pen) {
                 const uint32_t lm = low_bits(q);
@@ -1150,8 +1309,9 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
         // phase 2: wave maxima
 #pragma unroll
         for (int u = 0; u < kRowBatch; ++u) {
-            const int q = q0 + u;
-            if (q >= nrows) break;
+            const int j = j0 + u;
+            if (j >= nloc) break;
+            const int q = s_row + a.rsplit * j;
             if (q < m.rows && !m.sampled) wave_argmax(rmax[u], ridx[u]);
             else rmax[u] = wave_max(rmax[u]);
         }
@@ -1159,8 +1319,9 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
         // enough, and terms below 2^-126 add nothing), wave sums, partials to LDS
 #pragma unroll
         for (int u = 0; u < kRowBatch; ++u) {
-            const int q = q0 + u;
-            if (q >= nrows) break;
+            const int j = j0 + u;
+            if (j >= nloc) break;
+            const int q = s_row + a.rsplit * j;
             float4 res;
             if (q < m.rows && !m.sampled) {
                 res = make_float4(0.f, 0.f, rmax[u], __int_as_float(ridx[u]));
@@ -1175,17 +1336,17 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
                 }
                 res = make_float4(mx, wave_sum(sm), 0.f, 0.f);
             }
-            if (lane == 0) s_part[q][wave] = res;
+            if (lane == 0) s_part[j][wave] = res;
         }
     }
     __syncthreads();
-    for (int q = tid; q < nrows; q += kThreads) {
-        const RowRef r = row_ref(a, m, q);
+    for (int j = tid; j < nloc; j += kThreads) {
+        const RowRef r = row_ref(a, m, s_row + a.rsplit * j);
         const bool greedy_row = r.kind == 0 && !m.sampled;
-        float4 acc = s_part[q][0];
+        float4 acc = s_part[j][0];
         if (greedy_row) {
             for (int w = 1; w < 4; ++w) {
-                const float4 o = s_part[q][w];
+                const float4 o = s_part[j][w];
                 if (better(o.z, __float_as_int(o.w), acc.z, __float_as_int(acc.w))) {
                     acc.z = o.z;
                     acc.w = o.w;
@@ -1194,25 +1355,69 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
         } else {
             const float cs = r.kind == 2 ? kLog2e : kLog2e / m.temp;
             float mx = acc.x;
-            for (int w = 1; w < 4; ++w) mx = fmaxf(mx, s_part[q][w].x);
+            for (int w = 1; w < 4; ++w) mx = fmaxf(mx, s_part[j][w].x);
             float sm = 0.f;
             if (mx != kNegInf)
                 for (int w = 0; w < 4; ++w)
-                    if (s_part[q][w].x != kNegInf)
-                        sm += s_part[q][w].y * exp2f((s_part[q][w].x - mx) * cs);
+                    if (s_part[j][w].x != kNegInf)
+                        sm += s_part[j][w].y * exp2f((s_part[j][w].x - mx) * cs);
             acc.x = mx;
             acc.y = sm;
         }
         a.stats[(size_t)r.slot * a.nchunk + c] = acc;   // read by later kernels
     }
 
-    // ---- candidates for the k-th-largest threshold of truncated / top-n rows
-    if (m.topk || m.ntop > 0) {
-        for (int q = 0; q < nrows; ++q) {
+    // ---- candidates for the k-th-largest threshold of truncated / top-n rows: row number
+    // n of those goes to wave n mod 4; a row whose candidates overflow the slots is listed
+    // and redone by the whole workgroup with the exact kk-th key.
+    if (cand_any) {
+        auto cand_kk = [&](int q) {
+            if (q % a.rsplit != s_row) return 0;
+            const RowRef r = row_ref(a, m, q);
+            const bool trunc = m.topk && r.kind != 2, topn = r.kind == 2 && m.ntop > 0;
+            return trunc ? m.topk_k : topn ? m.ntop : 0;
+        };
+        // the first row of this wave at or after row q (nrows when none)
+        auto next_row = [&](int q, int idx) {
+            for (; q < nrows; ++q)
+                if (cand_kk(q) > 0) {
+                    if ((idx & 3) == wave) break;
+                    ++idx;
+                }
+            return q;
+        };
+        // idx counts the candidate rows before q, so the n-th goes to wave n mod 4
+        auto rows_before = [&](int q) {
+            int n = 0;
+            for (int i = 0; i < q; ++i) n += cand_kk(i) > 0 ? 1 : 0;
+            return n;
+        };
+        int q = next_row(0, 0);
+        float xa[kWe];
+        int ca[kWe];
+        if (q < nrows) wload_row<VEC, MAP>(a, m, row_ref(a, m, q), b, base, lane, xa, ca);
+        while (q < nrows) {
+            const int qn = next_row(q + 1, rows_before(q + 1));
+            float xb[kWe];
+            int cb[kWe];
+            if (qn < nrows) wload_row<VEC, MAP>(a, m, row_ref(a, m, qn), b, base, lane, xb, cb);
+            if (!wave_row_candidates(a, m, row_ref(a, m, q), c, base, s_draft, cand_kk(q), xa,
+                                     ca) &&
+                lane == 0)
+                s_ovf[atomicAdd(&s_novf, 1)] = q;
+#pragma unroll
+            for (int e = 0; e < kWe; ++e) {
+                xa[e] = xb[e];
+                ca[e] = cb[e];
+            }
+            q = qn;
+        }
+        __syncthreads();
+        const int novf = s_novf;
+        for (int o = 0; o < novf; ++o) {
+            const int q = s_ovf[o];
             const RowRef r = row_ref(a, m, q);
             const bool trunc = m.topk && r.kind != 2;
-            const bool topn = r.kind == 2 && m.ntop > 0;
-            if (!trunc && !topn) continue;
             const int kk = trunc ? m.topk_k : m.ntop;
             float x[kEpt];
             load_row_chunk<VEC, MAP>(a, m, r, base, x);
@@ -1224,54 +1429,28 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
                     val = penalize(val, cnt[e] + __popc(dm[e] & low_bits(r.i)), m.pp, m.fp);
                 key[e] = ord_key(val);
             }
-            const int n_valid = min(kChunk, a.vocab - base);
             uint2* out = a.cand + ((size_t)r.slot * a.nchunk + c) * a.capc;
-            // The chunk's candidates are all keys >= vk for a vk <= its kk-th largest key.
-            // First vk is a bound at or below the kk-th largest of the threads' maxima (kk
-            // distinct values, or 0 when fewer threads hold ids), within 2^-7 of it: a cheap
-            // bound that usually leaves a few more than kk keys. If those do not fit in capc
-            // slots, vk becomes the exact kk-th key (radix select) and ties at it are cut at
-            // capc (the count says so).
-            uint32_t vk = 0u;
-            if (n_valid > kk) {
-                uint32_t tmax = 0u;
-#pragma unroll
-                for (int e = 0; e < kEpt; ++e)
-                    if ((valid >> e) & 1u) tmax = max(tmax, key[e]);
-                vk = wg_kth_bound(tmax, kk, s_nib);
-            }
+            // vk is the exact kk-th key (radix select); every key above it and the ties at
+            // it up to capc slots are written (the count says how many there were).
+            const uint32_t vk = wg_select_kth(key, valid, kk, s_hist, s_sh);
             if (tid == 0) s_sh[2] = 0;
             __syncthreads();
 #pragma unroll
             for (int e = 0; e < kEpt; ++e)
-                if (((valid >> e) & 1u) && key[e] >= vk) {
+                if (((valid >> e) & 1u) && key[e] > vk) {
+                    const int pos = atomicAdd(&s_sh[2], 1);
+                    out[pos] = make_uint2(key[e], (uint32_t)elem_id(base, e));
+                }
+            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < kEpt; ++e)
+                if (((valid >> e) & 1u) && key[e] == vk) {
                     const int pos = atomicAdd(&s_sh[2], 1);
                     if (pos < a.capc)
                         out[pos] = make_uint2(key[e], (uint32_t)elem_id(base, e));
                 }
             __syncthreads();
-            int ncand = s_sh[2];
-            if (ncand > a.capc) {
-                vk = wg_select_kth(key, valid, kk, s_hist, s_sh);
-                if (tid == 0) s_sh[2] = 0;
-                __syncthreads();
-#pragma unroll
-                for (int e = 0; e < kEpt; ++e)
-                    if (((valid >> e) & 1u) && key[e] > vk) {
-                        const int pos = atomicAdd(&s_sh[2], 1);
-                        out[pos] = make_uint2(key[e], (uint32_t)elem_id(base, e));
-                    }
-                __syncthreads();
-#pragma unroll
-                for (int e = 0; e < kEpt; ++e)
-                    if (((valid >> e) & 1u) && key[e] == vk) {
-                        const int pos = atomicAdd(&s_sh[2], 1);
-                        if (pos < a.capc)
-                            out[pos] = make_uint2(key[e], (uint32_t)elem_id(base, e));
-                    }
-                __syncthreads();
-                ncand = s_sh[2];
-            }
+            const int ncand = s_sh[2];
             if (tid == 0)
                 a.cand_meta[(size_t)r.slot * a.nchunk + c] = make_uint2((uint32_t)ncand, vk);
             __syncthreads();
@@ -1660,9 +1839,14 @@ hipError_t launch_sample(const SampArgs& args, hipStream_t stream) {
     // whole stage is the fused kernel (sample_fused.hip).
     if (fused_fits(a)) return launch_fused(a, stream);
     const dim3 grid((unsigned)a.batch * a.nchunk), block(kThreads);
+    // the sweep splits each sequence's rows over up to 4 workgroups per chunk when the
+    // sequences alone give fewer than 512 workgroups
+    a.rsplit = 1;
+    while (a.rsplit < 4 && (long)a.batch * a.nchunk * a.rsplit < 512) a.rsplit *= 2;
+    const dim3 sweep_grid((unsigned)a.batch * a.nchunk * a.rsplit);
     const bool vec = (a.vocab % 4) == 0;
     const bool map = a.t2d != nullptr;
-#define VSA_SWEEP(V, M) hipLaunchKernelGGL((sweep_kernel<V, M>), grid, block, 0, stream, a)
+#define VSA_SWEEP(V, M) hipLaunchKernelGGL((sweep_kernel<V, M>), sweep_grid, block, 0, stream, a)
     if (map) {
         if (vec) VSA_SWEEP(true, true); else VSA_SWEEP(false, true);
     } else {

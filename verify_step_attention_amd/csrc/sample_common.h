@@ -247,7 +247,9 @@ __device__ __forceinline__ int4 load_nt4(const int32_t* p) {
     return make_int4(v[0], v[1], v[2], v[3]);
 }
 
-template <bool VEC>
+// NT: streaming loads (the nontemporal policy) for rows read once; plain loads for rows
+// read again shortly (they stay in L2).
+template <bool VEC, bool NT = true>
 __device__ __forceinline__ void load_chunk(const float* row, int base, int vocab,
                                            float (&x)[kEpt]) {
     const int tid = threadIdx.x;
@@ -256,7 +258,7 @@ __device__ __forceinline__ void load_chunk(const float* row, int base, int vocab
         for (int q = 0; q < kQuads; ++q) {
             const int j = base + 1024 * q + 4 * tid;
             float4 v = make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
-            if (j < vocab) v = load_nt4(row + j);
+            if (j < vocab) v = NT ? load_nt4(row + j) : *reinterpret_cast<const float4*>(row + j);
             x[4 * q] = v.x;
             x[4 * q + 1] = v.y;
             x[4 * q + 2] = v.z;
@@ -285,11 +287,11 @@ __device__ __forceinline__ float mapped_logit(const SampArgs& a, const float* ro
 }
 // MAP: the call has a reduced draft vocabulary (kernels are compiled both ways, so the
 // full-vocabulary path carries none of this).
-template <bool VEC, bool MAP>
+template <bool VEC, bool MAP, bool NT = true>
 __device__ __forceinline__ void load_draft_chunk(const SampArgs& a, int drow, int base,
                                                  float (&x)[kEpt]) {
     if constexpr (!MAP) {
-        load_chunk<VEC>(a.dl + (size_t)drow * a.vocab, base, a.vocab, x);
+        load_chunk<VEC, NT>(a.dl + (size_t)drow * a.vocab, base, a.vocab, x);
         return;
     }
     const float* row = a.dl + (size_t)drow * a.dvocab;
@@ -329,17 +331,17 @@ __device__ __forceinline__ float draft_logit(const SampArgs& a, int drow, int id
     return v;
 }
 // Row q of a sequence's row list (target, draft or raw) at the chunk's ids.
-template <bool VEC, bool MAP>
+template <bool VEC, bool MAP, bool NT = true>
 __device__ __forceinline__ void load_row_chunk(const SampArgs& a, const SeqMode& m,
                                                const RowRef& r, int base, float (&x)[kEpt]) {
     if constexpr (!MAP) {
         // one load path for every row kind: only the row's address differs
         const float* row = r.kind == 1 ? a.dl + (size_t)(m.d0 + r.i - 1) * a.vocab
                                        : a.tl + (size_t)(m.r0 + r.i) * a.vocab;
-        load_chunk<VEC>(row, base, a.vocab, x);
+        load_chunk<VEC, NT>(row, base, a.vocab, x);
     } else {
-        if (r.kind == 1) load_draft_chunk<VEC, MAP>(a, m.d0 + r.i - 1, base, x);
-        else load_chunk<VEC>(a.tl + (size_t)(m.r0 + r.i) * a.vocab, base, a.vocab, x);
+        if (r.kind == 1) load_draft_chunk<VEC, MAP, NT>(a, m.d0 + r.i - 1, base, x);
+        else load_chunk<VEC, NT>(a.tl + (size_t)(m.r0 + r.i) * a.vocab, base, a.vocab, x);
     }
 }
 

@@ -335,6 +335,7 @@ struct SampArgs {
     uint32_t wait_ticks;           // fused kernel: how long (100 MHz ticks) a workgroup waits
                                    // for its sequence's statistics before it hands its chunk
                                    // of the draw to the last arriver
+    int rsplit;                    // sweep: workgroups sharing a (sequence, chunk)'s rows
 };
 // The fused kernel keeps each sequence's counters and race words on lines 4b .. 4b + 3 and
 // its claim words on the lines after the first 4B.
