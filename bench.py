@@ -99,16 +99,31 @@ def counters_traffic():
         return None
 
 
-def cpu_baseline(w, kq=None, budget_s=12.0):
-    """The oracle as it stands, timed on the host on whole verify steps of the same workload
-    until about budget_s seconds have passed (at least one step). kq: the quantized cache,
-    when the step reads one."""
-    from oracle import attention as oatt, sampling as osamp
+def host_cpu():
+    """(logical CPUs this process may run on, os.cpu_count(), CPU model string)."""
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = 1
+        avail = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        avail = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return avail, os.cpu_count() or 1, model
+
+
+def cpu_baseline(w, name, kq=None, budget_s=8.0):
+    """The oracle as it stands, timed on the host on whole verify steps of the same workload
+    until about budget_s seconds have passed (at least one step), twice: with numpy's BLAS
+    limited to one thread, and with it at its default (every core it sees). kq: the
+    quantized cache, when the step reads one."""
+    from oracle import attention as oatt, sampling as osamp
+    from threadpoolctl import threadpool_info, threadpool_limits
     q = w.q_f32()
     if kq is None:
         k, v = w.kv_f32()
@@ -122,21 +137,33 @@ def cpu_baseline(w, kq=None, budget_s=12.0):
                                       w.cu_rows, w.ctx_lens, w.num_q_heads, w.num_kv_heads)
     prm = [osamp.RowParams(p.temperature, p.top_k, p.top_p, p.presence_penalty,
                            p.frequency_penalty, p.logprobs, p.top_logprobs) for p in w.params]
-    steps, t0 = 0, time.perf_counter()
-    while True:
-        attend()
-        osamp.verify_sample_accept(w.target_logits, w.draft_logits, w.draft_tokens, w.cu_rows,
-                                   w.token_counts, prm, w.positions, w.seed)
-        steps += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": round(steps * w.total_rows / dt, 3), "unit": "rows/s", "cores": cores,
+
+    def timed():
+        steps, t0 = 0, time.perf_counter()
+        while True:
+            attend()
+            osamp.verify_sample_accept(w.target_logits, w.draft_logits, w.draft_tokens,
+                                       w.cu_rows, w.token_counts, prm, w.positions, w.seed)
+            steps += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        return steps, time.perf_counter() - t0
+
+    with threadpool_limits(limits=1):
+        s1, t1 = timed()
+    sn, tn = timed()
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    avail, total, model = host_cpu()
+    return {"value": round(sn * w.total_rows / tn, 3), "unit": "rows/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{steps} whole verify step(s) of {WORKLOAD} (attention of all 20 rows"
+            "single_thread_value": round(s1 * w.total_rows / t1, 3),
+            "nproc": avail, "cpu_count": total, "cpu_model": model,
+            "sample": f"whole verify steps of {name} (attention of all {w.total_rows} rows"
                       f"{'' if kq is None else f' over the {kq.bits}-bit cache'} + "
-                      f"sample/accept of all 4 sequences), {dt:.1f} s on the host, numpy "
-                      f"BLAS threads = {cores}"}
+                      f"sample/accept of all {w.batch} sequences): {sn} step(s) in "
+                      f"{tn:.1f} s with numpy's BLAS at {threads} threads (value), {s1} "
+                      f"step(s) in {t1:.1f} s at 1 thread (single_thread_value); the oracle "
+                      f"is numpy, so only its BLAS calls use more than one core"}
 
 
 def sampling_main(args):
@@ -503,6 +530,10 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=7)
+    ap.add_argument("--workload", default=WORKLOAD,
+                    help="the workload of the timed steps (default: the metric's, "
+                         f"{WORKLOAD}); the others are the configurations of the parity "
+                         "tests, measured one by one for the per-configuration table")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--static-splits", action="store_true",
                     help="attention with fixed key ranges per split (bitwise reproducible) "
@@ -552,8 +583,9 @@ def main():
     global ATTN_FLAGS
     ATTN_FLAGS = 0 if args.static_splits else vsa.ATTN_DYNAMIC_SPLITS
 
-    print(f"[bench] building inputs for {WORKLOAD}", file=sys.stderr, flush=True)
-    w = wl.make_workload(WORKLOAD)
+    name = args.workload
+    print(f"[bench] building inputs for {name}", file=sys.stderr, flush=True)
+    w = wl.make_workload(name)
     nbytes = algorithmic_bytes(w, args.kv_bits, args.draft_vocab)
     step_bytes = nbytes["attention"] + nbytes["sample"]
     dev0 = wl.device_tensors(w)
@@ -732,10 +764,13 @@ def main():
 
     attn_us = float(np.mean(attn_ms)) * 1e3
     achieved = nbytes["attention"] / (attn_us * 1e-6) / 1e9
-    traffic = counters_traffic() if kq is None else None
+    traffic = counters_traffic() if kq is None and name == WORKLOAD else None
     rows_per_s = w.total_rows / (ms_step * 1e-3)
+    rows = np.diff(w.cu_rows)
     line = {
-        "metric": "verified draft-block rows/sec + achieved HBM GB/s, B=4 K=4 ctx 8192",
+        "metric": ("verified draft-block rows/sec + achieved HBM GB/s, B=4 K=4 ctx 8192"
+                   if name == WORKLOAD else
+                   f"verified draft-block rows/sec + achieved HBM GB/s, {name}"),
         "value": round(rows_per_s, 1),
         "unit": "rows/s",
         "n_gpus": 1,
@@ -745,12 +780,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if kq is None else f"bf16 q, u{kq.bits} kv codes",
+        "dtype": ("bf16" if w.dtype == wl.BF16 else "f32") if kq is None else
+                 f"bf16 q, u{kq.bits} kv codes",
         "data": "synthetic",
         "achieved_hbm_GBps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "launch": "eager" if not graphs else "hip_graph_replay",
         "config": {
-            "workload": WORKLOAD, "batch": w.batch, "drafts_per_seq": 4, "ctx": 8192,
+            "workload": name, "batch": w.batch,
+            "drafts_per_seq": sorted({int(r) - 1 for r in rows}),
+            "ctx": [int(w.ctx_lens.min()), int(w.ctx_lens.max())],
             "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
             "vocab": w.vocab, "rows_per_step": w.total_rows, "input_sets": len(sets),
             "algorithmic_bytes_per_step": step_bytes,
@@ -767,7 +805,8 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": ("verify_attention call (attn_bf16_kernel<128,1,false>)"
+            "kernel": (f"verify_attention call (attn_{'bf16' if w.dtype == wl.BF16 else 'f32'}"
+                       f"_kernel, D={w.head_dim})"
                        if kq is None else
                        f"verify_attention_kvq call (attn_kvq_kernel<128,1,{kq.bits}>)"),
             "achieved": round(achieved, 1),
@@ -787,7 +826,7 @@ def main():
             wc.draft_logits = widen_draft_logits(dev0["draft_logits"].cpu().numpy(),
                                                  d2t.cpu().numpy(), w.vocab)
             wc.draft_tokens = dev0["draft_tokens"].cpu().numpy()
-        line["cpu_baseline"] = cpu_baseline(wc, kq)
+        line["cpu_baseline"] = cpu_baseline(wc, name, kq)
     print(json.dumps(line), flush=True)
 
 

@@ -129,6 +129,7 @@ vsa_status attention_call(const void* q, const void* k_cache, const void* v_cach
     a.dyn = (flags & VSA_ATTN_DYNAMIC_SPLITS) != 0 && plan.nsplit >= 2 && dtype == VSA_BF16;
     a.units = plan.units;
     a.mcap = plan.mcap;
+    a.merge_kernel = plan.merge_kernel;
     const float sc = scale == 0.f ? 1.f / sqrtf((float)D) : scale;
     a.scale_log2 = sc * 1.4426950408889634f;
     a.window = window;
@@ -263,6 +264,7 @@ vsa_status verify_attention_kvq(const void* q, const uint8_t* k_codes, const voi
     a.dyn = (flags & VSA_ATTN_DYNAMIC_SPLITS) != 0 && plan.nsplit >= 2;
     a.units = plan.units;
     a.mcap = plan.mcap;
+    a.merge_kernel = plan.merge_kernel;
     const float sc = scale == 0.f ? 1.f / sqrtf((float)D) : scale;
     a.scale_log2 = sc * 1.4426950408889634f;
     if (plan.n_ctr_x &&

@@ -273,11 +273,18 @@ __device__ void attn_epilogue(const AttnArgs& a, LdsQuad ob, float* st, int unit
             const int row = s.r0 + n / a.group, head = g * a.group + n % a.group;
             *reinterpret_cast<float4*>(a.out + ((size_t)row * a.hq + head) * D + d) =
                 make_float4(o.x * il, o.y * il, o.z * il, o.w * il);
+        } else if (a.merge_kernel) {
+            *reinterpret_cast<float4*>(a.part_o + (pslot * a.mcap + n) * D + d) = o;
         } else {
             handoff_store4(reinterpret_cast<float4*>(a.part_o + (pslot * a.mcap + n) * D + d), o);
         }
     }
     if (a.nsplit == 1) return;
+    if (a.merge_kernel) {
+        for (int n = tid; n < M; n += kThreads)
+            a.part_ml[pslot * a.mcap + n] = make_float2(wm[n], wl[n]);
+        return;
+    }
     for (int n = tid; n < M; n += kThreads)
         handoff_store(a.part_ml + pslot * a.mcap + n, make_float2(wm[n], wl[n]));
     attn_finish_unit<D>(a, unit, g, s, true);
@@ -295,7 +302,7 @@ __device__ void attn_empty_split(const AttnArgs& a, int unit, int split, int g,
                        make_float4(0.f, 0.f, 0.f, 0.f));
     for (int n = threadIdx.x; n < M; n += kThreads)
         handoff_store(a.part_ml + pslot * a.mcap + n, make_float2(kNegInf, 0.f));
-    attn_finish_unit<D>(a, unit, g, s, true);
+    if (!a.merge_kernel) attn_finish_unit<D>(a, unit, g, s, true);
 }
 
 // -------------------------------------------------------------------------- bf16 / MFMA
@@ -439,7 +446,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const AttnArgs a) {
     const SeqGeom s = seq_geometry(a, geo, tid == 0 && split == 0 && g == 0);
     if (!s.ok) {
         __builtin_amdgcn_s_waitcnt(0);                 // no DMA outlives the workgroup
-        if (a.nsplit > 1) attn_finish_unit<D>(a, unit, g, s, false);
+        if (a.nsplit > 1 && !a.merge_kernel) attn_finish_unit<D>(a, unit, g, s, false);
         return;
     }
     const int L = s.ctx + s.rows;                      // keys of this sequence
@@ -876,7 +883,7 @@ __global__ __launch_bounds__(256, 1) void attn_kvq_kernel(const AttnArgs a) {
     const SeqGeom s = seq_geometry(a, b, tid == 0 && split == 0 && g == 0);
     if (!s.ok) {
         __builtin_amdgcn_s_waitcnt(0);
-        if (a.nsplit > 1) attn_finish_unit<D>(a, unit, g, s, false);
+        if (a.nsplit > 1 && !a.merge_kernel) attn_finish_unit<D>(a, unit, g, s, false);
         return;
     }
     const int L = s.ctx + s.rows;
@@ -1264,7 +1271,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const AttnArgs a) {
     const int tid = threadIdx.x;
     const SeqGeom s = seq_geometry(a, b, tid == 0 && split == 0 && g == 0);
     if (!s.ok) {
-        if (a.nsplit > 1) attn_finish_unit<D>(a, unit, g, s, false);
+        if (a.nsplit > 1 && !a.merge_kernel) attn_finish_unit<D>(a, unit, g, s, false);
         return;
     }
     const int M = s.rows * a.group;
@@ -1352,6 +1359,74 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const AttnArgs a) {
 }
 
 
+// -------------------------------------------------------------------------- split merge
+// For units whose partials are too many for one workgroup to merge quickly (many splits of
+// many columns, see plan_attention), this kernel runs after the attention kernel (stream
+// order makes every partial visible):
+//   out = sum_s w_s O_s,   w_s = 2^(m_s - m) / sum_s' 2^(m_s' - m) l_s',   m = max_s m_s
+// over the key splits s of one (sequence, KV head) unit. Thread e of the unit's slice owns
+// column n = e / (D/4) and 4 consecutive d; the geometry, (max, sum) and O loads of up to
+// kMergeGroup splits are issued together, so one memory round trip covers <= 8 splits.
+// Columns past the sequence's M read workspace slots nobody wrote this call; their
+// results are computed and dropped.
+template <int D>
+__global__ __launch_bounds__(256) void attn_merge_kernel(const AttnArgs a) {
+    constexpr int D4 = D / 4;
+    constexpr int SG = kMergeGroup;
+    const int chunks = (a.mcap * D4 + kThreads - 1) / kThreads;
+    const int unit = blockIdx.x / chunks;
+    const int e = (blockIdx.x % chunks) * kThreads + threadIdx.x;
+    if (unit >= a.units) return;
+    // the attention kernel has finished: its tile counter returns to zero for the next call
+    if (a.dyn && e == 0) __hip_atomic_store(counter_at(a.tile_ctr, a.tile_ctr_x, unit), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (e >= a.mcap * D4) return;
+    const int b = unit / a.hkv, g = unit % a.hkv;
+    const int n = e / D4, d4 = e % D4;
+    const int ns = a.nsplit;
+    const size_t base = (size_t)unit * ns;
+    const float2* pml = a.part_ml + base * a.mcap + n;
+    const float4* po = reinterpret_cast<const float4*>(a.part_o) + (base * a.mcap + n) * D4 + d4;
+    const size_t sstride = (size_t)a.mcap * D4;              // float4s between splits
+
+    float m_run = kNegInf, l_run = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    SeqGeom s{};
+    for (int s0 = 0; s0 < ns; s0 += SG) {
+        float2 ml[SG];
+        float4 v[SG];
+#pragma unroll
+        for (int u = 0; u < SG; ++u) {
+            const int sp = s0 + u < ns ? s0 + u : ns - 1;    // in bounds; dropped below
+            ml[u] = pml[(size_t)sp * a.mcap];
+            v[u] = po[sp * sstride];
+        }
+        if (s0 == 0) s = seq_geometry(a, b, false);
+        float m = m_run;
+#pragma unroll
+        for (int u = 0; u < SG; ++u)
+            if (s0 + u < ns) m = fmaxf(m, ml[u].x);
+        if (m == kNegInf) continue;
+        const float c = exp2f(m_run - m);                    // m_run = -inf gives 0
+        l_run *= c;
+        acc = make_float4(acc.x * c, acc.y * c, acc.z * c, acc.w * c);
+#pragma unroll
+        for (int u = 0; u < SG; ++u) {
+            const float f = (s0 + u < ns && ml[u].x != kNegInf) ? exp2f(ml[u].x - m) : 0.f;
+            l_run += f * ml[u].y;
+            acc.x += f * v[u].x;
+            acc.y += f * v[u].y;
+            acc.z += f * v[u].z;
+            acc.w += f * v[u].w;
+        }
+        m_run = m;
+    }
+    if (!s.ok || n >= s.rows * a.group) return;
+    const float il = 1.f / l_run;
+    const int row = s.r0 + n / a.group, head = g * a.group + n % a.group;
+    *reinterpret_cast<float4*>(a.out + ((size_t)row * a.hq + head) * D + 4 * d4) =
+        make_float4(acc.x * il, acc.y * il, acc.z * il, acc.w * il);
+}
+
 }  // namespace
 
 AttnPlan plan_attention(int B, int Hq, int Hkv, int D, int max_rows, int max_kv_len) {
@@ -1369,6 +1444,11 @@ AttnPlan plan_attention(int B, int Hq, int Hkv, int D, int max_rows, int max_kv_
     if (nsplit > kMaxSplits) nsplit = kMaxSplits;
     if (nsplit < 1) nsplit = 1;
     p.nsplit = nsplit;
+    // The last split of a unit to finish merges the unit's partials itself while they are
+    // few (it reads nsplit * mcap * D floats, from the device-coherent level: up to 128 KB
+    // takes one workgroup about a microsecond); beyond that a separate kernel merges, spread
+    // over the units' columns.
+    p.merge_kernel = nsplit > 1 && (size_t)nsplit * p.mcap * D * 4 > ((size_t)128 << 10);
     size_t off = kWsHeader;                                      // error word, counters
     p.n_ctr_x = extra_counters(2L * p.units);       // tile claims, then arrivals
     p.off_ctr_x = off;
@@ -1419,6 +1499,11 @@ hipError_t launch_attention(const AttnArgs& a, const AttnPlan& p, vsa_dtype dtyp
     } else {
         if (a.d == 128) hipLaunchKernelGGL((attn_f32_kernel<128>), grid, block, 0, stream, a);
         else hipLaunchKernelGGL((attn_f32_kernel<64>), grid, block, 0, stream, a);
+    }
+    if (p.merge_kernel) {
+        const dim3 mgrid(p.units * ((p.mcap * (a.d / 4) + kThreads - 1) / kThreads));
+        if (a.d == 128) hipLaunchKernelGGL((attn_merge_kernel<128>), mgrid, block, 0, stream, a);
+        else hipLaunchKernelGGL((attn_merge_kernel<64>), mgrid, block, 0, stream, a);
     }
     return hipGetLastError();
 }

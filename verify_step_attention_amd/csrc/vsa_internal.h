@@ -226,6 +226,7 @@ struct AttnArgs {
     float scale_log2;       // softmax scale * log2(e)
     int window;             // > 0: context keys seen per row are limited (see mask)
     int mask;               // kMaskBidirectional | kMaskSliding
+    int merge_kernel;       // the splits are merged by attn_merge_kernel, not in the kernel
 };
 constexpr int kMaskBidirectional = 1;   // block rows see every block row
 constexpr int kMaskSliding = 2;         // the window ends at each row's own position
@@ -237,6 +238,7 @@ struct AttnPlan {
     int nsplit;      // key splits per (sequence, KV head)
     int units;       // B * Hkv
     int tile;        // keys per workgroup tile
+    int merge_kernel;  // 1: a separate kernel merges the splits (see plan_attention)
     size_t off_ctr_x, n_ctr_x, off_ml, off_o, bytes;
 };
 
