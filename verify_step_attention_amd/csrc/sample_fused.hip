@@ -17,15 +17,16 @@
 //            sequence's arrival counter A.
 //   greedy   the last arriver merges the chunks, accepts the longest matching prefix and
 //            writes every output.
-//   sampled  every workgroup waits until A counts the whole sequence, merges the same
-//            statistics in the same order and takes the same acceptance decision (no
-//            round trip publishes it). The draw over the vocabulary (residual of the first
-//            rejected row, or the bonus row) is an exponential race; each workgroup races
-//            its own chunk from the values still in its registers and folds the winner
-//            into the sequence's 64-bit word with an atomic max (key bits over the
-//            complemented id: larger key, then lower id, wins). The workgroup that counts
-//            the last chunk into R writes the token and returns the sequence's words and
-//            counters to zero.
+//   sampled  the last arriver merges the chunks, takes the acceptance decisions, writes
+//            the accepted length and drafts, and publishes the decision (a record of the
+//            draw's rows and their merged statistics, written through, then a go flag);
+//            every other workgroup waits for the flag and reads the record. The draw over
+//            the vocabulary (residual of the first rejected row, or the bonus row) is an
+//            exponential race; each workgroup races its own chunk from the values still in
+//            its registers and folds the winner into the sequence's 64-bit word with an
+//            atomic max (key bits over the complemented id: larger key, then lower id,
+//            wins). The workgroup that counts the last chunk into the done counter D writes
+//            the token and returns the sequence's words and counters to zero.
 // Waiting can time out (a budget per workgroup; other work may hold CUs). A chunk is then
 // never lost: its owner marks it abandoned and counts in; every workgroup counts into the
 // sequence's done counter D exactly once (after racing its chunk, or abandoning it), and the
