@@ -77,9 +77,12 @@ __device__ __forceinline__ float race_e2(uint32_t hi, uint32_t lo) {
     const uint32_t h = low ? hi : ~hi, l = low ? lo : ~lo;
     const float v = ((float)h + ((float)l + 0.5f) * k2m32) * k2m32;   // U, or c = 1 - U
     const float w = low ? v : 1.0f - v;
-    const float lg = -__builtin_amdgcn_logf(w);
-    const float corr = v * __builtin_amdgcn_rcpf(1.0f - w);
-    return low ? lg : (w == 1.0f ? v * kLog2e : lg * corr);
+    float lg = -__builtin_amdgcn_logf(w);
+    float hi_c = lg * (v * __builtin_amdgcn_rcpf(1.0f - w));
+    float one_c = v * kLog2e;
+    // every candidate on every lane, so the selects below stay selects (no divergent branch)
+    asm volatile("" : "+v"(lg), "+v"(hi_c), "+v"(one_c));
+    return low ? lg : (w == 1.0f ? one_c : hi_c);
 }
 
 // Race words of ids 4 i .. 4 i + 3 (blocks 2 i and 2 i + 1): (hi, lo) of id 4 i + r.
@@ -96,6 +99,15 @@ __device__ __forceinline__ RaceWords race_words4(uint64_t seed, int j0, int pos,
     RaceWords w;
     w.a = philox_block(seed, (uint32_t)j0 >> 1, (uint32_t)pos, (uint32_t)b, 1u);
     w.b = philox_block(seed, ((uint32_t)j0 >> 1) + 1u, (uint32_t)pos, (uint32_t)b, 1u);
+    return w;
+}
+// The same words with the key halves (k0, k1) = (low, high word of the seed) passed in, e.g.
+// held in vector registers so that the round keys need no scalar registers.
+__device__ __forceinline__ RaceWords race_words4_k(uint32_t k0, uint32_t k1, int j0, int pos,
+                                                   int b) {
+    RaceWords w;
+    w.a = philox4x32_10(make_uint4((uint32_t)j0 >> 1, (uint32_t)pos, (uint32_t)b, 1u), k0, k1);
+    w.b = philox4x32_10(make_uint4(((uint32_t)j0 >> 1) + 1u, (uint32_t)pos, (uint32_t)b, 1u), k0, k1);
     return w;
 }
 

@@ -106,14 +106,35 @@ __device__ __forceinline__ unsigned long long coh_load_u64(unsigned long long* p
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// wave-wide max of a packed race winner (every lane gets it)
-__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const unsigned long long o = __shfl_xor(v, off);
-        v = o > v ? o : v;
-    }
-    return v;
+// Wave-wide max of two packed race winners at once (both chains interleave), on the DPP
+// steps of the float reductions with each 64-bit value moved as two halves; the results
+// are wave-uniform.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ void max_step_u64(uint32_t& hi, uint32_t& lo) {
+    const uint32_t oh = (uint32_t)dpp_i<CTRL, ROWS>((int)hi, (int)hi);
+    const uint32_t ol = (uint32_t)dpp_i<CTRL, ROWS>((int)lo, (int)lo);
+    const bool take = (oh > hi) | ((oh == hi) & (ol > lo));
+    hi = take ? oh : hi;
+    lo = take ? ol : lo;
+}
+__device__ __forceinline__ void wave_max2_u64(unsigned long long& x, unsigned long long& y) {
+    uint32_t xh = (uint32_t)(x >> 32), xl = (uint32_t)x, yh = (uint32_t)(y >> 32), yl = (uint32_t)y;
+    max_step_u64<kDppSwap1>(xh, xl);
+    max_step_u64<kDppSwap1>(yh, yl);
+    max_step_u64<kDppSwap2>(xh, xl);
+    max_step_u64<kDppSwap2>(yh, yl);
+    max_step_u64<kDppHalfMirror>(xh, xl);
+    max_step_u64<kDppHalfMirror>(yh, yl);
+    max_step_u64<kDppMirror>(xh, xl);
+    max_step_u64<kDppMirror>(yh, yl);
+    max_step_u64<kDppBcast15, 0xA>(xh, xl);
+    max_step_u64<kDppBcast15, 0xA>(yh, yl);
+    max_step_u64<kDppBcast31, 0xC>(xh, xl);
+    max_step_u64<kDppBcast31, 0xC>(yh, yl);
+    x = ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)xh, 63) << 32) |
+        (uint32_t)__builtin_amdgcn_readlane((int)xl, 63);
+    y = ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)yh, 63) << 32) |
+        (uint32_t)__builtin_amdgcn_readlane((int)yl, 63);
 }
 
 // Race of one chunk: keys w_j / (-log2 U_j) (the keys w_j / E_j times ln 2, the same
@@ -134,37 +155,57 @@ __device__ __forceinline__ void race_chunk_regs(const SampArgs& a, const DrawSpe
                                                 unsigned long long* best_r,
                                                 unsigned long long* best_p) {
     const int tid = threadIdx.x;
+    // the weights p and w; the draw kind is uniform, so its tests sit outside the id loops
+    float pw[kEpt], rw[kEpt];
+#pragma unroll
+    for (int e = 0; e < kEpt; ++e) pw[e] = __builtin_amdgcn_exp2f((zp[e] - ds.m_p) * ds.cs) * ds.inv_zp;
+    if (ds.kind == 1 && ds.onehot_d >= 0) {
+#pragma unroll
+        for (int e = 0; e < kEpt; ++e)
+            rw[e] = fmaxf(0.f, pw[e] - (elem_id(base, e) == ds.onehot_d ? 1.f : 0.f));
+    } else if (ds.kind == 1) {
+#pragma unroll
+        for (int e = 0; e < kEpt; ++e)
+            rw[e] = fmaxf(0.f, pw[e] - __builtin_amdgcn_exp2f((xq[e] - ds.m_q) * ds.cs) * ds.inv_zq);
+    } else {
+#pragma unroll
+        for (int e = 0; e < kEpt; ++e) rw[e] = pw[e];
+    }
+    // the variates of the thread's ids; the key words sit in vector registers (the kernel's
+    // scalar registers are taken, and scalar round keys would be spilled and reloaded)
+    uint32_t k0 = (uint32_t)a.seed, k1 = (uint32_t)(a.seed >> 32);
+    asm volatile("" : "+v"(k0), "+v"(k1));
+    float inv_e[kEpt];
+#pragma unroll
+    for (int qd = 0; qd < kQuads; ++qd) {
+        const RaceWords w = race_words4_k(k0, k1, base + 1024 * qd + 4 * tid, ds.pos, b);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            inv_e[4 * qd + r] = __builtin_amdgcn_rcpf(race_e2(w.hi(r), w.lo(r)));
+    }
     float kr_best = 0.f, kp_best = 0.f;
     int jr = 0, jp = 0;
 #pragma unroll
-    for (int qd = 0; qd < kQuads; ++qd) {
-        const int j0 = base + 1024 * qd + 4 * tid;
-        const RaceWords w = race_words4(a.seed, j0, ds.pos, b);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int e = 4 * qd + r;
-            const int j = j0 + r;
-            const float p = __builtin_amdgcn_exp2f((zp[e] - ds.m_p) * ds.cs) * ds.inv_zp;
-            float wr = p;
-            if (ds.kind == 1) {
-                float q;
-                if (ds.onehot_d >= 0) q = j == ds.onehot_d ? 1.f : 0.f;
-                else q = __builtin_amdgcn_exp2f((xq[e] - ds.m_q) * ds.cs) * ds.inv_zq;
-                wr = fmaxf(0.f, p - q);
-            }
-            const float inv_e = __builtin_amdgcn_rcpf(race_e2(w.hi(r), w.lo(r)));
-            const float kr = wr * inv_e, kp = p * inv_e;
-            // a thread visits its ids in increasing order, so a strict > keeps the lower id
-            // of a tie; ids past the vocabulary hold -inf logits: weight 0, never a winner
-            const bool ur = kr > kr_best, up = kp > kp_best;
-            kr_best = ur ? kr : kr_best;
-            jr = ur ? j : jr;
-            kp_best = up ? kp : kp_best;
-            jp = up ? j : jp;
-        }
+    for (int e = 0; e < kEpt; ++e) {
+        const int j = elem_id(base, e);
+        const float kr = rw[e] * inv_e[e], kp = pw[e] * inv_e[e];
+        // a thread visits its ids in increasing order, so a strict > keeps the lower id of a
+        // tie; ids past the vocabulary hold -inf logits: weight 0, never a winner
+        const bool ur = kr > kr_best, up = kp > kp_best;
+        kr_best = ur ? kr : kr_best;
+        jr = ur ? j : jr;
+        kp_best = up ? kp : kp_best;
+        jp = up ? j : jp;
     }
-    *best_r = wave_max_u64(kr_best > 0.f ? pack_key(kr_best, jr) : 0ull);
-    *best_p = wave_max_u64(kp_best > 0.f ? pack_key(kp_best, jp) : 0ull);
+    unsigned long long r = kr_best > 0.f ? pack_key(kr_best, jr) : 0ull;
+    unsigned long long p = kp_best > 0.f ? pack_key(kp_best, jp) : 0ull;
+    wave_max2_u64(r, p);
+    *best_r = r;
+    *best_p = p;
+}
+
+__device__ __forceinline__ float uniform_f(float x) {
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
 }
 
 // Folds the workgroup's race winners into the sequence's words (thread 0; the atomics are
@@ -220,42 +261,94 @@ __device__ __forceinline__ void load_race_chunk(const SampArgs& a, const SeqMode
 }
 
 // Phase 1 of the fused kernel for the data rows q0 .. q0 + kRowBatch - 1 (target rows
-// 0 .. R - 1, then draft rows 1 .. K), whose chunk values are in xv. Each row is straight-line
-// code: penalties (target rows), the statistics, the wave reduction, a partial per wave in
-// LDS. A target row also yields its raw statistics (logprobs) from the values before its
-// penalties, so raw rows are never loaded. Then the waves' partials are combined and each
-// row's chunk entry is stored write-through.
-__device__ __forceinline__ void row_stats(FusedShared& sh, float (&x)[kEpt], int slot_u,
-                                          bool greedy, float cs, int base) {
+// 0 .. R - 1, then draft rows 1 .. K), whose chunk values are in xv: penalties (target rows),
+// the statistics, the wave reduction, a partial per wave in LDS. A target row also yields its
+// raw statistics (logprobs) from the values before its penalties, so raw rows are never
+// loaded. Then the waves' partials are combined and each row's chunk entry is stored
+// write-through. The statistics run G rows at a time in one straight-line block, so the
+// rows' reduction chains (each a few dozen dependent steps) overlap; every row's own
+// arithmetic is the same whatever the grouping.
+
+// (max, sum 2^((x - max) c)) of rows u0 .. u0 + G - 1 into LDS slots slot0 + u
+template <int G>
+__device__ __forceinline__ void group_maxsum(FusedShared& sh, const float (&xv)[kRowBatch][kEpt],
+                                             int u0, int slot0, float cs) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    float4 res;
-    if (greedy) {
+    float mx[G], sm[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        mx[g] = xv[u0 + g][0];
+#pragma unroll
+        for (int e = 1; e < kEpt; ++e) mx[g] = fmaxf(mx[g], xv[u0 + g][e]);
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) mx[g] = wave_max(mx[g]);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        // a row with no ordered value (max -inf) sums to 0; the select keeps this block
+        // free of branches
+        const float mcs = mx[g] * cs;
+        float t = 0.f;
+#pragma unroll
+        for (int e = 0; e < kEpt; ++e) t += __builtin_amdgcn_exp2f(__builtin_fmaf(xv[u0 + g][e], cs, -mcs));
+        sm[g] = mx[g] != kNegInf ? t : 0.f;
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) sm[g] = wave_sum(sm[g]);
+    if (lane == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) sh.part[slot0 + u0 + g][wave] = make_float4(mx[g], sm[g], 0.f, 0.f);
+    }
+}
+
+// (max, id of the max) of rows u0 .. u0 + G - 1 into LDS slots u; ties go to the lower id
+template <int G>
+__device__ __forceinline__ void group_argmax(FusedShared& sh, const float (&xv)[kRowBatch][kEpt],
+                                             int u0, int base) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    float bv[G];
+    int bi[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
         // a thread visits its ids in increasing order, so a strict > keeps the lowest id of a
         // tie; ids past the vocabulary hold -inf and never replace the start
-        float bv = kNegInf;
-        int bi = kBigIdx;
+        bv[g] = kNegInf;
+        bi[g] = kBigIdx;
 #pragma unroll
         for (int e = 0; e < kEpt; ++e) {
-            const bool up = x[e] > bv;
-            bv = up ? x[e] : bv;
-            bi = up ? elem_id(base, e) : bi;
+            const bool up = xv[u0 + g][e] > bv[g];
+            bv[g] = up ? xv[u0 + g][e] : bv[g];
+            bi[g] = up ? elem_id(base, e) : bi[g];
         }
-        wave_argmax(bv, bi);
-        res = make_float4(bv, __int_as_float(bi), 0.f, 0.f);
-    } else {
-        float mx = x[0];
-#pragma unroll
-        for (int e = 1; e < kEpt; ++e) mx = fmaxf(mx, x[e]);
-        mx = wave_max(mx);
-        float sm = 0.f;
-        if (mx != kNegInf) {
-            const float mcs = mx * cs;
-#pragma unroll
-            for (int e = 0; e < kEpt; ++e) sm += __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], cs, -mcs));
-        }
-        res = make_float4(mx, wave_sum(sm), 0.f, 0.f);
     }
-    if (lane == 0) sh.part[slot_u][wave] = res;
+#pragma unroll
+    for (int g = 0; g < G; ++g) wave_argmax(bv[g], bi[g]);
+    if (lane == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            sh.part[u0 + g][wave] = make_float4(bv[g], __int_as_float(bi[g]), 0.f, 0.f);
+    }
+}
+
+// The statistics of rows 0 .. n - 1 of the batch (n uniform), four rows to a group.
+__device__ __forceinline__ void batch_stats(FusedShared& sh, const float (&xv)[kRowBatch][kEpt],
+                                            int n, bool argmax, int slot0, float cs, int base) {
+#pragma unroll
+    for (int u0 = 0; u0 < kRowBatch; u0 += 4) {
+        if (u0 >= n) break;
+        const int left = n - u0;
+        if (argmax) {
+            if (left >= 4) group_argmax<4>(sh, xv, u0, base);
+            else if (left == 3) group_argmax<3>(sh, xv, u0, base);
+            else if (left == 2) group_argmax<2>(sh, xv, u0, base);
+            else group_argmax<1>(sh, xv, u0, base);
+        } else {
+            if (left >= 4) group_maxsum<4>(sh, xv, u0, slot0, cs);
+            else if (left == 3) group_maxsum<3>(sh, xv, u0, slot0, cs);
+            else if (left == 2) group_maxsum<2>(sh, xv, u0, slot0, cs);
+            else group_maxsum<1>(sh, xv, u0, slot0, cs);
+        }
+    }
 }
 
 template <bool VEC, bool MAP>
@@ -265,15 +358,16 @@ __device__ __forceinline__ void process_batch(
     const uint32_t (&dm)[kEpt], uint32_t dmo, const float (&fpc)[kEpt],
     const float (&ppc)[kEpt], int base, int c) {
     const int tid = threadIdx.x;
+    // rows of this batch, and how many of them are target rows (the first ones)
+    const int nhere = min(kRowBatch, ndata - q0);
+    const int ntg = max(0, min(nhere, m.rows - q0));
     // LDS partial slots: u for row q0 + u, kRowBatch + u for the raw row of target row q0 + u
+    if (m.raw) batch_stats(sh, xv, ntg, false, kRowBatch, kLog2e, base);
+    if (has_pen) {
 #pragma unroll
-    for (int u = 0; u < kRowBatch; ++u) {
-        const int q = q0 + u;
-        if (q >= ndata) continue;
-        const bool target = q < m.rows;
-        if (target && m.raw) row_stats(sh, xv[u], kRowBatch + u, false, kLog2e, base);
-        if (target && has_pen) {
-            const uint32_t lm = low_bits(q);
+        for (int u = 0; u < kRowBatch; ++u) {
+            if (u >= ntg) continue;
+            const uint32_t lm = low_bits(q0 + u);
             if (__ballot((dmo & lm) != 0u)) {
                 // a draft of an earlier position is among this wave's ids
 #pragma unroll
@@ -285,8 +379,10 @@ __device__ __forceinline__ void process_batch(
                     xv[u][e] = __fsub_rn(__fsub_rn(xv[u][e], fpc[e]), ppc[e]);
             }
         }
-        row_stats(sh, xv[u], u, target && !m.sampled, cs_t, base);
     }
+    // target rows of a greedy sequence: the argmax; every other row: (max, sum) (a greedy
+    // sequence loads no draft rows)
+    batch_stats(sh, xv, nhere, !m.sampled, 0, cs_t, base);
     __syncthreads();
     // combine the waves and store this chunk's entry of each row (and raw row), write-through
     for (int v = tid; v < 2 * kRowBatch; v += kThreads) {
@@ -319,6 +415,26 @@ __device__ __forceinline__ void process_batch(
         handoff_store(reinterpret_cast<float2*>(a.stats) + (size_t)r.slot * a.nchunk + c, out);
     }
 }
+
+// out = row u of the batch (u uniform), zeros when u is out of range: one branch, not a
+// select per row
+__device__ __forceinline__ void pick_row(const float (&xv)[kRowBatch][kEpt], int u,
+                                         float (&out)[kEpt]) {
+#pragma unroll
+    for (int e = 0; e < kEpt; ++e) out[e] = 0.f;
+    switch (u) {
+#define VSA_PICK(n) \
+    case n:         \
+        _Pragma("unroll") for (int e = 0; e < kEpt; ++e) out[e] = xv[n][e]; \
+        break;
+        VSA_PICK(0) VSA_PICK(1) VSA_PICK(2) VSA_PICK(3) VSA_PICK(4) VSA_PICK(5)
+        VSA_PICK(6) VSA_PICK(7) VSA_PICK(8) VSA_PICK(9) VSA_PICK(10) VSA_PICK(11)
+#undef VSA_PICK
+        default:
+            break;
+    }
+}
+static_assert(kRowBatch == 12, "pick_row covers the batch");
 
 template <bool VEC, bool MAP>
 __global__ __launch_bounds__(kThreads) void fused_kernel(const SampArgs a) {
@@ -576,32 +692,23 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const SampArgs a) {
         __syncthreads();
     }
     const DrawRec d = sh.rec;
-    const int acc = d.acc, kind = d.kind;
+    const int acc = __builtin_amdgcn_readfirstlane(d.acc);
+    const int kind = __builtin_amdgcn_readfirstlane(d.kind);
 
     // ---- the draw: this chunk's race from the registers (or reloaded past one row batch)
     DrawSpec ds;
     ds.kind = kind;
-    ds.pos = d.pos;
+    ds.pos = __builtin_amdgcn_readfirstlane(d.pos);
     ds.cs = cs_t;
-    ds.m_p = d.m_p;
-    ds.inv_zp = (float)(1.0 / d.z_p);
-    ds.onehot_d = d.onehot_d;
-    ds.m_q = d.m_q;
-    ds.inv_zq = (float)(1.0 / d.z_q);
+    ds.m_p = uniform_f(d.m_p);
+    ds.inv_zp = uniform_f((float)(1.0 / d.z_p));
+    ds.onehot_d = __builtin_amdgcn_readfirstlane(d.onehot_d);
+    ds.m_q = uniform_f(d.m_q);
+    ds.inv_zq = uniform_f((float)(1.0 / d.z_q));
     float zp[kEpt], xq[kEpt];
     if (ndata <= kRowBatch) {
-#pragma unroll
-        for (int e = 0; e < kEpt; ++e) {
-            zp[e] = xv[0][e];
-            xq[e] = 0.f;
-        }
-#pragma unroll
-        for (int u = 1; u < kRowBatch; ++u)
-#pragma unroll
-            for (int e = 0; e < kEpt; ++e) {
-                zp[e] = u == acc ? xv[u][e] : zp[e];
-                xq[e] = (kind == 1 && nd > 0 && u == m.rows + acc) ? xv[u][e] : xq[e];
-            }
+        pick_row(xv, acc, zp);
+        pick_row(xv, (kind == 1 && nd > 0) ? m.rows + acc : -1, xq);
     } else {
         load_race_chunk<VEC, MAP>(a, m, b, c, acc, sh.drafts, zp, xq, kind == 1 && !onehot);
     }
