@@ -17,6 +17,8 @@
 // fp32 path: the same tiling and merge with plain FMA arithmetic.
 #include "vsa_internal.h"
 
+#include <mutex>
+
 namespace vsa {
 
 namespace {
@@ -30,6 +32,7 @@ constexpr int kThreads = 256;        // threads per workgroup (every kernel here
                                      // so loops do not load the size from the dispatch packet)
 constexpr int kMaxSplits = 32;       // key splits per (sequence, KV head)
 constexpr int kMergeGroup = 8;       // splits whose partials a merge thread loads together
+constexpr uint32_t kMergeWaitTicks = 20000;  // 200 us of the 100 MHz real-time clock
 constexpr float kLazyLog2 = 8.f;     // online softmax: rescale only past this growth (log2)
 #ifndef VSA_ATTN_DMA_CPOL
 #define VSA_ATTN_DMA_CPOL 2
@@ -131,38 +134,24 @@ struct LdsQuad {
     }
 };
 
-// The end of every split of a (sequence, KV head) unit when the keys are split: the split
-// counts itself in on the unit's arrival counter after its partial state is stored (with
-// the hand-off stores: written through to the device-coherent level), and the last of the
-// unit's splits to arrive merges them,
-//   out = sum_s w_s O_s,   w_s = 2^(m_s - m) / sum_s' 2^(m_s' - m) l_s',   m = max_s m_s,
-// the (max, sum) and O of up to kMergeGroup splits loaded together. It also returns the unit's tile-claim and arrival counters to zero. A unit
-// whose geometry is invalid (merge = false) only counts in, so that its counters return to
-// zero as well.
-template <int D>
-__device__ void attn_finish_unit(const AttnArgs& a, int unit, int g, const SeqGeom& s,
-                                 bool merge) {
+// Merges output float4s [e_begin, e_end) of the unit (of M * D/4). Thread tasks: float4s
+// e, e + 256, ... (TPT of them; column e / (D/4), consecutive lanes on consecutive
+// float4s); the loads of all TPT tasks and up to kMergeGroup splits are in flight together
+// (a task past the range loads in bounds and is dropped, so TPT fits the range).
+template <int D, int TPT>
+__device__ void attn_merge_range(const AttnArgs& a, int unit, int g, const SeqGeom& s,
+                                 int e_begin, int e_end) {
     constexpr int D4 = D / 4;
     constexpr int SG = kMergeGroup;
-    __shared__ int s_last;
-    uint32_t* const arrive = counter_at(a.tile_ctr, a.tile_ctr_x, a.units + unit);
-    if (!handoff_arrive(arrive, (uint32_t)a.nsplit, &s_last)) return;
-    if (a.dyn && threadIdx.x == 0)
-        __hip_atomic_store(counter_at(a.tile_ctr, a.tile_ctr_x, unit), 0u, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    if (!merge) return;
-    // Thread tasks: output float4s e, e + 256, e + 512 (column e / (D/4), consecutive
-    // lanes on consecutive float4s); the loads of all three tasks and up to kMergeGroup
-    // splits are in flight together.
-    constexpr int TPT = 3;
-    const int M = s.rows * a.group;
-    const int ntask = M * D4;
+    const int ntask = e_end;
     const int ns = a.nsplit;
     const size_t base = (size_t)unit * ns;
-    const size_t sstride = (size_t)a.mcap * D4;              // float4s between splits
+    const uint32_t sstride = (uint32_t)a.mcap * D4;          // float4s between splits
     const float2* pml = a.part_ml + base * a.mcap;
-    const float4* po = reinterpret_cast<const float4*>(a.part_o) + base * a.mcap * D4;
-    for (int e0 = threadIdx.x; e0 < ntask; e0 += TPT * kThreads) {
+    // the unit's partial outputs (ns * mcap * D floats; a few MB at most)
+    const __amdgpu_buffer_rsrc_t po =
+        handoff_rsrc(a.part_o + base * a.mcap * D, (uint32_t)ns * sstride * 16u);
+    for (int e0 = e_begin + (int)threadIdx.x; e0 < ntask; e0 += TPT * kThreads) {
         float m_run[TPT], l_run[TPT];
         float4 acc[TPT];
 #pragma unroll
@@ -178,12 +167,20 @@ __device__ void attn_finish_unit(const AttnArgs& a, int unit, int g, const SeqGe
             for (int t = 0; t < TPT; ++t) {
                 int e = e0 + t * kThreads;
                 e = e < ntask ? e : ntask - 1;                   // in bounds; dropped below
-                const int n = e / D4;
 #pragma unroll
                 for (int u = 0; u < SG; ++u) {
                     const int sp = s0 + u < ns ? s0 + u : ns - 1;
-                    ml[t][u] = handoff_load(pml + (size_t)sp * a.mcap + n);
-                    v[t][u] = handoff_load4(po + sp * sstride + e);
+                    ml[t][u] = handoff_load(pml + (size_t)sp * a.mcap + e / D4);
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < TPT; ++t) {
+                int e = e0 + t * kThreads;
+                e = e < ntask ? e : ntask - 1;
+#pragma unroll
+                for (int u = 0; u < SG; ++u) {
+                    const int sp = s0 + u < ns ? s0 + u : ns - 1;
+                    v[t][u] = handoff_load16(po, ((uint32_t)sp * sstride + (uint32_t)e) * 16u);
                 }
             }
 #pragma unroll
@@ -222,6 +219,95 @@ __device__ void attn_finish_unit(const AttnArgs& a, int unit, int g, const SeqGe
     }
 }
 
+// Arrival of a split, and the merge of the unit's splits once all have arrived. Each split
+// has stored its partial state (O relative to the split's max, unnormalized; max in log2
+// units; sum) with the hand-off stores (written through to the device-coherent level);
+//   out = sum_s w_s O_s,   w_s = 2^(m_s - m) / sum_s' 2^(m_s' - m) l_s',   m = max_s m_s.
+// Sliced (a.slice_merge: every split of the grid is resident at once): the split that
+// arrives r-th merges the r-th of nsplit slices of the output. The last to arrive merges
+// its slice at once and hands every other slice to its owner through the owner's slot
+// (0 -> 1, go); an owner waits for the go (bounded), merges and returns the slot to 0. An
+// owner that times out marks its slot abandoned (0 -> 2, by compare-and-swap, so exactly
+// one of the two wins) and the last arriver merges that slice too. Otherwise the last to
+// arrive merges all of it. The unit's tile-claim and arrival counters return to zero; a
+// unit whose geometry is invalid (merge = false) only counts in.
+template <int D>
+__device__ void attn_finish_unit(const AttnArgs& a, int unit, int g, const SeqGeom& s,
+                                 bool merge) {
+    constexpr int D4 = D / 4;
+    __shared__ int s_rank, s_go;
+    __shared__ uint32_t s_slot[kMaxSplits];
+    const int ns = a.nsplit;
+    uint32_t* const arrive = counter_at(a.tile_ctr, a.tile_ctr_x, a.units + unit);
+    __builtin_amdgcn_s_waitcnt(0);                     // this workgroup's stores are complete
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t prev = atomicAdd(arrive, 1u);
+        if (prev == (uint32_t)ns - 1u) {
+            __hip_atomic_store(arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (a.dyn)
+                __hip_atomic_store(counter_at(a.tile_ctr, a.tile_ctr_x, unit), 0u,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        s_rank = (int)prev;
+    }
+    __syncthreads();
+    const int rank = s_rank;
+    const bool last = rank == ns - 1;
+    if (!merge) return;
+    const int ntask = s.rows * a.group * D4;
+    if (!a.slice_merge) {
+        if (last) attn_merge_range<D, 3>(a, unit, g, s, 0, ntask);
+        return;
+    }
+    // one slice: up to kThreads float4s a pass
+    auto merge_slice = [&](int lo, int hi) __attribute__((always_inline)) {
+        if (hi - lo <= kThreads) attn_merge_range<D, 1>(a, unit, g, s, lo, hi);
+        else attn_merge_range<D, 3>(a, unit, g, s, lo, hi);
+    };
+    auto slot = [&](int r) __attribute__((always_inline)) {
+        return counter_at(a.tile_ctr, a.tile_ctr_x, 2 * a.units + unit * ns + r);
+    };
+    auto slice_lo = [&](int r) __attribute__((always_inline)) {
+        return (int)((uint32_t)(r * ntask) / (uint32_t)ns);
+    };
+    if (!last) {
+        if (threadIdx.x == 0) {
+            uint32_t* const sl = slot(rank);
+            const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+            uint32_t v;
+            for (;;) {
+                v = __hip_atomic_load(sl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (v == 1u) break;
+                if (__builtin_amdgcn_s_memrealtime() - t0 >= (uint64_t)a.merge_wait) {
+                    // give the slice up, unless the go came in the meantime
+                    v = atomicCAS(sl, 0u, 2u);
+                    if (v == 0u) v = 2u;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+            s_go = (int)v;
+        }
+        __syncthreads();
+        if (s_go != 1) return;                         // abandoned to the last arriver
+        merge_slice(slice_lo(rank), slice_lo(rank + 1));
+        if (threadIdx.x == 0)
+            __hip_atomic_store(slot(rank), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+    // the last arriver: every other slice's go, then its own slice, then any abandoned one
+    if (threadIdx.x < ns - 1) s_slot[threadIdx.x] = atomicCAS(slot(threadIdx.x), 0u, 1u);
+    merge_slice(slice_lo(ns - 1), ntask);
+    __syncthreads();
+    for (int r = 0; r < ns - 1; ++r) {
+        if (s_slot[r] != 2u) continue;
+        merge_slice(slice_lo(r), slice_lo(r + 1));
+        if (threadIdx.x == 0)
+            __hip_atomic_store(slot(r), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
 // Combines the key groups of one workgroup and writes either the final output (single
 // split) or this split's partial state (O relative to the split's max, unnormalized; max in
 // log2 units; sum), which the unit's last split to finish merges (attn_finish_unit). The
@@ -255,6 +341,9 @@ __device__ void attn_epilogue(const AttnArgs& a, LdsQuad ob, float* st, int unit
     __syncthreads();
 
     const size_t pslot = (size_t)unit * a.nsplit + split;
+    // this split's partial output (mcap * D floats)
+    const __amdgpu_buffer_rsrc_t po =
+        handoff_rsrc(a.part_o + pslot * a.mcap * D, (uint32_t)(MC * D * 4));
     for (int e = tid; e < M * (D / 4); e += kThreads) {
         const int n = e / (D / 4), d = 4 * (e % (D / 4));
         float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -276,7 +365,7 @@ __device__ void attn_epilogue(const AttnArgs& a, LdsQuad ob, float* st, int unit
         } else if (a.merge_kernel) {
             *reinterpret_cast<float4*>(a.part_o + (pslot * a.mcap + n) * D + d) = o;
         } else {
-            handoff_store4(reinterpret_cast<float4*>(a.part_o + (pslot * a.mcap + n) * D + d), o);
+            handoff_store16(po, (uint32_t)(n * D + d) * 4u, o);
         }
     }
     if (a.nsplit == 1) return;
@@ -297,9 +386,10 @@ __device__ void attn_empty_split(const AttnArgs& a, int unit, int split, int g,
                                  const SeqGeom& s) {
     const int M = s.rows * a.group;
     const size_t pslot = (size_t)unit * a.nsplit + split;
+    const __amdgpu_buffer_rsrc_t po =
+        handoff_rsrc(a.part_o + pslot * a.mcap * D, (uint32_t)(a.mcap * D * 4));
     for (int e = threadIdx.x; e < M * (D / 4); e += kThreads)
-        handoff_store4(reinterpret_cast<float4*>(a.part_o + (pslot * a.mcap) * D) + e,
-                       make_float4(0.f, 0.f, 0.f, 0.f));
+        handoff_store16(po, (uint32_t)e * 16u, make_float4(0.f, 0.f, 0.f, 0.f));
     for (int n = threadIdx.x; n < M; n += kThreads)
         handoff_store(a.part_ml + pslot * a.mcap + n, make_float2(kNegInf, 0.f));
     if (!a.merge_kernel) attn_finish_unit<D>(a, unit, g, s, true);
@@ -1450,7 +1540,8 @@ AttnPlan plan_attention(int B, int Hq, int Hkv, int D, int max_rows, int max_kv_
     // over the units' columns.
     p.merge_kernel = nsplit > 1 && (size_t)nsplit * p.mcap * D * 4 > ((size_t)128 << 10);
     size_t off = kWsHeader;                                      // error word, counters
-    p.n_ctr_x = extra_counters(2L * p.units);       // tile claims, then arrivals
+    // tile claims, arrivals, then the merge slots of every (unit, split)
+    p.n_ctr_x = extra_counters(2L * p.units + (long)p.units * nsplit);
     p.off_ctr_x = off;
     off += (p.n_ctr_x * 4 + 255) / 256 * 256;
     p.off_ml = off;
@@ -1461,9 +1552,30 @@ AttnPlan plan_attention(int B, int Hq, int Hkv, int D, int max_rows, int max_kv_
     return p;
 }
 
-hipError_t launch_attention(const AttnArgs& a, const AttnPlan& p, vsa_dtype dtype,
+// Compute units of the current device (cached per device).
+static int device_cus() {
+    static std::mutex mu;
+    static int cus[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+            cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+hipError_t launch_attention(const AttnArgs& args, const AttnPlan& p, vsa_dtype dtype,
                             hipStream_t stream) {
     const dim3 grid(p.units * p.nsplit), block(kThreads);
+    // The merge is split over the unit's splits when the whole grid fits on the device at
+    // once (one workgroup per CU at most), so a split waiting for its slice never holds a CU
+    // that another split of its unit still needs; the wait is bounded in any case.
+    AttnArgs a = args;
+    a.slice_merge = p.nsplit > 1 && !p.merge_kernel && (int)grid.x <= device_cus();
+    a.merge_wait = kMergeWaitTicks;
     if (a.bits == 8 || a.bits == 4) {
 #define VSA_KVQ(DD, NBB, BB) hipLaunchKernelGGL((attn_kvq_kernel<DD, NBB, BB>), grid, block, 0, stream, a)
         if (a.bits == 8) {

@@ -181,6 +181,32 @@ __device__ __forceinline__ float4 handoff_load4(const float4* p) {
     return make_float4(a.x, a.y, b.x, b.y);
 }
 
+// 16-byte hand-off loads and stores through a buffer resource, with the cache policy of
+// the agent-scope atomic ones above (sc1): one instruction per float4 instead of two. They
+// are not single-copy atomic across the 16 bytes, which a hand-off does not need (the
+// values are complete before the counter says so). The resource's byte count bounds every
+// access: a load past it returns 0 and a store past it is dropped.
+typedef unsigned int vsa_u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kCpolSc1 = 16;                // cache-policy operand: sc1
+constexpr int kRawBufferWord3 = 0x00020000; // raw (untyped) access, 32-bit data format
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t handoff_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             kRawBufferWord3);
+}
+__device__ __forceinline__ float4 handoff_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const vsa_u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolSc1);
+    return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                       __uint_as_float(v.w));
+}
+__device__ __forceinline__ void handoff_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, float4 v) {
+    vsa_u32x4 u;
+    u.x = __float_as_uint(v.x);
+    u.y = __float_as_uint(v.y);
+    u.z = __float_as_uint(v.z);
+    u.w = __float_as_uint(v.w);
+    __builtin_amdgcn_raw_buffer_store_b128(u, r, off, 0, kCpolSc1);
+}
+
 // Every thread's hand-off stores are complete before thread 0 counts the workgroup in;
 // returns true (in every thread) in the last of `total` workgroups to arrive, which also
 // resets the counter for the next call unless `reset` is false (then whoever else reads
@@ -227,6 +253,8 @@ struct AttnArgs {
     int window;             // > 0: context keys seen per row are limited (see mask)
     int mask;               // kMaskBidirectional | kMaskSliding
     int merge_kernel;       // the splits are merged by attn_merge_kernel, not in the kernel
+    int slice_merge;        // in-kernel merge split over the unit's splits (all resident)
+    uint32_t merge_wait;    // real-time ticks a split waits for its slice of the merge
 };
 constexpr int kMaskBidirectional = 1;   // block rows see every block row
 constexpr int kMaskSliding = 2;         // the window ends at each row's own position
