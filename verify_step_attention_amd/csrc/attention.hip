@@ -344,7 +344,14 @@ __device__ void attn_epilogue(const AttnArgs& a, LdsQuad ob, float* st, int unit
     // this split's partial output (mcap * D floats)
     const __amdgpu_buffer_rsrc_t po =
         handoff_rsrc(a.part_o + pslot * a.mcap * D, (uint32_t)(MC * D * 4));
-    for (int e = tid; e < M * (D / 4); e += kThreads) {
+    // at most 32 NBX rows of D / 4 float4s; with one column block (at most four passes)
+    // every pass is unrolled, so their LDS reads overlap (more passes would spill)
+    constexpr int kPasses = (32 * NBX * (D / 4) + kThreads - 1) / kThreads;
+    constexpr int kUnroll = NBX == 1 ? kPasses : 1;
+#pragma unroll kUnroll
+    for (int pass = 0; pass < kPasses; ++pass) {
+        const int e = tid + pass * kThreads;
+        if (e >= M * (D / 4)) continue;
         const int n = e / (D / 4), d = 4 * (e % (D / 4));
         float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
@@ -780,12 +787,14 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(const AttnArgs a) {
         stats[kg * a.mcap + n] = m_run;
         stats[kStatCap + kg * a.mcap + n] = l_tot;
     }
+    // accumulator entries r = 4 i .. 4 i + 3 are 4 consecutive d: one 16-byte store each
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int d = 32 * db + 8 * (r >> 2) + 4 * h + (r & 3);
-            mine[col * OS + d] = o[db][r];
+        for (int i = 0; i < 4; ++i) {
+            const int d = 32 * db + 8 * i + 4 * h;
+            *reinterpret_cast<float4*>(mine + col * OS + d) =
+                make_float4(o[db][4 * i], o[db][4 * i + 1], o[db][4 * i + 2], o[db][4 * i + 3]);
         }
     __syncthreads();
     attn_epilogue<D, KG, NB>(a, ob, stats, unit, split, g, s, OS);
@@ -1329,12 +1338,14 @@ __global__ __launch_bounds__(256, 1) void attn_kvq_kernel(const AttnArgs a) {
         stats[kg * a.mcap + n] = m_run;
         stats[kStatCap + kg * a.mcap + n] = l_tot;
     }
+    // accumulator entries r = 4 i .. 4 i + 3 are 4 consecutive d: one 16-byte store each
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int d = 32 * db + 8 * (r >> 2) + 4 * h + (r & 3);
-            mine[col * OS + d] = o[db][r];
+        for (int i = 0; i < 4; ++i) {
+            const int d = 32 * db + 8 * i + 4 * h;
+            *reinterpret_cast<float4*>(mine + col * OS + d) =
+                make_float4(o[db][4 * i], o[db][4 * i + 1], o[db][4 * i + 2], o[db][4 * i + 3]);
         }
     __syncthreads();
     attn_epilogue<D, KG, NB>(a, ob, stats, unit, split, g, s, OS);
