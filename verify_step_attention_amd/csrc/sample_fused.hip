@@ -416,6 +416,29 @@ __device__ __forceinline__ void process_batch(
     }
 }
 
+// The draft ids of sequence m by scalar loads (read-only input, so the constant address
+// space), as draft_masks computes from them: dm (bit t of id e: draft t + 1 equals it), the
+// ids in sh.drafts (read after the next barrier) and, in lane t of wave 0, draft t + 1.
+__device__ __forceinline__ void scalar_drafts(const SampArgs& a, const SeqMode& m, int base,
+                                              FusedShared& sh, uint32_t (&dm)[kEpt],
+                                              int& dreg) {
+    typedef __attribute__((address_space(4))) const int const_int;
+    const const_int* dp = (const const_int*)(a.drafts + m.d0);
+#pragma unroll
+    for (int e = 0; e < kEpt; ++e) dm[e] = 0u;
+    for (int t = 0; t < m.k; ++t) {
+        const int d = dp[t];
+        if (threadIdx.x == 0) sh.drafts[t] = d;
+        if ((int)threadIdx.x == t) dreg = d;
+        const int off = d - base;
+        if (off >= 0 && off < kChunk && ((off & 1023) >> 2) == (int)threadIdx.x) {
+            const int ee = (off >> 10) * 4 + (off & 3);
+#pragma unroll
+            for (int e = 0; e < kEpt; ++e) dm[e] |= (e == ee) ? (1u << t) : 0u;
+        }
+    }
+}
+
 // out = row u of the batch (u uniform), zeros when u is out of range: one branch, not a
 // select per row
 __device__ __forceinline__ void pick_row(const float (&xv)[kRowBatch][kEpt], int u,
@@ -468,16 +491,14 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const SampArgs a) {
     const bool has_pen = m.pp != 0.f || m.fp != 0.f;
     float fpc[kEpt], ppc[kEpt];
 
-    // ---- phase 1: per-row statistics of this chunk, kRowBatch rows at a time
+    // ---- phase 1: per-row statistics of this chunk, kRowBatch rows at a time. The draft
+    // ids come by scalar loads, which wait apart from the rows' vector loads: the draft
+    // masks are ready while the rows still stream in.
     float xv[kRowBatch][kEpt];
 #pragma unroll
     for (int u = 0; u < kRowBatch; ++u)
         if (u < ndata) load_row_chunk<VEC, MAP>(a, m, row_ref(a, m, u), base, xv[u]);
-    // the draft ids after the first batch of rows (vector loads return in order)
-    dreg = tid < m.k ? a.drafts[m.d0 + tid] : 0;
-    if (tid < m.k) sh.drafts[tid] = dreg;
-    __syncthreads();
-    draft_masks(sh.drafts, m.k, base, dm);
+    scalar_drafts(a, m, base, sh, dm, dreg);
 #pragma unroll
     for (int e = 0; e < kEpt; ++e) {
         dmo |= dm[e];
