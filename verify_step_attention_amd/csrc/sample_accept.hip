@@ -1029,7 +1029,6 @@ __global__ __launch_bounds__(kThreads) void race_kernel(const SampArgs a) {
     uint32_t ebits = 0;
     const SeqMode m = seq_mode(a, b, &ebits);
     if (!m.valid || !m.sampled || m.topk || rq.kind == 0) return;
-    const int dreg = tid < m.k ? a.drafts[m.d0 + tid] : 0;
     const int base = c * kChunk;
     int cnt[kEpt];
     load_counts<VEC>(a.counts ? a.counts + (size_t)b * a.vocab : nullptr, base, a.vocab, cnt);
@@ -1039,10 +1038,9 @@ __global__ __launch_bounds__(kThreads) void race_kernel(const SampArgs a) {
     else
 #pragma unroll
         for (int e = 0; e < kEpt; ++e) xq[e] = 0.f;
-    if (tid < m.k) s_draft[tid] = dreg;
-    __syncthreads();
     uint32_t dm[kEpt];
-    draft_masks(s_draft, rq.a, base, dm);
+    int dreg = 0;
+    scalar_drafts(a, m, rq.a, base, s_draft, dm, dreg);
     const float4 part = rq.nucleus ? race_chunk<true>(a, m, rq, b, c, cnt, dm, xp, xq)
                                    : race_chunk<false>(a, m, rq, b, c, cnt, dm, xp, xq);
     if ((tid & 63) == 0) handoff_store4(a.race_part + ((size_t)b * a.nchunk + c) * 4 + (tid >> 6), part);
@@ -1226,7 +1224,7 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
     const SeqMode m = seq_mode(a, b, &ebits);
     if (c == 0 && tid == 0 && ebits) atomicOr(a.err, ebits);
     if (!m.valid) return;
-    const int dreg = tid < m.k ? a.drafts[m.d0 + tid] : 0;
+    int dreg = 0;
     uint32_t valid = 0;
 #pragma unroll
     for (int e = 0; e < kEpt; ++e) valid |= (elem_id(base, e) < a.vocab ? 1u : 0u) << e;
@@ -1262,9 +1260,8 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
                 load_row_chunk<VEC, MAP, false>(a, m, row_ref(a, m, s_row + a.rsplit * (j0 + u)),
                                                 base, xv[u]);
         if (j0 == 0) {
-            if (tid < m.k) s_draft[tid] = dreg;
-            __syncthreads();
-            draft_masks(s_draft, m.k, base, dm);
+            // the draft ids by scalar loads: no wait for this batch's rows
+            scalar_drafts(a, m, m.k, base, s_draft, dm, dreg);
 #pragma unroll
             for (int e = 0; e < kEpt; ++e) dmo |= dm[e];
         }

@@ -406,6 +406,31 @@ __device__ __forceinline__ void draft_masks(const int* s_draft, int k, int base,
     }
 }
 
+// The draft ids of sequence m by scalar loads (read-only input, so the constant address
+// space): those wait apart from the vector loads of the rows issued before, which return
+// in issue order. Computes what draft_masks computes over the first n drafts (dm), stores
+// the k ids in lds (thread 0; read after the next barrier) and gives lane t of wave 0 the
+// id of draft t + 1 (dreg).
+__device__ __forceinline__ void scalar_drafts(const SampArgs& a, const SeqMode& m, int n,
+                                              int base, int* lds, uint32_t (&dm)[kEpt],
+                                              int& dreg) {
+    typedef __attribute__((address_space(4))) const int const_int;
+    const const_int* dp = (const const_int*)(a.drafts + m.d0);
+#pragma unroll
+    for (int e = 0; e < kEpt; ++e) dm[e] = 0u;
+    for (int t = 0; t < m.k; ++t) {
+        const int d = dp[t];
+        if (threadIdx.x == 0) lds[t] = d;
+        if ((int)threadIdx.x == t) dreg = d;
+        const int off = d - base;
+        if (t < n && off >= 0 && off < kChunk && ((off & 1023) >> 2) == (int)threadIdx.x) {
+            const int ee = (off >> 10) * 4 + (off & 3);
+#pragma unroll
+            for (int e = 0; e < kEpt; ++e) dm[e] |= (e == ee) ? (1u << t) : 0u;
+        }
+    }
+}
+
 __device__ __forceinline__ uint32_t low_bits(int i) { return i >= 32 ? ~0u : (1u << i) - 1u; }
 
 // (max, normalizer) of a softmax row from its per-chunk (max, sum) entries, one wave: lane

@@ -416,29 +416,6 @@ __device__ __forceinline__ void process_batch(
     }
 }
 
-// The draft ids of sequence m by scalar loads (read-only input, so the constant address
-// space), as draft_masks computes from them: dm (bit t of id e: draft t + 1 equals it), the
-// ids in sh.drafts (read after the next barrier) and, in lane t of wave 0, draft t + 1.
-__device__ __forceinline__ void scalar_drafts(const SampArgs& a, const SeqMode& m, int base,
-                                              FusedShared& sh, uint32_t (&dm)[kEpt],
-                                              int& dreg) {
-    typedef __attribute__((address_space(4))) const int const_int;
-    const const_int* dp = (const const_int*)(a.drafts + m.d0);
-#pragma unroll
-    for (int e = 0; e < kEpt; ++e) dm[e] = 0u;
-    for (int t = 0; t < m.k; ++t) {
-        const int d = dp[t];
-        if (threadIdx.x == 0) sh.drafts[t] = d;
-        if ((int)threadIdx.x == t) dreg = d;
-        const int off = d - base;
-        if (off >= 0 && off < kChunk && ((off & 1023) >> 2) == (int)threadIdx.x) {
-            const int ee = (off >> 10) * 4 + (off & 3);
-#pragma unroll
-            for (int e = 0; e < kEpt; ++e) dm[e] |= (e == ee) ? (1u << t) : 0u;
-        }
-    }
-}
-
 // out = row u of the batch (u uniform), zeros when u is out of range: one branch, not a
 // select per row
 __device__ __forceinline__ void pick_row(const float (&xv)[kRowBatch][kEpt], int u,
@@ -498,7 +475,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const SampArgs a) {
 #pragma unroll
     for (int u = 0; u < kRowBatch; ++u)
         if (u < ndata) load_row_chunk<VEC, MAP>(a, m, row_ref(a, m, u), base, xv[u]);
-    scalar_drafts(a, m, base, sh, dm, dreg);
+    scalar_drafts(a, m, m.k, base, sh.drafts, dm, dreg);
 #pragma unroll
     for (int e = 0; e < kEpt; ++e) {
         dmo |= dm[e];
