@@ -43,6 +43,8 @@ namespace {
 
 constexpr int kRowBatch = 12;        // rows whose chunk loads are in flight together
 constexpr int kFusedRows = 3 * kMaxSeqRows;
+constexpr int kPrePos = 8;           // draw positions whose race variates a waiting workgroup
+                                     // may compute ahead (sequences with K < kPrePos)
 
 // The decision of a sampled sequence, published by its last arriver for the others (the
 // workspace's race-request slot of the sequence, 56 bytes: seven 8-byte stores).
@@ -63,7 +65,11 @@ struct FusedShared {
     DrawRec rec;                     // the decision, as the last arriver published it
     int acc, kind;                   // decision: accepted drafts, draw kind (1 resid, 2 bonus)
     int flag;
+    int go_seen;                     // the go flag, as thread 0 last read it
     uint32_t state[kMaxChunks];      // abandon flags seen by the workgroup completing D
+    // 1 / (-log2 U) of this chunk's ids for the draw at position positions[b] + p, computed
+    // while the workgroup waits for the decision
+    float einv[kPrePos][kEpt][kThreads];
 };
 
 __device__ __forceinline__ float2 coh_load2(const float2* p) { return handoff_load(p); }
@@ -149,9 +155,28 @@ struct DrawSpec {
     float inv_zp, inv_zq;
     int onehot_d;
 };
+// 1 / (-log2 U) of the thread's ids of the chunk at `base` for the draw at absolute position
+// pos. The key words sit in vector registers (the kernel's scalar registers are taken, and
+// scalar round keys would be spilled and reloaded).
+__device__ __forceinline__ void race_variates(const SampArgs& a, int b, int base, int pos,
+                                              float (&inv_e)[kEpt]) {
+    const int tid = threadIdx.x;
+    uint32_t k0 = (uint32_t)a.seed, k1 = (uint32_t)(a.seed >> 32);
+    asm volatile("" : "+v"(k0), "+v"(k1));
+#pragma unroll
+    for (int qd = 0; qd < kQuads; ++qd) {
+        const RaceWords w = race_words4_k(k0, k1, base + 1024 * qd + 4 * tid, pos, b);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            inv_e[4 * qd + r] = __builtin_amdgcn_rcpf(race_e2(w.hi(r), w.lo(r)));
+    }
+}
+
+// einv: this chunk's variates for the draw's position ([kEpt][kThreads] in LDS), or null
+// to compute them here.
 __device__ __forceinline__ void race_chunk_regs(const SampArgs& a, const DrawSpec& ds, int b,
                                                 int base, const float (&zp)[kEpt],
-                                                const float (&xq)[kEpt],
+                                                const float (&xq)[kEpt], const float* einv,
                                                 unsigned long long* best_r,
                                                 unsigned long long* best_p) {
     const int tid = threadIdx.x;
@@ -171,17 +196,13 @@ __device__ __forceinline__ void race_chunk_regs(const SampArgs& a, const DrawSpe
 #pragma unroll
         for (int e = 0; e < kEpt; ++e) rw[e] = pw[e];
     }
-    // the variates of the thread's ids; the key words sit in vector registers (the kernel's
-    // scalar registers are taken, and scalar round keys would be spilled and reloaded)
-    uint32_t k0 = (uint32_t)a.seed, k1 = (uint32_t)(a.seed >> 32);
-    asm volatile("" : "+v"(k0), "+v"(k1));
+    // the variates of the thread's ids: from the table computed while waiting, or here
     float inv_e[kEpt];
+    if (einv) {
 #pragma unroll
-    for (int qd = 0; qd < kQuads; ++qd) {
-        const RaceWords w = race_words4_k(k0, k1, base + 1024 * qd + 4 * tid, ds.pos, b);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            inv_e[4 * qd + r] = __builtin_amdgcn_rcpf(race_e2(w.hi(r), w.lo(r)));
+        for (int e = 0; e < kEpt; ++e) inv_e[e] = einv[e * kThreads + tid];
+    } else {
+        race_variates(a, b, base, ds.pos, inv_e);
     }
     float kr_best = 0.f, kp_best = 0.f;
     int jr = 0, jp = 0;
@@ -516,6 +537,26 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const SampArgs a) {
     const int xq0 = m.rows + nd;                 // first raw row in the row list
     bool abandoned_final = false;                // this workgroup abandoned its chunk and
                                                  // then completed D
+    int npre = 0;                                // positions whose variates are in sh.einv
+    if (!last && m.k < kPrePos) {
+        // While the last arriver decides: the race variates of every position the draw can
+        // take (positions[b] + a, a the accepted drafts, 0 <= a <= K), one position at a
+        // time, each followed by a look at the go flag (thread 0); the first look that finds
+        // it set ends this.
+        const int pos0 = a.positions[b];
+        for (int pp = 0; pp <= m.k; ++pp) {
+            float inv_e[kEpt];
+            race_variates(a, b, base, pos0 + pp, inv_e);
+#pragma unroll
+            for (int e = 0; e < kEpt; ++e) sh.einv[pp][e][tid] = inv_e[e];
+            if (tid == 0) sh.go_seen = (int)coh_load_u32(st.go);
+            __syncthreads();
+            npre = pp + 1;
+            const int seen = sh.go_seen;
+            __syncthreads();                             // sh.go_seen is rewritten next
+            if (seen) break;
+        }
+    }
     if (!last) {
         // a sampled sequence's other workgroups: wait (bounded) for the decision, then load
         // the record; on a timeout the chunk is abandoned to whoever completes D
@@ -714,7 +755,8 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const SampArgs a) {
     unsigned long long br, bp;
     bool final_wg = abandoned_final;
     if (!abandoned_final) {
-        race_chunk_regs(a, ds, b, base, zp, xq, &br, &bp);
+        race_chunk_regs(a, ds, b, base, zp, xq, acc < npre ? &sh.einv[acc][0][0] : nullptr, &br,
+                        &bp);
         publish_race(sh, st, br, bp);
         final_wg = count_done(sh, st, total);
     }
@@ -734,7 +776,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const SampArgs a) {
             if (sh.state[cc] == 0u) continue;
             float zr[kEpt], qr[kEpt];
             load_race_chunk<VEC, MAP>(a, m, b, cc, acc, sh.drafts, zr, qr, kind == 1 && !onehot);
-            race_chunk_regs(a, ds, b, cc * kChunk, zr, qr, &br, &bp);
+            race_chunk_regs(a, ds, b, cc * kChunk, zr, qr, nullptr, &br, &bp);
             publish_race(sh, st, br, bp);
         }
     }
