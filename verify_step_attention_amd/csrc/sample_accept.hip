@@ -35,8 +35,6 @@ using namespace samp;
 
 namespace {
 
-constexpr int kRowBatch = 12;                  // rows whose chunk loads are in flight together
-
 // ------------------------------------------------------------------ workgroup radix select
 // The k-th largest key (1-based) among the valid keys of the workgroup, 8 bits at a time.
 // hist: LDS[256]; sh: LDS[>= 2].
@@ -378,7 +376,7 @@ struct FinalShared {
 
 // ------------------------------------------------------------------ per-row selection
 // (max, normalizer) of one row from its chunk statistics, by one wave (every lane returns it).
-__device__ RowInfo row_stats_wave(const SampArgs& a, const SeqMode& m, const RowRef& r) {
+__device__ __forceinline__ RowInfo row_stats_wave(const SampArgs& a, const SeqMode& m, const RowRef& r) {
     const int lane = threadIdx.x & 63;
     float4 st[kChunkLoads];
 #pragma unroll
@@ -413,7 +411,7 @@ __device__ RowInfo row_stats_wave(const SampArgs& a, const SeqMode& m, const Row
 // Lower bounds of the row's k-th largest key usually leave a few dozen candidates, sorted
 // exactly; otherwise a radix select over the registers decides. The kept ids (key >= theta)
 // go to an LDS list that wave 0 sorts.
-__device__ void select_row(const SampArgs& a, const SeqMode& m, int q, FinalShared& fs) {
+__device__ __forceinline__ void select_row(const SampArgs& a, const SeqMode& m, int q, FinalShared& fs) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int* const ccount = fs.ccount;
     const RowRef r = row_ref(a, m, q);
@@ -1057,106 +1055,130 @@ __global__ __launch_bounds__(kThreads) void race_kernel(const SampArgs a) {
 
 // ------------------------------------------------------------------ wave-layout chunk
 // A whole chunk of one row in one wave: lane l holds the float4s l + 64 j (j < 8), that is
-// ids base + 4 (l + 64 j) + i (i < 4) as element e = 4 j + i. The candidate phase of the
-// sweep gives each truncated row to one wave: rows proceed side by side without workgroup
-// barriers, each wave loads its next row while it works on the current one, and the code
-// of one row is reused for the next (straight-line code that runs once per workgroup is
-// bound by instruction fetch).
+// ids base + 4 (l + 64 j) + i (i < 4) as element e = 4 j + i. The sweep gives each data row
+// (a target row together with its raw twin, which reads the same logits, or a draft row)
+// to one wave: penalties, statistics and candidates of the row with wave reductions only,
+// no workgroup barrier, while the wave's next row loads. Every global access in that loop
+// goes through a buffer resource whose byte count bounds it (a load past it returns 0, a
+// store past it is dropped), so no memory instruction there is conditional: the compiler
+// then counts the loads in flight exactly and the next row's loads overlap the current
+// row's work (a conditional load or store before a use makes it wait for all of them).
 constexpr int kWj = kChunk / 256;                 // float4s per lane
 constexpr int kWe = 4 * kWj;                      // ids per lane
+constexpr int kNtPolicy = 2;                      // cache policy of streamed rows: nt
+// candidate slots of a (row, chunk): capc <= max(top-k bound kKeep, top-logprobs bound 32)
+// + 32, so kCandStores stores per lane write any of them
+constexpr int kCandCap = kKeep + 32;
+constexpr int kCandStores = (kCandCap + 63) / 64;
 __device__ __forceinline__ int welem_id(int base, int lane, int e) {
     return base + 4 * (lane + 64 * (e >> 2)) + (e & 3);
 }
-template <bool VEC, class T>
-__device__ __forceinline__ void wload4(const T* row, int base, int vocab, int lane, T fill,
-                                       T (&x)[kWe]) {
+// Inclusive prefix sum over the wave's lanes (lane i: x_0 + ... + x_i): shifts by 1, 2, 4, 8
+// within rows of 16 lanes, then the row totals carried by broadcasts.
+__device__ __forceinline__ int wave_incl_scan_i(int x) {
+    x += dpp_i<0x111>(0, x);                      // row_shr:1 (lanes without a source add 0)
+    x += dpp_i<0x112>(0, x);
+    x += dpp_i<0x114>(0, x);
+    x += dpp_i<0x118>(0, x);
+    x += dpp_i<kDppBcast15, 0xA>(0, x);
+    x += dpp_i<kDppBcast31, 0xC>(0, x);
+    return x;
+}
+// The 32-bit words at the chunk's ids of the array that `rs` covers (0 past its end).
+template <bool VEC>
+__device__ __forceinline__ void wbuf_load(__amdgpu_buffer_rsrc_t rs, int base, int lane,
+                                          uint32_t (&x)[kWe]) {
     if (VEC) {
 #pragma unroll
         for (int j = 0; j < kWj; ++j) {
-            const int id0 = base + 4 * (lane + 64 * j);
-            if (id0 < vocab) {
-                const auto v = *reinterpret_cast<const decltype(make_float4(0, 0, 0, 0))*>(
-                    reinterpret_cast<const float*>(row) + id0);
-                x[4 * j] = __builtin_bit_cast(T, v.x);
-                x[4 * j + 1] = __builtin_bit_cast(T, v.y);
-                x[4 * j + 2] = __builtin_bit_cast(T, v.z);
-                x[4 * j + 3] = __builtin_bit_cast(T, v.w);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) x[4 * j + i] = fill;
-            }
+            const vsa_u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(
+                rs, (uint32_t)(base + 4 * (lane + 64 * j)) * 4u, 0, kNtPolicy);
+            x[4 * j] = v.x;
+            x[4 * j + 1] = v.y;
+            x[4 * j + 2] = v.z;
+            x[4 * j + 3] = v.w;
         }
     } else {
+#pragma unroll
+        for (int e = 0; e < kWe; ++e)
+            x[e] = __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)welem_id(base, lane, e) * 4u,
+                                                        0, kNtPolicy);
+    }
+}
+// Data row d of the sequence (target row d < R, else draft row d - R + 1) at the chunk's
+// ids, -inf past the vocabulary (draft rows through t2d when MAP). `present` false: no
+// row (the loads cover 0 bytes).
+template <bool VEC, bool MAP>
+__device__ __forceinline__ void wload_data(const SampArgs& a, const SeqMode& m, int d, bool present,
+                                           int base, int lane, uint32_t valid, float (&x)[kWe]) {
+    uint32_t u[kWe];
+    if (MAP && d >= m.rows) {
+        const float* row = a.dl + (size_t)(m.d0 + d - m.rows) * a.dvocab;
+        wbuf_load<VEC>(handoff_rsrc(a.t2d, present ? (uint32_t)a.vocab * 4u : 0u), base, lane, u);
+        const __amdgpu_buffer_rsrc_t rr = handoff_rsrc(row, present ? (uint32_t)a.dvocab * 4u : 0u);
+        uint32_t ebits = 0;
+#pragma unroll
+        for (int e = 0; e < kWe; ++e) {
+            const int mp = ((valid >> e) & 1u) ? (int)u[e] : -1;
+            // an entry outside [0, dvocab) reads past the resource: 0, replaced by -inf
+            const float v = __uint_as_float(
+                __builtin_amdgcn_raw_buffer_load_b32(rr, (uint32_t)mp * 4u, 0, kNtPolicy));
+            x[e] = (uint32_t)mp < (uint32_t)a.dvocab ? v : kNegInf;
+            ebits |= (mp < -1 || mp >= a.dvocab) ? VSA_DEVERR_DRAFT_MAP : 0u;
+        }
+        if (__ballot(ebits != 0u) && lane == 0) atomicOr(a.err, VSA_DEVERR_DRAFT_MAP);
+        return;
+    }
+    const float* row = d < m.rows ? a.tl + (size_t)(m.r0 + d) * a.vocab
+                                  : a.dl + (size_t)(m.d0 + d - m.rows) * a.vocab;
+    wbuf_load<VEC>(handoff_rsrc(row, present ? (uint32_t)a.vocab * 4u : 0u), base, lane, u);
+#pragma unroll
+    for (int e = 0; e < kWe; ++e) x[e] = ((valid >> e) & 1u) ? __uint_as_float(u[e]) : kNegInf;
+}
+
+// Chunk statistics of one row, by one wave (valid in every lane): (max v, sum of
+// 2^((v - max) cs)) for a softmax row, (0, 0, value, id) of the argmax (lowest id on ties)
+// for a greedy target row. Invalid ids hold -inf.
+__device__ __forceinline__ float4 wave_row_stats(int base, int lane, uint32_t valid, bool greedy,
+                                                 float cs, const float (&v)[kWe]) {
+    if (greedy) {
+        float bv = kNegInf;
+        int bi = kBigIdx;
 #pragma unroll
         for (int e = 0; e < kWe; ++e) {
             const int id = welem_id(base, lane, e);
-            x[e] = id < vocab ? row[id] : fill;
+            const bool t = ((valid >> e) & 1u) && better(v[e], id, bv, bi);
+            bv = t ? v[e] : bv;
+            bi = t ? id : bi;
         }
+        wave_argmax(bv, bi);
+        return make_float4(0.f, 0.f, bv, __int_as_float(bi));
     }
-}
-// Row r's values at the chunk's ids in the wave layout (draft rows through t2d when MAP),
-// and for target rows the base counts.
-template <bool VEC, bool MAP>
-__device__ __forceinline__ void wload_row(const SampArgs& a, const SeqMode& m, const RowRef& r,
-                                          int b, int base, int lane, float (&x)[kWe],
-                                          int (&cnt)[kWe]) {
-    if (r.kind != 1 || !MAP) {
-        const float* row = r.kind == 1 ? a.dl + (size_t)(m.d0 + r.i - 1) * a.vocab
-                                       : a.tl + (size_t)(m.r0 + r.i) * a.vocab;
-        wload4<VEC>(row, base, a.vocab, lane, kNegInf, x);
-    } else {
-        const float* row = a.dl + (size_t)(m.d0 + r.i - 1) * a.dvocab;
-        int map[kWe];
-        wload4<VEC>(a.t2d, base, a.vocab, lane, -1, map);
-        uint32_t ebits = 0;
+    float mx = v[0];
 #pragma unroll
-        for (int e = 0; e < kWe; ++e) x[e] = mapped_logit(a, row, map[e], &ebits);
-        if (ebits) atomicOr(a.err, ebits);
-    }
-    if (r.kind == 0 && a.counts)
-        wload4<VEC>(a.counts + (size_t)b * a.vocab, base, a.vocab, lane, 0, cnt);
-    else {
+    for (int e = 1; e < kWe; ++e) mx = fmaxf(mx, v[e]);
+    mx = wave_max(mx);
+    float sm = 0.f;
+    if (mx != kNegInf) {
 #pragma unroll
-        for (int e = 0; e < kWe; ++e) cnt[e] = 0;
+        for (int e = 0; e < kWe; ++e) sm += __builtin_amdgcn_exp2f((v[e] - mx) * cs);
     }
+    return make_float4(mx, wave_sum(sm), 0.f, 0.f);
 }
 
-// Candidates of one truncated or top-n row in this chunk, by one wave, from its loaded
-// values: every key >= vk for a vk at or below the chunk's kk-th largest key. vk is the
-// largest 16-bit-prefixed value T such that at least kk of the lanes' group maxima (the
-// maxima of 1, 2 or 4 disjoint groups of each lane's ids as kk needs: distinct ids) are
-// >= T, found by a binary search with ballot counts; it lies within 2^-7 of the kk-th
-// largest of those maxima, so the candidates are usually the kk largest and a few more.
-// Returns false when they do not fit in capc slots (the workgroup path then takes the row
-// and rewrites its slots).
-__device__ bool wave_row_candidates(const SampArgs& a, const SeqMode& m, const RowRef& r,
-                                    int c, int base, const int* s_draft, int kk,
-                                    const float (&x)[kWe], int (&cnt)[kWe]) {
-    const int lane = threadIdx.x & 63;
-    if (r.kind == 0) {
-        // the drafts d_1 .. d_i before target row i add to the counts
-        for (int t = 0; t < r.i; ++t) {
-            const int off = s_draft[t] - base;
-            if (off < 0 || off >= kChunk || ((off >> 2) & 63) != lane) continue;
-            const int ee = 4 * (off >> 8) + (off & 3);
-#pragma unroll
-            for (int e = 0; e < kWe; ++e) cnt[e] += e == ee ? 1 : 0;
-        }
-    }
-    uint32_t key[kWe];
-    uint32_t valid = 0u;
-#pragma unroll
-    for (int e = 0; e < kWe; ++e) {
-        const bool in = welem_id(base, lane, e) < a.vocab;
-        const float val = r.kind == 0 ? penalize(x[e], cnt[e], m.pp, m.fp) : x[e];
-        key[e] = in ? ord_key(val) : 0u;
-        valid |= (in ? 1u : 0u) << e;
-    }
-    const int n_valid = min(kChunk, a.vocab - base);
+// Candidates of one truncated or top-n row in this chunk, by one wave: every key >= vk for
+// a vk at or below the chunk's kk-th largest key. vk is the largest 16-bit-prefixed value T
+// such that at least kk of the lanes' group maxima (the maxima of 1, 2 or 4 disjoint groups
+// of each lane's ids as kk needs: distinct ids) are >= T, found by a binary search with
+// ballot counts; it lies within 2^-7 of the kk-th largest of those maxima, so the
+// candidates are usually the kk largest and a few more. They go to the wave's LDS list
+// (the first capc of them); *total counts them all (more than capc: the workgroup path
+// takes the row).
+__device__ __forceinline__ void wave_candidates(const SampArgs& a, int base, int lane, int kk, int n_valid,
+                                uint32_t valid, const uint32_t (&key)[kWe], uint2* list,
+                                int* total_out, uint32_t* vk_out) {
     uint32_t vk = 0u;
     if (n_valid > kk) {
-        // the maxima of 1, 2 or 4 disjoint groups of the lane's ids (distinct ids; invalid
-        // ids are 0, below every key), as kk needs
         const int ng = kk <= 16 ? 1 : kk <= 32 ? 2 : 4;
         uint32_t g8[8];
 #pragma unroll
@@ -1183,275 +1205,216 @@ __device__ bool wave_row_candidates(const SampArgs& a, const SeqMode& m, const R
         }
         vk = t;
     }
-    uint2* out = a.cand + ((size_t)r.slot * a.nchunk + c) * a.capc;
-    int total = 0;
+    // this lane's candidates as a mask of its elements, their count, and the candidates of
+    // the lanes before it: each lane fills consecutive slots, no ballot per element
+    uint32_t tm = 0u;
+#pragma unroll
+    for (int e = 0; e < kWe; ++e) tm |= (((valid >> e) & 1u) && key[e] >= vk) ? (1u << e) : 0u;
+    const int n = __popc(tm);
+    const int incl = wave_incl_scan_i(n);
+    const int off = incl - n;
+    // every element is written, a candidate to its slot and any other to the lane's spare
+    // slot past the list, so the writes take no branch
+    const int spare = kCandCap + lane;
 #pragma unroll
     for (int e = 0; e < kWe; ++e) {
-        const bool take = ((valid >> e) & 1u) && key[e] >= vk;
-        const unsigned long long bal = __ballot(take);
-        if (take) {
-            const int pos = total + __popcll(bal & ((1ull << lane) - 1ull));
-            if (pos < a.capc) out[pos] = make_uint2(key[e], (uint32_t)welem_id(base, lane, e));
-        }
-        total += __popcll(bal);
+        const int pos = off + __popc(tm & ((1u << e) - 1u));
+        const bool w = ((tm >> e) & 1u) && pos < a.capc;
+        list[w ? pos : spare] = make_uint2(key[e], (uint32_t)welem_id(base, lane, e));
     }
-    if (total > a.capc) return false;                  // the workgroup path rewrites the slots
-    if (lane == 0) a.cand_meta[(size_t)r.slot * a.nchunk + c] = make_uint2((uint32_t)total, vk);
-    return true;
+    *total_out = __builtin_amdgcn_readlane(incl, 63);
+    *vk_out = vk;
+}
+
+typedef unsigned int vsa_u32x2 __attribute__((ext_vector_type(2)));
+// A (row, chunk)'s candidate slots and count from the wave's LDS list: kCandStores + 1
+// stores per lane whatever the row (`on` false or an overflow: every one past its
+// resource, dropped), so every row issues the same memory instructions.
+__device__ __forceinline__ void wave_cand_store(const SampArgs& a, size_t sc, int lane, bool on,
+                                                const uint2* list, int total, uint32_t vk) {
+    const bool fits = on && total <= a.capc;
+    const int nout = fits ? total : 0;
+    const __amdgpu_buffer_rsrc_t rs = handoff_rsrc(a.cand + sc * a.capc, on ? (uint32_t)a.capc * 8u : 0u);
+#pragma unroll
+    for (int s = 0; s < kCandStores; ++s) {
+        const int i = lane + 64 * s;
+        const uint2 v = list[i < a.capc ? i : 0];
+        vsa_u32x2 w;
+        w.x = v.x;
+        w.y = v.y;
+        __builtin_amdgcn_raw_buffer_store_b64(w, rs, i < nout ? (uint32_t)i * 8u : (uint32_t)a.capc * 8u,
+                                              0, 0);
+    }
+    vsa_u32x2 meta;
+    meta.x = (uint32_t)total;
+    meta.y = vk;
+    const __amdgpu_buffer_rsrc_t rm = handoff_rsrc(a.cand_meta + sc, on ? 8u : 0u);
+    __builtin_amdgcn_raw_buffer_store_b64(meta, rm, (lane == 0 && fits) ? 0u : 8u, 0, 0);
 }
 
 template <bool VEC, bool MAP>
 __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
-    __shared__ float4 s_part[3 * kMaxSeqRows][4];
+    __shared__ uint2 s_list[4][2][kCandCap + 64];   // + a spare slot per lane
     __shared__ int s_draft[kMaxSeqRows];
     __shared__ uint32_t s_hist[256];
-    __shared__ int s_nib[2][4][16];
     __shared__ int s_ovf[3 * kMaxSeqRows];
     __shared__ int s_novf;
     __shared__ int s_sh[4];
 
     preload_args(a);
-    // workgroup (b, c, s): chunk c of the rows q = s, s + S, ... of sequence b (S = rsplit)
+    // workgroup (b, c, s): chunk c of the data rows d = s, s + S, ... of sequence b
+    // (S = rsplit); the workgroup's n-th data row goes to wave n mod 4
     const int s_row = blockIdx.x % a.rsplit, bc = blockIdx.x / a.rsplit;
     const int b = bc / a.nchunk, c = bc % a.nchunk;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    // the counts go out with the sequence's geometry and parameters; the draft ids and the
-    // first batch of rows are requested together once those arrive
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: row pointers in SGPRs
     const int base = c * kChunk;
-    int cnt[kEpt];
-    load_counts<VEC>(a.counts ? a.counts + (size_t)b * a.vocab : nullptr, base, a.vocab, cnt);
     uint32_t ebits = 0;
     const SeqMode m = seq_mode(a, b, &ebits);
-    if (c == 0 && tid == 0 && ebits) atomicOr(a.err, ebits);
+    if (c == 0 && tid == 0 && s_row == 0 && ebits) atomicOr(a.err, ebits);
     if (!m.valid) return;
-    int dreg = 0;
+    const int nd = seq_ndraft(a, m);
+    const int ndata = m.rows + nd;                     // data rows: targets, then drafts
+    const int nloc = s_row < ndata ? (ndata - s_row + a.rsplit - 1) / a.rsplit : 0;
+    if (nloc == 0) return;
+    if (tid < m.k) s_draft[tid] = a.drafts[m.d0 + tid];
+    if (tid == 0) s_novf = 0;
+    const bool has_pen = m.pp != 0.f || m.fp != 0.f;
+    const bool cand_trunc = m.topk;                    // candidates over z / w
+    const bool cand_raw = m.raw && m.ntop > 0;         // candidates over raw x (top-n)
+    const int n_valid = min(kChunk, a.vocab - base);
     uint32_t valid = 0;
 #pragma unroll
-    for (int e = 0; e < kEpt; ++e) valid |= (elem_id(base, e) < a.vocab ? 1u : 0u) << e;
-    // penalty terms of the base counts, each rounded as in z = (x - fp c) - pp [c > 0]
-    const bool has_pen = m.pp != 0.f || m.fp != 0.f;
-    float fpc[kEpt], ppc[kEpt];
-#pragma unroll
-    for (int e = 0; e < kEpt; ++e) {
-        fpc[e] = __fmul_rn(m.fp, (float)cnt[e]);
-        ppc[e] = cnt[e] > 0 ? m.pp : 0.f;
-    }
-    uint32_t dm[kEpt];              // drafts equal to each id (see draft_masks)
-    uint32_t dmo = 0;               // their union
+    for (int e = 0; e < kWe; ++e) valid |= (welem_id(base, lane, e) < a.vocab ? 1u : 0u) << e;
 
-    const int nrows = seq_nrows(a, m);
-    const int nd = seq_ndraft(a, m);
-    // this workgroup's rows: list index q = s_row + rsplit j, j < nloc
-    const int nloc = s_row < nrows ? (nrows - s_row + a.rsplit - 1) / a.rsplit : 0;
-    if (nloc == 0) return;
-    const bool cand_any = m.topk || m.ntop > 0;
-    const int n_valid = min(kChunk, a.vocab - base);
-    if (tid == 0) s_novf = 0;
-    // ---- per-row statistics of this chunk (loads of kRowBatch rows in flight at once).
-    // Values: z (penalized target), w (draft) or x (raw); softmax statistics are taken as
-    // (max v, sum 2^((v - max) c)) with c = log2(e) / T, greedy target rows as argmax.
-    // Each phase runs over the batch's rows so that independent reductions interleave.
-    for (int j0 = 0; j0 < nloc; j0 += kRowBatch) {
-        float xv[kRowBatch][kEpt];
-#pragma unroll
-        for (int u = 0; u < kRowBatch; ++u)
-            // plain loads: truncated rows are read again by the candidate phase
-            if (j0 + u < nloc)
-                load_row_chunk<VEC, MAP, false>(a, m, row_ref(a, m, s_row + a.rsplit * (j0 + u)),
-                                                base, xv[u]);
-        if (j0 == 0) {
-            // the draft ids by scalar loads: no wait for this batch's rows
-            scalar_drafts(a, m, m.k, base, s_draft, dm, dreg);
-#pragma unroll
-            for (int e = 0; e < kEpt; ++e) dmo |= dm[e];
-        }
-        float rmax[kRowBatch];
-        int ridx[kRowBatch];
-        // phase 1: penalties, per-thread max / argmax
-#pragma unroll
-        for (int u = 0; u < kRowBatch; ++u) {
-            const int j = j0 + u;
-            if (j >= nloc) break;
-            const int q = s_row + a.rsplit * j;
-            const bool target = q < m.rows;
-            if (target && has_pen) {
-                const uint32_t lm = low_bits(q);
-                if (__ballot((dmo & lm) != 0u)) {
-                    // a draft of an earlier position is among this wave's ids
-#pragma unroll
-                    for (int e = 0; e < kEpt; ++e)
-                        xv[u][e] = penalize(xv[u][e], cnt[e] + __popc(dm[e] & lm), m.pp, m.fp);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < kEpt; ++e)
-                        xv[u][e] = __fsub_rn(__fsub_rn(xv[u][e], fpc[e]), ppc[e]);
-                }
-            }
-            float bv = kNegInf;
-            int bi = kBigIdx;
-            if (target && !m.sampled) {
-#pragma unroll
-                for (int e = 0; e < kEpt; ++e)
-                    if (((valid >> e) & 1u) && better(xv[u][e], elem_id(base, e), bv, bi)) {
-                        bv = xv[u][e];
-                        bi = elem_id(base, e);
-                    }
-            } else {
-#pragma unroll
-                for (int e = 0; e < kEpt; ++e) bv = fmaxf(bv, xv[u][e]);
-            }
-            rmax[u] = bv;
-            ridx[u] = bi;
-        }
-        // phase 2: wave maxima
-#pragma unroll
-        for (int u = 0; u < kRowBatch; ++u) {
-            const int j = j0 + u;
-            if (j >= nloc) break;
-            const int q = s_row + a.rsplit * j;
-            if (q < m.rows && !m.sampled) wave_argmax(rmax[u], ridx[u]);
-            else rmax[u] = wave_max(rmax[u]);
-        }
-        // phase 3: sums of exp2 ((v - max) c) (arguments <= 0: the hardware exp2 is exact
-        // enough, and terms below 2^-126 add nothing), wave sums, partials to LDS
-#pragma unroll
-        for (int u = 0; u < kRowBatch; ++u) {
-            const int j = j0 + u;
-            if (j >= nloc) break;
-            const int q = s_row + a.rsplit * j;
-            float4 res;
-            if (q < m.rows && !m.sampled) {
-                res = make_float4(0.f, 0.f, rmax[u], __int_as_float(ridx[u]));
-            } else {
-                const float cs = q >= m.rows + nd ? kLog2e : kLog2e / m.temp;
-                const float mx = rmax[u];
-                float sm = 0.f;
-                if (mx != kNegInf) {
-#pragma unroll
-                    for (int e = 0; e < kEpt; ++e)
-                        sm += __builtin_amdgcn_exp2f((xv[u][e] - mx) * cs);
-                }
-                res = make_float4(mx, wave_sum(sm), 0.f, 0.f);
-            }
-            if (lane == 0) s_part[j][wave] = res;
-        }
+    // this wave's rows: u = wave, wave + 4, ... (data row s_row + rsplit u); the base counts
+    // (when penalties apply) and the first row are requested together
+    uint32_t cnt[kWe];
+    {
+        const bool pc = has_pen && a.counts != nullptr;
+        wbuf_load<VEC>(handoff_rsrc(pc ? (const void*)(a.counts + (size_t)b * a.vocab)
+                                       : (const void*)a.tl,
+                                    pc ? (uint32_t)a.vocab * 4u : 0u),
+                       base, lane, cnt);
     }
-    __syncthreads();
-    for (int j = tid; j < nloc; j += kThreads) {
-        const RowRef r = row_ref(a, m, s_row + a.rsplit * j);
-        const bool greedy_row = r.kind == 0 && !m.sampled;
-        float4 acc = s_part[j][0];
-        if (greedy_row) {
-            for (int w = 1; w < 4; ++w) {
-                const float4 o = s_part[j][w];
-                if (better(o.z, __float_as_int(o.w), acc.z, __float_as_int(acc.w))) {
-                    acc.z = o.z;
-                    acc.w = o.w;
-                }
+    float xa[kWe];
+    int u = wave;
+    wload_data<VEC, MAP>(a, m, s_row + a.rsplit * u, u < nloc, base, lane, valid, xa);
+    __syncthreads();                                   // s_draft, s_novf
+    for (; u < nloc; u += 4) {
+        float xb[kWe];
+        wload_data<VEC, MAP>(a, m, s_row + a.rsplit * (u + 4), u + 4 < nloc, base, lane, valid, xb);
+        const int d = s_row + a.rsplit * u;
+        const bool target = d < m.rows;
+        const RowRef r = row_ref(a, m, d);
+        float v[kWe];
+        if (target && has_pen) {
+            // z = (x - fp c) - pp [c > 0], c the base count plus the drafts d_1 .. d_i
+            int cc[kWe];
+#pragma unroll
+            for (int e = 0; e < kWe; ++e) cc[e] = (int)cnt[e];
+            for (int t = 0; t < d; ++t) {
+                const int off = s_draft[t] - base;
+                if (off < 0 || off >= kChunk || ((off >> 2) & 63) != lane) continue;
+                const int ee = 4 * (off >> 8) + (off & 3);
+#pragma unroll
+                for (int e = 0; e < kWe; ++e) cc[e] += e == ee ? 1 : 0;
             }
+#pragma unroll
+            for (int e = 0; e < kWe; ++e) v[e] = penalize(xa[e], cc[e], m.pp, m.fp);
         } else {
-            const float cs = r.kind == 2 ? kLog2e : kLog2e / m.temp;
-            float mx = acc.x;
-            for (int w = 1; w < 4; ++w) mx = fmaxf(mx, s_part[j][w].x);
-            float sm = 0.f;
-            if (mx != kNegInf)
-                for (int w = 0; w < 4; ++w)
-                    if (s_part[j][w].x != kNegInf)
-                        sm += s_part[j][w].y * exp2f((s_part[j][w].x - mx) * cs);
-            acc.x = mx;
-            acc.y = sm;
+#pragma unroll
+            for (int e = 0; e < kWe; ++e) v[e] = xa[e];
         }
-        a.stats[(size_t)r.slot * a.nchunk + c] = acc;   // read by later kernels
+        // this row's outputs: the statistics of r and of its raw twin, candidate lists
+        const bool twin = target && m.raw;
+        const float4 st_r = wave_row_stats(base, lane, valid, target && !m.sampled, kLog2e / m.temp, v);
+        float4 st_x = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (twin) st_x = wave_row_stats(base, lane, valid, false, kLog2e, xa);
+        int tot0 = 0, tot1 = 0;
+        uint32_t vk0 = 0u, vk1 = 0u;
+        if (cand_trunc) {
+            uint32_t key[kWe];
+#pragma unroll
+            for (int e = 0; e < kWe; ++e) key[e] = ((valid >> e) & 1u) ? ord_key(v[e]) : 0u;
+            wave_candidates(a, base, lane, m.topk_k, n_valid, valid, key, s_list[wave][0], &tot0, &vk0);
+        }
+        if (twin && cand_raw) {
+            uint32_t key[kWe];
+#pragma unroll
+            for (int e = 0; e < kWe; ++e) key[e] = ((valid >> e) & 1u) ? ord_key(xa[e]) : 0u;
+            wave_candidates(a, base, lane, m.ntop, n_valid, valid, key, s_list[wave][1], &tot1, &vk1);
+        }
+        wave_sync();
+        // the stores: the same instructions for every row (those not wanted fall past
+        // zero-byte resources)
+        const RowRef rx = row_ref(a, m, ndata + d);    // the raw twin (when there is one)
+        handoff_store16(handoff_rsrc(a.stats + (size_t)r.slot * a.nchunk + c, 16u),
+                        lane == 0 ? 0u : 16u, st_r);
+        handoff_store16(handoff_rsrc(a.stats + (size_t)rx.slot * a.nchunk + c, twin ? 16u : 0u),
+                        lane == 0 ? 0u : 16u, st_x);
+        wave_cand_store(a, (size_t)r.slot * a.nchunk + c, lane, cand_trunc, s_list[wave][0], tot0, vk0);
+        wave_cand_store(a, (size_t)rx.slot * a.nchunk + c, lane, twin && cand_raw, s_list[wave][1],
+                        tot1, vk1);
+        wave_sync();                                   // the lists are reused by the next row
+        if (lane == 0) {
+            if (cand_trunc && tot0 > a.capc) s_ovf[atomicAdd(&s_novf, 1)] = d;
+            if (twin && cand_raw && tot1 > a.capc) s_ovf[atomicAdd(&s_novf, 1)] = ndata + d;
+        }
+#pragma unroll
+        for (int e = 0; e < kWe; ++e) xa[e] = xb[e];
     }
 
-    // ---- candidates for the k-th-largest threshold of truncated / top-n rows: row number
-    // n of those goes to wave n mod 4; a row whose candidates overflow the slots is listed
-    // and redone by the whole workgroup with the exact kk-th key.
-    if (cand_any) {
-        auto cand_kk = [&](int q) {
-            if (q % a.rsplit != s_row) return 0;
-            const RowRef r = row_ref(a, m, q);
-            const bool trunc = m.topk && r.kind != 2, topn = r.kind == 2 && m.ntop > 0;
-            return trunc ? m.topk_k : topn ? m.ntop : 0;
-        };
-        // the first row of this wave at or after row q (nrows when none)
-        auto next_row = [&](int q, int idx) {
-            for (; q < nrows; ++q)
-                if (cand_kk(q) > 0) {
-                    if ((idx & 3) == wave) break;
-                    ++idx;
-                }
-            return q;
-        };
-        // idx counts the candidate rows before q, so the n-th goes to wave n mod 4
-        auto rows_before = [&](int q) {
-            int n = 0;
-            for (int i = 0; i < q; ++i) n += cand_kk(i) > 0 ? 1 : 0;
-            return n;
-        };
-        int q = next_row(0, 0);
-        float xa[kWe];
-        int ca[kWe];
-        if (q < nrows) wload_row<VEC, MAP>(a, m, row_ref(a, m, q), b, base, lane, xa, ca);
-        while (q < nrows) {
-            const int qn = next_row(q + 1, rows_before(q + 1));
-            float xb[kWe];
-            int cb[kWe];
-            if (qn < nrows) wload_row<VEC, MAP>(a, m, row_ref(a, m, qn), b, base, lane, xb, cb);
-            if (!wave_row_candidates(a, m, row_ref(a, m, q), c, base, s_draft, cand_kk(q), xa,
-                                     ca) &&
-                lane == 0)
-                s_ovf[atomicAdd(&s_novf, 1)] = q;
+    // ---- rows whose candidates overflowed the slots: the whole workgroup, with the exact
+    // kk-th key (radix select); every key above it and the ties at it up to capc slots are
+    // written (the count says how many there were)
+    __syncthreads();
+    const int novf = s_novf;
+    if (novf == 0) return;
+    int cnt_t[kEpt];
+    load_counts<VEC>(a.counts ? a.counts + (size_t)b * a.vocab : nullptr, base, a.vocab, cnt_t);
+    uint32_t dm[kEpt];
+    draft_masks(s_draft, m.k, base, dm);
+    uint32_t valid_t = 0;
 #pragma unroll
-            for (int e = 0; e < kWe; ++e) {
-                xa[e] = xb[e];
-                ca[e] = cb[e];
-            }
-            q = qn;
+    for (int e = 0; e < kEpt; ++e) valid_t |= (elem_id(base, e) < a.vocab ? 1u : 0u) << e;
+    for (int o = 0; o < novf; ++o) {
+        const int q = s_ovf[o];
+        const RowRef r = row_ref(a, m, q);
+        const int kk = r.kind != 2 ? m.topk_k : m.ntop;
+        float x[kEpt];
+        load_row_chunk<VEC, MAP>(a, m, r, base, x);
+        uint32_t key[kEpt];
+#pragma unroll
+        for (int e = 0; e < kEpt; ++e) {
+            float val = x[e];
+            if (r.kind == 0)
+                val = penalize(val, cnt_t[e] + __popc(dm[e] & low_bits(r.i)), m.pp, m.fp);
+            key[e] = ord_key(val);
         }
+        uint2* out = a.cand + ((size_t)r.slot * a.nchunk + c) * a.capc;
+        const uint32_t vk = wg_select_kth(key, valid_t, kk, s_hist, s_sh);
+        if (tid == 0) s_sh[2] = 0;
         __syncthreads();
-        const int novf = s_novf;
-        for (int o = 0; o < novf; ++o) {
-            const int q = s_ovf[o];
-            const RowRef r = row_ref(a, m, q);
-            const bool trunc = m.topk && r.kind != 2;
-            const int kk = trunc ? m.topk_k : m.ntop;
-            float x[kEpt];
-            load_row_chunk<VEC, MAP>(a, m, r, base, x);
-            uint32_t key[kEpt];
 #pragma unroll
-            for (int e = 0; e < kEpt; ++e) {
-                float val = x[e];
-                if (r.kind == 0)
-                    val = penalize(val, cnt[e] + __popc(dm[e] & low_bits(r.i)), m.pp, m.fp);
-                key[e] = ord_key(val);
+        for (int e = 0; e < kEpt; ++e)
+            if (((valid_t >> e) & 1u) && key[e] > vk) {
+                const int pos = atomicAdd(&s_sh[2], 1);
+                out[pos] = make_uint2(key[e], (uint32_t)elem_id(base, e));
             }
-            uint2* out = a.cand + ((size_t)r.slot * a.nchunk + c) * a.capc;
-            // vk is the exact kk-th key (radix select); every key above it and the ties at
-            // it up to capc slots are written (the count says how many there were).
-            const uint32_t vk = wg_select_kth(key, valid, kk, s_hist, s_sh);
-            if (tid == 0) s_sh[2] = 0;
-            __syncthreads();
+        __syncthreads();
 #pragma unroll
-            for (int e = 0; e < kEpt; ++e)
-                if (((valid >> e) & 1u) && key[e] > vk) {
-                    const int pos = atomicAdd(&s_sh[2], 1);
+        for (int e = 0; e < kEpt; ++e)
+            if (((valid_t >> e) & 1u) && key[e] == vk) {
+                const int pos = atomicAdd(&s_sh[2], 1);
+                if (pos < a.capc)
                     out[pos] = make_uint2(key[e], (uint32_t)elem_id(base, e));
-                }
-            __syncthreads();
-#pragma unroll
-            for (int e = 0; e < kEpt; ++e)
-                if (((valid >> e) & 1u) && key[e] == vk) {
-                    const int pos = atomicAdd(&s_sh[2], 1);
-                    if (pos < a.capc)
-                        out[pos] = make_uint2(key[e], (uint32_t)elem_id(base, e));
-                }
-            __syncthreads();
-            const int ncand = s_sh[2];
-            if (tid == 0)
-                a.cand_meta[(size_t)r.slot * a.nchunk + c] = make_uint2((uint32_t)ncand, vk);
-            __syncthreads();
-        }
+            }
+        __syncthreads();
+        const int ncand = s_sh[2];
+        if (tid == 0)
+            a.cand_meta[(size_t)r.slot * a.nchunk + c] = make_uint2((uint32_t)ncand, vk);
+        __syncthreads();
     }
 }
 
@@ -1504,7 +1467,7 @@ __device__ __forceinline__ int wave_scan_i(int v) {
 // and stores in ns the first position whose running mass reaches `target`, the running
 // mass before it (base included) and the ids of this histogram before it; when none does
 // (rounding at the very end), the last non-empty position.
-__device__ void nuc_crossing(NucShared& ns, int nb, bool rev, double base, double target) {
+__device__ __forceinline__ void nuc_crossing(NucShared& ns, int nb, bool rev, double base, double target) {
     const int lane = threadIdx.x & 63;
     const int per = nb / 64;
     double ms = 0.0;
@@ -1558,7 +1521,7 @@ __device__ void nuc_crossing(NucShared& ns, int nb, bool rev, double base, doubl
 // vocabulary skipped; the interval spares the mass for ids that cannot matter).
 // Target rows carry their penalties (base counts plus the drafts before the row).
 template <bool VEC, bool MAP, class F>
-__device__ void nuc_pass(const SampArgs& a, const SeqMode& m, const RowRef& r, int b,
+__device__ __forceinline__ void nuc_pass(const SampArgs& a, const SeqMode& m, const RowRef& r, int b,
                          const int* drafts, float vlo, float vhi, F&& f) {
     constexpr int kB = 4;                           // chunks whose loads are in flight together
     const bool pen = r.kind == 0 && (m.pp != 0.f || m.fp != 0.f);
@@ -1597,7 +1560,7 @@ struct NucRun {
     int cur = -1;
     double acc = 0.0;
     int n = 0;
-    __device__ void add(NucShared& ns, int k, double w) {
+    __device__ __forceinline__ void add(NucShared& ns, int k, double w) {
         if (k != cur) {
             flush(ns);
             cur = k;
@@ -1605,7 +1568,7 @@ struct NucRun {
         acc += w;
         ++n;
     }
-    __device__ void flush(NucShared& ns) {
+    __device__ __forceinline__ void flush(NucShared& ns) {
         if (cur >= 0) {
             atomicAdd(&ns.hm[cur], acc);
             atomicAdd(&ns.hn[cur], n);
@@ -1619,7 +1582,7 @@ struct NucRun {
 // Nucleus row q of sequence b (target or draft row of a sampled sequence with top_p < 1
 // and no top-k): y*, its kept mass and count to the row's workspace RowInfo.
 template <bool VEC, bool MAP>
-__device__ void nucleus_row(const SampArgs& a, const SeqMode& m, int b, int q, NucShared& ns) {
+__device__ __forceinline__ void nucleus_row(const SampArgs& a, const SeqMode& m, int b, int q, NucShared& ns) {
     const int tid = threadIdx.x, wave = tid >> 6;
     const RowRef r = row_ref(a, m, q);
     if (tid < m.k) ns.drafts[tid] = a.drafts[m.d0 + tid];
