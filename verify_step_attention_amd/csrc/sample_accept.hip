@@ -1065,7 +1065,6 @@ __global__ __launch_bounds__(kThreads) void race_kernel(const SampArgs a) {
 // row's work (a conditional load or store before a use makes it wait for all of them).
 constexpr int kWj = kChunk / 256;                 // float4s per lane
 constexpr int kWe = 4 * kWj;                      // ids per lane
-constexpr int kNtPolicy = 2;                      // cache policy of streamed rows: nt
 // candidate slots of a (row, chunk): capc <= max(top-k bound kKeep, top-logprobs bound 32)
 // + 32, so kCandStores stores per lane write any of them
 constexpr int kCandCap = kKeep + 32;
@@ -1092,7 +1091,7 @@ __device__ __forceinline__ void wbuf_load(__amdgpu_buffer_rsrc_t rs, int base, i
 #pragma unroll
         for (int j = 0; j < kWj; ++j) {
             const vsa_u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(
-                rs, (uint32_t)(base + 4 * (lane + 64 * j)) * 4u, 0, kNtPolicy);
+                rs, (uint32_t)(base + 4 * (lane + 64 * j)) * 4u, 0, 0);
             x[4 * j] = v.x;
             x[4 * j + 1] = v.y;
             x[4 * j + 2] = v.z;
@@ -1102,18 +1101,19 @@ __device__ __forceinline__ void wbuf_load(__amdgpu_buffer_rsrc_t rs, int base, i
 #pragma unroll
         for (int e = 0; e < kWe; ++e)
             x[e] = __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)welem_id(base, lane, e) * 4u,
-                                                        0, kNtPolicy);
+                                                        0, 0);
     }
 }
-// Data row d of the sequence (target row d < R, else draft row d - R + 1) at the chunk's
-// ids, -inf past the vocabulary (draft rows through t2d when MAP). `present` false: no
+// Row q of the sequence's row list at the chunk's ids (a raw row reads its target row's
+// logits; draft rows through t2d when MAP), -inf past the vocabulary. `present` false: no
 // row (the loads cover 0 bytes).
 template <bool VEC, bool MAP>
-__device__ __forceinline__ void wload_data(const SampArgs& a, const SeqMode& m, int d, bool present,
-                                           int base, int lane, uint32_t valid, float (&x)[kWe]) {
+__device__ __forceinline__ void wload_row(const SampArgs& a, const SeqMode& m, int q, bool present,
+                                          int base, int lane, uint32_t valid, float (&x)[kWe]) {
     uint32_t u[kWe];
-    if (MAP && d >= m.rows) {
-        const float* row = a.dl + (size_t)(m.d0 + d - m.rows) * a.dvocab;
+    const RowRef r = row_ref(a, m, q);
+    if (MAP && r.kind == 1) {
+        const float* row = a.dl + (size_t)(m.d0 + r.i - 1) * a.dvocab;
         wbuf_load<VEC>(handoff_rsrc(a.t2d, present ? (uint32_t)a.vocab * 4u : 0u), base, lane, u);
         const __amdgpu_buffer_rsrc_t rr = handoff_rsrc(row, present ? (uint32_t)a.dvocab * 4u : 0u);
         uint32_t ebits = 0;
@@ -1122,15 +1122,15 @@ __device__ __forceinline__ void wload_data(const SampArgs& a, const SeqMode& m, 
             const int mp = ((valid >> e) & 1u) ? (int)u[e] : -1;
             // an entry outside [0, dvocab) reads past the resource: 0, replaced by -inf
             const float v = __uint_as_float(
-                __builtin_amdgcn_raw_buffer_load_b32(rr, (uint32_t)mp * 4u, 0, kNtPolicy));
+                __builtin_amdgcn_raw_buffer_load_b32(rr, (uint32_t)mp * 4u, 0, 0));
             x[e] = (uint32_t)mp < (uint32_t)a.dvocab ? v : kNegInf;
             ebits |= (mp < -1 || mp >= a.dvocab) ? VSA_DEVERR_DRAFT_MAP : 0u;
         }
         if (__ballot(ebits != 0u) && lane == 0) atomicOr(a.err, VSA_DEVERR_DRAFT_MAP);
         return;
     }
-    const float* row = d < m.rows ? a.tl + (size_t)(m.r0 + d) * a.vocab
-                                  : a.dl + (size_t)(m.d0 + d - m.rows) * a.vocab;
+    const float* row = r.kind == 1 ? a.dl + (size_t)(m.d0 + r.i - 1) * a.vocab
+                                   : a.tl + (size_t)(m.r0 + r.i) * a.vocab;
     wbuf_load<VEC>(handoff_rsrc(row, present ? (uint32_t)a.vocab * 4u : 0u), base, lane, u);
 #pragma unroll
     for (int e = 0; e < kWe; ++e) x[e] = ((valid >> e) & 1u) ? __uint_as_float(u[e]) : kNegInf;
@@ -1254,7 +1254,7 @@ __device__ __forceinline__ void wave_cand_store(const SampArgs& a, size_t sc, in
 
 template <bool VEC, bool MAP>
 __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
-    __shared__ uint2 s_list[4][2][kCandCap + 64];   // + a spare slot per lane
+    __shared__ uint2 s_list[4][kCandCap + 64];      // + a spare slot per lane
     __shared__ int s_draft[kMaxSeqRows];
     __shared__ uint32_t s_hist[256];
     __shared__ int s_ovf[3 * kMaxSeqRows];
@@ -1262,8 +1262,9 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
     __shared__ int s_sh[4];
 
     preload_args(a);
-    // workgroup (b, c, s): chunk c of the data rows d = s, s + S, ... of sequence b
-    // (S = rsplit); the workgroup's n-th data row goes to wave n mod 4
+    // workgroup (b, c, s): chunk c of the rows q = s, s + S, ... of sequence b's row list
+    // (S = rsplit; targets, drafts, then raw rows); the workgroup's n-th row goes to wave
+    // n mod 4
     const int s_row = blockIdx.x % a.rsplit, bc = blockIdx.x / a.rsplit;
     const int b = bc / a.nchunk, c = bc % a.nchunk;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -1273,22 +1274,19 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
     const SeqMode m = seq_mode(a, b, &ebits);
     if (c == 0 && tid == 0 && s_row == 0 && ebits) atomicOr(a.err, ebits);
     if (!m.valid) return;
-    const int nd = seq_ndraft(a, m);
-    const int ndata = m.rows + nd;                     // data rows: targets, then drafts
-    const int nloc = s_row < ndata ? (ndata - s_row + a.rsplit - 1) / a.rsplit : 0;
+    const int nrows = seq_nrows(a, m);
+    const int nloc = s_row < nrows ? (nrows - s_row + a.rsplit - 1) / a.rsplit : 0;
     if (nloc == 0) return;
     if (tid < m.k) s_draft[tid] = a.drafts[m.d0 + tid];
     if (tid == 0) s_novf = 0;
     const bool has_pen = m.pp != 0.f || m.fp != 0.f;
-    const bool cand_trunc = m.topk;                    // candidates over z / w
-    const bool cand_raw = m.raw && m.ntop > 0;         // candidates over raw x (top-n)
     const int n_valid = min(kChunk, a.vocab - base);
     uint32_t valid = 0;
 #pragma unroll
     for (int e = 0; e < kWe; ++e) valid |= (welem_id(base, lane, e) < a.vocab ? 1u : 0u) << e;
 
-    // this wave's rows: u = wave, wave + 4, ... (data row s_row + rsplit u); the base counts
-    // (when penalties apply) and the first row are requested together
+    // this wave's rows: u = wave, wave + 4, ... (row s_row + rsplit u); the base counts (when
+    // penalties apply) and the first row are requested together
     uint32_t cnt[kWe];
     {
         const bool pc = has_pen && a.counts != nullptr;
@@ -1299,21 +1297,19 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
     }
     float xa[kWe];
     int u = wave;
-    wload_data<VEC, MAP>(a, m, s_row + a.rsplit * u, u < nloc, base, lane, valid, xa);
+    wload_row<VEC, MAP>(a, m, s_row + a.rsplit * u, u < nloc, base, lane, valid, xa);
     __syncthreads();                                   // s_draft, s_novf
     for (; u < nloc; u += 4) {
         float xb[kWe];
-        wload_data<VEC, MAP>(a, m, s_row + a.rsplit * (u + 4), u + 4 < nloc, base, lane, valid, xb);
-        const int d = s_row + a.rsplit * u;
-        const bool target = d < m.rows;
-        const RowRef r = row_ref(a, m, d);
-        float v[kWe];
-        if (target && has_pen) {
+        wload_row<VEC, MAP>(a, m, s_row + a.rsplit * (u + 4), u + 4 < nloc, base, lane, valid, xb);
+        const int q = s_row + a.rsplit * u;
+        const RowRef r = row_ref(a, m, q);
+        if (r.kind == 0 && has_pen) {
             // z = (x - fp c) - pp [c > 0], c the base count plus the drafts d_1 .. d_i
             int cc[kWe];
 #pragma unroll
             for (int e = 0; e < kWe; ++e) cc[e] = (int)cnt[e];
-            for (int t = 0; t < d; ++t) {
+            for (int t = 0; t < r.i; ++t) {
                 const int off = s_draft[t] - base;
                 if (off < 0 || off >= kChunk || ((off >> 2) & 63) != lane) continue;
                 const int ee = 4 * (off >> 8) + (off & 3);
@@ -1321,46 +1317,29 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
                 for (int e = 0; e < kWe; ++e) cc[e] += e == ee ? 1 : 0;
             }
 #pragma unroll
-            for (int e = 0; e < kWe; ++e) v[e] = penalize(xa[e], cc[e], m.pp, m.fp);
-        } else {
-#pragma unroll
-            for (int e = 0; e < kWe; ++e) v[e] = xa[e];
+            for (int e = 0; e < kWe; ++e) xa[e] = penalize(xa[e], cc[e], m.pp, m.fp);
         }
-        // this row's outputs: the statistics of r and of its raw twin, candidate lists
-        const bool twin = target && m.raw;
-        const float4 st_r = wave_row_stats(base, lane, valid, target && !m.sampled, kLog2e / m.temp, v);
-        float4 st_x = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (twin) st_x = wave_row_stats(base, lane, valid, false, kLog2e, xa);
-        int tot0 = 0, tot1 = 0;
-        uint32_t vk0 = 0u, vk1 = 0u;
-        if (cand_trunc) {
-            uint32_t key[kWe];
-#pragma unroll
-            for (int e = 0; e < kWe; ++e) key[e] = ((valid >> e) & 1u) ? ord_key(v[e]) : 0u;
-            wave_candidates(a, base, lane, m.topk_k, n_valid, valid, key, s_list[wave][0], &tot0, &vk0);
-        }
-        if (twin && cand_raw) {
+        // this row's outputs: its statistics and, for a truncated or top-n row, candidates
+        const float cs = r.kind == 2 ? kLog2e : kLog2e / m.temp;
+        const float4 st = wave_row_stats(base, lane, valid, r.kind == 0 && !m.sampled, cs, xa);
+        const bool cand = r.kind == 2 ? m.ntop > 0 : m.topk;
+        int tot = 0;
+        uint32_t vk = 0u;
+        if (cand) {
             uint32_t key[kWe];
 #pragma unroll
             for (int e = 0; e < kWe; ++e) key[e] = ((valid >> e) & 1u) ? ord_key(xa[e]) : 0u;
-            wave_candidates(a, base, lane, m.ntop, n_valid, valid, key, s_list[wave][1], &tot1, &vk1);
+            wave_candidates(a, base, lane, r.kind == 2 ? m.ntop : m.topk_k, n_valid, valid, key,
+                            s_list[wave], &tot, &vk);
         }
         wave_sync();
         // the stores: the same instructions for every row (those not wanted fall past
         // zero-byte resources)
-        const RowRef rx = row_ref(a, m, ndata + d);    // the raw twin (when there is one)
-        handoff_store16(handoff_rsrc(a.stats + (size_t)r.slot * a.nchunk + c, 16u),
-                        lane == 0 ? 0u : 16u, st_r);
-        handoff_store16(handoff_rsrc(a.stats + (size_t)rx.slot * a.nchunk + c, twin ? 16u : 0u),
-                        lane == 0 ? 0u : 16u, st_x);
-        wave_cand_store(a, (size_t)r.slot * a.nchunk + c, lane, cand_trunc, s_list[wave][0], tot0, vk0);
-        wave_cand_store(a, (size_t)rx.slot * a.nchunk + c, lane, twin && cand_raw, s_list[wave][1],
-                        tot1, vk1);
-        wave_sync();                                   // the lists are reused by the next row
-        if (lane == 0) {
-            if (cand_trunc && tot0 > a.capc) s_ovf[atomicAdd(&s_novf, 1)] = d;
-            if (twin && cand_raw && tot1 > a.capc) s_ovf[atomicAdd(&s_novf, 1)] = ndata + d;
-        }
+        const size_t sc = (size_t)r.slot * a.nchunk + c;
+        handoff_store16(handoff_rsrc(a.stats + sc, 16u), lane == 0 ? 0u : 16u, st);
+        wave_cand_store(a, sc, lane, cand, s_list[wave], tot, vk);
+        wave_sync();                                   // the list is reused by the next row
+        if (lane == 0 && cand && tot > a.capc) s_ovf[atomicAdd(&s_novf, 1)] = q;
 #pragma unroll
         for (int e = 0; e < kWe; ++e) xa[e] = xb[e];
     }
