@@ -1098,10 +1098,12 @@ __device__ __forceinline__ void wbuf_load(__amdgpu_buffer_rsrc_t rs, int base, i
             x[4 * j + 3] = v.w;
         }
     } else {
+        uint32_t o0 = (uint32_t)(base + 4 * lane) * 4u;
+        asm volatile("" : "+v"(o0));                   // offsets from here: not 32 hoisted registers
 #pragma unroll
         for (int e = 0; e < kWe; ++e)
-            x[e] = __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)welem_id(base, lane, e) * 4u,
-                                                        0, 0);
+            x[e] = __builtin_amdgcn_raw_buffer_load_b32(
+                rs, o0 + (uint32_t)(256 * (e >> 2) + (e & 3)) * 4u, 0, 0);
     }
 }
 // Row q of the sequence's row list at the chunk's ids (a raw row reads its target row's
@@ -1144,9 +1146,11 @@ __device__ __forceinline__ float4 wave_row_stats(int base, int lane, uint32_t va
     if (greedy) {
         float bv = kNegInf;
         int bi = kBigIdx;
+        int b0 = base + 4 * lane;
+        asm volatile("" : "+v"(b0));                   // ids from here: not 32 hoisted registers
 #pragma unroll
         for (int e = 0; e < kWe; ++e) {
-            const int id = welem_id(base, lane, e);
+            const int id = b0 + 256 * (e >> 2) + (e & 3);
             const bool t = ((valid >> e) & 1u) && better(v[e], id, bv, bi);
             bv = t ? v[e] : bv;
             bi = t ? id : bi;
@@ -1216,11 +1220,13 @@ __device__ __forceinline__ void wave_candidates(const SampArgs& a, int base, int
     // every element is written, a candidate to its slot and any other to the lane's spare
     // slot past the list, so the writes take no branch
     const int spare = kCandCap + lane;
+    int b0 = base + 4 * lane;
+    asm volatile("" : "+v"(b0));                       // ids from here: not 32 hoisted registers
 #pragma unroll
     for (int e = 0; e < kWe; ++e) {
         const int pos = off + __popc(tm & ((1u << e) - 1u));
         const bool w = ((tm >> e) & 1u) && pos < a.capc;
-        list[w ? pos : spare] = make_uint2(key[e], (uint32_t)welem_id(base, lane, e));
+        list[w ? pos : spare] = make_uint2(key[e], (uint32_t)(b0 + 256 * (e >> 2) + (e & 3)));
     }
     *total_out = __builtin_amdgcn_readlane(incl, 63);
     *vk_out = vk;
@@ -1253,7 +1259,7 @@ __device__ __forceinline__ void wave_cand_store(const SampArgs& a, size_t sc, in
 }
 
 template <bool VEC, bool MAP>
-__global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
+__global__ __launch_bounds__(kThreads, 3) void sweep_kernel(const SampArgs a) {
     __shared__ uint2 s_list[4][kCandCap + 64];      // + a spare slot per lane
     __shared__ int s_draft[kMaxSeqRows];
     __shared__ uint32_t s_hist[256];
@@ -1299,6 +1305,9 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
     int u = wave;
     wload_row<VEC, MAP>(a, m, s_row + a.rsplit * u, u < nloc, base, lane, valid, xa);
     __syncthreads();                                   // s_draft, s_novf
+    // the wave's target rows come in increasing order, so cnt accumulates the drafts d_1 ..
+    // d_i of each in place (`applied` of them so far)
+    int applied = 0;
     for (; u < nloc; u += 4) {
         float xb[kWe];
         wload_row<VEC, MAP>(a, m, s_row + a.rsplit * (u + 4), u + 4 < nloc, base, lane, valid, xb);
@@ -1306,18 +1315,16 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(const SampArgs a) {
         const RowRef r = row_ref(a, m, q);
         if (r.kind == 0 && has_pen) {
             // z = (x - fp c) - pp [c > 0], c the base count plus the drafts d_1 .. d_i
-            int cc[kWe];
-#pragma unroll
-            for (int e = 0; e < kWe; ++e) cc[e] = (int)cnt[e];
-            for (int t = 0; t < r.i; ++t) {
-                const int off = s_draft[t] - base;
-                if (off < 0 || off >= kChunk || ((off >> 2) & 63) != lane) continue;
+            for (; applied < r.i; ++applied) {
+                const int off = __builtin_amdgcn_readfirstlane(s_draft[applied]) - base;
+                if (off < 0 || off >= kChunk) continue;             // not in this chunk
                 const int ee = 4 * (off >> 8) + (off & 3);
+                const bool mine = ((off >> 2) & 63) == lane;
 #pragma unroll
-                for (int e = 0; e < kWe; ++e) cc[e] += e == ee ? 1 : 0;
+                for (int e = 0; e < kWe; ++e) cnt[e] += (mine && e == ee) ? 1u : 0u;
             }
 #pragma unroll
-            for (int e = 0; e < kWe; ++e) xa[e] = penalize(xa[e], cc[e], m.pp, m.fp);
+            for (int e = 0; e < kWe; ++e) xa[e] = penalize(xa[e], (int)cnt[e], m.pp, m.fp);
         }
         // this row's outputs: its statistics and, for a truncated or top-n row, candidates
         const float cs = r.kind == 2 ? kLog2e : kLog2e / m.temp;
