@@ -10,13 +10,13 @@
 // --mode lookup).
 //
 // Kernels, in stream order (each reads what the previous ones wrote):
-//   sweep_kernel     grid (B x chunks of 2048 ids). One workgroup reads one chunk of every
-//                    row of one sequence with coalesced loads: the count histogram once, then
-//                    each target row (penalized z), draft row and raw row. Per (row, chunk)
-//                    it writes max / sum-of-exp / argmax, and for truncated and top-n rows
-//                    the chunk's candidates for the k-th-largest threshold (keys at or above
-//                    a cheap bound on the chunk's k-th largest, or the exact k-th key from a
-//                    radix select).
+//   sweep_kernel     grid (B x chunks of 2048 ids x row splits). Each wave of a workgroup
+//                    takes whole rows of one sequence's row list (target rows as penalized z,
+//                    draft rows, raw rows) over one chunk: per (row, chunk) max /
+//                    sum-of-exp / argmax, and for truncated and top-n rows the chunk's
+//                    candidates for the k-th-largest threshold (keys at or above a cheap
+//                    bound on the chunk's k-th largest, or, when they overflow their slots,
+//                    the exact k-th key from a workgroup radix select).
 //   select_kernel    one workgroup per truncated or top-n row: the row's threshold and kept
 //                    list (sort of the few candidates above a bound on the row's k-th
 //                    largest), its nucleus, or the raw top-n logprobs; a nucleus without
