@@ -398,6 +398,11 @@ vsa_status sample_call(const float* target_logits, const float* draft_logits, in
     a.keep = reinterpret_cast<KeepEntry*>(ws + plan.off_keep);
     a.race = reinterpret_cast<RaceReq*>(ws + plan.off_race);
     a.race_part = reinterpret_cast<float4*>(ws + plan.off_race_part);
+    if (max_top_k > 0) {
+        a.nuc_hm = reinterpret_cast<double*>(ws + plan.off_nuc_hm);
+        a.nuc_hn = reinterpret_cast<uint32_t*>(ws + plan.off_nuc_hn);
+        a.nuc_info = reinterpret_cast<NucInfo*>(ws + plan.off_nuc_info);
+    }
     if (plan.n_ctr_x &&
         launch_zero_u32(a.ctr_x, plan.n_ctr_x, static_cast<hipStream_t>(stream)) != hipSuccess)
         return VSA_ERR_LAUNCH;

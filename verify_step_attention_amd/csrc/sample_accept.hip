@@ -310,7 +310,7 @@ __device__ uint32_t wg_select_slots(const uint2* cand, const int* ccount, int ca
 
 // ------------------------------------------------------------------ finalize helpers
 // Probability of id d under row `slot`'s truncated distribution (its kept list).
-__device__ double keep_lookup(const SampArgs& a, int kslot, int n, int d) {
+__device__ __forceinline__ double keep_lookup(const SampArgs& a, int kslot, int n, int d) {
     const int lane = threadIdx.x & 63;
     const KeepEntry* k = a.keep + (size_t)kslot * a.keepcap;
     double p = 0.0;
@@ -321,7 +321,7 @@ __device__ double keep_lookup(const SampArgs& a, int kslot, int n, int d) {
 // Exponential race over a kept list: weights max(0, p - q) (q from another kept list, a
 // one-hot proposal at `onehot_d`, or none) with a fallback to p if every weight is 0. fp64
 // keys w / E with E = -ln U from the two race words of the id; ties to the lowest id.
-__device__ int keep_race(const SampArgs& a, int pslot, int np, int qslot, int nq, int onehot_d,
+__device__ __forceinline__ int keep_race(const SampArgs& a, int pslot, int np, int qslot, int nq, int onehot_d,
                          int b, int pos) {
     const int lane = threadIdx.x & 63;
     const KeepEntry* kp = a.keep + (size_t)pslot * a.keepcap;
@@ -644,7 +644,7 @@ __device__ __forceinline__ void select_row(const SampArgs& a, const SeqMode& m, 
 // and kept lists, the acceptance tests, the draws over kept lists, the outputs, and a race
 // request for a draw over the whole vocabulary (race_kernel, next in the stream).
 template <bool MAP>
-__device__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, FinalShared& fs,
+__device__ __forceinline__ void finalize_sequence(const SampArgs& a, const SeqMode& m, int b, FinalShared& fs,
                                   RowInfo* rinfo /* LDS, one per row of the list */) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nrows = seq_nrows(a, m);
@@ -1326,8 +1326,12 @@ __global__ __launch_bounds__(kThreads, 3) void sweep_kernel(const SampArgs a) {
 #pragma unroll
             for (int e = 0; e < kWe; ++e) xa[e] = penalize(xa[e], (int)cnt[e], m.pp, m.fp);
         }
-        // this row's outputs: its statistics and, for a truncated or top-n row, candidates
-        const float cs = r.kind == 2 ? kLog2e : kLog2e / m.temp;
+        // this row's outputs: its statistics and, for a truncated or top-n row, candidates;
+        // log2(e) / T recomputed per row (hoisted, it would hold a vector register across
+        // the loop)
+        float temp = m.temp;
+        asm volatile("" : "+s"(temp));
+        const float cs = r.kind == 2 ? kLog2e : kLog2e / temp;
         const float4 st = wave_row_stats(base, lane, valid, r.kind == 0 && !m.sampled, cs, xa);
         const bool cand = r.kind == 2 ? m.ntop > 0 : m.topk;
         int tot = 0;
@@ -1409,25 +1413,26 @@ __global__ __launch_bounds__(kThreads, 3) void sweep_kernel(const SampArgs a) {
 // logit z, or the draft logit), where v* is the value at which the mass e^((v - vmax) / T)
 // of the ids sorted by v (descending) first reaches top_p of the row's mass; ties at v* are
 // kept (mlx-dspark release v0.1.0 "Lossless top-p / top-k sampling": the nucleus truncates
-// draft and target). No sort: one workgroup per row finds v* by a weighted selection. Pass
-// 1 over the row histograms the mass by (vmax - v) / T in steps of 1/16 and finds the
-// bucket where the mass from the top crosses the target; pass 2 lists that bucket's ids
-// (usually a few hundred); a radix selection on their ordered keys, 8 bits at a time,
-// weighted by mass, finds v*.
-
-constexpr int kNucBuckets = 2048;
-constexpr int kNucList = 4096;
-__device__ __forceinline__ int nuc_bucket(float v, float vmax, float s16) {
-    const float u = (vmax - v) * s16;         // monotone in v: ties share a bucket (s16 = 16/T)
-    return u < (float)(kNucBuckets - 1) ? (int)u : kNucBuckets - 1;
+// draft and target). No sort: a weighted selection over many workgroups per row.
+//  (1) Histogram pass (select kernel): nsel workgroups per row each bin a share of the
+//      row's chunks by (vmax - v) / T in steps of 1/16 (kNucBins bins, the last holding
+//      every lower value) with the mass in fp64, and add their bins into the row's
+//      histogram in the workspace; the last to finish finds the crossing bin b*, where the
+//      mass from the top reaches top_p of the row's mass.
+//  (2) Listing pass (finalize kernel): one workgroup per (sequence, chunk) appends, for
+//      each nucleus row of the sequence, the chunk's ids in b* (their ordered keys) to the
+//      row's list (one reservation per row and chunk); the last to finish runs, one wave
+//      per row, a radix selection on the listed keys weighted by mass (8 bits at a time,
+//      from the top), which gives v*. A row whose crossing bin is the last one, or whose
+//      list does not fit, takes the same radix selection over rescans of the whole row.
+__device__ __forceinline__ int nuc_bin(float v, float vmax, float s16) {
+    const float u = (vmax - v) * s16;         // monotone in v: ties share a bin (s16 = 16/T)
+    return u < (float)(kNucBins - 1) ? (int)u : kNucBins - 1;
 }
-struct NucShared {
-    double hm[kNucBuckets];                   // mass per bucket / digit
-    int hn[kNucBuckets];                      // ids per bucket / digit
-    uint32_t lkey[kNucList];                  // the crossing bucket's ids: ordered key of y
-    double lw[kNucList];                      // and mass
+struct NucBins {                              // LDS: a histogram of bins or radix digits
+    double hm[kNucBins];                      // mass per bin / digit
+    int hn[kNucBins];                         // ids per bin / digit
     int drafts[kMaxSeqRows];
-    int cnt;
     int pos, cnt_before;
     double mass_before;
 };
@@ -1449,19 +1454,21 @@ __device__ __forceinline__ int wave_scan_i(int v) {
     return v;
 }
 
-// Wave 0: walks positions 0..nb-1 of a histogram (bucket nb - 1 - p when rev) from `base`
-// and stores in ns the first position whose running mass reaches `target`, the running
-// mass before it (base included) and the ids of this histogram before it; when none does
-// (rounding at the very end), the last non-empty position.
-__device__ __forceinline__ void nuc_crossing(NucShared& ns, int nb, bool rev, double base, double target) {
+// One wave walks positions 0..nb-1 of hm / hn (nb a multiple of 64; position p is bin
+// nb - 1 - p when rev) from `base`: the first position whose running mass reaches `target`
+// (when none does, rounding at the very end, the last non-empty one), the running mass
+// before it (base included) and the ids of this histogram before it, in every lane.
+__device__ __forceinline__ void wave_crossing(const double* hm, const int* hn, int nb, bool rev,
+                                              double base, double target, int* pos_out,
+                                              double* mass_out, int* cnt_out) {
     const int lane = threadIdx.x & 63;
     const int per = nb / 64;
     double ms = 0.0;
     int cs = 0;
     for (int i = 0; i < per; ++i) {
         const int p = lane * per + i, idx = rev ? nb - 1 - p : p;
-        ms += ns.hm[idx];
-        cs += ns.hn[idx];
+        ms += hm[idx];
+        cs += hn[idx];
     }
     const double incl = wave_scan_d(ms);
     const int incl_n = wave_scan_i(cs);
@@ -1474,56 +1481,57 @@ __device__ __forceinline__ void nuc_crossing(NucShared& ns, int nb, bool rev, do
     const unsigned long long hit = __ballot(base + incl >= target);
     const unsigned long long nz = __ballot(cs > 0);
     const int L = hit ? __ffsll(hit) - 1 : (nz ? 63 - __clzll(nz) : 0);
-    if (lane != L) return;
     double acc = base + excl;
     int an = excl_n;
-    int pos = -1, last = -1, last_n = 0;
-    double last_m = 0.0;
-    for (int i = 0; i < per; ++i) {
-        const int p = lane * per + i, idx = rev ? nb - 1 - p : p;
-        if (hit && acc + ns.hm[idx] >= target) {
-            pos = p;
-            break;
+    int pos = -1;
+    if (lane == L) {
+        int last = -1, last_n = 0;
+        double last_m = 0.0;
+        for (int i = 0; i < per; ++i) {
+            const int p = lane * per + i, idx = rev ? nb - 1 - p : p;
+            if (hit && acc + hm[idx] >= target) {
+                pos = p;
+                break;
+            }
+            if (hn[idx] > 0) {
+                last = p;
+                last_m = acc;
+                last_n = an;
+            }
+            acc += hm[idx];
+            an += hn[idx];
         }
-        if (ns.hn[idx] > 0) {
-            last = p;
-            last_m = acc;
-            last_n = an;
+        if (pos < 0) {                                  // no crossing here: last non-empty
+            pos = last < 0 ? lane * per : last;
+            acc = last_m;
+            an = last_n;
         }
-        acc += ns.hm[idx];
-        an += ns.hn[idx];
     }
-    if (pos < 0) {                                  // no crossing here: last non-empty
-        pos = last < 0 ? lane * per : last;
-        acc = last_m;
-        an = last_n;
-    }
-    ns.pos = pos;
-    ns.mass_before = acc;
-    ns.cnt_before = an;
+    *pos_out = __shfl(pos, L);
+    *mass_out = __shfl(acc, L);
+    *cnt_out = __shfl(an, L);
 }
 
-// One pass over row r's values v, f(v) per id whose v lies in [vlo, vhi] (ids past the
-// vocabulary skipped; the interval spares the mass for ids that cannot matter).
-// Target rows carry their penalties (base counts plus the drafts before the row).
+// One pass over row r's values v in chunks [cb, ce), f(v) per id (ids past the vocabulary
+// skipped). Target rows carry their penalties (base counts plus the drafts before the row).
 template <bool VEC, bool MAP, class F>
 __device__ __forceinline__ void nuc_pass(const SampArgs& a, const SeqMode& m, const RowRef& r, int b,
-                         const int* drafts, float vlo, float vhi, F&& f) {
+                                         const int* drafts, int cb, int ce, F&& f) {
     constexpr int kB = 4;                           // chunks whose loads are in flight together
     const bool pen = r.kind == 0 && (m.pp != 0.f || m.fp != 0.f);
     const int32_t* crow = a.counts ? a.counts + (size_t)b * a.vocab : nullptr;
-    for (int c0 = 0; c0 < a.nchunk; c0 += kB) {
+    for (int c0 = cb; c0 < ce; c0 += kB) {
         float x[kB][kEpt];
         int cnt[kB][kEpt];
 #pragma unroll
         for (int u = 0; u < kB; ++u) {
-            if (c0 + u >= a.nchunk) break;
+            if (c0 + u >= ce) continue;
             load_row_chunk<VEC, MAP>(a, m, r, (c0 + u) * kChunk, x[u]);
             if (pen) load_counts<VEC>(crow, (c0 + u) * kChunk, a.vocab, cnt[u]);
         }
 #pragma unroll
         for (int u = 0; u < kB; ++u) {
-            if (c0 + u >= a.nchunk) break;
+            if (c0 + u >= ce) continue;
             const int base = (c0 + u) * kChunk;
             if (pen) {
                 uint32_t dm[kEpt];
@@ -1534,19 +1542,18 @@ __device__ __forceinline__ void nuc_pass(const SampArgs& a, const SeqMode& m, co
             }
 #pragma unroll
             for (int e = 0; e < kEpt; ++e)
-                if (elem_id(base, e) < a.vocab && x[u][e] >= vlo && x[u][e] <= vhi)
-                    f(x[u][e]);
+                if (elem_id(base, e) < a.vocab) f(x[u][e]);
         }
     }
 }
 
-// Per-thread run-length aggregation of (bucket, mass) before the LDS atomics: ids of one
-// thread that fall in the same bucket in a row cost one atomic.
+// Per-thread run-length aggregation of (bin, mass) before the LDS atomics: ids of one
+// thread that fall in the same bin in a row cost one atomic.
 struct NucRun {
     int cur = -1;
     double acc = 0.0;
     int n = 0;
-    __device__ __forceinline__ void add(NucShared& ns, int k, double w) {
+    __device__ __forceinline__ void add(NucBins& ns, int k, double w) {
         if (k != cur) {
             flush(ns);
             cur = k;
@@ -1554,7 +1561,7 @@ struct NucRun {
         acc += w;
         ++n;
     }
-    __device__ __forceinline__ void flush(NucShared& ns) {
+    __device__ __forceinline__ void flush(NucBins& ns) {
         if (cur >= 0) {
             atomicAdd(&ns.hm[cur], acc);
             atomicAdd(&ns.hn[cur], n);
@@ -1565,88 +1572,246 @@ struct NucRun {
     }
 };
 
-// Nucleus row q of sequence b (target or draft row of a sampled sequence with top_p < 1
-// and no top-k): y*, its kept mass and count to the row's workspace RowInfo.
+// The result of a nucleus row (no top-k) to its RowInfo.
+__device__ __forceinline__ void nuc_result(const SampArgs& a, const RowRef& r, float vmax,
+                                           uint32_t prefix, int kept, double zk) {
+    RowInfo* out = a.rows + r.slot;
+    out->theta = kNegInf;
+    out->kept_k = a.vocab;
+    out->kept_p = kept;
+    out->ythr = key_float(prefix);
+    out->ymax = vmax;
+    out->zk = zk;
+}
+
+// (1) Histogram pass of nucleus row q of sequence b, share s of a.nsel.
 template <bool VEC, bool MAP>
-__device__ __forceinline__ void nucleus_row(const SampArgs& a, const SeqMode& m, int b, int q, NucShared& ns) {
-    const int tid = threadIdx.x, wave = tid >> 6;
+__device__ __forceinline__ void nucleus_hist(const SampArgs& a, const SeqMode& m, int b, int q,
+                                             int s, NucBins& ns, int* s_last) {
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const RowRef r = row_ref(a, m, q);
     if (tid < m.k) ns.drafts[tid] = a.drafts[m.d0 + tid];
-    for (int i = tid; i < kNucBuckets; i += kThreads) {
+    for (int i = tid; i < kNucBins; i += kThreads) {
         ns.hm[i] = 0.0;
         ns.hn[i] = 0;
     }
-    if (tid == 0) ns.cnt = 0;
     const RowInfo st = row_stats_wave(a, m, r);      // the row's max of v (every wave)
     const float vmax = st.m;
     const float s16 = 16.f / m.temp;
     __syncthreads();
-    RowInfo* out = a.rows + r.slot;
+    NucInfo* const ni = a.nuc_info + r.slot;
     if (vmax == kNegInf) {                             // no orderable value: nothing kept
-        if (tid == 0) {
+        if (s == 0 && tid == 0) {
+            RowInfo* out = a.rows + r.slot;
             out->theta = kNegInf;
             out->kept_k = a.vocab;
             out->kept_p = 0;
             out->ythr = __builtin_inff();
             out->ymax = vmax;
             out->zk = 0.0;
+            ni->bstar = -1;
+            ni->listed = 0;
         }
         return;
     }
-    // ---- pass 1: mass per bucket of (ymax - y)
+    const int cb = (int)((long)s * a.nchunk / a.nsel), ce = (int)((long)(s + 1) * a.nchunk / a.nsel);
     {
         NucRun run;
-        nuc_pass<VEC, MAP>(a, m, r, b, ns.drafts, kNegInf, __builtin_inff(), [&](float v) {
-            run.add(ns, nuc_bucket(v, vmax, s16), nuc_mass(v, vmax, m.temp));
+        nuc_pass<VEC, MAP>(a, m, r, b, ns.drafts, cb, ce, [&](float v) {
+            run.add(ns, nuc_bin(v, vmax, s16), nuc_mass(v, vmax, m.temp));
         });
         run.flush(ns);
     }
     __syncthreads();
-    __shared__ double s_target;
+    // this share's bins into the row's histogram (device-scope atomics; the bins are zero
+    // between calls)
+    double* const ghm = a.nuc_hm + (size_t)r.slot * kNucBins;
+    uint32_t* const ghn = a.nuc_hn + (size_t)r.slot * kNucBins;
+    for (int i = tid; i < kNucBins; i += kThreads)
+        if (ns.hn[i] != 0) {
+            atomicAdd(ghm + i, ns.hm[i]);
+            atomicAdd(ghn + i, (uint32_t)ns.hn[i]);
+        }
+    if (!handoff_arrive(counter_at(a.ctr, a.ctr_x, 4 * a.batch + r.slot), (uint32_t)a.nsel, s_last))
+        return;
+    // the last share: the whole histogram (read where the atomics were performed), back to
+    // zero for the next call; the row's mass, the target and the crossing bin
+    for (int i = tid; i < kNucBins; i += kThreads) {
+        unsigned long long* const hb = reinterpret_cast<unsigned long long*>(ghm + i);
+        ns.hm[i] = __longlong_as_double(
+            (long long)__hip_atomic_load(hb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        ns.hn[i] = (int)__hip_atomic_load(ghn + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(hb, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(ghn + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
     if (wave == 0) {
         double t = 0.0;
-        for (int i = tid; i < kNucBuckets; i += 64) t += ns.hm[i];
+        for (int i = lane; i < kNucBins; i += 64) t += ns.hm[i];
         t = wave_sum_d(t);
         const double target = (double)m.top_p * t;
-        if (tid == 0) s_target = target;
-        nuc_crossing(ns, kNucBuckets, false, 0.0, target);
+        int pos, cbf;
+        double mb;
+        wave_crossing(ns.hm, ns.hn, kNucBins, false, 0.0, target, &pos, &mb, &cbf);
+        if (lane == 0) {
+            NucInfo info;
+            info.mass_before = mb;
+            info.target = target;
+            info.vmax = vmax;
+            info.bstar = pos;
+            info.cnt_before = cbf;
+            info.nb = ns.hn[pos];
+            info.listed = 0;
+            *ni = info;
+        }
     }
-    __syncthreads();
-    const double target = s_target;
-    const int bstar = ns.pos;
-    double base = ns.mass_before;
-    int cbase = ns.cnt_before;
-    const int nb = ns.hn[bstar];
-    __syncthreads();
-    // ---- pass 2: the crossing bucket's ids (when they fit the list)
-    const bool listed = nb <= kNucList;
-    // values v that can fall in bucket bstar, with a wide margin (the bucket test itself
-    // decides): v in [vmax - (bstar + 1) T / 16, vmax - bstar T / 16], widened by 1e-3 of
-    // the magnitudes
-    float vlo = kNegInf, vhi = __builtin_inff();
+}
+
+// (2) Listing pass: chunk c of every nucleus row of sequence b, one wave per row; the
+// ordered keys of the ids in the row's crossing bin go to its list (the row's candidate
+// area, kept as a compact array of keys, capacity nchunk * capc * 2) at offsets reserved
+// with one atomic per row and chunk.
+template <bool VEC, bool MAP>
+__device__ __forceinline__ void nucleus_list(const SampArgs& a, const SeqMode& m, int b, int c) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int base = c * kChunk;
+    const int ndata = m.rows + seq_ndraft(a, m);       // targets and drafts: the nucleus rows
+    const bool has_pen = m.pp != 0.f || m.fp != 0.f;
+    const float s16 = 16.f / m.temp;
+    const uint32_t cap = (uint32_t)a.nchunk * (uint32_t)a.capc * 2u;
+    uint32_t valid = 0;
+#pragma unroll
+    for (int e = 0; e < kWe; ++e) valid |= (welem_id(base, lane, e) < a.vocab ? 1u : 0u) << e;
+    uint32_t cnt[kWe];
     {
-        const double t = (double)m.temp;
-        const double slack = 1e-3 * (fabs((double)vmax) + (bstar + 1) * t / 16.0) + 1e-30;
-        if (bstar < kNucBuckets - 1) vlo = (float)((double)vmax - (bstar + 1) * t / 16.0 - slack);
-        vhi = (float)((double)vmax - bstar * t / 16.0 + slack);
+        const bool pc = has_pen && a.counts != nullptr;
+        wbuf_load<VEC>(handoff_rsrc(pc ? (const void*)(a.counts + (size_t)b * a.vocab)
+                                       : (const void*)a.tl,
+                                    pc ? (uint32_t)a.vocab * 4u : 0u),
+                       base, lane, cnt);
     }
-    if (listed) {
-        nuc_pass<VEC, MAP>(a, m, r, b, ns.drafts, vlo, vhi, [&](float v) {
-            if (nuc_bucket(v, vmax, s16) == bstar) {
-                const int p = atomicAdd(&ns.cnt, 1);
-                if (p < kNucList) {
-                    ns.lkey[p] = ord_key(v);
-                    ns.lw[p] = nuc_mass(v, vmax, m.temp);
-                }
+    int applied = 0;                                   // drafts already in cnt (see the sweep)
+    for (int q = wave; q < ndata; q += 4) {
+        const RowRef r = row_ref(a, m, q);
+        const int bstar = __builtin_amdgcn_readfirstlane(a.nuc_info[r.slot].bstar);
+        if (bstar < 0 || bstar == kNucBins - 1) continue;   // resolved, or rescanned
+        const float vmax = __int_as_float(
+            __builtin_amdgcn_readfirstlane(__float_as_int(a.nuc_info[r.slot].vmax)));
+        float x[kWe];
+        wload_row<VEC, MAP>(a, m, q, true, base, lane, valid, x);
+        if (r.kind == 0 && has_pen) {
+            for (; applied < r.i; ++applied) {
+                const int off = __builtin_amdgcn_readfirstlane(a.drafts[m.d0 + applied]) - base;
+                if (off < 0 || off >= kChunk) continue;
+                const int ee = 4 * (off >> 8) + (off & 3);
+                const bool mine = ((off >> 2) & 63) == lane;
+#pragma unroll
+                for (int e = 0; e < kWe; ++e) cnt[e] += (mine && e == ee) ? 1u : 0u;
             }
-        });
-        __syncthreads();
+#pragma unroll
+            for (int e = 0; e < kWe; ++e) x[e] = penalize(x[e], (int)cnt[e], m.pp, m.fp);
+        }
+        uint32_t tm = 0u;
+#pragma unroll
+        for (int e = 0; e < kWe; ++e)
+            tm |= (((valid >> e) & 1u) && nuc_bin(x[e], vmax, s16) == bstar) ? (1u << e) : 0u;
+        const int n = __popc(tm);
+        const int incl = wave_incl_scan_i(n);
+        const int total = __builtin_amdgcn_readlane(incl, 63);
+        if (total == 0) continue;
+        int r0 = 0;
+        if (lane == 0) r0 = atomicAdd(&a.nuc_info[r.slot].listed, total);
+        r0 = __builtin_amdgcn_readfirstlane(r0);
+        uint32_t* const list = reinterpret_cast<uint32_t*>(a.cand + (size_t)r.slot * a.nchunk * a.capc);
+        const __amdgpu_buffer_rsrc_t rl = handoff_rsrc(list, cap * 4u);
+        const int o = r0 + incl - n;
+#pragma unroll
+        for (int e = 0; e < kWe; ++e) {
+            const uint32_t pos = (uint32_t)(o + __popc(tm & ((1u << e) - 1u)));
+            __builtin_amdgcn_raw_buffer_store_b32(ord_key(x[e]), rl,
+                                                  ((tm >> e) & 1u) ? pos * 4u : cap * 4u, 0,
+                                                  kCpolSc1);
+        }
     }
-    const int nl = min(ns.cnt, kNucList);
-    // ---- radix selection on the ordered keys of the bucket's ids, weighted by mass
-    uint32_t prefix = 0u;
+}
+
+// v* of nucleus row q from its listed keys, by one wave: radix selection on the ordered
+// keys, 8 bits at a time from the top, weighted by mass. false: the row takes the rescan.
+__device__ __forceinline__ bool nucleus_finish_wave(const SampArgs& a, const SeqMode& m, int q,
+                                                    uint32_t* lkey /* LDS, kWaveList */,
+                                                    double* hm /* LDS, 256 */, int* hn /* 256 */) {
+    constexpr int kWaveList = 1024;
+    constexpr int kPer = kWaveList / 64;
+    const int lane = threadIdx.x & 63;
+    const RowRef r = row_ref(a, m, q);
+    const NucInfo ni = a.nuc_info[r.slot];
+    if (ni.bstar < 0) return true;                     // resolved by the histogram pass
+    const int listed = (int)__hip_atomic_load(&a.nuc_info[r.slot].listed, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t cap = (uint32_t)a.nchunk * (uint32_t)a.capc * 2u;
+    if (ni.bstar == kNucBins - 1 || ni.nb > kWaveList || listed != ni.nb || (uint32_t)listed > cap)
+        return false;
+    const uint32_t* list = reinterpret_cast<const uint32_t*>(a.cand + (size_t)r.slot * a.nchunk * a.capc);
+    const __amdgpu_buffer_rsrc_t rl = handoff_rsrc(list, (uint32_t)listed * 4u);
+    uint32_t kv[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+        kv[j] = __builtin_amdgcn_raw_buffer_load_b32(rl, (uint32_t)(lane + 64 * j) * 4u, 0, kCpolSc1);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) lkey[lane + 64 * j] = kv[j];
+    wave_sync();
+    double base = ni.mass_before;
+    int cbase = ni.cnt_before;
     double last_m = 0.0;
     int last_n = 0;
+    uint32_t prefix = 0u;
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            hm[lane + 64 * i] = 0.0;
+            hn[lane + 64 * i] = 0;
+        }
+        wave_sync();
+        for (int i = lane; i < listed; i += 64) {
+            const uint32_t key = lkey[i];
+            if (pass > 0 && (key >> (shift + 8)) != prefix) continue;
+            const int d = (int)((key >> shift) & 255u);
+            atomicAdd(&hm[d], nuc_mass(key_float(key), ni.vmax, m.temp));
+            atomicAdd(&hn[d], 1);
+        }
+        wave_sync();
+        int pos, cb;
+        double mb;
+        wave_crossing(hm, hn, 256, true, base, ni.target, &pos, &mb, &cb);
+        const int digit = 255 - pos;
+        base = mb;
+        cbase += cb;
+        last_m = hm[digit];
+        last_n = hn[digit];
+        prefix = (prefix << 8) | (uint32_t)digit;
+        wave_sync();
+    }
+    if (lane == 0) nuc_result(a, r, ni.vmax, prefix, cbase + last_n, base + last_m);
+    return true;
+}
+
+// The same selection by the whole workgroup over rescans of row q (the ids of the crossing
+// bin found again in each radix pass): any list size, any crossing bin.
+template <bool VEC, bool MAP>
+__device__ __forceinline__ void nucleus_rescan(const SampArgs& a, const SeqMode& m, int b, int q,
+                                               NucBins& ns) {
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const RowRef r = row_ref(a, m, q);
+    const NucInfo ni = a.nuc_info[r.slot];
+    const float s16 = 16.f / m.temp;
+    if (tid < m.k) ns.drafts[tid] = a.drafts[m.d0 + tid];
+    double base = ni.mass_before;
+    int cbase = ni.cnt_before;
+    double last_m = 0.0;
+    int last_n = 0;
+    uint32_t prefix = 0u;
     for (int pass = 0; pass < 4; ++pass) {
         const int shift = 24 - 8 * pass;
         for (int i = tid; i < 256; i += kThreads) {
@@ -1654,67 +1819,108 @@ __device__ __forceinline__ void nucleus_row(const SampArgs& a, const SeqMode& m,
             ns.hn[i] = 0;
         }
         __syncthreads();
-        auto visit = [&](uint32_t key, double w, NucRun& run) {
-            if (pass > 0 && (key >> (shift + 8)) != prefix) return;
-            run.add(ns, (int)((key >> shift) & 255u), w);
-        };
-        NucRun run;
-        if (listed) {
-            for (int i = tid; i < nl; i += kThreads) visit(ns.lkey[i], ns.lw[i], run);
-        } else {
-            nuc_pass<VEC, MAP>(a, m, r, b, ns.drafts, vlo, vhi, [&](float v) {
-                if (nuc_bucket(v, vmax, s16) == bstar)
-                    visit(ord_key(v), nuc_mass(v, vmax, m.temp), run);
+        {
+            NucRun run;
+            nuc_pass<VEC, MAP>(a, m, r, b, ns.drafts, 0, a.nchunk, [&](float v) {
+                if (nuc_bin(v, ni.vmax, s16) != ni.bstar) return;
+                const uint32_t key = ord_key(v);
+                if (pass > 0 && (key >> (shift + 8)) != prefix) return;
+                run.add(ns, (int)((key >> shift) & 255u), nuc_mass(v, ni.vmax, m.temp));
             });
+            run.flush(ns);
         }
-        run.flush(ns);
         __syncthreads();
-        if (wave == 0) nuc_crossing(ns, 256, true, base, target);
+        if (wave == 0) {
+            int pos, cb;
+            double mb;
+            wave_crossing(ns.hm, ns.hn, 256, true, base, ni.target, &pos, &mb, &cb);
+            if (lane == 0) {
+                ns.pos = pos;
+                ns.mass_before = mb;
+                ns.cnt_before = cb;
+            }
+        }
         __syncthreads();
         const int digit = 255 - ns.pos;
-        base = ns.mass_before;                         // includes the earlier mass
-        cbase += ns.cnt_before;                        // ids of this pass before the digit
+        base = ns.mass_before;
+        cbase += ns.cnt_before;
         last_m = ns.hm[digit];
         last_n = ns.hn[digit];
         prefix = (prefix << 8) | (uint32_t)digit;
         __syncthreads();
     }
-    if (tid == 0) {
-        out->theta = kNegInf;                          // no top-k
-        out->kept_k = a.vocab;
-        out->kept_p = cbase + last_n;
-        out->ythr = key_float(prefix);
-        out->ymax = vmax;
-        out->zk = base + last_m;
-    }
+    if (tid == 0) nuc_result(a, r, ni.vmax, prefix, cbase + last_n, base + last_m);
 }
+
 // ------------------------------------------------------------------ top-k pipeline kernels
-// grid (B x rows_cap): workgroup (b, q) selects row q of sequence b when it is a truncated
-// or top-n row; every other workgroup returns at once.
+// grid (B x rows_cap x nsel): workgroup (b, q, s) selects row q of sequence b when it is a
+// truncated or top-n row (s = 0), or runs share s of the histogram pass of a nucleus row;
+// every other workgroup returns at once.
 template <bool VEC, bool MAP>
 __global__ __launch_bounds__(kThreads) void select_kernel(const SampArgs a, int rows_cap) {
     __shared__ FinalShared s_final;
-    __shared__ NucShared s_nuc;
+    __shared__ NucBins s_bins;
+    __shared__ int s_last;
     preload_args(a);
-    const int b = blockIdx.x / rows_cap, q = blockIdx.x % rows_cap;
+    // the shares s > 0 come last in the grid: the workgroups with work are dispatched first
+    const int nbq = a.batch * rows_cap;
+    const int s = blockIdx.x / nbq, bq = blockIdx.x - s * nbq;
+    const int b = bq / rows_cap, q = bq % rows_cap;
     uint32_t ebits = 0;
     const SeqMode m = seq_mode(a, b, &ebits);
     if (!m.valid || q >= seq_nrows(a, m)) return;
-    if (m.nucleus && row_ref(a, m, q).kind != 2) nucleus_row<VEC, MAP>(a, m, b, q, s_nuc);
-    else select_row(a, m, q, s_final);
+    if (m.nucleus && row_ref(a, m, q).kind != 2) nucleus_hist<VEC, MAP>(a, m, b, q, s, s_bins, &s_last);
+    else if (s == 0) select_row(a, m, q, s_final);
 }
 
 
-// grid (B): merges the chunk statistics and runs the acceptance of one sequence.
-template <bool MAP>
+// grid (B x nfin): merges the chunk statistics and runs the acceptance of one sequence
+// (workgroup (b, 0)); for a sequence with nucleus rows, workgroup (b, c) first lists chunk
+// c of them and the last to finish completes the rows, then finalizes the sequence.
+template <bool VEC, bool MAP>
 __global__ __launch_bounds__(kThreads) void finalize_kernel(const SampArgs a) {
     __shared__ FinalShared s_final;
     __shared__ RowInfo s_rinfo[3 * kMaxSeqRows];
+    __shared__ uint32_t s_lkey[4][1024];
+    __shared__ double s_whm[4][256];
+    __shared__ int s_whn[4][256];
+    __shared__ NucBins s_bins;
+    __shared__ int s_fb[kMaxSeqRows * 2];
+    __shared__ int s_nfb;
+    __shared__ int s_last;
     preload_args(a);
-    const int b = blockIdx.x;
+    // chunk-major: the workgroups (b, 0), which finalize the sequences without nucleus rows,
+    // are dispatched first
+    const int c = blockIdx.x / a.batch, b = blockIdx.x - c * a.batch;
+    const int tid = threadIdx.x, wave = tid >> 6;
     uint32_t ebits = 0;
     const SeqMode m = seq_mode(a, b, &ebits);
     if (!m.valid) return;
+    if (m.nucleus) {
+        if (tid == 0) s_nfb = 0;
+        // the listed keys go out and come back with the hand-off cache policy (coherent
+        // across the XCDs), so the count-in needs no cache write-back
+        nucleus_list<VEC, MAP>(a, m, b, c);
+        if (!handoff_arrive(counter_at(a.ctr, a.ctr_x, 4 * b + 2), (uint32_t)a.nfin, &s_last)) return;
+        const int ndata = m.rows + seq_ndraft(a, m);
+        for (int q = wave; q < ndata; q += 4)
+            if (!nucleus_finish_wave(a, m, q, s_lkey[wave], s_whm[wave], s_whn[wave]) &&
+                (tid & 63) == 0)
+                s_fb[atomicAdd(&s_nfb, 1)] = q;
+        __syncthreads();
+        const int nfb = s_nfb;
+        for (int i = 0; i < nfb; ++i) {
+            const int q = s_fb[i];
+            __syncthreads();
+            nucleus_rescan<VEC, MAP>(a, m, b, q, s_bins);
+        }
+        // this workgroup's row results in place before the acceptance reads them back
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    } else if (c != 0) {
+        return;
+    }
     finalize_sequence<MAP>(a, m, b, s_final, s_rinfo);
 }
 
@@ -1732,7 +1938,8 @@ SampPlan plan_sample(int B, int total_rows, int V, int max_top_k, int max_top_lp
     p.slots = 3 * total_rows - B;
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     size_t off = kWsHeader;                         // error word, counters
-    p.n_ctr_x = extra_counters(4L * B);
+    // counters: four per sequence, then one per row slot (the nucleus histogram pass)
+    p.n_ctr_x = extra_counters(4L * B + (max_top_k > 0 ? (long)p.slots : 0L));
     p.off_ctr_x = off;
     off += up(p.n_ctr_x * 4);
     p.off_stats = off;
@@ -1749,6 +1956,14 @@ SampPlan plan_sample(int B, int total_rows, int V, int max_top_k, int max_top_lp
     off += up((size_t)B * sizeof(RaceReq));
     p.off_race_part = off;
     off += up((size_t)B * p.nchunk * 4 * 16);
+    // nucleus rows without top-k need max_top_k >= 1
+    const size_t nslots = max_top_k > 0 ? (size_t)p.slots : 0;
+    p.off_nuc_hm = off;
+    off += up(nslots * kNucBins * 8);
+    p.off_nuc_hn = off;
+    off += up(nslots * kNucBins * 4);
+    p.off_nuc_info = off;
+    off += up(nslots * sizeof(NucInfo));
     p.bytes = off;
     return p;
 }
@@ -1801,9 +2016,16 @@ hipError_t launch_sample(const SampArgs& args, hipStream_t stream) {
 #undef VSA_SWEEP
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // one workgroup per (sequence, row of its row list), then one per sequence
+    // one workgroup per (sequence, row of its row list), several per nucleus row; then one
+    // per sequence, or per (sequence, chunk) when nucleus rows may be present
     const int rows_cap = 3 * a.max_rows;
-    const dim3 sgrid((unsigned)a.batch * rows_cap);
+    a.nsel = 1;
+    a.nfin = 1;
+    if (a.max_top_k > 0 && a.nuc_info != nullptr) {
+        while (a.nsel < 16 && (long)a.batch * rows_cap * a.nsel * 2 <= 1024) a.nsel *= 2;
+        a.nfin = a.nchunk;
+    }
+    const dim3 sgrid((unsigned)a.batch * rows_cap * a.nsel);
     if (map) {
         if (vec) hipLaunchKernelGGL((select_kernel<true, true>), sgrid, block, 0, stream, a, rows_cap);
         else hipLaunchKernelGGL((select_kernel<false, true>), sgrid, block, 0, stream, a, rows_cap);
@@ -1813,8 +2035,14 @@ hipError_t launch_sample(const SampArgs& args, hipStream_t stream) {
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (map) hipLaunchKernelGGL(finalize_kernel<true>, dim3((unsigned)a.batch), block, 0, stream, a);
-    else hipLaunchKernelGGL(finalize_kernel<false>, dim3((unsigned)a.batch), block, 0, stream, a);
+    const dim3 fgrid((unsigned)a.batch * a.nfin);
+    if (map) {
+        if (vec) hipLaunchKernelGGL((finalize_kernel<true, true>), fgrid, block, 0, stream, a);
+        else hipLaunchKernelGGL((finalize_kernel<false, true>), fgrid, block, 0, stream, a);
+    } else {
+        if (vec) hipLaunchKernelGGL((finalize_kernel<true, false>), fgrid, block, 0, stream, a);
+        else hipLaunchKernelGGL((finalize_kernel<false, false>), fgrid, block, 0, stream, a);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     // Only the device knows which sequences end in a full-vocabulary draw; every other

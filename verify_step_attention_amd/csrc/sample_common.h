@@ -138,7 +138,7 @@ __device__ __forceinline__ double weight64(float v, float vmax, float temp) {
 // relative error (~1e-7) does not grow with the distance to the maximum.
 __device__ __forceinline__ double nuc_mass(float v, float vmax, float temp) {
     if (v == kNegInf) return 0.0;
-    double t = ((double)v - (double)vmax) / (double)temp * 1.4426950408889634;
+    double t = ((double)v - (double)vmax) * (1.4426950408889634 / (double)temp);
     if (!(t > -1100.0)) return 0.0;                  // NaN or below every double
     if (!(t <= 0.0)) t = 0.0;                        // v <= vmax
     const double n = floor(t);

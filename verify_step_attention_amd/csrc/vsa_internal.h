@@ -312,6 +312,21 @@ struct RowInfo {
     double zk;
 };
 
+// Nucleus rows without top-k: bins of (vmax - v) / T in steps of 1/16 (the last bin holds
+// every lower value), filled by several workgroups per row; the last to finish finds the
+// bin where the mass from the top reaches top_p of the row's mass.
+constexpr int kNucBins = 512;
+struct NucInfo {       // one nucleus row: its crossing bin, for the listing of that bin's ids
+    double mass_before;    // mass of the bins above the crossing bin
+    double target;         // top_p times the row's mass
+    float vmax;            // the row's max of v (the bins' origin)
+    int bstar;             // the crossing bin; -1: the row is resolved already
+    int cnt_before;        // ids in the bins above it
+    int nb;                // ids in it
+    int listed;            // ids listed so far by the listing pass (reservations)
+    int pad;
+};
+
 struct KeepEntry {     // one id of a truncated, renormalized distribution
     int idx;
     int pad;
@@ -366,6 +381,12 @@ struct SampArgs {
                                    // for its sequence's statistics before it hands its chunk
                                    // of the draw to the last arriver
     int rsplit;                    // sweep: workgroups sharing a (sequence, chunk)'s rows
+    // nucleus rows without top-k (null when max_top_k is 0)
+    double* nuc_hm;                // [slots][kNucBins] mass per bin (zero between calls)
+    uint32_t* nuc_hn;              // [slots][kNucBins] ids per bin (zero between calls)
+    NucInfo* nuc_info;             // [slots]
+    int nsel;                      // select: workgroups per nucleus row (histogram pass)
+    int nfin;                      // finalize: workgroups per sequence (listing pass)
 };
 // The fused kernel keeps each sequence's counters and race words on lines 4b .. 4b + 3 and
 // its claim words on the lines after the first 4B.
@@ -388,7 +409,7 @@ __device__ __forceinline__ void preload_args(const SampArgs& a) {
 struct SampPlan {
     int nchunk, capc, keepcap, slots;
     size_t off_ctr_x, n_ctr_x, off_stats, off_cand, off_meta, off_rows, off_keep,
-        off_race, off_race_part, bytes;
+        off_race, off_race_part, off_nuc_hm, off_nuc_hn, off_nuc_info, bytes;
 };
 
 SampPlan plan_sample(int B, int total_rows, int V, int max_top_k, int max_top_lp);
