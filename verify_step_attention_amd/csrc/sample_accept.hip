@@ -1437,21 +1437,30 @@ struct NucBins {                              // LDS: a histogram of bins or rad
     double mass_before;
 };
 
-__device__ __forceinline__ double wave_scan_d(double v) {
-    const int lane = threadIdx.x & 63;
-    for (int off = 1; off < 64; off <<= 1) {
-        const double o = __shfl_up(v, off);
-        if (lane >= off) v += o;
-    }
-    return v;
+
+// Inclusive prefix sum of a double over the wave's lanes, by DPP moves of its two halves
+// (shifts by 1, 2, 4, 8 within rows of 16 lanes, then the row totals by broadcasts).
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ double dpp_d(double v) {
+    const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, ROWS, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, ROWS, 0xF, false);
+    return __longlong_as_double((long long)(((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo));
 }
-__device__ __forceinline__ int wave_scan_i(int v) {
-    const int lane = threadIdx.x & 63;
-    for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(v, off);
-        if (lane >= off) v += o;
-    }
-    return v;
+__device__ __forceinline__ double wave_incl_scan_d(double x) {
+    x += dpp_d<0x111>(x);
+    x += dpp_d<0x112>(x);
+    x += dpp_d<0x114>(x);
+    x += dpp_d<0x118>(x);
+    x += dpp_d<kDppBcast15, 0xA>(x);
+    x += dpp_d<kDppBcast31, 0xC>(x);
+    return x;
+}
+__device__ __forceinline__ double readlane_d(double v, int l) {
+    const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
 }
 
 // One wave walks positions 0..nb-1 of hm / hn (nb a multiple of 64; position p is bin
@@ -1470,19 +1479,14 @@ __device__ __forceinline__ void wave_crossing(const double* hm, const int* hn, i
         ms += hm[idx];
         cs += hn[idx];
     }
-    const double incl = wave_scan_d(ms);
-    const int incl_n = wave_scan_i(cs);
-    double excl = __shfl_up(incl, 1);
-    int excl_n = __shfl_up(incl_n, 1);
-    if (lane == 0) {
-        excl = 0.0;
-        excl_n = 0;
-    }
+    const double incl = wave_incl_scan_d(ms);
+    const int incl_n = wave_incl_scan_i(cs);
     const unsigned long long hit = __ballot(base + incl >= target);
     const unsigned long long nz = __ballot(cs > 0);
-    const int L = hit ? __ffsll(hit) - 1 : (nz ? 63 - __clzll(nz) : 0);
-    double acc = base + excl;
-    int an = excl_n;
+    const int L = hit ? __ffsll(hit) - 1 : (nz ? 63 - __clzll(nz) : 0);   // uniform
+    // lane L walks its positions from the running totals of the lanes before it
+    double acc = base + (L > 0 ? readlane_d(incl, L - 1) : 0.0);
+    int an = L > 0 ? __builtin_amdgcn_readlane(incl_n, L - 1) : 0;
     int pos = -1;
     if (lane == L) {
         int last = -1, last_n = 0;
@@ -1507,9 +1511,9 @@ __device__ __forceinline__ void wave_crossing(const double* hm, const int* hn, i
             an = last_n;
         }
     }
-    *pos_out = __shfl(pos, L);
-    *mass_out = __shfl(acc, L);
-    *cnt_out = __shfl(an, L);
+    *pos_out = __builtin_amdgcn_readlane(pos, L);
+    *mass_out = readlane_d(acc, L);
+    *cnt_out = __builtin_amdgcn_readlane(an, L);
 }
 
 // One pass over row r's values v in chunks [cb, ce), f(v) per id (ids past the vocabulary
@@ -1694,12 +1698,14 @@ __device__ __forceinline__ void nucleus_list(const SampArgs& a, const SeqMode& m
     int applied = 0;                                   // drafts already in cnt (see the sweep)
     for (int q = wave; q < ndata; q += 4) {
         const RowRef r = row_ref(a, m, q);
-        const int bstar = __builtin_amdgcn_readfirstlane(a.nuc_info[r.slot].bstar);
-        if (bstar < 0 || bstar == kNucBins - 1) continue;   // resolved, or rescanned
-        const float vmax = __int_as_float(
-            __builtin_amdgcn_readfirstlane(__float_as_int(a.nuc_info[r.slot].vmax)));
+        // the row's crossing bin and its chunk, requested together
+        const int bstar_v = a.nuc_info[r.slot].bstar;
+        const float vmax_v = a.nuc_info[r.slot].vmax;
         float x[kWe];
         wload_row<VEC, MAP>(a, m, q, true, base, lane, valid, x);
+        const int bstar = __builtin_amdgcn_readfirstlane(bstar_v);
+        if (bstar < 0 || bstar == kNucBins - 1) continue;   // resolved, or rescanned
+        const float vmax = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(vmax_v)));
         if (r.kind == 0 && has_pen) {
             for (; applied < r.i; ++applied) {
                 const int off = __builtin_amdgcn_readfirstlane(a.drafts[m.d0 + applied]) - base;
@@ -1745,28 +1751,43 @@ __device__ __forceinline__ bool nucleus_finish_wave(const SampArgs& a, const Seq
     constexpr int kPer = kWaveList / 64;
     const int lane = threadIdx.x & 63;
     const RowRef r = row_ref(a, m, q);
-    const NucInfo ni = a.nuc_info[r.slot];
-    if (ni.bstar < 0) return true;                     // resolved by the histogram pass
-    const int listed = (int)__hip_atomic_load(&a.nuc_info[r.slot].listed, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
+    // the row's record, its list count and the first kWaveList slots of its list, requested
+    // together (slots past the count are masked below)
     const uint32_t cap = (uint32_t)a.nchunk * (uint32_t)a.capc * 2u;
-    if (ni.bstar == kNucBins - 1 || ni.nb > kWaveList || listed != ni.nb || (uint32_t)listed > cap)
-        return false;
     const uint32_t* list = reinterpret_cast<const uint32_t*>(a.cand + (size_t)r.slot * a.nchunk * a.capc);
-    const __amdgpu_buffer_rsrc_t rl = handoff_rsrc(list, (uint32_t)listed * 4u);
+    const __amdgpu_buffer_rsrc_t rl = handoff_rsrc(list, cap * 4u);
     uint32_t kv[kPer];
 #pragma unroll
     for (int j = 0; j < kPer; ++j)
         kv[j] = __builtin_amdgcn_raw_buffer_load_b32(rl, (uint32_t)(lane + 64 * j) * 4u, 0, kCpolSc1);
+    const NucInfo ni = a.nuc_info[r.slot];
+    const int listed = (int)__hip_atomic_load(&a.nuc_info[r.slot].listed, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    if (ni.bstar < 0) return true;                     // resolved by the histogram pass
+    if (ni.bstar == kNucBins - 1 || ni.nb > kWaveList || listed != ni.nb || (uint32_t)listed > cap)
+        return false;
+    // the keys' common leading bits: digits above the first differing bit are fixed (every
+    // key has them, so the crossing is there with nothing above it)
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) lkey[lane + 64 * j] = kv[j];
+    for (int j = 0; j < kPer; ++j) {
+        lkey[lane + 64 * j] = kv[j];
+        if (lane + 64 * j < listed) {
+            kmin = min(kmin, kv[j]);
+            kmax = max(kmax, kv[j]);
+        }
+    }
+    kmin = (uint32_t)wave_min_i((int)(kmin ^ 0x80000000u)) ^ 0x80000000u;
+    kmax = ~((uint32_t)wave_min_i((int)(~kmax ^ 0x80000000u)) ^ 0x80000000u);
+    const int same = kmin == kmax ? 32 : __clz((int)(kmin ^ kmax));
+    const int pass0 = same / 8;                        // passes before it: one digit each
     wave_sync();
     double base = ni.mass_before;
     int cbase = ni.cnt_before;
     double last_m = 0.0;
-    int last_n = 0;
-    uint32_t prefix = 0u;
-    for (int pass = 0; pass < 4; ++pass) {
+    int last_n = listed;
+    uint32_t prefix = pass0 > 0 ? kmin >> (32 - 8 * pass0) : 0u;
+    for (int pass = pass0; pass < 4; ++pass) {
         const int shift = 24 - 8 * pass;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -1774,12 +1795,28 @@ __device__ __forceinline__ bool nucleus_finish_wave(const SampArgs& a, const Seq
             hn[lane + 64 * i] = 0;
         }
         wave_sync();
+        // each lane's keys of one digit in a row cost one atomic
+        int cur = -1, n = 0;
+        double acc = 0.0;
         for (int i = lane; i < listed; i += 64) {
             const uint32_t key = lkey[i];
             if (pass > 0 && (key >> (shift + 8)) != prefix) continue;
             const int d = (int)((key >> shift) & 255u);
-            atomicAdd(&hm[d], nuc_mass(key_float(key), ni.vmax, m.temp));
-            atomicAdd(&hn[d], 1);
+            if (d != cur) {
+                if (cur >= 0) {
+                    atomicAdd(&hm[cur], acc);
+                    atomicAdd(&hn[cur], n);
+                }
+                cur = d;
+                acc = 0.0;
+                n = 0;
+            }
+            acc += nuc_mass(key_float(key), ni.vmax, m.temp);
+            ++n;
+        }
+        if (cur >= 0) {
+            atomicAdd(&hm[cur], acc);
+            atomicAdd(&hn[cur], n);
         }
         wave_sync();
         int pos, cb;
@@ -1792,6 +1829,11 @@ __device__ __forceinline__ bool nucleus_finish_wave(const SampArgs& a, const Seq
         last_n = hn[digit];
         prefix = (prefix << 8) | (uint32_t)digit;
         wave_sync();
+    }
+    if (pass0 == 4) {                                  // every key equal: all of them kept
+        double t = 0.0;
+        for (int i = lane; i < listed; i += 64) t += nuc_mass(key_float(lkey[i]), ni.vmax, m.temp);
+        last_m = wave_sum_d(t);
     }
     if (lane == 0) nuc_result(a, r, ni.vmax, prefix, cbase + last_n, base + last_m);
     return true;
