@@ -318,16 +318,57 @@ __device__ __forceinline__ double keep_lookup(const SampArgs& a, int kslot, int 
         if (k[i].idx == d) p = k[i].p;
     return wave_sum_d(p);
 }
+// A double moved by DPP (its two halves with the same control); lanes without a source read 0.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ double dpp_d(double v) {
+    const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, ROWS, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, ROWS, 0xF, false);
+    return __longlong_as_double((long long)(((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+// (value, id) with the larger value, ties to the lower id, over the wave (every lane), for
+// non-negative values (a lane without a source reads value 0, id 0, which never wins over
+// a value > 0 and, at 0, only over a larger id: callers treat 0 as "none")
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ void argmax_step_d(double& v, int& i) {
+    const double ov = dpp_d<CTRL, ROWS>(v);
+    const int oi = dpp_i<CTRL, ROWS>(kBigIdx, i);
+    const bool take = (ov > v) | ((ov == v) & (oi < i));
+    v = take ? ov : v;
+    i = take ? oi : i;
+}
+__device__ __forceinline__ void wave_argmax_d(double& v, int& i) {
+    argmax_step_d<kDppSwap1>(v, i);
+    argmax_step_d<kDppSwap2>(v, i);
+    argmax_step_d<kDppHalfMirror>(v, i);
+    argmax_step_d<kDppMirror>(v, i);
+    argmax_step_d<kDppBcast15, 0xA>(v, i);
+    argmax_step_d<kDppBcast31, 0xC>(v, i);
+    const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), 63);
+    v = __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+    i = __builtin_amdgcn_readlane(i, 63);
+}
+
 // Exponential race over a kept list: weights max(0, p - q) (q from another kept list, a
 // one-hot proposal at `onehot_d`, or none) with a fallback to p if every weight is 0. fp64
 // keys w / E with E = -ln U from the two race words of the id; ties to the lowest id.
 __device__ __forceinline__ int keep_race(const SampArgs& a, int pslot, int np, int qslot, int nq, int onehot_d,
-                         int b, int pos) {
+                         int b, int pos, int* qidx /* LDS, kKeep */, double* qp /* LDS, kKeep */) {
     const int lane = threadIdx.x & 63;
     const KeepEntry* kp = a.keep + (size_t)pslot * a.keepcap;
     const KeepEntry* kq = qslot >= 0 ? a.keep + (size_t)qslot * a.keepcap : nullptr;
     const bool resid = kq != nullptr || onehot_d >= 0;
-    double best = -1.0, fbest = -1.0;
+    // the q list in LDS: every p entry scans it there, one broadcast read per entry
+    if (kq) {
+        for (int t = lane; t < nq; t += 64) {
+            qidx[t] = kq[t].idx;
+            qp[t] = kq[t].p;
+        }
+        wave_sync();
+    }
+    double best = 0.0, fbest = 0.0;
     int bi = kBigIdx, fbi = kBigIdx;
     for (int i = lane; i < np; i += 64) {
         const int j = kp[i].idx;
@@ -335,7 +376,7 @@ __device__ __forceinline__ int keep_race(const SampArgs& a, int pslot, int np, i
         double q = 0.0;
         if (kq)
             for (int t = 0; t < nq; ++t)
-                if (kq[t].idx == j) q = kq[t].p;
+                if (qidx[t] == j) q = qp[t];
         if (j == onehot_d) q = 1.0;
         const double r = resid ? fmax(0.0, p - q) : p;
         const uint4 w = philox_block(a.seed, (uint32_t)j >> 1, (uint32_t)pos, (uint32_t)b, 1u);
@@ -349,14 +390,9 @@ __device__ __forceinline__ int keep_race(const SampArgs& a, int pslot, int np, i
             if (key > fbest || (key == fbest && j < fbi)) { fbest = key; fbi = j; }
         }
     }
-    for (int off = 32; off >= 1; off >>= 1) {
-        const double ob = __shfl_xor(best, off);
-        const int oi = __shfl_xor(bi, off);
-        if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
-        const double fb = __shfl_xor(fbest, off);
-        const int fi = __shfl_xor(fbi, off);
-        if (fb > fbest || (fb == fbest && fi < fbi)) { fbest = fb; fbi = fi; }
-    }
+    wave_argmax_d(best, bi);
+    wave_argmax_d(fbest, fbi);
+    if (kq) wave_sync();                               // the LDS list may be reused next
     return best > 0.0 ? bi : fbi;
 }
 
@@ -668,6 +704,11 @@ __device__ __forceinline__ void finalize_sequence(const SampArgs& a, const SeqMo
         }
     }
 
+    // the truncated rows' selection results (select_kernel, a kernel earlier), requested
+    // ahead of the statistics (thread q holds row q's; nrows <= kThreads)
+    RowInfo sel_ri{};
+    const bool sel_row = tid < nrows && (m.topk || m.nucleus) && row_ref(a, m, tid).kind != 2;
+    if (sel_row) sel_ri = a.rows[row_ref(a, m, tid).slot];
     // ---- A: merge the chunk statistics of every row. One wave per row, rows q = wave,
     //      wave + 4, ...; the (<= kMaxChunks) chunk entries of up to 3 rows per wave are
     //      loaded in one round (up to kChunkLoads per lane per row), only the half of each
@@ -723,19 +764,15 @@ __device__ __forceinline__ void finalize_sequence(const SampArgs& a, const SeqMo
     }
     __syncthreads();
 
-    // ---- B: selection results of truncated rows (select_kernel, a kernel earlier)
-    for (int q = tid; q < nrows; q += kThreads) {
-        const RowRef r = row_ref(a, m, q);
-        if ((m.topk || m.nucleus) && r.kind != 2) {
-            const RowInfo sr = a.rows[r.slot];
-            rinfo[q].theta = sr.theta;
-            rinfo[q].kept_k = sr.kept_k;
-            rinfo[q].kept_p = sr.kept_p;
-            if (m.nucleus) {
-                rinfo[q].ythr = sr.ythr;
-                rinfo[q].ymax = sr.ymax;
-                rinfo[q].zk = sr.zk;
-            }
+    // ---- B: selection results of truncated rows
+    if (sel_row) {
+        rinfo[tid].theta = sel_ri.theta;
+        rinfo[tid].kept_k = sel_ri.kept_k;
+        rinfo[tid].kept_p = sel_ri.kept_p;
+        if (m.nucleus) {
+            rinfo[tid].ythr = sel_ri.ythr;
+            rinfo[tid].ymax = sel_ri.ymax;
+            rinfo[tid].zk = sel_ri.zk;
         }
     }
     __syncthreads();
@@ -839,30 +876,36 @@ __device__ __forceinline__ void finalize_sequence(const SampArgs& a, const SeqMo
                 }
             }
         } else {
-            // truncated rows: probabilities from the kept lists, one draft at a time
-            bool all = true;
-            for (int t = 1; t <= m.k; ++t) {
-                const int pos = base_pos + t - 1;
-                const int d = drafts[t - 1];
-                const bool valid = d >= 0 && d < a.vocab;
-                if (!valid) ebits |= VSA_DEVERR_DRAFT_ID;
-                const double pd = fs.pq[0][t - 1], qd = fs.pq[1][t - 1];   // 0 if invalid
-                if (accept_uniform(a.seed, b, pos) * qd < pd) { ++acc; continue; }
-                all = false;
+            // truncated rows: every draft's test at once (lane t - 1: p and q from the kept
+            // lists, 0 for an invalid draft, so that it is rejected); the accepted prefix
+            // ends at the first lane that rejects
+            bool ok = false;
+            const int d_l = lane < m.k ? drafts[lane] : -1;
+            const bool valid_l = d_l >= 0 && d_l < a.vocab;
+            if (lane < m.k) ok = accept_uniform(a.seed, b, base_pos + lane) * fs.pq[1][lane] <
+                                 fs.pq[0][lane];
+            const unsigned long long rej = __ballot(lane < m.k && !ok);
+            acc = rej ? __ffsll(rej) - 1 : m.k;
+            if (__ballot(lane < m.k && lane <= acc && !valid_l)) ebits |= VSA_DEVERR_DRAFT_ID;
+            const bool all = acc == m.k;
+            if (!all) {
+                const int t = acc + 1, pos = base_pos + acc;
+                const int d = drafts[acc];
                 const RowRef rp = row_ref(a, m, t - 1);
                 if (onehot) {
-                    tok = keep_race(a, rp.slot, rinfo[t - 1].kept_p, -1, 0, d, b, pos);
+                    tok = keep_race(a, rp.slot, rinfo[t - 1].kept_p, -1, 0, d, b, pos, fs.lidx,
+                                    fs.lp);
                 } else {
                     const RowRef rqr = row_ref(a, m, m.rows + t - 1);
                     tok = keep_race(a, rp.slot, rinfo[t - 1].kept_p, rqr.slot,
-                                    rinfo[m.rows + t - 1].kept_p, -1, b, pos);
+                                    rinfo[m.rows + t - 1].kept_p, -1, b, pos, fs.lidx, fs.lp);
                 }
                 if (tok < 0 || tok >= a.vocab) tok = 0;
-                break;
             }
             if (all) {
                 const RowRef rp = row_ref(a, m, m.k);
-                tok = keep_race(a, rp.slot, rinfo[m.k].kept_p, -1, 0, -1, b, base_pos + m.k);
+                tok = keep_race(a, rp.slot, rinfo[m.k].kept_p, -1, 0, -1, b, base_pos + m.k,
+                                fs.lidx, fs.lp);
                 if (tok < 0 || tok >= a.vocab) tok = 0;
             }
         }
@@ -1438,15 +1481,7 @@ struct NucBins {                              // LDS: a histogram of bins or rad
 };
 
 
-// Inclusive prefix sum of a double over the wave's lanes, by DPP moves of its two halves
-// (shifts by 1, 2, 4, 8 within rows of 16 lanes, then the row totals by broadcasts).
-template <int CTRL, int ROWS = 0xF>
-__device__ __forceinline__ double dpp_d(double v) {
-    const unsigned long long u = (unsigned long long)__double_as_longlong(v);
-    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, ROWS, 0xF, false);
-    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, ROWS, 0xF, false);
-    return __longlong_as_double((long long)(((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo));
-}
+// Inclusive prefix sum of a double over the wave's lanes (dpp_d moves its two halves).
 __device__ __forceinline__ double wave_incl_scan_d(double x) {
     x += dpp_d<0x111>(x);
     x += dpp_d<0x112>(x);
