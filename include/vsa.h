@@ -56,12 +56,15 @@ typedef enum vsa_status {
     VSA_ERR_INVALID_ARG = 1,  /* a host-side argument is null, negative or inconsistent */
     VSA_ERR_UNSUPPORTED = 2,  /* valid but outside the supported shapes (see limits) */
     VSA_ERR_WORKSPACE = 3,    /* workspace missing, misaligned or too small */
-    VSA_ERR_LAUNCH = 4        /* the HIP runtime refused a launch */
+    VSA_ERR_LAUNCH = 4,       /* the HIP runtime refused a launch */
+    VSA_STATUS_MAX_ENUM = 0x7fffffff  /* not a status: gives the type the range of int */
 } vsa_status;
 
 typedef enum vsa_dtype {
     VSA_F32 = 0,              /* IEEE binary32 */
-    VSA_BF16 = 1              /* bfloat16 bit patterns (uint16) */
+    VSA_BF16 = 1,             /* bfloat16 bit patterns (uint16) */
+    VSA_DTYPE_MAX_ENUM = 0x7fffffff  /* not a type: any int a caller passes is a value of
+                                        the enumeration, and other values are rejected */
 } vsa_dtype;
 
 /* Device error word bits (uint32 at workspace byte 0). */
@@ -132,7 +135,7 @@ const char* vsa_status_string(vsa_status status);
  *   scale      softmax scale; 0 => 1/sqrt(D)
  *   flags      0, or VSA_ATTN_DYNAMIC_SPLITS (other bits: VSA_ERR_INVALID_ARG)
  *   out        [total_rows, Hq, D] float32, written for every row
- * Limits: (Hq / Hkv) * max_rows_per_seq <= 128.
+ * Limits: (Hq / Hkv) * max_rows_per_seq <= 128; B * Hkv <= 4194304.
  *
  * The keys of each (sequence, KV head) are split over several workgroups whose partial
  * softmax states are merged. With flags = 0 every split owns a fixed key range, so the
@@ -293,8 +296,8 @@ vsa_status verify_attention_kvq(const void* q, const uint8_t* k_codes, const voi
  *                  sequence (-inf when top-k is off), NaN for greedy sequences
  *   diag_kept      [total_rows, 2] int32 kept-set sizes after top-k and after top-p of
  *                  each target row of a sampled sequence (0 for greedy sequences)
- * Limits: 1 <= V <= 524288; K_b <= 31; top_k <= 256; at most 256 ids may tie into one
- * top-k kept set (VSA_DEVERR_TIE_OVERFLOW beyond). A nucleus without top-k (top_p < 1 and
+ * Limits: 1 <= V <= 524288; B <= 4194304; K_b <= 31; top_k <= 256; at most 256 ids may tie
+ * into one top-k kept set (VSA_DEVERR_TIE_OVERFLOW beyond). A nucleus without top-k (top_p < 1 and
  * top_k 0 or >= V) keeps {j : z_j >= z*} over the whole vocabulary, z* found by a
  * weighted selection rather than a sort; it runs in the truncation pipeline, so a call
  * with such a sequence and max_top_k = 0 sets VSA_DEVERR_PARAMS for it (decoded greedily).
@@ -382,7 +385,8 @@ vsa_status verify_sample_accept_onehot(
  *              nibble of byte i
  *   sb         [N, K / 64, 2] fp16 (scale, bias)
  *   bits       8 or 4
- *   M, N, K    1 <= M <= 16; K a multiple of 64 (else VSA_ERR_UNSUPPORTED)
+ *   M, N, K    1 <= M <= 16; K a multiple of 64, at most 16777216 (else
+ *              VSA_ERR_UNSUPPORTED)
  *   y          [M, N] float32 (16-byte aligned when N % 4 == 0), fully written
  *   workspace  small_m_qmm_workspace_size(M, N, K) bytes, 256-byte aligned: partial sums
  *              of the input splits (no state kept between calls)

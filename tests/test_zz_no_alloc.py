@@ -65,8 +65,9 @@ def test_noalloc_error_word_and_size_limit():
     big = vsa.verify_attention_workspace_size(64, 32, 8, 128, 32, 65536)
     assert big > vsa.NOALLOC_SCRATCH_BYTES
     lib = vsa.library()
-    st = lib.verify_attention_noalloc(None, None, None, vsa.VSA_BF16, None, None, 64, 64, 32, 8,
-                                      128, 65536, 32, 65536, 0.0, 0, None, None, None)
+    p = [dev[k].data_ptr() for k in ("q", "k_cache", "v_cache", "cu_rows", "ctx_lens")]
+    st = lib.verify_attention_noalloc(p[0], p[1], p[2], vsa.VSA_BF16, p[3], p[4], 64, 64, 32, 8,
+                                      128, 65536, 32, 65536, 0.0, 0, out.data_ptr(), None, None)
     assert st == vsa.VSA_ERR_WORKSPACE
     # the next call after the refusal still matches the workspace path
     w = wl.make_workload("qwen3_4b")

@@ -42,15 +42,16 @@ const char* vsa_status_string(vsa_status status) {
         case VSA_ERR_UNSUPPORTED: return "VSA_ERR_UNSUPPORTED";
         case VSA_ERR_WORKSPACE: return "VSA_ERR_WORKSPACE";
         case VSA_ERR_LAUNCH: return "VSA_ERR_LAUNCH";
+        default: return "VSA_ERR_UNKNOWN";  // any other int a caller passes
     }
-    return "VSA_ERR_UNKNOWN";
 }
 
 size_t verify_attention_workspace_size(int B, int Hq, int Hkv, int D, int max_rows_per_seq,
                                        int max_kv_len) {
-    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || (D != 64 && D != 128) ||
-        max_rows_per_seq < 1 || max_rows_per_seq > kMaxRowsPerSeq || max_kv_len < 1 ||
-        (Hq / Hkv) * max_rows_per_seq > 128)
+    if (B < 1 || B > kMaxBatch || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 ||
+        (long)B * Hkv > kMaxAttnUnits || (D != 64 && D != 128) || max_rows_per_seq < 1 ||
+        max_rows_per_seq > kMaxRowsPerSeq || max_kv_len < 1 ||
+        (long)(Hq / Hkv) * max_rows_per_seq > 128)
         return 0;
     return plan_attention(B, Hq, Hkv, D, max_rows_per_seq, max_kv_len).bytes;
 }
@@ -88,10 +89,11 @@ vsa_status attention_call(const void* q, const void* k_cache, const void* v_cach
     if (dtype != VSA_F32 && dtype != VSA_BF16) return VSA_ERR_INVALID_ARG;
     if (B < 1 || total_rows < B || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || S_max < 1 ||
         max_rows_per_seq < 1 || max_kv_len < 1 || max_kv_len > S_max ||
-        total_rows > B * max_rows_per_seq || !(scale >= 0.f) || !isfinite(scale))
+        (long)total_rows > (long)B * max_rows_per_seq || !(scale >= 0.f) || !isfinite(scale))
         return VSA_ERR_INVALID_ARG;
     if ((D != 64 && D != 128) || max_rows_per_seq > kMaxRowsPerSeq ||
-        (Hq / Hkv) * max_rows_per_seq > 128)
+        (long)(Hq / Hkv) * max_rows_per_seq > 128 || B > kMaxBatch ||
+        (long)B * Hkv > kMaxAttnUnits)
         return VSA_ERR_UNSUPPORTED;
     // A window bounds the keys of every sequence by window + rows (plus one tile of
     // rounding), so the split count is planned for that; it never exceeds the one the
@@ -195,6 +197,7 @@ vsa_status verify_attention_noalloc(const void* q, const void* k_cache, const vo
                                     int Hkv, int D, int S_max, int max_rows_per_seq,
                                     int max_kv_len, float scale, uint32_t flags, float* out,
                                     uint32_t* device_error, void* stream) {
+    if (!q || !k_cache || !v_cache || !cu_rows || !ctx_lens || !out) return VSA_ERR_INVALID_ARG;
     if (flags & ~VSA_ATTN_DYNAMIC_SPLITS) return VSA_ERR_INVALID_ARG;
     const size_t need = verify_attention_workspace_size(B, Hq, Hkv, D, max_rows_per_seq,
                                                         max_kv_len);
@@ -226,10 +229,11 @@ vsa_status verify_attention_kvq(const void* q, const uint8_t* k_codes, const voi
     if (flags & ~VSA_ATTN_DYNAMIC_SPLITS) return VSA_ERR_INVALID_ARG;
     if (B < 1 || total_rows < B || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || S_max < 1 ||
         max_rows_per_seq < 1 || max_kv_len < 1 || max_kv_len > S_max ||
-        total_rows > B * max_rows_per_seq || !(scale >= 0.f) || !isfinite(scale))
+        (long)total_rows > (long)B * max_rows_per_seq || !(scale >= 0.f) || !isfinite(scale))
         return VSA_ERR_INVALID_ARG;
     if ((D != 64 && D != 128) || max_rows_per_seq > kMaxRowsPerSeq ||
-        (Hq / Hkv) * max_rows_per_seq > 128)
+        (long)(Hq / Hkv) * max_rows_per_seq > 128 || B > kMaxBatch ||
+        (long)B * Hkv > kMaxAttnUnits)
         return VSA_ERR_UNSUPPORTED;
     const AttnPlan plan = plan_attention(B, Hq, Hkv, D, max_rows_per_seq, max_kv_len);
     if (!workspace || !aligned256(workspace) || workspace_bytes < plan.bytes)
@@ -282,8 +286,8 @@ extern "C" {
 size_t verify_sample_accept_workspace_size(int B, int total_rows, int V, int max_rows_per_seq,
                                            int max_top_k, int max_top_logprobs) {
     if (B < 1 || total_rows < B || V < 1 || V > kMaxVocab || max_rows_per_seq < 1 ||
-        max_rows_per_seq > kMaxRowsPerSeq || total_rows > B * max_rows_per_seq ||
-        max_top_k < 0 || max_top_k > kMaxTopK || max_top_logprobs < 0 ||
+        max_rows_per_seq > kMaxRowsPerSeq || (long)total_rows > (long)B * max_rows_per_seq ||
+        B > kMaxBatch || max_top_k < 0 || max_top_k > kMaxTopK || max_top_logprobs < 0 ||
         max_top_logprobs > kMaxTopLogprobs)
         return 0;
     return plan_sample(B, total_rows, V, max_top_k, max_top_logprobs).bytes;
@@ -345,7 +349,7 @@ vsa_status sample_call(const float* target_logits, const float* draft_logits, in
     if (!target_logits || !cu_rows || !params || !positions || !accepted_len || !out_tokens)
         return VSA_ERR_INVALID_ARG;
     if (B < 1 || total_rows < B || V < 1 || max_rows_per_seq < 1 || max_top_k < 0 ||
-        max_top_logprobs < 0 || total_rows > B * max_rows_per_seq)
+        max_top_logprobs < 0 || (long)total_rows > (long)B * max_rows_per_seq)
         return VSA_ERR_INVALID_ARG;
     if (total_rows > B && !draft_tokens) return VSA_ERR_INVALID_ARG;
     if (draft_vocab < 1 || draft_vocab > V || (draft_vocab != V && !t2d))
@@ -353,7 +357,7 @@ vsa_status sample_call(const float* target_logits, const float* draft_logits, in
     if (t2d && (V % 4) == 0 && (reinterpret_cast<uintptr_t>(t2d) & 15u) != 0)
         return VSA_ERR_INVALID_ARG;
     if (V > kMaxVocab || max_rows_per_seq > kMaxRowsPerSeq || max_top_k > kMaxTopK ||
-        max_top_logprobs > kMaxTopLogprobs)
+        max_top_logprobs > kMaxTopLogprobs || B > kMaxBatch)
         return VSA_ERR_UNSUPPORTED;
     const SampPlan plan = plan_sample(B, total_rows, V, max_top_k, max_top_logprobs);
     if (!workspace || !aligned256(workspace) || workspace_bytes < plan.bytes)
@@ -444,7 +448,7 @@ vsa_status verify_sample_accept_onehot(
 }
 
 size_t small_m_qmm_workspace_size(int M, int N, int K) {
-    if (M < 1 || M > 16 || N < 1 || K < 64 || K % 64 != 0) return 0;
+    if (M < 1 || M > 16 || N < 1 || K < 64 || K % 64 != 0 || K > kMaxQmmK) return 0;
     const QmmPlan p = plan_qmm(M, N, K);
     return p.bytes > 0 ? p.bytes : 256;
 }
@@ -455,7 +459,7 @@ vsa_status small_m_qmm(const void* x, const uint8_t* codes, const void* sb, int 
     if (!x || !codes || !sb || !y) return VSA_ERR_INVALID_ARG;
     if (bits != 8 && bits != 4) return VSA_ERR_INVALID_ARG;
     if (M < 1 || N < 1 || K < 1) return VSA_ERR_INVALID_ARG;
-    if (M > 16 || K % 64 != 0) return VSA_ERR_UNSUPPORTED;
+    if (M > 16 || K % 64 != 0 || K > kMaxQmmK) return VSA_ERR_UNSUPPORTED;
     const uintptr_t ax = reinterpret_cast<uintptr_t>(x), ac = reinterpret_cast<uintptr_t>(codes);
     const uintptr_t as = reinterpret_cast<uintptr_t>(sb), ay = reinterpret_cast<uintptr_t>(y);
     if ((ax & 15u) || (ac & 15u) || (as & 3u) || (ay & ((N % 4) == 0 ? 15u : 3u)))

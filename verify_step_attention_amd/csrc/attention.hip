@@ -1539,7 +1539,7 @@ AttnPlan plan_attention(int B, int Hq, int Hkv, int D, int max_rows, int max_kv_
     p.units = B * Hkv;
     p.tile = 128;
     // Aim for about VSA_ATTN_TARGET_WGS workgroups over the 256 CUs, at least one tile each.
-    const int tiles = (max_kv_len + p.tile - 1) / p.tile;
+    const int tiles = (int)(((long)max_kv_len + p.tile - 1) / p.tile);
     int nsplit = (VSA_ATTN_TARGET_WGS + p.units - 1) / p.units;
     if (nsplit > tiles) nsplit = tiles;
     if (nsplit > kMaxSplits) nsplit = kMaxSplits;

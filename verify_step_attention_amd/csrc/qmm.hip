@@ -258,7 +258,7 @@ __global__ __launch_bounds__(256) void qmm_reduce_kernel(const QmmArgs a) {
 
 QmmPlan plan_qmm(int M, int N, int K) {
     QmmPlan p{};
-    p.tiles = (N + kQRows - 1) / kQRows;
+    p.tiles = (int)(((long)N + kQRows - 1) / kQRows);
     // about two workgroups per CU over the 256 CUs, splits of at least one chunk
     const int groups = K / 64;
     int nsplit = (512 + p.tiles - 1) / p.tiles;

@@ -1372,7 +1372,8 @@ __global__ __launch_bounds__(kThreads, 3) void sweep_kernel(const SampArgs a) {
         // this row's outputs: its statistics and, for a truncated or top-n row, candidates;
         // log2(e) / T recomputed per row (hoisted, it would hold a vector register across
         // the loop)
-        float temp = m.temp;
+        // the sequence's T is uniform over the wave: held in a scalar register, opaque
+        float temp = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(m.temp)));
         asm volatile("" : "+s"(temp));
         const float cs = r.kind == 2 ? kLog2e : kLog2e / temp;
         const float4 st = wave_row_stats(base, lane, valid, r.kind == 0 && !m.sampled, cs, xa);

@@ -292,6 +292,9 @@ hipError_t launch_qmm(const QmmArgs& a, hipStream_t stream);
 
 // ---------------------------------------------------------------- vocabulary stage
 constexpr int kChunk = 2048;         // vocabulary ids per workgroup chunk (8 per thread)
+constexpr int kMaxBatch = 1 << 22;  // sequences per call
+constexpr int kMaxQmmK = 1 << 24;   // inner dimension of small_m_qmm
+constexpr long kMaxAttnUnits = 1L << 22;  // (sequence, KV head) pairs per attention call
 constexpr int kMaxChunks = 256;      // chunks per row (vocabulary <= kMaxChunks * kChunk)
 constexpr int kChunkLoads = kMaxChunks / 64;   // per-lane loads when a wave reads a row's chunks
 constexpr int kKeep = 256;           // kept-set capacity of one truncated row
