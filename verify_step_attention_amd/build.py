@@ -23,6 +23,11 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"),
 ]
 
+# Per-source flags. The attention kernels keep their MFMA accumulators in ordinary vector
+# registers: with the default accumulation-register form, every rescale of O (a vector
+# multiply) copied the accumulators out and back, about 150 moves per 32-key sub-tile.
+SOURCE_FLAGS = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 
 def _run(cmd, verbose):
     if verbose:
@@ -42,7 +47,8 @@ def build(verbose=False, extra_flags=()):
     tmp = LIB + ".tmp"
     with tempfile.TemporaryDirectory(prefix="vsa_build_") as td:
         objs = [os.path.join(td, os.path.basename(s) + ".o") for s in srcs]
-        jobs = [[HIPCC, *FLAGS, *extra_flags, "-c", s, "-o", o] for s, o in zip(srcs, objs)]
+        jobs = [[HIPCC, *FLAGS, *SOURCE_FLAGS.get(os.path.basename(s), []), *extra_flags, "-c",
+                 s, "-o", o] for s, o in zip(srcs, objs)]
         workers = min(len(jobs), max(1, min(8, os.cpu_count() or 1)))
         with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
             list(ex.map(lambda c: _run(c, verbose), jobs))
