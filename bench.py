@@ -84,15 +84,25 @@ def algorithmic_bytes(w, kv_bits=16, draft_vocab=0):
             "kv": kv, "q_out": q + o, "target_logits": tl, "draft_logits": dl, "counts": cnt}
 
 
+def attention_build_digest():
+    """SHA-256 of the attention source and the flags it is compiled with: the recorded
+    counters hold for the kernel binary these two determine."""
+    from verify_step_attention_amd import build as vbuild
+    h = hashlib.sha256()
+    with open(ATTN_SRC, "rb") as f:
+        h.update(f.read())
+    flags = vbuild.FLAGS + vbuild.SOURCE_FLAGS.get(os.path.basename(ATTN_SRC), [])
+    h.update(json.dumps([f for f in flags if not f.startswith(ROOT)]).encode())
+    return h.hexdigest()
+
+
 def counters_traffic():
     """(fetch+write bytes per attention launch) from the recorded rocprofv3 runs, if they were
     taken on the current attention source; else None."""
     try:
         with open(COUNTERS) as f:
             rec = json.load(f)
-        with open(ATTN_SRC, "rb") as f:
-            digest = hashlib.sha256(f.read()).hexdigest()
-        if rec.get("attention_source_sha256") != digest:
+        if rec.get("attention_build_sha256") != attention_build_digest():
             return None
         return rec["bytes_per_launch"]
     except (OSError, KeyError, ValueError):
@@ -491,11 +501,9 @@ def record_traffic(fetch_dir, write_dir, copy_mib, command):
         raise SystemExit(f"no attention kernel in the counters: {list(kernels)}")
     a = {"fetch_bytes": sum(kernels[k]["fetch_bytes"] for k in attn),
          "write_bytes": sum(kernels[k]["write_bytes"] for k in attn)}
-    with open(ATTN_SRC, "rb") as f:
-        digest = hashlib.sha256(f.read()).hexdigest()
     rec = {"command": command, "copy_probe_mib": copy_mib,
            "copy_fetch_scale": round(f_scale, 4), "copy_write_scale": round(w_scale, 4),
-           "attention_source_sha256": digest,
+           "attention_build_sha256": attention_build_digest(),
            "bytes_per_launch": a["fetch_bytes"] + a["write_bytes"], "kernels": kernels}
     with open(COUNTERS, "w") as f:
         json.dump(rec, f, indent=1)
