@@ -296,8 +296,9 @@ vsa_status verify_attention_kvq(const void* q, const uint8_t* k_codes, const voi
  *                  sequence (-inf when top-k is off), NaN for greedy sequences
  *   diag_kept      [total_rows, 2] int32 kept-set sizes after top-k and after top-p of
  *                  each target row of a sampled sequence (0 for greedy sequences)
- * Limits: 1 <= V <= 524288; B <= 4194304; K_b <= 31; top_k <= 256; at most 256 ids may tie
- * into one top-k kept set (VSA_DEVERR_TIE_OVERFLOW beyond). A nucleus without top-k (top_p < 1 and
+ * Limits: 1 <= V <= 524288; B <= 4194304, B * ceil(V / 2048) <= 16777215 and
+ * 3 * B * max_rows_per_seq <= 16777215 (workgroups of one launch); K_b <= 31; top_k <= 256;
+ * at most 256 ids may tie into one top-k kept set (VSA_DEVERR_TIE_OVERFLOW beyond). A nucleus without top-k (top_p < 1 and
  * top_k 0 or >= V) keeps {j : z_j >= z*} over the whole vocabulary, z* found by a
  * weighted selection rather than a sort; it runs in the truncation pipeline, so a call
  * with such a sequence and max_top_k = 0 sets VSA_DEVERR_PARAMS for it (decoded greedily).
@@ -385,8 +386,8 @@ vsa_status verify_sample_accept_onehot(
  *              nibble of byte i
  *   sb         [N, K / 64, 2] fp16 (scale, bias)
  *   bits       8 or 4
- *   M, N, K    1 <= M <= 16; K a multiple of 64, at most 16777216 (else
- *              VSA_ERR_UNSUPPORTED)
+ *   M, N, K    1 <= M <= 16; K a multiple of 64, at most 16777216; ceil(N / 128) <=
+ *              16777215 (else VSA_ERR_UNSUPPORTED)
  *   y          [M, N] float32 (16-byte aligned when N % 4 == 0), fully written
  *   workspace  small_m_qmm_workspace_size(M, N, K) bytes, 256-byte aligned: partial sums
  *              of the input splits (no state kept between calls)

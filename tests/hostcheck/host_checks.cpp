@@ -152,6 +152,14 @@ int main() {
     EXPECT(verify_sample_accept_workspace_size(200000, 600000, 8, 3, 0, 0) > 0);
     EXPECT(verify_attention_workspace_size(65536, 128, 128, 128, 1, 8192) == 0);
     EXPECT(small_m_qmm_workspace_size(8, 1024, 1 << 30) == 0);
+    // grids beyond one dispatch (2^24 - 1 workgroups of 256 threads) are refused
+    EXPECT(verify_sample_accept_workspace_size(1 << 22, 1 << 22, 524288, 1, 0, 0) == 0);
+    EXPECT(verify_sample_accept_workspace_size(1 << 22, 1 << 22, 2048, 1, 0, 0) > 0);
+    EXPECT(sample((const float*)F, (const int32_t*)F, 1 << 22, 1 << 22, 524288, 1, 0, 0, W,
+                  1u << 30) == VSA_ERR_UNSUPPORTED);
+    EXPECT(small_m_qmm_workspace_size(8, INT_MAX, 4096) == 0);
+    EXPECT(small_m_qmm(W, (const uint8_t*)W, W, 4, 8, INT_MAX, 4096, (float*)W, W, 1u << 30,
+                       nullptr) == VSA_ERR_UNSUPPORTED);
     std::printf("%s (%d failures)\n", g_fails ? "FAILED" : "ok", g_fails);
     return g_fails ? 1 : 0;
 }

@@ -281,13 +281,23 @@ vsa_status verify_attention_kvq(const void* q, const uint8_t* k_codes, const voi
 
 }  // extern "C"
 
+namespace {
+// The vocabulary stage launches up to B * ceil(V / 2048) workgroups (statistics, draws) and
+// B * 3 * max_rows_per_seq (selections); both must fit one dispatch.
+bool sample_grids_fit(int B, int V, int max_rows_per_seq) {
+    return (long)B * ((V + kChunk - 1) / kChunk) <= kMaxGridWgs &&
+           (long)B * 3 * max_rows_per_seq <= kMaxGridWgs;
+}
+}  // namespace
+
 extern "C" {
 
 size_t verify_sample_accept_workspace_size(int B, int total_rows, int V, int max_rows_per_seq,
                                            int max_top_k, int max_top_logprobs) {
     if (B < 1 || total_rows < B || V < 1 || V > kMaxVocab || max_rows_per_seq < 1 ||
         max_rows_per_seq > kMaxRowsPerSeq || (long)total_rows > (long)B * max_rows_per_seq ||
-        B > kMaxBatch || max_top_k < 0 || max_top_k > kMaxTopK || max_top_logprobs < 0 ||
+        B > kMaxBatch || !sample_grids_fit(B, V, max_rows_per_seq) || max_top_k < 0 ||
+        max_top_k > kMaxTopK || max_top_logprobs < 0 ||
         max_top_logprobs > kMaxTopLogprobs)
         return 0;
     return plan_sample(B, total_rows, V, max_top_k, max_top_logprobs).bytes;
@@ -357,7 +367,8 @@ vsa_status sample_call(const float* target_logits, const float* draft_logits, in
     if (t2d && (V % 4) == 0 && (reinterpret_cast<uintptr_t>(t2d) & 15u) != 0)
         return VSA_ERR_INVALID_ARG;
     if (V > kMaxVocab || max_rows_per_seq > kMaxRowsPerSeq || max_top_k > kMaxTopK ||
-        max_top_logprobs > kMaxTopLogprobs || B > kMaxBatch)
+        max_top_logprobs > kMaxTopLogprobs || B > kMaxBatch ||
+        !sample_grids_fit(B, V, max_rows_per_seq))
         return VSA_ERR_UNSUPPORTED;
     const SampPlan plan = plan_sample(B, total_rows, V, max_top_k, max_top_logprobs);
     if (!workspace || !aligned256(workspace) || workspace_bytes < plan.bytes)
@@ -450,6 +461,7 @@ vsa_status verify_sample_accept_onehot(
 size_t small_m_qmm_workspace_size(int M, int N, int K) {
     if (M < 1 || M > 16 || N < 1 || K < 64 || K % 64 != 0 || K > kMaxQmmK) return 0;
     const QmmPlan p = plan_qmm(M, N, K);
+    if ((long)p.tiles * p.nsplit > kMaxGridWgs) return 0;
     return p.bytes > 0 ? p.bytes : 256;
 }
 
@@ -465,6 +477,7 @@ vsa_status small_m_qmm(const void* x, const uint8_t* codes, const void* sb, int 
     if ((ax & 15u) || (ac & 15u) || (as & 3u) || (ay & ((N % 4) == 0 ? 15u : 3u)))
         return VSA_ERR_INVALID_ARG;
     const QmmPlan plan = plan_qmm(M, N, K);
+    if ((long)plan.tiles * plan.nsplit > kMaxGridWgs) return VSA_ERR_UNSUPPORTED;
     if (plan.bytes > 0 && (!workspace || !aligned256(workspace) || workspace_bytes < plan.bytes))
         return VSA_ERR_WORKSPACE;
     QmmArgs a{};

@@ -295,6 +295,8 @@ constexpr int kChunk = 2048;         // vocabulary ids per workgroup chunk (8 pe
 constexpr int kMaxBatch = 1 << 22;  // sequences per call
 constexpr int kMaxQmmK = 1 << 24;   // inner dimension of small_m_qmm
 constexpr long kMaxAttnUnits = 1L << 22;  // (sequence, KV head) pairs per attention call
+// Workgroups of 256 threads in one launch: a dispatch's grid size counts work-items in 32 bits.
+constexpr long kMaxGridWgs = (1L << 24) - 1;
 constexpr int kMaxChunks = 256;      // chunks per row (vocabulary <= kMaxChunks * kChunk)
 constexpr int kChunkLoads = kMaxChunks / 64;   // per-lane loads when a wave reads a row's chunks
 constexpr int kKeep = 256;           // kept-set capacity of one truncated row
